@@ -90,8 +90,10 @@ def block_summaries(kt, v, bidx, n_blocks):
     d, dv = kt.shape[1], v.shape[1]
     S = np.zeros((n_blocks, d, dv))
     z = np.zeros((n_blocks, d))
+    order = np.argsort(bidx, kind="stable")
+    bounds = np.searchsorted(bidx[order], np.arange(n_blocks + 1))
     for b in range(n_blocks):
-        sel = bidx == b
+        sel = order[bounds[b]:bounds[b + 1]]          # tokens j with b(j) = b
         kb, vb = kt[sel], v[sel]
         S[b] = kb.T @ vb            # sum over tokens of the outer products k~_j v_j^T
         z[b] = kb.sum(axis=0)
@@ -105,8 +107,9 @@ def block_summaries(kt, v, bidx, n_blocks):
 
 def mix_summaries(mc, S, z):
     mc = np.asarray(mc, np.float64)
-    St = np.einsum("ib,bkc->ikc", mc, S)
-    zt = mc @ z
+    m = S.shape[0]
+    St = (mc @ S.reshape(m, -1)).reshape(S.shape)     # S~_i = sum_b m_ib S_b
+    zt = mc @ z                                       # z~_i = sum_b m_ib z_b
     return St, zt
 
 
@@ -116,12 +119,17 @@ def mix_summaries(mc, S, z):
 # ----------------------------------------------------------------------------------------
 
 def readout(qt, St, zt, bidx, normalized=True):
+    """Each query token t of block i = b(t) reads q~_t^T S~_i (and q~_t^T z~_i); evaluated block
+    by block so no per-token copy of S~ is ever formed."""
     qt = np.asarray(qt, np.float64)
-    num = np.einsum("tk,tkc->tc", qt, St[bidx])
-    if not normalized:
-        return num
-    den = np.einsum("tk,tk->t", qt, zt[bidx])
-    return num / den[:, None]
+    out = np.empty((qt.shape[0], St.shape[2]))
+    for i in range(St.shape[0]):
+        sel = np.nonzero(bidx == i)[0]
+        if sel.size == 0:
+            continue
+        num = qt[sel] @ St[i]
+        out[sel] = num / (qt[sel] @ zt[i])[:, None] if normalized else num
+    return out
 
 
 def _as_head_mc(mc, h, n_blocks):
