@@ -1,0 +1,148 @@
+/*
+ * mhla.h - C ABI of the MI355X (gfx950) forward of token-level multi-head linear attention.
+ *
+ * What is computed (page titles and sections):
+ *   "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head"
+ *     - Method, Overall framework: the N tokens are cut into M non-overlapping blocks (1D spans
+ *       or tiles of a 2D/3D token grid); each block b has a local summary
+ *       S_b = sum_{j in b} phi(K_j) V_j^T (d x d) and normaliser z_b = sum_{j in b} phi(K_j).
+ *     - Key design 2 (multi-head mixing): row i of the coefficient matrix M_c (M x M) mixes
+ *       the summaries for query block i: S~_i = sum_b m_ib S_b, z~_i = sum_b m_ib z_b; a query
+ *       q in block i reads out o = phi(q)^T S~_i / phi(q)^T z~_i (flowchart).  The same section
+ *       allows the normaliser to be dropped for long sequences (UNNORMALIZED readout).
+ *   "Rectifying Magnitude Neglect in Linear Attention"
+ *     - Method, Key design (MALA formula design): with one block (M = 1),
+ *       Y_i = beta_i phi(Q_i) sum_j phi(K_j)^T V_j - gamma_i sum_j V_j,
+ *       beta_i = 1 + 1/(phi(Q_i) sum_m phi(K_m)^T), gamma_i = phi(Q_i) sum_m phi(K_m)^T / N.
+ *   phi is ELU+1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise.  No 1/sqrt(d) scaling is applied.
+ *
+ * Conventions
+ *   - Q, K, V, O are dense [B, H, N, d] row-major (d fastest), device memory, 16-byte aligned.
+ *   - Tokens are in raster order over the token grid, last axis fastest.  Blocks are numbered
+ *     in raster order over the block grid; block extents must divide the grid exactly.
+ *   - M_c is float32 row-major, device memory: [M, M] shared by all heads, or [H, M, M] when
+ *     mc_per_head = 1.  Row i belongs to query block i.  M_c may be NULL only when M == 1.
+ *   - d (head_dim) is one of 16, 32, 64, 128 and is the same for keys and values.
+ *
+ * Ownership and concurrency
+ *   - The caller owns every device buffer (Q, K, V, M_c, O, workspace).  The library owns only
+ *     the host-side plan; it never allocates device memory.
+ *   - Inputs are read-only.  O must not alias Q, K, V or the workspace (exact aliasing is
+ *     rejected; partial overlap is undefined).
+ *   - mhla_forward is asynchronous on the given HIP stream (NULL = default stream).  One
+ *     (plan, workspace) pair may be in flight on one stream at a time.
+ *
+ * Errors
+ *   - Every call returns mhla_status; MHLA_OK is 0.  Arguments are validated before any
+ *     launch; nothing is launched when a call fails validation.  A failed HIP launch returns
+ *     MHLA_ERR_HIP.  NaN/Inf in the data propagate per IEEE and are not errors; there is no
+ *     epsilon in any division.  The library never aborts and never throws across this ABI.
+ */
+#ifndef MHLA_H
+#define MHLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MHLA_OK = 0,
+  MHLA_ERR_INVALID_ARG = 1,   /* NULL pointer, bad struct_size, misaligned or aliased buffer   */
+  MHLA_ERR_UNSUPPORTED = 2,   /* head_dim, dtype, feature map or mode not supported            */
+  MHLA_ERR_SHAPE = 3,         /* grid/block extents inconsistent or not divisible              */
+  MHLA_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than mhla_workspace_size            */
+  MHLA_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed                    */
+  MHLA_ERR_INTERNAL = 6
+} mhla_status;
+
+typedef enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_FP32 = 1 } mhla_dtype;
+
+typedef enum { MHLA_PHI_ELU1 = 0 } mhla_phi;
+
+typedef enum {
+  MHLA_READOUT_NORMALIZED = 0,    /* o = phi(q)^T S~_i / phi(q)^T z~_i                         */
+  MHLA_READOUT_UNNORMALIZED = 1,  /* o = phi(q)^T S~_i                                        */
+  MHLA_READOUT_MALA = 2           /* magnitude-aware readout; requires M == 1                  */
+} mhla_readout;
+
+typedef enum {
+  MHLA_ACCURACY_AUTO = 0,   /* bf16 operands for MHLA with bf16 inputs; split for MALA / fp32   */
+  MHLA_ACCURACY_BF16 = 1,   /* single bf16 MFMA operands, fp32 accumulation                     */
+  MHLA_ACCURACY_SPLIT = 2   /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
+} mhla_accuracy;
+
+typedef struct {
+  uint32_t struct_size;     /* = sizeof(mhla_desc)                                             */
+  int32_t in_dtype;         /* mhla_dtype of Q, K, V                                           */
+  int32_t out_dtype;        /* mhla_dtype of O                                                 */
+  int32_t phi;              /* mhla_phi                                                        */
+  int32_t readout;          /* mhla_readout                                                    */
+  int32_t accuracy;         /* mhla_accuracy                                                   */
+  int32_t ndim;             /* 1, 2 or 3                                                       */
+  int32_t mc_per_head;      /* 0: M_c is [M, M]; 1: M_c is [H, M, M]                           */
+  int64_t grid[3];          /* token grid extents, first ndim used; N = product                */
+  int64_t block[3];         /* block extents, first ndim used; each divides grid exactly       */
+  int64_t batch;            /* B >= 1                                                          */
+  int64_t heads;            /* H >= 1                                                          */
+  int64_t head_dim;         /* d in {16, 32, 64, 128}                                          */
+} mhla_desc;
+
+typedef struct mhla_plan* mhla_handle;
+
+/* Facts about a plan, for callers that size buffers or account bytes and FLOPs. */
+typedef struct {
+  uint32_t struct_size;     /* caller sets = sizeof(mhla_plan_info)                            */
+  int64_t n_tokens;         /* N                                                               */
+  int64_t n_blocks;         /* M                                                               */
+  int64_t block_tokens;     /* n_b = N / M                                                     */
+  int64_t workspace_bytes;  /* same as mhla_workspace_size                                     */
+  int32_t summary_splits;   /* token slices per block in the summary kernel                    */
+  int32_t readout_splits;   /* token slices per block in the readout kernel                    */
+  int32_t n_kernels;        /* kernels launched per mhla_forward                               */
+  int32_t split_operands;   /* 1 if hi/lo operand splitting is in use                          */
+} mhla_plan_info;
+
+/* Validate a descriptor and build a host-side plan.  No device memory is allocated.
+ * Errors: INVALID_ARG (NULL, struct_size), UNSUPPORTED (dtype, phi, readout, d, MALA with
+ * M > 1), SHAPE (ndim, non-positive or non-dividing extents, sizes beyond 2^31 tokens). */
+mhla_status mhla_create(const mhla_desc* desc, mhla_handle* out);
+
+/* Device workspace the caller must pass to mhla_forward, in bytes (256-byte aligned start). */
+mhla_status mhla_workspace_size(mhla_handle h, size_t* bytes);
+
+/* Run the forward on `stream` (a hipStream_t, NULL = default stream).
+ * q, k, v: device [B,H,N,d] of in_dtype.  o: device [B,H,N,d] of out_dtype.
+ * mc: device float32 [M,M] or [H,M,M]; NULL allowed iff M == 1.
+ * workspace: device, >= mhla_workspace_size bytes, 256-byte aligned; its contents on entry are
+ * ignored and on return are unspecified.  Asynchronous: returns after the launches. */
+mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void* v,
+                         const float* mc, void* o, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Release a plan.  NULL is accepted. */
+mhla_status mhla_destroy(mhla_handle h);
+
+/* Static, human-readable text for a status code. */
+const char* mhla_status_string(mhla_status s);
+
+/* Fill `info` for a plan (info->struct_size must be set by the caller). */
+mhla_status mhla_plan_get_info(mhla_handle h, mhla_plan_info* info);
+
+/* Per-kernel timing.  While enabled, every mhla_forward records HIP events around each of its
+ * kernels on the caller's stream (the plan owns the events).  mhla_timing_read synchronises on
+ * the last recorded event, returns for kernel `index` (0 <= index < n_kernels) the summed
+ * milliseconds and the number of timed launches, and leaves the counters untouched;
+ * mhla_timing_reset clears them.  `name` receives a static string naming the kernel. */
+mhla_status mhla_timing_enable(mhla_handle h, int enable);
+mhla_status mhla_timing_read(mhla_handle h, int index, double* total_ms, int64_t* launches,
+                             const char** name);
+mhla_status mhla_timing_reset(mhla_handle h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHLA_H */

@@ -1,0 +1,56 @@
+"""Helpers for GPU parity tests: upload seeded inputs, run the HIP library through its C ABI,
+compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+import token_blocked_linear_amd as T
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x).view(np.int16)
+        return torch.from_numpy(bits).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0")
+
+
+def run_hip(w: synth.Workload, q, k, v, mc, *, out_dtype="fp32", accuracy="auto", repeat=1):
+    """One (or `repeat`) forward(s) through the C ABI; returns float64 numpy outputs."""
+    import torch
+    mc_per_head = mc is not None and np.ndim(mc) == 3
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, accuracy=accuracy,
+                  mc_per_head=mc_per_head)
+    tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
+    tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    ws = plan.alloc_workspace()
+    outs = []
+    for _ in range(repeat):
+        o = torch.empty(w.qkv_shape, dtype=odt, device="cuda:0")
+        plan.forward(tq, tk, tv, tmc, o, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    res = [o.float().cpu().numpy().astype(np.float64) for o in outs]
+    plan.close()
+    return res if repeat > 1 else res[0]
+
+
+def rel_err(got, want):
+    want = np.asarray(want, np.float64)
+    rms = float(np.sqrt(np.mean(want * want)))
+    return float(np.max(np.abs(np.asarray(got, np.float64) - want))) / rms
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def oracle_full(w, q, k, v, mc):
+    return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout)

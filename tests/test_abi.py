@@ -1,0 +1,194 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every function the header
+declares, validates descriptors and forward arguments before any launch, and its host-side
+fast division is exact."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import token_blocked_linear_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhla.h")
+
+
+def _lib_or_skip():
+    if not os.path.exists(T.library_path()):
+        pytest.skip("libmhla.so is not built (run __graft_entry__.build())")
+    return T.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mhla_status|const char\*)\s+(mhla_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == sorted(T.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    _lib_or_skip()
+    out = subprocess.run(["nm", "-D", "--defined-only", T.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(mhla_\w+)$", out, re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+
+
+def test_struct_layouts_match_header():
+    # mhla_desc: 8 x int32 (incl. struct_size) + 2 x int64[3] + 3 x int64 = 32 + 48 + 24
+    assert ctypes.sizeof(T.MhlaDesc) == 104
+    assert ctypes.sizeof(T.MhlaPlanInfo) == 56
+
+
+def _desc(**kw):
+    base = dict(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
+    base.update(kw)
+    return T.make_desc(**base)
+
+
+def _status(desc):
+    lib = _lib_or_skip()
+    h = ctypes.c_void_p()
+    st = lib.mhla_create(ctypes.byref(desc), ctypes.byref(h))
+    if st == 0:
+        lib.mhla_destroy(h)
+    return st
+
+
+def test_create_accepts_workload_shapes():
+    import synth
+    for w in synth.WORKLOADS.values():
+        d = T.make_desc(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                        in_dtype=w.dtype, out_dtype="fp32", readout=w.readout)
+        assert _status(d) == T.MHLA_OK, w.name
+
+
+@pytest.mark.parametrize("mutate,want", [
+    (lambda d: setattr(d, "struct_size", 8), 1),
+    (lambda d: setattr(d, "in_dtype", 7), 2),
+    (lambda d: setattr(d, "out_dtype", -1), 2),
+    (lambda d: setattr(d, "phi", 3), 2),
+    (lambda d: setattr(d, "readout", 9), 2),
+    (lambda d: setattr(d, "accuracy", 5), 2),
+    (lambda d: setattr(d, "head_dim", 48), 2),
+    (lambda d: setattr(d, "head_dim", 256), 2),
+    (lambda d: setattr(d, "ndim", 0), 3),
+    (lambda d: setattr(d, "ndim", 4), 3),
+    (lambda d: setattr(d, "batch", 0), 3),
+    (lambda d: setattr(d, "heads", -2), 3),
+    (lambda d: d.block.__setitem__(1, 15), 3),           # 15 does not divide 64
+    (lambda d: d.grid.__setitem__(0, 0), 3),
+    (lambda d: setattr(d, "readout", T.MHLA_READOUT_MALA), 2),   # MALA needs M == 1
+    (lambda d: setattr(d, "mc_per_head", 2), 1),
+])
+def test_create_rejections(mutate, want):
+    d = _desc()
+    mutate(d)
+    assert _status(d) == want
+
+
+def test_create_null_arguments():
+    lib = _lib_or_skip()
+    h = ctypes.c_void_p()
+    assert lib.mhla_create(None, ctypes.byref(h)) == T.MHLA_OK + 1
+    d = _desc()
+    assert lib.mhla_create(ctypes.byref(d), None) == 1
+    assert lib.mhla_destroy(None) == 0
+
+
+def test_mala_with_one_block_is_accepted():
+    d = _desc(block=(64, 64), readout="mala")
+    assert _status(d) == 0
+
+
+def test_plan_info_and_workspace():
+    _lib_or_skip()
+    p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
+    info = p.info
+    assert (info.n_tokens, info.n_blocks, info.block_tokens) == (4096, 16, 256)
+    assert info.n_kernels == 3 and info.summary_splits >= 1 and info.readout_splits >= 1
+    assert p.workspace_bytes == info.workspace_bytes > 0
+    assert info.split_operands == 0
+    pm = T.Plan(grid=(64, 64), block=(64, 64), batch=16, heads=8, head_dim=64, readout="mala")
+    assert pm.info.n_blocks == 1 and pm.info.split_operands == 1 and pm.info.summary_splits > 1
+    p32 = T.Plan(grid=(8, 8), block=(4, 4), batch=1, heads=1, head_dim=16, in_dtype="fp32")
+    assert p32.info.split_operands == 1
+    for q in (p, pm, p32):
+        q.close()
+
+
+def test_forward_argument_errors_before_launch():
+    """Every case below must be rejected by validation; none reaches a launch (there is no GPU
+    here, so a launch would return MHLA_ERR_HIP instead)."""
+    lib = _lib_or_skip()
+    p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
+    ws = p.workspace_bytes
+    A, B, C, O, MC, W = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x100000
+    f = lambda *a: lib.mhla_forward(p.handle, *a)  # noqa: E731
+    assert f(None, B, C, MC, O, W, ws, None) == 1          # NULL q
+    assert f(A, B, C, None, O, W, ws, None) == 1           # NULL M_c with M > 1
+    assert f(A, B, C, MC, A, W, ws, None) == 1             # o aliases q
+    assert f(A + 2, B, C, MC, O, W, ws, None) == 1         # misaligned q
+    assert f(A, B, C, MC, O, None, ws, None) == 4          # no workspace
+    assert f(A, B, C, MC, O, W, ws - 1, None) == 4         # workspace too small
+    assert f(A, B, C, MC, O, W + 16, ws, None) == 4        # workspace misaligned
+    assert lib.mhla_forward(None, A, B, C, MC, O, W, ws, None) == 1
+    p.close()
+
+
+def test_status_strings():
+    _lib_or_skip()
+    for s in range(7):
+        assert T.mhla_status_string(s)
+    assert T.mhla_status_string(0) == "success"
+    assert T.mhla_status_string(99) == "unknown status"
+
+
+def test_timing_api_without_launches():
+    _lib_or_skip()
+    p = T.Plan(grid=(64,), block=(16,), batch=1, heads=1, head_dim=32)
+    T.mhla_timing_enable(p.handle, True)
+    name, ms, n = T.mhla_timing_read(p.handle, 0)
+    assert (name, ms, n) == ("summary", 0.0, 0)
+    assert T.mhla_timing_read(p.handle, 2)[0] == "readout"
+    with pytest.raises(T.MhlaError):
+        T.mhla_timing_read(p.handle, 3)
+    T.mhla_timing_reset(p.handle)
+    p.close()
+
+
+def test_fastdiv_exhaustive_on_host(tmp_path):
+    """The token -> grid-coordinate division is exact (checked with g++ on the host header)."""
+    src = tmp_path / "fd.cpp"
+    src.write_text(r'''
+#include "fastdiv.hpp"
+#include <cstdio>
+int main() {
+  const unsigned ds[] = {1,2,3,4,5,6,7,8,9,10,12,14,15,16,17,31,32,33,49,63,64,100,255,256,257,
+                         1000,1024,4095,4096,65535,65536,1000003,2147483647u};
+  for (unsigned d : ds) {
+    mhla::FastDiv f = mhla::make_fastdiv(d);
+    for (unsigned n = 0; n < 300000; ++n)
+      if (mhla::fdiv(n, f) != n / d) { printf("fail %u %u\n", n, d); return 1; }
+    for (unsigned n = 2147483647u; n > 2147483647u - 300000u; --n)
+      if (mhla::fdiv(n, f) != n / d) { printf("fail %u %u\n", n, d); return 1; }
+    for (unsigned n = 1; n < 2147483648u / 7; n = n * 7 + 3)
+      if (mhla::fdiv(n, f) != n / d) { printf("fail %u %u\n", n, d); return 1; }
+  }
+  for (unsigned d = 1; d < 3000; ++d) {
+    mhla::FastDiv f = mhla::make_fastdiv(d);
+    for (unsigned n = 0; n < 20000; ++n)
+      if (mhla::fdiv(n, f) != n / d) { printf("fail %u %u\n", n, d); return 1; }
+  }
+  printf("ok\n");
+  return 0;
+}
+''')
+    exe = tmp_path / "fd"
+    csrc = os.path.join(ROOT, "token_blocked_linear_amd", "csrc")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", csrc, str(src), "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)], capture_output=True, text=True).stdout.strip() == "ok"

@@ -1,0 +1,152 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bar: max|o_gpu - o_oracle| / RMS(o_oracle) <= 2e-2 for bf16 inputs and <= 1e-4 for the
+fp32 validation build, over every compared element.  Outputs are fp32 for these checks; a
+bf16 output additionally carries its own rounding (at most 2^-8 relative), which the bf16-
+output test allows for explicitly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import announce, oracle_full, rel_err, run_hip
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+FP32_TOL = 1e-4
+
+
+def _tol(w):
+    return FP32_TOL if w.dtype == "fp32" else BF16_TOL
+
+
+# ------------------------------------------------------------------------------------------
+# small and medium shapes: whole tensors, several tiles, ragged tails
+# ------------------------------------------------------------------------------------------
+
+SMALL = [
+    synth.WORKLOADS["tiny"],
+    synth.WORKLOADS["tiny"].with_(name="tiny_m1", block=(8, 8), mc_kind="none"),
+    synth.WORKLOADS["tiny"].with_(name="tiny_identity", mc_kind="identity"),
+    synth.WORKLOADS["tiny"].with_(name="tiny_unnorm", readout="unnormalized"),
+    synth.WORKLOADS["tiny"].with_(name="tiny_mala", block=(8, 8), mc_kind="none", readout="mala"),
+    synth.Workload("ragged1d", "bf16", 2, 3, 64, (1000,), (200,), 11, "softmax_l1"),
+    synth.Workload("odd2d_d32", "bf16", 2, 2, 32, (30, 42), (5, 7), 12, "softmax_l1"),
+    synth.Workload("odd3d_d128", "bf16", 1, 2, 128, (6, 10, 12), (3, 5, 4), 13, "softmax_l1"),
+    synth.Workload("d16_bf16", "bf16", 3, 2, 16, (20, 20), (10, 4), 14, "locality"),
+    synth.Workload("ones_mix", "bf16", 1, 2, 64, (48, 48), (16, 24), 15, "ones"),
+    synth.Workload("identity_mix", "bf16", 1, 2, 64, (48, 48), (16, 24), 16, "identity"),
+    synth.Workload("one_token_blocks", "bf16", 1, 1, 64, (40,), (1,), 17, "softmax_l1"),
+    synth.Workload("single_token", "bf16", 1, 1, 32, (1,), (1,), 18, "none"),
+    synth.Workload("m1_long_ragged", "bf16", 1, 3, 64, (3001,), (3001,), 19, "none"),
+    synth.Workload("unnorm_2d", "bf16", 2, 2, 64, (32, 32), (8, 8), 20, "softmax_l1", "unnormalized"),
+    synth.Workload("mala_ragged", "bf16", 2, 2, 64, (37, 45), (37, 45), 21, "none", "mala"),
+    synth.Workload("mala_d128", "bf16", 1, 2, 128, (2500,), (2500,), 22, "none", "mala"),
+    synth.Workload("fp32_2d", "fp32", 2, 2, 64, (24, 24), (8, 12), 23, "softmax_l1"),
+    synth.Workload("fp32_mala", "fp32", 1, 2, 32, (700,), (700,), 24, "none", "mala"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_parity_small(w):
+    announce(f"small {w.name} shape={w.qkv_shape} grid={w.grid} block={w.block} {w.readout}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc)
+    want = oracle_full(w, q, k, v, mc)
+    err = rel_err(got, want)
+    print(f"  err={err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= _tol(w), (w.name, err)
+
+
+def test_parity_per_head_mc():
+    w = synth.Workload("per_head_mc", "bf16", 2, 3, 64, (32, 32), (8, 16), 30, "none")
+    announce(w.name)
+    q, k, v, _, rng = synth.make_inputs(w)
+    mc = rng.uniform(0.0, 1.0, (w.heads, w.n_blocks, w.n_blocks)).astype(np.float32).astype(np.float64)
+    got = run_hip(w, q, k, v, mc)
+    want = np.stack([np.stack([oracle.mhla_blockwise(q[b, h], k[b, h], v[b, h], mc[h], w.grid, w.block)
+                               for h in range(w.heads)]) for b in range(w.batch)])
+    assert rel_err(got, want) <= BF16_TOL
+
+
+def test_split_accuracy_option_is_tighter():
+    w = synth.Workload("split_opt", "bf16", 2, 2, 64, (32, 32), (8, 8), 31, "softmax_l1")
+    announce(w.name)
+    q, k, v, mc, _ = synth.make_inputs(w)
+    want = oracle_full(w, q, k, v, mc)
+    e_fast = rel_err(run_hip(w, q, k, v, mc, accuracy="bf16"), want)
+    e_split = rel_err(run_hip(w, q, k, v, mc, accuracy="split"), want)
+    print(f"  bf16 operands {e_fast:.3e}  split operands {e_split:.3e}")
+    assert e_fast <= BF16_TOL and e_split <= 1e-3 and e_split < e_fast
+
+
+def test_bf16_output_within_bar_plus_output_rounding():
+    w = synth.WORKLOADS["deit_t"]
+    announce("bf16 output deit_t")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc, out_dtype="bf16")
+    want = oracle_full(w, q, k, v, mc)
+    rms = np.sqrt(np.mean(want ** 2))
+    excess = np.abs(got - want) - (BF16_TOL * rms + 2.0 ** -8 * np.abs(want))
+    assert excess.max() <= 0, excess.max()
+
+
+def test_deterministic():
+    w = synth.WORKLOADS["image"].with_(batch=2)
+    announce("determinism image b=2")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    a, b = run_hip(w, q, k, v, mc, repeat=2)
+    assert np.array_equal(a, b)
+    wm = synth.WORKLOADS["image_mala"].with_(batch=2)
+    q, k, v, mc, _ = synth.make_inputs(wm)
+    a, b = run_hip(wm, q, k, v, mc, repeat=2)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------
+# full-size workloads, as timed by the benchmark
+# ------------------------------------------------------------------------------------------
+
+FULL = ["deit_t", "image", "image_mala", "video3d"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size(name):
+    w = synth.WORKLOADS[name]
+    announce(f"full {name} shape={w.qkv_shape}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc)
+    want = oracle_full(w, q, k, v, mc)
+    err = rel_err(got, want)
+    print(f"  err={err:.3e}")
+    assert err <= BF16_TOL, (name, err)
+    # the plain token-level definition at sampled queries of a few heads
+    rng = np.random.default_rng(99)
+    samples = [(int(rng.integers(w.batch)), int(rng.integers(w.heads)),
+                sorted(rng.choice(w.n_tokens, 24, replace=False).tolist())) for _ in range(3)]
+    plain = oracle.forward_sampled(q, k, v, mc, w.grid, w.block, samples, mode=w.readout)
+    rms = np.sqrt(np.mean(want ** 2))
+    for (b, h, toks), ref in zip(samples, plain):
+        assert np.max(np.abs(got[b, h, toks] - ref)) / rms <= BF16_TOL
+
+
+def test_parity_long1d_full_size():
+    w = synth.WORKLOADS["long1d"]
+    announce(f"full long1d shape={w.qkv_shape}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc)
+    heads = [(0, 0), (0, 7), (0, 15)]
+    want = oracle.forward(q, k, v, mc, w.grid, w.block, heads=heads)
+    err = rel_err(np.stack([got[b, h] for b, h in heads]), want)
+    print(f"  err(3 heads)={err:.3e}")
+    assert err <= BF16_TOL
+    rms = np.sqrt(np.mean(want ** 2))
+    rng = np.random.default_rng(5)
+    samples = [(0, h, sorted(rng.choice(w.n_tokens, 16, replace=False).tolist())) for h in range(w.heads)]
+    plain = oracle.forward_sampled(q, k, v, mc, w.grid, w.block, samples)
+    for (b, h, toks), ref in zip(samples, plain):
+        assert np.max(np.abs(got[b, h, toks] - ref)) / rms <= BF16_TOL, h
+    assert np.all(np.isfinite(got))

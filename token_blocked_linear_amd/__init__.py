@@ -1,0 +1,265 @@
+"""Python binding of the gfx950 MHLA forward library (``libmhla.so``, C ABI in include/mhla.h).
+
+The functions carry the C names and only marshal arguments: every step of the forward runs
+in the library's HIP kernels.  torch is used for device memory and streams only.  If the
+library has not been built the import of this module still succeeds, but every call raises
+``MhlaLibraryMissing`` -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "MHLA_OK", "MHLA_DTYPE_BF16", "MHLA_DTYPE_FP32", "MHLA_PHI_ELU1",
+    "MHLA_READOUT_NORMALIZED", "MHLA_READOUT_UNNORMALIZED", "MHLA_READOUT_MALA",
+    "MHLA_ACCURACY_AUTO", "MHLA_ACCURACY_BF16", "MHLA_ACCURACY_SPLIT",
+    "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
+    "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
+    "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
+    "make_desc", "Plan", "EXPORTED_SYMBOLS",
+]
+
+MHLA_OK = 0
+MHLA_DTYPE_BF16, MHLA_DTYPE_FP32 = 0, 1
+MHLA_PHI_ELU1 = 0
+MHLA_READOUT_NORMALIZED, MHLA_READOUT_UNNORMALIZED, MHLA_READOUT_MALA = 0, 1, 2
+MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT = 0, 1, 2
+
+_READOUTS = {"normalized": MHLA_READOUT_NORMALIZED, "unnormalized": MHLA_READOUT_UNNORMALIZED,
+             "mala": MHLA_READOUT_MALA}
+_DTYPES = {"bf16": MHLA_DTYPE_BF16, "fp32": MHLA_DTYPE_FP32}
+_ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MHLA_ACCURACY_SPLIT}
+
+EXPORTED_SYMBOLS = (
+    "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
+    "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
+)
+
+
+class MhlaDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("phi", ctypes.c_int32),
+        ("readout", ctypes.c_int32),
+        ("accuracy", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("mc_per_head", ctypes.c_int32),
+        ("grid", ctypes.c_int64 * 3),
+        ("block", ctypes.c_int64 * 3),
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+    ]
+
+
+class MhlaPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("n_tokens", ctypes.c_int64),
+        ("n_blocks", ctypes.c_int64),
+        ("block_tokens", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+        ("summary_splits", ctypes.c_int32),
+        ("readout_splits", ctypes.c_int32),
+        ("n_kernels", ctypes.c_int32),
+        ("split_operands", ctypes.c_int32),
+    ]
+
+
+class MhlaLibraryMissing(RuntimeError):
+    pass
+
+
+class MhlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {mhla_status_string(status)} (status {status})")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmhla.so")
+
+
+def load_library() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise MhlaLibraryMissing(
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(there is no CPU fallback for the MHLA forward)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.mhla_create.argtypes = [ctypes.POINTER(MhlaDesc), ctypes.POINTER(P)]
+    lib.mhla_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.mhla_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
+    lib.mhla_destroy.argtypes = [P]
+    lib.mhla_status_string.argtypes = [I32]
+    lib.mhla_status_string.restype = ctypes.c_char_p
+    lib.mhla_plan_get_info.argtypes = [P, ctypes.POINTER(MhlaPlanInfo)]
+    lib.mhla_timing_enable.argtypes = [P, I32]
+    lib.mhla_timing_read.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
+                                     ctypes.POINTER(ctypes.c_char_p)]
+    lib.mhla_timing_reset.argtypes = [P]
+    for name in EXPORTED_SYMBOLS:
+        if name != "mhla_status_string":
+            getattr(lib, name).restype = I32
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != MHLA_OK:
+        raise MhlaError(status, what)
+
+
+# ------------------------------------------------------------------------------------------
+# C-named wrappers
+# ------------------------------------------------------------------------------------------
+
+def mhla_status_string(status: int) -> str:
+    return load_library().mhla_status_string(int(status)).decode()
+
+
+def mhla_create(desc: MhlaDesc) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load_library().mhla_create(ctypes.byref(desc), ctypes.byref(h)), "mhla_create")
+    return h
+
+
+def mhla_workspace_size(h) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mhla_workspace_size(h, ctypes.byref(n)), "mhla_workspace_size")
+    return n.value
+
+
+def mhla_forward(h, q: int, k: int, v: int, mc: int, o: int, workspace: int, workspace_bytes: int,
+                 stream: int) -> None:
+    """Pointers are integer device addresses (0 for NULL); ``stream`` a raw hipStream_t."""
+    _check(load_library().mhla_forward(h, q, k, v, mc or None, o, workspace or None,
+                                       workspace_bytes, stream or None), "mhla_forward")
+
+
+def mhla_destroy(h) -> None:
+    _check(load_library().mhla_destroy(h), "mhla_destroy")
+
+
+def mhla_plan_get_info(h) -> MhlaPlanInfo:
+    info = MhlaPlanInfo()
+    info.struct_size = ctypes.sizeof(MhlaPlanInfo)
+    _check(load_library().mhla_plan_get_info(h, ctypes.byref(info)), "mhla_plan_get_info")
+    return info
+
+
+def mhla_timing_enable(h, enable: bool) -> None:
+    _check(load_library().mhla_timing_enable(h, 1 if enable else 0), "mhla_timing_enable")
+
+
+def mhla_timing_read(h, index: int):
+    ms, n, name = ctypes.c_double(), ctypes.c_int64(), ctypes.c_char_p()
+    _check(load_library().mhla_timing_read(h, index, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(name)),
+           "mhla_timing_read")
+    return name.value.decode(), ms.value, n.value
+
+
+def mhla_timing_reset(h) -> None:
+    _check(load_library().mhla_timing_reset(h), "mhla_timing_reset")
+
+
+# ------------------------------------------------------------------------------------------
+# Convenience over torch tensors (marshalling only)
+# ------------------------------------------------------------------------------------------
+
+def make_desc(*, grid: Sequence[int], block: Sequence[int], batch: int, heads: int, head_dim: int,
+              in_dtype: str = "bf16", out_dtype: str = "fp32", readout: str = "normalized",
+              accuracy: str = "auto", mc_per_head: bool = False) -> MhlaDesc:
+    if len(grid) != len(block) or not 1 <= len(grid) <= 3:
+        raise ValueError("grid and block must have the same rank, 1 to 3")
+    d = MhlaDesc()
+    d.struct_size = ctypes.sizeof(MhlaDesc)
+    d.in_dtype = _DTYPES[in_dtype]
+    d.out_dtype = _DTYPES[out_dtype]
+    d.phi = MHLA_PHI_ELU1
+    d.readout = _READOUTS[readout]
+    d.accuracy = _ACCURACY[accuracy]
+    d.ndim = len(grid)
+    d.mc_per_head = 1 if mc_per_head else 0
+    for i, (g, b) in enumerate(zip(grid, block)):
+        d.grid[i] = int(g)
+        d.block[i] = int(b)
+    d.batch, d.heads, d.head_dim = int(batch), int(heads), int(head_dim)
+    return d
+
+
+class Plan:
+    """Owns one plan handle.  ``forward`` takes torch tensors already on the GPU."""
+
+    def __init__(self, **desc_kwargs):
+        self.desc_kwargs = dict(desc_kwargs)
+        self.desc = make_desc(**desc_kwargs)
+        self.handle = mhla_create(self.desc)
+        self.workspace_bytes = mhla_workspace_size(self.handle)
+        self.info = mhla_plan_get_info(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            mhla_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
+
+    def expected_shapes(self):
+        kw = self.desc_kwargs
+        n = 1
+        for g in kw["grid"]:
+            n *= int(g)
+        qkv = (int(kw["batch"]), int(kw["heads"]), n, int(kw["head_dim"]))
+        m = int(self.info.n_blocks)
+        mc = (int(kw["heads"]), m, m) if kw.get("mc_per_head") else (m, m)
+        return qkv, mc
+
+    def check_args(self, q, k, v, mc, o, workspace):
+        """Host-side checks that every buffer has the shape, dtype and layout the kernels
+        index; the C ABI receives bare pointers and cannot see them."""
+        import torch
+        qkv, mc_shape = self.expected_shapes()
+        tin = torch.bfloat16 if self.desc_kwargs.get("in_dtype", "bf16") == "bf16" else torch.float32
+        tout = torch.bfloat16 if self.desc_kwargs.get("out_dtype", "fp32") == "bf16" else torch.float32
+        for name, t, dt in (("q", q, tin), ("k", k, tin), ("v", v, tin), ("o", o, tout)):
+            if tuple(t.shape) != qkv or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name}: expected contiguous {dt} cuda tensor of shape {qkv}, "
+                                 f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+        if mc is None:
+            if self.info.n_blocks != 1:
+                raise ValueError("mc is required when there is more than one block")
+        elif (tuple(mc.shape) != mc_shape or mc.dtype != torch.float32 or not mc.is_contiguous()
+              or not mc.is_cuda):
+            raise ValueError(f"mc: expected contiguous float32 cuda tensor {mc_shape}")
+        if workspace.dtype != torch.uint8 or workspace.numel() < self.workspace_bytes or not workspace.is_cuda:
+            raise ValueError(f"workspace: expected >= {self.workspace_bytes} bytes of uint8 on the GPU")
+
+    def forward(self, q, k, v, mc, o, workspace, stream=None):
+        import torch
+        self.check_args(q, k, v, mc, o, workspace)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        mhla_forward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     mc.data_ptr() if mc is not None else 0, o.data_ptr(), workspace.data_ptr(),
+                     workspace.numel(), stream.cuda_stream)
+        return o

@@ -1,0 +1,174 @@
+// Device-side building blocks shared by the three gfx950 kernels of the MHLA forward:
+// launch parameter structs, the block geometry, fast integer division, bf16 packing,
+// the feature map and the 16x16x32 bf16 MFMA wrapper.
+//
+// Summary-stack fragment layout (written by the summary kernel, consumed by mix and readout).
+// For head_dim D let NKC = max(D,32)/32 (32-feature chunks of the key dimension k) and
+// NCT = D/16 (16-channel tiles of the value dimension c).  Element (kc, ct, lane, e) of a
+// d x d summary S holds
+//     S[k = 32*kc + 8*(lane/16) + e][c = 16*ct + lane%16],     e = 0..7,
+// at flat index ((kc*NCT + ct)*64 + lane)*8 + e.  One (kc, ct) fragment is therefore exactly
+// the per-lane A operand of a v_mfma_f32_16x16x32_bf16 whose rows are the 16 channels c and
+// whose contraction runs over the 32 key features k, so the readout loads it with one
+// 16-byte read per lane.  Rows k >= D (only when D = 16) are zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fastdiv.hpp"
+
+namespace mhla {
+
+constexpr int kThreads = 256;  // every kernel runs 4 wave64s per workgroup
+
+template <int D> struct Dims {
+  static constexpr int DK = D < 32 ? 32 : D;   // key dimension padded to the MFMA K=32 chunk
+  static constexpr int NKC = DK / 32;
+  static constexpr int NCT = D / 16;
+  static constexpr int FRAG = NKC * NCT * 512; // elements of one fragment-layout summary
+};
+
+// Token-grid geometry, padded to 3 axes with leading extents of 1.
+struct Geom {
+  int32_t G1, G2;          // grid extents of axes 1 and 2 (axis 0 is implied)
+  int32_t B0, B1, B2;      // block extents
+  int32_t NB1, NB2;        // block-grid extents of axes 1 and 2
+  FastDiv fB2, fB1;        // divide block-local token indices
+  int32_t n_b;             // tokens per block
+  int32_t N;               // tokens per head
+  int32_t M;               // blocks per head
+};
+
+// First token (raster index) of block b.
+__device__ inline int32_t block_base_token(const Geom& g, int32_t b) {
+  int32_t b2 = b % g.NB2;
+  int32_t t = b / g.NB2;
+  int32_t b1 = t % g.NB1;
+  int32_t b0 = t / g.NB1;
+  return ((b0 * g.B0) * g.G1 + b1 * g.B1) * g.G2 + b2 * g.B2;
+}
+
+// Raster token index of block-local token j (0 <= j < n_b) relative to the block's base.
+__device__ inline int32_t block_token_offset(const Geom& g, uint32_t j) {
+  uint32_t q2 = fdiv(j, g.fB2);
+  uint32_t j2 = j - q2 * (uint32_t)g.B2;
+  uint32_t j0 = fdiv(q2, g.fB1);
+  uint32_t j1 = q2 - j0 * (uint32_t)g.B1;
+  return (int32_t)((j0 * (uint32_t)g.G1 + j1) * (uint32_t)g.G2 + j2);
+}
+
+// ---------------------------------------------------------------------------------------
+// Launch parameters
+// ---------------------------------------------------------------------------------------
+struct SummaryParams {
+  const void* k;           // [BH][N][D] of the input dtype
+  const void* v;
+  float* ps;               // partial summaries  [BH][M][splits][FRAG]   (fp32)
+  float* pz;               // partial normaliser [BH][M][splits][D]      (fp32)
+  float* pu;               // partial sum of V   [BH][M][splits][D]      (fp32, MALA only)
+  Geom g;
+  int32_t splits;          // token slices per block
+  int32_t tok_per_split;
+};
+
+struct MixParams {
+  const float* ps;
+  const float* pz;
+  const float* pu;
+  const float* mc;         // fp32 [M][M] or [H][M][M]
+  int64_t mc_head_stride;  // 0 or M*M
+  uint16_t* st_hi;         // mixed summaries, bf16 bits [BH][M][FRAG]
+  uint16_t* st_lo;         // low parts (split accuracy) or nullptr
+  float* zt;               // mixed normaliser [BH][M][D]; MALA: z
+  float* ubar;             // MALA: mean of V [BH][D]
+  int32_t M;
+  int32_t splits;
+  int32_t H;
+  int32_t N;
+};
+
+struct ReadoutParams {
+  const void* q;           // [BH][N][D] of the input dtype
+  void* o;                 // [BH][N][D] of the output dtype
+  const uint16_t* st_hi;
+  const uint16_t* st_lo;
+  const float* zt;
+  const float* ubar;
+  Geom g;
+  int32_t splits;          // token slices per query block
+  int32_t tok_per_split;
+};
+
+// ---------------------------------------------------------------------------------------
+// Numerics helpers
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest even (gfx950 converts natively); returns the 16-bit pattern.
+__device__ inline uint32_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// hi = bf16(x), lo = bf16(x - hi): x == hi + lo to about 2^-17 relative.
+__device__ inline void split_bf16(float x, uint32_t& hi_bits, uint32_t& lo_bits) {
+  hi_bits = f32_to_bf16_bits(x);
+  lo_bits = f32_to_bf16_bits(x - __uint_as_float(hi_bits << 16));
+}
+
+// ELU(x) + 1 with alpha = 1.
+__device__ inline float phi_elu1(float x) {
+  return x > 0.0f ? x + 1.0f : __expf(x);
+}
+
+__device__ inline f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16-byte global loads and stores.
+__device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ inline void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+// Input element loaders: 8 consecutive elements starting at element index `idx` as fp32.
+template <typename T> struct In8;
+template <> struct In8<uint16_t> {       // bf16 bits
+  u32x4_t w;
+  __device__ inline void load(const void* base, int64_t idx) {
+    w = ld16(reinterpret_cast<const uint16_t*>(base) + idx);
+  }
+  __device__ inline void zero() { w = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ inline float get(int e) const {
+    uint32_t x = w[e >> 1];
+    return (e & 1) ? bf16hi_to_f32(x) : bf16lo_to_f32(x);
+  }
+  __device__ inline uint32_t bits(int e) const {   // exact bf16 bits (no rounding needed)
+    uint32_t x = w[e >> 1];
+    return (e & 1) ? (x >> 16) : (x & 0xffffu);
+  }
+};
+template <> struct In8<float> {
+  u32x4_t w0, w1;
+  __device__ inline void load(const void* base, int64_t idx) {
+    const float* p = reinterpret_cast<const float*>(base) + idx;
+    w0 = ld16(p);
+    w1 = ld16(p + 4);
+  }
+  __device__ inline void zero() {
+    w0 = u32x4_t{0u, 0u, 0u, 0u};
+    w1 = w0;
+  }
+  __device__ inline float get(int e) const { return __uint_as_float(e < 4 ? w0[e] : w1[e - 4]); }
+};
+
+}  // namespace mhla

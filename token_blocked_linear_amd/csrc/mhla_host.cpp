@@ -1,0 +1,359 @@
+// Host side of the C ABI declared in include/mhla.h: descriptor validation, the plan
+// (geometry, kernel variants, token slicing, workspace layout), launches of the summary,
+// mixing and readout kernels on the caller's stream, and optional per-kernel HIP events.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "mhla.h"
+#include "mhla_device.hpp"
+
+namespace mhla {
+hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
+                          bool want_u, dim3 grid, hipStream_t stream);
+hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool mala, bool split,
+                      hipStream_t stream);
+hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
+                          bool split, dim3 grid, hipStream_t stream);
+}  // namespace mhla
+
+namespace {
+
+constexpr int kNumKernels = 3;
+const char* const kKernelNames[kNumKernels] = {"summary", "mix", "readout"};
+
+struct TimedLaunch {
+  hipEvent_t ev[kNumKernels + 1];
+};
+
+}  // namespace
+
+struct mhla_plan {
+  mhla_desc desc;
+  int d;
+  int64_t B, H, BH, N, M, n_b;
+  mhla::Geom geom;
+  bool in_fp32, out_fp32, mala, split, split_v;
+  int mode;
+  int frag;
+  int32_t sum_splits, sum_tok;
+  int32_t rd_splits, rd_tok;
+  // workspace layout (byte offsets)
+  size_t off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_ubar, ws_bytes;
+  // timing
+  bool timing;
+  std::vector<TimedLaunch> timed;
+  size_t timed_used;
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
+  if (d->struct_size != sizeof(mhla_desc)) return MHLA_ERR_INVALID_ARG;
+  if (d->in_dtype != MHLA_DTYPE_BF16 && d->in_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
+  if (d->out_dtype != MHLA_DTYPE_BF16 && d->out_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
+  if (d->phi != MHLA_PHI_ELU1) return MHLA_ERR_UNSUPPORTED;
+  if (d->readout < MHLA_READOUT_NORMALIZED || d->readout > MHLA_READOUT_MALA) return MHLA_ERR_UNSUPPORTED;
+  if (d->accuracy < MHLA_ACCURACY_AUTO || d->accuracy > MHLA_ACCURACY_SPLIT) return MHLA_ERR_UNSUPPORTED;
+  if (d->mc_per_head != 0 && d->mc_per_head != 1) return MHLA_ERR_INVALID_ARG;
+  if (!(d->head_dim == 16 || d->head_dim == 32 || d->head_dim == 64 || d->head_dim == 128))
+    return MHLA_ERR_UNSUPPORTED;
+  if (d->ndim < 1 || d->ndim > 3) return MHLA_ERR_SHAPE;
+  if (d->batch < 1 || d->heads < 1) return MHLA_ERR_SHAPE;
+
+  int64_t grid[3] = {1, 1, 1}, block[3] = {1, 1, 1};
+  const int pad = 3 - d->ndim;
+  for (int a = 0; a < d->ndim; ++a) {
+    if (d->grid[a] < 1 || d->block[a] < 1) return MHLA_ERR_SHAPE;
+    if (d->grid[a] % d->block[a] != 0) return MHLA_ERR_SHAPE;
+    if (d->grid[a] > (int64_t)1 << 31) return MHLA_ERR_SHAPE;
+    grid[pad + a] = d->grid[a];
+    block[pad + a] = d->block[a];
+  }
+  const int64_t N = grid[0] * grid[1] * grid[2];
+  const int64_t nb = block[0] * block[1] * block[2];
+  if (N >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
+  const int64_t M = N / nb;
+  const int64_t BH = d->batch * d->heads;
+  if (BH > 65535 || M > 65535) return MHLA_ERR_SHAPE;
+  if (d->readout == MHLA_READOUT_MALA && M != 1) return MHLA_ERR_UNSUPPORTED;
+  // element offsets are 64-bit; guard the total size against overflow
+  if (BH > ((int64_t)1 << 62) / (N * d->head_dim * 4)) return MHLA_ERR_SHAPE;
+
+  P->desc = *d;
+  P->d = (int)d->head_dim;
+  P->B = d->batch;
+  P->H = d->heads;
+  P->BH = BH;
+  P->N = N;
+  P->M = M;
+  P->n_b = nb;
+  mhla::Geom& g = P->geom;
+  g.G1 = (int32_t)grid[1];
+  g.G2 = (int32_t)grid[2];
+  g.B0 = (int32_t)block[0];
+  g.B1 = (int32_t)block[1];
+  g.B2 = (int32_t)block[2];
+  g.NB1 = (int32_t)(grid[1] / block[1]);
+  g.NB2 = (int32_t)(grid[2] / block[2]);
+  g.fB2 = mhla::make_fastdiv((uint32_t)block[2]);
+  g.fB1 = mhla::make_fastdiv((uint32_t)block[1]);
+  g.n_b = (int32_t)nb;
+  g.N = (int32_t)N;
+  g.M = (int32_t)M;
+
+  P->in_fp32 = d->in_dtype == MHLA_DTYPE_FP32;
+  P->out_fp32 = d->out_dtype == MHLA_DTYPE_FP32;
+  P->mala = d->readout == MHLA_READOUT_MALA;
+  P->mode = d->readout;
+  if (d->accuracy == MHLA_ACCURACY_SPLIT)
+    P->split = true;
+  else if (d->accuracy == MHLA_ACCURACY_BF16)
+    P->split = false;
+  else
+    P->split = P->mala || P->in_fp32;
+  P->split_v = P->split && P->in_fp32;
+
+  const int dk = P->d < 32 ? 32 : P->d;
+  P->frag = (dk / 32) * (P->d / 16) * 512;
+
+  // Token slicing: enough workgroups to fill 256 CUs several times over, slices >= 256 tokens.
+  {
+    const int64_t units = BH * M;
+    int64_t s = 1;
+    if (units < 1024) {
+      s = (1024 + units - 1) / units;
+      const int64_t max_s = (nb + 255) / 256;
+      if (s > max_s) s = max_s;
+      if (s < 1) s = 1;
+    }
+    int64_t tok = (nb + s - 1) / s;
+    tok = (tok + 31) / 32 * 32;
+    s = (nb + tok - 1) / tok;
+    P->sum_splits = (int32_t)s;
+    P->sum_tok = (int32_t)tok;
+  }
+  {
+    int64_t s = (nb + 255) / 256;
+    int64_t tok = (nb + s - 1) / s;
+    tok = (tok + 15) / 16 * 16;
+    s = (nb + tok - 1) / tok;
+    P->rd_splits = (int32_t)s;
+    P->rd_tok = (int32_t)tok;
+  }
+
+  // Workspace layout.
+  const size_t f = (size_t)P->frag, dd = (size_t)P->d;
+  const size_t slots = (size_t)BH * M * P->sum_splits;
+  size_t off = 0;
+  P->off_ps = off;   off = align256(off + slots * f * 4);
+  P->off_pz = off;   off = align256(off + slots * dd * 4);
+  P->off_pu = off;   off = align256(off + (P->mala ? slots * dd * 4 : 0));
+  P->off_st_hi = off; off = align256(off + (size_t)BH * M * f * 2);
+  P->off_st_lo = off; off = align256(off + (P->split ? (size_t)BH * M * f * 2 : 0));
+  P->off_zt = off;   off = align256(off + (size_t)BH * M * dd * 4);
+  P->off_ubar = off; off = align256(off + (P->mala ? (size_t)BH * dd * 4 : 0));
+  P->ws_bytes = off;
+
+  P->timing = false;
+  P->timed_used = 0;
+  return MHLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mhla_status mhla_create(const mhla_desc* desc, mhla_handle* out) {
+  if (!desc || !out) return MHLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  try {
+    mhla_plan* P = new (std::nothrow) mhla_plan();
+    if (!P) return MHLA_ERR_INTERNAL;
+    const mhla_status s = build_plan(desc, P);
+    if (s != MHLA_OK) {
+      delete P;
+      return s;
+    }
+    if (std::getenv("MHLA_LOG"))
+      std::fprintf(stderr,
+                   "mhla: N=%lld M=%lld n_b=%lld d=%d split=%d summary_splits=%d readout_splits=%d "
+                   "workspace=%zu\n",
+                   (long long)P->N, (long long)P->M, (long long)P->n_b, P->d, (int)P->split,
+                   P->sum_splits, P->rd_splits, P->ws_bytes);
+    *out = P;
+    return MHLA_OK;
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
+
+mhla_status mhla_workspace_size(mhla_handle h, size_t* bytes) {
+  if (!h || !bytes) return MHLA_ERR_INVALID_ARG;
+  *bytes = h->ws_bytes;
+  return MHLA_OK;
+}
+
+mhla_status mhla_plan_get_info(mhla_handle h, mhla_plan_info* info) {
+  if (!h || !info || info->struct_size != sizeof(mhla_plan_info)) return MHLA_ERR_INVALID_ARG;
+  info->n_tokens = h->N;
+  info->n_blocks = h->M;
+  info->block_tokens = h->n_b;
+  info->workspace_bytes = (int64_t)h->ws_bytes;
+  info->summary_splits = h->sum_splits;
+  info->readout_splits = h->rd_splits;
+  info->n_kernels = kNumKernels;
+  info->split_operands = h->split ? 1 : 0;
+  return MHLA_OK;
+}
+
+mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void* v,
+                         const float* mc, void* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!h || !q || !k || !v || !o) return MHLA_ERR_INVALID_ARG;
+  if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return MHLA_ERR_INVALID_ARG;
+  if (mc && !aligned(mc, 4)) return MHLA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v || (workspace && o == workspace)) return MHLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < h->ws_bytes) return MHLA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
+  try {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* ps = reinterpret_cast<float*>(ws + h->off_ps);
+    float* pz = reinterpret_cast<float*>(ws + h->off_pz);
+    float* pu = h->mala ? reinterpret_cast<float*>(ws + h->off_pu) : nullptr;
+    uint16_t* st_hi = reinterpret_cast<uint16_t*>(ws + h->off_st_hi);
+    uint16_t* st_lo = h->split ? reinterpret_cast<uint16_t*>(ws + h->off_st_lo) : nullptr;
+    float* zt = reinterpret_cast<float*>(ws + h->off_zt);
+    float* ubar = h->mala ? reinterpret_cast<float*>(ws + h->off_ubar) : nullptr;
+
+    TimedLaunch* tl = nullptr;
+    if (h->timing) {
+      if (h->timed_used == h->timed.size()) {
+        TimedLaunch t;
+        for (int i = 0; i <= kNumKernels; ++i)
+          if (hipEventCreate(&t.ev[i]) != hipSuccess) return MHLA_ERR_HIP;
+        h->timed.push_back(t);
+      }
+      tl = &h->timed[h->timed_used++];
+      if (hipEventRecord(tl->ev[0], s) != hipSuccess) return MHLA_ERR_HIP;
+    }
+
+    mhla::SummaryParams sp;
+    sp.k = k;
+    sp.v = v;
+    sp.ps = ps;
+    sp.pz = pz;
+    sp.pu = pu;
+    sp.g = h->geom;
+    sp.splits = h->sum_splits;
+    sp.tok_per_split = h->sum_tok;
+    hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
+                                        dim3(h->sum_splits, (unsigned)h->M, (unsigned)h->BH), s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+    if (tl && hipEventRecord(tl->ev[1], s) != hipSuccess) return MHLA_ERR_HIP;
+
+    mhla::MixParams mp;
+    mp.ps = ps;
+    mp.pz = pz;
+    mp.pu = pu;
+    mp.mc = mc;
+    mp.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+    mp.st_hi = st_hi;
+    mp.st_lo = st_lo;
+    mp.zt = zt;
+    mp.ubar = ubar;
+    mp.M = (int32_t)h->M;
+    mp.splits = h->sum_splits;
+    mp.H = (int32_t)h->H;
+    mp.N = (int32_t)h->N;
+    // mc == NULL is only accepted for M == 1; the mixing kernel then uses the weight 1.
+    e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->mala, h->split, s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+    if (tl && hipEventRecord(tl->ev[2], s) != hipSuccess) return MHLA_ERR_HIP;
+
+    mhla::ReadoutParams rp;
+    rp.q = q;
+    rp.o = o;
+    rp.st_hi = st_hi;
+    rp.st_lo = st_lo;
+    rp.zt = zt;
+    rp.ubar = ubar;
+    rp.g = h->geom;
+    rp.splits = h->rd_splits;
+    rp.tok_per_split = h->rd_tok;
+    e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split,
+                             dim3(h->rd_splits, (unsigned)h->M, (unsigned)h->BH), s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+    if (tl && hipEventRecord(tl->ev[3], s) != hipSuccess) return MHLA_ERR_HIP;
+    return MHLA_OK;
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
+
+mhla_status mhla_destroy(mhla_handle h) {
+  if (!h) return MHLA_OK;
+  for (auto& t : h->timed)
+    for (int i = 0; i <= kNumKernels; ++i) (void)hipEventDestroy(t.ev[i]);
+  delete h;
+  return MHLA_OK;
+}
+
+const char* mhla_status_string(mhla_status s) {
+  switch (s) {
+    case MHLA_OK: return "success";
+    case MHLA_ERR_INVALID_ARG: return "invalid argument";
+    case MHLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MHLA_ERR_SHAPE: return "inconsistent or unsupported shape";
+    case MHLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MHLA_ERR_HIP: return "HIP runtime or launch failure";
+    case MHLA_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+mhla_status mhla_timing_enable(mhla_handle h, int enable) {
+  if (!h) return MHLA_ERR_INVALID_ARG;
+  h->timing = enable != 0;
+  return MHLA_OK;
+}
+
+mhla_status mhla_timing_read(mhla_handle h, int index, double* total_ms, int64_t* launches,
+                             const char** name) {
+  if (!h || index < 0 || index >= kNumKernels) return MHLA_ERR_INVALID_ARG;
+  if (name) *name = kKernelNames[index];
+  double sum = 0.0;
+  if (h->timed_used > 0) {
+    if (hipEventSynchronize(h->timed[h->timed_used - 1].ev[kNumKernels]) != hipSuccess)
+      return MHLA_ERR_HIP;
+    for (size_t i = 0; i < h->timed_used; ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, h->timed[i].ev[index], h->timed[i].ev[index + 1]) != hipSuccess)
+        return MHLA_ERR_HIP;
+      sum += ms;
+    }
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int64_t)h->timed_used;
+  return MHLA_OK;
+}
+
+mhla_status mhla_timing_reset(mhla_handle h) {
+  if (!h) return MHLA_ERR_INVALID_ARG;
+  h->timed_used = 0;
+  return MHLA_OK;
+}
+
+}  // extern "C"
