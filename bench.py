@@ -1,0 +1,212 @@
+"""Benchmark of the MHLA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long1d] [--all]
+
+A step is one full forward (summary -> mixing -> readout) over one batch of seeded synthetic
+input already resident in HBM.  W untimed steps, then exactly K steps between
+torch.cuda.synchronize() calls; `value` is tokens/s = steps * B * N / elapsed.  Per-kernel
+durations come from HIP events the library records around each of its kernels on the launch
+stream during the same timed loop; the dominant kernel's algorithmic bytes (or FLOPs) per
+launch divided by its mean duration gives `roofline.achieved`.  The fp64 CPU oracle is timed
+on a bounded sample of the same workload (`cpu_baseline`).  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+FP32_VALU_PEAK_TFLOPS = 157.3
+RANGE_WORKLOADS = ["image", "image_mala", "video3d", "long1d"]   # the N = 4096 .. 65536 configs
+
+
+def kernel_accounting(w: synth.Workload, out_bytes: int):
+    """Algorithmic bytes and FLOPs per launch of each kernel (summaries are not algorithmic)."""
+    BH, N, d, M = w.batch * w.heads, w.n_tokens, w.head_dim, w.n_blocks
+    in_b = 2 if w.dtype == "bf16" else 4
+    tok = BH * N
+    acc = {
+        "summary": dict(bytes=tok * 2 * d * in_b, flops=tok * (2 * d * d + d), bound="hbm"),
+        "readout": dict(bytes=tok * d * (in_b + out_bytes), flops=tok * (2 * d * d + 2 * d), bound="hbm"),
+    }
+    if w.readout == "mala":
+        acc["mix"] = dict(bytes=0, flops=BH * 2 * d * d, bound="alu")
+    else:
+        acc["mix"] = dict(bytes=M * M * 4, flops=BH * 2 * M * M * (d * d + d), bound="alu")
+    total_bytes = tok * d * (3 * in_b + out_bytes) + (0 if w.readout == "mala" else M * M * 4)
+    total_flops = sum(a["flops"] for a in acc.values())
+    return acc, total_bytes, total_flops
+
+
+def to_dev(x, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0")
+
+
+def run_workload(name: str, steps: int, warmup: int, out_dtype: str):
+    import torch
+    import token_blocked_linear_amd as T
+
+    w = synth.WORKLOADS[name]
+    q, k, v, mc, _ = synth.make_inputs(w)
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout)
+    tq, tk, tv = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)
+    tmc = None if mc is None else torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    o = torch.empty(w.qkv_shape, dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32,
+                    device="cuda:0")
+    ws = plan.alloc_workspace()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.forward(tq, tk, tv, tmc, o, ws, stream)
+    torch.cuda.synchronize()
+    T.mhla_timing_reset(plan.handle)
+    T.mhla_timing_enable(plan.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.forward(tq, tk, tv, tmc, o, ws, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    T.mhla_timing_enable(plan.handle, False)
+    kernels = {}
+    for i in range(plan.info.n_kernels):
+        kname, ms, n = T.mhla_timing_read(plan.handle, i)
+        kernels[kname] = ms / max(n, 1) * 1e-3          # mean seconds per launch
+    ob = 2 if out_dtype == "bf16" else 4
+    acc, total_bytes, total_flops = kernel_accounting(w, ob)
+    per_kernel = {}
+    for kname, t in kernels.items():
+        a = acc[kname]
+        gbs = a["bytes"] / t / 1e9
+        tfl = a["flops"] / t / 1e12
+        if a["bound"] == "hbm":
+            frac = gbs / HBM_PEAK_GBS
+        else:
+            frac = tfl / FP32_VALU_PEAK_TFLOPS
+        per_kernel[kname] = dict(us=round(t * 1e6, 2), alg_GBps=round(gbs, 1), TFLOPs=round(tfl, 2),
+                                 bound=a["bound"], frac=round(frac, 4))
+    step_s = elapsed / steps
+    res = dict(
+        workload=w, plan=plan, elapsed=elapsed, step_s=step_s,
+        tokens_per_s=w.batch * w.n_tokens / step_s,
+        e2e_hbm_frac=total_bytes / step_s / (HBM_PEAK_GBS * 1e9),
+        e2e_tflops=total_flops / step_s / 1e12,
+        kernels=kernels, per_kernel=per_kernel, acc=acc, inputs=(q, k, v, mc),
+    )
+    del tq, tk, tv, tmc, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(res, budget_s: float = 12.0):
+    """The fp64 oracle (as it stands) on a bounded sample: whole (batch, head) pairs, cycled
+    until the time budget is used."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    w = res["workload"]
+    q, k, v, mc = res["inputs"]
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        p = pairs[done % len(pairs)]
+        oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout, heads=[p])
+        done += 1
+    t = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    # one (batch, head) pair is 1/H of the work of N tokens in the metric's unit (B*N tokens,
+    # every token carrying all H heads)
+    return {"value": round(done * w.n_tokens / w.heads / t, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} whole (batch, head) pairs of {w.name} ({w.n_tokens} tokens each) in "
+                      f"{t:.1f} s, counted as {done}/{w.heads} of the heads of {w.n_tokens} tokens"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long1d", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="also time the other N=4096..65536 workloads")
+    ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    res = run_workload(args.workload, args.steps, args.warmup, args.out_dtype)
+    w = res["workload"]
+    dom = max(res["kernels"], key=lambda k: res["kernels"][k])
+    pk = res["per_kernel"][dom]
+    a = res["acc"][dom]
+    if pk["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": pk["alg_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": pk["frac"], "traffic": None, "kernel": dom,
+                "alg_bytes_per_launch": a["bytes"], "mean_launch_us": pk["us"]}
+    else:
+        roof = {"bound": "alu", "achieved": pk["TFLOPs"], "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": pk["frac"], "traffic": None, "kernel": dom,
+                "alg_flops_per_launch": a["flops"], "mean_launch_us": pk["us"]}
+
+    others = {}
+    if args.all:
+        for name in RANGE_WORKLOADS:
+            if name == args.workload:
+                continue
+            r = run_workload(name, args.steps, args.warmup, args.out_dtype)
+            others[name] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms": round(r["step_s"] * 1e3, 4),
+                            "e2e_hbm_frac": round(r["e2e_hbm_frac"], 4), "kernels": r["per_kernel"]}
+            del r
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(res)
+    line = {
+        "metric": "MHLA fwd tokens/sec + % of bf16 MFMA/HBM roofline at N=4096..65536",
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V rounded to bf16; M_c from the workload's generator)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "grid": list(w.grid), "block": list(w.block), "n_blocks": w.n_blocks,
+                   "tokens_per_step": w.batch * w.n_tokens, "readout": w.readout,
+                   "in_dtype": w.dtype, "out_dtype": args.out_dtype, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "end_to_end": {"alg_hbm_frac": round(res["e2e_hbm_frac"], 4), "TFLOPs": round(res["e2e_tflops"], 2)},
+        "kernels": res["per_kernel"],
+        "cpu_baseline": cpu,
+    }
+    if others:
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
