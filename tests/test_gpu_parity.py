@@ -46,6 +46,10 @@ SMALL = [
     synth.Workload("mala_d128", "bf16", 1, 2, 128, (2500,), (2500,), 22, "none", "mala"),
     synth.Workload("fp32_2d", "fp32", 2, 2, 64, (24, 24), (8, 12), 23, "softmax_l1"),
     synth.Workload("fp32_mala", "fp32", 1, 2, 32, (700,), (700,), 24, "none", "mala"),
+    # mixing-kernel variants: M in (64, 128], M in (128, 256) not a multiple of 32, M = 256 2D
+    synth.Workload("m100", "bf16", 1, 2, 64, (1000,), (10,), 25, "softmax_l1"),
+    synth.Workload("m200_d128", "bf16", 1, 2, 128, (3200,), (16,), 26, "softmax_gauss"),
+    synth.Workload("m144_2d", "bf16", 2, 1, 32, (48, 48), (4, 4), 27, "locality"),
 ]
 
 

@@ -64,6 +64,7 @@ __device__ inline int32_t block_token_offset(const Geom& g, uint32_t j) {
 struct SummaryParams {
   const void* k;           // [BH][N][D] of the input dtype
   const void* v;
+  uint16_t* sb;            // bf16 summaries [BH][M][FRAG] (one token slice, bf16 operands)
   float* ps;               // partial summaries  [BH][M][splits][FRAG]   (fp32)
   float* pz;               // partial normaliser [BH][M][splits][D]      (fp32)
   float* pu;               // partial sum of V   [BH][M][splits][D]      (fp32, MALA only)
@@ -86,6 +87,23 @@ struct MixParams {
   int32_t splits;
   int32_t H;
   int32_t N;
+};
+
+// MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,
+// plus the fp32 normaliser mixing z~[i] = sum_b M_c[i][b] z[b].
+struct MixMfmaParams {
+  const uint16_t* x;       // bf16 [BH][M][FRAG]
+  const float* z;          // fp32 [BH][M][D]
+  const float* mc;         // fp32 [M][M] or [H][M][M]
+  int64_t mc_head_stride;
+  uint16_t* y;             // bf16 [BH][M][FRAG]
+  float* zt;               // fp32 [BH][M][D]
+  int32_t M;
+  int32_t H;
+  int32_t D;
+  int32_t frag;
+  int32_t n_wg_x;          // workgroups per (head, row group) striding over column tiles
+  int32_t wave_rows;       // waves sharing the i-tiles of a row group (1, 2 or 4)
 };
 
 struct ReadoutParams {

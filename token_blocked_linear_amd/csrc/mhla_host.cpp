@@ -15,9 +15,10 @@
 
 namespace mhla {
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
-                          bool want_u, dim3 grid, hipStream_t stream);
+                          bool want_u, bool out_bf16, dim3 grid, hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool mala, bool split,
                       hipStream_t stream);
+hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
                           bool split, dim3 grid, hipStream_t stream);
 }  // namespace mhla
@@ -39,12 +40,13 @@ struct mhla_plan {
   int64_t B, H, BH, N, M, n_b;
   mhla::Geom geom;
   bool in_fp32, out_fp32, mala, split, split_v;
+  bool mix_mfma;   // bf16 summary stack mixed on MFMA (else fp32 partials mixed on VALU)
   int mode;
   int frag;
   int32_t sum_splits, sum_tok;
   int32_t rd_splits, rd_tok;
   // workspace layout (byte offsets)
-  size_t off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_ubar, ws_bytes;
+  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_ubar, ws_bytes;
   // timing
   bool timing;
   std::vector<TimedLaunch> timed;
@@ -151,11 +153,16 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
     P->rd_tok = (int32_t)tok;
   }
 
+  // Mixing path: a bf16 stack on MFMA when the summaries come from one token slice with bf16
+  // operands (the bf16 accuracy level); otherwise fp32 partials reduced and mixed on VALU.
+  P->mix_mfma = !P->split && !P->mala && !P->in_fp32 && P->sum_splits == 1 && M <= 256;
+
   // Workspace layout.
   const size_t f = (size_t)P->frag, dd = (size_t)P->d;
   const size_t slots = (size_t)BH * M * P->sum_splits;
   size_t off = 0;
-  P->off_ps = off;   off = align256(off + slots * f * 4);
+  P->off_sb = off;   off = align256(off + (P->mix_mfma ? (size_t)BH * M * f * 2 : 0));
+  P->off_ps = off;   off = align256(off + (P->mix_mfma ? 0 : slots * f * 4));
   P->off_pz = off;   off = align256(off + slots * dd * 4);
   P->off_pu = off;   off = align256(off + (P->mala ? slots * dd * 4 : 0));
   P->off_st_hi = off; off = align256(off + (size_t)BH * M * f * 2);
@@ -259,11 +266,29 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.g = h->geom;
     sp.splits = h->sum_splits;
     sp.tok_per_split = h->sum_tok;
+    sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
     hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
+                                        h->mix_mfma,
                                         dim3(h->sum_splits, (unsigned)h->M, (unsigned)h->BH), s);
     if (e != hipSuccess) return MHLA_ERR_HIP;
     if (tl && hipEventRecord(tl->ev[1], s) != hipSuccess) return MHLA_ERR_HIP;
 
+    if (h->mix_mfma) {
+      mhla::MixMfmaParams mm;
+      mm.x = reinterpret_cast<const uint16_t*>(ws + h->off_sb);
+      mm.z = pz;
+      mm.mc = mc;
+      mm.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+      mm.y = st_hi;
+      mm.zt = zt;
+      mm.M = (int32_t)h->M;
+      mm.H = (int32_t)h->H;
+      mm.D = h->d;
+      mm.frag = h->frag;
+      mm.n_wg_x = 0;
+      mm.wave_rows = 0;
+      e = mhla::launch_mix_mfma(mm, (int)h->BH, s);
+    }
     mhla::MixParams mp;
     mp.ps = ps;
     mp.pz = pz;
@@ -279,7 +304,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     mp.H = (int32_t)h->H;
     mp.N = (int32_t)h->N;
     // mc == NULL is only accepted for M == 1; the mixing kernel then uses the weight 1.
-    e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->mala, h->split, s);
+    if (!h->mix_mfma) e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->mala, h->split, s);
     if (e != hipSuccess) return MHLA_ERR_HIP;
     if (tl && hipEventRecord(tl->ev[2], s) != hipSuccess) return MHLA_ERR_HIP;
 

@@ -1,0 +1,205 @@
+// MFMA mixing kernel: S~_i = sum_b m_ib S_b over a bf16 summary stack, and the fp32
+// normaliser mixing z~_i = sum_b m_ib z_b ("MHLA: Restoring Expressivity of Linear Attention
+// via Token-Level Multi-Head", Method -> Key design 2: the mixing is one product of M_c with the
+// stack of summaries; row i of M_c belongs to query block i).
+//
+// Per (batch, head) the summaries form X[M][P] (P = fragment positions of a d x d summary) and
+// the kernel computes Y = M_c X as Y^T = X^T M_c^T on v_mfma_f32_16x16x32_bf16:
+//   A = X^T   16 positions x 32 blocks, read from an LDS tile that holds X transposed
+//             (blocks contiguous; filled with 16-byte global loads and an 8x8 register
+//             transpose, like the summary kernel);
+//   B = M_c^T 32 blocks x 16 query blocks, converted to bf16 once per workgroup and held in
+//             registers for its lifetime;
+//   D         lane (g, l) holds Y[i = 16*it + l][p .. p+3] -> one 8-byte store.
+// The contraction over blocks is padded to a multiple of 32 with zero rows.  The normaliser
+// rides along as one extra column tile: z_b enters as interleaved bf16 (hi, lo) column pairs
+// (z = hi + lo to about 2^-17) and leaves as fp32 z~ = Y[hi col] + Y[lo col], so numerator and
+// denominator are mixed with the same bf16-rounded coefficients and the denominator keeps fp32
+// accuracy in z.
+#include "mhla_device.hpp"
+
+namespace mhla {
+
+// NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave.
+template <int NBC, int ITW>
+__global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
+  constexpr int MPAD = 32 * NBC;
+  constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
+  constexpr int NPT = PB / 16;            // 16-column MFMA tiles per staged tile
+  constexpr int XP = MPAD + 8;            // LDS pitch (elements) of one transposed column
+  constexpr int CG = PB / 8;              // 8-column groups per tile
+
+  extern __shared__ __align__(16) uint16_t xt[];   // [PB][XP]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pr = lane & 15, lg = lane >> 4;
+  const int bh = blockIdx.z;
+  const int M = p.M;
+  // NULL M_c is accepted for M == 1: the single coefficient is 1
+  const float* mc = p.mc ? p.mc + (int64_t)(bh % p.H) * p.mc_head_stride : nullptr;
+
+  // ---------------- wave roles -------------------------------------------------------------
+  // `wave_rows` waves split the workgroup's i-tiles; the remaining factor splits columns.
+  const int WI = p.wave_rows;
+  const int WPW = 4 / WI;
+  const int wi = wave % WI, wp = wave / WI;
+  const int it0 = (blockIdx.y * WI + wi) * ITW;     // first i-tile of this wave
+  const int nit = (M + 15) >> 4;
+
+  // M_c^T operand fragments: lane holds M_c[16*it + pr][32*bc + 8*lg + e], e = 0..7.
+  u32x4_t bfrag[ITW][NBC];
+#pragma unroll
+  for (int a = 0; a < ITW; ++a)
+#pragma unroll
+    for (int bc = 0; bc < NBC; ++bc) {
+      const int i = 16 * (it0 + a) + pr;
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int b = 32 * bc + 8 * lg + e;
+        m[e] = (i < M && b < M) ? (mc ? mc[(int64_t)i * M + b] : 1.0f) : 0.f;
+      }
+      bfrag[a][bc] = u32x4_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]),
+                             pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7])};
+    }
+
+  const int P = p.frag;
+  const int n_tiles = P / PB;
+  const uint16_t* x = p.x + (int64_t)bh * M * P;
+  uint16_t* y = p.y + (int64_t)bh * M * P;
+
+  const int cg = tid % CG, rg = tid / CG;           // loader role: rows 8*rg.., columns 8*cg..
+  u32x4_t raw[8];
+  auto issue = [&](int tile) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int b = 8 * rg + r;
+      raw[r] = (b < M) ? ld16(x + (int64_t)b * P + (int64_t)tile * PB + 8 * cg) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // tiles n_tiles .. n_tiles + n_ztiles - 1 hold the normaliser: within z tile j, column 2c is
+  // hi(z_b[j*PB/2 + c]) and column 2c + 1 its low part
+  const int D = p.D;
+  const int n_ztiles = (2 * D + PB - 1) / PB;
+  const int last = n_tiles + n_ztiles;            // one past the last tile
+  const float* zsrc = p.z + (int64_t)bh * M * D;
+  auto issue_z = [&](int zj) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int b = 8 * rg + r;
+      const int c0 = zj * (PB / 2) + 4 * cg;
+      if (b < M && c0 < D) {
+        const u32x4_t zz = ld16(zsrc + (int64_t)b * D + c0);
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t h, l;
+          split_bf16(__uint_as_float(zz[j]), h, l);
+          w[j] = h | (l << 16);
+        }
+        raw[r] = u32x4_t{w[0], w[1], w[2], w[3]};
+      } else {
+        raw[r] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto issue_any = [&](int t) {
+    if (t < n_tiles) issue(t);
+    else issue_z(t - n_tiles);
+  };
+
+  int tile = blockIdx.x;
+  if (tile < last) issue_any(tile);
+  for (; tile < last; tile += p.n_wg_x) {
+    // transpose 8 rows x 8 columns into LDS: column-major with blocks contiguous
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x4_t col;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t w0 = raw[2 * r][e >> 1], w1 = raw[2 * r + 1][e >> 1];
+        col[r] = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+      }
+      *reinterpret_cast<u32x4_t*>(xt + (8 * cg + e) * XP + 8 * rg) = col;
+    }
+    __syncthreads();
+    if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);
+    const bool ztile = tile >= n_tiles;
+    const int zbase = (tile - n_tiles) * (PB / 2);
+
+    for (int pt = wp; pt < NPT; pt += WPW) {
+      f32x4_t accs[ITW];
+#pragma unroll
+      for (int a = 0; a < ITW; ++a) accs[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bc = 0; bc < NBC; ++bc) {
+        const u32x4_t afrag =
+            *reinterpret_cast<const u32x4_t*>(xt + (16 * pt + pr) * XP + 32 * bc + 8 * lg);
+#pragma unroll
+        for (int a = 0; a < ITW; ++a) accs[a] = mfma_bf16(afrag, bfrag[a][bc], accs[a]);
+      }
+#pragma unroll
+      for (int a = 0; a < ITW; ++a) {
+        if (it0 + a >= nit) break;
+        const f32x4_t acc = accs[a];
+        const int i = 16 * (it0 + a) + pr;
+        const int q = 16 * pt + 4 * lg;
+        if (i < M && !ztile) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)i * P + (int64_t)tile * PB + q);
+          dst[0] = pack_bf16x2(acc[0], acc[1]);
+          dst[1] = pack_bf16x2(acc[2], acc[3]);
+        } else if (i < M && ztile && zbase + q / 2 < D) {
+          float* zd = p.zt + ((int64_t)bh * M + i) * D + zbase + q / 2;
+          zd[0] = acc[0] + acc[1];
+          zd[1] = acc[2] + acc[3];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int NBC, int ITW>
+static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipStream_t s) {
+  constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD + 8;
+  const size_t lds = (size_t)PB * XP * 2;
+  auto kern = mix_mfma_kernel<NBC, ITW>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(p.n_wg_x, row_groups, bh), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+// Chooses the contraction padding, rows per wave and the wave split from M.
+hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream) {
+  const int M = p.M;
+  if (M < 1 || M > 256) return hipErrorInvalidValue;
+  const int nbc = (M + 31) / 32;
+  const int NBC = nbc <= 1 ? 1 : nbc <= 2 ? 2 : nbc <= 4 ? 4 : 8;
+  const int nit = (M + 15) / 16;
+  // i-tiles per wave: at most 4 (register budget), all rows in one workgroup when possible
+  const int itw = nit <= 4 ? 1 : (nit + 3) / 4;
+  const int ITW = itw <= 1 ? 1 : 2;   // beyond 128 rows a second row group shares the tile
+  int wave_rows = 4;
+  while (wave_rows > 1 && (wave_rows / 2) * ITW >= nit) wave_rows /= 2;
+  p.wave_rows = wave_rows;
+  const int rows_per_wg = wave_rows * ITW * 16;
+  const int row_groups = (M + rows_per_wg - 1) / rows_per_wg;
+  const int pb = 16384 / (32 * NBC);
+  const int n_tiles = p.frag / pb;
+  if (p.frag % pb != 0) return hipErrorInvalidValue;
+  const int n_all = n_tiles + (2 * p.D + pb - 1) / pb;     // summary tiles + normaliser tiles
+  // enough column workgroups to cover ~8 per CU across all heads
+  int want = (2048 + bh * row_groups - 1) / (bh * row_groups);
+  if (want > n_all) want = n_all;
+  if (want < 1) want = 1;
+  p.n_wg_x = want;
+#define MHLA_MIX_CASE(N, I) \
+  if (NBC == N && ITW == I) return launch_t<N, I>(p, row_groups, bh, stream);
+  MHLA_MIX_CASE(1, 1) MHLA_MIX_CASE(2, 1) MHLA_MIX_CASE(4, 2) MHLA_MIX_CASE(8, 2)
+#undef MHLA_MIX_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mhla

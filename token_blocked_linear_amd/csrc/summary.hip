@@ -17,7 +17,7 @@
 
 namespace mhla {
 
-template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U>
+template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
   using Dm = Dims<D>;
   constexpr int DK = Dm::DK, NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -199,16 +199,22 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
   // ---- write the partial summary in fragment layout ------------------------------------
   const int64_t slot = ((int64_t)bh * g.M + blk) * p.splits + split;
   if (mfma_wave) {
-    float* out = p.ps + slot * FRAG;
 #pragma unroll
     for (int a = 0; a < KCW; ++a)
 #pragma unroll
       for (int c = 0; c < CTW; ++c) {
         const int kc = wr * KCW + a, ct = wc * CTW + c;
-        float* dst = out + ((kc * NCT + ct) * 64 + lane) * 8;
+        const int off = ((kc * NCT + ct) * 64 + lane) * 8;
         const f32x4_t r0 = acc[a][0][c], r1 = acc[a][1][c];
-        st16(dst, __builtin_bit_cast(u32x4_t, r0));
-        st16(dst + 4, __builtin_bit_cast(u32x4_t, r1));
+        if constexpr (OUT_BF16) {   // one token slice: the bf16 stack feeds the MFMA mixing
+          st16(p.sb + slot * FRAG + off,
+               u32x4_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
+                       pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])});
+        } else {
+          float* dst = p.ps + slot * FRAG + off;
+          st16(dst, __builtin_bit_cast(u32x4_t, r0));
+          st16(dst + 4, __builtin_bit_cast(u32x4_t, r1));
+        }
       }
   }
 
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
   }
 }
 
-template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U>
+template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false>
 static hipError_t launch_summary_t(const SummaryParams& p, dim3 grid, hipStream_t stream) {
   using Dm = Dims<D>;
   constexpr int LPR = D / 8, TG_ALL = kThreads / LPR, TG = TG_ALL < 32 ? TG_ALL : 32;
@@ -243,7 +249,7 @@ static hipError_t launch_summary_t(const SummaryParams& p, dim3 grid, hipStream_
   size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2;
   const size_t red = (size_t)TG * D * 4 * (WANT_U ? 2 : 1);
   if (red > lds) lds = red;
-  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U>;
+  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -253,16 +259,20 @@ static hipError_t launch_summary_t(const SummaryParams& p, dim3 grid, hipStream_
 
 template <typename TIn, int D>
 static hipError_t dispatch_flags(const SummaryParams& p, bool split_k, bool split_v, bool want_u,
-                                 dim3 grid, hipStream_t s) {
+                                 bool out_bf16, dim3 grid, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     if (split_v) return hipErrorInvalidValue;   // bf16 V is exact: never split
+    if (out_bf16) {
+      if (split_k || want_u) return hipErrorInvalidValue;
+      return launch_summary_t<TIn, D, false, false, false, true>(p, grid, s);
+    }
     if (split_k)
       return want_u ? launch_summary_t<TIn, D, true, false, true>(p, grid, s)
                     : launch_summary_t<TIn, D, true, false, false>(p, grid, s);
     return want_u ? launch_summary_t<TIn, D, false, false, true>(p, grid, s)
                   : launch_summary_t<TIn, D, false, false, false>(p, grid, s);
   } else {
-    if (split_k != split_v) return hipErrorInvalidValue;
+    if (split_k != split_v || out_bf16) return hipErrorInvalidValue;
     if (split_k)
       return want_u ? launch_summary_t<TIn, D, true, true, true>(p, grid, s)
                     : launch_summary_t<TIn, D, true, true, false>(p, grid, s);
@@ -272,21 +282,21 @@ static hipError_t dispatch_flags(const SummaryParams& p, bool split_k, bool spli
 }
 
 template <typename TIn>
-static hipError_t dispatch_d(const SummaryParams& p, int d, bool sk, bool sv, bool wu, dim3 grid,
-                             hipStream_t s) {
+static hipError_t dispatch_d(const SummaryParams& p, int d, bool sk, bool sv, bool wu, bool ob,
+                             dim3 grid, hipStream_t s) {
   switch (d) {
-    case 16: return dispatch_flags<TIn, 16>(p, sk, sv, wu, grid, s);
-    case 32: return dispatch_flags<TIn, 32>(p, sk, sv, wu, grid, s);
-    case 64: return dispatch_flags<TIn, 64>(p, sk, sv, wu, grid, s);
-    case 128: return dispatch_flags<TIn, 128>(p, sk, sv, wu, grid, s);
+    case 16: return dispatch_flags<TIn, 16>(p, sk, sv, wu, ob, grid, s);
+    case 32: return dispatch_flags<TIn, 32>(p, sk, sv, wu, ob, grid, s);
+    case 64: return dispatch_flags<TIn, 64>(p, sk, sv, wu, ob, grid, s);
+    case 128: return dispatch_flags<TIn, 128>(p, sk, sv, wu, ob, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
-                          bool want_u, dim3 grid, hipStream_t stream) {
-  return in_fp32 ? dispatch_d<float>(p, d, split_k, split_v, want_u, grid, stream)
-                 : dispatch_d<uint16_t>(p, d, split_k, split_v, want_u, grid, stream);
+                          bool want_u, bool out_bf16, dim3 grid, hipStream_t stream) {
+  return in_fp32 ? dispatch_d<float>(p, d, split_k, split_v, want_u, out_bf16, grid, stream)
+                 : dispatch_d<uint16_t>(p, d, split_k, split_v, want_u, out_bf16, grid, stream);
 }
 
 }  // namespace mhla
