@@ -158,6 +158,20 @@ __device__ inline f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, f32x4_t 
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
+// Buffer resources (V#): a base address and a byte range.  A raw buffer load whose offset lies
+// outside the range returns zeros instead of touching memory, so guarded loads need no branch
+// (branches around loads make the compiler wait for every outstanding load).  The last word
+// is the gfx9-family untyped-buffer configuration.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // >= every range used here (ranges < 2^31)
+
+__device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4_t buf_ld16(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // Input element loaders: 8 consecutive elements starting at element index `idx` as fp32.
 template <typename T> struct In8;
 template <> struct In8<uint16_t> {       // bf16 bits
@@ -165,6 +179,7 @@ template <> struct In8<uint16_t> {       // bf16 bits
   __device__ inline void load(const void* base, int64_t idx) {
     w = ld16(reinterpret_cast<const uint16_t*>(base) + idx);
   }
+  __device__ inline void load_buf(Rsrc r, uint32_t byte_off) { w = buf_ld16(r, byte_off); }
   __device__ inline void zero() { w = u32x4_t{0u, 0u, 0u, 0u}; }
   __device__ inline float get(int e) const {
     uint32_t x = w[e >> 1];
@@ -181,6 +196,10 @@ template <> struct In8<float> {
     const float* p = reinterpret_cast<const float*>(base) + idx;
     w0 = ld16(p);
     w1 = ld16(p + 4);
+  }
+  __device__ inline void load_buf(Rsrc r, uint32_t byte_off) {
+    w0 = buf_ld16(r, byte_off);
+    w1 = buf_ld16(r, byte_off == kOutOfRange ? kOutOfRange : byte_off + 16u);
   }
   __device__ inline void zero() {
     w0 = u32x4_t{0u, 0u, 0u, 0u};

@@ -15,7 +15,7 @@
 
 namespace mhla {
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
-                          bool want_u, bool out_bf16, dim3 grid, hipStream_t stream);
+                          bool want_u, bool out_bf16, int n_units, hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool mala, bool split,
                       hipStream_t stream);
 hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream);
@@ -90,6 +90,9 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   if (d->readout == MHLA_READOUT_MALA && M != 1) return MHLA_ERR_UNSUPPORTED;
   // element offsets are 64-bit; guard the total size against overflow
   if (BH > ((int64_t)1 << 62) / (N * d->head_dim * 4)) return MHLA_ERR_SHAPE;
+  // the kernels address one head of Q, K, V (and one head's summary stack) through buffer
+  // resources with 31-bit byte ranges
+  if (N * d->head_dim * 4 >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
 
   P->desc = *d;
   P->d = (int)d->head_dim;
@@ -268,8 +271,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.tok_per_split = h->sum_tok;
     sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
     hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
-                                        h->mix_mfma,
-                                        dim3(h->sum_splits, (unsigned)h->M, (unsigned)h->BH), s);
+                                        h->mix_mfma, (int)(h->sum_splits * h->M * h->BH), s);
     if (e != hipSuccess) return MHLA_ERR_HIP;
     if (tl && hipEventRecord(tl->ev[1], s) != hipSuccess) return MHLA_ERR_HIP;
 

@@ -26,8 +26,16 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
   constexpr int MPAD = 32 * NBC;
   constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
   constexpr int NPT = PB / 16;            // 16-column MFMA tiles per staged tile
-  constexpr int XP = MPAD + 8;            // LDS pitch (elements) of one transposed column
+  constexpr int XP = MPAD;                // LDS pitch (elements) of one transposed column
   constexpr int CG = PB / 8;              // 8-column groups per tile
+  // LDS bank swizzle on the 16-byte chunks (8 blocks) of a transposed column r: columns are
+  // written 8 apart (r = 8*cg + e) and read 8 consecutive (r = 16*pt + pr).  With >= 8 chunks
+  // per column, chunk c lives at c ^ ((r & 7) ^ ((r >> 3) & 7)); a 64-byte column (MPAD = 32)
+  // has 4 chunks and two columns share each 128-byte bank row, so the low two bits are used.
+  auto swz = [](int r, int c) {
+    if constexpr (MPAD >= 64) return c ^ ((r & 7) ^ ((r >> 3) & 7));
+    else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+  };
 
   extern __shared__ __align__(16) uint16_t xt[];   // [PB][XP]
 
@@ -70,11 +78,13 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
 
   const int cg = tid % CG, rg = tid / CG;           // loader role: rows 8*rg.., columns 8*cg..
   u32x4_t raw[8];
+  // the stack of this head through a buffer resource: rows b >= M read as zero, no branch
+  const Rsrc rsx = make_rsrc(x, (uint32_t)M * P * 2u);
   auto issue = [&](int tile) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int b = 8 * rg + r;
-      raw[r] = (b < M) ? ld16(x + (int64_t)b * P + (int64_t)tile * PB + 8 * cg) : u32x4_t{0u, 0u, 0u, 0u};
+      raw[r] = buf_ld16(rsx, b < M ? (uint32_t)(b * P + tile * PB + 8 * cg) * 2u : kOutOfRange);
     }
   };
 
@@ -121,7 +131,8 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
         const uint32_t w0 = raw[2 * r][e >> 1], w1 = raw[2 * r + 1][e >> 1];
         col[r] = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
       }
-      *reinterpret_cast<u32x4_t*>(xt + (8 * cg + e) * XP + 8 * rg) = col;
+      const int r = 8 * cg + e;
+      *reinterpret_cast<u32x4_t*>(xt + r * XP + 8 * swz(r, rg)) = col;
     }
     __syncthreads();
     if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);
@@ -134,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
       for (int a = 0; a < ITW; ++a) accs[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int bc = 0; bc < NBC; ++bc) {
-        const u32x4_t afrag =
-            *reinterpret_cast<const u32x4_t*>(xt + (16 * pt + pr) * XP + 32 * bc + 8 * lg);
+        const int r = 16 * pt + pr;
+        const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + r * XP + 8 * swz(r, 4 * bc + lg));
 #pragma unroll
         for (int a = 0; a < ITW; ++a) accs[a] = mfma_bf16(afrag, bfrag[a][bc], accs[a]);
       }
@@ -162,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
 
 template <int NBC, int ITW>
 static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipStream_t s) {
-  constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD + 8;
+  constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD;
   const size_t lds = (size_t)PB * XP * 2;
   auto kern = mix_mfma_kernel<NBC, ITW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -190,8 +201,9 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream) {
   const int n_tiles = p.frag / pb;
   if (p.frag % pb != 0) return hipErrorInvalidValue;
   const int n_all = n_tiles + (2 * p.D + pb - 1) / pb;     // summary tiles + normaliser tiles
-  // enough column workgroups to cover ~8 per CU across all heads
-  int want = (2048 + bh * row_groups - 1) / (bh * row_groups);
+  // about two workgroups per CU across all heads: each converts its M_c rows once and then
+  // strides over many column tiles
+  int want = (512 + bh * row_groups - 1) / (bh * row_groups);
   if (want > n_all) want = n_all;
   if (want < 1) want = 1;
   p.n_wg_x = want;

@@ -1,36 +1,46 @@
 // Summary kernel: phi(K) in registers, per-block S_b = sum_j phi(K_j) V_j^T on bf16 MFMA with
-// fp32 accumulation, z_b = sum_j phi(K_j) (and, for the MALA readout, u = sum_j V_j) in fp32.
+// fp32 accumulation, z_b = sum_j phi(K_j) (and, for the MALA readout, u = sum_j V_j).
 //
 // Source: "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head",
 // Method -> Overall framework (local KV summary S_b and normaliser z_b of every block); the
 // MALA linear form in "Rectifying Magnitude Neglect in Linear Attention", Method -> Key design,
 // also needs sum_j V_j.
 //
-// One workgroup (4 wave64s) owns one token slice of one block of one (batch, head).  Tokens
-// are streamed in rounds.  Each thread owns 8 consecutive block-local tokens x 8 consecutive
-// features: it issues one 16-byte load per token row (D/8 lanes cover a row, so every load
-// instruction reads whole rows), applies phi in fp32, and transposes its 8x8 piece in
-// registers so that LDS holds phi(K)^T and V^T with tokens contiguous (one 16-byte LDS write
-// per feature).  The MFMA phase then reads every operand with one 16-byte LDS read.
-// The next round's global loads are issued before the MFMA phase of the current one.
+// Work units are (batch*head, block, token slice); the grid is persistent and each workgroup
+// (4 wave64s) strides over units.  Tokens stream in rounds of up to 256: every thread owns 8
+// consecutive block-local tokens x 8 consecutive features, issues one 16-byte load per token
+// row (D/8 lanes cover a row, so each load instruction reads whole rows), applies phi in fp32,
+// and transposes its 8x8 piece in registers so that LDS holds phi(K)^T and V^T with tokens
+// contiguous (one 16-byte LDS write per feature).  The MFMA phase reads every operand with one
+// 16-byte LDS read.  The next round's loads -- of this unit or the next one -- are in flight
+// during the MFMA phase.  z (and u) come from the same MFMAs against an all-ones operand, so
+// they carry exactly the operands' rounding and need no cross-thread reduction.
 #include "mhla_device.hpp"
 
 namespace mhla {
 
 template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
+__global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int n_units) {
   using Dm = Dims<D>;
   constexpr int DK = Dm::DK, NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
   constexpr int LPR = D / 8;               // threads per token row
   constexpr int TG_ALL = kThreads / LPR;   // token groups the workgroup could cover
   constexpr int TG = TG_ALL < 32 ? TG_ALL : 32;   // token groups of 8 per round (<= 256 tokens)
   constexpr int ROUND = TG * 8;            // tokens per round
-  constexpr int PITCH = ROUND + 8;         // LDS row pitch in bf16 elements (16-byte pad)
+  constexpr int PITCH = ROUND;             // LDS row pitch (bf16 elements): rows start on 128 B
+  static_assert(ROUND >= 64, "the chunk swizzle needs at least 8 chunks per row");
   // MFMA work split: waves form WR x WC over (32-feature chunks, 16-channel tiles).
   constexpr int WR = NKC >= 2 ? 2 : 1;
   constexpr int WC = NCT >= 2 ? 2 : 1;
   constexpr int KCW = NKC / WR;
   constexpr int CTW = NCT / WC;
+  constexpr uint32_t kOnes = 0x3f803f80u;  // two bf16 1.0
+  // LDS bank swizzle: the 16-byte token chunk c of row f lives at chunk c ^ h(f).  phi(K)^T
+  // rows are written 8 rows apart (f = 8*fgrp + e) and read as rows {b..b+3, b+8..b+11};
+  // V^T rows are written 8 apart and read 8 consecutive.  Both h keep any 8 consecutive
+  // lanes of either access on 8 distinct 16-byte bank groups.
+  auto hk = [](int f) { return ((f >> 3) & 7) ^ ((f & 3) << 1); };
+  auto hv = [](int c) { return (c & 7) ^ ((c >> 3) & 7); };
 
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* kt_hi = smem;                                   // [DK][PITCH]
@@ -41,19 +51,13 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int split = blockIdx.x;
-  const int blk = blockIdx.y;
-  const int bh = blockIdx.z;
   const Geom& g = p.g;
-
   const int fgrp = tid % LPR;              // features [8*fgrp, 8*fgrp+8)
   const int tgrp = tid / LPR;              // tokens [8*tgrp, 8*tgrp+8) of each round
   const bool loader = tgrp < TG;           // small D: some threads only help with MFMA
-
-  const int32_t j_begin = split * p.tok_per_split;
-  const int32_t j_end = min(j_begin + p.tok_per_split, g.n_b);
-  const int32_t base_tok = block_base_token(g, blk);
-  const int64_t head_off = (int64_t)bh * g.N * D;
+  const bool mfma_wave = wave < WR * WC;
+  const int wr = wave / WC, wc = wave % WC;
+  const int pr = lane & 15, lg = lane >> 4;
 
   if (DK > D) {  // key rows beyond D stay zero for the whole kernel
     for (int i = tid; i < (DK - D) * PITCH; i += kThreads) {
@@ -62,108 +66,146 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
     }
   }
 
-  In8<TIn> rk[8], rv[8];
-  auto issue_loads = [&](int32_t round_base) {
+  // ---- unit bookkeeping --------------------------------------------------------------------
+  struct Unit {
+    int split, blk, bh;
+    int32_t j_begin, j_end, base_tok;
+    int64_t head_off;
+  };
+  auto make_unit = [&](int u) {
+    Unit U;
+    U.split = u % p.splits;
+    const int t = u / p.splits;
+    U.blk = t % g.M;
+    U.bh = t / g.M;
+    U.j_begin = U.split * p.tok_per_split;
+    U.j_end = min(U.j_begin + p.tok_per_split, g.n_b);
+    U.base_tok = block_base_token(g, U.blk);
+    U.head_off = (int64_t)U.bh * g.N * D;
+    return U;
+  };
+
+  // When the block's last extent is a multiple of 8, a thread's 8 block-local tokens
+  // j0..j0+7 (j0 a multiple of 8) lie in one grid row: their rows are consecutive in memory
+  // and one index computation serves all 8 loads.
+  const bool contig8 = (g.B2 & 7) == 0;
+
+  // Loads of one round into a register buffer.  Rows of tokens past the unit's end are zero:
+  // they add nothing to S (their V is zero) and z masks them explicitly.
+  // Loads go through buffer resources spanning one head; rows past the unit's end get an
+  // out-of-range offset and read as zero, with no branch around the loads.
+  constexpr uint32_t ES = sizeof(TIn);
+  const uint32_t head_bytes = (uint32_t)g.N * D * ES;
+  auto issue_loads = [&](In8<TIn> (&rk)[8], In8<TIn> (&rv)[8], const Unit& U, int32_t round_base) {
+    const Rsrc rsk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, head_bytes);
+    const Rsrc rsv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + U.head_off, head_bytes);
+    const int32_t j0 = round_base + 8 * tgrp;
+    if (contig8) {
+      const bool ok = loader && j0 < U.j_end;
+      const uint32_t t0 = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j0)) : 0u;
+      const uint32_t off0 = (t0 * D + 8 * fgrp) * ES;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int32_t j = round_base + 8 * tgrp + i;
-      if (loader && j < j_end) {
-        const int64_t t = base_tok + block_token_offset(g, (uint32_t)j);
-        const int64_t idx = head_off + t * D + 8 * fgrp;
-        rk[i].load(p.k, idx);
-        rv[i].load(p.v, idx);
-      } else {
-        rk[i].zero();
-        rv[i].zero();
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t off = ok ? off0 + (uint32_t)(i * D * ES) : kOutOfRange;
+        rk[i].load_buf(rsk, off);
+        rv[i].load_buf(rsv, off);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int32_t j = j0 + i;
+        const bool ok = loader && j < U.j_end;
+        const uint32_t t = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j)) : 0u;
+        const uint32_t off = ok ? (t * D + 8 * fgrp) * ES : kOutOfRange;
+        rk[i].load_buf(rsk, off);
+        rv[i].load_buf(rsv, off);
       }
     }
   };
 
-  float zacc[8], uacc[8];
+  f32x4_t acc[KCW][2][CTW], accz[KCW][2], accu[CTW];
+  auto reset = [&]() {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) { zacc[e] = 0.f; uacc[e] = 0.f; }
+    for (int a = 0; a < KCW; ++a)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        accz[a][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) acc[a][r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) accu[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  reset();
 
-  f32x4_t acc[KCW][2][CTW];
-#pragma unroll
-  for (int a = 0; a < KCW; ++a)
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int c = 0; c < CTW; ++c) acc[a][r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const bool mfma_wave = wave < WR * WC;
-  const int wr = wave / WC, wc = wave % WC;
-
-  issue_loads(j_begin);
-  for (int32_t rb = j_begin; rb < j_end; rb += ROUND) {
-    // ---- phi, split, transpose into LDS --------------------------------------------------
+  // One round: phi / split / transpose into LDS, MFMAs, and the unit's epilogue if it ends.
+  // `after_lds` runs once the round's registers are in LDS (single-buffer refill point).
+  auto process = [&](const In8<TIn> (&rk)[8], const In8<TIn> (&rv)[8], const Unit& U, int32_t rb,
+                     auto&& after_lds) {
     if (loader) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int f = 8 * fgrp + e;
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool valid = rb + 8 * tgrp + i < j_end;
-        x[i] = valid ? phi_elu1(rk[i].get(e)) : 0.f;   // padding is zero AFTER phi
-        zacc[e] += x[i];
-      }
-      u32x4_t hi, lo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (SPLIT_K) {
-          uint32_t h0, l0, h1, l1;
-          split_bf16(x[2 * i], h0, l0);
-          split_bf16(x[2 * i + 1], h1, l1);
-          hi[i] = h0 | (h1 << 16);
-          lo[i] = l0 | (l1 << 16);
-        } else {
-          hi[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-        }
-      }
-      *reinterpret_cast<u32x4_t*>(kt_hi + f * PITCH + 8 * tgrp) = hi;
-      if (SPLIT_K) *reinterpret_cast<u32x4_t*>(kt_lo + f * PITCH + 8 * tgrp) = lo;
-
-      u32x4_t vh, vl;
-      if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vh[i] = rv[2 * i].bits(e) | (rv[2 * i + 1].bits(e) << 16);   // exact: no rounding
-        if (WANT_U) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) uacc[e] += rv[i].get(e);
-        }
-      } else {
+      for (int e = 0; e < 8; ++e) {
+        const int f = 8 * fgrp + e;
+        u32x4_t hi, lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v0 = rv[2 * i].get(e), v1 = rv[2 * i + 1].get(e);
-          if (WANT_U) uacc[e] += v0 + v1;
-          if (SPLIT_V) {
+          const float x0 = phi_elu1(rk[2 * i].get(e)), x1 = phi_elu1(rk[2 * i + 1].get(e));
+          if (SPLIT_K) {
             uint32_t h0, l0, h1, l1;
-            split_bf16(v0, h0, l0);
-            split_bf16(v1, h1, l1);
-            vh[i] = h0 | (h1 << 16);
-            vl[i] = l0 | (l1 << 16);
+            split_bf16(x0, h0, l0);
+            split_bf16(x1, h1, l1);
+            hi[i] = h0 | (h1 << 16);
+            lo[i] = l0 | (l1 << 16);
           } else {
-            vh[i] = pack_bf16x2(v0, v1);
+            hi[i] = pack_bf16x2(x0, x1);
           }
         }
+        const int kofs = f * PITCH + 8 * (tgrp ^ hk(f));
+        *reinterpret_cast<u32x4_t*>(kt_hi + kofs) = hi;
+        if (SPLIT_K) *reinterpret_cast<u32x4_t*>(kt_lo + kofs) = lo;
+
+        u32x4_t vh, vl;
+        if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vh[i] = rv[2 * i].bits(e) | (rv[2 * i + 1].bits(e) << 16);   // exact: no rounding
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v0 = rv[2 * i].get(e), v1 = rv[2 * i + 1].get(e);
+            if (SPLIT_V) {
+              uint32_t h0, l0, h1, l1;
+              split_bf16(v0, h0, l0);
+              split_bf16(v1, h1, l1);
+              vh[i] = h0 | (h1 << 16);
+              vl[i] = l0 | (l1 << 16);
+            } else {
+              vh[i] = pack_bf16x2(v0, v1);
+            }
+          }
+        }
+        const int vofs = f * PITCH + 8 * (tgrp ^ hv(f));
+        *reinterpret_cast<u32x4_t*>(vt_hi + vofs) = vh;
+        if (SPLIT_V) *reinterpret_cast<u32x4_t*>(vt_lo + vofs) = vl;
       }
-      *reinterpret_cast<u32x4_t*>(vt_hi + f * PITCH + 8 * tgrp) = vh;
-      if (SPLIT_V) *reinterpret_cast<u32x4_t*>(vt_lo + f * PITCH + 8 * tgrp) = vl;
-    }
     }
     __syncthreads();
+    after_lds();
 
-    const int32_t valid_round = min(ROUND, j_end - rb);
-    if (rb + ROUND < j_end) issue_loads(rb + ROUND);
-
-    // ---- MFMA: S_quadrant += phi(K)^T V over this round --------------------------------
+    const int32_t valid_round = min(ROUND, U.j_end - rb);
     if (mfma_wave) {
       const int nsteps = (valid_round + 31) >> 5;
-      const int pr = lane & 15, lg = lane >> 4;
+      const u32x4_t ones = {kOnes, kOnes, kOnes, kOnes};
       for (int ks = 0; ks < nsteps; ++ks) {
-        const int tok = 32 * ks + 8 * lg;
+        const int chunk = 4 * ks + lg;           // 16-byte chunk of tokens 32ks + 8lg ..
+        // token validity as the B operand of the z product (phi(0) = 1 on padding rows)
+        u32x4_t vmask = ones;
+        const int left = valid_round - 8 * chunk;
+        if (left < 8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vmask[i] = (2 * i < left ? 0x3f80u : 0u) | (2 * i + 1 < left ? 0x3f800000u : 0u);
+        }
         u32x4_t a_hi[KCW][2], a_lo[KCW][2], b_hi[CTW], b_lo[CTW];
 #pragma unroll
         for (int a = 0; a < KCW; ++a) {
@@ -171,132 +213,208 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p) {
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
             const int f = 32 * kc + 8 * (pr >> 2) + 4 * r + (pr & 3);
-            a_hi[a][r] = *reinterpret_cast<const u32x4_t*>(kt_hi + f * PITCH + tok);
-            if (SPLIT_K) a_lo[a][r] = *reinterpret_cast<const u32x4_t*>(kt_lo + f * PITCH + tok);
+            const int ofs = f * PITCH + 8 * (chunk ^ hk(f));
+            a_hi[a][r] = *reinterpret_cast<const u32x4_t*>(kt_hi + ofs);
+            if (SPLIT_K) a_lo[a][r] = *reinterpret_cast<const u32x4_t*>(kt_lo + ofs);
           }
         }
 #pragma unroll
         for (int c = 0; c < CTW; ++c) {
           const int ch = 16 * (wc * CTW + c) + pr;
-          b_hi[c] = *reinterpret_cast<const u32x4_t*>(vt_hi + ch * PITCH + tok);
-          if (SPLIT_V) b_lo[c] = *reinterpret_cast<const u32x4_t*>(vt_lo + ch * PITCH + tok);
+          const int ofs = ch * PITCH + 8 * (chunk ^ hv(ch));
+          b_hi[c] = *reinterpret_cast<const u32x4_t*>(vt_hi + ofs);
+          if (SPLIT_V) b_lo[c] = *reinterpret_cast<const u32x4_t*>(vt_lo + ofs);
         }
 #pragma unroll
         for (int a = 0; a < KCW; ++a)
 #pragma unroll
-          for (int r = 0; r < 2; ++r)
+          for (int r = 0; r < 2; ++r) {
 #pragma unroll
             for (int c = 0; c < CTW; ++c) {
               acc[a][r][c] = mfma_bf16(a_hi[a][r], b_hi[c], acc[a][r][c]);
               if (SPLIT_K) acc[a][r][c] = mfma_bf16(a_lo[a][r], b_hi[c], acc[a][r][c]);
               if (SPLIT_V) acc[a][r][c] = mfma_bf16(a_hi[a][r], b_lo[c], acc[a][r][c]);
             }
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- write the partial summary in fragment layout ------------------------------------
-  const int64_t slot = ((int64_t)bh * g.M + blk) * p.splits + split;
-  if (mfma_wave) {
+            if (wc == 0) {
+              accz[a][r] = mfma_bf16(a_hi[a][r], vmask, accz[a][r]);
+              if (SPLIT_K) accz[a][r] = mfma_bf16(a_lo[a][r], vmask, accz[a][r]);
+            }
+          }
+        if (WANT_U && wr == 0) {
 #pragma unroll
-    for (int a = 0; a < KCW; ++a)
-#pragma unroll
-      for (int c = 0; c < CTW; ++c) {
-        const int kc = wr * KCW + a, ct = wc * CTW + c;
-        const int off = ((kc * NCT + ct) * 64 + lane) * 8;
-        const f32x4_t r0 = acc[a][0][c], r1 = acc[a][1][c];
-        if constexpr (OUT_BF16) {   // one token slice: the bf16 stack feeds the MFMA mixing
-          st16(p.sb + slot * FRAG + off,
-               u32x4_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
-                       pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])});
-        } else {
-          float* dst = p.ps + slot * FRAG + off;
-          st16(dst, __builtin_bit_cast(u32x4_t, r0));
-          st16(dst + 4, __builtin_bit_cast(u32x4_t, r1));
+          for (int c = 0; c < CTW; ++c) {
+            accu[c] = mfma_bf16(ones, b_hi[c], accu[c]);
+            if (SPLIT_V) accu[c] = mfma_bf16(ones, b_lo[c], accu[c]);
+          }
         }
       }
-  }
+    }
 
-  // ---- deterministic reduction of z (and u) over the token groups ----------------------
-  float* red = reinterpret_cast<float*>(smem);          // [TG][D] (aliases the key planes)
-  float* red_u = red + TG * D;
-  __syncthreads();
-  if (loader) {
+    // ---- unit epilogue: summary in fragment layout, z, u ------------------------------
+    if (rb + ROUND >= U.j_end && mfma_wave) {
+      const int64_t slot = ((int64_t)U.bh * g.M + U.blk) * p.splits + U.split;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      red[tgrp * D + 8 * fgrp + e] = zacc[e];
-      if (WANT_U) red_u[tgrp * D + 8 * fgrp + e] = uacc[e];
+      for (int a = 0; a < KCW; ++a)
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) {
+          const int kc = wr * KCW + a, ct = wc * CTW + c;
+          const int off = ((kc * NCT + ct) * 64 + lane) * 8;
+          const f32x4_t r0 = acc[a][0][c], r1 = acc[a][1][c];
+          if constexpr (OUT_BF16) {   // one token slice: the bf16 stack feeds the MFMA mixing
+            st16(p.sb + slot * FRAG + off,
+                 u32x4_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
+                         pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])});
+          } else {
+            float* dst = p.ps + slot * FRAG + off;
+            st16(dst, __builtin_bit_cast(u32x4_t, r0));
+            st16(dst + 4, __builtin_bit_cast(u32x4_t, r1));
+          }
+        }
+      // z: every column of the validity product holds the row sum; lanes of column 0 store.
+      // Row 4g + r of row tile (kc, rt) is key feature 32*kc + 8g + 4*rt + r.
+      if (wc == 0 && pr == 0) {
+#pragma unroll
+        for (int a = 0; a < KCW; ++a)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int f = 32 * (wr * KCW + a) + 8 * lg + 4 * r;
+            if (f < D) st16(p.pz + slot * D + f, __builtin_bit_cast(u32x4_t, accz[a][r]));
+          }
+      }
+      // u: every row of the ones-product holds the column sum; lanes of row group 0 store.
+      if (WANT_U && wr == 0 && lg == 0) {
+#pragma unroll
+        for (int c = 0; c < CTW; ++c) p.pu[slot * D + 16 * (wc * CTW + c) + pr] = accu[c][0];
+      }
+      reset();
     }
-  }
-  __syncthreads();
-  if (tid < D) {
-    float s = 0.f, su = 0.f;
-    for (int t = 0; t < TG; ++t) {
-      s += red[t * D + tid];
-      if (WANT_U) su += red_u[t * D + tid];
+    __syncthreads();
+  };
+
+  // Advance (unit, round) -> the next round of this unit or the first round of the next unit.
+  auto advance = [&](int& unit, Unit& U, int32_t& rb) {
+    if (rb + ROUND < U.j_end) {
+      rb += ROUND;
+    } else {
+      unit += gridDim.x;
+      if (unit < n_units) {
+        U = make_unit(unit);
+        rb = U.j_begin;
+      }
     }
-    p.pz[slot * D + tid] = s;
-    if (WANT_U) p.pu[slot * D + tid] = su;
+  };
+
+  int unit = blockIdx.x;
+  if (unit >= n_units) return;
+  Unit U = make_unit(unit);
+  int32_t rb = U.j_begin;
+
+  auto nothing = [] {};
+  if constexpr (sizeof(TIn) == 2 && D <= 64) {
+    // Two register buffers: the loads of round r+1 are in flight while round r goes through
+    // phi, LDS and MFMA.
+    In8<TIn> ka[8], va[8], kb[8], vb[8];
+    issue_loads(ka, va, U, rb);
+    while (true) {
+      int nu = unit;
+      Unit NU = U;
+      int32_t nrb = rb;
+      advance(nu, NU, nrb);
+      if (nu < n_units) issue_loads(kb, vb, NU, nrb);
+      process(ka, va, U, rb, nothing);
+      if (nu >= n_units) break;
+      unit = nu;
+      U = NU;
+      rb = nrb;
+      advance(nu, NU, nrb);
+      if (nu < n_units) issue_loads(ka, va, NU, nrb);
+      process(kb, vb, U, rb, nothing);
+      if (nu >= n_units) break;
+      unit = nu;
+      U = NU;
+      rb = nrb;
+    }
+  } else {
+    // One buffer (d = 128 would spill two; fp32 inputs are twice as wide): refilled as soon as
+    // the round sits in LDS, so the loads overlap the MFMA phase.
+    In8<TIn> ka[8], va[8];
+    issue_loads(ka, va, U, rb);
+    while (true) {
+      int nu = unit;
+      Unit NU = U;
+      int32_t nrb = rb;
+      advance(nu, NU, nrb);
+      process(ka, va, U, rb, [&] {
+        if (nu < n_units) issue_loads(ka, va, NU, nrb);
+      });
+      if (nu >= n_units) break;
+      unit = nu;
+      U = NU;
+      rb = nrb;
+    }
   }
 }
 
 template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false>
-static hipError_t launch_summary_t(const SummaryParams& p, dim3 grid, hipStream_t stream) {
+static hipError_t launch_summary_t(const SummaryParams& p, int n_units, hipStream_t stream) {
   using Dm = Dims<D>;
   constexpr int LPR = D / 8, TG_ALL = kThreads / LPR, TG = TG_ALL < 32 ? TG_ALL : 32;
-  constexpr int ROUND = TG * 8, PITCH = ROUND + 8;
-  size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2;
-  const size_t red = (size_t)TG * D * 4 * (WANT_U ? 2 : 1);
-  if (red > lds) lds = red;
+  constexpr int ROUND = TG * 8, PITCH = ROUND;
+  const size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2;
   auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, p);
+  // persistent grid: as many workgroups as fit on the chip at once (LDS-limited), at most
+  // one per unit
+  const int per_cu = (int)(160 * 1024 / lds) < 1 ? 1 : (int)(160 * 1024 / lds);
+  int grid = 256 * (per_cu > 4 ? 4 : per_cu);
+  if (grid > n_units) grid = n_units;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, p, n_units);
   return hipGetLastError();
 }
 
 template <typename TIn, int D>
 static hipError_t dispatch_flags(const SummaryParams& p, bool split_k, bool split_v, bool want_u,
-                                 bool out_bf16, dim3 grid, hipStream_t s) {
+                                 bool out_bf16, int n, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     if (split_v) return hipErrorInvalidValue;   // bf16 V is exact: never split
     if (out_bf16) {
       if (split_k || want_u) return hipErrorInvalidValue;
-      return launch_summary_t<TIn, D, false, false, false, true>(p, grid, s);
+      return launch_summary_t<TIn, D, false, false, false, true>(p, n, s);
     }
     if (split_k)
-      return want_u ? launch_summary_t<TIn, D, true, false, true>(p, grid, s)
-                    : launch_summary_t<TIn, D, true, false, false>(p, grid, s);
-    return want_u ? launch_summary_t<TIn, D, false, false, true>(p, grid, s)
-                  : launch_summary_t<TIn, D, false, false, false>(p, grid, s);
+      return want_u ? launch_summary_t<TIn, D, true, false, true>(p, n, s)
+                    : launch_summary_t<TIn, D, true, false, false>(p, n, s);
+    return want_u ? launch_summary_t<TIn, D, false, false, true>(p, n, s)
+                  : launch_summary_t<TIn, D, false, false, false>(p, n, s);
   } else {
     if (split_k != split_v || out_bf16) return hipErrorInvalidValue;
     if (split_k)
-      return want_u ? launch_summary_t<TIn, D, true, true, true>(p, grid, s)
-                    : launch_summary_t<TIn, D, true, true, false>(p, grid, s);
-    return want_u ? launch_summary_t<TIn, D, false, false, true>(p, grid, s)
-                  : launch_summary_t<TIn, D, false, false, false>(p, grid, s);
+      return want_u ? launch_summary_t<TIn, D, true, true, true>(p, n, s)
+                    : launch_summary_t<TIn, D, true, true, false>(p, n, s);
+    return want_u ? launch_summary_t<TIn, D, false, false, true>(p, n, s)
+                  : launch_summary_t<TIn, D, false, false, false>(p, n, s);
   }
 }
 
 template <typename TIn>
 static hipError_t dispatch_d(const SummaryParams& p, int d, bool sk, bool sv, bool wu, bool ob,
-                             dim3 grid, hipStream_t s) {
+                             int n, hipStream_t s) {
   switch (d) {
-    case 16: return dispatch_flags<TIn, 16>(p, sk, sv, wu, ob, grid, s);
-    case 32: return dispatch_flags<TIn, 32>(p, sk, sv, wu, ob, grid, s);
-    case 64: return dispatch_flags<TIn, 64>(p, sk, sv, wu, ob, grid, s);
-    case 128: return dispatch_flags<TIn, 128>(p, sk, sv, wu, ob, grid, s);
+    case 16: return dispatch_flags<TIn, 16>(p, sk, sv, wu, ob, n, s);
+    case 32: return dispatch_flags<TIn, 32>(p, sk, sv, wu, ob, n, s);
+    case 64: return dispatch_flags<TIn, 64>(p, sk, sv, wu, ob, n, s);
+    case 128: return dispatch_flags<TIn, 128>(p, sk, sv, wu, ob, n, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+// n_units = splits * M * BH work units; the kernel picks its own persistent grid.
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
-                          bool want_u, bool out_bf16, dim3 grid, hipStream_t stream) {
-  return in_fp32 ? dispatch_d<float>(p, d, split_k, split_v, want_u, out_bf16, grid, stream)
-                 : dispatch_d<uint16_t>(p, d, split_k, split_v, want_u, out_bf16, grid, stream);
+                          bool want_u, bool out_bf16, int n_units, hipStream_t stream) {
+  return in_fp32 ? dispatch_d<float>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream)
+                 : dispatch_d<uint16_t>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream);
 }
 
 }  // namespace mhla
