@@ -84,6 +84,10 @@ _LIB: Optional[ctypes.CDLL] = None
 
 
 def library_path() -> str:
+    """The in-tree build; MHLA_LIBRARY may name another build of the same library."""
+    override = os.environ.get("MHLA_LIBRARY")
+    if override:
+        return override
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmhla.so")
 
 

@@ -18,6 +18,15 @@
 
 #include "fastdiv.hpp"
 
+// Cache policy of the loads that stream Q, K, V (each byte is read once) and of the output
+// stores.  0 = default; the build can set the gfx9 cache-policy bits for these streams.
+#ifndef MHLA_STREAM_CPOL
+#define MHLA_STREAM_CPOL 0
+#endif
+#ifndef MHLA_STREAM_STORE_NT
+#define MHLA_STREAM_STORE_NT 0
+#endif
+
 namespace mhla {
 
 constexpr int kThreads = 256;  // every kernel runs 4 wave64s per workgroup
@@ -71,7 +80,35 @@ struct SummaryParams {
   Geom g;
   int32_t splits;          // token slices per block
   int32_t tok_per_split;
+  // Side job for the MFMA mixing path: convert M_c (fp32) once per forward into bf16 operand
+  // fragments mcf[(h*nitp + it)*nbc + bc][lane][8] = M_c[h][16 it + lane%16][32 bc + 8(lane/16) + e]
+  // (zero outside M x M).  mcf == nullptr: nothing to convert.
+  const float* mc;
+  int64_t mc_head_stride;
+  uint16_t* mcf;
+  int32_t mcf_heads, mcf_nitp, mcf_nbc;
 };
+
+// Launch shape of the MFMA mixing kernel for M blocks: nbc 32-block chunks of the contraction,
+// itw 16-row i-tiles per wave, wave_rows waves sharing a row group's i-tiles, row_groups
+// workgroups per column tile.  Shared by the host plan and the kernel launcher.
+struct MixShape {
+  int nbc, itw, wave_rows, row_groups, nitp;
+};
+inline MixShape mix_shape(int M) {
+  MixShape s;
+  const int nbc = (M + 31) / 32;
+  s.nbc = nbc <= 1 ? 1 : nbc <= 2 ? 2 : nbc <= 4 ? 4 : 8;
+  const int nit = (M + 15) / 16;
+  const int itw = nit <= 4 ? 1 : (nit + 3) / 4;
+  s.itw = itw <= 1 ? 1 : itw <= 2 ? 2 : 4;
+  s.wave_rows = 4;
+  while (s.wave_rows > 1 && (s.wave_rows / 2) * s.itw >= nit) s.wave_rows /= 2;
+  const int rows_per_wg = s.wave_rows * s.itw * 16;
+  s.row_groups = (M + rows_per_wg - 1) / rows_per_wg;
+  s.nitp = s.row_groups * s.wave_rows * s.itw;
+  return s;
+}
 
 struct MixParams {
   const float* ps;
@@ -94,8 +131,8 @@ struct MixParams {
 struct MixMfmaParams {
   const uint16_t* x;       // bf16 [BH][M][FRAG]
   const float* z;          // fp32 [BH][M][D]
-  const float* mc;         // fp32 [M][M] or [H][M][M]
-  int64_t mc_head_stride;
+  const uint16_t* mcf;     // bf16 M_c operand fragments (see SummaryParams)
+  int32_t mcf_per_head;    // 1: fragments per head, 0: shared
   uint16_t* y;             // bf16 [BH][M][FRAG]
   float* zt;               // fp32 [BH][M][D]
   int32_t M;
@@ -157,6 +194,10 @@ __device__ inline f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, f32x4_t 
 // 16-byte global loads and stores.
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+__device__ inline void st16_stream(void* p, u32x4_t v) {
+  if (MHLA_STREAM_STORE_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+  else *reinterpret_cast<u32x4_t*>(p) = v;
+}
 
 // Buffer resources (V#): a base address and a byte range.  A raw buffer load whose offset lies
 // outside the range returns zeros instead of touching memory, so guarded loads need no branch
@@ -172,6 +213,11 @@ __device__ inline u32x4_t buf_ld16(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+__device__ inline u32x4_t buf_ld16_stream(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, MHLA_STREAM_CPOL));
+}
+
 // Input element loaders: 8 consecutive elements starting at element index `idx` as fp32.
 template <typename T> struct In8;
 template <> struct In8<uint16_t> {       // bf16 bits
@@ -179,7 +225,7 @@ template <> struct In8<uint16_t> {       // bf16 bits
   __device__ inline void load(const void* base, int64_t idx) {
     w = ld16(reinterpret_cast<const uint16_t*>(base) + idx);
   }
-  __device__ inline void load_buf(Rsrc r, uint32_t byte_off) { w = buf_ld16(r, byte_off); }
+  __device__ inline void load_buf(Rsrc r, uint32_t byte_off) { w = buf_ld16_stream(r, byte_off); }
   __device__ inline void zero() { w = u32x4_t{0u, 0u, 0u, 0u}; }
   __device__ inline float get(int e) const {
     uint32_t x = w[e >> 1];
@@ -198,8 +244,8 @@ template <> struct In8<float> {
     w1 = ld16(p + 4);
   }
   __device__ inline void load_buf(Rsrc r, uint32_t byte_off) {
-    w0 = buf_ld16(r, byte_off);
-    w1 = buf_ld16(r, byte_off == kOutOfRange ? kOutOfRange : byte_off + 16u);
+    w0 = buf_ld16_stream(r, byte_off);
+    w1 = buf_ld16_stream(r, byte_off == kOutOfRange ? kOutOfRange : byte_off + 16u);
   }
   __device__ inline void zero() {
     w0 = u32x4_t{0u, 0u, 0u, 0u};

@@ -46,7 +46,9 @@ struct mhla_plan {
   int32_t sum_splits, sum_tok;
   int32_t rd_splits, rd_tok;
   // workspace layout (byte offsets)
-  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_ubar, ws_bytes;
+  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_ubar, off_mcf, ws_bytes;
+  mhla::MixShape mix;   // MFMA mixing launch shape (mix_mfma only)
+  int mcf_heads;
   // timing
   bool timing;
   std::vector<TimedLaunch> timed;
@@ -172,6 +174,11 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   P->off_st_lo = off; off = align256(off + (P->split ? (size_t)BH * M * f * 2 : 0));
   P->off_zt = off;   off = align256(off + (size_t)BH * M * dd * 4);
   P->off_ubar = off; off = align256(off + (P->mala ? (size_t)BH * dd * 4 : 0));
+  // bf16 M_c operand fragments for the MFMA mixing kernel
+  P->mcf_heads = d->mc_per_head ? (int)d->heads : 1;
+  P->mix = mhla::mix_shape((int)M);
+  P->off_mcf = off;
+  off = align256(off + (P->mix_mfma ? (size_t)P->mcf_heads * P->mix.nitp * P->mix.nbc * 512 * 2 : 0));
   P->ws_bytes = off;
 
   P->timing = false;
@@ -270,6 +277,12 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.splits = h->sum_splits;
     sp.tok_per_split = h->sum_tok;
     sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
+    sp.mc = mc;
+    sp.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+    sp.mcf = h->mix_mfma ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
+    sp.mcf_heads = h->mcf_heads;
+    sp.mcf_nitp = h->mix.nitp;
+    sp.mcf_nbc = h->mix.nbc;
     hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
                                         h->mix_mfma, (int)(h->sum_splits * h->M * h->BH), s);
     if (e != hipSuccess) return MHLA_ERR_HIP;
@@ -279,8 +292,8 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
       mhla::MixMfmaParams mm;
       mm.x = reinterpret_cast<const uint16_t*>(ws + h->off_sb);
       mm.z = pz;
-      mm.mc = mc;
-      mm.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+      mm.mcf = reinterpret_cast<const uint16_t*>(ws + h->off_mcf);
+      mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
       mm.y = st_hi;
       mm.zt = zt;
       mm.M = (int32_t)h->M;

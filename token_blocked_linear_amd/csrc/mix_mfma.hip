@@ -22,7 +22,8 @@ namespace mhla {
 
 // NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave.
 template <int NBC, int ITW>
-__global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mix_mfma_kernel(
+    MixMfmaParams p) {
   constexpr int MPAD = 32 * NBC;
   constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
   constexpr int NPT = PB / 16;            // 16-column MFMA tiles per staged tile
@@ -43,9 +44,6 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
   const int pr = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.z;
   const int M = p.M;
-  // NULL M_c is accepted for M == 1: the single coefficient is 1
-  const float* mc = p.mc ? p.mc + (int64_t)(bh % p.H) * p.mc_head_stride : nullptr;
-
   // ---------------- wave roles -------------------------------------------------------------
   // `wave_rows` waves split the workgroup's i-tiles; the remaining factor splits columns.
   const int WI = p.wave_rows;
@@ -53,23 +51,17 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
   const int wi = wave % WI, wp = wave / WI;
   const int it0 = (blockIdx.y * WI + wi) * ITW;     // first i-tile of this wave
   const int nit = (M + 15) >> 4;
+  const int nitp = gridDim.y * WI * ITW;
 
-  // M_c^T operand fragments: lane holds M_c[16*it + pr][32*bc + 8*lg + e], e = 0..7.
+  // M_c^T operand fragments (converted to bf16 by the summary kernel): lane holds
+  // M_c[16*it + pr][32*bc + 8*lg + e], e = 0..7, one 16-byte load each.
+  const uint16_t* mcf = p.mcf + (int64_t)(p.mcf_per_head ? bh % p.H : 0) * nitp * NBC * 512;
   u32x4_t bfrag[ITW][NBC];
 #pragma unroll
   for (int a = 0; a < ITW; ++a)
 #pragma unroll
-    for (int bc = 0; bc < NBC; ++bc) {
-      const int i = 16 * (it0 + a) + pr;
-      float m[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int b = 32 * bc + 8 * lg + e;
-        m[e] = (i < M && b < M) ? (mc ? mc[(int64_t)i * M + b] : 1.0f) : 0.f;
-      }
-      bfrag[a][bc] = u32x4_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]),
-                             pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7])};
-    }
+    for (int bc = 0; bc < NBC; ++bc)
+      bfrag[a][bc] = ld16(mcf + (((int64_t)(it0 + a) * NBC + bc) * 64 + lane) * 8);
 
   const int P = p.frag;
   const int n_tiles = P / PB;
@@ -139,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void mix_mfma_kernel(MixMfmaParams p) {
     const bool ztile = tile >= n_tiles;
     const int zbase = (tile - n_tiles) * (PB / 2);
 
+#pragma unroll 1
     for (int pt = wp; pt < NPT; pt += WPW) {
       f32x4_t accs[ITW];
 #pragma unroll
@@ -182,34 +175,25 @@ static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipSt
   return hipGetLastError();
 }
 
-// Chooses the contraction padding, rows per wave and the wave split from M.
+// Launch with the shape mix_shape(M) (the host sized the M_c fragments with the same shape).
 hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream) {
   const int M = p.M;
   if (M < 1 || M > 256) return hipErrorInvalidValue;
-  const int nbc = (M + 31) / 32;
-  const int NBC = nbc <= 1 ? 1 : nbc <= 2 ? 2 : nbc <= 4 ? 4 : 8;
-  const int nit = (M + 15) / 16;
-  // i-tiles per wave: at most 4 (register budget), all rows in one workgroup when possible
-  const int itw = nit <= 4 ? 1 : (nit + 3) / 4;
-  const int ITW = itw <= 1 ? 1 : 2;   // beyond 128 rows a second row group shares the tile
-  int wave_rows = 4;
-  while (wave_rows > 1 && (wave_rows / 2) * ITW >= nit) wave_rows /= 2;
-  p.wave_rows = wave_rows;
-  const int rows_per_wg = wave_rows * ITW * 16;
-  const int row_groups = (M + rows_per_wg - 1) / rows_per_wg;
+  const MixShape sh = mix_shape(M);
+  const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups;
+  p.wave_rows = sh.wave_rows;
   const int pb = 16384 / (32 * NBC);
   const int n_tiles = p.frag / pb;
   if (p.frag % pb != 0) return hipErrorInvalidValue;
   const int n_all = n_tiles + (2 * p.D + pb - 1) / pb;     // summary tiles + normaliser tiles
-  // about two workgroups per CU across all heads: each converts its M_c rows once and then
-  // strides over many column tiles
+  // about two workgroups per CU across all heads, each striding over many column tiles
   int want = (512 + bh * row_groups - 1) / (bh * row_groups);
   if (want > n_all) want = n_all;
   if (want < 1) want = 1;
   p.n_wg_x = want;
 #define MHLA_MIX_CASE(N, I) \
   if (NBC == N && ITW == I) return launch_t<N, I>(p, row_groups, bh, stream);
-  MHLA_MIX_CASE(1, 1) MHLA_MIX_CASE(2, 1) MHLA_MIX_CASE(4, 2) MHLA_MIX_CASE(8, 2)
+  MHLA_MIX_CASE(1, 1) MHLA_MIX_CASE(2, 1) MHLA_MIX_CASE(4, 2) MHLA_MIX_CASE(8, 4)
 #undef MHLA_MIX_CASE
   return hipErrorInvalidValue;
 }

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
       }
       const int64_t dst = coff + 16 * ct + 4 * lg;
       if constexpr (sizeof(TOut) == 4) {
-        st16(reinterpret_cast<float*>(p.o) + dst,
+        st16_stream(reinterpret_cast<float*>(p.o) + dst,
              u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                      __float_as_uint(o[3])});
       } else {

@@ -66,6 +66,29 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
     }
   }
 
+  // ---- side job: bf16 operand fragments of M_c for the MFMA mixing kernel -----------------
+  if (p.mcf) {
+    const int nitp = p.mcf_nitp, nbc = p.mcf_nbc, M = g.M;
+    const int total = p.mcf_heads * nitp * nbc * 64;      // lane fragments of 8 elements
+    for (int idx = blockIdx.x * kThreads + tid; idx < total; idx += gridDim.x * kThreads) {
+      const int l = idx & 63;
+      int t = idx >> 6;
+      const int bc = t % nbc;
+      t /= nbc;
+      const int it = t % nitp, hh = t / nitp;
+      const int i = 16 * it + (l & 15);
+      const float* row = p.mc ? p.mc + (int64_t)hh * p.mc_head_stride + (int64_t)i * M : nullptr;
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int b = 32 * bc + 8 * (l >> 4) + e;
+        m[e] = (i < M && b < M) ? (row ? row[b] : 1.0f) : 0.f;   // NULL M_c (M == 1): [1]
+      }
+      st16(p.mcf + (int64_t)idx * 8, u32x4_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]),
+                                             pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7])});
+    }
+  }
+
   // ---- unit bookkeeping --------------------------------------------------------------------
   struct Unit {
     int split, blk, bh;
