@@ -44,8 +44,12 @@ def kernel_accounting(w: synth.Workload, out_bytes: int):
         acc["mix"] = dict(bytes=0, flops=BH * 2 * d * d, bound="alu")
     else:
         acc["mix"] = dict(bytes=M * M * 4, flops=BH * 2 * M * M * (d * d + d), bound="alu")
+    # mixing step run in the readout's prologue: its inputs are summaries (not algorithmic),
+    # so the fused kernel carries the readout's bytes plus M_c
+    acc["mix+readout"] = dict(bytes=acc["readout"]["bytes"] + acc["mix"]["bytes"],
+                              flops=acc["readout"]["flops"] + acc["mix"]["flops"], bound="hbm")
     total_bytes = tok * d * (3 * in_b + out_bytes) + (0 if w.readout == "mala" else M * M * 4)
-    total_flops = sum(a["flops"] for a in acc.values())
+    total_flops = acc["summary"]["flops"] + acc["mix+readout"]["flops"]
     return acc, total_bytes, total_flops
 
 

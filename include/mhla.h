@@ -101,7 +101,9 @@ typedef struct {
   int64_t workspace_bytes;  /* same as mhla_workspace_size                                     */
   int32_t summary_splits;   /* token slices per block in the summary kernel                    */
   int32_t readout_splits;   /* token slices per block in the readout kernel                    */
-  int32_t n_kernels;        /* kernels launched per mhla_forward                               */
+  int32_t n_kernels;        /* kernels launched per mhla_forward: 3 (summary, mix, readout),   */
+                            /* or 2 (summary, mix+readout) when the mixing step runs in the    */
+                            /* readout's prologue: MALA readout, or at most 16 blocks          */
   int32_t split_operands;   /* 1 if hi/lo operand splitting is in use                          */
 } mhla_plan_info;
 

@@ -110,14 +110,18 @@ def test_plan_info_and_workspace():
     p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
     info = p.info
     assert (info.n_tokens, info.n_blocks, info.block_tokens) == (4096, 16, 256)
-    assert info.n_kernels == 3 and info.summary_splits >= 1 and info.readout_splits >= 1
+    # 16 blocks: the mixing step runs in the readout's prologue
+    assert info.n_kernels == 2 and info.summary_splits >= 1 and info.readout_splits >= 1
     assert p.workspace_bytes == info.workspace_bytes > 0
     assert info.split_operands == 0
     pm = T.Plan(grid=(64, 64), block=(64, 64), batch=16, heads=8, head_dim=64, readout="mala")
     assert pm.info.n_blocks == 1 and pm.info.split_operands == 1 and pm.info.summary_splits > 1
     p32 = T.Plan(grid=(8, 8), block=(4, 4), batch=1, heads=1, head_dim=16, in_dtype="fp32")
     assert p32.info.split_operands == 1
-    for q in (p, pm, p32):
+    assert pm.info.n_kernels == 2
+    p3 = T.Plan(grid=(128, 128), block=(16, 16), batch=2, heads=4, head_dim=64)
+    assert p3.info.n_blocks == 64 and p3.info.n_kernels == 3
+    for q in (p, pm, p32, p3):
         q.close()
 
 
@@ -150,15 +154,21 @@ def test_status_strings():
 
 def test_timing_api_without_launches():
     _lib_or_skip()
-    p = T.Plan(grid=(64,), block=(16,), batch=1, heads=1, head_dim=32)
+    p = T.Plan(grid=(1024,), block=(16,), batch=1, heads=1, head_dim=32)     # 64 blocks
     T.mhla_timing_enable(p.handle, True)
     name, ms, n = T.mhla_timing_read(p.handle, 0)
     assert (name, ms, n) == ("summary", 0.0, 0)
+    assert T.mhla_timing_read(p.handle, 1)[0] == "mix"
     assert T.mhla_timing_read(p.handle, 2)[0] == "readout"
     with pytest.raises(T.MhlaError):
         T.mhla_timing_read(p.handle, 3)
     T.mhla_timing_reset(p.handle)
     p.close()
+    f = T.Plan(grid=(64,), block=(16,), batch=1, heads=1, head_dim=32)       # 4 blocks: fused
+    assert [T.mhla_timing_read(f.handle, i)[0] for i in range(2)] == ["summary", "mix+readout"]
+    with pytest.raises(T.MhlaError):
+        T.mhla_timing_read(f.handle, 2)
+    f.close()
 
 
 def test_fastdiv_exhaustive_on_host(tmp_path):

@@ -118,8 +118,7 @@ struct MixParams {
   int64_t mc_head_stride;  // 0 or M*M
   uint16_t* st_hi;         // mixed summaries, bf16 bits [BH][M][FRAG]
   uint16_t* st_lo;         // low parts (split accuracy) or nullptr
-  float* zt;               // mixed normaliser [BH][M][D]; MALA: z
-  float* ubar;             // MALA: mean of V [BH][D]
+  float* zt;               // mixed normaliser [BH][M][D]
   int32_t M;
   int32_t splits;
   int32_t H;
@@ -146,13 +145,23 @@ struct MixMfmaParams {
 struct ReadoutParams {
   const void* q;           // [BH][N][D] of the input dtype
   void* o;                 // [BH][N][D] of the output dtype
-  const uint16_t* st_hi;
+  const uint16_t* st_hi;   // mixed summaries from the mixing kernel (not fused)
   const uint16_t* st_lo;
   const float* zt;
-  const float* ubar;
   Geom g;
   int32_t splits;          // token slices per query block
   int32_t tok_per_split;
+  int32_t BH;
+  int32_t xcd_map;         // 1: all workgroups of a head on one XCD (BH % 8 == 0)
+  // inputs of a mixing step fused into the prologue
+  const uint16_t* sb;      // bf16 summary stack [BH][M][FRAG]                 (bf16 fusion)
+  const float* ps;         // fp32 partial summaries [BH][M][ssplits][FRAG]     (partials fusion)
+  const float* pz;         // normaliser partials [BH][M][ssplits][D]
+  const float* pu;         // sum of V partials   [BH][M][ssplits][D]           (MALA)
+  const float* mc;         // fp32 [M][M] or [H][M][M]; NULL when M == 1
+  int64_t mc_head_stride;
+  int32_t H;
+  int32_t ssplits;         // token slices of the summary kernel
 };
 
 // ---------------------------------------------------------------------------------------

@@ -16,20 +16,25 @@
 namespace mhla {
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
                           bool want_u, bool out_bf16, int n_units, hipStream_t stream);
-hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool mala, bool split,
-                      hipStream_t stream);
+hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream);
 hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
-                          bool split, dim3 grid, hipStream_t stream);
+                          bool split, int fuse, int n_wg, hipStream_t stream);
 }  // namespace mhla
 
 namespace {
 
-constexpr int kNumKernels = 3;
-const char* const kKernelNames[kNumKernels] = {"summary", "mix", "readout"};
+constexpr int kMaxKernels = 3;
+
+// Mixing step placement: a separate kernel, or the readout's prologue (few blocks).
+enum { kFuseNone = 0, kFuseBf16 = 1, kFusePartials = 2 };
+#ifndef MHLA_FUSE_MAX_BLOCKS
+#define MHLA_FUSE_MAX_BLOCKS 16
+#endif
+constexpr int kFuseMaxBlocks = MHLA_FUSE_MAX_BLOCKS;
 
 struct TimedLaunch {
-  hipEvent_t ev[kNumKernels + 1];
+  hipEvent_t ev[kMaxKernels + 1];
 };
 
 }  // namespace
@@ -40,13 +45,16 @@ struct mhla_plan {
   int64_t B, H, BH, N, M, n_b;
   mhla::Geom geom;
   bool in_fp32, out_fp32, mala, split, split_v;
-  bool mix_mfma;   // bf16 summary stack mixed on MFMA (else fp32 partials mixed on VALU)
+  bool mix_mfma;   // bf16 summary stack (mixed on MFMA or in the readout prologue)
+  int fuse;        // kFuse*: where the mixing step runs
+  int n_kernels;
+  const char* kernel_names[kMaxKernels];
   int mode;
   int frag;
   int32_t sum_splits, sum_tok;
   int32_t rd_splits, rd_tok;
   // workspace layout (byte offsets)
-  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_ubar, off_mcf, ws_bytes;
+  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_mcf, ws_bytes;
   mhla::MixShape mix;   // MFMA mixing launch shape (mix_mfma only)
   int mcf_heads;
   // timing
@@ -158,9 +166,19 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
     P->rd_tok = (int32_t)tok;
   }
 
-  // Mixing path: a bf16 stack on MFMA when the summaries come from one token slice with bf16
-  // operands (the bf16 accuracy level); otherwise fp32 partials reduced and mixed on VALU.
+  // Summary output: a bf16 stack when one token slice covers a block with bf16 operands (the
+  // bf16 accuracy level); otherwise fp32 partials per token slice.
   P->mix_mfma = !P->split && !P->mala && !P->in_fp32 && P->sum_splits == 1 && M <= 256;
+  // Mixing step: in the readout's prologue for MALA (the centring) and for few blocks; else a
+  // kernel of its own (MFMA for the bf16 stack, VALU for fp32 partials).
+  if (P->mala) P->fuse = kFusePartials;
+  else if (M <= kFuseMaxBlocks) P->fuse = P->mix_mfma ? kFuseBf16 : kFusePartials;
+  else P->fuse = kFuseNone;
+  const bool mix_kernel = P->fuse == kFuseNone;
+  P->n_kernels = 0;
+  P->kernel_names[P->n_kernels++] = "summary";
+  if (mix_kernel) P->kernel_names[P->n_kernels++] = "mix";
+  P->kernel_names[P->n_kernels++] = mix_kernel ? "readout" : "mix+readout";
 
   // Workspace layout.
   const size_t f = (size_t)P->frag, dd = (size_t)P->d;
@@ -170,16 +188,17 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   P->off_ps = off;   off = align256(off + (P->mix_mfma ? 0 : slots * f * 4));
   P->off_pz = off;   off = align256(off + slots * dd * 4);
   P->off_pu = off;   off = align256(off + (P->mala ? slots * dd * 4 : 0));
-  P->off_st_hi = off; off = align256(off + (size_t)BH * M * f * 2);
-  P->off_st_lo = off; off = align256(off + (P->split ? (size_t)BH * M * f * 2 : 0));
-  P->off_zt = off;   off = align256(off + (size_t)BH * M * dd * 4);
-  P->off_ubar = off; off = align256(off + (P->mala ? (size_t)BH * dd * 4 : 0));
+  P->off_st_hi = off; off = align256(off + (mix_kernel ? (size_t)BH * M * f * 2 : 0));
+  P->off_st_lo = off; off = align256(off + (mix_kernel && P->split ? (size_t)BH * M * f * 2 : 0));
+  P->off_zt = off;   off = align256(off + (mix_kernel ? (size_t)BH * M * dd * 4 : 0));
   // bf16 M_c operand fragments for the MFMA mixing kernel
   P->mcf_heads = d->mc_per_head ? (int)d->heads : 1;
   P->mix = mhla::mix_shape((int)M);
   P->off_mcf = off;
-  off = align256(off + (P->mix_mfma ? (size_t)P->mcf_heads * P->mix.nitp * P->mix.nbc * 512 * 2 : 0));
+  const bool mcf = mix_kernel && P->mix_mfma;
+  off = align256(off + (mcf ? (size_t)P->mcf_heads * P->mix.nitp * P->mix.nbc * 512 * 2 : 0));
   P->ws_bytes = off;
+  if (BH * M * P->rd_splits >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
 
   P->timing = false;
   P->timed_used = 0;
@@ -228,7 +247,7 @@ mhla_status mhla_plan_get_info(mhla_handle h, mhla_plan_info* info) {
   info->workspace_bytes = (int64_t)h->ws_bytes;
   info->summary_splits = h->sum_splits;
   info->readout_splits = h->rd_splits;
-  info->n_kernels = kNumKernels;
+  info->n_kernels = h->n_kernels;
   info->split_operands = h->split ? 1 : 0;
   return MHLA_OK;
 }
@@ -253,75 +272,78 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     uint16_t* st_hi = reinterpret_cast<uint16_t*>(ws + h->off_st_hi);
     uint16_t* st_lo = h->split ? reinterpret_cast<uint16_t*>(ws + h->off_st_lo) : nullptr;
     float* zt = reinterpret_cast<float*>(ws + h->off_zt);
-    float* ubar = h->mala ? reinterpret_cast<float*>(ws + h->off_ubar) : nullptr;
-
+    // one event before the first kernel and one after each kernel (timing enabled)
     TimedLaunch* tl = nullptr;
+    int ev_i = 0;
     if (h->timing) {
       if (h->timed_used == h->timed.size()) {
         TimedLaunch t;
-        for (int i = 0; i <= kNumKernels; ++i)
+        for (int i = 0; i <= kMaxKernels; ++i)
           if (hipEventCreate(&t.ev[i]) != hipSuccess) return MHLA_ERR_HIP;
         h->timed.push_back(t);
       }
       tl = &h->timed[h->timed_used++];
-      if (hipEventRecord(tl->ev[0], s) != hipSuccess) return MHLA_ERR_HIP;
+      if (hipEventRecord(tl->ev[ev_i++], s) != hipSuccess) return MHLA_ERR_HIP;
     }
+    auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[ev_i++], s) == hipSuccess; };
+
+    const bool mix_kernel = h->fuse == kFuseNone;
+    const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
 
     mhla::SummaryParams sp;
     sp.k = k;
     sp.v = v;
+    sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
     sp.ps = ps;
     sp.pz = pz;
     sp.pu = pu;
     sp.g = h->geom;
     sp.splits = h->sum_splits;
     sp.tok_per_split = h->sum_tok;
-    sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
     sp.mc = mc;
-    sp.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
-    sp.mcf = h->mix_mfma ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
+    sp.mc_head_stride = mc_stride;
+    sp.mcf = (mix_kernel && h->mix_mfma) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
     sp.mcf_heads = h->mcf_heads;
     sp.mcf_nitp = h->mix.nitp;
     sp.mcf_nbc = h->mix.nbc;
     hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
                                         h->mix_mfma, (int)(h->sum_splits * h->M * h->BH), s);
-    if (e != hipSuccess) return MHLA_ERR_HIP;
-    if (tl && hipEventRecord(tl->ev[1], s) != hipSuccess) return MHLA_ERR_HIP;
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
-    if (h->mix_mfma) {
-      mhla::MixMfmaParams mm;
-      mm.x = reinterpret_cast<const uint16_t*>(ws + h->off_sb);
-      mm.z = pz;
-      mm.mcf = reinterpret_cast<const uint16_t*>(ws + h->off_mcf);
-      mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
-      mm.y = st_hi;
-      mm.zt = zt;
-      mm.M = (int32_t)h->M;
-      mm.H = (int32_t)h->H;
-      mm.D = h->d;
-      mm.frag = h->frag;
-      mm.n_wg_x = 0;
-      mm.wave_rows = 0;
-      e = mhla::launch_mix_mfma(mm, (int)h->BH, s);
+    if (mix_kernel) {
+      if (h->mix_mfma) {
+        mhla::MixMfmaParams mm;
+        mm.x = sp.sb;
+        mm.z = pz;
+        mm.mcf = reinterpret_cast<const uint16_t*>(ws + h->off_mcf);
+        mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
+        mm.y = st_hi;
+        mm.zt = zt;
+        mm.M = (int32_t)h->M;
+        mm.H = (int32_t)h->H;
+        mm.D = h->d;
+        mm.frag = h->frag;
+        mm.n_wg_x = 0;
+        mm.wave_rows = 0;
+        e = mhla::launch_mix_mfma(mm, (int)h->BH, s);
+      } else {
+        mhla::MixParams mp;
+        mp.ps = ps;
+        mp.pz = pz;
+        mp.pu = pu;
+        mp.mc = mc;          // NULL only when M == 1: the kernel then uses the weight 1
+        mp.mc_head_stride = mc_stride;
+        mp.st_hi = st_hi;
+        mp.st_lo = st_lo;
+        mp.zt = zt;
+        mp.M = (int32_t)h->M;
+        mp.splits = h->sum_splits;
+        mp.H = (int32_t)h->H;
+        mp.N = (int32_t)h->N;
+        e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->split, s);
+      }
+      if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
     }
-    mhla::MixParams mp;
-    mp.ps = ps;
-    mp.pz = pz;
-    mp.pu = pu;
-    mp.mc = mc;
-    mp.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
-    mp.st_hi = st_hi;
-    mp.st_lo = st_lo;
-    mp.zt = zt;
-    mp.ubar = ubar;
-    mp.M = (int32_t)h->M;
-    mp.splits = h->sum_splits;
-    mp.H = (int32_t)h->H;
-    mp.N = (int32_t)h->N;
-    // mc == NULL is only accepted for M == 1; the mixing kernel then uses the weight 1.
-    if (!h->mix_mfma) e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->mala, h->split, s);
-    if (e != hipSuccess) return MHLA_ERR_HIP;
-    if (tl && hipEventRecord(tl->ev[2], s) != hipSuccess) return MHLA_ERR_HIP;
 
     mhla::ReadoutParams rp;
     rp.q = q;
@@ -329,14 +351,22 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     rp.st_hi = st_hi;
     rp.st_lo = st_lo;
     rp.zt = zt;
-    rp.ubar = ubar;
     rp.g = h->geom;
     rp.splits = h->rd_splits;
     rp.tok_per_split = h->rd_tok;
-    e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split,
-                             dim3(h->rd_splits, (unsigned)h->M, (unsigned)h->BH), s);
-    if (e != hipSuccess) return MHLA_ERR_HIP;
-    if (tl && hipEventRecord(tl->ev[3], s) != hipSuccess) return MHLA_ERR_HIP;
+    rp.BH = (int32_t)h->BH;
+    rp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
+    rp.sb = sp.sb;
+    rp.ps = ps;
+    rp.pz = pz;
+    rp.pu = pu;
+    rp.mc = mc;
+    rp.mc_head_stride = mc_stride;
+    rp.H = (int32_t)h->H;
+    rp.ssplits = h->sum_splits;
+    e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse,
+                             (int)(h->rd_splits * h->M * h->BH), s);
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
     return MHLA_OK;
   } catch (...) {
     return MHLA_ERR_INTERNAL;
@@ -346,7 +376,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
 mhla_status mhla_destroy(mhla_handle h) {
   if (!h) return MHLA_OK;
   for (auto& t : h->timed)
-    for (int i = 0; i <= kNumKernels; ++i) (void)hipEventDestroy(t.ev[i]);
+    for (int i = 0; i <= kMaxKernels; ++i) (void)hipEventDestroy(t.ev[i]);
   delete h;
   return MHLA_OK;
 }
@@ -372,11 +402,11 @@ mhla_status mhla_timing_enable(mhla_handle h, int enable) {
 
 mhla_status mhla_timing_read(mhla_handle h, int index, double* total_ms, int64_t* launches,
                              const char** name) {
-  if (!h || index < 0 || index >= kNumKernels) return MHLA_ERR_INVALID_ARG;
-  if (name) *name = kKernelNames[index];
+  if (!h || index < 0 || index >= h->n_kernels) return MHLA_ERR_INVALID_ARG;
+  if (name) *name = h->kernel_names[index];
   double sum = 0.0;
   if (h->timed_used > 0) {
-    if (hipEventSynchronize(h->timed[h->timed_used - 1].ev[kNumKernels]) != hipSuccess)
+    if (hipEventSynchronize(h->timed[h->timed_used - 1].ev[h->n_kernels]) != hipSuccess)
       return MHLA_ERR_HIP;
     for (size_t i = 0; i < h->timed_used; ++i) {
       float ms = 0.f;

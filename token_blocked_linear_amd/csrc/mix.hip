@@ -3,11 +3,8 @@
 // ("MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head", Method ->
 // Key design 2, multi-head mixing; row i of M_c belongs to query block i).
 //
-// MALA mode (one block; "Rectifying Magnitude Neglect in Linear Attention", Method -> Key
-// design, linear form Y_i = beta_i phi(Q_i) S - gamma_i u with S = sum_j phi(K_j)^T V_j,
-// u = sum_j V_j, beta_i = 1 + 1/s_i, gamma_i = s_i/N, s_i = phi(Q_i) z):  substituting
-// S = C + z u^T / N gives Y_i = u/N + beta_i phi(Q_i) C exactly, with C = S - z u^T / N.
-// C is formed here in fp32, so the readout never subtracts two large, nearly equal terms.
+// This VALU kernel serves the fp32-partials path (split accuracy, fp32 inputs) when there are
+// too many blocks for the readout to mix in its prologue.
 //
 // Every output element is a fixed-order fp32 sum (deterministic).  The result is written
 // in the fragment layout as bf16 (hi) and, for split accuracy, the bf16 residual (lo).
@@ -67,60 +64,14 @@ __global__ __launch_bounds__(kThreads) void mix_kernel(MixParams p, int frag, in
   }
 }
 
-// MALA (M == 1): grid (ceil((FRAG + D) / 256), 1, BH).
-template <bool SPLIT>
-__global__ __launch_bounds__(kThreads) void mala_center_kernel(MixParams p, int frag, int d) {
-  const int pos = blockIdx.x * kThreads + threadIdx.x;
-  if (pos >= frag + d) return;
-  const int bh = blockIdx.z;
-  const int64_t slot0 = (int64_t)bh * p.splits;
-  const float inv_n = 1.0f / (float)p.N;
-  if (pos >= frag) {
-    const int c = pos - frag;
-    float z = 0.f, u = 0.f;
-    for (int sp = 0; sp < p.splits; ++sp) {
-      z += p.pz[(slot0 + sp) * d + c];
-      u += p.pu[(slot0 + sp) * d + c];
-    }
-    p.zt[(int64_t)bh * d + c] = z;
-    p.ubar[(int64_t)bh * d + c] = u * inv_n;
-    return;
-  }
-  // fragment position -> (k, c)
-  const int e = pos & 7;
-  const int lane = (pos >> 3) & 63;
-  const int fr = pos >> 9;
-  const int nct = d / 16;
-  const int kc = fr / nct, ct = fr % nct;
-  const int k = 32 * kc + 8 * (lane >> 4) + e;
-  const int c = 16 * ct + (lane & 15);
-  float s = 0.f, z = 0.f, u = 0.f;
-  for (int sp = 0; sp < p.splits; ++sp) {
-    s += p.ps[(slot0 + sp) * frag + pos];
-    if (k < d) z += p.pz[(slot0 + sp) * d + k];
-    u += p.pu[(slot0 + sp) * d + c];
-  }
-  const float cval = s - z * u * inv_n;
-  store_hi_lo<SPLIT>(p.st_hi, p.st_lo, (int64_t)bh * frag + pos, cval);
-}
-
-hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool mala, bool split,
-                      hipStream_t stream) {
+hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream) {
   const dim3 block(kThreads);
   const int nx = (frag + d + kThreads - 1) / kThreads;
-  if (mala) {
-    const dim3 grid(nx, 1, bh);
-    if (split)
-      hipLaunchKernelGGL(mala_center_kernel<true>, grid, block, 0, stream, p, frag, d);
-    else
-      hipLaunchKernelGGL(mala_center_kernel<false>, grid, block, 0, stream, p, frag, d);
-  } else {
-    const dim3 grid(nx, (p.M + kMixRows - 1) / kMixRows, bh);
-    if (split)
-      hipLaunchKernelGGL(mix_kernel<true>, grid, block, 0, stream, p, frag, d);
-    else
-      hipLaunchKernelGGL(mix_kernel<false>, grid, block, 0, stream, p, frag, d);
-  }
+  const dim3 grid(nx, (p.M + kMixRows - 1) / kMixRows, bh);
+  if (split)
+    hipLaunchKernelGGL(mix_kernel<true>, grid, block, 0, stream, p, frag, d);
+  else
+    hipLaunchKernelGGL(mix_kernel<false>, grid, block, 0, stream, p, frag, d);
   return hipGetLastError();
 }
 

@@ -10,7 +10,11 @@
 //             transpose, like the summary kernel);
 //   B = M_c^T 32 blocks x 16 query blocks, converted to bf16 once per workgroup and held in
 //             registers for its lifetime;
-//   D         lane (g, l) holds Y[i = 16*it + l][p .. p+3] -> one 8-byte store.
+//   D         16 positions x 16 query blocks.
+// The columns are taken 32 at a time as two MFMA tiles pt = 0, 1 whose 16 A rows are the
+// positions 8*(m/4) + 4*pt + m%4, m = 0..15.  Over the two tiles lane (g, l) then holds the 8
+// consecutive positions 8g .. 8g+7 of row i = 16*it + l: one 16-byte store, and the four lane
+// groups of a row write 64 contiguous bytes.
 // The contraction over blocks is padded to a multiple of 32 with zero rows.  The normaliser
 // rides along as one extra column tile: z_b enters as interleaved bf16 (hi, lo) column pairs
 // (z = hi + lo to about 2^-17) and leaves as fp32 z~ = Y[hi col] + Y[lo col], so numerator and
@@ -26,7 +30,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     MixMfmaParams p) {
   constexpr int MPAD = 32 * NBC;
   constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
-  constexpr int NPT = PB / 16;            // 16-column MFMA tiles per staged tile
+  constexpr int NCG = PB / 32;            // 32-column groups per staged tile
   constexpr int XP = MPAD;                // LDS pitch (elements) of one transposed column
   constexpr int CG = PB / 8;              // 8-column groups per tile
   // LDS bank swizzle on the 16-byte chunks (8 blocks) of a transposed column r: columns are
@@ -85,14 +89,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int D = p.D;
   const int n_ztiles = (2 * D + PB - 1) / PB;
   const int last = n_tiles + n_ztiles;            // one past the last tile
-  const float* zsrc = p.z + (int64_t)bh * M * D;
+  // z of this head through a buffer resource (32-bit offsets; rows b >= M read as zero)
+  const Rsrc rsz = make_rsrc(p.z + (int64_t)bh * M * D, (uint32_t)M * D * 4u);
   auto issue_z = [&](int zj) {
+    const int c0 = zj * (PB / 2) + 4 * cg;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int b = 8 * rg + r;
-      const int c0 = zj * (PB / 2) + 4 * cg;
-      if (b < M && c0 < D) {
-        const u32x4_t zz = ld16(zsrc + (int64_t)b * D + c0);
+      if (c0 < D) {
+        const u32x4_t zz = buf_ld16(rsz, b < M ? (uint32_t)(b * D + c0) * 4u : kOutOfRange);
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -127,36 +132,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       *reinterpret_cast<u32x4_t*>(xt + r * XP + 8 * swz(r, rg)) = col;
     }
     __syncthreads();
-    if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);
+    if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);   // in flight during the MFMAs
     const bool ztile = tile >= n_tiles;
     const int zbase = (tile - n_tiles) * (PB / 2);
 
 #pragma unroll 1
-    for (int pt = wp; pt < NPT; pt += WPW) {
-      f32x4_t accs[ITW];
+    for (int cgp = wp; cgp < NCG; cgp += WPW) {
+      f32x4_t accs[2][ITW];
 #pragma unroll
-      for (int a = 0; a < ITW; ++a) accs[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-      for (int bc = 0; bc < NBC; ++bc) {
-        const int r = 16 * pt + pr;
-        const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + r * XP + 8 * swz(r, 4 * bc + lg));
+        for (int a = 0; a < ITW; ++a) accs[pt][a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int a = 0; a < ITW; ++a) accs[a] = mfma_bf16(afrag, bfrag[a][bc], accs[a]);
-      }
+      for (int bc = 0; bc < NBC; ++bc)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
+          const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + r * XP + 8 * swz(r, 4 * bc + lg));
+#pragma unroll
+          for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag[a][bc], accs[pt][a]);
+          // with 128 registers of M_c fragments, keep each operand read next to its MFMAs
+          if constexpr (NBC * ITW >= 32) __builtin_amdgcn_sched_barrier(0);
+        }
+      const int q = 32 * cgp + 8 * lg;         // first of this lane's 8 tile columns
 #pragma unroll
       for (int a = 0; a < ITW; ++a) {
         if (it0 + a >= nit) break;
-        const f32x4_t acc = accs[a];
         const int i = 16 * (it0 + a) + pr;
-        const int q = 16 * pt + 4 * lg;
-        if (i < M && !ztile) {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)i * P + (int64_t)tile * PB + q);
-          dst[0] = pack_bf16x2(acc[0], acc[1]);
-          dst[1] = pack_bf16x2(acc[2], acc[3]);
-        } else if (i < M && ztile && zbase + q / 2 < D) {
-          float* zd = p.zt + ((int64_t)bh * M + i) * D + zbase + q / 2;
-          zd[0] = acc[0] + acc[1];
-          zd[1] = acc[2] + acc[3];
+        if (i >= M) continue;
+        const f32x4_t c0 = accs[0][a], c1 = accs[1][a];
+        if (!ztile) {
+          st16(y + (int64_t)i * P + (int64_t)tile * PB + q,
+               u32x4_t{pack_bf16x2(c0[0], c0[1]), pack_bf16x2(c0[2], c0[3]),
+                       pack_bf16x2(c1[0], c1[1]), pack_bf16x2(c1[2], c1[3])});
+        } else if (zbase + q / 2 < D) {
+          // columns 2c, 2c+1 are hi, lo of z index zbase + c: four consecutive z~ values
+          st16(p.zt + ((int64_t)bh * M + i) * D + zbase + q / 2,
+               u32x4_t{__float_as_uint(c0[0] + c0[1]), __float_as_uint(c0[2] + c0[3]),
+                       __float_as_uint(c1[0] + c1[1]), __float_as_uint(c1[2] + c1[3])});
         }
       }
     }

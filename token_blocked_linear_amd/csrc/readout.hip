@@ -3,27 +3,51 @@
 //   unnormalised  o_t = phi(q_t)^T S~_i
 //   MALA          o_t = u/N + (1 + 1/s_t) phi(q_t)^T C,   s_t = phi(q_t)^T z
 // Sources: "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head",
-// Method -> Overall framework (flowchart readout) and Key design 2 (the normaliser may be
-// dropped); "Rectifying Magnitude Neglect in Linear Attention", Method -> Key design (beta,
-// gamma and the linear form; the centred summary C is formed by the mixing kernel).
+// Method -> Overall framework (flowchart readout) and Key design 2 (mixing S~_i = sum_b m_ib S_b;
+// the normaliser may be dropped); "Rectifying Magnitude Neglect in Linear Attention", Method ->
+// Key design (beta, gamma and the linear form, with C = S - z u^T / N so that
+// Y = u/N + beta q~^T C exactly).
 //
 // One workgroup (4 wave64s) owns one token slice of one query block of one (batch, head).
 // Prologue: the block's mixed summary is staged in LDS in fragment layout (each MFMA A operand
-// is one 16-byte LDS read), together with one extra "normaliser" fragment per 32-feature
-// chunk whose rows 4g+0 hold hi(z~[k]) and rows 4g+1 hold lo(z~[k]) for every lane group g.
+// is one 16-byte LDS read), together with one extra "normaliser" fragment per 32-feature chunk
+// whose rows 4g+0 hold hi(z~[k]) and rows 4g+1 hold lo(z~[k]) for every lane group g.  The mixed
+// summary either comes from the mixing kernel, or -- for few blocks -- is formed right here:
+//   FUSE_BF16      S~_i = sum_b m_ib S_b from the bf16 stack, z~_i likewise, in fp32;
+//   FUSE_PARTIALS  from the fp32 token-slice partials: S_b = sum of slices, then the mixing
+//                  (MHLA) or the centring C = S - z u^T / N (MALA), split into bf16 hi + lo.
+// With all workgroups of a head on one XCD, the stack is read from HBM once per head and from
+// that XCD's L2 afterwards.
 // Main loop: each wave walks 16-token tiles; the lane owning token t = lane%16 and key
-// features 32*kc + 8*(lane/16) + 0..7 loads them with one 16-byte global read (the next
-// tile's loads are issued before the current tile is computed), applies phi in fp32, and
-// MFMAs compute O^T = S~^T phi(Q)^T: lane (t, g) holds channels 16*ct + 4g + 0..3 of token t,
-// and the normaliser fragment leaves phi(q_t)^T z~ = D[4g] + D[4g+1] in every lane of token t
-// with no cross-lane reduction.
+// features 32*kc + 8*(lane/16) + 0..7 loads them with one 16-byte read (the next tile's loads
+// are issued before the current tile is computed), applies phi in fp32, and MFMAs compute
+// O^T = S~^T phi(Q)^T: lane (t, g) holds channels 16*ct + 4g + 0..3 of token t, and the
+// normaliser fragment leaves phi(q_t)^T z~ = D[4g] + D[4g+1] in every lane of token t with no
+// cross-lane reduction.
 #include "mhla_device.hpp"
 
 namespace mhla {
 
 enum { kModeNormalized = 0, kModeUnnormalized = 1, kModeMala = 2 };
+enum { kFuseNone = 0, kFuseBf16 = 1, kFusePartials = 2 };
 
-template <typename TIn, typename TOut, int D, bool SPLIT>
+template <bool SPLIT>
+__device__ inline void store_frag8(uint16_t* s_hi, uint16_t* s_lo, int pos, const float (&a)[8]) {
+  if (SPLIT) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split_bf16(a[e], h[e], l[e]);
+    st16(s_hi + pos, u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16)});
+    st16(s_lo + pos, u32x4_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                             l[6] | (l[7] << 16)});
+  } else {
+    st16(s_hi + pos, u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                             pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])});
+  }
+}
+
+template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
 __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int mode) {
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -33,16 +57,32 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
   uint16_t* s_hi = smem;                   // [FRAG]
   uint16_t* s_lo = s_hi + FRAG;            // [FRAG]       (SPLIT)
   uint16_t* s_z = s_lo + (SPLIT ? FRAG : 0);   // [ZF]
-  float* s_ub = reinterpret_cast<float*>(s_z + ZF);   // [D]   (MALA)
+  float* s_ub = reinterpret_cast<float*>(s_z + ZF);   // [D]   mean of V (MALA)
+  float* s_zt = s_ub + D;                             // [D]   z~ (fp32) before fragmenting
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int split = blockIdx.x;
-  const int blk = blockIdx.y;
-  const int bh = blockIdx.z;
   const Geom& g = p.g;
   const int pr = lane & 15, lg = lane >> 4;
+
+  // ---- workgroup -> (token slice, block, head); heads pinned to XCDs when requested --------
+  int split, blk, bh;
+  {
+    const int per_head = p.splits * g.M;
+    const int L = blockIdx.x;
+    int r;
+    if (p.xcd_map) {   // dispatch is round-robin over the 8 XCDs by workgroup index
+      const int xcd = L & 7, s = L >> 3;
+      bh = (s / per_head) * 8 + xcd;
+      r = s % per_head;
+    } else {
+      bh = L / per_head;
+      r = L % per_head;
+    }
+    blk = r / p.splits;
+    split = r % p.splits;
+  }
 
   const int32_t j_begin = split * p.tok_per_split;
   const int32_t j_end = min(j_begin + p.tok_per_split, g.n_b);
@@ -75,35 +115,158 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
   int tile = wave;
   if (tile < n_tiles) issue(tile);
 
-  // ---- prologue: mixed summary, normaliser fragments, mean of V ---------------------------
-  const int64_t row = (int64_t)bh * g.M + blk;
-  {
+  // ---- prologue: mixed summary (loaded or formed here), z~, mean of V ------------------
+  const int M = g.M;
+  const int64_t row = (int64_t)bh * M + blk;
+  if constexpr (FUSE == kFuseNone) {
     const uint16_t* src_hi = p.st_hi + row * FRAG;
     for (int i = tid * 8; i < FRAG; i += kThreads * 8) {
       st16(s_hi + i, ld16(src_hi + i));
       if (SPLIT) st16(s_lo + i, ld16(p.st_lo + row * FRAG + i));
     }
-    if (tid < NKC * 64) {                       // one lane-fragment of 8 elements per thread
-      const int kc = tid >> 6, l = tid & 63;
-      const int rowp = l & 15, grp = l >> 4;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if ((rowp & 3) < 2) {
-        const float* zsrc = p.zt + row * D;
-        uint32_t bits[8];
+    if (tid < D) s_zt[tid] = p.zt[row * D + tid];
+  } else if constexpr (FUSE == kFuseBf16) {
+    // S~_i = sum_b m_ib S_b and z~_i = sum_b m_ib z_b in fp32 (NULL M_c: M == 1, weight 1)
+    const float* mrow =
+        p.mc ? p.mc + (int64_t)(bh % p.H) * p.mc_head_stride + (int64_t)blk * M : nullptr;
+    // blocks are taken 8 at a time with all 8 loads in flight; blocks >= M read as zero
+    // through the buffer resource and carry the weight 0
+    const Rsrc rss = make_rsrc(p.sb + (int64_t)bh * M * FRAG, (uint32_t)M * FRAG * 2u);
+    auto weight = [&](int b) { return b < M ? (mrow ? mrow[b] : 1.0f) : 0.0f; };
+    for (int pos = tid * 8; pos < FRAG; pos += kThreads * 8) {
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int b0 = 0; b0 < M; b0 += 8) {
+        u32x4_t w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 32 * kc + 8 * grp + e;
-          const float zv = k < D ? zsrc[k] : 0.f;
-          uint32_t h, lo;
-          split_bf16(zv, h, lo);
-          bits[e] = (rowp & 3) == 0 ? h : lo;
+        for (int j = 0; j < 8; ++j)
+          w[j] = buf_ld16(rss, b0 + j < M ? (uint32_t)((b0 + j) * FRAG + pos) * 2u : kOutOfRange);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float m = weight(b0 + j);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t x = w[j][e >> 1];
+            a[e] = fmaf(m, (e & 1) ? bf16hi_to_f32(x) : bf16lo_to_f32(x), a[e]);
+          }
+        }
+      }
+      store_frag8<false>(s_hi, s_lo, pos, a);
+    }
+    if (tid < D) {
+      // one token slice per block on this path: z_b = pz[bh][b][:]
+      const float* zsrc = p.pz + (int64_t)bh * M * D + tid;
+      float a = 0.f;
+      for (int b0 = 0; b0 < M; b0 += 8) {
+        float zb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zb[j] = zsrc[(int64_t)min(b0 + j, M - 1) * D];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaf(weight(b0 + j), zb[j], a);
+      }
+      s_zt[tid] = a;
+    }
+  } else {  // kFusePartials
+    const int ss = p.ssplits;
+    if (mode == kModeMala) {
+      // one block: S, z, u are sums over the token slices; C = S - z u^T / N
+      const float inv_n = 1.0f / (float)g.N;
+      const Rsrc rsp = make_rsrc(p.ps + (int64_t)bh * ss * FRAG, (uint32_t)ss * FRAG * 4u);
+      if (tid < D) {
+        float z = 0.f, u = 0.f;
+        for (int s = 0; s < ss; ++s) {
+          z += p.pz[((int64_t)bh * ss + s) * D + tid];
+          u += p.pu[((int64_t)bh * ss + s) * D + tid];
+        }
+        s_zt[tid] = z;
+        s_ub[tid] = u;          // u for now; scaled to u / N below
+      }
+      __syncthreads();
+      for (int pos = tid * 8; pos < FRAG; pos += kThreads * 8) {
+        const int l = (pos >> 3) & 63, fr = pos >> 9;
+        const int kc = fr / NCT, ct = fr % NCT;
+        const int k0 = 32 * kc + 8 * (l >> 4);
+        const float uc = s_ub[16 * ct + (l & 15)] * inv_n;
+        // slices 4 at a time with all loads in flight; slices >= ss read as zero
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < ss; s0 += 4) {
+          u32x4_t w[4][2];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t off = s0 + j < ss ? (uint32_t)((s0 + j) * FRAG + pos) * 4u : kOutOfRange;
+            w[j][0] = buf_ld16(rsp, off);
+            w[j][1] = buf_ld16(rsp, off == kOutOfRange ? kOutOfRange : off + 16u);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] += __uint_as_float(w[j][0][e]);
+              a[4 + e] += __uint_as_float(w[j][1][e]);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = bits[2 * i] | (bits[2 * i + 1] << 16);
+        for (int e = 0; e < 8; ++e) {
+          const int k = k0 + e;
+          a[e] -= (k < D ? s_zt[k] : 0.f) * uc;
+        }
+        store_frag8<SPLIT>(s_hi, s_lo, pos, a);
       }
-      st16(s_z + (kc * 64 + l) * 8, u32x4_t{w[0], w[1], w[2], w[3]});
+      __syncthreads();
+      if (tid < D) s_ub[tid] *= inv_n;
+    } else {
+      // MHLA from fp32 partials: S~_i = sum_b m_ib sum_s S_{b,s}
+      const float* mrow =
+          p.mc ? p.mc + (int64_t)(bh % p.H) * p.mc_head_stride + (int64_t)blk * M : nullptr;
+      for (int pos = tid * 8; pos < FRAG; pos += kThreads * 8) {
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < M; ++b) {
+          const float m = mrow ? mrow[b] : 1.0f;
+          float sb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          for (int s = 0; s < ss; ++s) {
+            const float* src = p.ps + (((int64_t)bh * M + b) * ss + s) * FRAG + pos;
+            const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sb[e] += __uint_as_float(w0[e]);
+              sb[4 + e] += __uint_as_float(w1[e]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = fmaf(m, sb[e], a[e]);
+        }
+        store_frag8<SPLIT>(s_hi, s_lo, pos, a);
+      }
+      if (tid < D) {
+        float a = 0.f;
+        for (int b = 0; b < M; ++b) {
+          float zb = 0.f;
+          for (int s = 0; s < ss; ++s) zb += p.pz[(((int64_t)bh * M + b) * ss + s) * D + tid];
+          a = fmaf(mrow ? mrow[b] : 1.0f, zb, a);
+        }
+        s_zt[tid] = a;
+      }
     }
-    if (mode == kModeMala && tid < D) s_ub[tid] = p.ubar[(int64_t)bh * D + tid];
+  }
+  __syncthreads();
+  // normaliser fragments from z~ (fp32 in LDS)
+  if (tid < NKC * 64) {                       // one lane-fragment of 8 elements per thread
+    const int kc = tid >> 6, l = tid & 63;
+    const int rowp = l & 15, grp = l >> 4;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if ((rowp & 3) < 2) {
+      uint32_t bits[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * kc + 8 * grp + e;
+        const float zv = k < D ? s_zt[k] : 0.f;
+        uint32_t h, lo;
+        split_bf16(zv, h, lo);
+        bits[e] = (rowp & 3) == 0 ? h : lo;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = bits[2 * i] | (bits[2 * i + 1] << 16);
+    }
+    st16(s_z + (kc * 64 + l) * 8, u32x4_t{w[0], w[1], w[2], w[3]});
   }
   __syncthreads();
 
@@ -179,8 +342,8 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
       const int64_t dst = coff + 16 * ct + 4 * lg;
       if constexpr (sizeof(TOut) == 4) {
         st16_stream(reinterpret_cast<float*>(p.o) + dst,
-             u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-                     __float_as_uint(o[3])});
+                    u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                            __float_as_uint(o[3])});
       } else {
         uint32_t* out = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.o) + dst);
         out[0] = pack_bf16x2(o[0], o[1]);
@@ -190,36 +353,53 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
   }
 }
 
-template <typename TIn, typename TOut, int D>
-static hipError_t launch_t(const ReadoutParams& p, int mode, bool split, dim3 grid, hipStream_t s) {
+template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
+static hipError_t launch_t(const ReadoutParams& p, int mode, int n_wg, hipStream_t s) {
   using Dm = Dims<D>;
-  const size_t lds = (size_t)Dm::FRAG * 2 * (split ? 2 : 1) + (size_t)Dm::NKC * 512 * 2 + D * 4;
-  if (split)
-    hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, true>), grid, dim3(kThreads), lds, s, p, mode);
-  else
-    hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, false>), grid, dim3(kThreads), lds, s, p, mode);
+  const size_t lds = (size_t)Dm::FRAG * 2 * (SPLIT ? 2 : 1) + (size_t)Dm::NKC * 512 * 2 + 2 * D * 4;
+  hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, SPLIT, FUSE>), dim3(n_wg), dim3(kThreads), lds,
+                     s, p, mode);
   return hipGetLastError();
 }
 
+// Valid (split, fuse) pairs: the bf16-stack fusion exists for bf16 operands only; the others
+// for both operand precisions.
+template <typename TIn, typename TOut, int D>
+static hipError_t dispatch_fuse(const ReadoutParams& p, int mode, bool split, int fuse, int n_wg,
+                                hipStream_t s) {
+  if (split) {
+    if (fuse == kFuseNone) return launch_t<TIn, TOut, D, true, kFuseNone>(p, mode, n_wg, s);
+    if (fuse == kFusePartials) return launch_t<TIn, TOut, D, true, kFusePartials>(p, mode, n_wg, s);
+    return hipErrorInvalidValue;
+  }
+  if (fuse == kFuseNone) return launch_t<TIn, TOut, D, false, kFuseNone>(p, mode, n_wg, s);
+  if (fuse == kFusePartials) return launch_t<TIn, TOut, D, false, kFusePartials>(p, mode, n_wg, s);
+  if constexpr (sizeof(TIn) == 2) {
+    if (fuse == kFuseBf16) return launch_t<TIn, TOut, D, false, kFuseBf16>(p, mode, n_wg, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename TIn, typename TOut>
-static hipError_t dispatch_d(const ReadoutParams& p, int d, int mode, bool split, dim3 grid,
-                             hipStream_t s) {
+static hipError_t dispatch_d(const ReadoutParams& p, int d, int mode, bool split, int fuse,
+                             int n_wg, hipStream_t s) {
   switch (d) {
-    case 16: return launch_t<TIn, TOut, 16>(p, mode, split, grid, s);
-    case 32: return launch_t<TIn, TOut, 32>(p, mode, split, grid, s);
-    case 64: return launch_t<TIn, TOut, 64>(p, mode, split, grid, s);
-    case 128: return launch_t<TIn, TOut, 128>(p, mode, split, grid, s);
+    case 16: return dispatch_fuse<TIn, TOut, 16>(p, mode, split, fuse, n_wg, s);
+    case 32: return dispatch_fuse<TIn, TOut, 32>(p, mode, split, fuse, n_wg, s);
+    case 64: return dispatch_fuse<TIn, TOut, 64>(p, mode, split, fuse, n_wg, s);
+    case 128: return dispatch_fuse<TIn, TOut, 128>(p, mode, split, fuse, n_wg, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+// n_wg = splits * M * BH workgroups (one-dimensional grid).
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
-                          bool split, dim3 grid, hipStream_t stream) {
+                          bool split, int fuse, int n_wg, hipStream_t stream) {
   if (in_fp32)
-    return out_fp32 ? dispatch_d<float, float>(p, d, mode, split, grid, stream)
-                    : dispatch_d<float, uint16_t>(p, d, mode, split, grid, stream);
-  return out_fp32 ? dispatch_d<uint16_t, float>(p, d, mode, split, grid, stream)
-                  : dispatch_d<uint16_t, uint16_t>(p, d, mode, split, grid, stream);
+    return out_fp32 ? dispatch_d<float, float>(p, d, mode, split, fuse, n_wg, stream)
+                    : dispatch_d<float, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
+  return out_fp32 ? dispatch_d<uint16_t, float>(p, d, mode, split, fuse, n_wg, stream)
+                  : dispatch_d<uint16_t, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
 }
 
 }  // namespace mhla
