@@ -9,6 +9,14 @@ durations come from HIP events the library records around each of its kernels on
 stream during the same timed loop; the dominant kernel's algorithmic bytes (or FLOPs) per
 launch divided by its mean duration gives `roofline.achieved`.  The fp64 CPU oracle is timed
 on a bounded sample of the same workload (`cpu_baseline`).  One JSON line is printed.
+
+`roofline.traffic` is the dominant kernel's measured HBM bytes per launch (FETCH_SIZE plus
+WRITE_SIZE hardware counters, each scaled by what the counter reads for a plain copy of known
+size), taken from profiles/traffic.md when that record was made from the current kernel sources
+(same digest of the csrc/ files and the header), else null.
+
+    python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter calibration
+    python bench.py --digest             # digest of the kernel sources
 """
 from __future__ import annotations
 
@@ -31,8 +39,55 @@ FP32_VALU_PEAK_TFLOPS = 157.3
 RANGE_WORKLOADS = ["image", "image_mala", "video3d", "long1d"]   # the N = 4096 .. 65536 configs
 
 
-def kernel_accounting(w: synth.Workload, out_bytes: int):
-    """Algorithmic bytes and FLOPs per launch of each kernel (summaries are not algorithmic)."""
+SOURCE_DIRS = ["token_blocked_linear_amd/csrc", "include"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.md")
+TRAFFIC_TAG = "traffic-json: "
+
+
+def source_digest() -> str:
+    """sha256 over the kernel and boundary sources (file names and contents, sorted)."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in SOURCE_DIRS:
+        full = os.path.join(ROOT, d)
+        for name in sorted(os.listdir(full)):
+            if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(full, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str, out_dtype: str):
+    """Calibrated HBM bytes per launch from profiles/traffic.md, or None when absent or stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = source_digest()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if not line.startswith(TRAFFIC_TAG):
+                continue
+            r = json.loads(line[len(TRAFFIC_TAG):])
+            if (r.get("workload"), r.get("kernel"), r.get("out_dtype")) == (workload, kernel, out_dtype):
+                return r["hbm_bytes_per_launch"] if r.get("source_digest") == digest else None
+    return None
+
+
+def copy_calibration(n_bytes: int = 1 << 30, reps: int = 10):
+    """A plain device copy of known size: counters read on it calibrate FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "launches": reps}),
+          flush=True)
+
+
+def kernel_accounting(w: synth.Workload, out_bytes: int, split: bool = False):
+    """Algorithmic bytes and FLOPs per launch of each kernel (summaries are not algorithmic).
+    The mixing kernel contracts a bf16 stack on MFMA, or fp32 partials on the VALU (`split`)."""
     BH, N, d, M = w.batch * w.heads, w.n_tokens, w.head_dim, w.n_blocks
     in_b = 2 if w.dtype == "bf16" else 4
     tok = BH * N
@@ -40,10 +95,11 @@ def kernel_accounting(w: synth.Workload, out_bytes: int):
         "summary": dict(bytes=tok * 2 * d * in_b, flops=tok * (2 * d * d + d), bound="hbm"),
         "readout": dict(bytes=tok * d * (in_b + out_bytes), flops=tok * (2 * d * d + 2 * d), bound="hbm"),
     }
+    mix_bound = "alu" if split else "mfma"
     if w.readout == "mala":
-        acc["mix"] = dict(bytes=0, flops=BH * 2 * d * d, bound="alu")
+        acc["mix"] = dict(bytes=0, flops=BH * 2 * d * d, bound=mix_bound)
     else:
-        acc["mix"] = dict(bytes=M * M * 4, flops=BH * 2 * M * M * (d * d + d), bound="alu")
+        acc["mix"] = dict(bytes=M * M * 4, flops=BH * 2 * M * M * (d * d + d), bound=mix_bound)
     # mixing step run in the readout's prologue: its inputs are summaries (not algorithmic),
     # so the fused kernel carries the readout's bytes plus M_c
     acc["mix+readout"] = dict(bytes=acc["readout"]["bytes"] + acc["mix"]["bytes"],
@@ -91,7 +147,7 @@ def run_workload(name: str, steps: int, warmup: int, out_dtype: str):
         kname, ms, n = T.mhla_timing_read(plan.handle, i)
         kernels[kname] = ms / max(n, 1) * 1e-3          # mean seconds per launch
     ob = 2 if out_dtype == "bf16" else 4
-    acc, total_bytes, total_flops = kernel_accounting(w, ob)
+    acc, total_bytes, total_flops = kernel_accounting(w, ob, bool(plan.info.split_operands))
     per_kernel = {}
     for kname, t in kernels.items():
         a = acc[kname]
@@ -99,6 +155,8 @@ def run_workload(name: str, steps: int, warmup: int, out_dtype: str):
         tfl = a["flops"] / t / 1e12
         if a["bound"] == "hbm":
             frac = gbs / HBM_PEAK_GBS
+        elif a["bound"] == "mfma":
+            frac = tfl / BF16_MFMA_PEAK_TFLOPS
         else:
             frac = tfl / FP32_VALU_PEAK_TFLOPS
         per_kernel[kname] = dict(us=round(t * 1e6, 2), alg_GBps=round(gbs, 1), TFLOPs=round(tfl, 2),
@@ -148,7 +206,13 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other N=4096..65536 workloads")
     ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--digest", action="store_true")
     args = ap.parse_args()
+
+    if args.digest:
+        print(source_digest())
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -160,6 +224,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
     res = run_workload(args.workload, args.steps, args.warmup, args.out_dtype)
     w = res["workload"]
     dom = max(res["kernels"], key=lambda k: res["kernels"][k])
@@ -167,10 +235,11 @@ def main():
     a = res["acc"][dom]
     if pk["bound"] == "hbm":
         roof = {"bound": "hbm", "achieved": pk["alg_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": pk["frac"], "traffic": None, "kernel": dom,
+                "frac": pk["frac"], "traffic": measured_traffic(w.name, dom, args.out_dtype), "kernel": dom,
                 "alg_bytes_per_launch": a["bytes"], "mean_launch_us": pk["us"]}
     else:
-        roof = {"bound": "alu", "achieved": pk["TFLOPs"], "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+        peak = BF16_MFMA_PEAK_TFLOPS if pk["bound"] == "mfma" else FP32_VALU_PEAK_TFLOPS
+        roof = {"bound": pk["bound"], "achieved": pk["TFLOPs"], "peak": peak, "unit": "TFLOP/s",
                 "frac": pk["frac"], "traffic": None, "kernel": dom,
                 "alg_flops_per_launch": a["flops"], "mean_launch_us": pk["us"]}
 

@@ -20,11 +20,19 @@
 
 // Cache policy of the loads that stream Q, K, V (each byte is read once) and of the output
 // stores.  0 = default; the build can set the gfx9 cache-policy bits for these streams.
-#ifndef MHLA_STREAM_CPOL
-#define MHLA_STREAM_CPOL 0
+// Cache policy (the aux operand of buffer loads; 2 = nt: lines are kept only briefly) for the
+// data each kernel streams once, and whether the readout's output stores are non-temporal.
+#ifndef MHLA_SUMMARY_LOAD_CPOL
+#define MHLA_SUMMARY_LOAD_CPOL 2      // K, V
 #endif
-#ifndef MHLA_STREAM_STORE_NT
-#define MHLA_STREAM_STORE_NT 0
+#ifndef MHLA_MIX_LOAD_CPOL
+#define MHLA_MIX_LOAD_CPOL 2          // the summary stack
+#endif
+#ifndef MHLA_READOUT_LOAD_CPOL
+#define MHLA_READOUT_LOAD_CPOL 0      // Q
+#endif
+#ifndef MHLA_READOUT_STORE_NT
+#define MHLA_READOUT_STORE_NT 0       // O
 #endif
 
 namespace mhla {
@@ -203,8 +211,9 @@ __device__ inline f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, f32x4_t 
 // 16-byte global loads and stores.
 __device__ inline u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ inline void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
-__device__ inline void st16_stream(void* p, u32x4_t v) {
-  if (MHLA_STREAM_STORE_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+template <bool NT>
+__device__ inline void st16_pol(void* p, u32x4_t v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
   else *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
@@ -218,13 +227,9 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // >= every range used here (ran
 __device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+template <int CPOL = 0>
 __device__ inline u32x4_t buf_ld16(Rsrc r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-__device__ inline u32x4_t buf_ld16_stream(Rsrc r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4_t,
-                            __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, MHLA_STREAM_CPOL));
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL));
 }
 
 // Input element loaders: 8 consecutive elements starting at element index `idx` as fp32.
@@ -234,7 +239,8 @@ template <> struct In8<uint16_t> {       // bf16 bits
   __device__ inline void load(const void* base, int64_t idx) {
     w = ld16(reinterpret_cast<const uint16_t*>(base) + idx);
   }
-  __device__ inline void load_buf(Rsrc r, uint32_t byte_off) { w = buf_ld16_stream(r, byte_off); }
+  template <int CPOL>
+  __device__ inline void load_buf(Rsrc r, uint32_t byte_off) { w = buf_ld16<CPOL>(r, byte_off); }
   __device__ inline void zero() { w = u32x4_t{0u, 0u, 0u, 0u}; }
   __device__ inline float get(int e) const {
     uint32_t x = w[e >> 1];
@@ -252,9 +258,10 @@ template <> struct In8<float> {
     w0 = ld16(p);
     w1 = ld16(p + 4);
   }
+  template <int CPOL>
   __device__ inline void load_buf(Rsrc r, uint32_t byte_off) {
-    w0 = buf_ld16_stream(r, byte_off);
-    w1 = buf_ld16_stream(r, byte_off == kOutOfRange ? kOutOfRange : byte_off + 16u);
+    w0 = buf_ld16<CPOL>(r, byte_off);
+    w1 = buf_ld16<CPOL>(r, byte_off == kOutOfRange ? kOutOfRange : byte_off + 16u);
   }
   __device__ inline void zero() {
     w0 = u32x4_t{0u, 0u, 0u, 0u};

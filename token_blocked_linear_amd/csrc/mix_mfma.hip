@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int b = 8 * rg + r;
-      raw[r] = buf_ld16(rsx, b < M ? (uint32_t)(b * P + tile * PB + 8 * cg) * 2u : kOutOfRange);
+      raw[r] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? (uint32_t)(b * P + tile * PB + 8 * cg) * 2u : kOutOfRange);
     }
   };
 

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int k0 = 32 * kc + 8 * lg;
-      raw[kc].load_buf(rsq, (valid && k0 < D) ? (rel + k0) * ES : kOutOfRange);
+      raw[kc].template load_buf<MHLA_READOUT_LOAD_CPOL>(rsq, (valid && k0 < D) ? (rel + k0) * ES : kOutOfRange);
     }
   };
   int tile = wave;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
       }
       const int64_t dst = coff + 16 * ct + 4 * lg;
       if constexpr (sizeof(TOut) == 4) {
-        st16_stream(reinterpret_cast<float*>(p.o) + dst,
+        st16_pol<MHLA_READOUT_STORE_NT>(reinterpret_cast<float*>(p.o) + dst,
                     u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                             __float_as_uint(o[3])});
       } else {

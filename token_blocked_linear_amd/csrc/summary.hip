@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t off = ok ? off0 + (uint32_t)(i * D * ES) : kOutOfRange;
-        rk[i].load_buf(rsk, off);
-        rv[i].load_buf(rsv, off);
+        rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, off);
+        rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, off);
       }
     } else {
 #pragma unroll
@@ -140,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         const bool ok = loader && j < U.j_end;
         const uint32_t t = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j)) : 0u;
         const uint32_t off = ok ? (t * D + 8 * fgrp) * ES : kOutOfRange;
-        rk[i].load_buf(rsk, off);
-        rv[i].load_buf(rsv, off);
+        rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, off);
+        rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, off);
       }
     }
   };
