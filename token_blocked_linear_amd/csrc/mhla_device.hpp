@@ -178,6 +178,7 @@ struct ReadoutParams {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

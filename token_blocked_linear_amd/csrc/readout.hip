@@ -21,9 +21,13 @@
 // Main loop: each wave walks 16-token tiles; the lane owning token t = lane%16 and key
 // features 32*kc + 8*(lane/16) + 0..7 loads them with one 16-byte read (the next tile's loads
 // are issued before the current tile is computed), applies phi in fp32, and MFMAs compute
-// O^T = S~^T phi(Q)^T: lane (t, g) holds channels 16*ct + 4g + 0..3 of token t, and the
-// normaliser fragment leaves phi(q_t)^T z~ = D[4g] + D[4g+1] in every lane of token t with no
-// cross-lane reduction.
+// O^T = S~^T phi(Q)^T, with the normaliser fragment leaving phi(q_t)^T z~ = D[4g] + D[4g+1] in
+// every lane of token t with no cross-lane reduction.  Output channels are taken 32 at a time as
+// two MFMA tiles h = 0, 1 whose A row m is channel 8*(m/4) + 4h + m%4 of the group, so lane
+// (t, g) ends with the 8 consecutive channels 8g .. 8g+7 of token t: 16-byte stores, and the four
+// lane groups of a token write 64 (bf16) or 128 (fp32) contiguous bytes.  In LDS, bit 2 of a
+// fragment's lane index is flipped when bit 3 is set, so that every 8 lanes of these operand
+// reads cover all banks once.
 #include "mhla_device.hpp"
 
 namespace mhla {
@@ -44,6 +48,17 @@ __device__ inline void store_frag8(uint16_t* s_hi, uint16_t* s_lo, int pos, cons
   } else {
     st16(s_hi + pos, u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
                              pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])});
+  }
+}
+
+// LDS element offset of fragment element `pos` (a multiple of 8): see the bank note above
+template <int NCT>
+__device__ inline int lds_pos(int pos) {
+  if constexpr (NCT >= 2) {
+    const int u = pos >> 3;
+    return (u ^ (((u >> 3) & 1) << 2)) << 3;
+  } else {
+    return pos;
   }
 }
 
@@ -121,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
   if constexpr (FUSE == kFuseNone) {
     const uint16_t* src_hi = p.st_hi + row * FRAG;
     for (int i = tid * 8; i < FRAG; i += kThreads * 8) {
-      st16(s_hi + i, ld16(src_hi + i));
-      if (SPLIT) st16(s_lo + i, ld16(p.st_lo + row * FRAG + i));
+      st16(s_hi + lds_pos<NCT>(i), ld16(src_hi + i));
+      if (SPLIT) st16(s_lo + lds_pos<NCT>(i), ld16(p.st_lo + row * FRAG + i));
     }
     if (tid < D) s_zt[tid] = p.zt[row * D + tid];
   } else if constexpr (FUSE == kFuseBf16) {
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
           }
         }
       }
-      store_frag8<false>(s_hi, s_lo, pos, a);
+      store_frag8<false>(s_hi, s_lo, lds_pos<NCT>(pos), a);
     }
     if (tid < D) {
       // one token slice per block on this path: z_b = pz[bh][b][:]
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
           const int k = k0 + e;
           a[e] -= (k < D ? s_zt[k] : 0.f) * uc;
         }
-        store_frag8<SPLIT>(s_hi, s_lo, pos, a);
+        store_frag8<SPLIT>(s_hi, s_lo, lds_pos<NCT>(pos), a);
       }
       __syncthreads();
       if (tid < D) s_ub[tid] *= inv_n;
@@ -234,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
 #pragma unroll
           for (int e = 0; e < 8; ++e) a[e] = fmaf(m, sb[e], a[e]);
         }
-        store_frag8<SPLIT>(s_hi, s_lo, pos, a);
+        store_frag8<SPLIT>(s_hi, s_lo, lds_pos<NCT>(pos), a);
       }
       if (tid < D) {
         float a = 0.f;
@@ -269,6 +284,13 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
     st16(s_z + (kc * 64 + l) * 8, u32x4_t{w[0], w[1], w[2], w[3]});
   }
   __syncthreads();
+
+  // A row pr of tile ct is channel 32*(ct/2) + 8*(pr/4) + 4*(ct%2) + pr%4 (d >= 32): it sits in
+  // fragment ct & ~1 (or the next one for pr >= 8) at lane 16*lg + 8*b + 4*(ct%2) + pr%4,
+  // b = (pr/4)%2, which the LDS swizzle moves to 16*lg + 8*b + 4*((ct%2) ^ b) + pr%4
+  const int b3 = (pr >> 2) & 1;
+  const int a_even = ((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (0 ^ b3) + (pr & 3)) * 8;
+  const int a_odd = ((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (1 ^ b3) + (pr & 3)) * 8;
 
   for (; tile < n_tiles; tile += kThreads / 64) {
     // take this tile's inputs and issue the next tile's loads
@@ -310,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
       if (SPLIT) accz = mfma_bf16(az, b_lo, accz);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const int off = ((kc * NCT + ct) * 64 + lane) * 8;
+        const int off = NCT >= 2 ? (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? a_odd : a_even)
+                                 : (kc * 64 + lane) * 8;
         const u32x4_t a_hi = *reinterpret_cast<const u32x4_t*>(s_hi + off);
         acc[ct] = mfma_bf16(a_hi, b_hi, acc[ct]);
         if (SPLIT) {
@@ -329,25 +352,42 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
     float scale = 1.f;
     if (mode == kModeNormalized) scale = 1.0f / den;
     else if (mode == kModeMala) scale = 1.0f + 1.0f / den;
+    // lane (t, g) holds channels cg0 + 0..7 of each 32-channel group (d = 16: channels 4g..4g+3)
+    constexpr int NG = NCT >= 2 ? NCT / 2 : 1;      // channel groups
+    constexpr int W = NCT >= 2 ? 8 : 4;             // channels per lane and group
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float o[4];
+    for (int cgp = 0; cgp < NG; ++cgp) {
+      const int c0 = NCT >= 2 ? 32 * cgp + 8 * lg : 4 * lg;
+      float o[W];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = acc[ct][r] * scale;
-      if (mode == kModeMala) {
-        const u32x4_t ub = *reinterpret_cast<const u32x4_t*>(s_ub + 16 * ct + 4 * lg);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] += __uint_as_float(ub[r]);
+      for (int r = 0; r < 4; ++r) {
+        o[r] = acc[NCT >= 2 ? 2 * cgp : 0][r] * scale;
+        if constexpr (W == 8) o[4 + r] = acc[2 * cgp + 1][r] * scale;
       }
-      const int64_t dst = coff + 16 * ct + 4 * lg;
+      if (mode == kModeMala) {
+#pragma unroll
+        for (int j = 0; j < W; j += 4) {
+          const u32x4_t ub = *reinterpret_cast<const u32x4_t*>(s_ub + c0 + j);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[j + r] += __uint_as_float(ub[r]);
+        }
+      }
+      const int64_t dst = coff + c0;
       if constexpr (sizeof(TOut) == 4) {
-        st16_pol<MHLA_READOUT_STORE_NT>(reinterpret_cast<float*>(p.o) + dst,
-                    u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
-                            __float_as_uint(o[3])});
+#pragma unroll
+        for (int j = 0; j < W; j += 4)
+          st16_pol<MHLA_READOUT_STORE_NT>(
+              reinterpret_cast<float*>(p.o) + dst + j,
+              u32x4_t{__float_as_uint(o[j]), __float_as_uint(o[j + 1]), __float_as_uint(o[j + 2]),
+                      __float_as_uint(o[j + 3])});
+      } else if constexpr (W == 8) {
+        st16_pol<MHLA_READOUT_STORE_NT>(
+            reinterpret_cast<uint16_t*>(p.o) + dst,
+            u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                    pack_bf16x2(o[6], o[7])});
       } else {
-        uint32_t* out = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.o) + dst);
-        out[0] = pack_bf16x2(o[0], o[1]);
-        out[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(p.o) + dst) =
+            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       }
     }
   }
