@@ -18,8 +18,6 @@
 
 #include "fastdiv.hpp"
 
-// Cache policy of the loads that stream Q, K, V (each byte is read once) and of the output
-// stores.  0 = default; the build can set the gfx9 cache-policy bits for these streams.
 // Cache policy (the aux operand of buffer loads; 2 = nt: lines are kept only briefly) for the
 // data each kernel streams once, and whether the readout's output stores are non-temporal.
 #ifndef MHLA_SUMMARY_LOAD_CPOL
@@ -189,14 +187,24 @@ __device__ inline uint32_t f32_to_bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (RNE) in one word, `lo` in the low half: one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // hi = bf16(x), lo = bf16(x - hi): x == hi + lo to about 2^-17 relative.
 __device__ inline void split_bf16(float x, uint32_t& hi_bits, uint32_t& lo_bits) {
   hi_bits = f32_to_bf16_bits(x);
   lo_bits = f32_to_bf16_bits(x - __uint_as_float(hi_bits << 16));
+}
+
+// split_bf16 of two values at once, packed like pack_bf16x2 (x0 in the low halves).
+__device__ inline void split_bf16x2(float x0, float x1, uint32_t& hi2, uint32_t& lo2) {
+  hi2 = pack_bf16x2(x0, x1);
+  lo2 = pack_bf16x2(x0 - __uint_as_float(hi2 << 16), x1 - __uint_as_float(hi2 & 0xffff0000u));
 }
 
 // ELU(x) + 1 with alpha = 1.

@@ -1,4 +1,4 @@
-// Readout kernel: for every query token t of block i,
+// Readout kernels: for every query token t of block i,
 //   normalised    o_t = phi(q_t)^T S~_i / phi(q_t)^T z~_i
 //   unnormalised  o_t = phi(q_t)^T S~_i
 //   MALA          o_t = u/N + (1 + 1/s_t) phi(q_t)^T C,   s_t = phi(q_t)^T z
@@ -8,19 +8,19 @@
 // Key design (beta, gamma and the linear form, with C = S - z u^T / N so that
 // Y = u/N + beta q~^T C exactly).
 //
-// One workgroup (4 wave64s) owns one token slice of one query block of one (batch, head).
-// Prologue: the block's mixed summary is staged in LDS in fragment layout (each MFMA A operand
+// One workgroup (4 wave64s) serves one unit: a token slice of one query block of one
+// (batch, head).  The block's mixed summary sits in LDS in fragment layout (each MFMA A operand
 // is one 16-byte LDS read), together with one extra "normaliser" fragment per 32-feature chunk
 // whose rows 4g+0 hold hi(z~[k]) and rows 4g+1 hold lo(z~[k]) for every lane group g.  The mixed
-// summary either comes from the mixing kernel, or -- for few blocks -- is formed right here:
+// summary either comes from the mixing kernel (all of a thread's loads in flight at once), or --
+// for few blocks, and for MALA -- is formed in the prologue:
 //   FUSE_BF16      S~_i = sum_b m_ib S_b from the bf16 stack, z~_i likewise, in fp32;
 //   FUSE_PARTIALS  from the fp32 token-slice partials: S_b = sum of slices, then the mixing
 //                  (MHLA) or the centring C = S - z u^T / N (MALA), split into bf16 hi + lo.
-// With all workgroups of a head on one XCD, the stack is read from HBM once per head and from
-// that XCD's L2 afterwards.
-// Main loop: each wave walks 16-token tiles; the lane owning token t = lane%16 and key
-// features 32*kc + 8*(lane/16) + 0..7 loads them with one 16-byte read (the next tile's loads
-// are issued before the current tile is computed), applies phi in fp32, and MFMAs compute
+// With all units of a head on one XCD (workgroups are dealt to the 8 XCDs round-robin), a head's
+// summaries are fetched from HBM once and then hit in that XCD's L2.
+// Per 16-token tile: the lane owning token t = lane%16 and key features 32*kc + 8*(lane/16) + 0..7
+// loads them with one 16-byte read (issued a tile ahead), applies phi in fp32, and MFMAs compute
 // O^T = S~^T phi(Q)^T, with the normaliser fragment leaving phi(q_t)^T z~ = D[4g] + D[4g+1] in
 // every lane of token t with no cross-lane reduction.  Output channels are taken 32 at a time as
 // two MFMA tiles h = 0, 1 whose A row m is channel 8*(m/4) + 4h + m%4 of the group, so lane
@@ -38,13 +38,11 @@ enum { kFuseNone = 0, kFuseBf16 = 1, kFusePartials = 2 };
 template <bool SPLIT>
 __device__ inline void store_frag8(uint16_t* s_hi, uint16_t* s_lo, int pos, const float (&a)[8]) {
   if (SPLIT) {
-    uint32_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(a[e], h[e], l[e]);
-    st16(s_hi + pos, u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                             h[6] | (h[7] << 16)});
-    st16(s_lo + pos, u32x4_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                             l[6] | (l[7] << 16)});
+    for (int i = 0; i < 4; ++i) split_bf16x2(a[2 * i], a[2 * i + 1], h[i], l[i]);
+    st16(s_hi + pos, u32x4_t{h[0], h[1], h[2], h[3]});
+    st16(s_lo + pos, u32x4_t{l[0], l[1], l[2], l[3]});
   } else {
     st16(s_hi + pos, u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
                              pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])});
@@ -62,8 +60,198 @@ __device__ inline int lds_pos(int pos) {
   }
 }
 
+
+// Normaliser fragments from z~ (fp32 in LDS): rows 4g = hi, 4g + 1 = lo, other rows zero.
+template <int D>
+__device__ inline void build_zfrag(const float* s_zt, uint16_t* s_z, int tid) {
+  constexpr int NKC = Dims<D>::NKC;
+  if (tid < NKC * 64) {                       // one lane-fragment of 8 elements per thread
+    const int kc = tid >> 6, l = tid & 63;
+    const int rowp = l & 15, grp = l >> 4;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if ((rowp & 3) < 2) {
+      uint32_t bits[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 32 * kc + 8 * grp + e;
+        const float zv = k < D ? s_zt[k] : 0.f;
+        uint32_t h, lo;
+        split_bf16(zv, h, lo);
+        bits[e] = (rowp & 3) == 0 ? h : lo;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = bits[2 * i] | (bits[2 * i + 1] << 16);
+    }
+    st16(s_z + (kc * 64 + l) * 8, u32x4_t{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// A-operand LDS offsets: A row pr of tile ct is channel 32*(ct/2) + 8*(pr/4) + 4*(ct%2) + pr%4
+// (d >= 32).  It sits in fragment ct & ~1 (or the next one for pr >= 8) at lane
+// 16*lg + 8*b + 4*(ct%2) + pr%4, b = (pr/4)%2, which the LDS swizzle moves to
+// 16*lg + 8*b + 4*((ct%2) ^ b) + pr%4.  Only these two lane-dependent bases exist.
+struct AOffsets {
+  int even, odd;
+};
+__device__ inline AOffsets a_offsets(int lane) {
+  const int pr = lane & 15, lg = lane >> 4, b3 = (pr >> 2) & 1;
+  return {((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (0 ^ b3) + (pr & 3)) * 8,
+          ((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (1 ^ b3) + (pr & 3)) * 8};
+}
+
+// One 16-token tile: phi(Q) -> MFMAs against the staged summary -> scale -> 16-byte stores.
+// `cur` holds this lane's query features; `coff` the element offset of its token row in Q / O.
+template <typename TIn, typename TOut, int D, bool SPLIT>
+__device__ __forceinline__ void readout_tile(const In8<TIn> (&cur)[Dims<D>::NKC], bool cvalid,
+                                             int64_t coff, const uint16_t* s_hi,
+                                             const uint16_t* s_lo, const uint16_t* s_z,
+                                             const float* s_ub, AOffsets ao, int lane, int mode,
+                                             void* out) {
+  using Dm = Dims<D>;
+  constexpr int NKC = Dm::NKC, NCT = Dm::NCT;
+  const int lg = lane >> 4;
+  f32x4_t acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    // phi on every lane, no branch: tokens past the slice (their loads read zero) give finite
+    // values whose output columns are never stored, and key rows k >= D (d = 16) meet zero rows
+    // of the summary and normaliser fragments
+    u32x4_t b_hi, b_lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = phi_elu1(cur[kc].get(2 * i)), x1 = phi_elu1(cur[kc].get(2 * i + 1));
+      if (SPLIT) {
+        uint32_t h, l;
+        split_bf16x2(x0, x1, h, l);
+        b_hi[i] = h;
+        b_lo[i] = l;
+      }
+      else b_hi[i] = pack_bf16x2(x0, x1);
+    }
+    const u32x4_t az = *reinterpret_cast<const u32x4_t*>(s_z + (kc * 64 + lane) * 8);
+    accz = mfma_bf16(az, b_hi, accz);
+    if (SPLIT) accz = mfma_bf16(az, b_lo, accz);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int off = NCT >= 2 ? (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? ao.odd : ao.even)
+                               : (kc * 64 + lane) * 8;
+      const u32x4_t a_hi = *reinterpret_cast<const u32x4_t*>(s_hi + off);
+      acc[ct] = mfma_bf16(a_hi, b_hi, acc[ct]);
+      if (SPLIT) {
+        const u32x4_t a_lo = *reinterpret_cast<const u32x4_t*>(s_lo + off);
+        acc[ct] = mfma_bf16(a_lo, b_hi, acc[ct]);
+        acc[ct] = mfma_bf16(a_hi, b_lo, acc[ct]);
+      }
+    }
+    // keep each chunk's LDS operand reads next to their MFMAs: hoisting all of them would
+    // cost NKC*NCT*4 registers and halve the waves per SIMD at d = 128
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (!cvalid) return;
+  const float den = accz[0] + accz[1];      // phi(q_t)^T z~  (hi row + lo row)
+  float scale = 1.f;
+  if (mode == kModeNormalized) scale = 1.0f / den;
+  else if (mode == kModeMala) scale = 1.0f + 1.0f / den;
+  // lane (t, g) holds channels c0 + 0..7 of each 32-channel group (d = 16: channels 4g..4g+3)
+  constexpr int NG = NCT >= 2 ? NCT / 2 : 1;      // channel groups
+  constexpr int W = NCT >= 2 ? 8 : 4;             // channels per lane and group
+#pragma unroll
+  for (int cgp = 0; cgp < NG; ++cgp) {
+    const int c0 = NCT >= 2 ? 32 * cgp + 8 * lg : 4 * lg;
+    float o[W];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o[r] = acc[NCT >= 2 ? 2 * cgp : 0][r] * scale;
+      if constexpr (W == 8) o[4 + r] = acc[2 * cgp + 1][r] * scale;
+    }
+    if (mode == kModeMala) {
+#pragma unroll
+      for (int j = 0; j < W; j += 4) {
+        const u32x4_t ub = *reinterpret_cast<const u32x4_t*>(s_ub + c0 + j);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[j + r] += __uint_as_float(ub[r]);
+      }
+    }
+    const int64_t dst = coff + c0;
+    if constexpr (sizeof(TOut) == 4) {
+#pragma unroll
+      for (int j = 0; j < W; j += 4)
+        st16_pol<MHLA_READOUT_STORE_NT>(
+            reinterpret_cast<float*>(out) + dst + j,
+            u32x4_t{__float_as_uint(o[j]), __float_as_uint(o[j + 1]), __float_as_uint(o[j + 2]),
+                    __float_as_uint(o[j + 3])});
+    } else if constexpr (W == 8) {
+      st16_pol<MHLA_READOUT_STORE_NT>(
+          reinterpret_cast<uint16_t*>(out) + dst,
+          u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                  pack_bf16x2(o[6], o[7])});
+    } else {
+      *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(out) + dst) =
+          u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+// A unit's coordinates.  Unit L -> (head, block, token slice); with xcd_map (B*H % 8 == 0), unit
+// L belongs to head 8 * ((L/8) / per_head) + L%8, so that the units of a head share an XCD.
+struct RdUnit {
+  int bh, blk;
+  int32_t j_begin, j_end, base_tok;
+  int n_tiles;
+  int64_t head_off, row;
+};
+template <int D>
+__device__ inline RdUnit rd_unit(const ReadoutParams& p, int L) {
+  const Geom& g = p.g;
+  const int per_head = p.splits * g.M;
+  int r;
+  RdUnit u;
+  if (p.xcd_map) {
+    const int xcd = L & 7, s = L >> 3;
+    u.bh = (s / per_head) * 8 + xcd;
+    r = s % per_head;
+  } else {
+    u.bh = L / per_head;
+    r = L % per_head;
+  }
+  u.blk = r / p.splits;
+  const int split = r % p.splits;
+  u.j_begin = split * p.tok_per_split;
+  u.j_end = min(u.j_begin + p.tok_per_split, g.n_b);
+  u.base_tok = block_base_token(g, u.blk);
+  u.n_tiles = (u.j_end - u.j_begin + 15) >> 4;
+  u.head_off = (int64_t)u.bh * g.N * D;
+  u.row = (int64_t)u.bh * g.M + u.blk;
+  return u;
+}
+
+// Issue the query loads of tile t of unit u into `dst` through a buffer resource over the
+// unit's head: tokens past the slice and key features beyond D (d = 16) read as zero.
+template <typename TIn, int D>
+__device__ inline void rd_issue(const ReadoutParams& p, const RdUnit& u, int t, int lane,
+                                In8<TIn> (&dst)[Dims<D>::NKC], bool& v, int64_t& off) {
+  constexpr uint32_t ES = sizeof(TIn);
+  const int pr = lane & 15, lg = lane >> 4;
+  const int32_t j = u.j_begin + t * 16 + pr;
+  v = j < u.j_end;
+  off = v ? u.head_off + (int64_t)(u.base_tok + block_token_offset(p.g, (uint32_t)j)) * D : 0;
+  const Rsrc rsq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + u.head_off, (uint32_t)p.g.N * D * ES);
+  const uint32_t rel = (uint32_t)(off - u.head_off);
+#pragma unroll
+  for (int kc = 0; kc < Dims<D>::NKC; ++kc) {
+    const int k0 = 32 * kc + 8 * lg;
+    dst[kc].template load_buf<MHLA_READOUT_LOAD_CPOL>(rsq, (v && k0 < D) ? (rel + k0) * ES : kOutOfRange);
+  }
+}
+
 template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
-__global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int mode) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void readout_kernel(
+    ReadoutParams p, int mode) {
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
   constexpr int ZF = NKC * 512;            // normaliser fragments (elements)
@@ -79,67 +267,42 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const Geom& g = p.g;
-  const int pr = lane & 15, lg = lane >> 4;
+  const RdUnit U = rd_unit<D>(p, blockIdx.x);
+  const int bh = U.bh, blk = U.blk;
 
-  // ---- workgroup -> (token slice, block, head); heads pinned to XCDs when requested --------
-  int split, blk, bh;
-  {
-    const int per_head = p.splits * g.M;
-    const int L = blockIdx.x;
-    int r;
-    if (p.xcd_map) {   // dispatch is round-robin over the 8 XCDs by workgroup index
-      const int xcd = L & 7, s = L >> 3;
-      bh = (s / per_head) * 8 + xcd;
-      r = s % per_head;
-    } else {
-      bh = L / per_head;
-      r = L % per_head;
-    }
-    blk = r / p.splits;
-    split = r % p.splits;
-  }
-
-  const int32_t j_begin = split * p.tok_per_split;
-  const int32_t j_end = min(j_begin + p.tok_per_split, g.n_b);
-  const int32_t base_tok = block_base_token(g, blk);
-  const int64_t head_off = (int64_t)bh * g.N * D;
-  const int n_tiles = (j_end - j_begin + 15) >> 4;
-
-  // first tile's query loads go out before the prologue
-  auto tok_offset = [&](int tile, bool& valid) -> int64_t {
-    const int32_t j = j_begin + tile * 16 + pr;
-    valid = j < j_end;
-    return valid ? head_off + (int64_t)(base_tok + block_token_offset(g, (uint32_t)j)) * D : 0;
-  };
-  // query loads through a buffer resource over this head: invalid tokens and key features
-  // beyond D (d = 16) read as zero without a branch
-  constexpr uint32_t ES = sizeof(TIn);
-  const Rsrc rsq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + head_off, (uint32_t)g.N * D * ES);
+  // this wave's first query tile goes out before the prologue
   In8<TIn> raw[NKC];
   bool valid = false;
   int64_t toff = 0;
-  auto issue = [&](int tile) {
-    toff = tok_offset(tile, valid);
-    const uint32_t rel = (uint32_t)(toff - head_off);       // element offset within the head
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const int k0 = 32 * kc + 8 * lg;
-      raw[kc].template load_buf<MHLA_READOUT_LOAD_CPOL>(rsq, (valid && k0 < D) ? (rel + k0) * ES : kOutOfRange);
-    }
-  };
   int tile = wave;
-  if (tile < n_tiles) issue(tile);
+  if (tile < U.n_tiles) rd_issue<TIn, D>(p, U, tile, lane, raw, valid, toff);
 
   // ---- prologue: mixed summary (loaded or formed here), z~, mean of V ------------------
   const int M = g.M;
-  const int64_t row = (int64_t)bh * M + blk;
+  // fragment chunks of 8 elements per thread; the prologues take PC of them per pass
+  constexpr int PER = (FRAG + kThreads * 8 - 1) / (kThreads * 8);
+  constexpr int PC = PER < 2 ? PER : 2;
   if constexpr (FUSE == kFuseNone) {
-    const uint16_t* src_hi = p.st_hi + row * FRAG;
-    for (int i = tid * 8; i < FRAG; i += kThreads * 8) {
-      st16(s_hi + lds_pos<NCT>(i), ld16(src_hi + i));
-      if (SPLIT) st16(s_lo + lds_pos<NCT>(i), ld16(p.st_lo + row * FRAG + i));
+    // the mixing kernel's output: every chunk of this thread in flight at once
+    const Rsrc rhi = make_rsrc(p.st_hi + U.row * FRAG, FRAG * 2u);
+    const Rsrc rlo = make_rsrc(SPLIT ? p.st_lo + U.row * FRAG : p.st_hi, SPLIT ? FRAG * 2u : 0u);
+    u32x4_t th[PER], tl[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = (tid + j * kThreads) * 8;
+      const uint32_t off = i < FRAG ? (uint32_t)i * 2u : kOutOfRange;
+      th[j] = buf_ld16(rhi, off);
+      if (SPLIT) tl[j] = buf_ld16(rlo, off);
     }
-    if (tid < D) s_zt[tid] = p.zt[row * D + tid];
+    if (tid < D) s_zt[tid] = p.zt[U.row * D + tid];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = (tid + j * kThreads) * 8;
+      if (i < FRAG) {
+        st16(s_hi + lds_pos<NCT>(i), th[j]);
+        if (SPLIT) st16(s_lo + lds_pos<NCT>(i), tl[j]);
+      }
+    }
   } else if constexpr (FUSE == kFuseBf16) {
     // S~_i = sum_b m_ib S_b and z~_i = sum_b m_ib z_b in fp32 (NULL M_c: M == 1, weight 1)
     const float* mrow =
@@ -148,24 +311,39 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
     // through the buffer resource and carry the weight 0
     const Rsrc rss = make_rsrc(p.sb + (int64_t)bh * M * FRAG, (uint32_t)M * FRAG * 2u);
     auto weight = [&](int b) { return b < M ? (mrow ? mrow[b] : 1.0f) : 0.0f; };
-    for (int pos = tid * 8; pos < FRAG; pos += kThreads * 8) {
-      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int b0 = 0; b0 < M; b0 += 8) {
-        u32x4_t w[8];
+    for (int j0 = 0; j0 < PER; j0 += PC) {
+      float a[PC][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          w[j] = buf_ld16(rss, b0 + j < M ? (uint32_t)((b0 + j) * FRAG + pos) * 2u : kOutOfRange);
+      for (int c = 0; c < PC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[c][e] = 0.f;
+      for (int b0 = 0; b0 < M; b0 += 8) {
+        u32x4_t w[PC][8];
+#pragma unroll
+        for (int c = 0; c < PC; ++c) {
+          const int i = (tid + (j0 + c) * kThreads) * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            w[c][j] = buf_ld16(rss, (b0 + j < M && i < FRAG) ? (uint32_t)((b0 + j) * FRAG + i) * 2u
+                                                             : kOutOfRange);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float m = weight(b0 + j);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t x = w[j][e >> 1];
-            a[e] = fmaf(m, (e & 1) ? bf16hi_to_f32(x) : bf16lo_to_f32(x), a[e]);
-          }
+          for (int c = 0; c < PC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t x = w[c][j][e >> 1];
+              a[c][e] = fmaf(m, (e & 1) ? bf16hi_to_f32(x) : bf16lo_to_f32(x), a[c][e]);
+            }
         }
       }
-      store_frag8<false>(s_hi, s_lo, lds_pos<NCT>(pos), a);
+#pragma unroll
+      for (int c = 0; c < PC; ++c) {
+        const int i = (tid + (j0 + c) * kThreads) * 8;
+        if (i < FRAG) store_frag8<false>(s_hi, s_lo, lds_pos<NCT>(i), a[c]);
+      }
     }
     if (tid < D) {
       // one token slice per block on this path: z_b = pz[bh][b][:]
@@ -196,35 +374,51 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
         s_ub[tid] = u;          // u for now; scaled to u / N below
       }
       __syncthreads();
-      for (int pos = tid * 8; pos < FRAG; pos += kThreads * 8) {
-        const int l = (pos >> 3) & 63, fr = pos >> 9;
-        const int kc = fr / NCT, ct = fr % NCT;
-        const int k0 = 32 * kc + 8 * (l >> 4);
-        const float uc = s_ub[16 * ct + (l & 15)] * inv_n;
-        // slices 4 at a time with all loads in flight; slices >= ss read as zero
-        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < ss; s0 += 4) {
-          u32x4_t w[4][2];
+      for (int j0 = 0; j0 < PER; j0 += PC) {
+        // slices 4 at a time, PC chunks each, all loads in flight; slices >= ss read as zero
+        float a[PC][8];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t off = s0 + j < ss ? (uint32_t)((s0 + j) * FRAG + pos) * 4u : kOutOfRange;
-            w[j][0] = buf_ld16(rsp, off);
-            w[j][1] = buf_ld16(rsp, off == kOutOfRange ? kOutOfRange : off + 16u);
+        for (int c = 0; c < PC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[c][e] = 0.f;
+        for (int s0 = 0; s0 < ss; s0 += 4) {
+          u32x4_t w[PC][4][2];
+#pragma unroll
+          for (int c = 0; c < PC; ++c) {
+            const int i = (tid + (j0 + c) * kThreads) * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bool ok = s0 + j < ss && i < FRAG;
+              const uint32_t off = (uint32_t)((s0 + j) * FRAG + i) * 4u;
+              w[c][j][0] = buf_ld16(rsp, ok ? off : kOutOfRange);
+              w[c][j][1] = buf_ld16(rsp, ok ? off + 16u : kOutOfRange);
+            }
           }
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int c = 0; c < PC; ++c)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a[e] += __uint_as_float(w[j][0][e]);
-              a[4 + e] += __uint_as_float(w[j][1][e]);
-            }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                a[c][e] += __uint_as_float(w[c][j][0][e]);
+                a[c][4 + e] += __uint_as_float(w[c][j][1][e]);
+              }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = k0 + e;
-          a[e] -= (k < D ? s_zt[k] : 0.f) * uc;
+        for (int c = 0; c < PC; ++c) {
+          const int pos = (tid + (j0 + c) * kThreads) * 8;
+          if (pos >= FRAG) continue;
+          const int l = (pos >> 3) & 63, fr = pos >> 9;
+          const int kc = fr / NCT, ct = fr % NCT;
+          const int k0 = 32 * kc + 8 * (l >> 4);
+          const float uc = s_ub[16 * ct + (l & 15)] * inv_n;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = k0 + e;
+            a[c][e] -= (k < D ? s_zt[k] : 0.f) * uc;
+          }
+          store_frag8<SPLIT>(s_hi, s_lo, lds_pos<NCT>(pos), a[c]);
         }
-        store_frag8<SPLIT>(s_hi, s_lo, lds_pos<NCT>(pos), a);
       }
       __syncthreads();
       if (tid < D) s_ub[tid] *= inv_n;
@@ -263,133 +457,18 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(ReadoutParams p, int 
     }
   }
   __syncthreads();
-  // normaliser fragments from z~ (fp32 in LDS)
-  if (tid < NKC * 64) {                       // one lane-fragment of 8 elements per thread
-    const int kc = tid >> 6, l = tid & 63;
-    const int rowp = l & 15, grp = l >> 4;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if ((rowp & 3) < 2) {
-      uint32_t bits[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = 32 * kc + 8 * grp + e;
-        const float zv = k < D ? s_zt[k] : 0.f;
-        uint32_t h, lo;
-        split_bf16(zv, h, lo);
-        bits[e] = (rowp & 3) == 0 ? h : lo;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = bits[2 * i] | (bits[2 * i + 1] << 16);
-    }
-    st16(s_z + (kc * 64 + l) * 8, u32x4_t{w[0], w[1], w[2], w[3]});
-  }
+  build_zfrag<D>(s_zt, s_z, tid);
   __syncthreads();
 
-  // A row pr of tile ct is channel 32*(ct/2) + 8*(pr/4) + 4*(ct%2) + pr%4 (d >= 32): it sits in
-  // fragment ct & ~1 (or the next one for pr >= 8) at lane 16*lg + 8*b + 4*(ct%2) + pr%4,
-  // b = (pr/4)%2, which the LDS swizzle moves to 16*lg + 8*b + 4*((ct%2) ^ b) + pr%4
-  const int b3 = (pr >> 2) & 1;
-  const int a_even = ((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (0 ^ b3) + (pr & 3)) * 8;
-  const int a_odd = ((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (1 ^ b3) + (pr & 3)) * 8;
-
-  for (; tile < n_tiles; tile += kThreads / 64) {
-    // take this tile's inputs and issue the next tile's loads
+  const AOffsets ao = a_offsets(lane);
+  for (; tile < U.n_tiles; tile += kThreads / 64) {
     In8<TIn> cur[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) cur[kc] = raw[kc];
     const bool cvalid = valid;
     const int64_t coff = toff;
-    if (tile + kThreads / 64 < n_tiles) issue(tile + kThreads / 64);
-
-    f32x4_t acc[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      const int k0 = 32 * kc + 8 * lg;
-      u32x4_t b_hi, b_lo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x0 = 0.f, x1 = 0.f;
-        if (cvalid && k0 < D) {
-          x0 = phi_elu1(cur[kc].get(2 * i));
-          x1 = phi_elu1(cur[kc].get(2 * i + 1));
-        }
-        if (SPLIT) {
-          uint32_t h0, l0, h1, l1;
-          split_bf16(x0, h0, l0);
-          split_bf16(x1, h1, l1);
-          b_hi[i] = h0 | (h1 << 16);
-          b_lo[i] = l0 | (l1 << 16);
-        } else {
-          b_hi[i] = pack_bf16x2(x0, x1);
-        }
-      }
-      const u32x4_t az = *reinterpret_cast<const u32x4_t*>(s_z + (kc * 64 + lane) * 8);
-      accz = mfma_bf16(az, b_hi, accz);
-      if (SPLIT) accz = mfma_bf16(az, b_lo, accz);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int off = NCT >= 2 ? (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? a_odd : a_even)
-                                 : (kc * 64 + lane) * 8;
-        const u32x4_t a_hi = *reinterpret_cast<const u32x4_t*>(s_hi + off);
-        acc[ct] = mfma_bf16(a_hi, b_hi, acc[ct]);
-        if (SPLIT) {
-          const u32x4_t a_lo = *reinterpret_cast<const u32x4_t*>(s_lo + off);
-          acc[ct] = mfma_bf16(a_lo, b_hi, acc[ct]);
-          acc[ct] = mfma_bf16(a_hi, b_lo, acc[ct]);
-        }
-      }
-      // keep each chunk's LDS operand reads next to their MFMAs: hoisting all of them would
-      // cost NKC*NCT*4 registers and halve the waves per SIMD at d = 128
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    if (!cvalid) continue;
-    const float den = accz[0] + accz[1];      // phi(q_t)^T z~  (hi row + lo row)
-    float scale = 1.f;
-    if (mode == kModeNormalized) scale = 1.0f / den;
-    else if (mode == kModeMala) scale = 1.0f + 1.0f / den;
-    // lane (t, g) holds channels cg0 + 0..7 of each 32-channel group (d = 16: channels 4g..4g+3)
-    constexpr int NG = NCT >= 2 ? NCT / 2 : 1;      // channel groups
-    constexpr int W = NCT >= 2 ? 8 : 4;             // channels per lane and group
-#pragma unroll
-    for (int cgp = 0; cgp < NG; ++cgp) {
-      const int c0 = NCT >= 2 ? 32 * cgp + 8 * lg : 4 * lg;
-      float o[W];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        o[r] = acc[NCT >= 2 ? 2 * cgp : 0][r] * scale;
-        if constexpr (W == 8) o[4 + r] = acc[2 * cgp + 1][r] * scale;
-      }
-      if (mode == kModeMala) {
-#pragma unroll
-        for (int j = 0; j < W; j += 4) {
-          const u32x4_t ub = *reinterpret_cast<const u32x4_t*>(s_ub + c0 + j);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[j + r] += __uint_as_float(ub[r]);
-        }
-      }
-      const int64_t dst = coff + c0;
-      if constexpr (sizeof(TOut) == 4) {
-#pragma unroll
-        for (int j = 0; j < W; j += 4)
-          st16_pol<MHLA_READOUT_STORE_NT>(
-              reinterpret_cast<float*>(p.o) + dst + j,
-              u32x4_t{__float_as_uint(o[j]), __float_as_uint(o[j + 1]), __float_as_uint(o[j + 2]),
-                      __float_as_uint(o[j + 3])});
-      } else if constexpr (W == 8) {
-        st16_pol<MHLA_READOUT_STORE_NT>(
-            reinterpret_cast<uint16_t*>(p.o) + dst,
-            u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                    pack_bf16x2(o[6], o[7])});
-      } else {
-        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(p.o) + dst) =
-            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      }
-    }
+    if (tile + kThreads / 64 < U.n_tiles) rd_issue<TIn, D>(p, U, tile + kThreads / 64, lane, raw, valid, toff);
+    readout_tile<TIn, TOut, D, SPLIT>(cur, cvalid, coff, s_hi, s_lo, s_z, s_ub, ao, lane, mode, p.o);
   }
 }
 

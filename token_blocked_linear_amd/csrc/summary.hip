@@ -174,11 +174,10 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         for (int i = 0; i < 4; ++i) {
           const float x0 = phi_elu1(rk[2 * i].get(e)), x1 = phi_elu1(rk[2 * i + 1].get(e));
           if (SPLIT_K) {
-            uint32_t h0, l0, h1, l1;
-            split_bf16(x0, h0, l0);
-            split_bf16(x1, h1, l1);
-            hi[i] = h0 | (h1 << 16);
-            lo[i] = l0 | (l1 << 16);
+            uint32_t h, l;
+            split_bf16x2(x0, x1, h, l);
+            hi[i] = h;
+            lo[i] = l;
           } else {
             hi[i] = pack_bf16x2(x0, x1);
           }
@@ -197,11 +196,10 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
           for (int i = 0; i < 4; ++i) {
             const float v0 = rv[2 * i].get(e), v1 = rv[2 * i + 1].get(e);
             if (SPLIT_V) {
-              uint32_t h0, l0, h1, l1;
-              split_bf16(v0, h0, l0);
-              split_bf16(v1, h1, l1);
-              vh[i] = h0 | (h1 << 16);
-              vl[i] = l0 | (l1 << 16);
+              uint32_t h, l;
+              split_bf16x2(v0, v1, h, l);
+              vh[i] = h;
+              vl[i] = l;
             } else {
               vh[i] = pack_bf16x2(v0, v1);
             }
