@@ -29,6 +29,9 @@
 #ifndef MHLA_READOUT_LOAD_CPOL
 #define MHLA_READOUT_LOAD_CPOL 0      // Q
 #endif
+#ifndef MHLA_READOUT_TILES
+#define MHLA_READOUT_TILES 1          // 16-token query tiles per readout wave and step (d <= 64)
+#endif
 #ifndef MHLA_READOUT_STORE_NT
 #define MHLA_READOUT_STORE_NT 0       // O
 #endif

@@ -99,52 +99,66 @@ __device__ inline AOffsets a_offsets(int lane) {
           ((pr >> 3) * 64 + 16 * lg + 8 * b3 + 4 * (1 ^ b3) + (pr & 3)) * 8};
 }
 
-// One 16-token tile: phi(Q) -> MFMAs against the staged summary -> scale -> 16-byte stores.
-// `cur` holds this lane's query features; `coff` the element offset of its token row in Q / O.
-template <typename TIn, typename TOut, int D, bool SPLIT>
-__device__ __forceinline__ void readout_tile(const In8<TIn> (&cur)[Dims<D>::NKC], bool cvalid,
-                                             int64_t coff, const uint16_t* s_hi,
-                                             const uint16_t* s_lo, const uint16_t* s_z,
-                                             const float* s_ub, AOffsets ao, int lane, int mode,
-                                             void* out) {
+// NT 16-token tiles at once: phi(Q) -> MFMAs against the staged summary (each A operand read
+// from LDS feeds the NT tiles) -> scale -> 16-byte stores.  cur[t] holds this lane's query
+// features of tile t; coff[t] the element offset of its token row in Q / O.
+template <typename TIn, typename TOut, int D, bool SPLIT, int NT>
+__device__ __forceinline__ void readout_tiles(const In8<TIn> (&cur)[NT][Dims<D>::NKC],
+                                              const bool (&cvalid)[NT], const int64_t (&coff)[NT],
+                                              const uint16_t* s_hi, const uint16_t* s_lo,
+                                              const uint16_t* s_z, const float* s_ub, AOffsets ao,
+                                              int lane, int mode, void* out) {
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT;
   const int lg = lane >> 4;
-  f32x4_t acc[NCT];
+  f32x4_t acc[NT][NCT], accz[NT];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    accz[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[t][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
     // phi on every lane, no branch: tokens past the slice (their loads read zero) give finite
     // values whose output columns are never stored, and key rows k >= D (d = 16) meet zero rows
     // of the summary and normaliser fragments
-    u32x4_t b_hi, b_lo;
+    u32x4_t b_hi[NT], b_lo[NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x0 = phi_elu1(cur[kc].get(2 * i)), x1 = phi_elu1(cur[kc].get(2 * i + 1));
-      if (SPLIT) {
-        uint32_t h, l;
-        split_bf16x2(x0, x1, h, l);
-        b_hi[i] = h;
-        b_lo[i] = l;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = phi_elu1(cur[t][kc].get(2 * i)), x1 = phi_elu1(cur[t][kc].get(2 * i + 1));
+        if (SPLIT) {
+          uint32_t h, l;
+          split_bf16x2(x0, x1, h, l);
+          b_hi[t][i] = h;
+          b_lo[t][i] = l;
+        } else {
+          b_hi[t][i] = pack_bf16x2(x0, x1);
+        }
       }
-      else b_hi[i] = pack_bf16x2(x0, x1);
-    }
     const u32x4_t az = *reinterpret_cast<const u32x4_t*>(s_z + (kc * 64 + lane) * 8);
-    accz = mfma_bf16(az, b_hi, accz);
-    if (SPLIT) accz = mfma_bf16(az, b_lo, accz);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      accz[t] = mfma_bf16(az, b_hi[t], accz[t]);
+      if (SPLIT) accz[t] = mfma_bf16(az, b_lo[t], accz[t]);
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int off = NCT >= 2 ? (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? ao.odd : ao.even)
                                : (kc * 64 + lane) * 8;
       const u32x4_t a_hi = *reinterpret_cast<const u32x4_t*>(s_hi + off);
-      acc[ct] = mfma_bf16(a_hi, b_hi, acc[ct]);
-      if (SPLIT) {
-        const u32x4_t a_lo = *reinterpret_cast<const u32x4_t*>(s_lo + off);
-        acc[ct] = mfma_bf16(a_lo, b_hi, acc[ct]);
-        acc[ct] = mfma_bf16(a_hi, b_lo, acc[ct]);
+      u32x4_t a_lo;
+      if (SPLIT) a_lo = *reinterpret_cast<const u32x4_t*>(s_lo + off);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[t][ct] = mfma_bf16(a_hi, b_hi[t], acc[t][ct]);
+        if (SPLIT) {
+          acc[t][ct] = mfma_bf16(a_lo, b_hi[t], acc[t][ct]);
+          acc[t][ct] = mfma_bf16(a_hi, b_lo[t], acc[t][ct]);
+        }
       }
     }
     // keep each chunk's LDS operand reads next to their MFMAs: hoisting all of them would
@@ -152,47 +166,50 @@ __device__ __forceinline__ void readout_tile(const In8<TIn> (&cur)[Dims<D>::NKC]
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  if (!cvalid) return;
-  const float den = accz[0] + accz[1];      // phi(q_t)^T z~  (hi row + lo row)
-  float scale = 1.f;
-  if (mode == kModeNormalized) scale = 1.0f / den;
-  else if (mode == kModeMala) scale = 1.0f + 1.0f / den;
-  // lane (t, g) holds channels c0 + 0..7 of each 32-channel group (d = 16: channels 4g..4g+3)
-  constexpr int NG = NCT >= 2 ? NCT / 2 : 1;      // channel groups
-  constexpr int W = NCT >= 2 ? 8 : 4;             // channels per lane and group
 #pragma unroll
-  for (int cgp = 0; cgp < NG; ++cgp) {
-    const int c0 = NCT >= 2 ? 32 * cgp + 8 * lg : 4 * lg;
-    float o[W];
+  for (int t = 0; t < NT; ++t) {
+    if (!cvalid[t]) continue;
+    const float den = accz[t][0] + accz[t][1];      // phi(q_t)^T z~  (hi row + lo row)
+    float scale = 1.f;
+    if (mode == kModeNormalized) scale = 1.0f / den;
+    else if (mode == kModeMala) scale = 1.0f + 1.0f / den;
+    // lane (t, g) holds channels c0 + 0..7 of each 32-channel group (d = 16: channels 4g..4g+3)
+    constexpr int NG = NCT >= 2 ? NCT / 2 : 1;      // channel groups
+    constexpr int W = NCT >= 2 ? 8 : 4;             // channels per lane and group
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      o[r] = acc[NCT >= 2 ? 2 * cgp : 0][r] * scale;
-      if constexpr (W == 8) o[4 + r] = acc[2 * cgp + 1][r] * scale;
-    }
-    if (mode == kModeMala) {
+    for (int cgp = 0; cgp < NG; ++cgp) {
+      const int c0 = NCT >= 2 ? 32 * cgp + 8 * lg : 4 * lg;
+      float o[W];
 #pragma unroll
-      for (int j = 0; j < W; j += 4) {
-        const u32x4_t ub = *reinterpret_cast<const u32x4_t*>(s_ub + c0 + j);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[j + r] += __uint_as_float(ub[r]);
+      for (int r = 0; r < 4; ++r) {
+        o[r] = acc[t][NCT >= 2 ? 2 * cgp : 0][r] * scale;
+        if constexpr (W == 8) o[4 + r] = acc[t][2 * cgp + 1][r] * scale;
       }
-    }
-    const int64_t dst = coff + c0;
-    if constexpr (sizeof(TOut) == 4) {
+      if (mode == kModeMala) {
 #pragma unroll
-      for (int j = 0; j < W; j += 4)
+        for (int j = 0; j < W; j += 4) {
+          const u32x4_t ub = *reinterpret_cast<const u32x4_t*>(s_ub + c0 + j);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[j + r] += __uint_as_float(ub[r]);
+        }
+      }
+      const int64_t dst = coff[t] + c0;
+      if constexpr (sizeof(TOut) == 4) {
+#pragma unroll
+        for (int j = 0; j < W; j += 4)
+          st16_pol<MHLA_READOUT_STORE_NT>(
+              reinterpret_cast<float*>(out) + dst + j,
+              u32x4_t{__float_as_uint(o[j]), __float_as_uint(o[j + 1]), __float_as_uint(o[j + 2]),
+                      __float_as_uint(o[j + 3])});
+      } else if constexpr (W == 8) {
         st16_pol<MHLA_READOUT_STORE_NT>(
-            reinterpret_cast<float*>(out) + dst + j,
-            u32x4_t{__float_as_uint(o[j]), __float_as_uint(o[j + 1]), __float_as_uint(o[j + 2]),
-                    __float_as_uint(o[j + 3])});
-    } else if constexpr (W == 8) {
-      st16_pol<MHLA_READOUT_STORE_NT>(
-          reinterpret_cast<uint16_t*>(out) + dst,
-          u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                  pack_bf16x2(o[6], o[7])});
-    } else {
-      *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(out) + dst) =
-          u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            reinterpret_cast<uint16_t*>(out) + dst,
+            u32x4_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                    pack_bf16x2(o[6], o[7])});
+      } else {
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(out) + dst) =
+            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
     }
   }
 }
@@ -249,8 +266,17 @@ __device__ inline void rd_issue(const ReadoutParams& p, const RdUnit& u, int t, 
   }
 }
 
+// Query tiles per wave and step: two (each staged A operand feeds two MFMAs) where the registers
+// allow it at 4 waves per SIMD; one at d = 128 and for fp32 inputs.
+template <typename TIn, int D>
+constexpr int readout_tiles_per_step() { return sizeof(TIn) == 2 && D <= 64 ? MHLA_READOUT_TILES : 1; }
+// waves per SIMD the register allocation must allow (fp32 inputs at d = 128 need more registers)
+template <typename TIn, int D>
+constexpr int readout_waves() { return sizeof(TIn) == 4 && D == 128 ? 3 : 4; }
+
 template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void readout_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    readout_waves<TIn, D>()))) void readout_kernel(
     ReadoutParams p, int mode) {
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -270,12 +296,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const RdUnit U = rd_unit<D>(p, blockIdx.x);
   const int bh = U.bh, blk = U.blk;
 
-  // this wave's first query tile goes out before the prologue
-  In8<TIn> raw[NKC];
-  bool valid = false;
-  int64_t toff = 0;
+  // NT tiles per wave and step (tiles wave, wave + 4, ...); the first step's query loads go out
+  // before the prologue, each later step's during the previous step
+  constexpr int NT = readout_tiles_per_step<TIn, D>();
+  constexpr int WSTEP = kThreads / 64;
+  In8<TIn> raw[NT][NKC];
+  bool valid[NT];
+  int64_t toff[NT];
+  auto issue_step = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      valid[j] = false;
+      toff[j] = 0;
+      if (t0 + j * WSTEP < U.n_tiles) {
+        rd_issue<TIn, D>(p, U, t0 + j * WSTEP, lane, raw[j], valid[j], toff[j]);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) raw[j][kc].zero();
+      }
+    }
+  };
   int tile = wave;
-  if (tile < U.n_tiles) rd_issue<TIn, D>(p, U, tile, lane, raw, valid, toff);
+  issue_step(tile);
 
   // ---- prologue: mixed summary (loaded or formed here), z~, mean of V ------------------
   const int M = g.M;
@@ -461,14 +503,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __syncthreads();
 
   const AOffsets ao = a_offsets(lane);
-  for (; tile < U.n_tiles; tile += kThreads / 64) {
-    In8<TIn> cur[NKC];
+  for (; tile < U.n_tiles; tile += NT * WSTEP) {
+    In8<TIn> cur[NT][NKC];
+    bool cvalid[NT];
+    int64_t coff[NT];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) cur[kc] = raw[kc];
-    const bool cvalid = valid;
-    const int64_t coff = toff;
-    if (tile + kThreads / 64 < U.n_tiles) rd_issue<TIn, D>(p, U, tile + kThreads / 64, lane, raw, valid, toff);
-    readout_tile<TIn, TOut, D, SPLIT>(cur, cvalid, coff, s_hi, s_lo, s_z, s_ub, ao, lane, mode, p.o);
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) cur[j][kc] = raw[j][kc];
+      cvalid[j] = valid[j];
+      coff[j] = toff[j];
+    }
+    if (tile + NT * WSTEP < U.n_tiles) issue_step(tile + NT * WSTEP);
+    readout_tiles<TIn, TOut, D, SPLIT, NT>(cur, cvalid, coff, s_hi, s_lo, s_z, s_ub, ao, lane, mode, p.o);
   }
 }
 
