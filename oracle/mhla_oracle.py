@@ -23,7 +23,9 @@ sum (the token-expanded identity of [MHLA] Key design 2), so ``mhla_plain`` and
 pages' steps (phi -> per-block S_b, z_b -> mixing with M_c -> readout).
 
 Readings where the pages are silent (full list in the design notes):
-  * phi is ELU+1 with alpha = 1; no 1/sqrt(d) scaling before phi.
+  * phi is ELU+1 with alpha = 1 by default; ReLU (max(x, 0)) and exp (elementwise e^x, no
+    shift) are the other maps [MALA] Ablation names as working alike.  No 1/sqrt(d)
+    scaling before phi.
   * The readout display equation of Key design 2 did not survive extraction;
     the flowchart gives o = q~^T S~_i / q~^T z~_i, used here.
   * S_b has rows indexed by the key feature, columns by the value feature.
@@ -37,7 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "phi_elu1", "block_index", "block_summaries", "mix_summaries", "readout",
+    "phi_elu1", "phi_relu", "phi_exp", "phi_map", "block_index", "block_summaries", "mix_summaries", "readout",
     "mhla_blockwise", "mhla_plain", "mhla_plain_sampled", "mhla_attention_matrix",
     "mala_linear", "mala_weights", "mala_plain", "mala_plain_sampled",
     "forward", "forward_sampled",
@@ -53,6 +55,27 @@ def phi_elu1(x):
     """ELU(x) + 1 with alpha = 1:  x + 1 for x > 0,  exp(x) for x <= 0."""
     x = np.asarray(x, dtype=np.float64)
     return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_relu(x):
+    """ReLU(x) = max(x, 0)."""
+    return np.maximum(np.asarray(x, dtype=np.float64), 0.0)
+
+
+def phi_exp(x):
+    """e^x elementwise (no max subtraction: the pages give none)."""
+    return np.exp(np.asarray(x, dtype=np.float64))
+
+
+def phi_map(x, phi="elu1"):
+    """The feature map named by ``phi``: "elu1" (default), "relu" or "exp"."""
+    if phi == "elu1":
+        return phi_elu1(x)
+    if phi == "relu":
+        return phi_relu(x)
+    if phi == "exp":
+        return phi_exp(x)
+    raise ValueError(phi)
 
 
 # ----------------------------------------------------------------------------------------
@@ -141,7 +164,7 @@ def _as_head_mc(mc, h, n_blocks):
     return mc
 
 
-def mhla_blockwise(q, k, v, mc, grid, block, normalized=True):
+def mhla_blockwise(q, k, v, mc, grid, block, normalized=True, phi="elu1"):
     """MHLA forward for one (batch, head): q, k, v [N, d] -> o [N, d], pages' step order."""
     bidx = block_index(grid, block)
     n_blocks = int(bidx.max()) + 1
@@ -149,7 +172,7 @@ def mhla_blockwise(q, k, v, mc, grid, block, normalized=True):
         if n_blocks != 1:
             raise ValueError("M_c is required when there is more than one block")
         mc = np.ones((1, 1))
-    qt, kt = phi_elu1(q), phi_elu1(k)
+    qt, kt = phi_map(q, phi), phi_map(k, phi)
     S, z = block_summaries(kt, v, bidx, n_blocks)
     St, zt = mix_summaries(mc, S, z)
     return readout(qt, St, zt, bidx, normalized)
@@ -168,29 +191,29 @@ def mhla_attention_matrix(qt, kt, mc, bidx):
     return mc[np.ix_(bidx, bidx)] * (qt @ kt.T)
 
 
-def mhla_plain(q, k, v, mc, grid, block, normalized=True):
+def mhla_plain(q, k, v, mc, grid, block, normalized=True, phi="elu1"):
     """o_t = sum_t' A[t,t'] v_t' / sum_t' A[t,t'] with the N x N matrix built explicitly."""
     bidx = block_index(grid, block)
     if mc is None:
         mc = np.ones((1, 1))
-    A = mhla_attention_matrix(phi_elu1(q), phi_elu1(k), mc, bidx)
+    A = mhla_attention_matrix(phi_map(q, phi), phi_map(k, phi), mc, bidx)
     num = A @ np.asarray(v, np.float64)
     if not normalized:
         return num
     return num / A.sum(axis=1)[:, None]
 
 
-def mhla_plain_sampled(q, k, v, mc, grid, block, tokens, normalized=True):
+def mhla_plain_sampled(q, k, v, mc, grid, block, tokens, normalized=True, phi="elu1"):
     """The plain definition evaluated for the query tokens ``tokens`` only (O(N d) each)."""
     bidx = block_index(grid, block)
     if mc is None:
         mc = np.ones((1, 1))
     mc = np.asarray(mc, np.float64)
-    kt = phi_elu1(k)
+    kt = phi_map(k, phi)
     v = np.asarray(v, np.float64)
     out = np.empty((len(tokens), v.shape[1]))
     for r, t in enumerate(tokens):
-        qt = phi_elu1(q[t])
+        qt = phi_map(q[t], phi)
         w = mc[bidx[t], bidx] * (kt @ qt)
         out[r] = (w @ v) / (w.sum() if normalized else 1.0)
     return out
@@ -202,9 +225,9 @@ def mhla_plain_sampled(q, k, v, mc, grid, block, tokens, normalized=True):
 # linear form Y_i = beta phi(Q_i) sum_j phi(K_j)^T V_j - gamma sum_j V_j.  One block (M = 1).
 # ----------------------------------------------------------------------------------------
 
-def mala_linear(q, k, v):
+def mala_linear(q, k, v, phi="elu1"):
     """The linear-complexity form: compute sum_j phi(K_j)^T V_j first, then read out."""
-    qt, kt = phi_elu1(q), phi_elu1(k)
+    qt, kt = phi_map(q, phi), phi_map(k, phi)
     v = np.asarray(v, np.float64)
     n = kt.shape[0]
     kv = kt.T @ v                    # sum_j phi(K_j)^T V_j          [d, dv]
@@ -226,17 +249,17 @@ def mala_weights(qt, kt):
     return beta[:, None] * a - gamma[:, None]
 
 
-def mala_plain(q, k, v):
-    return mala_weights(phi_elu1(q), phi_elu1(k)) @ np.asarray(v, np.float64)
+def mala_plain(q, k, v, phi="elu1"):
+    return mala_weights(phi_map(q, phi), phi_map(k, phi)) @ np.asarray(v, np.float64)
 
 
-def mala_plain_sampled(q, k, v, tokens):
-    kt = phi_elu1(k)
+def mala_plain_sampled(q, k, v, tokens, phi="elu1"):
+    kt = phi_map(k, phi)
     v = np.asarray(v, np.float64)
     n = kt.shape[0]
     out = np.empty((len(tokens), v.shape[1]))
     for r, t in enumerate(tokens):
-        a = kt @ phi_elu1(q[t])
+        a = kt @ phi_map(q[t], phi)
         s = a.sum()
         w = (1.0 + 1.0 / s) * a - s / n
         out[r] = w @ v
@@ -254,7 +277,7 @@ def _check_mode(mode, n_blocks):
         raise ValueError("the MALA readout is defined for a single block (M = 1)")
 
 
-def forward(q, k, v, mc, grid, block, mode="normalized", heads=None):
+def forward(q, k, v, mc, grid, block, mode="normalized", heads=None, phi="elu1"):
     """Blockwise oracle over [B, H, N, d] inputs; returns float64 [B, H, N, d].
 
     ``heads`` optionally restricts the computation to a list of (b, h) pairs; the result
@@ -271,16 +294,16 @@ def forward(q, k, v, mc, grid, block, mode="normalized", heads=None):
         kh = np.asarray(k[b, h], np.float64)
         vh = np.asarray(v[b, h], np.float64)
         if mode == "mala":
-            out[r] = mala_linear(qh, kh, vh)
+            out[r] = mala_linear(qh, kh, vh, phi)
         else:
             mch = _as_head_mc(mc, h, n_blocks)
-            out[r] = mhla_blockwise(qh, kh, vh, mch, grid, block, mode == "normalized")
+            out[r] = mhla_blockwise(qh, kh, vh, mch, grid, block, mode == "normalized", phi)
     if heads is None:
         return out.reshape(B, H, N, -1)
     return out
 
 
-def forward_sampled(q, k, v, mc, grid, block, samples, mode="normalized"):
+def forward_sampled(q, k, v, mc, grid, block, samples, mode="normalized", phi="elu1"):
     """Plain definition at sampled outputs.  ``samples`` = list of (b, h, [tokens]).
     Returns a list of float64 arrays [len(tokens), d]."""
     n_blocks = int(block_index(grid, block).max()) + 1
@@ -291,8 +314,8 @@ def forward_sampled(q, k, v, mc, grid, block, samples, mode="normalized"):
         kh = np.asarray(k[b, h], np.float64)
         vh = np.asarray(v[b, h], np.float64)
         if mode == "mala":
-            res.append(mala_plain_sampled(qh, kh, vh, toks))
+            res.append(mala_plain_sampled(qh, kh, vh, toks, phi))
         else:
             mch = _as_head_mc(mc, h, n_blocks)
-            res.append(mhla_plain_sampled(qh, kh, vh, mch, grid, block, toks, mode == "normalized"))
+            res.append(mhla_plain_sampled(qh, kh, vh, mch, grid, block, toks, mode == "normalized", phi))
     return res

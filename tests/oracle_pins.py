@@ -44,9 +44,15 @@ def torch_phi(x):
     return torch.nn.functional.elu(torch.as_tensor(np.asarray(x), dtype=torch.float64)) + 1.0
 
 
-def textbook_linear_attention(q, k, v):
+def torch_phi_named(x, phi):
+    t = torch.as_tensor(np.asarray(x), dtype=torch.float64)
+    return {"elu1": lambda: torch.nn.functional.elu(t) + 1.0, "relu": lambda: torch.relu(t),
+            "exp": lambda: torch.exp(t)}[phi]()
+
+
+def textbook_linear_attention(q, k, v, phi="elu1"):
     """Kernelised attention with an explicit N x N score matrix: (phiQ phiK^T V) / (phiQ phiK^T 1)."""
-    qt, kt = torch_phi(q), torch_phi(k)
+    qt, kt = torch_phi_named(q, phi), torch_phi_named(k, phi)
     a = qt @ kt.T
     vv = torch.as_tensor(np.asarray(v), dtype=torch.float64)
     return ((a @ vv) / a.sum(dim=1, keepdim=True)).numpy()
@@ -300,9 +306,90 @@ def pin_batched_forward(o):
     _close(outm[0, 1], o.mala_plain(q[0, 1], k[0, 1], v[0, 1]))
 
 
+def pin_phi_maps(o):
+    """ReLU and exp ([MALA] Ablation names ELU+1, ReLU and exp): closed-form values and the
+    name dispatch."""
+    x = np.array([0.0, 1.0, -1.0, 2.5, -3.0, 1e-300, -1e-300, math.log(2.0), -math.log(4.0)])
+    _close(o.phi_relu(x), [0.0, 1.0, 0.0, 2.5, 0.0, 1e-300, 0.0, math.log(2.0), 0.0], rtol=1e-15, atol=0)
+    _close(o.phi_exp(x), [1.0, math.e, 1 / math.e, math.exp(2.5), math.exp(-3.0), 1.0, 1.0, 2.0, 0.25],
+           rtol=1e-15, atol=0)
+    assert o.phi_exp(np.array([-800.0]))[0] == 0.0 and np.isinf(o.phi_exp(np.array([800.0]))[0])
+    y = np.linspace(-5, 5, 101)
+    for name, f in (("elu1", o.phi_elu1), ("relu", o.phi_relu), ("exp", o.phi_exp)):
+        _close(o.phi_map(y, name), f(y), rtol=0, atol=0)
+    try:
+        o.phi_map(y, "gelu")
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("unknown feature map accepted")
+
+
+def pin_other_maps_blockwise_equals_plain(o):
+    """The token-expanded identity holds for every feature map (pure algebra), and one block is
+    textbook linear attention with that map."""
+    rng = np.random.default_rng(21)
+    for phi in ("relu", "exp"):
+        for grid, block in GEOMS:
+            n = int(np.prod(grid))
+            m = int(np.prod([g // b for g, b in zip(grid, block)]))
+            q, k, v = _rand(rng, n, 6), _rand(rng, n, 6), _rand(rng, n, 6)
+            mc = rng.uniform(0.05, 1.0, (m, m))
+            for norm in (True, False):
+                a = o.mhla_blockwise(q, k, v, mc, grid, block, norm, phi)
+                b = o.mhla_plain(q, k, v, mc, grid, block, norm, phi)
+                assert np.array_equal(np.isnan(a), np.isnan(b))
+                np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12, equal_nan=True)
+            toks = [0, n // 2, n - 1]
+            np.testing.assert_allclose(o.mhla_plain_sampled(q, k, v, mc, grid, block, toks, True, phi),
+                                       o.mhla_plain(q, k, v, mc, grid, block, True, phi)[toks],
+                                       rtol=1e-10, atol=1e-12, equal_nan=True)
+        for grid in [(20,), (4, 5)]:
+            n = int(np.prod(grid))
+            q, k, v = _rand(rng, n, 5), _rand(rng, n, 5), _rand(rng, n, 5)
+            np.testing.assert_allclose(o.mhla_blockwise(q, k, v, None, grid, grid, True, phi),
+                                       textbook_linear_attention(q, k, v, phi), rtol=1e-10,
+                                       atol=1e-12, equal_nan=True)
+
+
+def pin_relu_zero_denominator(o):
+    """With ReLU a query whose features are all <= 0 has q~ = 0: numerator and denominator are
+    both exactly 0, and the division (no epsilon) gives NaN in the blockwise and plain forms;
+    the unnormalised readout gives exact zeros."""
+    rng = np.random.default_rng(22)
+    grid, block = (12,), (4,)
+    q, k, v = np.abs(_rand(rng, 12, 4)), _rand(rng, 12, 4), _rand(rng, 12, 4)
+    q[5] = -q[5]
+    q[7] = 0.0
+    mc = rng.uniform(0.05, 1.0, (3, 3))
+    for f in (o.mhla_blockwise, o.mhla_plain):
+        with np.errstate(invalid="ignore", divide="ignore"):
+            a = f(q, k, v, mc, grid, block, True, "relu")
+        assert np.all(np.isnan(a[[5, 7]])) and not np.any(np.isnan(np.delete(a, [5, 7], axis=0)))
+        u = f(q, k, v, mc, grid, block, False, "relu")
+        assert np.all(u[[5, 7]] == 0.0)
+
+
+def pin_mala_other_maps(o):
+    """MALA under exp and ReLU: weights sum to one, linear form == N x N form."""
+    rng = np.random.default_rng(23)
+    n, d = 30, 6
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    for phi in ("exp", "relu"):
+        qt, kt = o.phi_map(q, phi), o.phi_map(k, phi)
+        ok = qt.sum(axis=1) > 0
+        W = o.mala_weights(qt[ok], kt)
+        _close(W.sum(axis=1), np.ones(ok.sum()))
+        _close(o.mala_linear(q, k, v, phi)[ok], W @ v)
+        _close(o.mala_plain(q, k, v, phi)[ok], W @ v)
+        _close(o.mala_plain_sampled(q, k, v, [int(np.flatnonzero(ok)[0])], phi),
+               (W @ v)[:1])
+
+
 ALL_PINS = [
     pin_phi, pin_golden_mhla_1d, pin_golden_mhla_2d, pin_golden_mala, pin_blockwise_equals_plain,
     pin_single_block_is_linear_attention, pin_all_ones_mixing_is_global, pin_identity_mixing_is_block_local,
     pin_rank_bounds, pin_normalized_invariances, pin_mala_properties, pin_gather_equals_block_major_1d,
-    pin_full_width_tiles_are_spans, pin_batched_forward,
+    pin_full_width_tiles_are_spans, pin_batched_forward, pin_phi_maps,
+    pin_other_maps_blockwise_equals_plain, pin_relu_zero_denominator, pin_mala_other_maps,
 ]

@@ -63,15 +63,15 @@ def _readout_wrong_block(qt, St, zt, bidx, normalized=True):
     return _ORIG["readout"](qt, St, zt, (bidx + 1) % m, normalized)
 
 
-def _mala_linear_no_one_in_beta(q, k, v):
-    qt, kt = O.phi_elu1(q), O.phi_elu1(k)
+def _mala_linear_no_one_in_beta(q, k, v, phi="elu1"):
+    qt, kt = O.phi_map(q, phi), O.phi_map(k, phi)
     v = np.asarray(v, np.float64)
     s = qt @ kt.sum(0)
     return (1.0 / s)[:, None] * (qt @ (kt.T @ v)) - (s / kt.shape[0])[:, None] * v.sum(0)
 
 
-def _mala_linear_gamma_wrong_n(q, k, v):
-    qt, kt = O.phi_elu1(q), O.phi_elu1(k)
+def _mala_linear_gamma_wrong_n(q, k, v, phi="elu1"):
+    qt, kt = O.phi_map(q, phi), O.phi_map(k, phi)
     v = np.asarray(v, np.float64)
     s = qt @ kt.sum(0)
     return (1 + 1.0 / s)[:, None] * (qt @ (kt.T @ v)) - (s / (kt.shape[0] - 1))[:, None] * v.sum(0)
@@ -79,6 +79,15 @@ def _mala_linear_gamma_wrong_n(q, k, v):
 
 def _mala_weights_sign(qt, kt):
     return -_ORIG["mala_weights"](qt, kt) + 2.0 / np.asarray(kt).shape[0]
+
+
+def _phi_relu_leaky(x):
+    x = np.asarray(x, np.float64)
+    return np.where(x > 0.0, x, 0.01 * x)
+
+
+def _phi_exp_base2(x):
+    return np.exp2(np.asarray(x, np.float64))
 
 
 _ORIG = {name: getattr(O, name) for name in
@@ -98,6 +107,8 @@ MUTATIONS = {
     "mala_beta_missing_one": ("mala_linear", _mala_linear_no_one_in_beta),
     "mala_gamma_wrong_n": ("mala_linear", _mala_linear_gamma_wrong_n),
     "mala_weights_sign": ("mala_weights", _mala_weights_sign),
+    "relu_leaky": ("phi_relu", _phi_relu_leaky),
+    "exp_base_two": ("phi_exp", _phi_exp_base2),
 }
 
 
