@@ -60,7 +60,11 @@ typedef enum {
 
 typedef enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_FP32 = 1 } mhla_dtype;
 
-typedef enum { MHLA_PHI_ELU1 = 0 } mhla_phi;
+/* Feature map phi applied to Q and K.  ELU+1 is the default; ReLU and exp are the other maps the
+ * "Rectifying Magnitude Neglect in Linear Attention" notes find equivalent (Ablation).  Readings:
+ * relu(x) = max(x, 0); exp(x) = e^x elementwise with no max subtraction.  With ReLU a query with no
+ * positive feature has a zero normaliser: the IEEE result 0/0 = NaN is returned (no epsilon). */
+typedef enum { MHLA_PHI_ELU1 = 0, MHLA_PHI_RELU = 1, MHLA_PHI_EXP = 2 } mhla_phi;
 
 typedef enum {
   MHLA_READOUT_NORMALIZED = 0,    /* o = phi(q)^T S~_i / phi(q)^T z~_i                         */
@@ -69,7 +73,9 @@ typedef enum {
 } mhla_readout;
 
 typedef enum {
-  MHLA_ACCURACY_AUTO = 0,   /* bf16 operands for MHLA with bf16 inputs; split for MALA / fp32   */
+  MHLA_ACCURACY_AUTO = 0,   /* bf16 operands for MHLA with ELU+1 and bf16 inputs; split for     */
+                            /* MALA, fp32 inputs and the ReLU / exp maps (whose outputs sit      */
+                            /* near the 2e-2 bar with single bf16 operands)                      */
   MHLA_ACCURACY_BF16 = 1,   /* single bf16 MFMA operands, fp32 accumulation                     */
   MHLA_ACCURACY_SPLIT = 2   /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
 } mhla_accuracy;

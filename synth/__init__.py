@@ -51,6 +51,7 @@ class Workload:
     seed: int
     mc_kind: str                     # "softmax_l1" | "softmax_l1_noise" | "softmax_gauss" | "none"
     readout: str = "normalized"      # "normalized" | "unnormalized" | "mala"
+    phi: str = "elu1"                # feature map: "elu1" | "relu" | "exp"
 
     @property
     def ndim(self) -> int:

@@ -24,7 +24,7 @@ def run_hip(w: synth.Workload, q, k, v, mc, *, out_dtype="fp32", accuracy="auto"
     import torch
     mc_per_head = mc is not None and np.ndim(mc) == 3
     plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
-                  in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, accuracy=accuracy,
+                  in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, accuracy=accuracy, phi=w.phi,
                   mc_per_head=mc_per_head)
     tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
     tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
@@ -53,4 +53,4 @@ def announce(msg: str) -> None:
 
 
 def oracle_full(w, q, k, v, mc):
-    return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout)
+    return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout, phi=w.phi)

@@ -100,6 +100,11 @@ def test_create_null_arguments():
     assert lib.mhla_destroy(None) == 0
 
 
+def test_feature_maps_accepted():
+    for phi in ("elu1", "relu", "exp"):
+        assert _status(_desc(phi=phi)) == 0
+
+
 def test_mala_with_one_block_is_accepted():
     d = _desc(block=(64, 64), readout="mala")
     assert _status(d) == 0

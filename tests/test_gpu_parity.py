@@ -99,6 +99,89 @@ def test_bf16_output_within_bar_plus_output_rounding():
     assert excess.max() <= 0, excess.max()
 
 
+# ------------------------------------------------------------------------------------------
+# the other feature maps (ReLU, exp) on every kernel path
+# ------------------------------------------------------------------------------------------
+
+MAP_SHAPES = ["tiny", "tiny_mala", "ragged1d", "odd2d_d32", "odd3d_d128", "d16_bf16", "one_token_blocks",
+              "unnorm_2d", "mala_ragged", "fp32_2d", "fp32_mala", "m100", "m200_d128"]
+MAP_CASES = [w.with_(name=f"{w.name}_{phi}", phi=phi) for w in SMALL if w.name in MAP_SHAPES
+             for phi in ("relu", "exp")]
+
+
+def _compare_with_nan(w, got, want):
+    """NaN (ReLU's 0/0) at exactly the oracle's positions; the bar on every other element."""
+    nan_g, nan_w = np.isnan(got), np.isnan(want)
+    assert np.array_equal(nan_g, nan_w), (int(nan_g.sum()), int(nan_w.sum()))
+    ok = ~nan_w
+    rms = np.sqrt(np.mean(want[ok] ** 2))
+    return float(np.max(np.abs(got[ok] - want[ok]))) / rms
+
+
+@pytest.mark.parametrize("w", MAP_CASES, ids=lambda w: w.name)
+def test_parity_feature_maps_small(w):
+    announce(f"{w.name} shape={w.qkv_shape}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want = oracle_full(w, q, k, v, mc)
+    err = _compare_with_nan(w, got, want)
+    print(f"  err={err:.3e}")
+    assert err <= _tol(w), (w.name, err)
+
+
+BF16_OPERAND_MAP_SHAPES = ["ragged1d", "odd2d_d32", "odd3d_d128", "m100", "m200_d128"]
+
+
+@pytest.mark.parametrize("phi", ["relu", "exp"])
+@pytest.mark.parametrize("name", BF16_OPERAND_MAP_SHAPES)
+def test_feature_maps_bf16_operand_path(name, phi):
+    """The single-bf16-operand kernels under ReLU / exp (chosen explicitly; the automatic choice
+    for these maps is the split path) on shapes with a separate mixing kernel and with d = 32..128."""
+    w = next(x for x in SMALL if x.name == name).with_(phi=phi)
+    announce(f"{name} phi={phi} accuracy=bf16")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc, accuracy="bf16")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want = oracle_full(w, q, k, v, mc)
+    err = _compare_with_nan(w, got, want)
+    print(f"  err={err:.3e}")
+    assert err <= BF16_TOL, (name, phi, err)
+
+
+@pytest.mark.parametrize("phi", ["relu", "exp"])
+@pytest.mark.parametrize("name", ["image", "video3d"])
+def test_parity_feature_maps_full(name, phi):
+    w = synth.WORKLOADS[name].with_(phi=phi)
+    announce(f"full {name} phi={phi}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got = run_hip(w, q, k, v, mc)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want = oracle_full(w, q, k, v, mc)
+    err = _compare_with_nan(w, got, want)
+    print(f"  err={err:.3e}")
+    assert err <= BF16_TOL, (name, phi, err)
+
+
+def test_relu_zero_denominator_gives_nan_where_the_oracle_does():
+    """Queries with no positive feature have phi(q) = 0 under ReLU: 0/0 in both the kernels and
+    the oracle (normalised), exact zeros unnormalised."""
+    w = synth.Workload("relu_zero_q", "bf16", 1, 2, 32, (256,), (64,), 31, "softmax_l1", phi="relu")
+    announce("relu zero denominator")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    q = np.abs(q)
+    q[0, 0, [3, 100, 255]] = -q[0, 0, [3, 100, 255]]
+    q[0, 1, 17] = 0.0
+    got = run_hip(w, q, k, v, mc)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want = oracle_full(w, q, k, v, mc)
+    assert np.all(np.isnan(got[0, 0, [3, 100, 255]])) and np.all(np.isnan(got[0, 1, 17]))
+    assert _compare_with_nan(w, got, want) <= BF16_TOL
+    wu = w.with_(readout="unnormalized")
+    gu = run_hip(wu, q, k, v, mc)
+    assert np.all(gu[0, 0, [3, 100, 255]] == 0.0) and np.all(gu[0, 1, 17] == 0.0)
+
+
 BF16_OUT = [w for w in SMALL if w.dtype == "bf16"] + [synth.WORKLOADS[n] for n in FULL_NAMES_BF16_OUT]
 
 

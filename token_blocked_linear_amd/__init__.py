@@ -12,7 +12,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = [
-    "MHLA_OK", "MHLA_DTYPE_BF16", "MHLA_DTYPE_FP32", "MHLA_PHI_ELU1",
+    "MHLA_OK", "MHLA_DTYPE_BF16", "MHLA_DTYPE_FP32", "MHLA_PHI_ELU1", "MHLA_PHI_RELU", "MHLA_PHI_EXP",
     "MHLA_READOUT_NORMALIZED", "MHLA_READOUT_UNNORMALIZED", "MHLA_READOUT_MALA",
     "MHLA_ACCURACY_AUTO", "MHLA_ACCURACY_BF16", "MHLA_ACCURACY_SPLIT",
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
@@ -23,13 +23,14 @@ __all__ = [
 
 MHLA_OK = 0
 MHLA_DTYPE_BF16, MHLA_DTYPE_FP32 = 0, 1
-MHLA_PHI_ELU1 = 0
+MHLA_PHI_ELU1, MHLA_PHI_RELU, MHLA_PHI_EXP = 0, 1, 2
 MHLA_READOUT_NORMALIZED, MHLA_READOUT_UNNORMALIZED, MHLA_READOUT_MALA = 0, 1, 2
 MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT = 0, 1, 2
 
 _READOUTS = {"normalized": MHLA_READOUT_NORMALIZED, "unnormalized": MHLA_READOUT_UNNORMALIZED,
              "mala": MHLA_READOUT_MALA}
 _DTYPES = {"bf16": MHLA_DTYPE_BF16, "fp32": MHLA_DTYPE_FP32}
+_PHIS = {"elu1": MHLA_PHI_ELU1, "relu": MHLA_PHI_RELU, "exp": MHLA_PHI_EXP}
 _ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MHLA_ACCURACY_SPLIT}
 
 EXPORTED_SYMBOLS = (
@@ -184,14 +185,14 @@ def mhla_timing_reset(h) -> None:
 
 def make_desc(*, grid: Sequence[int], block: Sequence[int], batch: int, heads: int, head_dim: int,
               in_dtype: str = "bf16", out_dtype: str = "fp32", readout: str = "normalized",
-              accuracy: str = "auto", mc_per_head: bool = False) -> MhlaDesc:
+              accuracy: str = "auto", mc_per_head: bool = False, phi: str = "elu1") -> MhlaDesc:
     if len(grid) != len(block) or not 1 <= len(grid) <= 3:
         raise ValueError("grid and block must have the same rank, 1 to 3")
     d = MhlaDesc()
     d.struct_size = ctypes.sizeof(MhlaDesc)
     d.in_dtype = _DTYPES[in_dtype]
     d.out_dtype = _DTYPES[out_dtype]
-    d.phi = MHLA_PHI_ELU1
+    d.phi = _PHIS[phi]
     d.readout = _READOUTS[readout]
     d.accuracy = _ACCURACY[accuracy]
     d.ndim = len(grid)

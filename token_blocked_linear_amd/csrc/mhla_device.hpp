@@ -210,9 +210,21 @@ __device__ inline void split_bf16x2(float x0, float x1, uint32_t& hi2, uint32_t&
   lo2 = pack_bf16x2(x0 - __uint_as_float(hi2 << 16), x1 - __uint_as_float(hi2 & 0xffff0000u));
 }
 
+// Feature maps ("MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head",
+// Background: a positive phi; "Rectifying Magnitude Neglect in Linear Attention", Ablation: ELU+1,
+// ReLU and exp work alike).  Numbering as mhla_phi in include/mhla.h.
+enum { kPhiElu1 = 0, kPhiRelu = 1, kPhiExp = 2 };
+
 // ELU(x) + 1 with alpha = 1.
 __device__ inline float phi_elu1(float x) {
   return x > 0.0f ? x + 1.0f : __expf(x);
+}
+
+template <int PHI>
+__device__ inline float phi_map(float x) {
+  if constexpr (PHI == kPhiRelu) return fmaxf(x, 0.0f);
+  else if constexpr (PHI == kPhiExp) return __expf(x);
+  else return phi_elu1(x);
 }
 
 __device__ inline f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {

@@ -15,11 +15,11 @@
 
 namespace mhla {
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
-                          bool want_u, bool out_bf16, int n_units, hipStream_t stream);
+                          bool want_u, bool out_bf16, int phi, int n_units, hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream);
 hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
-                          bool split, int fuse, int n_wg, hipStream_t stream);
+                          bool split, int fuse, int phi, int n_wg, hipStream_t stream);
 }  // namespace mhla
 
 namespace {
@@ -73,7 +73,8 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   if (d->struct_size != sizeof(mhla_desc)) return MHLA_ERR_INVALID_ARG;
   if (d->in_dtype != MHLA_DTYPE_BF16 && d->in_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
   if (d->out_dtype != MHLA_DTYPE_BF16 && d->out_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
-  if (d->phi != MHLA_PHI_ELU1) return MHLA_ERR_UNSUPPORTED;
+  if (d->phi != MHLA_PHI_ELU1 && d->phi != MHLA_PHI_RELU && d->phi != MHLA_PHI_EXP)
+    return MHLA_ERR_UNSUPPORTED;
   if (d->readout < MHLA_READOUT_NORMALIZED || d->readout > MHLA_READOUT_MALA) return MHLA_ERR_UNSUPPORTED;
   if (d->accuracy < MHLA_ACCURACY_AUTO || d->accuracy > MHLA_ACCURACY_SPLIT) return MHLA_ERR_UNSUPPORTED;
   if (d->mc_per_head != 0 && d->mc_per_head != 1) return MHLA_ERR_INVALID_ARG;
@@ -135,7 +136,7 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   else if (d->accuracy == MHLA_ACCURACY_BF16)
     P->split = false;
   else
-    P->split = P->mala || P->in_fp32;
+    P->split = P->mala || P->in_fp32 || d->phi != MHLA_PHI_ELU1;
   P->split_v = P->split && P->in_fp32;
 
   const int dk = P->d < 32 ? 32 : P->d;
@@ -307,7 +308,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.mcf_nitp = h->mix.nitp;
     sp.mcf_nbc = h->mix.nbc;
     hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
-                                        h->mix_mfma, (int)(h->sum_splits * h->M * h->BH), s);
+                                        h->mix_mfma, (int)h->desc.phi, (int)(h->sum_splits * h->M * h->BH), s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
     if (mix_kernel) {
@@ -365,7 +366,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     rp.H = (int32_t)h->H;
     rp.ssplits = h->sum_splits;
     e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse,
-                             (int)(h->rd_splits * h->M * h->BH), s);
+                             (int)h->desc.phi, (int)(h->rd_splits * h->M * h->BH), s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
     return MHLA_OK;
   } catch (...) {

@@ -28,6 +28,8 @@
 // lane groups of a token write 64 (bf16) or 128 (fp32) contiguous bytes.  In LDS, bit 2 of a
 // fragment's lane index is flipped when bit 3 is set, so that every 8 lanes of these operand
 // reads cover all banks once.
+#include <type_traits>
+
 #include "mhla_device.hpp"
 
 namespace mhla {
@@ -102,7 +104,7 @@ __device__ inline AOffsets a_offsets(int lane) {
 // NT 16-token tiles at once: phi(Q) -> MFMAs against the staged summary (each A operand read
 // from LDS feeds the NT tiles) -> scale -> 16-byte stores.  cur[t] holds this lane's query
 // features of tile t; coff[t] the element offset of its token row in Q / O.
-template <typename TIn, typename TOut, int D, bool SPLIT, int NT>
+template <typename TIn, typename TOut, int D, bool SPLIT, int NT, int PHI>
 __device__ __forceinline__ void readout_tiles(const In8<TIn> (&cur)[NT][Dims<D>::NKC],
                                               const bool (&cvalid)[NT], const int64_t (&coff)[NT],
                                               const uint16_t* s_hi, const uint16_t* s_lo,
@@ -129,7 +131,7 @@ __device__ __forceinline__ void readout_tiles(const In8<TIn> (&cur)[NT][Dims<D>:
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x0 = phi_elu1(cur[t][kc].get(2 * i)), x1 = phi_elu1(cur[t][kc].get(2 * i + 1));
+        const float x0 = phi_map<PHI>(cur[t][kc].get(2 * i)), x1 = phi_map<PHI>(cur[t][kc].get(2 * i + 1));
         if (SPLIT) {
           uint32_t h, l;
           split_bf16x2(x0, x1, h, l);
@@ -274,7 +276,7 @@ constexpr int readout_tiles_per_step() { return sizeof(TIn) == 2 && D <= 64 ? MH
 template <typename TIn, int D>
 constexpr int readout_waves() { return sizeof(TIn) == 4 && D == 128 ? 3 : 4; }
 
-template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
+template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE, int PHI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     readout_waves<TIn, D>()))) void readout_kernel(
     ReadoutParams p, int mode) {
@@ -515,57 +517,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       coff[j] = toff[j];
     }
     if (tile + NT * WSTEP < U.n_tiles) issue_step(tile + NT * WSTEP);
-    readout_tiles<TIn, TOut, D, SPLIT, NT>(cur, cvalid, coff, s_hi, s_lo, s_z, s_ub, ao, lane, mode, p.o);
+    readout_tiles<TIn, TOut, D, SPLIT, NT, PHI>(cur, cvalid, coff, s_hi, s_lo, s_z, s_ub, ao, lane, mode, p.o);
   }
 }
 
-template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
+template <int PHI, typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
 static hipError_t launch_t(const ReadoutParams& p, int mode, int n_wg, hipStream_t s) {
   using Dm = Dims<D>;
   const size_t lds = (size_t)Dm::FRAG * 2 * (SPLIT ? 2 : 1) + (size_t)Dm::NKC * 512 * 2 + 2 * D * 4;
-  hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, SPLIT, FUSE>), dim3(n_wg), dim3(kThreads), lds,
+  hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, SPLIT, FUSE, PHI>), dim3(n_wg), dim3(kThreads), lds,
                      s, p, mode);
   return hipGetLastError();
 }
 
 // Valid (split, fuse) pairs: the bf16-stack fusion exists for bf16 operands only; the others
 // for both operand precisions.
-template <typename TIn, typename TOut, int D>
+template <int PHI, typename TIn, typename TOut, int D>
 static hipError_t dispatch_fuse(const ReadoutParams& p, int mode, bool split, int fuse, int n_wg,
                                 hipStream_t s) {
   if (split) {
-    if (fuse == kFuseNone) return launch_t<TIn, TOut, D, true, kFuseNone>(p, mode, n_wg, s);
-    if (fuse == kFusePartials) return launch_t<TIn, TOut, D, true, kFusePartials>(p, mode, n_wg, s);
+    if (fuse == kFuseNone) return launch_t<PHI, TIn, TOut, D, true, kFuseNone>(p, mode, n_wg, s);
+    if (fuse == kFusePartials) return launch_t<PHI, TIn, TOut, D, true, kFusePartials>(p, mode, n_wg, s);
     return hipErrorInvalidValue;
   }
-  if (fuse == kFuseNone) return launch_t<TIn, TOut, D, false, kFuseNone>(p, mode, n_wg, s);
-  if (fuse == kFusePartials) return launch_t<TIn, TOut, D, false, kFusePartials>(p, mode, n_wg, s);
+  if (fuse == kFuseNone) return launch_t<PHI, TIn, TOut, D, false, kFuseNone>(p, mode, n_wg, s);
+  if (fuse == kFusePartials) return launch_t<PHI, TIn, TOut, D, false, kFusePartials>(p, mode, n_wg, s);
   if constexpr (sizeof(TIn) == 2) {
-    if (fuse == kFuseBf16) return launch_t<TIn, TOut, D, false, kFuseBf16>(p, mode, n_wg, s);
+    if (fuse == kFuseBf16) return launch_t<PHI, TIn, TOut, D, false, kFuseBf16>(p, mode, n_wg, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename TIn, typename TOut>
+template <int PHI, typename TIn, typename TOut>
 static hipError_t dispatch_d(const ReadoutParams& p, int d, int mode, bool split, int fuse,
                              int n_wg, hipStream_t s) {
   switch (d) {
-    case 16: return dispatch_fuse<TIn, TOut, 16>(p, mode, split, fuse, n_wg, s);
-    case 32: return dispatch_fuse<TIn, TOut, 32>(p, mode, split, fuse, n_wg, s);
-    case 64: return dispatch_fuse<TIn, TOut, 64>(p, mode, split, fuse, n_wg, s);
-    case 128: return dispatch_fuse<TIn, TOut, 128>(p, mode, split, fuse, n_wg, s);
+    case 16: return dispatch_fuse<PHI, TIn, TOut, 16>(p, mode, split, fuse, n_wg, s);
+    case 32: return dispatch_fuse<PHI, TIn, TOut, 32>(p, mode, split, fuse, n_wg, s);
+    case 64: return dispatch_fuse<PHI, TIn, TOut, 64>(p, mode, split, fuse, n_wg, s);
+    case 128: return dispatch_fuse<PHI, TIn, TOut, 128>(p, mode, split, fuse, n_wg, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 // n_wg = splits * M * BH workgroups (one-dimensional grid).
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
-                          bool split, int fuse, int n_wg, hipStream_t stream) {
-  if (in_fp32)
-    return out_fp32 ? dispatch_d<float, float>(p, d, mode, split, fuse, n_wg, stream)
-                    : dispatch_d<float, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
-  return out_fp32 ? dispatch_d<uint16_t, float>(p, d, mode, split, fuse, n_wg, stream)
-                  : dispatch_d<uint16_t, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
+                          bool split, int fuse, int phi, int n_wg, hipStream_t stream) {
+  auto go = [&](auto phi_c) {
+    constexpr int PHI = decltype(phi_c)::value;
+    if (in_fp32)
+      return out_fp32 ? dispatch_d<PHI, float, float>(p, d, mode, split, fuse, n_wg, stream)
+                      : dispatch_d<PHI, float, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
+    return out_fp32 ? dispatch_d<PHI, uint16_t, float>(p, d, mode, split, fuse, n_wg, stream)
+                    : dispatch_d<PHI, uint16_t, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
+  };
+  switch (phi) {
+    case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
+    case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
+    case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mhla

@@ -15,11 +15,13 @@
 // 16-byte LDS read.  The next round's loads -- of this unit or the next one -- are in flight
 // during the MFMA phase.  z (and u) come from the same MFMAs against an all-ones operand, so
 // they carry exactly the operands' rounding and need no cross-thread reduction.
+#include <type_traits>
+
 #include "mhla_device.hpp"
 
 namespace mhla {
 
-template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16>
+template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16, int PHI>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int n_units) {
   using Dm = Dims<D>;
   constexpr int DK = Dm::DK, NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         u32x4_t hi, lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x0 = phi_elu1(rk[2 * i].get(e)), x1 = phi_elu1(rk[2 * i + 1].get(e));
+          const float x0 = phi_map<PHI>(rk[2 * i].get(e)), x1 = phi_map<PHI>(rk[2 * i + 1].get(e));
           if (SPLIT_K) {
             uint32_t h, l;
             split_bf16x2(x0, x1, h, l);
@@ -376,13 +378,13 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   }
 }
 
-template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false>
+template <int PHI, typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false>
 static hipError_t launch_summary_t(const SummaryParams& p, int n_units, hipStream_t stream) {
   using Dm = Dims<D>;
   constexpr int LPR = D / 8, TG_ALL = kThreads / LPR, TG = TG_ALL < 32 ? TG_ALL : 32;
   constexpr int ROUND = TG * 8, PITCH = ROUND;
   const size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2;
-  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16>;
+  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16, PHI>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -395,47 +397,56 @@ static hipError_t launch_summary_t(const SummaryParams& p, int n_units, hipStrea
   return hipGetLastError();
 }
 
-template <typename TIn, int D>
+template <int PHI, typename TIn, int D>
 static hipError_t dispatch_flags(const SummaryParams& p, bool split_k, bool split_v, bool want_u,
                                  bool out_bf16, int n, hipStream_t s) {
   if constexpr (sizeof(TIn) == 2) {
     if (split_v) return hipErrorInvalidValue;   // bf16 V is exact: never split
     if (out_bf16) {
       if (split_k || want_u) return hipErrorInvalidValue;
-      return launch_summary_t<TIn, D, false, false, false, true>(p, n, s);
+      return launch_summary_t<PHI, TIn, D, false, false, false, true>(p, n, s);
     }
     if (split_k)
-      return want_u ? launch_summary_t<TIn, D, true, false, true>(p, n, s)
-                    : launch_summary_t<TIn, D, true, false, false>(p, n, s);
-    return want_u ? launch_summary_t<TIn, D, false, false, true>(p, n, s)
-                  : launch_summary_t<TIn, D, false, false, false>(p, n, s);
+      return want_u ? launch_summary_t<PHI, TIn, D, true, false, true>(p, n, s)
+                    : launch_summary_t<PHI, TIn, D, true, false, false>(p, n, s);
+    return want_u ? launch_summary_t<PHI, TIn, D, false, false, true>(p, n, s)
+                  : launch_summary_t<PHI, TIn, D, false, false, false>(p, n, s);
   } else {
     if (split_k != split_v || out_bf16) return hipErrorInvalidValue;
     if (split_k)
-      return want_u ? launch_summary_t<TIn, D, true, true, true>(p, n, s)
-                    : launch_summary_t<TIn, D, true, true, false>(p, n, s);
-    return want_u ? launch_summary_t<TIn, D, false, false, true>(p, n, s)
-                  : launch_summary_t<TIn, D, false, false, false>(p, n, s);
+      return want_u ? launch_summary_t<PHI, TIn, D, true, true, true>(p, n, s)
+                    : launch_summary_t<PHI, TIn, D, true, true, false>(p, n, s);
+    return want_u ? launch_summary_t<PHI, TIn, D, false, false, true>(p, n, s)
+                  : launch_summary_t<PHI, TIn, D, false, false, false>(p, n, s);
   }
 }
 
-template <typename TIn>
+template <int PHI, typename TIn>
 static hipError_t dispatch_d(const SummaryParams& p, int d, bool sk, bool sv, bool wu, bool ob,
                              int n, hipStream_t s) {
   switch (d) {
-    case 16: return dispatch_flags<TIn, 16>(p, sk, sv, wu, ob, n, s);
-    case 32: return dispatch_flags<TIn, 32>(p, sk, sv, wu, ob, n, s);
-    case 64: return dispatch_flags<TIn, 64>(p, sk, sv, wu, ob, n, s);
-    case 128: return dispatch_flags<TIn, 128>(p, sk, sv, wu, ob, n, s);
+    case 16: return dispatch_flags<PHI, TIn, 16>(p, sk, sv, wu, ob, n, s);
+    case 32: return dispatch_flags<PHI, TIn, 32>(p, sk, sv, wu, ob, n, s);
+    case 64: return dispatch_flags<PHI, TIn, 64>(p, sk, sv, wu, ob, n, s);
+    case 128: return dispatch_flags<PHI, TIn, 128>(p, sk, sv, wu, ob, n, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 // n_units = splits * M * BH work units; the kernel picks its own persistent grid.
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
-                          bool want_u, bool out_bf16, int n_units, hipStream_t stream) {
-  return in_fp32 ? dispatch_d<float>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream)
-                 : dispatch_d<uint16_t>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream);
+                          bool want_u, bool out_bf16, int phi, int n_units, hipStream_t stream) {
+  auto go = [&](auto phi_c) {
+    constexpr int PHI = decltype(phi_c)::value;
+    return in_fp32 ? dispatch_d<PHI, float>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream)
+                   : dispatch_d<PHI, uint16_t>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream);
+  };
+  switch (phi) {
+    case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
+    case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
+    case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mhla
