@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long1d] [--all]
 
+Defaults: 20 warm-up and 100 timed steps.
+
 A step is one full forward (summary -> mixing -> readout) over one batch of seeded synthetic
 input already resident in HBM.  W untimed steps, then exactly K steps between
 torch.cuda.synchronize() calls; `value` is tokens/s = steps * B * N / elapsed.  Per-kernel
@@ -71,6 +73,26 @@ def measured_traffic(workload: str, kernel: str, out_dtype: str):
             if (r.get("workload"), r.get("kernel"), r.get("out_dtype")) == (workload, kernel, out_dtype):
                 return r["hbm_bytes_per_launch"] if r.get("source_digest") == digest else None
     return None
+
+
+def measured_copy_GBps(n_bytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy bandwidth (read + write bytes / time) measured now: the practical
+    HBM ceiling the kernels are also reported against."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n_bytes / t / 1e9
 
 
 def copy_calibration(n_bytes: int = 1 << 30, reps: int = 10):
@@ -223,8 +245,8 @@ def cpu_baseline(res, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long1d", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also time the other N=4096..65536 workloads")
     ap.add_argument("--out-dtype", default="bf16", choices=["fp32", "bf16"])
@@ -265,6 +287,11 @@ def main():
         roof = {"bound": pk["bound"], "achieved": pk["TFLOPs"], "peak": peak, "unit": "TFLOP/s",
                 "frac": pk["frac"], "traffic": None, "kernel": dom,
                 "alg_flops_per_launch": a["flops"], "mean_launch_us": pk["us"]}
+
+    copy_bw = measured_copy_GBps()
+    if roof["unit"] == "GB/s":
+        roof["measured_copy_GBps"] = round(copy_bw, 1)
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_bw, 4)
 
     others = {}
     if args.all:
