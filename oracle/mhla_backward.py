@@ -84,9 +84,13 @@ def mhla_backward_blockwise(q, k, v, mc, grid, block, do, normalized=True, phi="
     dmc = dSt.reshape(m, -1) @ S.reshape(m, -1).T + dzt @ z.T
     dS = (mc.T @ dSt.reshape(m, -1)).reshape(S.shape)
     dz = mc.T @ dzt
-    # summary backward, token by token through its block
-    dkt = np.einsum("jcd,jd->jc", dS[bidx], v) + dz[bidx]
-    dv = np.einsum("jcd,jc->jd", dS[bidx], kt)
+    # summary backward: every token of block b goes through dS_b and dz_b
+    dkt = np.empty_like(kt)
+    dv = np.empty_like(v)
+    for b in range(n_blocks):
+        sel = np.nonzero(bidx == b)[0]
+        dkt[sel] = v[sel] @ dS[b].T + dz[b][None, :]
+        dv[sel] = kt[sel] @ dS[b]
     return dqt * dphi_map(q, phi), dkt * dphi_map(k, phi), dv, dmc
 
 
