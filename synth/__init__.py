@@ -35,7 +35,7 @@ __all__ = [
     "Workload", "WORKLOADS", "get_workload", "block_grid_shape", "num_blocks",
     "round_to_bf16", "bf16_bits", "bits_to_f32",
     "mc_softmax_l1", "mc_locality_init", "mc_softmax_l1_noisy_clipped", "mc_softmax_gaussian",
-    "make_inputs", "make_mc",
+    "make_inputs", "make_mc", "make_grad_output",
 ]
 
 
@@ -203,6 +203,17 @@ def make_inputs(w: Workload, rng: Optional[np.random.Generator] = None):
         raise ValueError(w.dtype)
     mc = make_mc(w, rng)
     return q, k, v, mc, rng
+
+
+def make_grad_output(w: Workload, rng: np.random.Generator, dtype: str = "fp32") -> np.ndarray:
+    """Upstream gradient dL/dO for the backward: [B, H, N, d] standard normal float32, rounded
+    to bf16 when ``dtype`` is "bf16" (the element type it crosses the boundary in)."""
+    do = rng.standard_normal(w.qkv_shape, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16(do)
+    if dtype != "fp32":
+        raise ValueError(dtype)
+    return do
 
 
 def make_mc(w: Workload, rng: np.random.Generator):

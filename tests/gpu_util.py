@@ -54,3 +54,31 @@ def announce(msg: str) -> None:
 
 def oracle_full(w, q, k, v, mc):
     return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout, phi=w.phi)
+
+
+def run_hip_backward(w: synth.Workload, q, k, v, mc, do, *, out_dtype="fp32", want_dmc=True, repeat=1):
+    """Backward through the C ABI; returns float64 numpy (dq, dk, dv, dmc or None), or a list of
+    such tuples for ``repeat`` > 1 (same inputs, fresh outputs every call)."""
+    import torch
+    mc_per_head = mc is not None and np.ndim(mc) == 3
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, phi=w.phi,
+                  mc_per_head=mc_per_head)
+    tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
+    tdo = to_device(do, out_dtype)
+    tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
+    ws = plan.alloc_backward_workspace()
+    res = []
+    for _ in range(repeat):
+        dq, dk, dv = (torch.empty_like(tdo) for _ in range(3))
+        dmc = torch.full(tuple(np.shape(mc)), float("nan"), device="cuda:0") if (want_dmc and mc is not None) else None
+        plan.backward(tq, tk, tv, tmc, tdo, dq, dk, dv, dmc, ws)
+        res.append((dq, dk, dv, dmc))
+    torch.cuda.synchronize()
+    out = [tuple(None if t is None else t.float().cpu().numpy().astype(np.float64) for t in r) for r in res]
+    plan.close()
+    return out if repeat > 1 else out[0]
+
+
+def oracle_backward(w, q, k, v, mc, do, heads=None):
+    return oracle.backward(q, k, v, mc, w.grid, w.block, do, mode=w.readout, heads=heads, phi=w.phi)

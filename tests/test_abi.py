@@ -149,6 +149,42 @@ def test_forward_argument_errors_before_launch():
     p.close()
 
 
+def test_backward_support_and_workspace():
+    _lib_or_skip()
+    p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
+    assert T.mhla_backward_workspace_size(p.handle) > 0
+    p.close()
+    for kw in (dict(block=(64, 64), readout="mala"), dict(head_dim=16)):
+        u = T.Plan(**dict(dict(grid=(64, 64), block=(16, 16), batch=2, heads=2, head_dim=64), **kw))
+        with pytest.raises(T.MhlaError) as e:
+            T.mhla_backward_workspace_size(u.handle)
+        assert e.value.status == 2                           # MHLA_ERR_UNSUPPORTED
+        u.close()
+
+
+def test_backward_argument_errors_before_launch():
+    """Rejected by validation, before any launch (a launch here would give MHLA_ERR_HIP)."""
+    lib = _lib_or_skip()
+    p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
+    ws = T.mhla_backward_workspace_size(p.handle)
+    Q, K, V, MC, DO, DQ, DK, DV, DMC, W = (0x10000 * i for i in range(1, 11))
+    W = 0x1000000
+    f = lambda *a: lib.mhla_backward(p.handle, *a)  # noqa: E731
+    assert f(None, K, V, MC, DO, DQ, DK, DV, DMC, W, ws, None) == 1     # NULL q
+    assert f(Q, K, V, MC, None, DQ, DK, DV, DMC, W, ws, None) == 1      # NULL dO
+    assert f(Q, K, V, MC, DO, DQ, DK, None, DMC, W, ws, None) == 1      # NULL dv
+    assert f(Q, K, V, None, DO, DQ, DK, DV, DMC, W, ws, None) == 1      # NULL M_c with M > 1
+    assert f(Q, K, V, MC, DO, DO, DK, DV, DMC, W, ws, None) == 1        # dq aliases dO
+    assert f(Q, K, V, MC, DO, DQ, DQ, DV, DMC, W, ws, None) == 1        # dk aliases dq
+    assert f(Q, K, V, MC, DO, DQ + 8, DK, DV, DMC, W, ws, None) == 1    # misaligned dq
+    assert f(Q, K, V, MC, DO, DQ, DK, DV, DMC + 2, W, ws, None) == 1    # misaligned dM_c
+    assert f(Q, K, V, MC, DO, DQ, DK, DV, DMC, None, ws, None) == 4     # no workspace
+    assert f(Q, K, V, MC, DO, DQ, DK, DV, DMC, W, ws - 1, None) == 4    # workspace too small
+    assert f(Q, K, V, MC, DO, DQ, DK, DV, DMC, W + 16, ws, None) == 4   # misaligned workspace
+    assert lib.mhla_backward(None, Q, K, V, MC, DO, DQ, DK, DV, DMC, W, ws, None) == 1
+    p.close()
+
+
 def test_status_strings():
     _lib_or_skip()
     for s in range(7):

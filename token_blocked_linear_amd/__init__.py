@@ -18,7 +18,7 @@ __all__ = [
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
-    "make_desc", "Plan", "EXPORTED_SYMBOLS",
+    "mhla_backward_workspace_size", "mhla_backward", "make_desc", "Plan", "EXPORTED_SYMBOLS",
 ]
 
 MHLA_OK = 0
@@ -36,6 +36,7 @@ _ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MH
 EXPORTED_SYMBOLS = (
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
+    "mhla_backward_workspace_size", "mhla_backward",
 )
 
 
@@ -106,6 +107,8 @@ def load_library() -> ctypes.CDLL:
     lib.mhla_create.argtypes = [ctypes.POINTER(MhlaDesc), ctypes.POINTER(P)]
     lib.mhla_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
+    lib.mhla_backward_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.mhla_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.mhla_destroy.argtypes = [P]
     lib.mhla_status_string.argtypes = [I32]
     lib.mhla_status_string.restype = ctypes.c_char_p
@@ -151,6 +154,19 @@ def mhla_forward(h, q: int, k: int, v: int, mc: int, o: int, workspace: int, wor
     """Pointers are integer device addresses (0 for NULL); ``stream`` a raw hipStream_t."""
     _check(load_library().mhla_forward(h, q, k, v, mc or None, o, workspace or None,
                                        workspace_bytes, stream or None), "mhla_forward")
+
+
+def mhla_backward_workspace_size(h) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mhla_backward_workspace_size(h, ctypes.byref(n)), "mhla_backward_workspace_size")
+    return n.value
+
+
+def mhla_backward(h, q: int, k: int, v: int, mc: int, dout: int, dq: int, dk: int, dv: int, dmc: int,
+                  workspace: int, workspace_bytes: int, stream: int) -> None:
+    """Pointers are integer device addresses (0 for NULL); ``stream`` a raw hipStream_t."""
+    _check(load_library().mhla_backward(h, q, k, v, mc or None, dout, dq, dk, dv, dmc or None,
+                                        workspace or None, workspace_bytes, stream or None), "mhla_backward")
 
 
 def mhla_destroy(h) -> None:
@@ -239,10 +255,11 @@ class Plan:
         mc = (int(kw["heads"]), m, m) if kw.get("mc_per_head") else (m, m)
         return qkv, mc
 
-    def check_args(self, q, k, v, mc, o, workspace):
+    def check_args(self, q, k, v, mc, o, workspace, ws_bytes=None):
         """Host-side checks that every buffer has the shape, dtype and layout the kernels
         index; the C ABI receives bare pointers and cannot see them."""
         import torch
+        ws_bytes = self.workspace_bytes if ws_bytes is None else ws_bytes
         qkv, mc_shape = self.expected_shapes()
         tin = torch.bfloat16 if self.desc_kwargs.get("in_dtype", "bf16") == "bf16" else torch.float32
         tout = torch.bfloat16 if self.desc_kwargs.get("out_dtype", "fp32") == "bf16" else torch.float32
@@ -256,8 +273,34 @@ class Plan:
         elif (tuple(mc.shape) != mc_shape or mc.dtype != torch.float32 or not mc.is_contiguous()
               or not mc.is_cuda):
             raise ValueError(f"mc: expected contiguous float32 cuda tensor {mc_shape}")
-        if workspace.dtype != torch.uint8 or workspace.numel() < self.workspace_bytes or not workspace.is_cuda:
-            raise ValueError(f"workspace: expected >= {self.workspace_bytes} bytes of uint8 on the GPU")
+        if workspace.dtype != torch.uint8 or workspace.numel() < ws_bytes or not workspace.is_cuda:
+            raise ValueError(f"workspace: expected >= {ws_bytes} bytes of uint8 on the GPU")
+
+    def alloc_backward_workspace(self, device="cuda"):
+        import torch
+        n = mhla_backward_workspace_size(self.handle)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def backward(self, q, k, v, mc, dout, dq, dk, dv, dmc, workspace, stream=None):
+        """Gradients into dq, dk, dv (the plan's out_dtype, like dout) and dmc (fp32, M_c's shape,
+        or None to skip)."""
+        import torch
+        self.check_args(q, k, v, mc, dout, workspace, mhla_backward_workspace_size(self.handle))
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            if t.shape != dout.shape or t.dtype != dout.dtype or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name}: expected a contiguous cuda tensor like dout")
+        if dmc is not None:
+            _, mc_shape = self.expected_shapes()
+            if (tuple(dmc.shape) != mc_shape or dmc.dtype != torch.float32 or not dmc.is_contiguous()
+                    or not dmc.is_cuda):
+                raise ValueError(f"dmc: expected contiguous float32 cuda tensor of shape {mc_shape}")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        mhla_backward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                      mc.data_ptr() if mc is not None else 0, dout.data_ptr(), dq.data_ptr(),
+                      dk.data_ptr(), dv.data_ptr(), dmc.data_ptr() if dmc is not None else 0,
+                      workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+        return dq, dk, dv, dmc
 
     def forward(self, q, k, v, mc, o, workspace, stream=None):
         import torch

@@ -1,0 +1,583 @@
+// Backward pass of the MHLA forward: gradients of L = sum(dO * O) with respect to Q, K, V and
+// M_c.  "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head", Method ->
+// Key design 3 trains M_c end to end; the pages give no gradient formulas, so these kernels
+// take the chain rule of the forward steps (Overall framework, Key design 2) in reverse:
+//   g_t = dO_t / den_t, gden_t = -(dO_t . o_t) / den_t   (normalised; else dO_t, 0)
+//   dq~_t = S~_i g_t + z~_i gden_t                         dq_kernel
+//   dz~_i = sum_{t in i} q~_t gden_t                       dq_kernel
+//   dS~_i = sum_{t in i} q~_t g_t^T                        the summary kernel with K := Q, V := g
+//                                                          (g kept in fp32 and split: a bf16 g
+//                                                          costs percents where phi is exp)
+//   dS_b = sum_i m_ib dS~_i, dz_b likewise                 the mixing kernel with M_c^T
+//   dM_c[i, b] = <dS~_i, S_b> + <dz~_i, z_b>                dmc_kernel, dmc_reduce_kernel
+//   dk~_j = dS_b v_j + dz_b, dv_j = dS_b^T k~_j            keyside_kernel
+//   dq = dq~ * phi'(q), dk = dk~ * phi'(k).
+// Every product runs on bf16 MFMA with hi/lo operand splits (about fp32 accuracy).  Head sizes
+// 32, 64 and 128.
+//
+// A summary T staged in fragment layout is the A operand of out[col] = sum_k T[k][col] B[k]
+// (frag_lds.hpp).  dq~ = S~ g and dk~ = dS v need the transposed summaries; each workgroup builds
+// them in LDS from the staged ones.  Both tile kernels take the per-token operands in the
+// readout's layout (lane (t, g) holds features or channels 32c + 8g + 0..7 of token t), and the
+// permuted A rows give every lane 8 consecutive outputs of its token, so phi'(x) of the same
+// features is in the lane and the stores are 16-byte.
+#include <type_traits>
+
+#include "frag_lds.hpp"
+
+namespace mhla {
+
+enum { kBwdNormalized = 0, kBwdUnnormalized = 1 };
+
+template <int PHI>
+__device__ inline float dphi_map(float x) {
+  if constexpr (PHI == kPhiRelu) return x > 0.0f ? 1.0f : 0.0f;
+  else if constexpr (PHI == kPhiExp) return __expf(x);
+  else return x > 0.0f ? 1.0f : __expf(x);
+}
+
+// Unit L -> (head, block, token slice), as the readout numbers them.
+struct BwdUnit {
+  int bh, blk, split;
+  int32_t j_begin, j_end, base_tok;
+  int n_tiles;
+  int64_t head_off, row;
+};
+template <int D>
+__device__ inline BwdUnit bwd_unit(const BwdParams& p, int L) {
+  const Geom& g = p.g;
+  const int per_head = p.splits * g.M;
+  int r;
+  BwdUnit u;
+  if (p.xcd_map) {
+    const int xcd = L & 7, s = L >> 3;
+    u.bh = (s / per_head) * 8 + xcd;
+    r = s % per_head;
+  } else {
+    u.bh = L / per_head;
+    r = L % per_head;
+  }
+  u.blk = r / p.splits;
+  u.split = r % p.splits;
+  u.j_begin = u.split * p.tok_per_split;
+  u.j_end = min(u.j_begin + p.tok_per_split, g.n_b);
+  u.base_tok = block_base_token(g, u.blk);
+  u.n_tiles = (u.j_end - u.j_begin + 15) >> 4;
+  u.head_off = (int64_t)u.bh * g.N * D;
+  u.row = (int64_t)u.bh * g.M + u.blk;
+  return u;
+}
+
+// A fragment-layout summary (hi and lo) from global memory into LDS.
+template <int D>
+__device__ inline void stage_frag(const uint16_t* ghi, const uint16_t* glo, uint16_t* s_hi,
+                                  uint16_t* s_lo, int tid) {
+  constexpr int FRAG = Dims<D>::FRAG, NCT = Dims<D>::NCT;
+  constexpr int PER = (FRAG + kThreads * 8 - 1) / (kThreads * 8);
+  u32x4_t th[PER], tl[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = (tid + j * kThreads) * 8;
+    if (i < FRAG) {
+      th[j] = ld16(ghi + i);
+      tl[j] = ld16(glo + i);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = (tid + j * kThreads) * 8;
+    if (i < FRAG) {
+      st16(s_hi + lds_pos<NCT>(i), th[j]);
+      st16(s_lo + lds_pos<NCT>(i), tl[j]);
+    }
+  }
+}
+
+// F(T^T) from F(T), both in LDS: element (kc, ct, lane, e) of the transposed summary holds
+// T[16ct + lane%16][32kc + 8(lane/16) + e].  D >= 32 (no padding rows).
+template <int D>
+__device__ inline void transpose_frag(const uint16_t* src_hi, const uint16_t* src_lo,
+                                      uint16_t* dst_hi, uint16_t* dst_lo, int tid) {
+  constexpr int NCT = Dims<D>::NCT, FRAG = Dims<D>::FRAG;
+  for (int u = tid; u < FRAG; u += kThreads) {
+    const int e = u & 7, lane = (u >> 3) & 63, fr = u >> 9;
+    const int kc = fr / NCT, ct = fr % NCT;
+    const int r = 16 * ct + (lane & 15);             // row of T
+    const int c = 32 * kc + 8 * (lane >> 4) + e;     // column of T
+    const int us = ((((r >> 5) * NCT + (c >> 4)) * 64 + 16 * ((r & 31) >> 3) + (c & 15)) << 3) + (r & 7);
+    const int di = lds_pos<NCT>(u & ~7) + e;
+    const int si = lds_pos<NCT>(us & ~7) + (us & 7);
+    dst_hi[di] = src_hi[si];
+    dst_lo[di] = src_lo[si];
+  }
+}
+
+// out (NCT accumulator tiles, permuted rows) += T^T B with T = the staged summary (hi, lo) and
+// B the lane's operands for contraction chunk kc (hi, lo; lo may be zero).
+template <int D, bool B_LO>
+__device__ inline void frag_mfma(f32x4_t (&acc)[Dims<D>::NCT], const uint16_t* s_hi,
+                                 const uint16_t* s_lo, AOffsets ao, int kc, u32x4_t bh, u32x4_t bl) {
+  constexpr int NCT = Dims<D>::NCT;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int off = (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? ao.odd : ao.even);
+    const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(s_hi + off);
+    const u32x4_t al = *reinterpret_cast<const u32x4_t*>(s_lo + off);
+    acc[ct] = mfma_bf16(ah, bh, acc[ct]);
+    acc[ct] = mfma_bf16(al, bh, acc[ct]);
+    if (B_LO) acc[ct] = mfma_bf16(ah, bl, acc[ct]);
+  }
+}
+
+// 8 values of a lane as bf16 hi / lo operand words (x[2i] in the low half of word i).
+__device__ inline void split8(const float (&x)[8], u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h, l;
+    split_bf16x2(x[2 * i], x[2 * i + 1], h, l);
+    hi[i] = h;
+    lo[i] = l;
+  }
+}
+
+// Value r (0..7) of the lane's output group cgp from permuted accumulator tiles.
+template <int NCT>
+__device__ inline float acc_out(const f32x4_t (&acc)[NCT], int cgp, int r) {
+  return r < 4 ? acc[2 * cgp][r] : acc[2 * cgp + 1][r - 4];
+}
+
+template <typename T>
+__device__ inline void store8(T* dst, const float (&x)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    st16(dst, u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+    st16(dst + 4, u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+  } else {
+    st16(dst, u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                      pack_bf16x2(x[6], x[7])});
+  }
+}
+
+// ---- query side: dq, g, dz~ ----------------------------------------------------------------
+template <typename TIn, typename TOut, int D, int PHI>
+__global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
+  static_assert(D >= 32, "the backward serves head sizes 32, 64 and 128");
+  using Dm = Dims<D>;
+  constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG, ZF = NKC * 512, NG = NCT / 2;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* sa_hi = smem;                 // F(S~)
+  uint16_t* sa_lo = sa_hi + FRAG;
+  uint16_t* sb_hi = sa_lo + FRAG;         // F(S~^T)
+  uint16_t* sb_lo = sb_hi + FRAG;
+  uint16_t* s_z = sb_lo + FRAG;           // normaliser fragments
+  float* s_zt = reinterpret_cast<float*>(s_z + ZF);   // z~ [D]
+  float* s_dzw = s_zt + D;                            // per-wave dz~ [4][D]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
+  const Geom& geo = p.g;
+  const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
+
+  stage_frag<D>(p.st_hi + U.row * FRAG, p.st_lo + U.row * FRAG, sa_hi, sa_lo, tid);
+  if (tid < D) s_zt[tid] = p.zt[U.row * D + tid];
+  __syncthreads();
+  transpose_frag<D>(sa_hi, sa_lo, sb_hi, sb_lo, tid);
+  build_zfrag<D>(s_zt, s_z, tid);
+  __syncthreads();
+
+  const AOffsets ao = a_offsets(lane);
+  constexpr uint32_t ES = sizeof(TIn), EO = sizeof(TOut);
+  const Rsrc rq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + U.head_off, (uint32_t)geo.N * D * ES);
+  const Rsrc rdo = make_rsrc(reinterpret_cast<const TOut*>(p.dout) + U.head_off, (uint32_t)geo.N * D * EO);
+  float dzacc[NKC][8];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dzacc[kc][e] = 0.f;
+
+  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
+    const int32_t j = U.j_begin + tile * 16 + pr;
+    const bool valid = j < U.j_end;
+    const uint32_t rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
+    In8<TIn> cq[NKC];
+    In8<TOut> cdo[NG];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) cq[kc].template load_buf<0>(rq, valid ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange);
+#pragma unroll
+    for (int c = 0; c < NG; ++c) cdo[c].template load_buf<0>(rdo, valid ? (rel + 32 * c + 8 * lg) * EO : kOutOfRange);
+
+    // phi(q): fp32 values and hi / lo operands
+    float ph[NKC][8];
+    u32x4_t bqh[NKC], bql[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ph[kc][e] = phi_map<PHI>(cq[kc].get(e));
+      split8(ph[kc], bqh[kc], bql[kc]);
+    }
+    // num = S~^T q~, den = q~ . z~
+    f32x4_t acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const u32x4_t az = *reinterpret_cast<const u32x4_t*>(s_z + (kc * 64 + lane) * 8);
+      accz = mfma_bf16(az, bqh[kc], accz);
+      accz = mfma_bf16(az, bql[kc], accz);
+      frag_mfma<D, true>(acc, sa_hi, sa_lo, ao, kc, bqh[kc], bql[kc]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float den = accz[0] + accz[1];
+
+    // g and gden over the lane's channels 32c + 8lg + r; the dot dO . o is completed across the
+    // four lanes of the token
+    float g[NG][8];
+    float gden = 0.f;
+    if (mode == kBwdNormalized) {
+      const float inv = 1.0f / den;
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float d_o = cdo[c].get(r);
+          part = fmaf(d_o, acc_out<NCT>(acc, c, r) * inv, part);
+          g[c][r] = d_o * inv;
+        }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      gden = -part * inv;
+    } else {
+#pragma unroll
+      for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) g[c][r] = cdo[c].get(r);
+    }
+    if (!valid) {                     // tokens past the slice contribute nothing
+      gden = 0.f;
+#pragma unroll
+      for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) g[c][r] = 0.f;
+    }
+
+    // dq~ = S~ g + z~ gden: contraction over channels, chunk c = the lane's channel group c
+    f32x4_t acc2[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc2[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      u32x4_t bgh, bgl;
+      split8(g[c], bgh, bgl);
+      frag_mfma<D, true>(acc2, sb_hi, sb_lo, ao, c, bgh, bgl);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (valid) {
+      const int64_t row = U.head_off + rel;
+#pragma unroll
+      for (int c = 0; c < NG; ++c) {
+        const int f0 = 32 * c + 8 * lg;
+        float out[8], gv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          out[r] = (acc_out<NCT>(acc2, c, r) + s_zt[f0 + r] * gden) * dphi_map<PHI>(cq[c].get(r));
+          gv[r] = g[c][r];
+        }
+        store8(reinterpret_cast<TOut*>(p.dq) + row + f0, out);
+        store8(reinterpret_cast<float*>(p.gbuf) + row + f0, gv);
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dzacc[kc][e] = fmaf(ph[kc][e], gden, dzacc[kc][e]);
+  }
+
+  // dz~ of this unit: sum over the 16 token lanes, then over the four waves (fixed order)
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = dzacc[kc][e];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (pr == 0) s_dzw[wave * D + 32 * kc + 8 * lg + e] = x;
+    }
+  __syncthreads();
+  if (tid < D)
+    p.dpz[((int64_t)U.row * p.splits + U.split) * D + tid] =
+        ((s_dzw[tid] + s_dzw[D + tid]) + s_dzw[2 * D + tid]) + s_dzw[3 * D + tid];
+}
+
+// ---- key side: dk, dv --------------------------------------------------------------------
+template <typename TIn, typename TOut, int D, int PHI>
+__global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
+  static_assert(D >= 32, "the backward serves head sizes 32, 64 and 128");
+  using Dm = Dims<D>;
+  constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG, NG = NCT / 2;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* s1_hi = smem;                 // F(dS_b)
+  uint16_t* s1_lo = s1_hi + FRAG;
+  uint16_t* s2_hi = s1_lo + FRAG;         // F(dS_b^T)
+  uint16_t* s2_lo = s2_hi + FRAG;
+  float* s_dz = reinterpret_cast<float*>(s2_lo + FRAG);   // dz_b [D]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
+  const Geom& geo = p.g;
+  const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
+
+  stage_frag<D>(p.ds_hi + U.row * FRAG, p.ds_lo + U.row * FRAG, s1_hi, s1_lo, tid);
+  if (tid < D) s_dz[tid] = p.dz[U.row * D + tid];
+  __syncthreads();
+  transpose_frag<D>(s1_hi, s1_lo, s2_hi, s2_lo, tid);
+  __syncthreads();
+
+  const AOffsets ao = a_offsets(lane);
+  constexpr uint32_t ES = sizeof(TIn);
+  const Rsrc rk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, (uint32_t)geo.N * D * ES);
+  const Rsrc rv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + U.head_off, (uint32_t)geo.N * D * ES);
+
+  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
+    const int32_t j = U.j_begin + tile * 16 + pr;
+    const bool valid = j < U.j_end;
+    const uint32_t rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
+    In8<TIn> ck[NKC], cv[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const uint32_t off = valid ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange;
+      ck[kc].template load_buf<0>(rk, off);
+      cv[kc].template load_buf<0>(rv, off);
+    }
+    f32x4_t acc1[NCT], acc2[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      acc1[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc2[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      // dv = dS_b^T phi(k): contraction over key features
+      float ph[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ph[e] = phi_map<PHI>(ck[kc].get(e));
+      u32x4_t bh, bl;
+      split8(ph, bh, bl);
+      frag_mfma<D, true>(acc1, s1_hi, s1_lo, ao, kc, bh, bl);
+      // dk~ = dS_b v: contraction over value channels (bf16 V is exact in one operand)
+      if constexpr (sizeof(TIn) == 2) {
+        frag_mfma<D, false>(acc2, s2_hi, s2_lo, ao, kc, cv[kc].w, cv[kc].w);
+      } else {
+        float vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = cv[kc].get(e);
+        u32x4_t vh, vl;
+        split8(vv, vh, vl);
+        frag_mfma<D, true>(acc2, s2_hi, s2_lo, ao, kc, vh, vl);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!valid) continue;
+    const int64_t row = U.head_off + rel;
+#pragma unroll
+    for (int c = 0; c < NG; ++c) {
+      const int f0 = 32 * c + 8 * lg;
+      float dvo[8], dko[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        dvo[r] = acc_out<NCT>(acc1, c, r);
+        dko[r] = (acc_out<NCT>(acc2, c, r) + s_dz[f0 + r]) * dphi_map<PHI>(ck[c].get(r));
+      }
+      store8(reinterpret_cast<TOut*>(p.dv) + row + f0, dvo);
+      store8(reinterpret_cast<TOut*>(p.dk) + row + f0, dko);
+    }
+  }
+}
+
+// ---- dM_c ---------------------------------------------------------------------------------
+// dmc[bh][i][b] = sum over positions of dS~_i and S_b (fragment positions, then the D normaliser
+// entries), both summed over their token slices while loaded.  A 64 x 64 tile per workgroup;
+// 32 positions per step staged through LDS as bf16 hi / lo; each wave owns a 32 x 32 quarter
+// (2 x 2 MFMA tiles): A = dS~ rows, B = S rows, both with 8 consecutive positions per lane.
+constexpr int kDmcTile = 64, kDmcK = 32, kDmcPitch = kDmcK + 8;   // pitch in bf16 elements
+
+__global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
+  __shared__ __align__(16) uint16_t a_hi[kDmcTile * kDmcPitch], a_lo[kDmcTile * kDmcPitch];
+  __shared__ __align__(16) uint16_t b_hi[kDmcTile * kDmcPitch], b_lo[kDmcTile * kDmcPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bh = blockIdx.z, i0 = blockIdx.y * kDmcTile, b0 = blockIdx.x * kDmcTile;
+  const int M = p.M, FRAG = p.frag, D = p.D;
+  const int total = FRAG + D;
+  const int lrow = tid >> 2, lcol = (tid & 3) * 8;   // loader: one row, 8 positions
+  const int wi = (wave >> 1) * 32, wb = (wave & 1) * 32;
+
+  // sum over token slices of 8 consecutive values at position pos of summary row (bh, m)
+  auto load8 = [&](const float* part, const float* zpart, int zsplits, int m, int pos, float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    if (m >= M) return;
+    const int64_t r = (int64_t)bh * M + m;
+    if (pos < FRAG) {
+      for (int s = 0; s < p.ssplits; ++s) {
+        const float* src = part + (r * p.ssplits + s) * FRAG + pos;
+        const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] += __uint_as_float(w0[e]);
+          x[4 + e] += __uint_as_float(w1[e]);
+        }
+      }
+    } else {
+      const int f = pos - FRAG;
+      for (int s = 0; s < zsplits; ++s) {
+        const float* src = zpart + (r * zsplits + s) * D + f;
+        const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] += __uint_as_float(w0[e]);
+          x[4 + e] += __uint_as_float(w1[e]);
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int p0 = 0; p0 < total; p0 += kDmcK) {
+    float xa[8], xb[8];
+    load8(p.dps, p.dpz, p.zsplits_d, i0 + lrow, p0 + lcol, xa);
+    load8(p.ps, p.pz, p.ssplits, b0 + lrow, p0 + lcol, xb);
+    u32x4_t ah, al, bhh, bll;
+    split8(xa, ah, al);
+    split8(xb, bhh, bll);
+    const int o = lrow * kDmcPitch + lcol;
+    st16(a_hi + o, ah);
+    st16(a_lo + o, al);
+    st16(b_hi + o, bhh);
+    st16(b_lo + o, bll);
+    __syncthreads();
+    const int kk = 8 * (lane >> 4);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int ra = (wi + 16 * a + (lane & 15)) * kDmcPitch + kk;
+      const u32x4_t fah = *reinterpret_cast<const u32x4_t*>(a_hi + ra);
+      const u32x4_t fal = *reinterpret_cast<const u32x4_t*>(a_lo + ra);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int rb = (wb + 16 * c + (lane & 15)) * kDmcPitch + kk;
+        const u32x4_t fbh = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
+        const u32x4_t fbl = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
+        acc[a][c] = mfma_bf16(fah, fbh, acc[a][c]);
+        acc[a][c] = mfma_bf16(fal, fbh, acc[a][c]);
+        acc[a][c] = mfma_bf16(fah, fbl, acc[a][c]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + wi + 16 * a + 4 * (lane >> 4) + r;
+        const int b = b0 + wb + 16 * c + (lane & 15);
+        if (i < M && b < M) p.out[((int64_t)bh * M + i) * M + b] = acc[a][c][r];
+      }
+}
+
+// dM_c from the per-(batch, head) partials: a shared M_c gathers every (batch, head), a
+// per-head one every batch item of its head.  Fixed summation order.
+__global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part, float* dmc, int M,
+                                                              int B, int H, int per_head) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t mm = (int64_t)M * M;
+  const int64_t n_out = per_head ? (int64_t)H * mm : mm;
+  if (idx >= n_out) return;
+  float s = 0.f;
+  if (per_head) {
+    const int h = (int)(idx / mm);
+    const int64_t e = idx % mm;
+    for (int b = 0; b < B; ++b) s += part[((int64_t)b * H + h) * mm + e];
+  } else {
+    for (int bh = 0; bh < B * H; ++bh) s += part[(int64_t)bh * mm + idx];
+  }
+  dmc[idx] = s;
+}
+
+// ---- launches -----------------------------------------------------------------------------
+template <int D>
+static size_t dq_lds() {
+  using Dm = Dims<D>;
+  return (size_t)4 * Dm::FRAG * 2 + (size_t)Dm::NKC * 512 * 2 + (size_t)D * 4 + (size_t)4 * D * 4;
+}
+template <int D>
+static size_t keyside_lds() {
+  return (size_t)4 * Dims<D>::FRAG * 2 + (size_t)D * 4;
+}
+
+template <int PHI, typename TIn, typename TOut, int D>
+static hipError_t launch_bwd_t(const BwdParams& p, int mode, int n_units, bool key_side, hipStream_t s) {
+  if (key_side) {
+    auto kern = keyside_kernel<TIn, TOut, D, PHI>;
+    const size_t lds = keyside_lds<D>();
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(n_units), dim3(kThreads), lds, s, p);
+  } else {
+    auto kern = dq_kernel<TIn, TOut, D, PHI>;
+    const size_t lds = dq_lds<D>();
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(n_units), dim3(kThreads), lds, s, p, mode);
+  }
+  return hipGetLastError();
+}
+
+template <int PHI, typename TIn, typename TOut>
+static hipError_t bwd_dispatch_d(const BwdParams& p, int d, int mode, int n, bool ks, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_bwd_t<PHI, TIn, TOut, 32>(p, mode, n, ks, s);
+    case 64: return launch_bwd_t<PHI, TIn, TOut, 64>(p, mode, n, ks, s);
+    case 128: return launch_bwd_t<PHI, TIn, TOut, 128>(p, mode, n, ks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// n_units = splits * M * BH; key_side selects keyside_kernel (dk, dv), else dq_kernel.
+hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
+                            bool key_side, int n_units, hipStream_t stream) {
+  auto go = [&](auto phi_c) {
+    constexpr int PHI = decltype(phi_c)::value;
+    if (in_fp32)
+      return out_fp32 ? bwd_dispatch_d<PHI, float, float>(p, d, mode, n_units, key_side, stream)
+                      : bwd_dispatch_d<PHI, float, uint16_t>(p, d, mode, n_units, key_side, stream);
+    return out_fp32 ? bwd_dispatch_d<PHI, uint16_t, float>(p, d, mode, n_units, key_side, stream)
+                    : bwd_dispatch_d<PHI, uint16_t, uint16_t>(p, d, mode, n_units, key_side, stream);
+  };
+  switch (phi) {
+    case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
+    case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
+    case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dmc(const DmcParams& p, int bh, float* dmc, int B, int H, int per_head,
+                      hipStream_t stream) {
+  const int t = (p.M + kDmcTile - 1) / kDmcTile;
+  hipLaunchKernelGGL(dmc_kernel, dim3(t, t, bh), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_out = (int64_t)(per_head ? H : 1) * p.M * p.M;
+  hipLaunchKernelGGL(dmc_reduce_kernel, dim3((unsigned)((n_out + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, stream, p.out, dmc, p.M, B, H, per_head);
+  return hipGetLastError();
+}
+
+}  // namespace mhla

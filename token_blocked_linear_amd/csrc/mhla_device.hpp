@@ -129,9 +129,46 @@ struct MixParams {
   uint16_t* st_lo;         // low parts (split accuracy) or nullptr
   float* zt;               // mixed normaliser [BH][M][D]
   int32_t M;
-  int32_t splits;
+  int32_t splits;          // token slices per block of ps
   int32_t H;
   int32_t N;
+  int32_t zsplits;         // token slices per block of pz
+  int32_t mc_transposed;   // 1: mix with M_c^T (the backward's dS_b = sum_i m_ib dS~_i)
+};
+
+// Backward pass (chain rule of the forward steps; see csrc/bwd.hip).
+struct BwdParams {
+  const void* q;           // [BH][N][D] input type
+  const void* k;
+  const void* v;
+  const void* dout;        // [BH][N][D] output type
+  void* dq;                // [BH][N][D] output type
+  void* dk;
+  void* dv;
+  const uint16_t* st_hi;   // mixed summaries S~ (fragments, bf16 hi / lo) [BH][M][FRAG]
+  const uint16_t* st_lo;
+  const float* zt;         // z~ [BH][M][D]
+  const uint16_t* ds_hi;   // dS = M_c^T dS~ (fragments, hi / lo) [BH][M][FRAG]
+  const uint16_t* ds_lo;
+  const float* dz;         // dz [BH][M][D]
+  void* gbuf;              // g = dO / den (or dO) [BH][N][D] fp32
+  float* dpz;              // dz~ partials [BH][M][splits][D]
+  Geom g;
+  int32_t splits;          // token slices per block (readout slicing)
+  int32_t tok_per_split;
+  int32_t BH;
+  int32_t xcd_map;
+};
+
+// dM_c partials per (batch, head): dmc[bh][i][b] = <dS~_i, S_b> + <dz~_i, z_b>, summaries summed
+// over their token slices on the fly.
+struct DmcParams {
+  const float* dps;        // dS~ partials [BH][M][ssplits][FRAG]
+  const float* ps;         // S partials   [BH][M][ssplits][FRAG]
+  const float* dpz;        // dz~ partials [BH][M][zsplits_d][D]
+  const float* pz;         // z partials   [BH][M][ssplits][D]
+  float* out;              // [BH][M][M]
+  int32_t M, frag, D, ssplits, zsplits_d;
 };
 
 // MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,

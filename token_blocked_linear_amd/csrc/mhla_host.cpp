@@ -16,10 +16,16 @@
 namespace mhla {
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
                           bool want_u, bool out_bf16, int phi, int n_units, hipStream_t stream);
+hipError_t launch_summary_bf16k_fp32v(const SummaryParams& p, int d, int phi, int n_units,
+                                      hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream);
 hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
                           bool split, int fuse, int phi, int n_wg, hipStream_t stream);
+hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
+                            bool key_side, int n_units, hipStream_t stream);
+hipError_t launch_dmc(const DmcParams& p, int bh, float* dmc, int B, int H, int per_head,
+                      hipStream_t stream);
 }  // namespace mhla
 
 namespace {
@@ -341,6 +347,8 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
         mp.splits = h->sum_splits;
         mp.H = (int32_t)h->H;
         mp.N = (int32_t)h->N;
+        mp.zsplits = h->sum_splits;
+        mp.mc_transposed = 0;
         e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->split, s);
       }
       if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
@@ -368,6 +376,190 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse,
                              (int)h->desc.phi, (int)(h->rd_splits * h->M * h->BH), s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+    return MHLA_OK;
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
+
+namespace {
+
+// Backward workspace: forward summaries recomputed at split precision, the backward's own
+// summaries, g, and the per-(batch, head) dM_c partials.
+struct BwdLayout {
+  size_t ps, pz, st_hi, st_lo, zt, dps, dpzs, dpzq, ds_hi, ds_lo, dz, gbuf, dmcp, total;
+};
+
+BwdLayout bwd_layout(const mhla_plan* h) {
+  BwdLayout L;
+  const size_t f = (size_t)h->frag, dd = (size_t)h->d;
+  const size_t rows = (size_t)h->BH * h->M;
+  const size_t slots = rows * h->sum_splits, rslots = rows * h->rd_splits;
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t bytes) { at = off; off = align256(off + bytes); };
+  take(L.ps, slots * f * 4);
+  take(L.pz, slots * dd * 4);
+  take(L.st_hi, rows * f * 2);
+  take(L.st_lo, rows * f * 2);
+  take(L.zt, rows * dd * 4);
+  take(L.dps, slots * f * 4);
+  take(L.dpzs, slots * dd * 4);
+  take(L.dpzq, rslots * dd * 4);
+  take(L.ds_hi, rows * f * 2);
+  take(L.ds_lo, rows * f * 2);
+  take(L.dz, rows * dd * 4);
+  take(L.gbuf, (size_t)h->BH * h->N * dd * 4);
+  take(L.dmcp, rows * (size_t)h->M * 4);
+  L.total = off;
+  return L;
+}
+
+mhla_status bwd_supported(const mhla_plan* h) {
+  if (h->mala) return MHLA_ERR_UNSUPPORTED;     // the MALA readout has no backward here
+  if (h->d < 32) return MHLA_ERR_UNSUPPORTED;   // head sizes 32, 64, 128
+  return MHLA_OK;
+}
+
+}  // namespace
+
+mhla_status mhla_backward_workspace_size(mhla_handle h, size_t* bytes) {
+  if (!h || !bytes) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = bwd_supported(h);
+  if (st != MHLA_OK) return st;
+  *bytes = bwd_layout(h).total;
+  return MHLA_OK;
+}
+
+mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const void* v, const float* mc,
+                          const void* dout, void* dq, void* dk, void* dv, float* dmc, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!h || !q || !k || !v || !dout || !dq || !dk || !dv) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = bwd_supported(h);
+  if (st != MHLA_OK) return st;
+  if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
+  const void* ins[] = {q, k, v, dout};
+  void* outs[] = {dq, dk, dv};
+  for (const void* a : ins)
+    if (!aligned(a, 16)) return MHLA_ERR_INVALID_ARG;
+  for (void* a : outs) {
+    if (!aligned(a, 16)) return MHLA_ERR_INVALID_ARG;
+    for (const void* b : ins)
+      if (a == b) return MHLA_ERR_INVALID_ARG;
+    if (workspace && a == workspace) return MHLA_ERR_INVALID_ARG;
+  }
+  if (dq == dk || dq == dv || dk == dv) return MHLA_ERR_INVALID_ARG;
+  if (mc && !aligned(mc, 4)) return MHLA_ERR_INVALID_ARG;
+  if (dmc && !aligned(dmc, 4)) return MHLA_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(h);
+  if (!workspace || workspace_bytes < L.total) return MHLA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
+  try {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+    const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+    const int phi = (int)h->desc.phi;
+    const int units_sum = (int)(h->sum_splits * h->M * h->BH);
+    const int units_rd = (int)(h->rd_splits * h->M * h->BH);
+
+    // 1-2. the forward's summaries and mixed summaries at split precision
+    mhla::SummaryParams sp = {};
+    sp.k = k;
+    sp.v = v;
+    sp.ps = F(L.ps);
+    sp.pz = F(L.pz);
+    sp.g = h->geom;
+    sp.splits = h->sum_splits;
+    sp.tok_per_split = h->sum_tok;
+    hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, true, h->in_fp32, false, false, phi,
+                                        units_sum, s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+    mhla::MixParams mp = {};
+    mp.ps = F(L.ps);
+    mp.pz = F(L.pz);
+    mp.mc = mc;
+    mp.mc_head_stride = mc_stride;
+    mp.st_hi = U16(L.st_hi);
+    mp.st_lo = U16(L.st_lo);
+    mp.zt = F(L.zt);
+    mp.M = (int32_t)h->M;
+    mp.splits = h->sum_splits;
+    mp.H = (int32_t)h->H;
+    mp.N = (int32_t)h->N;
+    mp.zsplits = h->sum_splits;
+    mp.mc_transposed = 0;
+    if ((e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, true, s)) != hipSuccess) return MHLA_ERR_HIP;
+
+    // 3. query side: dq, g, dz~ partials
+    mhla::BwdParams bp = {};
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.dout = dout;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.st_hi = U16(L.st_hi);
+    bp.st_lo = U16(L.st_lo);
+    bp.zt = F(L.zt);
+    bp.ds_hi = U16(L.ds_hi);
+    bp.ds_lo = U16(L.ds_lo);
+    bp.dz = F(L.dz);
+    bp.gbuf = ws + L.gbuf;
+    bp.dpz = F(L.dpzq);
+    bp.g = h->geom;
+    bp.splits = h->rd_splits;
+    bp.tok_per_split = h->rd_tok;
+    bp.BH = (int32_t)h->BH;
+    bp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
+    if ((e = mhla::launch_bwd_tiles(bp, h->d, h->in_fp32, h->out_fp32, h->mode, phi, false, units_rd, s)) !=
+        hipSuccess)
+      return MHLA_ERR_HIP;
+
+    // 4. dS~ = sum_t q~_t g_t^T: the summary kernel with K := Q, V := g (g in fp32, split)
+    mhla::SummaryParams sq = sp;
+    sq.k = q;
+    sq.v = ws + L.gbuf;
+    sq.ps = F(L.dps);
+    sq.pz = F(L.dpzs);
+    e = h->in_fp32 ? mhla::launch_summary(sq, h->d, true, true, true, false, false, phi, units_sum, s)
+                   : mhla::launch_summary_bf16k_fp32v(sq, h->d, phi, units_sum, s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+
+    // 5. dS = M_c^T dS~, dz = M_c^T dz~
+    mhla::MixParams mt = mp;
+    mt.ps = F(L.dps);
+    mt.pz = F(L.dpzq);
+    mt.zsplits = h->rd_splits;
+    mt.mc_transposed = 1;
+    mt.st_hi = U16(L.ds_hi);
+    mt.st_lo = U16(L.ds_lo);
+    mt.zt = F(L.dz);
+    if ((e = mhla::launch_mix(mt, h->d, h->frag, (int)h->BH, true, s)) != hipSuccess) return MHLA_ERR_HIP;
+
+    // 6. key side: dk, dv
+    if ((e = mhla::launch_bwd_tiles(bp, h->d, h->in_fp32, h->out_fp32, h->mode, phi, true, units_rd, s)) !=
+        hipSuccess)
+      return MHLA_ERR_HIP;
+
+    // 7. dM_c
+    if (dmc) {
+      mhla::DmcParams dp = {};
+      dp.dps = F(L.dps);
+      dp.ps = F(L.ps);
+      dp.dpz = F(L.dpzq);
+      dp.pz = F(L.pz);
+      dp.out = F(L.dmcp);
+      dp.M = (int32_t)h->M;
+      dp.frag = h->frag;
+      dp.D = h->d;
+      dp.ssplits = h->sum_splits;
+      dp.zsplits_d = h->rd_splits;
+      if ((e = mhla::launch_dmc(dp, (int)h->BH, dmc, (int)h->B, (int)h->H, h->desc.mc_per_head ? 1 : 0, s)) !=
+          hipSuccess)
+        return MHLA_ERR_HIP;
+    }
     return MHLA_OK;
   } catch (...) {
     return MHLA_ERR_INTERNAL;

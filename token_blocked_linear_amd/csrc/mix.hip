@@ -4,7 +4,8 @@
 // Key design 2, multi-head mixing; row i of M_c belongs to query block i).
 //
 // This VALU kernel serves the fp32-partials path (split accuracy, fp32 inputs) when there are
-// too many blocks for the readout to mix in its prologue.
+// too many blocks for the readout to mix in its prologue, and the backward's transposed mixing
+// dS_b = sum_i m_ib dS~_i (chain rule of the same step).
 //
 // Every output element is a fixed-order fp32 sum (deterministic).  The result is written
 // in the fragment layout as bf16 (hi) and, for split accuracy, the bf16 residual (lo).
@@ -44,14 +45,20 @@ __global__ __launch_bounds__(kThreads) void mix_kernel(MixParams p, int frag, in
 #pragma unroll
   for (int r = 0; r < kMixRows; ++r) acc[r] = 0.f;
 
+  // weight of summary b in output row i: M_c[i][b], or M_c[b][i] for the transposed mixing
+  const int64_t si = p.mc_transposed ? 1 : M, sb = p.mc_transposed ? M : 1;
   for (int b = 0; b < M; ++b) {
-    const int64_t slot0 = ((int64_t)bh * M + b) * p.splits;
     float s = 0.f;
-    for (int sp = 0; sp < p.splits; ++sp)
-      s += is_z ? p.pz[(slot0 + sp) * d + zpos] : p.ps[(slot0 + sp) * frag + pos];
+    if (is_z) {
+      const int64_t slot0 = ((int64_t)bh * M + b) * p.zsplits;
+      for (int sp = 0; sp < p.zsplits; ++sp) s += p.pz[(slot0 + sp) * d + zpos];
+    } else {
+      const int64_t slot0 = ((int64_t)bh * M + b) * p.splits;
+      for (int sp = 0; sp < p.splits; ++sp) s += p.ps[(slot0 + sp) * frag + pos];
+    }
 #pragma unroll
     for (int r = 0; r < kMixRows; ++r)
-      if (r < nrows) acc[r] = fmaf(mc ? mc[(int64_t)(i0 + r) * M + b] : 1.0f, s, acc[r]);
+      if (r < nrows) acc[r] = fmaf(mc ? mc[(int64_t)(i0 + r) * si + b * sb] : 1.0f, s, acc[r]);
   }
 #pragma unroll
   for (int r = 0; r < kMixRows; ++r) {

@@ -21,7 +21,9 @@
 
 namespace mhla {
 
-template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16, int PHI>
+// TV, the element type of V, is TIn except in the backward, which feeds bf16 Q as K and the
+// fp32 gradient g as V.
+template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16, int PHI, typename TV>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int n_units) {
   using Dm = Dims<D>;
   constexpr int DK = Dm::DK, NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -119,21 +121,20 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   // they add nothing to S (their V is zero) and z masks them explicitly.
   // Loads go through buffer resources spanning one head; rows past the unit's end get an
   // out-of-range offset and read as zero, with no branch around the loads.
-  constexpr uint32_t ES = sizeof(TIn);
-  const uint32_t head_bytes = (uint32_t)g.N * D * ES;
-  auto issue_loads = [&](In8<TIn> (&rk)[8], In8<TIn> (&rv)[8], const Unit& U, int32_t round_base) {
+  constexpr uint32_t ES = sizeof(TIn), ESV = sizeof(TV);
+  const uint32_t head_bytes = (uint32_t)g.N * D * ES, head_bytes_v = (uint32_t)g.N * D * ESV;
+  auto issue_loads = [&](In8<TIn> (&rk)[8], In8<TV> (&rv)[8], const Unit& U, int32_t round_base) {
     const Rsrc rsk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, head_bytes);
-    const Rsrc rsv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + U.head_off, head_bytes);
+    const Rsrc rsv = make_rsrc(reinterpret_cast<const TV*>(p.v) + U.head_off, head_bytes_v);
     const int32_t j0 = round_base + 8 * tgrp;
     if (contig8) {
       const bool ok = loader && j0 < U.j_end;
       const uint32_t t0 = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j0)) : 0u;
-      const uint32_t off0 = (t0 * D + 8 * fgrp) * ES;
+      const uint32_t e0 = t0 * D + 8 * fgrp;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t off = ok ? off0 + (uint32_t)(i * D * ES) : kOutOfRange;
-        rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, off);
-        rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, off);
+        rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, ok ? (e0 + (uint32_t)(i * D)) * ES : kOutOfRange);
+        rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, ok ? (e0 + (uint32_t)(i * D)) * ESV : kOutOfRange);
       }
     } else {
 #pragma unroll
@@ -141,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         const int32_t j = j0 + i;
         const bool ok = loader && j < U.j_end;
         const uint32_t t = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j)) : 0u;
-        const uint32_t off = ok ? (t * D + 8 * fgrp) * ES : kOutOfRange;
-        rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, off);
-        rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, off);
+        const uint32_t e = t * D + 8 * fgrp;
+        rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, ok ? e * ES : kOutOfRange);
+        rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, ok ? e * ESV : kOutOfRange);
       }
     }
   };
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
 
   // One round: phi / split / transpose into LDS, MFMAs, and the unit's epilogue if it ends.
   // `after_lds` runs once the round's registers are in LDS (single-buffer refill point).
-  auto process = [&](const In8<TIn> (&rk)[8], const In8<TIn> (&rv)[8], const Unit& U, int32_t rb,
+  auto process = [&](const In8<TIn> (&rk)[8], const In8<TV> (&rv)[8], const Unit& U, int32_t rb,
                      auto&& after_lds) {
     if (loader) {
 #pragma unroll
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         if (SPLIT_K) *reinterpret_cast<u32x4_t*>(kt_lo + kofs) = lo;
 
         u32x4_t vh, vl;
-        if constexpr (sizeof(TIn) == 2) {
+        if constexpr (sizeof(TV) == 2) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             vh[i] = rv[2 * i].bits(e) | (rv[2 * i + 1].bits(e) << 16);   // exact: no rounding
@@ -333,10 +334,11 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   int32_t rb = U.j_begin;
 
   auto nothing = [] {};
-  if constexpr (sizeof(TIn) == 2 && D <= 64) {
+  if constexpr (sizeof(TIn) == 2 && sizeof(TV) == 2 && D <= 64) {
     // Two register buffers: the loads of round r+1 are in flight while round r goes through
     // phi, LDS and MFMA.
-    In8<TIn> ka[8], va[8], kb[8], vb[8];
+    In8<TIn> ka[8], kb[8];
+    In8<TV> va[8], vb[8];
     issue_loads(ka, va, U, rb);
     while (true) {
       int nu = unit;
@@ -360,7 +362,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   } else {
     // One buffer (d = 128 would spill two; fp32 inputs are twice as wide): refilled as soon as
     // the round sits in LDS, so the loads overlap the MFMA phase.
-    In8<TIn> ka[8], va[8];
+    In8<TIn> ka[8];
+    In8<TV> va[8];
     issue_loads(ka, va, U, rb);
     while (true) {
       int nu = unit;
@@ -378,13 +381,14 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   }
 }
 
-template <int PHI, typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false>
+template <int PHI, typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false,
+          typename TV = TIn>
 static hipError_t launch_summary_t(const SummaryParams& p, int n_units, hipStream_t stream) {
   using Dm = Dims<D>;
   constexpr int LPR = D / 8, TG_ALL = kThreads / LPR, TG = TG_ALL < 32 ? TG_ALL : 32;
   constexpr int ROUND = TG * 8, PITCH = ROUND;
   const size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2;
-  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16, PHI>;
+  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16, PHI, TV>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -440,6 +444,27 @@ hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool spli
     constexpr int PHI = decltype(phi_c)::value;
     return in_fp32 ? dispatch_d<PHI, float>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream)
                    : dispatch_d<PHI, uint16_t>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream);
+  };
+  switch (phi) {
+    case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
+    case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
+    case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// bf16 K with fp32 V (the backward's dS~ = sum_t phi(q_t) g_t^T): both operands split, fp32
+// partials, no u.  Head sizes 32, 64, 128.
+hipError_t launch_summary_bf16k_fp32v(const SummaryParams& p, int d, int phi, int n_units,
+                                      hipStream_t stream) {
+  auto go = [&](auto phi_c) -> hipError_t {
+    constexpr int PHI = decltype(phi_c)::value;
+    switch (d) {
+      case 32: return launch_summary_t<PHI, uint16_t, 32, true, true, false, false, float>(p, n_units, stream);
+      case 64: return launch_summary_t<PHI, uint16_t, 64, true, true, false, false, float>(p, n_units, stream);
+      case 128: return launch_summary_t<PHI, uint16_t, 128, true, true, false, false, float>(p, n_units, stream);
+      default: return hipErrorInvalidValue;
+    }
   };
   switch (phi) {
     case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
