@@ -17,6 +17,9 @@ WRITE_SIZE hardware counters, each scaled by what the counter reads for a plain 
 size), taken from profiles/traffic.md when that record was made from the current kernel sources
 (same digest of the csrc/ files and the header), else null.
 
+`backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the same
+inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
+
     python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter calibration
     python bench.py --digest             # digest of the kernel sources
 """
@@ -109,7 +112,8 @@ def copy_calibration(n_bytes: int = 1 << 30, reps: int = 10):
 
 def kernel_accounting(w: synth.Workload, out_bytes: int, split: bool = False):
     """Algorithmic bytes and FLOPs per launch of each kernel (summaries are not algorithmic).
-    The mixing kernel contracts a bf16 stack on MFMA, or fp32 partials on the VALU (`split`)."""
+    The mixing kernel contracts on MFMA (a bf16 stack, or fp32 partials as split operands up
+    to 256 blocks); `split` with more blocks runs it on the VALU."""
     BH, N, d, M = w.batch * w.heads, w.n_tokens, w.head_dim, w.n_blocks
     in_b = 2 if w.dtype == "bf16" else 4
     tok = BH * N
@@ -117,7 +121,7 @@ def kernel_accounting(w: synth.Workload, out_bytes: int, split: bool = False):
         "summary": dict(bytes=tok * 2 * d * in_b, flops=tok * (2 * d * d + d), bound="hbm"),
         "readout": dict(bytes=tok * d * (in_b + out_bytes), flops=tok * (2 * d * d + 2 * d), bound="hbm"),
     }
-    mix_bound = "alu" if split else "mfma"
+    mix_bound = "alu" if split and M > 256 else "mfma"
     if w.readout == "mala":
         acc["mix"] = dict(bytes=0, flops=BH * 2 * d * d, bound=mix_bound)
     else:
@@ -192,19 +196,7 @@ def run_workload(name: str, steps: int, warmup: int, out_dtype: str, n_cold: int
         kernels[kname] = ms / max(n, 1) * 1e-3          # mean seconds per launch
     ob = 2 if out_dtype == "bf16" else 4
     acc, total_bytes, total_flops = kernel_accounting(w, ob, bool(plan.info.split_operands))
-    per_kernel = {}
-    for kname, t in kernels.items():
-        a = acc[kname]
-        gbs = a["bytes"] / t / 1e9
-        tfl = a["flops"] / t / 1e12
-        if a["bound"] == "hbm":
-            frac = gbs / HBM_PEAK_GBS
-        elif a["bound"] == "mfma":
-            frac = tfl / BF16_MFMA_PEAK_TFLOPS
-        else:
-            frac = tfl / FP32_VALU_PEAK_TFLOPS
-        per_kernel[kname] = dict(us=round(t * 1e6, 2), alg_GBps=round(gbs, 1), TFLOPs=round(tfl, 2),
-                                 bound=a["bound"], frac=round(frac, 4))
+    per_kernel = {kname: price(acc[kname], t) for kname, t in kernels.items()}
     step_s = elapsed / steps
     res = dict(
         workload=w, plan=plan, elapsed=elapsed, step_s=step_s,
@@ -217,6 +209,97 @@ def run_workload(name: str, steps: int, warmup: int, out_dtype: str, n_cold: int
     del tq, tk, tv, tmc, o, ws
     torch.cuda.empty_cache()
     return res
+
+
+def backward_accounting(w: synth.Workload, grad_bytes: int):
+    """Algorithmic bytes and FLOPs per launch of each backward kernel.  Bytes count the problem's
+    tensors only (Q, K, V, dO read; dQ, dK, dV, M_c, dM_c); the summaries and g = dO / den are
+    intermediates of this decomposition and count as zero, as the forward's summaries do."""
+    BH, N, d, M = w.batch * w.heads, w.n_tokens, w.head_dim, w.n_blocks
+    in_b, ob = (2 if w.dtype == "bf16" else 4), grad_bytes
+    tok = BH * N
+    # split-operand MFMA mixing up to 256 blocks, VALU beyond
+    mix = dict(bytes=M * M * 4, flops=BH * 2 * M * M * (d * d + d), bound="mfma" if M <= 256 else "alu")
+    acc = {
+        "bwd_summary": dict(bytes=tok * 2 * d * in_b, flops=tok * (2 * d * d + d), bound="hbm"),
+        "bwd_mix": dict(mix),
+        "bwd_dq": dict(bytes=tok * d * (in_b + 2 * ob), flops=tok * (4 * d * d + 6 * d), bound="hbm"),
+        "bwd_dsummary": dict(bytes=tok * d * in_b, flops=tok * (2 * d * d + d), bound="hbm"),
+        "bwd_dmix": dict(mix),
+        "bwd_keyside": dict(bytes=tok * d * (2 * in_b + 2 * ob), flops=tok * (4 * d * d + 2 * d), bound="hbm"),
+        "bwd_dmc": dict(bytes=M * M * 4, flops=BH * 2 * M * M * (d * d + d), bound="mfma"),
+    }
+    total_bytes = tok * d * (3 * in_b + 4 * ob) + 2 * M * M * 4
+    total_flops = sum(a["flops"] for a in acc.values())
+    return acc, total_bytes, total_flops
+
+
+def price(a, t):
+    """Achieved rates of one kernel (accounting `a`, mean seconds `t`) against its bound."""
+    gbs = a["bytes"] / t / 1e9
+    tfl = a["flops"] / t / 1e12
+    if a["bound"] == "hbm":
+        frac = gbs / HBM_PEAK_GBS
+    elif a["bound"] == "mfma":
+        frac = tfl / BF16_MFMA_PEAK_TFLOPS
+    else:
+        frac = tfl / FP32_VALU_PEAK_TFLOPS
+    return dict(us=round(t * 1e6, 2), alg_GBps=round(gbs, 1), TFLOPs=round(tfl, 2), bound=a["bound"],
+                frac=round(frac, 4))
+
+
+def run_backward(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
+    """The backward (dQ, dK, dV, dM_c) on the same inputs, dO seeded per workload; per-kernel
+    durations from the library's HIP events on the launch stream."""
+    import torch
+    import token_blocked_linear_amd as T
+
+    w = synth.WORKLOADS[name]
+    q, k, v, mc = inputs
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype=grad_dtype, readout=w.readout)
+    do = synth.make_grad_output(w, np.random.default_rng(w.seed + 1000), grad_dtype)
+    tq, tk, tv, tdo = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), to_dev(do, grad_dtype)
+    tmc = None if mc is None else torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    dq, dk, dv = (torch.empty_like(tdo) for _ in range(3))
+    dmc = None if tmc is None else torch.empty_like(tmc)
+    ws = plan.alloc_backward_workspace()
+    stream = torch.cuda.current_stream()
+    call = (tq, tk, tv, tmc, tdo, dq, dk, dv, dmc, ws, stream)
+    for _ in range(warmup):
+        plan.backward(*call)
+    torch.cuda.synchronize()
+    T.mhla_timing_reset(plan.handle)
+    T.mhla_timing_enable(plan.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.backward(*call)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    T.mhla_timing_enable(plan.handle, False)
+    ob = 2 if grad_dtype == "bf16" else 4
+    acc, total_bytes, total_flops = backward_accounting(w, ob)
+    per_kernel = {}
+    for i in range(7):
+        kname, ms, n = T.mhla_backward_timing_read(plan.handle, i)
+        per_kernel[kname] = price(acc[kname], ms / max(n, 1) * 1e-3)
+    plan.close()
+    step_s = elapsed / steps
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["us"])
+    pk, a = per_kernel[dom], acc[dom]
+    if pk["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": pk["alg_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": pk["frac"], "kernel": dom, "alg_bytes_per_launch": a["bytes"], "mean_launch_us": pk["us"]}
+    else:
+        peak = BF16_MFMA_PEAK_TFLOPS if pk["bound"] == "mfma" else FP32_VALU_PEAK_TFLOPS
+        roof = {"bound": pk["bound"], "achieved": pk["TFLOPs"], "peak": peak, "unit": "TFLOP/s",
+                "frac": pk["frac"], "kernel": dom, "alg_flops_per_launch": a["flops"], "mean_launch_us": pk["us"]}
+    return {"grad_dtype": grad_dtype, "ms_per_step": round(step_s * 1e3, 4),
+            "tokens_per_s": round(w.batch * w.n_tokens / step_s, 1),
+            "e2e_alg_hbm_frac": round(total_bytes / step_s / (HBM_PEAK_GBS * 1e9), 4),
+            "e2e_TFLOPs": round(total_flops / step_s / 1e12, 2),
+            "roofline": roof, "kernels": per_kernel}
 
 
 def cpu_baseline(res, budget_s: float = 12.0):
@@ -251,6 +334,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other N=4096..65536 workloads")
     ap.add_argument("--out-dtype", default="bf16", choices=["fp32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--digest", action="store_true")
     args = ap.parse_args()
@@ -312,6 +396,10 @@ def main():
            "cold_cache_ms": round(r2["cold_step_s"] * 1e3, 4), "kernels": r2["per_kernel"]}
     del r2
 
+    bwd = None
+    if not args.no_backward and w.readout != "mala":
+        bwd = run_backward(args.workload, args.steps, args.warmup, args.out_dtype, res["inputs"])
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(res)
     line = {
         "metric": "MHLA fwd tokens/sec + % of bf16 MFMA/HBM roofline at N=4096..65536",
@@ -340,6 +428,8 @@ def main():
         "cpu_baseline": cpu,
     }
     line[f"{other_out}_output"] = alt
+    if bwd is not None:
+        line["backward"] = bwd
     if others:
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)

@@ -170,6 +170,13 @@ mhla_status mhla_timing_read(mhla_handle h, int index, double* total_ms, int64_t
                              const char** name);
 mhla_status mhla_timing_reset(mhla_handle h);
 
+/* Per-kernel timing of mhla_backward, under the same switch and reset as the forward's: seven
+ * entries in launch order, index 0..6 = "bwd_summary" (S, z recomputed), "bwd_mix" (S~, z~),
+ * "bwd_dq" (dQ, g, dz~), "bwd_dsummary" (dS~), "bwd_dmix" (dS, dz), "bwd_keyside" (dK, dV),
+ * "bwd_dmc" (dM_c: two kernels; empty when dmc is NULL). */
+mhla_status mhla_backward_timing_read(mhla_handle h, int index, double* total_ms, int64_t* launches,
+                                      const char** name);
+
 #ifdef __cplusplus
 }
 #endif

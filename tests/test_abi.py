@@ -204,6 +204,11 @@ def test_timing_api_without_launches():
     with pytest.raises(T.MhlaError):
         T.mhla_timing_read(p.handle, 3)
     T.mhla_timing_reset(p.handle)
+    names = [T.mhla_backward_timing_read(p.handle, i)[0] for i in range(7)]
+    assert names == ["bwd_summary", "bwd_mix", "bwd_dq", "bwd_dsummary", "bwd_dmix", "bwd_keyside", "bwd_dmc"]
+    assert T.mhla_backward_timing_read(p.handle, 2)[1:] == (0.0, 0)
+    with pytest.raises(T.MhlaError):
+        T.mhla_backward_timing_read(p.handle, 7)
     p.close()
     f = T.Plan(grid=(64,), block=(16,), batch=1, heads=1, head_dim=32)       # 4 blocks: fused
     assert [T.mhla_timing_read(f.handle, i)[0] for i in range(2)] == ["summary", "mix+readout"]

@@ -65,6 +65,9 @@ CASES = [
     synth.Workload("bw_m100", "bf16", 1, 2, 64, (1000,), (10,), 110, "softmax_l1"),
     synth.Workload("bw_m200_d128", "bf16", 1, 2, 128, (3200,), (16,), 111, "softmax_gauss"),
     synth.Workload("bw_m144_d32", "bf16", 2, 1, 32, (48, 48), (4, 4), 112, "locality"),
+    synth.Workload("bw_two_slices", "bf16", 1, 1, 64, (16384,), (512,), 116, "softmax_gauss"),
+    synth.Workload("bw_m256_d32", "bf16", 1, 2, 32, (4096,), (16,), 117, "softmax_gauss"),
+    synth.Workload("bw_m300_valu_mix", "bf16", 1, 1, 32, (4800,), (16,), 118, "softmax_gauss"),
     synth.Workload("bw_fp32_2d", "fp32", 2, 2, 64, (24, 24), (8, 12), 113, "softmax_l1"),
     synth.Workload("bw_fp32_d128", "fp32", 1, 2, 128, (900,), (300,), 114, "softmax_gauss"),
     synth.Workload("bw_fp32_unnorm_d32", "fp32", 1, 2, 32, (20, 20), (5, 4), 115, "softmax_l1", "unnormalized"),

@@ -109,6 +109,31 @@ MAP_CASES = [w.with_(name=f"{w.name}_{phi}", phi=phi) for w in SMALL if w.name i
              for phi in ("relu", "exp")]
 
 
+# the mixing kernel on split operands over fp32 partials (more than 16 blocks, up to 256):
+# fp32 inputs, ReLU / exp (split by default), two token slices per block, M = 256
+SPLIT_MIX_CASES = [
+    synth.Workload("fp32_m100", "fp32", 1, 2, 64, (1000,), (10,), 41, "softmax_l1"),
+    synth.Workload("fp32_m144_2d_d32", "fp32", 2, 1, 32, (48, 48), (4, 4), 42, "locality"),
+    synth.Workload("relu_m32_two_slices", "bf16", 1, 1, 64, (16384,), (512,), 43, "softmax_gauss", phi="relu"),
+    synth.Workload("exp_m256_d32", "bf16", 1, 2, 32, (4096,), (16,), 44, "softmax_gauss", phi="exp"),
+    synth.Workload("exp_m200_d128", "bf16", 1, 2, 128, (3200,), (16,), 45, "softmax_gauss", phi="exp"),
+    synth.Workload("relu_m300_valu", "bf16", 1, 1, 32, (4800,), (16,), 46, "softmax_gauss", phi="relu"),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT_MIX_CASES, ids=lambda w: w.name)
+def test_parity_split_mixing(w):
+    announce(f"split mixing {w.name} shape={w.qkv_shape} blocks={w.n_blocks} phi={w.phi}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    if w.phi == "relu":
+        q = np.abs(q)
+    got = run_hip(w, q, k, v, mc)
+    err = rel_err(got, oracle_full(w, q, k, v, mc))
+    print(f"  err={err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= _tol(w), (w.name, err)
+
+
 def _compare_with_nan(w, got, want):
     """NaN (ReLU's 0/0) at exactly the oracle's positions; the bar on every other element."""
     nan_g, nan_w = np.isnan(got), np.isnan(want)

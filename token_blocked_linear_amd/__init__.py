@@ -18,7 +18,7 @@ __all__ = [
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
-    "mhla_backward_workspace_size", "mhla_backward", "make_desc", "Plan", "EXPORTED_SYMBOLS",
+    "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read", "make_desc", "Plan", "EXPORTED_SYMBOLS",
 ]
 
 MHLA_OK = 0
@@ -36,7 +36,7 @@ _ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MH
 EXPORTED_SYMBOLS = (
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
-    "mhla_backward_workspace_size", "mhla_backward",
+    "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
 )
 
 
@@ -117,6 +117,7 @@ def load_library() -> ctypes.CDLL:
     lib.mhla_timing_read.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64),
                                      ctypes.POINTER(ctypes.c_char_p)]
     lib.mhla_timing_reset.argtypes = [P]
+    lib.mhla_backward_timing_read.argtypes = lib.mhla_timing_read.argtypes
     for name in EXPORTED_SYMBOLS:
         if name != "mhla_status_string":
             getattr(lib, name).restype = I32
@@ -188,6 +189,13 @@ def mhla_timing_read(h, index: int):
     ms, n, name = ctypes.c_double(), ctypes.c_int64(), ctypes.c_char_p()
     _check(load_library().mhla_timing_read(h, index, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(name)),
            "mhla_timing_read")
+    return name.value.decode(), ms.value, n.value
+
+
+def mhla_backward_timing_read(h, index: int):
+    ms, n, name = ctypes.c_double(), ctypes.c_int64(), ctypes.c_char_p()
+    _check(load_library().mhla_backward_timing_read(h, index, ctypes.byref(ms), ctypes.byref(n),
+                                                    ctypes.byref(name)), "mhla_backward_timing_read")
     return name.value.decode(), ms.value, n.value
 
 

@@ -396,50 +396,52 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
 }
 
 // ---- dM_c ---------------------------------------------------------------------------------
-// dmc[bh][i][b] = sum over positions of dS~_i and S_b (fragment positions, then the D normaliser
-// entries), both summed over their token slices while loaded.  A 64 x 64 tile per workgroup;
-// 32 positions per step staged through LDS as bf16 hi / lo; each wave owns a 32 x 32 quarter
-// (2 x 2 MFMA tiles): A = dS~ rows, B = S rows, both with 8 consecutive positions per lane.
+// dmc[i][b] = sum over (batch-head, position) of dS~_i and S_b (fragment positions, then the D
+// normaliser entries), both summed over their token slices while loaded.  A 64 x 64 output tile
+// and one chunk of 32-position steps per workgroup; each step is staged through LDS as bf16
+// hi / lo, and each wave owns a 32 x 32 quarter (2 x 2 MFMA tiles): A = dS~ rows, B = S rows,
+// both with 8 consecutive positions per lane.  The next step's loads are in flight during the
+// MFMAs.
 constexpr int kDmcTile = 64, kDmcK = 32, kDmcPitch = kDmcK + 8;   // pitch in bf16 elements
 
 __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
   __shared__ __align__(16) uint16_t a_hi[kDmcTile * kDmcPitch], a_lo[kDmcTile * kDmcPitch];
   __shared__ __align__(16) uint16_t b_hi[kDmcTile * kDmcPitch], b_lo[kDmcTile * kDmcPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bh = blockIdx.z, i0 = blockIdx.y * kDmcTile, b0 = blockIdx.x * kDmcTile;
   const int M = p.M, FRAG = p.frag, D = p.D;
-  const int total = FRAG + D;
+  const int nt = (M + kDmcTile - 1) / kDmcTile;
+  const int i0 = (blockIdx.x / nt) * kDmcTile, b0 = (blockIdx.x % nt) * kDmcTile;
+  const int chunk = blockIdx.y, grp = blockIdx.z;
   const int lrow = tid >> 2, lcol = (tid & 3) * 8;   // loader: one row, 8 positions
   const int wi = (wave >> 1) * 32, wb = (wave & 1) * 32;
+  const int64_t total_steps = (int64_t)p.group_bh * p.steps_per_bh;
+  const int64_t s_begin = (int64_t)chunk * p.steps_per_chunk;
+  const int64_t s_end = min(s_begin + p.steps_per_chunk, total_steps);
 
   // sum over token slices of 8 consecutive values at position pos of summary row (bh, m)
-  auto load8 = [&](const float* part, const float* zpart, int zsplits, int m, int pos, float (&x)[8]) {
+  auto load8 = [&](const float* part, const float* zpart, int zsplits, int bh, int m, int pos, float (&x)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = 0.f;
     if (m >= M) return;
     const int64_t r = (int64_t)bh * M + m;
-    if (pos < FRAG) {
-      for (int s = 0; s < p.ssplits; ++s) {
-        const float* src = part + (r * p.ssplits + s) * FRAG + pos;
-        const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
+    const bool in_s = pos < FRAG;
+    const int ns = in_s ? p.ssplits : zsplits;
+    for (int s = 0; s < ns; ++s) {
+      const float* src = in_s ? part + (r * p.ssplits + s) * FRAG + pos : zpart + (r * zsplits + s) * D + (pos - FRAG);
+      const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] += __uint_as_float(w0[e]);
-          x[4 + e] += __uint_as_float(w1[e]);
-        }
-      }
-    } else {
-      const int f = pos - FRAG;
-      for (int s = 0; s < zsplits; ++s) {
-        const float* src = zpart + (r * zsplits + s) * D + f;
-        const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] += __uint_as_float(w0[e]);
-          x[4 + e] += __uint_as_float(w1[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        x[e] += __uint_as_float(w0[e]);
+        x[4 + e] += __uint_as_float(w1[e]);
       }
     }
+  };
+  auto load_step = [&](int64_t step, float (&xa)[8], float (&xb)[8]) {
+    const int j = (int)(step / p.steps_per_bh);
+    const int pos = (int)(step % p.steps_per_bh) * kDmcK + lcol;
+    const int bh = p.per_head ? j * p.H + grp : j;
+    load8(p.dps, p.dpz, p.zsplits_d, bh, i0 + lrow, pos, xa);
+    load8(p.ps, p.pz, p.ssplits, bh, b0 + lrow, pos, xb);
   };
 
   f32x4_t acc[2][2];
@@ -448,10 +450,9 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int p0 = 0; p0 < total; p0 += kDmcK) {
-    float xa[8], xb[8];
-    load8(p.dps, p.dpz, p.zsplits_d, i0 + lrow, p0 + lcol, xa);
-    load8(p.ps, p.pz, p.ssplits, b0 + lrow, p0 + lcol, xb);
+  float xa[8], xb[8];
+  if (s_begin < s_end) load_step(s_begin, xa, xb);
+  for (int64_t step = s_begin; step < s_end; ++step) {
     u32x4_t ah, al, bhh, bll;
     split8(xa, ah, al);
     split8(xb, bhh, bll);
@@ -461,6 +462,7 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
     st16(b_hi + o, bhh);
     st16(b_lo + o, bll);
     __syncthreads();
+    if (step + 1 < s_end) load_step(step + 1, xa, xb);
     const int kk = 8 * (lane >> 4);
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -479,6 +481,7 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
     }
     __syncthreads();
   }
+  float* out = p.out + ((int64_t)grp * p.nchunks + chunk) * M * M;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -487,27 +490,36 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + wi + 16 * a + 4 * (lane >> 4) + r;
         const int b = b0 + wb + 16 * c + (lane & 15);
-        if (i < M && b < M) p.out[((int64_t)bh * M + i) * M + b] = acc[a][c][r];
+        if (i < M && b < M) out[(int64_t)i * M + b] = acc[a][c][r];
       }
 }
 
-// dM_c from the per-(batch, head) partials: a shared M_c gathers every (batch, head), a
-// per-head one every batch item of its head.  Fixed summation order.
-__global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part, float* dmc, int M,
-                                                              int B, int H, int per_head) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t mm = (int64_t)M * M;
-  const int64_t n_out = per_head ? (int64_t)H * mm : mm;
-  if (idx >= n_out) return;
-  float s = 0.f;
-  if (per_head) {
-    const int h = (int)(idx / mm);
-    const int64_t e = idx % mm;
-    for (int b = 0; b < B; ++b) s += part[((int64_t)b * H + h) * mm + e];
+// dM_c from the chunk partials: out[g][e] = sum over chunks c in order of part[g][c][e].  Many
+// outputs: one thread each (coalesced over e); few: one wave each, lanes striding over the
+// chunks and a fixed shuffle tree.  Both orders are fixed for a given shape.
+__global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part, float* dmc, int64_t mm,
+                                                              int groups, int nchunks, int wave_per_output) {
+  const int64_t n_out = (int64_t)groups * mm;
+  if (!wave_per_output) {
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= n_out) return;
+    const int64_t g = idx / mm, e = idx % mm;
+    const float* src = part + g * nchunks * mm + e;
+    float s = 0.f;
+    for (int c = 0; c < nchunks; ++c) s += src[(int64_t)c * mm];
+    dmc[idx] = s;
   } else {
-    for (int bh = 0; bh < B * H; ++bh) s += part[(int64_t)bh * mm + idx];
+    const int lane = threadIdx.x & 63;
+    const int64_t idx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (idx >= n_out) return;                      // whole waves leave together
+    const int64_t g = idx / mm, e = idx % mm;
+    const float* src = part + g * nchunks * mm + e;
+    float s = 0.f;
+    for (int c = lane; c < nchunks; c += 64) s += src[(int64_t)c * mm];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (lane == 0) dmc[idx] = s;
   }
-  dmc[idx] = s;
 }
 
 // ---- launches -----------------------------------------------------------------------------
@@ -568,15 +580,17 @@ hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp
   }
 }
 
-hipError_t launch_dmc(const DmcParams& p, int bh, float* dmc, int B, int H, int per_head,
-                      hipStream_t stream) {
+hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream) {
   const int t = (p.M + kDmcTile - 1) / kDmcTile;
-  hipLaunchKernelGGL(dmc_kernel, dim3(t, t, bh), dim3(kThreads), 0, stream, p);
+  const int groups = p.per_head ? p.H : 1;
+  hipLaunchKernelGGL(dmc_kernel, dim3(t * t, p.nchunks, groups), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n_out = (int64_t)(per_head ? H : 1) * p.M * p.M;
-  hipLaunchKernelGGL(dmc_reduce_kernel, dim3((unsigned)((n_out + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, stream, p.out, dmc, p.M, B, H, per_head);
+  const int64_t mm = (int64_t)p.M * p.M, n_out = (int64_t)groups * mm;
+  const int wave_per_output = n_out < 16384 ? 1 : 0;
+  const int64_t per_wg = wave_per_output ? kThreads / 64 : kThreads;
+  hipLaunchKernelGGL(dmc_reduce_kernel, dim3((unsigned)((n_out + per_wg - 1) / per_wg)), dim3(kThreads), 0,
+                     stream, p.out, dmc, mm, groups, p.nchunks, wave_per_output);
   return hipGetLastError();
 }
 

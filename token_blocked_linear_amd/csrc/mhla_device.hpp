@@ -95,6 +95,8 @@ struct SummaryParams {
   const float* mc;
   int64_t mc_head_stride;
   uint16_t* mcf;
+  uint16_t* mcf_lo;        // non-null: also the low parts (M_c = hi + lo, for the split mixing)
+  int32_t mcf_transposed;  // 1: fragments of M_c^T (the backward's mixing)
   int32_t mcf_heads, mcf_nitp, mcf_nbc;
 };
 
@@ -104,12 +106,12 @@ struct SummaryParams {
 struct MixShape {
   int nbc, itw, wave_rows, row_groups, nitp;
 };
-inline MixShape mix_shape(int M) {
+inline MixShape mix_shape(int M, bool split) {
   MixShape s;
   const int nbc = (M + 31) / 32;
   s.nbc = nbc <= 1 ? 1 : nbc <= 2 ? 2 : nbc <= 4 ? 4 : 8;
   const int nit = (M + 15) / 16;
-  const int itw = nit <= 4 ? 1 : (nit + 3) / 4;
+  const int itw = nit <= 4 || split ? 1 : (nit + 3) / 4;   // split: one i-tile per wave
   s.itw = itw <= 1 ? 1 : itw <= 2 ? 2 : 4;
   s.wave_rows = 4;
   while (s.wave_rows > 1 && (s.wave_rows / 2) * s.itw >= nit) s.wave_rows /= 2;
@@ -162,24 +164,34 @@ struct BwdParams {
 
 // dM_c partials per (batch, head): dmc[bh][i][b] = <dS~_i, S_b> + <dz~_i, z_b>, summaries summed
 // over their token slices on the fly.
+// The contraction runs over (batch-head, position) pairs of a group: every (batch, head) for a
+// shared M_c, every batch item of head g for a per-head one (bh = j*H + g).  It is cut into
+// `nchunks` chunks of `steps_per_chunk` 32-position steps, each chunk giving one partial.
 struct DmcParams {
   const float* dps;        // dS~ partials [BH][M][ssplits][FRAG]
   const float* ps;         // S partials   [BH][M][ssplits][FRAG]
   const float* dpz;        // dz~ partials [BH][M][zsplits_d][D]
   const float* pz;         // z partials   [BH][M][ssplits][D]
-  float* out;              // [BH][M][M]
+  float* out;              // partials [groups][nchunks][M][M]
   int32_t M, frag, D, ssplits, zsplits_d;
+  int32_t H, per_head, group_bh;           // group_bh: (batch, head) pairs per group
+  int32_t steps_per_bh;                    // (FRAG + D) / 32
+  int32_t nchunks, steps_per_chunk;
 };
 
 // MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,
 // plus the fp32 normaliser mixing z~[i] = sum_b M_c[i][b] z[b].
 struct MixMfmaParams {
-  const uint16_t* x;       // bf16 [BH][M][FRAG]
-  const float* z;          // fp32 [BH][M][D]
-  const uint16_t* mcf;     // bf16 M_c operand fragments (see SummaryParams)
+  const uint16_t* x;       // bf16 [BH][M][FRAG] (bf16 kernel)
+  const float* xf;         // fp32 partials [BH][M][xsplits][FRAG] (split kernel)
+  const float* z;          // fp32 partials [BH][M][zsplits][D]
+  const uint16_t* mcf;     // bf16 W operand fragments (see SummaryParams); hi part if split
+  const uint16_t* mcf_lo;  // low part (split kernel)
   int32_t mcf_per_head;    // 1: fragments per head, 0: shared
-  uint16_t* y;             // bf16 [BH][M][FRAG]
+  uint16_t* y;             // bf16 [BH][M][FRAG]; hi part if split
+  uint16_t* y_lo;          // low part (split kernel)
   float* zt;               // fp32 [BH][M][D]
+  int32_t xsplits, zsplits;
   int32_t M;
   int32_t H;
   int32_t D;

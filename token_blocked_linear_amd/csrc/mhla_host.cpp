@@ -19,13 +19,12 @@ hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool spli
 hipError_t launch_summary_bf16k_fp32v(const SummaryParams& p, int d, int phi, int n_units,
                                       hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream);
-hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream);
+hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
                           bool split, int fuse, int phi, int n_wg, hipStream_t stream);
 hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
                             bool key_side, int n_units, hipStream_t stream);
-hipError_t launch_dmc(const DmcParams& p, int bh, float* dmc, int B, int H, int per_head,
-                      hipStream_t stream);
+hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream);
 }  // namespace mhla
 
 namespace {
@@ -39,9 +38,21 @@ enum { kFuseNone = 0, kFuseBf16 = 1, kFusePartials = 2 };
 #endif
 constexpr int kFuseMaxBlocks = MHLA_FUSE_MAX_BLOCKS;
 
+// Timing: one event before a call's first kernel and one after each of its kernels.
+constexpr int kMaxTimedKernels = 7;
 struct TimedLaunch {
-  hipEvent_t ev[kMaxKernels + 1];
+  hipEvent_t ev[kMaxTimedKernels + 1];
 };
+struct PassTimer {
+  std::vector<TimedLaunch> calls;
+  size_t used = 0;
+};
+
+// The backward's kernels in launch order (the dM_c entry covers its two kernels and is empty
+// when no dM_c is requested).
+constexpr int kBwdKernels = 7;
+const char* const kBwdNames[kBwdKernels] = {"bwd_summary", "bwd_mix",     "bwd_dq", "bwd_dsummary",
+                                            "bwd_dmix",    "bwd_keyside", "bwd_dmc"};
 
 }  // namespace
 
@@ -52,6 +63,7 @@ struct mhla_plan {
   mhla::Geom geom;
   bool in_fp32, out_fp32, mala, split, split_v;
   bool mix_mfma;   // bf16 summary stack (mixed on MFMA or in the readout prologue)
+  bool mix_split;  // mixing kernel on MFMA with split operands over fp32 partials
   int fuse;        // kFuse*: where the mixing step runs
   int n_kernels;
   const char* kernel_names[kMaxKernels];
@@ -60,16 +72,45 @@ struct mhla_plan {
   int32_t sum_splits, sum_tok;
   int32_t rd_splits, rd_tok;
   // workspace layout (byte offsets)
-  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_mcf, ws_bytes;
-  mhla::MixShape mix;   // MFMA mixing launch shape (mix_mfma only)
+  size_t off_sb, off_ps, off_pz, off_pu, off_st_hi, off_st_lo, off_zt, off_mcf, off_mcf_lo, ws_bytes;
+  mhla::MixShape mix;   // MFMA mixing launch shape (mix_mfma or mix_split)
   int mcf_heads;
   // timing
   bool timing;
-  std::vector<TimedLaunch> timed;
-  size_t timed_used;
+  PassTimer fwd_timer, bwd_timer;
 };
 
 namespace {
+
+// Start a timed call on `s`: take the next event set (created on first use) and record the
+// start event.
+bool timer_begin(PassTimer& t, hipStream_t s, TimedLaunch*& tl) {
+  if (t.used == t.calls.size()) {
+    TimedLaunch c;
+    for (int i = 0; i <= kMaxTimedKernels; ++i)
+      if (hipEventCreate(&c.ev[i]) != hipSuccess) return false;
+    t.calls.push_back(c);
+  }
+  tl = &t.calls[t.used++];
+  return hipEventRecord(tl->ev[0], s) == hipSuccess;
+}
+
+// Summed milliseconds of kernel `index` over the timed calls (waits for the last one).
+mhla_status timer_read(const PassTimer& t, int index, int n_kernels, double* total_ms, int64_t* launches) {
+  double sum = 0.0;
+  if (t.used > 0) {
+    if (hipEventSynchronize(t.calls[t.used - 1].ev[n_kernels]) != hipSuccess) return MHLA_ERR_HIP;
+    for (size_t i = 0; i < t.used; ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, t.calls[i].ev[index], t.calls[i].ev[index + 1]) != hipSuccess)
+        return MHLA_ERR_HIP;
+      sum += ms;
+    }
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int64_t)t.used;
+  return MHLA_OK;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -177,11 +218,13 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   // bf16 accuracy level); otherwise fp32 partials per token slice.
   P->mix_mfma = !P->split && !P->mala && !P->in_fp32 && P->sum_splits == 1 && M <= 256;
   // Mixing step: in the readout's prologue for MALA (the centring) and for few blocks; else a
-  // kernel of its own (MFMA for the bf16 stack, VALU for fp32 partials).
+  // kernel of its own: MFMA over the bf16 stack, MFMA with split operands over fp32 partials
+  // (M <= 256), VALU over fp32 partials beyond.
   if (P->mala) P->fuse = kFusePartials;
   else if (M <= kFuseMaxBlocks) P->fuse = P->mix_mfma ? kFuseBf16 : kFusePartials;
   else P->fuse = kFuseNone;
   const bool mix_kernel = P->fuse == kFuseNone;
+  P->mix_split = mix_kernel && !P->mix_mfma && M <= 256;
   P->n_kernels = 0;
   P->kernel_names[P->n_kernels++] = "summary";
   if (mix_kernel) P->kernel_names[P->n_kernels++] = "mix";
@@ -196,19 +239,21 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   P->off_pz = off;   off = align256(off + slots * dd * 4);
   P->off_pu = off;   off = align256(off + (P->mala ? slots * dd * 4 : 0));
   P->off_st_hi = off; off = align256(off + (mix_kernel ? (size_t)BH * M * f * 2 : 0));
-  P->off_st_lo = off; off = align256(off + (mix_kernel && P->split ? (size_t)BH * M * f * 2 : 0));
+  P->off_st_lo = off;
+  off = align256(off + (mix_kernel && (P->split || P->mix_split) ? (size_t)BH * M * f * 2 : 0));
   P->off_zt = off;   off = align256(off + (mix_kernel ? (size_t)BH * M * dd * 4 : 0));
-  // bf16 M_c operand fragments for the MFMA mixing kernel
+  // bf16 M_c operand fragments (and their low parts) for the MFMA mixing kernel
   P->mcf_heads = d->mc_per_head ? (int)d->heads : 1;
-  P->mix = mhla::mix_shape((int)M);
+  P->mix = mhla::mix_shape((int)M, P->mix_split);
+  const size_t mcf_bytes = (size_t)P->mcf_heads * P->mix.nitp * P->mix.nbc * 512 * 2;
   P->off_mcf = off;
-  const bool mcf = mix_kernel && P->mix_mfma;
-  off = align256(off + (mcf ? (size_t)P->mcf_heads * P->mix.nitp * P->mix.nbc * 512 * 2 : 0));
+  off = align256(off + (mix_kernel && (P->mix_mfma || P->mix_split) ? mcf_bytes : 0));
+  P->off_mcf_lo = off;
+  off = align256(off + (P->mix_split ? mcf_bytes : 0));
   P->ws_bytes = off;
   if (BH * M * P->rd_splits >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
 
   P->timing = false;
-  P->timed_used = 0;
   return MHLA_OK;
 }
 
@@ -279,20 +324,10 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     uint16_t* st_hi = reinterpret_cast<uint16_t*>(ws + h->off_st_hi);
     uint16_t* st_lo = h->split ? reinterpret_cast<uint16_t*>(ws + h->off_st_lo) : nullptr;
     float* zt = reinterpret_cast<float*>(ws + h->off_zt);
-    // one event before the first kernel and one after each kernel (timing enabled)
     TimedLaunch* tl = nullptr;
     int ev_i = 0;
-    if (h->timing) {
-      if (h->timed_used == h->timed.size()) {
-        TimedLaunch t;
-        for (int i = 0; i <= kMaxKernels; ++i)
-          if (hipEventCreate(&t.ev[i]) != hipSuccess) return MHLA_ERR_HIP;
-        h->timed.push_back(t);
-      }
-      tl = &h->timed[h->timed_used++];
-      if (hipEventRecord(tl->ev[ev_i++], s) != hipSuccess) return MHLA_ERR_HIP;
-    }
-    auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[ev_i++], s) == hipSuccess; };
+    if (h->timing && !timer_begin(h->fwd_timer, s, tl)) return MHLA_ERR_HIP;
+    auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[++ev_i], s) == hipSuccess; };
 
     const bool mix_kernel = h->fuse == kFuseNone;
     const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
@@ -309,7 +344,9 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.tok_per_split = h->sum_tok;
     sp.mc = mc;
     sp.mc_head_stride = mc_stride;
-    sp.mcf = (mix_kernel && h->mix_mfma) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
+    sp.mcf = (mix_kernel && (h->mix_mfma || h->mix_split)) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
+    sp.mcf_lo = h->mix_split ? reinterpret_cast<uint16_t*>(ws + h->off_mcf_lo) : nullptr;
+    sp.mcf_transposed = 0;
     sp.mcf_heads = h->mcf_heads;
     sp.mcf_nitp = h->mix.nitp;
     sp.mcf_nbc = h->mix.nbc;
@@ -318,21 +355,24 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
     if (mix_kernel) {
-      if (h->mix_mfma) {
-        mhla::MixMfmaParams mm;
+      if (h->mix_mfma || h->mix_split) {
+        mhla::MixMfmaParams mm = {};
         mm.x = sp.sb;
+        mm.xf = ps;
+        mm.xsplits = h->sum_splits;
         mm.z = pz;
+        mm.zsplits = h->mix_split ? h->sum_splits : 1;
         mm.mcf = reinterpret_cast<const uint16_t*>(ws + h->off_mcf);
+        mm.mcf_lo = reinterpret_cast<const uint16_t*>(ws + h->off_mcf_lo);
         mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
         mm.y = st_hi;
+        mm.y_lo = reinterpret_cast<uint16_t*>(ws + h->off_st_lo);
         mm.zt = zt;
         mm.M = (int32_t)h->M;
         mm.H = (int32_t)h->H;
         mm.D = h->d;
         mm.frag = h->frag;
-        mm.n_wg_x = 0;
-        mm.wave_rows = 0;
-        e = mhla::launch_mix_mfma(mm, (int)h->BH, s);
+        e = mhla::launch_mix_mfma(mm, (int)h->BH, h->mix_split, s);
       } else {
         mhla::MixParams mp;
         mp.ps = ps;
@@ -387,7 +427,12 @@ namespace {
 // Backward workspace: forward summaries recomputed at split precision, the backward's own
 // summaries, g, and the per-(batch, head) dM_c partials.
 struct BwdLayout {
-  size_t ps, pz, st_hi, st_lo, zt, dps, dpzs, dpzq, ds_hi, ds_lo, dz, gbuf, dmcp, total;
+  size_t ps, pz, st_hi, st_lo, zt, dps, dpzs, dpzq, ds_hi, ds_lo, dz, gbuf, dmcp;
+  size_t mcf_hi, mcf_lo, mcft_hi, mcft_lo, total;   // M_c and M_c^T operand fragments
+  bool mfma_mix;                                     // M <= 256: mixing on MFMA
+  mhla::MixShape mix;
+  // dM_c: groups (H for a per-head M_c, else 1) x chunks of the (batch-head, position) steps
+  int dmc_groups, dmc_group_bh, dmc_steps_per_bh, dmc_nchunks, dmc_steps_per_chunk;
 };
 
 BwdLayout bwd_layout(const mhla_plan* h) {
@@ -409,7 +454,28 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   take(L.ds_lo, rows * f * 2);
   take(L.dz, rows * dd * 4);
   take(L.gbuf, (size_t)h->BH * h->N * dd * 4);
-  take(L.dmcp, rows * (size_t)h->M * 4);
+  {
+    L.dmc_groups = h->desc.mc_per_head ? (int)h->H : 1;
+    L.dmc_group_bh = h->desc.mc_per_head ? (int)h->B : (int)h->BH;
+    L.dmc_steps_per_bh = (h->frag + h->d) / 32;
+    const int64_t total = (int64_t)L.dmc_group_bh * L.dmc_steps_per_bh;
+    const int64_t t = (h->M + 63) / 64;
+    // about 2048 workgroups (8 per CU)
+    int64_t n = (2048 + t * t * L.dmc_groups - 1) / (t * t * L.dmc_groups);
+    if (n > total) n = total;
+    if (n < 1) n = 1;
+    const int64_t spc = (total + n - 1) / n;
+    L.dmc_steps_per_chunk = (int)spc;
+    L.dmc_nchunks = (int)((total + spc - 1) / spc);
+  }
+  take(L.dmcp, (size_t)L.dmc_groups * L.dmc_nchunks * h->M * h->M * 4);
+  L.mfma_mix = h->M <= 256;
+  L.mix = mhla::mix_shape((int)h->M, true);
+  const size_t fb = L.mfma_mix ? (size_t)h->mcf_heads * L.mix.nitp * L.mix.nbc * 512 * 2 : 0;
+  take(L.mcf_hi, fb);
+  take(L.mcf_lo, fb);
+  take(L.mcft_hi, fb);
+  take(L.mcft_lo, fb);
   L.total = off;
   return L;
 }
@@ -462,6 +528,10 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     const int phi = (int)h->desc.phi;
     const int units_sum = (int)(h->sum_splits * h->M * h->BH);
     const int units_rd = (int)(h->rd_splits * h->M * h->BH);
+    TimedLaunch* tl = nullptr;
+    int ev_i = 0;
+    if (h->timing && !timer_begin(h->bwd_timer, s, tl)) return MHLA_ERR_HIP;
+    auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[++ev_i], s) == hipSuccess; };
 
     // 1-2. the forward's summaries and mixed summaries at split precision
     mhla::SummaryParams sp = {};
@@ -472,24 +542,59 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     sp.g = h->geom;
     sp.splits = h->sum_splits;
     sp.tok_per_split = h->sum_tok;
+    if (L.mfma_mix) {   // side job: M_c operand fragments (hi, lo) for the mixing kernel
+      sp.mc = mc;
+      sp.mc_head_stride = mc_stride;
+      sp.mcf = U16(L.mcf_hi);
+      sp.mcf_lo = U16(L.mcf_lo);
+      sp.mcf_transposed = 0;
+      sp.mcf_heads = h->mcf_heads;
+      sp.mcf_nitp = L.mix.nitp;
+      sp.mcf_nbc = L.mix.nbc;
+    }
     hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, true, h->in_fp32, false, false, phi,
                                         units_sum, s);
-    if (e != hipSuccess) return MHLA_ERR_HIP;
-    mhla::MixParams mp = {};
-    mp.ps = F(L.ps);
-    mp.pz = F(L.pz);
-    mp.mc = mc;
-    mp.mc_head_stride = mc_stride;
-    mp.st_hi = U16(L.st_hi);
-    mp.st_lo = U16(L.st_lo);
-    mp.zt = F(L.zt);
-    mp.M = (int32_t)h->M;
-    mp.splits = h->sum_splits;
-    mp.H = (int32_t)h->H;
-    mp.N = (int32_t)h->N;
-    mp.zsplits = h->sum_splits;
-    mp.mc_transposed = 0;
-    if ((e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, true, s)) != hipSuccess) return MHLA_ERR_HIP;
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+    // mixing with W = M_c (mc_transposed = 0) or M_c^T (1): S~ = M_c S, then dS = M_c^T dS~
+    auto mix = [&](const float* xs, const float* zs, int zsplits, int transposed, uint16_t* y_hi,
+                   uint16_t* y_lo, float* zo) -> hipError_t {
+      if (L.mfma_mix) {
+        mhla::MixMfmaParams mm = {};
+        mm.xf = xs;
+        mm.xsplits = h->sum_splits;
+        mm.z = zs;
+        mm.zsplits = zsplits;
+        mm.mcf = U16(transposed ? L.mcft_hi : L.mcf_hi);
+        mm.mcf_lo = U16(transposed ? L.mcft_lo : L.mcf_lo);
+        mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
+        mm.y = y_hi;
+        mm.y_lo = y_lo;
+        mm.zt = zo;
+        mm.M = (int32_t)h->M;
+        mm.H = (int32_t)h->H;
+        mm.D = h->d;
+        mm.frag = h->frag;
+        return mhla::launch_mix_mfma(mm, (int)h->BH, true, s);
+      }
+      mhla::MixParams mp = {};
+      mp.ps = xs;
+      mp.pz = zs;
+      mp.mc = mc;
+      mp.mc_head_stride = mc_stride;
+      mp.st_hi = y_hi;
+      mp.st_lo = y_lo;
+      mp.zt = zo;
+      mp.M = (int32_t)h->M;
+      mp.splits = h->sum_splits;
+      mp.H = (int32_t)h->H;
+      mp.N = (int32_t)h->N;
+      mp.zsplits = zsplits;
+      mp.mc_transposed = transposed;
+      return mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, true, s);
+    };
+    if ((e = mix(F(L.ps), F(L.pz), h->sum_splits, 0, U16(L.st_hi), U16(L.st_lo), F(L.zt))) != hipSuccess ||
+        !mark())
+      return MHLA_ERR_HIP;
 
     // 3. query side: dq, g, dz~ partials
     mhla::BwdParams bp = {};
@@ -514,7 +619,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     bp.BH = (int32_t)h->BH;
     bp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
     if ((e = mhla::launch_bwd_tiles(bp, h->d, h->in_fp32, h->out_fp32, h->mode, phi, false, units_rd, s)) !=
-        hipSuccess)
+            hipSuccess ||
+        !mark())
       return MHLA_ERR_HIP;
 
     // 4. dS~ = sum_t q~_t g_t^T: the summary kernel with K := Q, V := g (g in fp32, split)
@@ -523,24 +629,24 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     sq.v = ws + L.gbuf;
     sq.ps = F(L.dps);
     sq.pz = F(L.dpzs);
+    if (L.mfma_mix) {   // side job: M_c^T operand fragments for the transposed mixing
+      sq.mcf = U16(L.mcft_hi);
+      sq.mcf_lo = U16(L.mcft_lo);
+      sq.mcf_transposed = 1;
+    }
     e = h->in_fp32 ? mhla::launch_summary(sq, h->d, true, true, true, false, false, phi, units_sum, s)
                    : mhla::launch_summary_bf16k_fp32v(sq, h->d, phi, units_sum, s);
-    if (e != hipSuccess) return MHLA_ERR_HIP;
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
-    // 5. dS = M_c^T dS~, dz = M_c^T dz~
-    mhla::MixParams mt = mp;
-    mt.ps = F(L.dps);
-    mt.pz = F(L.dpzq);
-    mt.zsplits = h->rd_splits;
-    mt.mc_transposed = 1;
-    mt.st_hi = U16(L.ds_hi);
-    mt.st_lo = U16(L.ds_lo);
-    mt.zt = F(L.dz);
-    if ((e = mhla::launch_mix(mt, h->d, h->frag, (int)h->BH, true, s)) != hipSuccess) return MHLA_ERR_HIP;
+    // 5. dS = M_c^T dS~, dz = M_c^T dz~ (dz~ partials per readout token slice)
+    if ((e = mix(F(L.dps), F(L.dpzq), h->rd_splits, 1, U16(L.ds_hi), U16(L.ds_lo), F(L.dz))) != hipSuccess ||
+        !mark())
+      return MHLA_ERR_HIP;
 
     // 6. key side: dk, dv
     if ((e = mhla::launch_bwd_tiles(bp, h->d, h->in_fp32, h->out_fp32, h->mode, phi, true, units_rd, s)) !=
-        hipSuccess)
+            hipSuccess ||
+        !mark())
       return MHLA_ERR_HIP;
 
     // 7. dM_c
@@ -556,10 +662,15 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
       dp.D = h->d;
       dp.ssplits = h->sum_splits;
       dp.zsplits_d = h->rd_splits;
-      if ((e = mhla::launch_dmc(dp, (int)h->BH, dmc, (int)h->B, (int)h->H, h->desc.mc_per_head ? 1 : 0, s)) !=
-          hipSuccess)
-        return MHLA_ERR_HIP;
+      dp.H = (int32_t)h->H;
+      dp.per_head = h->desc.mc_per_head ? 1 : 0;
+      dp.group_bh = L.dmc_group_bh;
+      dp.steps_per_bh = L.dmc_steps_per_bh;
+      dp.nchunks = L.dmc_nchunks;
+      dp.steps_per_chunk = L.dmc_steps_per_chunk;
+      if ((e = mhla::launch_dmc(dp, dmc, s)) != hipSuccess) return MHLA_ERR_HIP;
     }
+    if (!mark()) return MHLA_ERR_HIP;
     return MHLA_OK;
   } catch (...) {
     return MHLA_ERR_INTERNAL;
@@ -568,8 +679,9 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
 
 mhla_status mhla_destroy(mhla_handle h) {
   if (!h) return MHLA_OK;
-  for (auto& t : h->timed)
-    for (int i = 0; i <= kMaxKernels; ++i) (void)hipEventDestroy(t.ev[i]);
+  for (PassTimer* t : {&h->fwd_timer, &h->bwd_timer})
+    for (auto& c : t->calls)
+      for (int i = 0; i <= kMaxTimedKernels; ++i) (void)hipEventDestroy(c.ev[i]);
   delete h;
   return MHLA_OK;
 }
@@ -597,25 +709,20 @@ mhla_status mhla_timing_read(mhla_handle h, int index, double* total_ms, int64_t
                              const char** name) {
   if (!h || index < 0 || index >= h->n_kernels) return MHLA_ERR_INVALID_ARG;
   if (name) *name = h->kernel_names[index];
-  double sum = 0.0;
-  if (h->timed_used > 0) {
-    if (hipEventSynchronize(h->timed[h->timed_used - 1].ev[h->n_kernels]) != hipSuccess)
-      return MHLA_ERR_HIP;
-    for (size_t i = 0; i < h->timed_used; ++i) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, h->timed[i].ev[index], h->timed[i].ev[index + 1]) != hipSuccess)
-        return MHLA_ERR_HIP;
-      sum += ms;
-    }
-  }
-  if (total_ms) *total_ms = sum;
-  if (launches) *launches = (int64_t)h->timed_used;
-  return MHLA_OK;
+  return timer_read(h->fwd_timer, index, h->n_kernels, total_ms, launches);
+}
+
+mhla_status mhla_backward_timing_read(mhla_handle h, int index, double* total_ms, int64_t* launches,
+                                      const char** name) {
+  if (!h || index < 0 || index >= kBwdKernels) return MHLA_ERR_INVALID_ARG;
+  if (name) *name = kBwdNames[index];
+  return timer_read(h->bwd_timer, index, kBwdKernels, total_ms, launches);
 }
 
 mhla_status mhla_timing_reset(mhla_handle h) {
   if (!h) return MHLA_ERR_INVALID_ARG;
-  h->timed_used = 0;
+  h->fwd_timer.used = 0;
+  h->bwd_timer.used = 0;
   return MHLA_OK;
 }
 

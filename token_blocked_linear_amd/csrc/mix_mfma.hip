@@ -1,33 +1,40 @@
-// MFMA mixing kernel: S~_i = sum_b m_ib S_b over a bf16 summary stack, and the fp32
-// normaliser mixing z~_i = sum_b m_ib z_b ("MHLA: Restoring Expressivity of Linear Attention
-// via Token-Level Multi-Head", Method -> Key design 2: the mixing is one product of M_c with the
-// stack of summaries; row i of M_c belongs to query block i).
+// MFMA mixing kernel: S~_i = sum_b m_ib S_b over a stack of summaries, and the fp32 normaliser
+// mixing z~_i = sum_b m_ib z_b ("MHLA: Restoring Expressivity of Linear Attention via Token-Level
+// Multi-Head", Method -> Key design 2: the mixing is one product of M_c with the stack of
+// summaries; row i of M_c belongs to query block i).  The backward runs the same product with
+// M_c^T (dS_b = sum_i m_ib dS~_i, the chain rule of this step).
 //
 // Per (batch, head) the summaries form X[M][P] (P = fragment positions of a d x d summary) and
-// the kernel computes Y = M_c X as Y^T = X^T M_c^T on v_mfma_f32_16x16x32_bf16:
+// the kernel computes Y = W X (W = M_c or M_c^T) as Y^T = X^T W^T on v_mfma_f32_16x16x32_bf16:
 //   A = X^T   16 positions x 32 blocks, read from an LDS tile that holds X transposed
 //             (blocks contiguous; filled with 16-byte global loads and an 8x8 register
 //             transpose, like the summary kernel);
-//   B = M_c^T 32 blocks x 16 query blocks, converted to bf16 once per workgroup and held in
-//             registers for its lifetime;
+//   B = W^T   32 blocks x 16 query blocks, bf16 operand fragments prepared by the summary
+//             kernel, held in registers for the workgroup's lifetime;
 //   D         16 positions x 16 query blocks.
 // The columns are taken 32 at a time as two MFMA tiles pt = 0, 1 whose 16 A rows are the
 // positions 8*(m/4) + 4*pt + m%4, m = 0..15.  Over the two tiles lane (g, l) then holds the 8
 // consecutive positions 8g .. 8g+7 of row i = 16*it + l: one 16-byte store, and the four lane
 // groups of a row write 64 contiguous bytes.
 // The contraction over blocks is padded to a multiple of 32 with zero rows.  The normaliser
-// rides along as one extra column tile: z_b enters as interleaved bf16 (hi, lo) column pairs
-// (z = hi + lo to about 2^-17) and leaves as fp32 z~ = Y[hi col] + Y[lo col], so numerator and
-// denominator are mixed with the same bf16-rounded coefficients and the denominator keeps fp32
-// accuracy in z.
+// rides along as extra column tiles: z_b enters as interleaved bf16 (hi, lo) column pairs
+// (z = hi + lo to about 2^-17) and leaves as fp32 z~ = Y[hi col] + Y[lo col].
+//
+// Two precisions:
+//   SPLIT = false  bf16 stack (one token slice per block) and bf16 W: the bf16 forward;
+//   SPLIT = true   fp32 partial summaries, summed over their token slices as they are loaded,
+//                  and W, both as bf16 hi + lo; three MFMAs per product (hi*hi + lo*hi + hi*lo,
+//                  about 2^-16 relative) and Y leaves as bf16 hi and lo.  One i-tile per wave
+//                  keeps the doubled W fragments in registers.
 #include "mhla_device.hpp"
 
 namespace mhla {
 
 // NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave.
-template <int NBC, int ITW>
+template <int NBC, int ITW, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mix_mfma_kernel(
     MixMfmaParams p) {
+  static_assert(!SPLIT || ITW == 1, "the split kernel holds one i-tile of W per wave");
   constexpr int MPAD = 32 * NBC;
   constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
   constexpr int NCG = PB / 32;            // 32-column groups per staged tile
@@ -42,7 +49,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
   };
 
-  extern __shared__ __align__(16) uint16_t xt[];   // [PB][XP]
+  extern __shared__ __align__(16) uint16_t xt[];   // [PB][XP] (hi), then [PB][XP] (lo) if SPLIT
+  uint16_t* xt_lo = xt + PB * XP;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pr = lane & 15, lg = lane >> 4;
@@ -57,30 +65,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int nit = (M + 15) >> 4;
   const int nitp = gridDim.y * WI * ITW;
 
-  // M_c^T operand fragments (converted to bf16 by the summary kernel): lane holds
-  // M_c[16*it + pr][32*bc + 8*lg + e], e = 0..7, one 16-byte load each.
-  const uint16_t* mcf = p.mcf + (int64_t)(p.mcf_per_head ? bh % p.H : 0) * nitp * NBC * 512;
-  u32x4_t bfrag[ITW][NBC];
+  // W^T operand fragments: lane holds W[16*it + pr][32*bc + 8*lg + e], e = 0..7, one 16-byte
+  // load each.
+  const int64_t fofs = (int64_t)(p.mcf_per_head ? bh % p.H : 0) * nitp * NBC * 512;
+  u32x4_t bfrag[ITW][NBC], bfrag_lo[SPLIT ? NBC : 1];
 #pragma unroll
   for (int a = 0; a < ITW; ++a)
 #pragma unroll
-    for (int bc = 0; bc < NBC; ++bc)
-      bfrag[a][bc] = ld16(mcf + (((int64_t)(it0 + a) * NBC + bc) * 64 + lane) * 8);
+    for (int bc = 0; bc < NBC; ++bc) {
+      const int64_t o = fofs + (((int64_t)(it0 + a) * NBC + bc) * 64 + lane) * 8;
+      bfrag[a][bc] = ld16(p.mcf + o);
+      if constexpr (SPLIT) bfrag_lo[bc] = ld16(p.mcf_lo + o);
+    }
 
   const int P = p.frag;
   const int n_tiles = P / PB;
-  const uint16_t* x = p.x + (int64_t)bh * M * P;
   uint16_t* y = p.y + (int64_t)bh * M * P;
+  uint16_t* y_lo = SPLIT ? p.y_lo + (int64_t)bh * M * P : nullptr;
 
   const int cg = tid % CG, rg = tid / CG;           // loader role: rows 8*rg.., columns 8*cg..
-  u32x4_t raw[8];
+  // raw: bf16 [row][8 columns], or for SPLIT fp32 [row][2][4 columns] summed over token slices
+  u32x4_t raw[SPLIT ? 16 : 8];
   // the stack of this head through a buffer resource: rows b >= M read as zero, no branch
-  const Rsrc rsx = make_rsrc(x, (uint32_t)M * P * 2u);
+  const Rsrc rsx = SPLIT ? make_rsrc(p.xf + (int64_t)bh * M * p.xsplits * P, (uint32_t)M * p.xsplits * P * 4u)
+                         : make_rsrc(p.x + (int64_t)bh * M * P, (uint32_t)M * P * 2u);
   auto issue = [&](int tile) {
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int b = 8 * rg + r;
-      raw[r] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? (uint32_t)(b * P + tile * PB + 8 * cg) * 2u : kOutOfRange);
+      for (int r = 0; r < 8; ++r) {
+        const int b = 8 * rg + r;
+        const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits) * P + tile * PB + 8 * cg) * 4u : kOutOfRange;
+        raw[2 * r] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, o0);
+        raw[2 * r + 1] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? o0 + 16u : kOutOfRange);
+      }
+      for (int s = 1; s < p.xsplits; ++s) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int b = 8 * rg + r;
+          const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits + s) * P + tile * PB + 8 * cg) * 4u : kOutOfRange;
+          const u32x4_t w0 = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, o0);
+          const u32x4_t w1 = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? o0 + 16u : kOutOfRange);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            raw[2 * r][j] = __float_as_uint(__uint_as_float(raw[2 * r][j]) + __uint_as_float(w0[j]));
+            raw[2 * r + 1][j] = __float_as_uint(__uint_as_float(raw[2 * r + 1][j]) + __uint_as_float(w1[j]));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int b = 8 * rg + r;
+        raw[r] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? (uint32_t)(b * P + tile * PB + 8 * cg) * 2u : kOutOfRange);
+      }
     }
   };
 
@@ -89,25 +126,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int D = p.D;
   const int n_ztiles = (2 * D + PB - 1) / PB;
   const int last = n_tiles + n_ztiles;            // one past the last tile
-  // z of this head through a buffer resource (32-bit offsets; rows b >= M read as zero)
-  const Rsrc rsz = make_rsrc(p.z + (int64_t)bh * M * D, (uint32_t)M * D * 4u);
+  // z partials of this head through a buffer resource (rows b >= M read as zero)
+  const int zsp = SPLIT ? p.zsplits : 1;
+  const Rsrc rsz = make_rsrc(p.z + (int64_t)bh * M * zsp * D, (uint32_t)M * zsp * D * 4u);
   auto issue_z = [&](int zj) {
     const int c0 = zj * (PB / 2) + 4 * cg;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int b = 8 * rg + r;
+      u32x4_t w = {0u, 0u, 0u, 0u};
       if (c0 < D) {
-        const u32x4_t zz = buf_ld16(rsz, b < M ? (uint32_t)(b * D + c0) * 4u : kOutOfRange);
-        uint32_t w[4];
+        float zs[4] = {0.f, 0.f, 0.f, 0.f};
+        const int nzs = SPLIT ? p.zsplits : 1;   // the bf16 kernel's z has one token slice
+        for (int s = 0; s < nzs; ++s) {
+          const u32x4_t zz = buf_ld16(rsz, b < M ? (uint32_t)((b * nzs + s) * D + c0) * 4u : kOutOfRange);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) zs[j] += __uint_as_float(zz[j]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint32_t h, l;
-          split_bf16(__uint_as_float(zz[j]), h, l);
+          split_bf16(zs[j], h, l);
           w[j] = h | (l << 16);
         }
-        raw[r] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
+      if constexpr (SPLIT) {
+        raw[2 * r] = w;                        // bf16 (hi, lo) pairs: no further split
       } else {
-        raw[r] = u32x4_t{0u, 0u, 0u, 0u};
+        raw[r] = w;
       }
     }
   };
@@ -119,21 +165,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   int tile = blockIdx.x;
   if (tile < last) issue_any(tile);
   for (; tile < last; tile += p.n_wg_x) {
+    const bool ztile = tile >= n_tiles;
     // transpose 8 rows x 8 columns into LDS: column-major with blocks contiguous
+    if (SPLIT && !ztile) {
+      // fp32 rows: row rr holds columns 0..3 in raw[2rr] and 4..7 in raw[2rr + 1]
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x4_t col;
+      for (int e = 0; e < 8; ++e) {
+        u32x4_t col, col_lo;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t w0 = raw[2 * r][e >> 1], w1 = raw[2 * r + 1][e >> 1];
-        col[r] = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+        for (int r = 0; r < 4; ++r) {
+          uint32_t h, l;
+          split_bf16x2(__uint_as_float(raw[4 * r + (e >> 2)][e & 3]),
+                       __uint_as_float(raw[4 * r + 2 + (e >> 2)][e & 3]), h, l);
+          col[r] = h;
+          col_lo[r] = l;
+        }
+        const int rr = 8 * cg + e;
+        *reinterpret_cast<u32x4_t*>(xt + rr * XP + 8 * swz(rr, rg)) = col;
+        *reinterpret_cast<u32x4_t*>(xt_lo + rr * XP + 8 * swz(rr, rg)) = col_lo;
       }
-      const int r = 8 * cg + e;
-      *reinterpret_cast<u32x4_t*>(xt + r * XP + 8 * swz(r, rg)) = col;
+    } else {
+      // bf16 rows: word e/2 of a row holds columns e & ~1 (low half) and e | 1.  The split
+      // kernel keeps its bf16 (normaliser) rows in raw[2rr] and an all-zero low part.
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u32x4_t col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t w0 = raw[SPLIT ? 4 * r : 2 * r][e >> 1], w1 = raw[SPLIT ? 4 * r + 2 : 2 * r + 1][e >> 1];
+          col[r] = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+        }
+        const int rr = 8 * cg + e;
+        *reinterpret_cast<u32x4_t*>(xt + rr * XP + 8 * swz(rr, rg)) = col;
+        if constexpr (SPLIT) *reinterpret_cast<u32x4_t*>(xt_lo + rr * XP + 8 * swz(rr, rg)) = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
     __syncthreads();
     if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);   // in flight during the MFMAs
-    const bool ztile = tile >= n_tiles;
     const int zbase = (tile - n_tiles) * (PB / 2);
 
 #pragma unroll 1
@@ -148,9 +216,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
           const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
-          const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + r * XP + 8 * swz(r, 4 * bc + lg));
+          const int ofs = r * XP + 8 * swz(r, 4 * bc + lg);
+          const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + ofs);
 #pragma unroll
           for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag[a][bc], accs[pt][a]);
+          if constexpr (SPLIT) {
+            const u32x4_t afrag_lo = *reinterpret_cast<const u32x4_t*>(xt_lo + ofs);
+            accs[pt][0] = mfma_bf16(afrag_lo, bfrag[0][bc], accs[pt][0]);
+            accs[pt][0] = mfma_bf16(afrag, bfrag_lo[bc], accs[pt][0]);
+          }
           // with 128 registers of M_c fragments, keep each operand read next to its MFMAs
           if constexpr (NBC * ITW >= 32) __builtin_amdgcn_sched_barrier(0);
         }
@@ -162,9 +236,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if (i >= M) continue;
         const f32x4_t c0 = accs[0][a], c1 = accs[1][a];
         if (!ztile) {
-          st16(y + (int64_t)i * P + (int64_t)tile * PB + q,
-               u32x4_t{pack_bf16x2(c0[0], c0[1]), pack_bf16x2(c0[2], c0[3]),
-                       pack_bf16x2(c1[0], c1[1]), pack_bf16x2(c1[2], c1[3])});
+          const int64_t o = (int64_t)i * P + (int64_t)tile * PB + q;
+          if constexpr (SPLIT) {
+            const float v[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split_bf16x2(v[2 * j], v[2 * j + 1], h[j], l[j]);
+            st16(y + o, u32x4_t{h[0], h[1], h[2], h[3]});
+            st16(y_lo + o, u32x4_t{l[0], l[1], l[2], l[3]});
+          } else {
+            st16(y + o, u32x4_t{pack_bf16x2(c0[0], c0[1]), pack_bf16x2(c0[2], c0[3]),
+                                pack_bf16x2(c1[0], c1[1]), pack_bf16x2(c1[2], c1[3])});
+          }
         } else if (zbase + q / 2 < D) {
           // columns 2c, 2c+1 are hi, lo of z index zbase + c: four consecutive z~ values
           st16(p.zt + ((int64_t)bh * M + i) * D + zbase + q / 2,
@@ -177,22 +260,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <int NBC, int ITW>
+template <int NBC, int ITW, bool SPLIT>
 static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipStream_t s) {
   constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD;
-  const size_t lds = (size_t)PB * XP * 2;
-  auto kern = mix_mfma_kernel<NBC, ITW>;
+  const size_t lds = (size_t)PB * XP * 2 * (SPLIT ? 2 : 1);
+  auto kern = mix_mfma_kernel<NBC, ITW, SPLIT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.n_wg_x, row_groups, bh), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
-// Launch with the shape mix_shape(M) (the host sized the M_c fragments with the same shape).
-hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream) {
+// Launch with the shape mix_shape(M, split) (the host sized the W fragments with the same shape).
+hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stream) {
   const int M = p.M;
   if (M < 1 || M > 256) return hipErrorInvalidValue;
-  const MixShape sh = mix_shape(M);
+  if (split ? (!p.xf || !p.mcf_lo || !p.y_lo || p.xsplits < 1) : (!p.x || p.zsplits != 1))
+    return hipErrorInvalidValue;
+  const MixShape sh = mix_shape(M, split);
   const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups;
   p.wave_rows = sh.wave_rows;
   const int pb = 16384 / (32 * NBC);
@@ -203,10 +288,15 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, hipStream_t stream) {
   int want = (512 + bh * row_groups - 1) / (bh * row_groups);
   if (want > n_all) want = n_all;
   if (want < 1) want = 1;
+  // several row groups: a multiple of 8 workgroups per row group puts the row groups of one
+  // column tile on the same XCD (workgroups are dealt to the 8 XCDs round robin), so the
+  // tile they all load is fetched from HBM once into that XCD's L2
+  if (row_groups > 1 && want > 8) want &= ~7;
   p.n_wg_x = want;
-#define MHLA_MIX_CASE(N, I) \
-  if (NBC == N && ITW == I) return launch_t<N, I>(p, row_groups, bh, stream);
-  MHLA_MIX_CASE(1, 1) MHLA_MIX_CASE(2, 1) MHLA_MIX_CASE(4, 2) MHLA_MIX_CASE(8, 4)
+#define MHLA_MIX_CASE(N, I, S) \
+  if (NBC == N && ITW == I && split == S) return launch_t<N, I, S>(p, row_groups, bh, stream);
+  MHLA_MIX_CASE(1, 1, false) MHLA_MIX_CASE(2, 1, false) MHLA_MIX_CASE(4, 2, false) MHLA_MIX_CASE(8, 4, false)
+  MHLA_MIX_CASE(1, 1, true) MHLA_MIX_CASE(2, 1, true) MHLA_MIX_CASE(4, 1, true) MHLA_MIX_CASE(8, 1, true)
 #undef MHLA_MIX_CASE
   return hipErrorInvalidValue;
 }

@@ -81,15 +81,25 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
       t /= nbc;
       const int it = t % nitp, hh = t / nitp;
       const int i = 16 * it + (l & 15);
-      const float* row = p.mc ? p.mc + (int64_t)hh * p.mc_head_stride + (int64_t)i * M : nullptr;
+      // W[i][b] = M_c[i][b], or M_c[b][i] for the transposed mixing
+      const float* mch = p.mc ? p.mc + (int64_t)hh * p.mc_head_stride : nullptr;
+      const int64_t si = p.mcf_transposed ? 1 : M, sb = p.mcf_transposed ? M : 1;
       float m[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int b = 32 * bc + 8 * (l >> 4) + e;
-        m[e] = (i < M && b < M) ? (row ? row[b] : 1.0f) : 0.f;   // NULL M_c (M == 1): [1]
+        m[e] = (i < M && b < M) ? (mch ? mch[i * si + b * sb] : 1.0f) : 0.f;   // NULL M_c (M == 1): [1]
       }
-      st16(p.mcf + (int64_t)idx * 8, u32x4_t{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]),
-                                             pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7])});
+      u32x4_t hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h, l;
+        split_bf16x2(m[2 * j], m[2 * j + 1], h, l);
+        hi[j] = h;
+        lo[j] = l;
+      }
+      st16(p.mcf + (int64_t)idx * 8, hi);
+      if (p.mcf_lo) st16(p.mcf_lo + (int64_t)idx * 8, lo);
     }
   }
 
