@@ -121,7 +121,7 @@ def kernel_accounting(w: synth.Workload, out_bytes: int, split: bool = False):
         "summary": dict(bytes=tok * 2 * d * in_b, flops=tok * (2 * d * d + d), bound="hbm"),
         "readout": dict(bytes=tok * d * (in_b + out_bytes), flops=tok * (2 * d * d + 2 * d), bound="hbm"),
     }
-    mix_bound = "alu" if split and M > 256 else "mfma"
+    mix_bound = "alu" if split and (M > 256 or w.readout == "mala") else "mfma"
     if w.readout == "mala":
         acc["mix"] = dict(bytes=0, flops=BH * 2 * d * d, bound=mix_bound)
     else:
