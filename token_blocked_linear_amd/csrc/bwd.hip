@@ -3,8 +3,8 @@
 // Key design 3 trains M_c end to end; the pages give no gradient formulas, so these kernels
 // take the chain rule of the forward steps (Overall framework, Key design 2) in reverse:
 //   g_t = dO_t / den_t, gden_t = -(dO_t . o_t) / den_t   (normalised; else dO_t, 0)
-//   dq~_t = S~_i g_t + z~_i gden_t                         dq_kernel
-//   dz~_i = sum_{t in i} q~_t gden_t                       dq_kernel
+//   dq~_t = S~_i g_t + z~_i gden_t                         dq_kernel (also 1/den_t, -(dO_t . o_t))
+//   dz~_i = sum_{t in i} q~_t gden_t                       the summary kernel (below)
 //   dS~_i = sum_{t in i} q~_t g_t^T                        the summary kernel with K := Q, V := g
 //                                                          (g kept in fp32 and split: a bf16 g
 //                                                          costs percents where phi is exp)
@@ -93,39 +93,68 @@ __device__ inline void stage_frag(const uint16_t* ghi, const uint16_t* glo, uint
   }
 }
 
-// F(T^T) from F(T), both in LDS: element (kc, ct, lane, e) of the transposed summary holds
+// F(T^T) from F(T), both in LDS.  Element (kc, ct, lane, e) of the transposed summary holds
 // T[16ct + lane%16][32kc + 8(lane/16) + e].  D >= 32 (no padding rows).
+// Work in 8 x 8 blocks: the 8 source chunks of lanes 16g + 8h + j (j = 0..7) of fragment
+// (kc, ct) hold T[r0 + e][c0 + j] (r0 = 32kc + 8g, c0 = 16ct + 8h); row r0 + e of the block is
+// one destination chunk, so a thread does 8 16-byte reads, an 8 x 8 transpose of 16-bit
+// elements in registers and 8 16-byte writes.
 template <int D>
 __device__ inline void transpose_frag(const uint16_t* src_hi, const uint16_t* src_lo,
                                       uint16_t* dst_hi, uint16_t* dst_lo, int tid) {
-  constexpr int NCT = Dims<D>::NCT, FRAG = Dims<D>::FRAG;
-  for (int u = tid; u < FRAG; u += kThreads) {
-    const int e = u & 7, lane = (u >> 3) & 63, fr = u >> 9;
-    const int kc = fr / NCT, ct = fr % NCT;
-    const int r = 16 * ct + (lane & 15);             // row of T
-    const int c = 32 * kc + 8 * (lane >> 4) + e;     // column of T
-    const int us = ((((r >> 5) * NCT + (c >> 4)) * 64 + 16 * ((r & 31) >> 3) + (c & 15)) << 3) + (r & 7);
-    const int di = lds_pos<NCT>(u & ~7) + e;
-    const int si = lds_pos<NCT>(us & ~7) + (us & 7);
-    dst_hi[di] = src_hi[si];
-    dst_lo[di] = src_lo[si];
+  constexpr int NCT = Dims<D>::NCT, NBLK = Dims<D>::FRAG / 64;
+  for (int blk = tid; blk < 2 * NBLK; blk += kThreads) {   // the hi blocks, then the lo blocks
+    const bool lo = blk >= NBLK;
+    const int bb = lo ? blk - NBLK : blk;
+    const uint16_t* src = lo ? src_lo : src_hi;
+    uint16_t* dst = lo ? dst_lo : dst_hi;
+    const int h = bb & 1, g = (bb >> 1) & 3, fr = bb >> 3;   // fr = kc * NCT + ct
+    const int r0 = 32 * (fr / NCT) + 8 * g, c0 = 16 * (fr % NCT) + 8 * h;
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const u32x4_t*>(src + lds_pos<NCT>((fr * 64 + 16 * g + 8 * h + j) * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x4_t w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a = v[2 * k][e >> 1], b = v[2 * k + 1][e >> 1];
+        w[k] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      const int r = r0 + e;
+      const int dchunk = ((c0 >> 5) * NCT + (r >> 4)) * 64 + 16 * ((c0 & 31) >> 3) + (r & 15);
+      *reinterpret_cast<u32x4_t*>(dst + lds_pos<NCT>(dchunk * 8)) = w;
+    }
   }
 }
 
 // out (NCT accumulator tiles, permuted rows) += T^T B with T = the staged summary (hi, lo) and
-// B the lane's operands for contraction chunk kc (hi, lo; lo may be zero).
+// B the lane's operands for contraction chunk kc (hi, lo; lo may be zero).  Tiles go in groups
+// of four: the group's operand reads are issued together and its MFMAs run in three rounds of
+// independent accumulators (hi*hi, lo*hi, hi*lo), so no MFMA waits on the one before it.
 template <int D, bool B_LO>
 __device__ inline void frag_mfma(f32x4_t (&acc)[Dims<D>::NCT], const uint16_t* s_hi,
                                  const uint16_t* s_lo, AOffsets ao, int kc, u32x4_t bh, u32x4_t bl) {
-  constexpr int NCT = Dims<D>::NCT;
+  constexpr int NCT = Dims<D>::NCT, G = NCT < 4 ? NCT : 4;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int off = (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? ao.odd : ao.even);
-    const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(s_hi + off);
-    const u32x4_t al = *reinterpret_cast<const u32x4_t*>(s_lo + off);
-    acc[ct] = mfma_bf16(ah, bh, acc[ct]);
-    acc[ct] = mfma_bf16(al, bh, acc[ct]);
-    if (B_LO) acc[ct] = mfma_bf16(ah, bl, acc[ct]);
+  for (int c0 = 0; c0 < NCT; c0 += G) {
+    u32x4_t ah[G], al[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int ct = c0 + g;
+      const int off = (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? ao.odd : ao.even);
+      ah[g] = *reinterpret_cast<const u32x4_t*>(s_hi + off);
+      al[g] = *reinterpret_cast<const u32x4_t*>(s_lo + off);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[c0 + g] = mfma_bf16(ah[g], bh, acc[c0 + g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[c0 + g] = mfma_bf16(al[g], bh, acc[c0 + g]);
+    if (B_LO) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[c0 + g] = mfma_bf16(ah[g], bl, acc[c0 + g]);
+    }
   }
 }
 
@@ -170,7 +199,6 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
   uint16_t* sb_lo = sb_hi + FRAG;
   uint16_t* s_z = sb_lo + FRAG;           // normaliser fragments
   float* s_zt = reinterpret_cast<float*>(s_z + ZF);   // z~ [D]
-  float* s_dzw = s_zt + D;                            // per-wave dz~ [4][D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
   const Geom& geo = p.g;
@@ -187,22 +215,28 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
   constexpr uint32_t ES = sizeof(TIn), EO = sizeof(TOut);
   const Rsrc rq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + U.head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rdo = make_rsrc(reinterpret_cast<const TOut*>(p.dout) + U.head_off, (uint32_t)geo.N * D * EO);
-  float dzacc[NKC][8];
-#pragma unroll
-  for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dzacc[kc][e] = 0.f;
 
-  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
+  // Per tile: this lane's token (validity, element offset) and its Q, dO loads.  The next tile's
+  // loads are issued before the current tile's stores: the memory counter is in order and
+  // counts stores too, so loads issued after the stores would wait for them.
+  auto token_of = [&](int tile, bool& valid, uint32_t& rel) {
     const int32_t j = U.j_begin + tile * 16 + pr;
-    const bool valid = j < U.j_end;
-    const uint32_t rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
-    In8<TIn> cq[NKC];
-    In8<TOut> cdo[NG];
+    valid = tile < U.n_tiles && j < U.j_end;
+    rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
+  };
+  auto issue = [&](In8<TIn> (&cq)[NKC], In8<TOut> (&cdo)[NG], bool valid, uint32_t rel) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) cq[kc].template load_buf<0>(rq, valid ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange);
 #pragma unroll
     for (int c = 0; c < NG; ++c) cdo[c].template load_buf<0>(rdo, valid ? (rel + 32 * c + 8 * lg) * EO : kOutOfRange);
+  };
+  In8<TIn> cq[NKC];
+  In8<TOut> cdo[NG];
+  bool valid;
+  uint32_t rel;
+  token_of(wave, valid, rel);
+  issue(cq, cdo, valid, rel);
+  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
 
     // phi(q): fp32 values and hi / lo operands
     float ph[NKC][8];
@@ -231,10 +265,9 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
     // g and gden over the lane's channels 32c + 8lg + r; the dot dO . o is completed across the
     // four lanes of the token
     float g[NG][8];
-    float gden = 0.f;
+    float gden = 0.f, inv = 1.0f, part = 0.f;
     if (mode == kBwdNormalized) {
-      const float inv = 1.0f / den;
-      float part = 0.f;
+      inv = 1.0f / den;
 #pragma unroll
       for (int c = 0; c < NG; ++c)
 #pragma unroll
@@ -272,43 +305,38 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    bool nvalid;
+    uint32_t nrel;
+    token_of(tile + kThreads / 64, nvalid, nrel);
+    In8<TIn> nq[NKC];
+    In8<TOut> ndo[NG];
+    issue(nq, ndo, nvalid, nrel);
+
     if (valid) {
       const int64_t row = U.head_off + rel;
 #pragma unroll
       for (int c = 0; c < NG; ++c) {
         const int f0 = 32 * c + 8 * lg;
-        float out[8], gv[8];
+        float out[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
+        for (int r = 0; r < 8; ++r)
           out[r] = (acc_out<NCT>(acc2, c, r) + s_zt[f0 + r] * gden) * dphi_map<PHI>(cq[c].get(r));
-          gv[r] = g[c][r];
-        }
         store8(reinterpret_cast<TOut*>(p.dq) + row + f0, out);
-        store8(reinterpret_cast<float*>(p.gbuf) + row + f0, gv);
+      }
+      // the token's weights for dS~ and dz~ (kscale = 1/den, zw = gden * den = -(dO . o))
+      if (lg == 0) {
+        const int64_t t = (int64_t)U.bh * geo.N + rel / D;
+        p.tok_scale[t] = inv;
+        p.tok_zw[t] = -part;
       }
     }
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc)
+    for (int kc = 0; kc < NKC; ++kc) cq[kc] = nq[kc];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dzacc[kc][e] = fmaf(ph[kc][e], gden, dzacc[kc][e]);
+    for (int c = 0; c < NG; ++c) cdo[c] = ndo[c];
+    valid = nvalid;
+    rel = nrel;
   }
-
-  // dz~ of this unit: sum over the 16 token lanes, then over the four waves (fixed order)
-#pragma unroll
-  for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = dzacc[kc][e];
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      x += __shfl_xor(x, 4);
-      x += __shfl_xor(x, 8);
-      if (pr == 0) s_dzw[wave * D + 32 * kc + 8 * lg + e] = x;
-    }
-  __syncthreads();
-  if (tid < D)
-    p.dpz[((int64_t)U.row * p.splits + U.split) * D + tid] =
-        ((s_dzw[tid] + s_dzw[D + tid]) + s_dzw[2 * D + tid]) + s_dzw[3 * D + tid];
 }
 
 // ---- key side: dk, dv --------------------------------------------------------------------
@@ -339,17 +367,26 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
   const Rsrc rk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + U.head_off, (uint32_t)geo.N * D * ES);
 
-  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
+  // next tile's K, V loads before the current tile's stores (see dq_kernel)
+  auto token_of = [&](int tile, bool& valid, uint32_t& rel) {
     const int32_t j = U.j_begin + tile * 16 + pr;
-    const bool valid = j < U.j_end;
-    const uint32_t rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
-    In8<TIn> ck[NKC], cv[NKC];
+    valid = tile < U.n_tiles && j < U.j_end;
+    rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
+  };
+  auto issue = [&](In8<TIn> (&ck)[NKC], In8<TIn> (&cv)[NKC], bool valid, uint32_t rel) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const uint32_t off = valid ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange;
       ck[kc].template load_buf<0>(rk, off);
       cv[kc].template load_buf<0>(rv, off);
     }
+  };
+  In8<TIn> ck[NKC], cv[NKC];
+  bool valid;
+  uint32_t rel;
+  token_of(wave, valid, rel);
+  issue(ck, cv, valid, rel);
+  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
     f32x4_t acc1[NCT], acc2[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -378,20 +415,34 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (!valid) continue;
-    const int64_t row = U.head_off + rel;
+    bool nvalid;
+    uint32_t nrel;
+    token_of(tile + kThreads / 64, nvalid, nrel);
+    In8<TIn> nk[NKC], nv[NKC];
+    issue(nk, nv, nvalid, nrel);
+
+    if (valid) {
+      const int64_t row = U.head_off + rel;
 #pragma unroll
-    for (int c = 0; c < NG; ++c) {
-      const int f0 = 32 * c + 8 * lg;
-      float dvo[8], dko[8];
+      for (int c = 0; c < NG; ++c) {
+        const int f0 = 32 * c + 8 * lg;
+        float dvo[8], dko[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        dvo[r] = acc_out<NCT>(acc1, c, r);
-        dko[r] = (acc_out<NCT>(acc2, c, r) + s_dz[f0 + r]) * dphi_map<PHI>(ck[c].get(r));
+        for (int r = 0; r < 8; ++r) {
+          dvo[r] = acc_out<NCT>(acc1, c, r);
+          dko[r] = (acc_out<NCT>(acc2, c, r) + s_dz[f0 + r]) * dphi_map<PHI>(ck[c].get(r));
+        }
+        store8(reinterpret_cast<TOut*>(p.dv) + row + f0, dvo);
+        store8(reinterpret_cast<TOut*>(p.dk) + row + f0, dko);
       }
-      store8(reinterpret_cast<TOut*>(p.dv) + row + f0, dvo);
-      store8(reinterpret_cast<TOut*>(p.dk) + row + f0, dko);
     }
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      ck[kc] = nk[kc];
+      cv[kc] = nv[kc];
+    }
+    valid = nvalid;
+    rel = nrel;
   }
 }
 
@@ -464,21 +515,29 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
     __syncthreads();
     if (step + 1 < s_end) load_step(step + 1, xa, xb);
     const int kk = 8 * (lane >> 4);
+    u32x4_t fah[2], fal[2], fbh[2], fbl[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int ra = (wi + 16 * a + (lane & 15)) * kDmcPitch + kk;
-      const u32x4_t fah = *reinterpret_cast<const u32x4_t*>(a_hi + ra);
-      const u32x4_t fal = *reinterpret_cast<const u32x4_t*>(a_lo + ra);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int rb = (wb + 16 * c + (lane & 15)) * kDmcPitch + kk;
-        const u32x4_t fbh = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
-        const u32x4_t fbl = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
-        acc[a][c] = mfma_bf16(fah, fbh, acc[a][c]);
-        acc[a][c] = mfma_bf16(fal, fbh, acc[a][c]);
-        acc[a][c] = mfma_bf16(fah, fbl, acc[a][c]);
-      }
+      const int rb = (wb + 16 * a + (lane & 15)) * kDmcPitch + kk;
+      fah[a] = *reinterpret_cast<const u32x4_t*>(a_hi + ra);
+      fal[a] = *reinterpret_cast<const u32x4_t*>(a_lo + ra);
+      fbh[a] = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
+      fbl[a] = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
     }
+    // three rounds over the four independent accumulators
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbh[c], acc[a][c]);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fal[a], fbh[c], acc[a][c]);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbl[c], acc[a][c]);
     __syncthreads();
   }
   float* out = p.out + ((int64_t)grp * p.nchunks + chunk) * M * M;
@@ -526,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part,
 template <int D>
 static size_t dq_lds() {
   using Dm = Dims<D>;
-  return (size_t)4 * Dm::FRAG * 2 + (size_t)Dm::NKC * 512 * 2 + (size_t)D * 4 + (size_t)4 * D * 4;
+  return (size_t)4 * Dm::FRAG * 2 + (size_t)Dm::NKC * 512 * 2 + (size_t)D * 4;
 }
 template <int D>
 static size_t keyside_lds() {

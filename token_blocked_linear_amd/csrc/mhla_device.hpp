@@ -98,6 +98,10 @@ struct SummaryParams {
   uint16_t* mcf_lo;        // non-null: also the low parts (M_c = hi + lo, for the split mixing)
   int32_t mcf_transposed;  // 1: fragments of M_c^T (the backward's mixing)
   int32_t mcf_heads, mcf_nitp, mcf_nbc;
+  // Per-token weights (the backward's summary): phi(K_j) scaled by kscale[j], the normaliser
+  // product weighted by zw[j]; [BH][N] fp32 each.
+  const float* kscale;
+  const float* zw;
 };
 
 // Launch shape of the MFMA mixing kernel for M blocks: nbc 32-block chunks of the contraction,
@@ -153,8 +157,8 @@ struct BwdParams {
   const uint16_t* ds_hi;   // dS = M_c^T dS~ (fragments, hi / lo) [BH][M][FRAG]
   const uint16_t* ds_lo;
   const float* dz;         // dz [BH][M][D]
-  void* gbuf;              // g = dO / den (or dO) [BH][N][D] fp32
-  float* dpz;              // dz~ partials [BH][M][splits][D]
+  float* tok_scale;        // per token 1/den (1 unnormalised) [BH][N]
+  float* tok_zw;           // per token -(dO . o) (0 unnormalised) [BH][N]
   Geom g;
   int32_t splits;          // token slices per block (readout slicing)
   int32_t tok_per_split;

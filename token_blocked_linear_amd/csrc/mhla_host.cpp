@@ -16,8 +16,8 @@
 namespace mhla {
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
                           bool want_u, bool out_bf16, int phi, int n_units, hipStream_t stream);
-hipError_t launch_summary_bf16k_fp32v(const SummaryParams& p, int d, int phi, int n_units,
-                                      hipStream_t stream);
+hipError_t launch_summary_tokw(const SummaryParams& p, int d, bool in_fp32, bool v_fp32, int phi, int n_units,
+                               hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream);
 hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
@@ -332,7 +332,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     const bool mix_kernel = h->fuse == kFuseNone;
     const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
 
-    mhla::SummaryParams sp;
+    mhla::SummaryParams sp = {};
     sp.k = k;
     sp.v = v;
     sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
@@ -427,7 +427,7 @@ namespace {
 // Backward workspace: forward summaries recomputed at split precision, the backward's own
 // summaries, g, and the per-(batch, head) dM_c partials.
 struct BwdLayout {
-  size_t ps, pz, st_hi, st_lo, zt, dps, dpzs, dpzq, ds_hi, ds_lo, dz, gbuf, dmcp;
+  size_t ps, pz, st_hi, st_lo, zt, dps, dpzs, ds_hi, ds_lo, dz, tok_scale, tok_zw, dmcp;
   size_t mcf_hi, mcf_lo, mcft_hi, mcft_lo, total;   // M_c and M_c^T operand fragments
   bool mfma_mix;                                     // M <= 256: mixing on MFMA
   mhla::MixShape mix;
@@ -439,7 +439,7 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   BwdLayout L;
   const size_t f = (size_t)h->frag, dd = (size_t)h->d;
   const size_t rows = (size_t)h->BH * h->M;
-  const size_t slots = rows * h->sum_splits, rslots = rows * h->rd_splits;
+  const size_t slots = rows * h->sum_splits;
   size_t off = 0;
   auto take = [&](size_t& at, size_t bytes) { at = off; off = align256(off + bytes); };
   take(L.ps, slots * f * 4);
@@ -449,11 +449,11 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   take(L.zt, rows * dd * 4);
   take(L.dps, slots * f * 4);
   take(L.dpzs, slots * dd * 4);
-  take(L.dpzq, rslots * dd * 4);
   take(L.ds_hi, rows * f * 2);
   take(L.ds_lo, rows * f * 2);
   take(L.dz, rows * dd * 4);
-  take(L.gbuf, (size_t)h->BH * h->N * dd * 4);
+  take(L.tok_scale, (size_t)h->BH * h->N * 4);
+  take(L.tok_zw, (size_t)h->BH * h->N * 4);
   {
     L.dmc_groups = h->desc.mc_per_head ? (int)h->H : 1;
     L.dmc_group_bh = h->desc.mc_per_head ? (int)h->B : (int)h->BH;
@@ -611,8 +611,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     bp.ds_hi = U16(L.ds_hi);
     bp.ds_lo = U16(L.ds_lo);
     bp.dz = F(L.dz);
-    bp.gbuf = ws + L.gbuf;
-    bp.dpz = F(L.dpzq);
+    bp.tok_scale = F(L.tok_scale);
+    bp.tok_zw = F(L.tok_zw);
     bp.g = h->geom;
     bp.splits = h->rd_splits;
     bp.tok_per_split = h->rd_tok;
@@ -623,23 +623,25 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
         !mark())
       return MHLA_ERR_HIP;
 
-    // 4. dS~ = sum_t q~_t g_t^T: the summary kernel with K := Q, V := g (g in fp32, split)
+    // 4. dS~ = sum_t (q~_t / den_t) dO_t^T and dz~ = sum_t q~_t gden_t: the summary kernel with
+    //    K := Q scaled per token by 1/den, V := dO, normaliser weights -(dO . o)
     mhla::SummaryParams sq = sp;
     sq.k = q;
-    sq.v = ws + L.gbuf;
+    sq.v = dout;
     sq.ps = F(L.dps);
     sq.pz = F(L.dpzs);
+    sq.kscale = F(L.tok_scale);
+    sq.zw = F(L.tok_zw);
     if (L.mfma_mix) {   // side job: M_c^T operand fragments for the transposed mixing
       sq.mcf = U16(L.mcft_hi);
       sq.mcf_lo = U16(L.mcft_lo);
       sq.mcf_transposed = 1;
     }
-    e = h->in_fp32 ? mhla::launch_summary(sq, h->d, true, true, true, false, false, phi, units_sum, s)
-                   : mhla::launch_summary_bf16k_fp32v(sq, h->d, phi, units_sum, s);
+    e = mhla::launch_summary_tokw(sq, h->d, h->in_fp32, h->out_fp32, phi, units_sum, s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
-    // 5. dS = M_c^T dS~, dz = M_c^T dz~ (dz~ partials per readout token slice)
-    if ((e = mix(F(L.dps), F(L.dpzq), h->rd_splits, 1, U16(L.ds_hi), U16(L.ds_lo), F(L.dz))) != hipSuccess ||
+    // 5. dS = M_c^T dS~, dz = M_c^T dz~
+    if ((e = mix(F(L.dps), F(L.dpzs), h->sum_splits, 1, U16(L.ds_hi), U16(L.ds_lo), F(L.dz))) != hipSuccess ||
         !mark())
       return MHLA_ERR_HIP;
 
@@ -654,14 +656,14 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
       mhla::DmcParams dp = {};
       dp.dps = F(L.dps);
       dp.ps = F(L.ps);
-      dp.dpz = F(L.dpzq);
+      dp.dpz = F(L.dpzs);
       dp.pz = F(L.pz);
       dp.out = F(L.dmcp);
       dp.M = (int32_t)h->M;
       dp.frag = h->frag;
       dp.D = h->d;
       dp.ssplits = h->sum_splits;
-      dp.zsplits_d = h->rd_splits;
+      dp.zsplits_d = h->sum_splits;
       dp.H = (int32_t)h->H;
       dp.per_head = h->desc.mc_per_head ? 1 : 0;
       dp.group_bh = L.dmc_group_bh;

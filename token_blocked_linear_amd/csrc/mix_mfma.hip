@@ -211,23 +211,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
         for (int a = 0; a < ITW; ++a) accs[pt][a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (SPLIT) {
+        // two accumulators (pt = 0, 1), both chunks' operands read first, then three rounds
+        // of independent MFMAs (hi*hi, lo*hi, hi*lo)
 #pragma unroll
-      for (int bc = 0; bc < NBC; ++bc)
+        for (int bc = 0; bc < NBC; ++bc) {
+          u32x4_t ah[2], al[2];
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
-          const int ofs = r * XP + 8 * swz(r, 4 * bc + lg);
-          const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + ofs);
-#pragma unroll
-          for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag[a][bc], accs[pt][a]);
-          if constexpr (SPLIT) {
-            const u32x4_t afrag_lo = *reinterpret_cast<const u32x4_t*>(xt_lo + ofs);
-            accs[pt][0] = mfma_bf16(afrag_lo, bfrag[0][bc], accs[pt][0]);
-            accs[pt][0] = mfma_bf16(afrag, bfrag_lo[bc], accs[pt][0]);
+          for (int pt = 0; pt < 2; ++pt) {
+            const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
+            const int ofs = r * XP + 8 * swz(r, 4 * bc + lg);
+            ah[pt] = *reinterpret_cast<const u32x4_t*>(xt + ofs);
+            al[pt] = *reinterpret_cast<const u32x4_t*>(xt_lo + ofs);
           }
-          // with 128 registers of M_c fragments, keep each operand read next to its MFMAs
-          if constexpr (NBC * ITW >= 32) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) accs[pt][0] = mfma_bf16(ah[pt], bfrag[0][bc], accs[pt][0]);
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) accs[pt][0] = mfma_bf16(al[pt], bfrag[0][bc], accs[pt][0]);
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) accs[pt][0] = mfma_bf16(ah[pt], bfrag_lo[bc], accs[pt][0]);
         }
+      } else {
+#pragma unroll
+        for (int bc = 0; bc < NBC; ++bc)
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) {
+            const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
+            const int ofs = r * XP + 8 * swz(r, 4 * bc + lg);
+            const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + ofs);
+#pragma unroll
+            for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag[a][bc], accs[pt][a]);
+            // with 128 registers of M_c fragments, keep each operand read next to its MFMAs
+            if constexpr (NBC * ITW >= 32) __builtin_amdgcn_sched_barrier(0);
+          }
+      }
       const int q = 32 * cgp + 8 * lg;         // first of this lane's 8 tile columns
 #pragma unroll
       for (int a = 0; a < ITW; ++a) {

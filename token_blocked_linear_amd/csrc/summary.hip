@@ -21,9 +21,12 @@
 
 namespace mhla {
 
-// TV, the element type of V, is TIn except in the backward, which feeds bf16 Q as K and the
-// fp32 gradient g as V.
-template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16, int PHI, typename TV>
+// TV, the element type of V, is TIn except in the backward, which feeds Q as K and dO (the
+// output's type) as V.  TOKW (backward): phi(K_j) is scaled by kscale[j] and the normaliser
+// product weights token j by zw[j] instead of 1, so that S = sum_j kscale_j phi(K_j) V_j^T and
+// z = sum_j kscale_j zw_j phi(K_j).
+template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16, int PHI, typename TV,
+          bool TOKW>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int n_units) {
   using Dm = Dims<D>;
   constexpr int DK = Dm::DK, NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -51,6 +54,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   uint16_t* kt_lo = kt_hi + DK * PITCH;                     // [DK][PITCH]   (SPLIT_K)
   uint16_t* vt_hi = kt_lo + (SPLIT_K ? DK * PITCH : 0);     // [D][PITCH]
   uint16_t* vt_lo = vt_hi + D * PITCH;                      // [D][PITCH]    (SPLIT_V)
+  float* s_zw = reinterpret_cast<float*>(vt_lo + (SPLIT_V ? D * PITCH : 0));   // [ROUND] (TOKW)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,7 +137,9 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
   // out-of-range offset and read as zero, with no branch around the loads.
   constexpr uint32_t ES = sizeof(TIn), ESV = sizeof(TV);
   const uint32_t head_bytes = (uint32_t)g.N * D * ES, head_bytes_v = (uint32_t)g.N * D * ESV;
-  auto issue_loads = [&](In8<TIn> (&rk)[8], In8<TV> (&rv)[8], const Unit& U, int32_t round_base) {
+  // tw (TOKW): kscale of the thread's 8 tokens in tw[0..7], zw in tw[8..15]; 0 past the end
+  auto issue_loads = [&](In8<TIn> (&rk)[8], In8<TV> (&rv)[8], float (&tw)[16], const Unit& U,
+                         int32_t round_base) {
     const Rsrc rsk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, head_bytes);
     const Rsrc rsv = make_rsrc(reinterpret_cast<const TV*>(p.v) + U.head_off, head_bytes_v);
     const int32_t j0 = round_base + 8 * tgrp;
@@ -146,6 +152,21 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, ok ? (e0 + (uint32_t)(i * D)) * ES : kOutOfRange);
         rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, ok ? (e0 + (uint32_t)(i * D)) * ESV : kOutOfRange);
       }
+      if constexpr (TOKW) {
+        // t0 is a multiple of 8 here (block and grid extents along the last axis are), and so
+        // is j_end: the 8 tokens are all in the unit or all past its end
+        const Rsrc rs = make_rsrc(p.kscale + (int64_t)U.bh * g.N, (uint32_t)g.N * 4u);
+        const Rsrc rz = make_rsrc(p.zw + (int64_t)U.bh * g.N, (uint32_t)g.N * 4u);
+        const u32x4_t s0 = buf_ld16(rs, ok ? t0 * 4u : kOutOfRange), s1 = buf_ld16(rs, ok ? t0 * 4u + 16u : kOutOfRange);
+        const u32x4_t z0 = buf_ld16(rz, ok ? t0 * 4u : kOutOfRange), z1 = buf_ld16(rz, ok ? t0 * 4u + 16u : kOutOfRange);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tw[i] = __uint_as_float(s0[i]);
+          tw[4 + i] = __uint_as_float(s1[i]);
+          tw[8 + i] = __uint_as_float(z0[i]);
+          tw[12 + i] = __uint_as_float(z1[i]);
+        }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -155,6 +176,11 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         const uint32_t e = t * D + 8 * fgrp;
         rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, ok ? e * ES : kOutOfRange);
         rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, ok ? e * ESV : kOutOfRange);
+        if constexpr (TOKW) {
+          const int64_t ti = (int64_t)U.bh * g.N + t;
+          tw[i] = ok ? p.kscale[ti] : 0.f;
+          tw[8 + i] = ok ? p.zw[ti] : 0.f;
+        }
       }
     }
   };
@@ -176,16 +202,26 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
 
   // One round: phi / split / transpose into LDS, MFMAs, and the unit's epilogue if it ends.
   // `after_lds` runs once the round's registers are in LDS (single-buffer refill point).
-  auto process = [&](const In8<TIn> (&rk)[8], const In8<TV> (&rv)[8], const Unit& U, int32_t rb,
-                     auto&& after_lds) {
+  auto process = [&](const In8<TIn> (&rk)[8], const In8<TV> (&rv)[8], const float (&tw)[16], const Unit& U,
+                     int32_t rb, auto&& after_lds) {
     if (loader) {
+      if (TOKW && fgrp == 0) {   // the round's normaliser weights, one writer per token group
+        st16(s_zw + 8 * tgrp, u32x4_t{__float_as_uint(tw[8]), __float_as_uint(tw[9]), __float_as_uint(tw[10]),
+                                      __float_as_uint(tw[11])});
+        st16(s_zw + 8 * tgrp + 4, u32x4_t{__float_as_uint(tw[12]), __float_as_uint(tw[13]),
+                                          __float_as_uint(tw[14]), __float_as_uint(tw[15])});
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int f = 8 * fgrp + e;
         u32x4_t hi, lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x0 = phi_map<PHI>(rk[2 * i].get(e)), x1 = phi_map<PHI>(rk[2 * i + 1].get(e));
+          float x0 = phi_map<PHI>(rk[2 * i].get(e)), x1 = phi_map<PHI>(rk[2 * i + 1].get(e));
+          if (TOKW) {
+            x0 *= tw[2 * i];
+            x1 *= tw[2 * i + 1];
+          }
           if (SPLIT_K) {
             uint32_t h, l;
             split_bf16x2(x0, x1, h, l);
@@ -232,13 +268,27 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
       const u32x4_t ones = {kOnes, kOnes, kOnes, kOnes};
       for (int ks = 0; ks < nsteps; ++ks) {
         const int chunk = 4 * ks + lg;           // 16-byte chunk of tokens 32ks + 8lg ..
-        // token validity as the B operand of the z product (phi(0) = 1 on padding rows)
-        u32x4_t vmask = ones;
-        const int left = valid_round - 8 * chunk;
-        if (left < 8) {
+        // token validity as the B operand of the z product (phi(0) = 1 on padding rows); with
+        // TOKW the tokens' weights instead, split hi (vmask) + lo (wlo); 0 past the end
+        u32x4_t vmask = ones, wlo = {0u, 0u, 0u, 0u};
+        if constexpr (TOKW) {
+          const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(s_zw + 8 * chunk);
+          const u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(s_zw + 8 * chunk + 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vmask[i] = (2 * i < left ? 0x3f80u : 0u) | (2 * i + 1 < left ? 0x3f800000u : 0u);
+          for (int i = 0; i < 4; ++i) {
+            const u32x4_t& w = i < 2 ? w0 : w1;
+            uint32_t h, l;
+            split_bf16x2(__uint_as_float(w[(2 * i) & 3]), __uint_as_float(w[(2 * i + 1) & 3]), h, l);
+            vmask[i] = h;
+            wlo[i] = l;
+          }
+        } else {
+          const int left = valid_round - 8 * chunk;
+          if (left < 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              vmask[i] = (2 * i < left ? 0x3f80u : 0u) | (2 * i + 1 < left ? 0x3f800000u : 0u);
+          }
         }
         u32x4_t a_hi[KCW][2], a_lo[KCW][2], b_hi[CTW], b_lo[CTW];
 #pragma unroll
@@ -272,6 +322,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
             if (wc == 0) {
               accz[a][r] = mfma_bf16(a_hi[a][r], vmask, accz[a][r]);
               if (SPLIT_K) accz[a][r] = mfma_bf16(a_lo[a][r], vmask, accz[a][r]);
+              if (TOKW) accz[a][r] = mfma_bf16(a_hi[a][r], wlo, accz[a][r]);
             }
           }
         if (WANT_U && wr == 0) {
@@ -349,21 +400,22 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
     // phi, LDS and MFMA.
     In8<TIn> ka[8], kb[8];
     In8<TV> va[8], vb[8];
-    issue_loads(ka, va, U, rb);
+    float twa[16], twb[16];
+    issue_loads(ka, va, twa, U, rb);
     while (true) {
       int nu = unit;
       Unit NU = U;
       int32_t nrb = rb;
       advance(nu, NU, nrb);
-      if (nu < n_units) issue_loads(kb, vb, NU, nrb);
-      process(ka, va, U, rb, nothing);
+      if (nu < n_units) issue_loads(kb, vb, twb, NU, nrb);
+      process(ka, va, twa, U, rb, nothing);
       if (nu >= n_units) break;
       unit = nu;
       U = NU;
       rb = nrb;
       advance(nu, NU, nrb);
-      if (nu < n_units) issue_loads(ka, va, NU, nrb);
-      process(kb, vb, U, rb, nothing);
+      if (nu < n_units) issue_loads(ka, va, twa, NU, nrb);
+      process(kb, vb, twb, U, rb, nothing);
       if (nu >= n_units) break;
       unit = nu;
       U = NU;
@@ -374,14 +426,15 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
     // the round sits in LDS, so the loads overlap the MFMA phase.
     In8<TIn> ka[8];
     In8<TV> va[8];
-    issue_loads(ka, va, U, rb);
+    float twa[16];
+    issue_loads(ka, va, twa, U, rb);
     while (true) {
       int nu = unit;
       Unit NU = U;
       int32_t nrb = rb;
       advance(nu, NU, nrb);
-      process(ka, va, U, rb, [&] {
-        if (nu < n_units) issue_loads(ka, va, NU, nrb);
+      process(ka, va, twa, U, rb, [&] {
+        if (nu < n_units) issue_loads(ka, va, twa, NU, nrb);
       });
       if (nu >= n_units) break;
       unit = nu;
@@ -392,13 +445,14 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
 }
 
 template <int PHI, typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16 = false,
-          typename TV = TIn>
+          typename TV = TIn, bool TOKW = false>
 static hipError_t launch_summary_t(const SummaryParams& p, int n_units, hipStream_t stream) {
   using Dm = Dims<D>;
   constexpr int LPR = D / 8, TG_ALL = kThreads / LPR, TG = TG_ALL < 32 ? TG_ALL : 32;
   constexpr int ROUND = TG * 8, PITCH = ROUND;
-  const size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2;
-  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16, PHI, TV>;
+  const size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2 +
+                    (TOKW ? (size_t)ROUND * 4 : 0);
+  auto kern = summary_kernel<TIn, D, SPLIT_K, SPLIT_V, WANT_U, OUT_BF16, PHI, TV, TOKW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -463,18 +517,27 @@ hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool spli
   }
 }
 
-// bf16 K with fp32 V (the backward's dS~ = sum_t phi(q_t) g_t^T): both operands split, fp32
-// partials, no u.  Head sizes 32, 64, 128.
-hipError_t launch_summary_bf16k_fp32v(const SummaryParams& p, int d, int phi, int n_units,
-                                      hipStream_t stream) {
+// The backward's dS~ = sum_t (phi(q_t) / den_t) dO_t^T and dz~ = sum_t phi(q_t) gden_t, as a
+// summary with K := Q scaled per token by kscale = 1/den and V := dO, whose normaliser product
+// weights token t by zw = gden_t * den_t = -(dO_t . o_t).  K split; V split when fp32 (bf16 dO
+// is exact); fp32 partials; head sizes 32, 64, 128.
+hipError_t launch_summary_tokw(const SummaryParams& p, int d, bool in_fp32, bool v_fp32, int phi, int n_units,
+                               hipStream_t stream) {
   auto go = [&](auto phi_c) -> hipError_t {
     constexpr int PHI = decltype(phi_c)::value;
-    switch (d) {
-      case 32: return launch_summary_t<PHI, uint16_t, 32, true, true, false, false, float>(p, n_units, stream);
-      case 64: return launch_summary_t<PHI, uint16_t, 64, true, true, false, false, float>(p, n_units, stream);
-      case 128: return launch_summary_t<PHI, uint16_t, 128, true, true, false, false, float>(p, n_units, stream);
-      default: return hipErrorInvalidValue;
-    }
+    auto by_d = [&](auto tin, auto tv) -> hipError_t {
+      using TI = decltype(tin);
+      using TV = decltype(tv);
+      constexpr bool SV = sizeof(TV) == 4;
+      switch (d) {
+        case 32: return launch_summary_t<PHI, TI, 32, true, SV, false, false, TV, true>(p, n_units, stream);
+        case 64: return launch_summary_t<PHI, TI, 64, true, SV, false, false, TV, true>(p, n_units, stream);
+        case 128: return launch_summary_t<PHI, TI, 128, true, SV, false, false, TV, true>(p, n_units, stream);
+        default: return hipErrorInvalidValue;
+      }
+    };
+    if (in_fp32) return v_fp32 ? by_d(float{}, float{}) : by_d(float{}, uint16_t{});
+    return v_fp32 ? by_d(uint16_t{}, float{}) : by_d(uint16_t{}, uint16_t{});
   };
   switch (phi) {
     case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
