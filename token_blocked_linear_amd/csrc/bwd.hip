@@ -449,11 +449,11 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
 // ---- dM_c ---------------------------------------------------------------------------------
 // dmc[i][b] = sum over (batch-head, position) of dS~_i and S_b (fragment positions, then the D
 // normaliser entries), both summed over their token slices while loaded.  A 64 x 64 output tile
-// and one chunk of 32-position steps per workgroup; each step is staged through LDS as bf16
+// and one chunk of 64-position steps per workgroup; each step is staged through LDS as bf16
 // hi / lo, and each wave owns a 32 x 32 quarter (2 x 2 MFMA tiles): A = dS~ rows, B = S rows,
 // both with 8 consecutive positions per lane.  The next step's loads are in flight during the
-// MFMAs.
-constexpr int kDmcTile = 64, kDmcK = 32, kDmcPitch = kDmcK + 8;   // pitch in bf16 elements
+// MFMAs.  Positions past FRAG + D (the last step of a (batch, head)) read as zero.
+constexpr int kDmcTile = 64, kDmcK = 64, kDmcPitch = kDmcK + 8;   // pitch in bf16 elements
 
 __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
   __shared__ __align__(16) uint16_t a_hi[kDmcTile * kDmcPitch], a_lo[kDmcTile * kDmcPitch];
@@ -461,9 +461,15 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, FRAG = p.frag, D = p.D;
   const int nt = (M + kDmcTile - 1) / kDmcTile;
-  const int i0 = (blockIdx.x / nt) * kDmcTile, b0 = (blockIdx.x % nt) * kDmcTile;
-  const int chunk = blockIdx.y, grp = blockIdx.z;
-  const int lrow = tid >> 2, lcol = (tid & 3) * 8;   // loader: one row, 8 positions
+  // Workgroup L -> (chunk, output tile): the nt^2 tiles of one chunk read the same rows, so
+  // they share an XCD (workgroups are dealt to the 8 XCDs round robin): L = 8 * (c8 * nt^2 +
+  // tile) + x with chunk = 8 * c8 + x.  Slots of chunks >= nchunks have nothing to do.
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int tile = slot % (nt * nt), chunk = 8 * (slot / (nt * nt)) + xcd;
+  if (chunk >= p.nchunks) return;
+  const int i0 = (tile / nt) * kDmcTile, b0 = (tile % nt) * kDmcTile;
+  const int grp = blockIdx.y;
+  const int lrow = tid >> 2, lcol = (tid & 3) * 16;   // loader: one row, 16 positions
   const int wi = (wave >> 1) * 32, wb = (wave & 1) * 32;
   const int64_t total_steps = (int64_t)p.group_bh * p.steps_per_bh;
   const int64_t s_begin = (int64_t)chunk * p.steps_per_chunk;
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
   auto load8 = [&](const float* part, const float* zpart, int zsplits, int bh, int m, int pos, float (&x)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    if (m >= M) return;
+    if (m >= M || pos >= FRAG + D) return;
     const int64_t r = (int64_t)bh * M + m;
     const bool in_s = pos < FRAG;
     const int ns = in_s ? p.ssplits : zsplits;
@@ -487,12 +493,15 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
       }
     }
   };
-  auto load_step = [&](int64_t step, float (&xa)[8], float (&xb)[8]) {
+  auto load_step = [&](int64_t step, float (&xa)[2][8], float (&xb)[2][8]) {
     const int j = (int)(step / p.steps_per_bh);
     const int pos = (int)(step % p.steps_per_bh) * kDmcK + lcol;
     const int bh = p.per_head ? j * p.H + grp : j;
-    load8(p.dps, p.dpz, p.zsplits_d, bh, i0 + lrow, pos, xa);
-    load8(p.ps, p.pz, p.ssplits, bh, b0 + lrow, pos, xb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      load8(p.dps, p.dpz, p.zsplits_d, bh, i0 + lrow, pos + 8 * h, xa[h]);
+      load8(p.ps, p.pz, p.ssplits, bh, b0 + lrow, pos + 8 * h, xb[h]);
+    }
   };
 
   f32x4_t acc[2][2];
@@ -501,43 +510,49 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  float xa[8], xb[8];
+  float xa[2][8], xb[2][8];
   if (s_begin < s_end) load_step(s_begin, xa, xb);
   for (int64_t step = s_begin; step < s_end; ++step) {
-    u32x4_t ah, al, bhh, bll;
-    split8(xa, ah, al);
-    split8(xb, bhh, bll);
-    const int o = lrow * kDmcPitch + lcol;
-    st16(a_hi + o, ah);
-    st16(a_lo + o, al);
-    st16(b_hi + o, bhh);
-    st16(b_lo + o, bll);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t ah, al, bhh, bll;
+      split8(xa[h], ah, al);
+      split8(xb[h], bhh, bll);
+      const int o = lrow * kDmcPitch + lcol + 8 * h;
+      st16(a_hi + o, ah);
+      st16(a_lo + o, al);
+      st16(b_hi + o, bhh);
+      st16(b_lo + o, bll);
+    }
     __syncthreads();
     if (step + 1 < s_end) load_step(step + 1, xa, xb);
-    const int kk = 8 * (lane >> 4);
-    u32x4_t fah[2], fal[2], fbh[2], fbl[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int ra = (wi + 16 * a + (lane & 15)) * kDmcPitch + kk;
-      const int rb = (wb + 16 * a + (lane & 15)) * kDmcPitch + kk;
-      fah[a] = *reinterpret_cast<const u32x4_t*>(a_hi + ra);
-      fal[a] = *reinterpret_cast<const u32x4_t*>(a_lo + ra);
-      fbh[a] = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
-      fbl[a] = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
+    for (int k2 = 0; k2 < kDmcK; k2 += 32) {
+      const int kk = k2 + 8 * (lane >> 4);
+      u32x4_t fah[2], fal[2], fbh[2], fbl[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int ra = (wi + 16 * a + (lane & 15)) * kDmcPitch + kk;
+        const int rb = (wb + 16 * a + (lane & 15)) * kDmcPitch + kk;
+        fah[a] = *reinterpret_cast<const u32x4_t*>(a_hi + ra);
+        fal[a] = *reinterpret_cast<const u32x4_t*>(a_lo + ra);
+        fbh[a] = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
+        fbl[a] = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
+      }
+      // three rounds over the four independent accumulators
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbh[c], acc[a][c]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fal[a], fbh[c], acc[a][c]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbl[c], acc[a][c]);
     }
-    // three rounds over the four independent accumulators
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbh[c], acc[a][c]);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fal[a], fbh[c], acc[a][c]);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbl[c], acc[a][c]);
     __syncthreads();
   }
   float* out = p.out + ((int64_t)grp * p.nchunks + chunk) * M * M;
@@ -565,7 +580,8 @@ __global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part,
     const int64_t g = idx / mm, e = idx % mm;
     const float* src = part + g * nchunks * mm + e;
     float s = 0.f;
-    for (int c = 0; c < nchunks; ++c) s += src[(int64_t)c * mm];
+#pragma unroll 8
+    for (int c = 0; c < nchunks; ++c) s += src[(int64_t)c * mm];   // loads issued ahead, adds in order
     dmc[idx] = s;
   } else {
     const int lane = threadIdx.x & 63;
@@ -642,7 +658,8 @@ hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp
 hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream) {
   const int t = (p.M + kDmcTile - 1) / kDmcTile;
   const int groups = p.per_head ? p.H : 1;
-  hipLaunchKernelGGL(dmc_kernel, dim3(t * t, p.nchunks, groups), dim3(kThreads), 0, stream, p);
+  const int c8 = (p.nchunks + 7) / 8;
+  hipLaunchKernelGGL(dmc_kernel, dim3(8 * c8 * t * t, groups), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t mm = (int64_t)p.M * p.M, n_out = (int64_t)groups * mm;

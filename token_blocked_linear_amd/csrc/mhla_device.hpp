@@ -170,7 +170,7 @@ struct BwdParams {
 // over their token slices on the fly.
 // The contraction runs over (batch-head, position) pairs of a group: every (batch, head) for a
 // shared M_c, every batch item of head g for a per-head one (bh = j*H + g).  It is cut into
-// `nchunks` chunks of `steps_per_chunk` 32-position steps, each chunk giving one partial.
+// `nchunks` chunks of `steps_per_chunk` 64-position steps, each chunk giving one partial.
 struct DmcParams {
   const float* dps;        // dS~ partials [BH][M][ssplits][FRAG]
   const float* ps;         // S partials   [BH][M][ssplits][FRAG]
@@ -179,7 +179,7 @@ struct DmcParams {
   float* out;              // partials [groups][nchunks][M][M]
   int32_t M, frag, D, ssplits, zsplits_d;
   int32_t H, per_head, group_bh;           // group_bh: (batch, head) pairs per group
-  int32_t steps_per_bh;                    // (FRAG + D) / 32
+  int32_t steps_per_bh;                    // ceil((FRAG + D) / 64)
   int32_t nchunks, steps_per_chunk;
 };
 

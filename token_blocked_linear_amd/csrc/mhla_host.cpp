@@ -457,7 +457,7 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   {
     L.dmc_groups = h->desc.mc_per_head ? (int)h->H : 1;
     L.dmc_group_bh = h->desc.mc_per_head ? (int)h->B : (int)h->BH;
-    L.dmc_steps_per_bh = (h->frag + h->d) / 32;
+    L.dmc_steps_per_bh = (h->frag + h->d + 63) / 64;   // 64-position steps (the last one padded)
     const int64_t total = (int64_t)L.dmc_group_bh * L.dmc_steps_per_bh;
     const int64_t t = (h->M + 63) / 64;
     // about 2048 workgroups (8 per CU)

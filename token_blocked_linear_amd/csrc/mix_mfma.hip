@@ -95,16 +95,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       for (int r = 0; r < 8; ++r) {
         const int b = 8 * rg + r;
         const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits) * P + tile * PB + 8 * cg) * 4u : kOutOfRange;
-        raw[2 * r] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, o0);
-        raw[2 * r + 1] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? o0 + 16u : kOutOfRange);
+        // default cache policy: the row groups of a column tile run on one XCD and share it
+        raw[2 * r] = buf_ld16(rsx, o0);
+        raw[2 * r + 1] = buf_ld16(rsx, b < M ? o0 + 16u : kOutOfRange);
       }
       for (int s = 1; s < p.xsplits; ++s) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int b = 8 * rg + r;
           const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits + s) * P + tile * PB + 8 * cg) * 4u : kOutOfRange;
-          const u32x4_t w0 = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, o0);
-          const u32x4_t w1 = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? o0 + 16u : kOutOfRange);
+          const u32x4_t w0 = buf_ld16(rsx, o0);
+          const u32x4_t w1 = buf_ld16(rsx, b < M ? o0 + 16u : kOutOfRange);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             raw[2 * r][j] = __float_as_uint(__uint_as_float(raw[2 * r][j]) + __uint_as_float(w0[j]));
