@@ -17,6 +17,7 @@ WRITE_SIZE hardware counters, each scaled by what the counter reads for a plain 
 size), taken from profiles/traffic.md when that record was made from the current kernel sources
 (same digest of the csrc/ files and the header), else null.
 
+`causal` times the chunkwise-causal forward (1D workloads) on the same inputs.
 `backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the same
 inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
 
@@ -130,6 +131,13 @@ def kernel_accounting(w: synth.Workload, out_bytes: int, split: bool = False):
     # so the fused kernel carries the readout's bytes plus M_c
     acc["mix+readout"] = dict(bytes=acc["readout"]["bytes"] + acc["mix"]["bytes"],
                               flops=acc["readout"]["flops"] + acc["mix"]["flops"], bound="hbm")
+    # causal readout: Q, K, V read and O written; the state readout and update (2 d^2 each) plus
+    # the in-sub-chunk term (scores and P V against up to SUB keys, SUB = 32 at d = 128, else 64)
+    sub = 32 if d >= 128 else 64
+    acc["causal"] = dict(bytes=tok * d * (3 * in_b + out_bytes), flops=tok * (4 * d * d + 2 * d * sub), bound="hbm")
+    acc["scan"] = dict(bytes=0, flops=0, bound="hbm")
+    if w.readout.startswith("causal"):
+        acc["mix"]["bound"] = "mfma" if M <= 256 else "alu"
     total_bytes = tok * d * (3 * in_b + out_bytes) + (0 if w.readout == "mala" else M * M * 4)
     total_flops = acc["summary"]["flops"] + acc["mix+readout"]["flops"]
     return acc, total_bytes, total_flops
@@ -163,11 +171,14 @@ def cold_steps(plan, args_fwd, stream, n: int):
     return float(np.median(times))
 
 
-def run_workload(name: str, steps: int, warmup: int, out_dtype: str, n_cold: int = 20, inputs=None):
+def run_workload(name: str, steps: int, warmup: int, out_dtype: str, n_cold: int = 20, inputs=None,
+                 readout=None):
     import torch
     import token_blocked_linear_amd as T
 
     w = synth.WORKLOADS[name]
+    if readout is not None:
+        w = w.with_(readout=readout)
     q, k, v, mc = inputs if inputs is not None else synth.make_inputs(w)[:4]
     plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
                   in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout)
@@ -335,6 +346,7 @@ def main():
     ap.add_argument("--out-dtype", default="bf16", choices=["fp32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-causal", action="store_true", help="skip the causal-readout measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--digest", action="store_true")
     args = ap.parse_args()
@@ -396,6 +408,14 @@ def main():
            "cold_cache_ms": round(r2["cold_step_s"] * 1e3, 4), "kernels": r2["per_kernel"]}
     del r2
 
+    causal = None
+    if w.ndim == 1 and w.readout == "normalized" and not args.no_causal:
+        rc = run_workload(args.workload, args.steps, args.warmup, args.out_dtype, n_cold=0, inputs=res["inputs"],
+                          readout="causal")
+        causal = {"readout": "causal (normalised)", "ms_per_step": round(rc["step_s"] * 1e3, 4),
+                  "tokens_per_s": round(rc["tokens_per_s"], 1), "kernels": rc["per_kernel"]}
+        del rc
+
     bwd = None
     if not args.no_backward and w.readout != "mala":
         bwd = run_backward(args.workload, args.steps, args.warmup, args.out_dtype, res["inputs"])
@@ -430,6 +450,8 @@ def main():
     line[f"{other_out}_output"] = alt
     if bwd is not None:
         line["backward"] = bwd
+    if causal is not None:
+        line["causal"] = causal
     if others:
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)

@@ -66,10 +66,18 @@ typedef enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_FP32 = 1 } mhla_dtype;
  * positive feature has a zero normaliser: the IEEE result 0/0 = NaN is returned (no epsilon). */
 typedef enum { MHLA_PHI_ELU1 = 0, MHLA_PHI_RELU = 1, MHLA_PHI_EXP = 2 } mhla_phi;
 
+/* Chunkwise-causal modes ("MHLA: Restoring Expressivity of Linear Attention via Token-Level
+ * Multi-Head", Key design 4 names chunkwise-parallel training and streaming inference; the causal
+ * form is a reading): the token-expanded sum of Key design 2 masked to keys t' <= t, i.e. query t
+ * of block i reads sum_{b<i} m_ib S_b plus m_ii times its own block's prefix up to t; entries of
+ * M_c above the diagonal are not read.  1D grids and d >= 32 only (else MHLA_ERR_UNSUPPORTED);
+ * always on split operands (the accuracy field is not consulted). */
 typedef enum {
   MHLA_READOUT_NORMALIZED = 0,    /* o = phi(q)^T S~_i / phi(q)^T z~_i                         */
   MHLA_READOUT_UNNORMALIZED = 1,  /* o = phi(q)^T S~_i                                        */
-  MHLA_READOUT_MALA = 2           /* magnitude-aware readout; requires M == 1                  */
+  MHLA_READOUT_MALA = 2,          /* magnitude-aware readout; requires M == 1                  */
+  MHLA_READOUT_CAUSAL_NORMALIZED = 3,    /* causal, normalised                                 */
+  MHLA_READOUT_CAUSAL_UNNORMALIZED = 4   /* causal, no normaliser                              */
 } mhla_readout;
 
 typedef enum {
@@ -109,7 +117,8 @@ typedef struct {
   int32_t readout_splits;   /* token slices per block in the readout kernel                    */
   int32_t n_kernels;        /* kernels launched per mhla_forward: 3 (summary, mix, readout),   */
                             /* or 2 (summary, mix+readout) when the mixing step runs in the    */
-                            /* readout's prologue: MALA readout, or at most 16 blocks          */
+                            /* readout's prologue: MALA readout, or at most 16 blocks; causal: */
+                            /* summary, mix (M > 1), scan (blocks over 256 tokens), causal     */
   int32_t split_operands;   /* 1 if hi/lo operand splitting is in use                          */
 } mhla_plan_info;
 

@@ -52,8 +52,11 @@ def announce(msg: str) -> None:
     sys.stdout.flush()
 
 
-def oracle_full(w, q, k, v, mc):
-    return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout, phi=w.phi)
+def oracle_full(w, q, k, v, mc, heads=None):
+    if w.readout.startswith("causal"):
+        mode = "unnormalized" if w.readout == "causal_unnormalized" else "normalized"
+        return oracle.forward_causal(q, k, v, mc, w.grid, w.block, mode=mode, heads=heads, phi=w.phi)
+    return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout, heads=heads, phi=w.phi)
 
 
 def run_hip_backward(w: synth.Workload, q, k, v, mc, do, *, out_dtype="fp32", want_dmc=True, repeat=1):

@@ -14,6 +14,7 @@ from typing import Optional, Sequence
 __all__ = [
     "MHLA_OK", "MHLA_DTYPE_BF16", "MHLA_DTYPE_FP32", "MHLA_PHI_ELU1", "MHLA_PHI_RELU", "MHLA_PHI_EXP",
     "MHLA_READOUT_NORMALIZED", "MHLA_READOUT_UNNORMALIZED", "MHLA_READOUT_MALA",
+    "MHLA_READOUT_CAUSAL_NORMALIZED", "MHLA_READOUT_CAUSAL_UNNORMALIZED",
     "MHLA_ACCURACY_AUTO", "MHLA_ACCURACY_BF16", "MHLA_ACCURACY_SPLIT",
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
@@ -25,10 +26,12 @@ MHLA_OK = 0
 MHLA_DTYPE_BF16, MHLA_DTYPE_FP32 = 0, 1
 MHLA_PHI_ELU1, MHLA_PHI_RELU, MHLA_PHI_EXP = 0, 1, 2
 MHLA_READOUT_NORMALIZED, MHLA_READOUT_UNNORMALIZED, MHLA_READOUT_MALA = 0, 1, 2
+MHLA_READOUT_CAUSAL_NORMALIZED, MHLA_READOUT_CAUSAL_UNNORMALIZED = 3, 4
 MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT = 0, 1, 2
 
 _READOUTS = {"normalized": MHLA_READOUT_NORMALIZED, "unnormalized": MHLA_READOUT_UNNORMALIZED,
-             "mala": MHLA_READOUT_MALA}
+             "mala": MHLA_READOUT_MALA, "causal": MHLA_READOUT_CAUSAL_NORMALIZED,
+             "causal_unnormalized": MHLA_READOUT_CAUSAL_UNNORMALIZED}
 _DTYPES = {"bf16": MHLA_DTYPE_BF16, "fp32": MHLA_DTYPE_FP32}
 _PHIS = {"elu1": MHLA_PHI_ELU1, "relu": MHLA_PHI_RELU, "exp": MHLA_PHI_EXP}
 _ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MHLA_ACCURACY_SPLIT}

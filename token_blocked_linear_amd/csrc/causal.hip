@@ -1,0 +1,422 @@
+// Chunkwise-causal MHLA readout over a 1D token sequence.
+//
+// "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head", Method -> Key
+// design 2 (the token-expanded identity q~^T S~_i = sum_t m_{i,b(t)} (q~^T K~_t) V_t^T) and Key
+// design 4 (compatible with chunkwise-parallel training and streaming inference).  The pages
+// give no causal form; the reading here masks the token-expanded sum at the token level: query
+// t sees keys t' <= t with weight m_{b(t),b(t')} (q~_t . k~_t').  For query t of block i:
+//   num_t = q~_t^T (S~<_i + m_ii (P_s + R_t)),   den_t = q~_t^T (z~<_i + m_ii (p_s + r_t))
+// with S~<_i = sum_{b<i} m_ib S_b (the mixing kernel with the strictly lower part of M_c),
+// P_s the summed partial summaries of the block's earlier token slices (an exclusive prefix
+// over slices), and R_t = sum of k~_j v_j^T over the slice's tokens j <= t.
+//
+// One workgroup (4 wave64s) per unit = (batch-head, block, token slice).  The unit's running
+// state (S~<_i + m_ii P_s, then + m_ii * each finished sub-chunk) lives in LDS as bf16 hi / lo
+// fragments -- the MFMA A operands of the readout, as in the readout kernel -- and in fp32
+// accumulators spread over the waves.  The slice is walked in sub-chunks of SUB tokens:
+//   1. stage the sub-chunk's phi(K) (row-major, and transposed scaled by m_ii) and V^T in LDS;
+//   2. every wave reads out its query tile (channels split between WQ waves): O^T = state^T q~
+//      on 16x16x32 MFMAs, plus the in-sub-chunk causal term: scores D[j][t] = phi(k_j).q~_t on
+//      16x16x32 MFMAs (keys as A rows), masked to j <= t and scaled by m_ii, which in the
+//      16x16x16 MFMA's layout are directly the B operand of V^T P (rows of the 16x16x32
+//      result = k of the 16x16x16 operand); the score sums give the in-chunk normaliser;
+//   3. the state absorbs the sub-chunk: acc += (m_ii phi(K))^T V on MFMA (permuted A rows so
+//      each lane owns 8 consecutive fragment elements), rewritten as hi / lo fragments.
+// Every product uses hi / lo bf16 operand splits (bf16 V is exact): about fp32 accuracy.
+#include <type_traits>
+
+#include "frag_lds.hpp"
+
+namespace mhla {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: A lane l = row l%16, k = 4(l/16) + 0..3; B lane l = k 4(l/16) + 0..3,
+// column l%16; D lane l = rows 4(l/16) + 0..3, column l%16 (checked on the MI355X with an
+// in-bounds probe against an integer matrix product).
+__device__ inline f32x4_t mfma16_bf16(const u32x2_t& a, const u32x2_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                   c, 0, 0, 0);
+}
+
+template <int D>
+struct CausalShape {
+  static constexpr int SUB = D >= 128 ? 32 : 64;   // tokens per sub-chunk
+  static constexpr int QT = SUB / 16;              // query tiles per sub-chunk
+  static constexpr int WQ = 4 / QT;                // waves per query tile (channel pairs split)
+  static constexpr int KP = D + 8;                 // LDS pitch of row-major phi(K) (elements)
+  static constexpr int TP = SUB + 8;               // LDS pitch of the transposed tiles
+};
+
+template <int D>
+constexpr size_t causal_lds_bytes(bool v_split) {
+  using CS = CausalShape<D>;
+  return (size_t)2 * (2 * Dims<D>::FRAG + Dims<D>::NKC * 512 + 2 * CS::SUB * CS::KP + 2 * D * CS::TP +
+                      (v_split ? 2 : 1) * D * CS::TP) +
+         (size_t)D * 4;
+}
+
+template <typename TOut>
+__device__ inline void store8_out(TOut* dst, const float (&x)[8]) {
+  if constexpr (sizeof(TOut) == 4) {
+    st16(dst, u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+    st16(dst + 4, u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+  } else {
+    st16(dst, u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                      pack_bf16x2(x[6], x[7])});
+  }
+}
+
+template <typename TIn, typename TOut, int D, int PHI>
+__global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
+  static_assert(D >= 32, "the causal readout serves head sizes 32, 64 and 128");
+  using Dm = Dims<D>;
+  using CS = CausalShape<D>;
+  constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
+  constexpr int SUB = CS::SUB, QT = CS::QT, WQ = CS::WQ, KP = CS::KP, TP = CS::TP;
+  constexpr bool VSPLIT = sizeof(TIn) == 4;     // fp32 V needs hi / lo; bf16 V is exact
+  constexpr int NFR = NKC * NCT;                 // state fragments
+  constexpr int FPW = (NFR + 3) / 4;             // fragments per wave in the state update
+  constexpr int PPW = NCT / 2 / WQ;              // channel pairs per wave in the readout
+  constexpr uint32_t ES = sizeof(TIn);
+
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* s_hi = smem;                        // state fragments (hi, lo)
+  uint16_t* s_lo = s_hi + FRAG;
+  uint16_t* s_z = s_lo + FRAG;                  // normaliser fragments
+  uint16_t* kr_hi = s_z + NKC * 512;            // phi(K) row-major [SUB][KP]
+  uint16_t* kr_lo = kr_hi + SUB * KP;
+  uint16_t* kt_hi = kr_lo + SUB * KP;           // m_ii phi(K)^T [D][TP]
+  uint16_t* kt_lo = kt_hi + D * TP;
+  uint16_t* vt_hi = kt_lo + D * TP;             // V^T [D][TP]
+  uint16_t* vt_lo = vt_hi + D * TP;             // (fp32 V only)
+  float* s_zt = reinterpret_cast<float*>(vt_lo + (VSPLIT ? D * TP : 0));   // normaliser state [D]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
+  const Geom& geo = p.g;
+
+  // unit L -> (head, block, token slice); all units of a head on one XCD when BH % 8 == 0
+  const int L = blockIdx.x;
+  const int per_head = p.splits * geo.M;
+  int bh, r;
+  if (p.xcd_map) {
+    const int xcd = L & 7, sl = L >> 3;
+    bh = (sl / per_head) * 8 + xcd;
+    r = sl % per_head;
+  } else {
+    bh = L / per_head;
+    r = L % per_head;
+  }
+  const int blk = r / p.splits, split = r % p.splits;
+  const int32_t j_begin = split * p.tok_per_split;
+  const int32_t j_end = min(j_begin + p.tok_per_split, geo.n_b);
+  const int32_t base_tok = block_base_token(geo, blk);
+  const int64_t head_off = (int64_t)bh * geo.N * D;
+  const int64_t row = (int64_t)bh * geo.M + blk;
+  const float mii = p.mc ? p.mc[(int64_t)(bh % p.H) * p.mc_head_stride + (int64_t)blk * geo.M + blk] : 1.0f;
+
+  // ---- state: S~<_i (+ m_ii * earlier slices), fp32 in the owning waves, hi / lo in LDS ----
+  f32x4_t sacc[FPW][2];
+#pragma unroll
+  for (int a = 0; a < FPW; ++a) {
+    const int fr = wave + 4 * a;
+    sacc[a][0] = sacc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (fr >= NFR) continue;
+    const int pos = (fr * 64 + lane) * 8;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (p.st_hi) {
+      const u32x4_t h = ld16(p.st_hi + row * FRAG + pos), l = ld16(p.st_lo + row * FRAG + pos);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t hw = h[e >> 1], lw = l[e >> 1];
+        x[e] = ((e & 1) ? bf16hi_to_f32(hw) : bf16lo_to_f32(hw)) + ((e & 1) ? bf16hi_to_f32(lw) : bf16lo_to_f32(lw));
+      }
+    }
+    if (p.pre) {
+      const float* pp = p.pre + (row * p.splits + split) * FRAG + pos;
+      const u32x4_t w0 = ld16(pp), w1 = ld16(pp + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = fmaf(mii, __uint_as_float(w0[e]), x[e]);
+        x[4 + e] = fmaf(mii, __uint_as_float(w1[e]), x[4 + e]);
+      }
+    }
+    sacc[a][0] = f32x4_t{x[0], x[1], x[2], x[3]};
+    sacc[a][1] = f32x4_t{x[4], x[5], x[6], x[7]};
+    store_frag8<true>(s_hi, s_lo, lds_pos<NCT>(pos), x);
+  }
+  if (tid < D) {
+    float zz = p.zt ? p.zt[row * D + tid] : 0.f;
+    if (p.prez) zz = fmaf(mii, p.prez[(row * p.splits + split) * D + tid], zz);
+    s_zt[tid] = zz;
+  }
+  __syncthreads();
+  build_zfrag<D>(s_zt, s_z, tid);
+
+  const AOffsets ao = a_offsets(lane);
+  const int qt = wave % QT, cp = wave / QT;
+  const Rsrc rq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + head_off, (uint32_t)geo.N * D * ES);
+  const Rsrc rk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + head_off, (uint32_t)geo.N * D * ES);
+  const Rsrc rv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + head_off, (uint32_t)geo.N * D * ES);
+
+  for (int32_t j0 = j_begin; j0 < j_end; j0 += SUB) {
+    // ---- this wave's query tile: loads first ----
+    const int32_t jq = j0 + 16 * qt + pr;
+    const bool qvalid = jq < j_end;
+    const uint32_t qrel = qvalid ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)jq)) * D : 0u;
+    In8<TIn> cq[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+      cq[kc].template load_buf<0>(rq, qvalid ? (qrel + 32 * kc + 8 * lg) * ES : kOutOfRange);
+
+    // ---- stage the sub-chunk: 8 tokens x 8 features per thread ----
+    constexpr int NB = (SUB / 8) * (D / 8);
+    if (tid < NB) {
+      const int tb = tid / (D / 8), fb = tid % (D / 8);
+      In8<TIn> rk8[8], rv8[8];
+      bool kv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int32_t j = j0 + 8 * tb + i;
+        kv[i] = j < j_end;
+        const uint32_t t = kv[i] ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)j)) : 0u;
+        const uint32_t off = kv[i] ? (t * D + 8 * fb) * ES : kOutOfRange;
+        rk8[i].template load_buf<0>(rk, off);
+        rv8[i].template load_buf<0>(rv, off);
+      }
+      float kf[8][8];                           // [token][feature]; tokens past the end: 0
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[i][e] = kv[i] ? phi_map<PHI>(rk8[i].get(e)) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) store_frag8<true>(kr_hi, kr_lo, (8 * tb + i) * KP + 8 * fb, kf[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float col[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) col[i] = mii * kf[i][e];
+        store_frag8<true>(kt_hi, kt_lo, (8 * fb + e) * TP + 8 * tb, col);
+        if constexpr (VSPLIT) {
+          float vc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vc[i] = rv8[i].get(e);
+          store_frag8<true>(vt_hi, vt_lo, (8 * fb + e) * TP + 8 * tb, vc);
+        } else {
+          u32x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = rv8[2 * i].bits(e) | (rv8[2 * i + 1].bits(e) << 16);   // exact
+          st16(vt_hi + (8 * fb + e) * TP + 8 * tb, w);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- readout of query tile qt, channel pairs [cp * PPW, (cp + 1) * PPW) ----
+    u32x4_t bq_hi[NKC], bq_lo[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h, l;
+        split_bf16x2(phi_map<PHI>(cq[kc].get(2 * i)), phi_map<PHI>(cq[kc].get(2 * i + 1)), h, l);
+        bq_hi[kc][i] = h;
+        bq_lo[kc][i] = l;
+      }
+    f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[2 * PPW];
+#pragma unroll
+    for (int t = 0; t < 2 * PPW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const u32x4_t az = *reinterpret_cast<const u32x4_t*>(s_z + (kc * 64 + lane) * 8);
+      accz = mfma_bf16(az, bq_hi[kc], accz);
+      accz = mfma_bf16(az, bq_lo[kc], accz);
+      u32x4_t ah[2 * PPW], al[2 * PPW];
+#pragma unroll
+      for (int t = 0; t < 2 * PPW; ++t) {
+        const int ct = 2 * cp * PPW + t;
+        const int off = (kc * NCT + (ct & ~1)) * 512 + ((ct & 1) ? ao.odd : ao.even);
+        ah[t] = *reinterpret_cast<const u32x4_t*>(s_hi + off);
+        al[t] = *reinterpret_cast<const u32x4_t*>(s_lo + off);
+      }
+#pragma unroll
+      for (int t = 0; t < 2 * PPW; ++t) acc[t] = mfma_bf16(ah[t], bq_hi[kc], acc[t]);
+#pragma unroll
+      for (int t = 0; t < 2 * PPW; ++t) acc[t] = mfma_bf16(al[t], bq_hi[kc], acc[t]);
+#pragma unroll
+      for (int t = 0; t < 2 * PPW; ++t) acc[t] = mfma_bf16(ah[t], bq_lo[kc], acc[t]);
+    }
+    // in-sub-chunk causal term over key tiles 0 .. qt
+    float dsum = 0.f;
+    for (int kt = 0; kt <= qt; ++kt) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int off = (16 * kt + pr) * KP + 32 * kc + 8 * lg;
+        const u32x4_t kh = *reinterpret_cast<const u32x4_t*>(kr_hi + off);
+        const u32x4_t kl = *reinterpret_cast<const u32x4_t*>(kr_lo + off);
+        sc = mfma_bf16(kh, bq_hi[kc], sc);
+        sc = mfma_bf16(kl, bq_hi[kc], sc);
+        sc = mfma_bf16(kh, bq_lo[kc], sc);
+      }
+      // lane: keys 16kt + 4lg + r, query 16qt + pr (positions within the sub-chunk)
+      float pv[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        pv[rr] = (16 * kt + 4 * lg + rr <= 16 * qt + pr) ? mii * sc[rr] : 0.f;
+        dsum += pv[rr];
+      }
+      u32x2_t ph, pl;
+      {
+        uint32_t h0, l0, h1, l1;
+        split_bf16x2(pv[0], pv[1], h0, l0);
+        split_bf16x2(pv[2], pv[3], h1, l1);
+        ph = u32x2_t{h0, h1};
+        pl = u32x2_t{l0, l1};
+      }
+#pragma unroll
+      for (int t = 0; t < 2 * PPW; ++t) {
+        const int ct = 2 * cp * PPW + t;
+        // A row pr of tile ct is channel 32 (ct / 2) + 8 (pr / 4) + 4 (ct % 2) + pr % 4, so that
+        // lane (t, g) ends with channels 8g .. 8g+7 of its pair, as in the state product
+        const int c = 32 * (ct >> 1) + 8 * (pr >> 2) + 4 * (ct & 1) + (pr & 3);
+        const int off = c * TP + 16 * kt + 4 * lg;
+        const u32x2_t vh = *reinterpret_cast<const u32x2_t*>(vt_hi + off);
+        acc[t] = mfma16_bf16(vh, ph, acc[t]);
+        acc[t] = mfma16_bf16(vh, pl, acc[t]);
+        if constexpr (VSPLIT) {
+          const u32x2_t vl = *reinterpret_cast<const u32x2_t*>(vt_lo + off);
+          acc[t] = mfma16_bf16(vl, ph, acc[t]);
+        }
+      }
+    }
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    if (qvalid) {
+      const float den = accz[0] + accz[1] + dsum;
+      const float scale = p.normalized ? 1.0f / den : 1.0f;
+#pragma unroll
+      for (int pp = 0; pp < PPW; ++pp) {
+        float o[8];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          o[rr] = acc[2 * pp][rr] * scale;
+          o[4 + rr] = acc[2 * pp + 1][rr] * scale;
+        }
+        const int c0 = 32 * (cp * PPW + pp) + 8 * lg;
+        store8_out(reinterpret_cast<TOut*>(p.o) + head_off + qrel + c0, o);
+      }
+    }
+    __syncthreads();   // the readout is done with the state fragments and the staged tiles
+
+    // ---- the state absorbs the sub-chunk: sacc += (m_ii phi(K))^T V ----
+#pragma unroll
+    for (int a = 0; a < FPW; ++a) {
+      const int fr = wave + 4 * a;
+      if (fr >= NFR) continue;
+      const int kc = fr / NCT, ct = fr % NCT;
+#pragma unroll
+      for (int ks = 0; ks < SUB / 32; ++ks) {
+        const int cb = (16 * ct + pr) * TP + 32 * ks + 8 * lg;
+        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(vt_hi + cb);
+        u32x4_t bl;
+        if constexpr (VSPLIT) bl = *reinterpret_cast<const u32x4_t*>(vt_lo + cb);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int f = 32 * kc + 8 * (pr >> 2) + 4 * rt + (pr & 3);
+          const int ka = f * TP + 32 * ks + 8 * lg;
+          const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(kt_hi + ka);
+          const u32x4_t al = *reinterpret_cast<const u32x4_t*>(kt_lo + ka);
+          sacc[a][rt] = mfma_bf16(ah, bh, sacc[a][rt]);
+          sacc[a][rt] = mfma_bf16(al, bh, sacc[a][rt]);
+          if constexpr (VSPLIT) sacc[a][rt] = mfma_bf16(ah, bl, sacc[a][rt]);
+        }
+      }
+      const float x[8] = {sacc[a][0][0], sacc[a][0][1], sacc[a][0][2], sacc[a][0][3],
+                          sacc[a][1][0], sacc[a][1][1], sacc[a][1][2], sacc[a][1][3]};
+      store_frag8<true>(s_hi, s_lo, lds_pos<NCT>((fr * 64 + lane) * 8), x);
+    }
+    if (tid < D) {   // normaliser state: + sum over the sub-chunk of m_ii phi(k)
+      float zs = 0.f;
+#pragma unroll
+      for (int j = 0; j < SUB; j += 8) {
+        const u32x4_t h = *reinterpret_cast<const u32x4_t*>(kt_hi + tid * TP + j);
+        const u32x4_t l = *reinterpret_cast<const u32x4_t*>(kt_lo + tid * TP + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          zs += (bf16lo_to_f32(h[i]) + bf16lo_to_f32(l[i])) + (bf16hi_to_f32(h[i]) + bf16hi_to_f32(l[i]));
+      }
+      s_zt[tid] += zs;
+    }
+    __syncthreads();
+    build_zfrag<D>(s_zt, s_z, tid);
+    __syncthreads();
+  }
+}
+
+// Exclusive prefix over the token slices of each block, in place:
+// part[row][s] <- sum_{s' < s} part[row][s'] for the FRAG summary positions and the D normaliser
+// entries; fixed order.
+__global__ __launch_bounds__(kThreads) void slice_prefix_kernel(float* ps, float* pz, int64_t rows, int splits,
+                                                                int frag, int d) {
+  const int64_t per_row = (int64_t)frag + d;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * per_row) return;
+  const int64_t rw = idx / per_row, pos = idx % per_row;
+  float run = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    float* x = pos < frag ? ps + (rw * splits + s) * frag + pos : pz + (rw * splits + s) * d + (pos - frag);
+    const float v = *x;
+    *x = run;
+    run += v;
+  }
+}
+
+template <int PHI, typename TIn, typename TOut, int D>
+static hipError_t launch_causal_t(const CausalParams& p, int n_units, hipStream_t s) {
+  auto kern = causal_kernel<TIn, TOut, D, PHI>;
+  const size_t lds = causal_lds_bytes<D>(sizeof(TIn) == 4);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(n_units), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int PHI, typename TIn, typename TOut>
+static hipError_t causal_dispatch_d(const CausalParams& p, int d, int n, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_causal_t<PHI, TIn, TOut, 32>(p, n, s);
+    case 64: return launch_causal_t<PHI, TIn, TOut, 64>(p, n, s);
+    case 128: return launch_causal_t<PHI, TIn, TOut, 128>(p, n, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// n_units = splits * M * BH.
+hipError_t launch_causal(const CausalParams& p, int d, bool in_fp32, bool out_fp32, int phi, int n_units,
+                         hipStream_t stream) {
+  auto go = [&](auto phi_c) {
+    constexpr int PHI = decltype(phi_c)::value;
+    if (in_fp32)
+      return out_fp32 ? causal_dispatch_d<PHI, float, float>(p, d, n_units, stream)
+                      : causal_dispatch_d<PHI, float, uint16_t>(p, d, n_units, stream);
+    return out_fp32 ? causal_dispatch_d<PHI, uint16_t, float>(p, d, n_units, stream)
+                    : causal_dispatch_d<PHI, uint16_t, uint16_t>(p, d, n_units, stream);
+  };
+  switch (phi) {
+    case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
+    case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
+    case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_slice_prefix(float* ps, float* pz, int64_t rows, int splits, int frag, int d, hipStream_t stream) {
+  const int64_t n = rows * ((int64_t)frag + d);
+  hipLaunchKernelGGL(slice_prefix_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     ps, pz, rows, splits, frag, d);
+  return hipGetLastError();
+}
+
+}  // namespace mhla

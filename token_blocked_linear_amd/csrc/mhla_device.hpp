@@ -97,6 +97,7 @@ struct SummaryParams {
   uint16_t* mcf;
   uint16_t* mcf_lo;        // non-null: also the low parts (M_c = hi + lo, for the split mixing)
   int32_t mcf_transposed;  // 1: fragments of M_c^T (the backward's mixing)
+  int32_t mcf_causal;      // 1: only the strictly lower part of M_c (entries b >= i are zero)
   int32_t mcf_heads, mcf_nitp, mcf_nbc;
   // Per-token weights (the backward's summary): phi(K_j) scaled by kscale[j], the normaliser
   // product weighted by zw[j]; [BH][N] fp32 each.
@@ -140,6 +141,7 @@ struct MixParams {
   int32_t N;
   int32_t zsplits;         // token slices per block of pz
   int32_t mc_transposed;   // 1: mix with M_c^T (the backward's dS_b = sum_i m_ib dS~_i)
+  int32_t causal;          // 1: weights m_ib with b >= i are taken as zero
 };
 
 // Backward pass (chain rule of the forward steps; see csrc/bwd.hip).
@@ -181,6 +183,30 @@ struct DmcParams {
   int32_t H, per_head, group_bh;           // group_bh: (batch, head) pairs per group
   int32_t steps_per_bh;                    // ceil((FRAG + D) / 64)
   int32_t nchunks, steps_per_chunk;
+};
+
+// Chunkwise-causal readout of a 1D sequence: query t of block i sees the earlier blocks through
+// S~<_i = sum_{b<i} m_ib S_b (the mixing kernel with the strictly lower part of M_c), the earlier
+// token slices of its own block through their summed partials, and its own slice causally.
+struct CausalParams {
+  const void* q;           // [BH][N][D] input type
+  const void* k;
+  const void* v;
+  void* o;                 // [BH][N][D] output type
+  const uint16_t* st_hi;   // S~<_i fragments (hi, lo) [BH][M][FRAG]; NULL when M == 1
+  const uint16_t* st_lo;
+  const float* zt;         // z~<_i [BH][M][D]; NULL when M == 1
+  const float* pre;        // exclusive prefix over token slices of the block's partial summaries
+  const float* prez;       //   [BH][M][splits][FRAG] and [..][D]; NULL with one slice per block
+  const float* mc;         // M_c (for m_ii); NULL when M == 1
+  int64_t mc_head_stride;
+  int32_t H;
+  Geom g;
+  int32_t splits;          // token slices per block
+  int32_t tok_per_split;
+  int32_t BH;
+  int32_t xcd_map;
+  int32_t normalized;
 };
 
 // MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,

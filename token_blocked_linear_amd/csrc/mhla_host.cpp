@@ -25,11 +25,14 @@ hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_
 hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
                             bool key_side, int n_units, hipStream_t stream);
 hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream);
+hipError_t launch_causal(const CausalParams& p, int d, bool in_fp32, bool out_fp32, int phi, int n_units,
+                         hipStream_t stream);
+hipError_t launch_slice_prefix(float* ps, float* pz, int64_t rows, int splits, int frag, int d, hipStream_t stream);
 }  // namespace mhla
 
 namespace {
 
-constexpr int kMaxKernels = 3;
+constexpr int kMaxKernels = 4;
 
 // Mixing step placement: a separate kernel, or the readout's prologue (few blocks).
 enum { kFuseNone = 0, kFuseBf16 = 1, kFusePartials = 2 };
@@ -64,6 +67,8 @@ struct mhla_plan {
   bool in_fp32, out_fp32, mala, split, split_v;
   bool mix_mfma;   // bf16 summary stack (mixed on MFMA or in the readout prologue)
   bool mix_split;  // mixing kernel on MFMA with split operands over fp32 partials
+  bool causal;     // chunkwise-causal readout (1D)
+  bool mix_kernel; // a mixing kernel of its own is launched
   int fuse;        // kFuse*: where the mixing step runs
   int n_kernels;
   const char* kernel_names[kMaxKernels];
@@ -122,7 +127,8 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   if (d->out_dtype != MHLA_DTYPE_BF16 && d->out_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
   if (d->phi != MHLA_PHI_ELU1 && d->phi != MHLA_PHI_RELU && d->phi != MHLA_PHI_EXP)
     return MHLA_ERR_UNSUPPORTED;
-  if (d->readout < MHLA_READOUT_NORMALIZED || d->readout > MHLA_READOUT_MALA) return MHLA_ERR_UNSUPPORTED;
+  if (d->readout < MHLA_READOUT_NORMALIZED || d->readout > MHLA_READOUT_CAUSAL_UNNORMALIZED)
+    return MHLA_ERR_UNSUPPORTED;
   if (d->accuracy < MHLA_ACCURACY_AUTO || d->accuracy > MHLA_ACCURACY_SPLIT) return MHLA_ERR_UNSUPPORTED;
   if (d->mc_per_head != 0 && d->mc_per_head != 1) return MHLA_ERR_INVALID_ARG;
   if (!(d->head_dim == 16 || d->head_dim == 32 || d->head_dim == 64 || d->head_dim == 128))
@@ -146,6 +152,8 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   const int64_t BH = d->batch * d->heads;
   if (BH > 65535 || M > 65535) return MHLA_ERR_SHAPE;
   if (d->readout == MHLA_READOUT_MALA && M != 1) return MHLA_ERR_UNSUPPORTED;
+  const bool causal = d->readout == MHLA_READOUT_CAUSAL_NORMALIZED || d->readout == MHLA_READOUT_CAUSAL_UNNORMALIZED;
+  if (causal && (d->ndim != 1 || d->head_dim < 32)) return MHLA_ERR_UNSUPPORTED;   // 1D sequences, d >= 32
   // element offsets are 64-bit; guard the total size against overflow
   if (BH > ((int64_t)1 << 62) / (N * d->head_dim * 4)) return MHLA_ERR_SHAPE;
   // the kernels address one head of Q, K, V (and one head's summary stack) through buffer
@@ -177,8 +185,11 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   P->in_fp32 = d->in_dtype == MHLA_DTYPE_FP32;
   P->out_fp32 = d->out_dtype == MHLA_DTYPE_FP32;
   P->mala = d->readout == MHLA_READOUT_MALA;
+  P->causal = causal;
   P->mode = d->readout;
-  if (d->accuracy == MHLA_ACCURACY_SPLIT)
+  if (causal)
+    P->split = true;   // the causal readout always runs on split operands
+  else if (d->accuracy == MHLA_ACCURACY_SPLIT)
     P->split = true;
   else if (d->accuracy == MHLA_ACCURACY_BF16)
     P->split = false;
@@ -213,6 +224,14 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
     P->rd_splits = (int32_t)s;
     P->rd_tok = (int32_t)tok;
   }
+  if (causal) {   // the summary's token slices are the causal readout's units
+    int64_t s = (nb + 255) / 256;
+    int64_t tok = (nb + s - 1) / s;
+    tok = (tok + 31) / 32 * 32;
+    s = (nb + tok - 1) / tok;
+    P->sum_splits = P->rd_splits = (int32_t)s;
+    P->sum_tok = P->rd_tok = (int32_t)tok;
+  }
 
   // Summary output: a bf16 stack when one token slice covers a block with bf16 operands (the
   // bf16 accuracy level); otherwise fp32 partials per token slice.
@@ -221,14 +240,21 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   // kernel of its own: MFMA over the bf16 stack, MFMA with split operands over fp32 partials
   // (M <= 256), VALU over fp32 partials beyond.
   if (P->mala) P->fuse = kFusePartials;
-  else if (M <= kFuseMaxBlocks) P->fuse = P->mix_mfma ? kFuseBf16 : kFusePartials;
+  else if (M <= kFuseMaxBlocks && !causal) P->fuse = P->mix_mfma ? kFuseBf16 : kFusePartials;
   else P->fuse = kFuseNone;
-  const bool mix_kernel = P->fuse == kFuseNone;
+  // causal: a mixing kernel (strictly lower M_c) unless there is one block
+  const bool mix_kernel = P->fuse == kFuseNone && !(causal && M == 1);
   P->mix_split = mix_kernel && !P->mix_mfma && M <= 256;
+  P->mix_kernel = mix_kernel;
   P->n_kernels = 0;
   P->kernel_names[P->n_kernels++] = "summary";
   if (mix_kernel) P->kernel_names[P->n_kernels++] = "mix";
-  P->kernel_names[P->n_kernels++] = mix_kernel ? "readout" : "mix+readout";
+  if (causal) {
+    if (P->sum_splits > 1) P->kernel_names[P->n_kernels++] = "scan";
+    P->kernel_names[P->n_kernels++] = "causal";
+  } else {
+    P->kernel_names[P->n_kernels++] = mix_kernel ? "readout" : "mix+readout";
+  }
 
   // Workspace layout.
   const size_t f = (size_t)P->frag, dd = (size_t)P->d;
@@ -329,7 +355,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     if (h->timing && !timer_begin(h->fwd_timer, s, tl)) return MHLA_ERR_HIP;
     auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[++ev_i], s) == hipSuccess; };
 
-    const bool mix_kernel = h->fuse == kFuseNone;
+    const bool mix_kernel = h->mix_kernel;
     const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
 
     mhla::SummaryParams sp = {};
@@ -347,6 +373,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.mcf = (mix_kernel && (h->mix_mfma || h->mix_split)) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
     sp.mcf_lo = h->mix_split ? reinterpret_cast<uint16_t*>(ws + h->off_mcf_lo) : nullptr;
     sp.mcf_transposed = 0;
+    sp.mcf_causal = h->causal ? 1 : 0;
     sp.mcf_heads = h->mcf_heads;
     sp.mcf_nitp = h->mix.nitp;
     sp.mcf_nbc = h->mix.nbc;
@@ -389,9 +416,41 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
         mp.N = (int32_t)h->N;
         mp.zsplits = h->sum_splits;
         mp.mc_transposed = 0;
+        mp.causal = h->causal ? 1 : 0;
         e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->split, s);
       }
       if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+    }
+
+    if (h->causal) {
+      const int64_t rows = h->BH * h->M;
+      if (h->sum_splits > 1) {   // partials -> exclusive prefix over the block's token slices
+        e = mhla::launch_slice_prefix(ps, pz, rows, h->sum_splits, h->frag, h->d, s);
+        if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+      }
+      mhla::CausalParams cp = {};
+      cp.q = q;
+      cp.k = k;
+      cp.v = v;
+      cp.o = o;
+      cp.st_hi = mix_kernel ? st_hi : nullptr;
+      cp.st_lo = mix_kernel ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo) : nullptr;
+      cp.zt = mix_kernel ? zt : nullptr;
+      cp.pre = h->sum_splits > 1 ? ps : nullptr;
+      cp.prez = h->sum_splits > 1 ? pz : nullptr;
+      cp.mc = mc;
+      cp.mc_head_stride = mc_stride;
+      cp.H = (int32_t)h->H;
+      cp.g = h->geom;
+      cp.splits = h->rd_splits;
+      cp.tok_per_split = h->rd_tok;
+      cp.BH = (int32_t)h->BH;
+      cp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
+      cp.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
+      e = mhla::launch_causal(cp, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
+                              (int)(h->rd_splits * h->M * h->BH), s);
+      if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+      return MHLA_OK;
     }
 
     mhla::ReadoutParams rp;
@@ -481,7 +540,7 @@ BwdLayout bwd_layout(const mhla_plan* h) {
 }
 
 mhla_status bwd_supported(const mhla_plan* h) {
-  if (h->mala) return MHLA_ERR_UNSUPPORTED;     // the MALA readout has no backward here
+  if (h->mala || h->causal) return MHLA_ERR_UNSUPPORTED;   // no MALA or causal backward here
   if (h->d < 32) return MHLA_ERR_UNSUPPORTED;   // head sizes 32, 64, 128
   return MHLA_OK;
 }

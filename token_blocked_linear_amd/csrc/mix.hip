@@ -58,7 +58,8 @@ __global__ __launch_bounds__(kThreads) void mix_kernel(MixParams p, int frag, in
     }
 #pragma unroll
     for (int r = 0; r < kMixRows; ++r)
-      if (r < nrows) acc[r] = fmaf(mc ? mc[(int64_t)(i0 + r) * si + b * sb] : 1.0f, s, acc[r]);
+      if (r < nrows && !(p.causal && b >= i0 + r))
+        acc[r] = fmaf(mc ? mc[(int64_t)(i0 + r) * si + b * sb] : 1.0f, s, acc[r]);
   }
 #pragma unroll
   for (int r = 0; r < kMixRows; ++r) {

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int b = 32 * bc + 8 * (l >> 4) + e;
-        m[e] = (i < M && b < M) ? (mch ? mch[i * si + b * sb] : 1.0f) : 0.f;   // NULL M_c (M == 1): [1]
+        m[e] = (i < M && b < M && !(p.mcf_causal && b >= i)) ? (mch ? mch[i * si + b * sb] : 1.0f)
+                                                               : 0.f;   // NULL M_c (M == 1): [1]
       }
       u32x4_t hi, lo;
 #pragma unroll
