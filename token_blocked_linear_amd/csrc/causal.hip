@@ -10,7 +10,7 @@
 // P_s the summed partial summaries of the block's earlier token slices (an exclusive prefix
 // over slices), and R_t = sum of k~_j v_j^T over the slice's tokens j <= t.
 //
-// One workgroup (4 wave64s) per unit = (batch-head, block, token slice).  The unit's running
+// One workgroup (4 wave64s, 8 at d = 128) per unit = (batch-head, block, token slice).  The unit's running
 // state (S~<_i + m_ii P_s, then + m_ii * each finished sub-chunk) lives in LDS as bf16 hi / lo
 // fragments -- the MFMA A operands of the readout, as in the readout kernel -- and in fp32
 // accumulators spread over the waves.  The slice is walked in sub-chunks of SUB tokens:
@@ -41,9 +41,11 @@ __device__ inline f32x4_t mfma16_bf16(const u32x2_t& a, const u32x2_t& b, f32x4_
 
 template <int D>
 struct CausalShape {
+  static constexpr int NW = D >= 128 ? 8 : 4;      // waves per workgroup
+  static constexpr int NT = 64 * NW;               // threads per workgroup
   static constexpr int SUB = D >= 128 ? 32 : 64;   // tokens per sub-chunk
   static constexpr int QT = SUB / 16;              // query tiles per sub-chunk
-  static constexpr int WQ = 4 / QT;                // waves per query tile (channel pairs split)
+  static constexpr int WQ = NW / QT;               // waves per query tile (channel pairs split)
   static constexpr int KP = D + 8;                 // LDS pitch of row-major phi(K) (elements)
   static constexpr int TP = SUB + 8;               // LDS pitch of the transposed tiles
 };
@@ -52,8 +54,7 @@ template <int D>
 constexpr size_t causal_lds_bytes(bool v_split) {
   using CS = CausalShape<D>;
   return (size_t)2 * (2 * Dims<D>::FRAG + Dims<D>::NKC * 512 + 2 * CS::SUB * CS::KP + 2 * D * CS::TP +
-                      (v_split ? 2 : 1) * D * CS::TP) +
-         (size_t)D * 4;
+                      (v_split ? 2 : 1) * D * CS::TP);
 }
 
 template <typename TOut>
@@ -68,15 +69,18 @@ __device__ inline void store8_out(TOut* dst, const float (&x)[8]) {
 }
 
 template <typename TIn, typename TOut, int D, int PHI>
-__global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
+__global__ __launch_bounds__(CausalShape<D>::NT) void causal_kernel(CausalParams p) {
   static_assert(D >= 32, "the causal readout serves head sizes 32, 64 and 128");
   using Dm = Dims<D>;
   using CS = CausalShape<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
-  constexpr int SUB = CS::SUB, QT = CS::QT, WQ = CS::WQ, KP = CS::KP, TP = CS::TP;
+  constexpr int SUB = CS::SUB, QT = CS::QT, WQ = CS::WQ, KP = CS::KP, TP = CS::TP, NW = CS::NW;
   constexpr bool VSPLIT = sizeof(TIn) == 4;     // fp32 V needs hi / lo; bf16 V is exact
   constexpr int NFR = NKC * NCT;                 // state fragments
-  constexpr int FPW = (NFR + 3) / 4;             // fragments per wave in the state update
+  // State fragments by wave: WPK waves share a 32-feature chunk kc = wave / WPK, each owning
+  // FPW consecutive channel tiles, so a wave reads its phi(K)^T rows once for all of them.
+  constexpr int WPK = NW / NKC;                  // waves per feature chunk
+  constexpr int FPW = NCT / WPK > 0 ? NCT / WPK : 1;   // fragments (channel tiles) per wave
   constexpr int PPW = NCT / 2 / WQ;              // channel pairs per wave in the readout
   constexpr uint32_t ES = sizeof(TIn);
 
@@ -90,7 +94,6 @@ __global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
   uint16_t* kt_lo = kt_hi + D * TP;
   uint16_t* vt_hi = kt_lo + D * TP;             // V^T [D][TP]
   uint16_t* vt_lo = vt_hi + D * TP;             // (fp32 V only)
-  float* s_zt = reinterpret_cast<float*>(vt_lo + (VSPLIT ? D * TP : 0));   // normaliser state [D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
   const Geom& geo = p.g;
@@ -116,12 +119,14 @@ __global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
   const float mii = p.mc ? p.mc[(int64_t)(bh % p.H) * p.mc_head_stride + (int64_t)blk * geo.M + blk] : 1.0f;
 
   // ---- state: S~<_i (+ m_ii * earlier slices), fp32 in the owning waves, hi / lo in LDS ----
+  const int my_kc = wave / WPK, my_ct0 = (wave % WPK) * FPW;
+  const bool updater = my_ct0 < NCT;             // d = 32: two of the four waves
   f32x4_t sacc[FPW][2];
 #pragma unroll
   for (int a = 0; a < FPW; ++a) {
-    const int fr = wave + 4 * a;
+    const int fr = my_kc * NCT + my_ct0 + a;
     sacc[a][0] = sacc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (fr >= NFR) continue;
+    if (!updater) continue;
     const int pos = (fr * 64 + lane) * 8;
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (p.st_hi) {
@@ -145,13 +150,39 @@ __global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
     sacc[a][1] = f32x4_t{x[4], x[5], x[6], x[7]};
     store_frag8<true>(s_hi, s_lo, lds_pos<NCT>(pos), x);
   }
-  if (tid < D) {
-    float zz = p.zt ? p.zt[row * D + tid] : 0.f;
-    if (p.prez) zz = fmaf(mii, p.prez[(row * p.splits + split) * D + tid], zz);
-    s_zt[tid] = zz;
+  // Normaliser state: wave kc (< NKC) holds z[32kc + 8lg + e] in zacc[e / 4][e % 4] on every lane
+  // (the layout of a 16x16x32 result against an all-ones B operand), and writes the normaliser
+  // fragment: lane (row 4g + 0) = hi(z), (row 4g + 1) = lo(z), other rows zero.
+  const bool zwave = wave % WPK == 0;            // one wave per feature chunk keeps z
+  f32x4_t zacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  auto write_zfrag = [&]() {
+    float z8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z8[e] = zacc[e >> 2][e & 3];
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if ((pr & 3) < 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h, l;
+        split_bf16x2(z8[2 * i], z8[2 * i + 1], h, l);
+        w[i] = (pr & 3) == 0 ? h : l;
+      }
+    }
+    st16(s_z + (my_kc * 64 + lane) * 8, w);
+  };
+  if (zwave) {
+    const int f0 = 32 * my_kc + 8 * lg;
+    float z8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float zz = p.zt ? p.zt[row * D + f0 + e] : 0.f;
+      if (p.prez) zz = fmaf(mii, p.prez[(row * p.splits + split) * D + f0 + e], zz);
+      z8[e] = zz;
+    }
+    zacc[0] = f32x4_t{z8[0], z8[1], z8[2], z8[3]};
+    zacc[1] = f32x4_t{z8[4], z8[5], z8[6], z8[7]};
+    write_zfrag();
   }
-  __syncthreads();
-  build_zfrag<D>(s_zt, s_z, tid);
 
   const AOffsets ao = a_offsets(lane);
   const int qt = wave % QT, cp = wave / QT;
@@ -159,60 +190,69 @@ __global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
   const Rsrc rk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + head_off, (uint32_t)geo.N * D * ES);
 
-  for (int32_t j0 = j_begin; j0 < j_end; j0 += SUB) {
-    // ---- this wave's query tile: loads first ----
+  // Staging role: 2 consecutive tokens x 8 features (lanes run over the token pairs, so the
+  // transposed 4-byte LDS writes of a wave fill consecutive words of one row).
+  constexpr int FG = D / 8, NPAIR = SUB / 2;
+  const int tp = tid % NPAIR, fg = tid / NPAIR;
+  const bool stager = fg < FG;
+  In8<TIn> ck[2], cv[2];     // the sub-chunk's K and V rows of this thread (prefetched)
+  In8<TIn> cq[NKC];          // the wave's query features (prefetched)
+  auto issue_kv = [&](int32_t j0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int32_t j = j0 + 2 * tp + i;
+      const bool ok = stager && j < j_end;
+      const uint32_t t = ok ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)j)) : 0u;
+      const uint32_t off = ok ? (t * D + 8 * fg) * ES : kOutOfRange;
+      ck[i].template load_buf<0>(rk, off);
+      cv[i].template load_buf<0>(rv, off);
+    }
+  };
+  auto issue_q = [&](In8<TIn> (&dst)[NKC], int32_t j0) {
     const int32_t jq = j0 + 16 * qt + pr;
-    const bool qvalid = jq < j_end;
-    const uint32_t qrel = qvalid ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)jq)) * D : 0u;
-    In8<TIn> cq[NKC];
+    const bool ok = jq < j_end;
+    const uint32_t rel = ok ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)jq)) * D : 0u;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc)
-      cq[kc].template load_buf<0>(rq, qvalid ? (qrel + 32 * kc + 8 * lg) * ES : kOutOfRange);
+    for (int kc = 0; kc < NKC; ++kc) dst[kc].template load_buf<0>(rq, ok ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange);
+  };
+  issue_kv(j_begin);
+  issue_q(cq, j_begin);
+  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
-    // ---- stage the sub-chunk: 8 tokens x 8 features per thread ----
-    constexpr int NB = (SUB / 8) * (D / 8);
-    if (tid < NB) {
-      const int tb = tid / (D / 8), fb = tid % (D / 8);
-      In8<TIn> rk8[8], rv8[8];
-      bool kv[8];
+  for (int32_t j0 = j_begin; j0 < j_end; j0 += SUB) {
+    // ---- stage the sub-chunk from the prefetched registers, then prefetch the next one ----
+    if (stager) {
+      float kf[2][8];                         // [token][feature]; tokens past the end: 0
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int32_t j = j0 + 8 * tb + i;
-        kv[i] = j < j_end;
-        const uint32_t t = kv[i] ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)j)) : 0u;
-        const uint32_t off = kv[i] ? (t * D + 8 * fb) * ES : kOutOfRange;
-        rk8[i].template load_buf<0>(rk, off);
-        rv8[i].template load_buf<0>(rv, off);
+      for (int i = 0; i < 2; ++i) {
+        const bool ok = j0 + 2 * tp + i < j_end;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[i][e] = ok ? phi_map<PHI>(ck[i].get(e)) : 0.f;
+        store_frag8<true>(kr_hi, kr_lo, (2 * tp + i) * KP + 8 * fg, kf[i]);
       }
-      float kf[8][8];                           // [token][feature]; tokens past the end: 0
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kf[i][e] = kv[i] ? phi_map<PHI>(rk8[i].get(e)) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) store_frag8<true>(kr_hi, kr_lo, (8 * tb + i) * KP + 8 * fb, kf[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float col[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) col[i] = mii * kf[i][e];
-        store_frag8<true>(kt_hi, kt_lo, (8 * fb + e) * TP + 8 * tb, col);
+        const int at = (8 * fg + e) * TP + 2 * tp;
+        uint32_t h, l;
+        split_bf16x2(mii * kf[0][e], mii * kf[1][e], h, l);
+        *reinterpret_cast<uint32_t*>(kt_hi + at) = h;
+        *reinterpret_cast<uint32_t*>(kt_lo + at) = l;
         if constexpr (VSPLIT) {
-          float vc[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) vc[i] = rv8[i].get(e);
-          store_frag8<true>(vt_hi, vt_lo, (8 * fb + e) * TP + 8 * tb, vc);
+          split_bf16x2(cv[0].get(e), cv[1].get(e), h, l);
+          *reinterpret_cast<uint32_t*>(vt_hi + at) = h;
+          *reinterpret_cast<uint32_t*>(vt_lo + at) = l;
         } else {
-          u32x4_t w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = rv8[2 * i].bits(e) | (rv8[2 * i + 1].bits(e) << 16);   // exact
-          st16(vt_hi + (8 * fb + e) * TP + 8 * tb, w);
+          *reinterpret_cast<uint32_t*>(vt_hi + at) = cv[0].bits(e) | (cv[1].bits(e) << 16);   // exact
         }
       }
     }
+    issue_kv(j0 + SUB);                        // past the end: out-of-range loads read zero
     __syncthreads();
 
     // ---- readout of query tile qt, channel pairs [cp * PPW, (cp + 1) * PPW) ----
+    const int32_t jq = j0 + 16 * qt + pr;
+    const bool qvalid = jq < j_end;
+    const uint32_t qrel = qvalid ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)jq)) * D : 0u;
     u32x4_t bq_hi[NKC], bq_lo[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
@@ -223,6 +263,9 @@ __global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
         bq_hi[kc][i] = h;
         bq_lo[kc][i] = l;
       }
+    // cq is free now: the next sub-chunk's queries go straight into it (a register copy of
+    // loaded values would make the loop wait for every outstanding load and store)
+    issue_q(cq, j0 + SUB);
     f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
     f32x4_t acc[2 * PPW];
 #pragma unroll
@@ -310,47 +353,48 @@ __global__ __launch_bounds__(kThreads) void causal_kernel(CausalParams p) {
     }
     __syncthreads();   // the readout is done with the state fragments and the staged tiles
 
-    // ---- the state absorbs the sub-chunk: sacc += (m_ii phi(K))^T V ----
-#pragma unroll
-    for (int a = 0; a < FPW; ++a) {
-      const int fr = wave + 4 * a;
-      if (fr >= NFR) continue;
-      const int kc = fr / NCT, ct = fr % NCT;
+    // ---- the state absorbs the sub-chunk: sacc += (m_ii phi(K))^T V, z += (m_ii phi(K))^T 1 ----
+    if (updater) {
 #pragma unroll
       for (int ks = 0; ks < SUB / 32; ++ks) {
-        const int cb = (16 * ct + pr) * TP + 32 * ks + 8 * lg;
-        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(vt_hi + cb);
-        u32x4_t bl;
-        if constexpr (VSPLIT) bl = *reinterpret_cast<const u32x4_t*>(vt_lo + cb);
+        u32x4_t ah[2], al[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const int f = 32 * kc + 8 * (pr >> 2) + 4 * rt + (pr & 3);
+          const int f = 32 * my_kc + 8 * (pr >> 2) + 4 * rt + (pr & 3);
           const int ka = f * TP + 32 * ks + 8 * lg;
-          const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(kt_hi + ka);
-          const u32x4_t al = *reinterpret_cast<const u32x4_t*>(kt_lo + ka);
-          sacc[a][rt] = mfma_bf16(ah, bh, sacc[a][rt]);
-          sacc[a][rt] = mfma_bf16(al, bh, sacc[a][rt]);
-          if constexpr (VSPLIT) sacc[a][rt] = mfma_bf16(ah, bl, sacc[a][rt]);
+          ah[rt] = *reinterpret_cast<const u32x4_t*>(kt_hi + ka);
+          al[rt] = *reinterpret_cast<const u32x4_t*>(kt_lo + ka);
+        }
+#pragma unroll
+        for (int a = 0; a < FPW; ++a) {
+          const int cb = (16 * (my_ct0 + a) + pr) * TP + 32 * ks + 8 * lg;
+          const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(vt_hi + cb);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) sacc[a][rt] = mfma_bf16(ah[rt], bh, sacc[a][rt]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) sacc[a][rt] = mfma_bf16(al[rt], bh, sacc[a][rt]);
+          if constexpr (VSPLIT) {
+            const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(vt_lo + cb);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) sacc[a][rt] = mfma_bf16(ah[rt], bl, sacc[a][rt]);
+          }
+        }
+        if (zwave) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            zacc[rt] = mfma_bf16(ah[rt], ones, zacc[rt]);
+            zacc[rt] = mfma_bf16(al[rt], ones, zacc[rt]);
+          }
         }
       }
-      const float x[8] = {sacc[a][0][0], sacc[a][0][1], sacc[a][0][2], sacc[a][0][3],
-                          sacc[a][1][0], sacc[a][1][1], sacc[a][1][2], sacc[a][1][3]};
-      store_frag8<true>(s_hi, s_lo, lds_pos<NCT>((fr * 64 + lane) * 8), x);
-    }
-    if (tid < D) {   // normaliser state: + sum over the sub-chunk of m_ii phi(k)
-      float zs = 0.f;
 #pragma unroll
-      for (int j = 0; j < SUB; j += 8) {
-        const u32x4_t h = *reinterpret_cast<const u32x4_t*>(kt_hi + tid * TP + j);
-        const u32x4_t l = *reinterpret_cast<const u32x4_t*>(kt_lo + tid * TP + j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          zs += (bf16lo_to_f32(h[i]) + bf16lo_to_f32(l[i])) + (bf16hi_to_f32(h[i]) + bf16hi_to_f32(l[i]));
+      for (int a = 0; a < FPW; ++a) {
+        const float x[8] = {sacc[a][0][0], sacc[a][0][1], sacc[a][0][2], sacc[a][0][3],
+                            sacc[a][1][0], sacc[a][1][1], sacc[a][1][2], sacc[a][1][3]};
+        store_frag8<true>(s_hi, s_lo, lds_pos<NCT>(((my_kc * NCT + my_ct0 + a) * 64 + lane) * 8), x);
       }
-      s_zt[tid] += zs;
+      if (zwave) write_zfrag();
     }
-    __syncthreads();
-    build_zfrag<D>(s_zt, s_z, tid);
     __syncthreads();
   }
 }
@@ -379,7 +423,7 @@ static hipError_t launch_causal_t(const CausalParams& p, int n_units, hipStream_
   const size_t lds = causal_lds_bytes<D>(sizeof(TIn) == 4);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(n_units), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(n_units), dim3(CausalShape<D>::NT), lds, s, p);
   return hipGetLastError();
 }
 
