@@ -39,9 +39,9 @@ __all__ = ["causal_blockwise", "causal_plain", "causal_sampled", "forward_causal
 
 
 def _blocks_1d(grid, block):
-    grid = tuple(int(g) for g in grid)
-    block = tuple(int(b) for b in block)
-    if len(grid) != 1 or len(block) != 1:
+    """Blocks of a 1D sequence (plain, or a RaggedGrid: a shorter last span, a CLS token first)."""
+    dims = grid.grid if isinstance(grid, F.RaggedGrid) else tuple(grid)
+    if len(dims) != 1:
         raise ValueError("the causal form is defined for a 1D token sequence")
     return F.block_index(grid, block)
 

@@ -39,6 +39,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "RaggedGrid",
     "phi_elu1", "phi_relu", "phi_exp", "phi_map", "block_index", "block_summaries", "mix_summaries", "readout",
     "mhla_blockwise", "mhla_plain", "mhla_plain_sampled", "mhla_attention_matrix",
     "mala_linear", "mala_weights", "mala_plain", "mala_plain_sampled",
@@ -83,22 +84,50 @@ def phi_map(x, phi="elu1"):
 # defined on the 2D/3D spatial grid for vision rather than on the flattened sequence).
 # ----------------------------------------------------------------------------------------
 
+class RaggedGrid:
+    """A token grid whose blocks may be cut short at the far edge of each axis, optionally
+    preceded by one CLS token (token 0) that forms block 0 on its own.  Passed in place of
+    ``grid`` (with ``block`` None) wherever the functions below take (grid, block).
+
+    Readings (the pages' rank bound [MHLA] Key design 1 is stated for a general n_b; DeiT
+    carries a CLS token beside its 14 x 14 patch grid): blocks tile the grid from its origin
+    with the given extents, the last block along an axis keeping what is left; blocks are
+    numbered in raster order over the (rounded-up) block grid, after the CLS block.
+    """
+
+    def __init__(self, grid, block, cls=False):
+        self.grid = tuple(int(g) for g in grid)
+        self.block = tuple(int(b) for b in block)
+        self.cls = bool(cls)
+        if len(self.grid) != len(self.block) or min(self.block) <= 0 or min(self.grid) <= 0:
+            raise ValueError("bad grid or block")
+
+
 def block_index(grid, block) -> np.ndarray:
     """b(t) for every token t of a grid in raster order (last axis fastest).
 
     A token with grid coordinates (c_0, ..., c_{n-1}) belongs to the block whose
     block-grid coordinates are (c_k // block_k); blocks are numbered in raster order.
+    With a RaggedGrid the block grid is rounded up and a CLS token comes first as block 0.
     """
+    cls = False
+    if isinstance(grid, RaggedGrid):
+        grid, block, cls, ragged = grid.grid, grid.block, grid.cls, True
+    else:
+        ragged = False
     grid = tuple(int(g) for g in grid)
     block = tuple(int(b) for b in block)
     assert len(grid) == len(block)
     for g, b in zip(grid, block):
-        if b <= 0 or g % b:
+        if b <= 0 or (g % b and not ragged):
             raise ValueError("block extents must divide the grid")
     coords = np.indices(grid).reshape(len(grid), -1)          # [ndim, N], raster order
     bcoords = coords // np.asarray(block)[:, None]
-    bgrid = [g // b for g, b in zip(grid, block)]
-    return np.ravel_multi_index(tuple(bcoords), bgrid).astype(np.int64)
+    bgrid = [-(-g // b) for g, b in zip(grid, block)]
+    bidx = np.ravel_multi_index(tuple(bcoords), bgrid).astype(np.int64)
+    if cls:
+        bidx = np.concatenate([[0], bidx + 1])
+    return bidx
 
 
 # ----------------------------------------------------------------------------------------
