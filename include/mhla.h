@@ -99,10 +99,27 @@ typedef struct {
   int32_t mc_per_head;      /* 0: M_c is [M, M]; 1: M_c is [H, M, M]                           */
   int64_t grid[3];          /* token grid extents, first ndim used; N = product                */
   int64_t block[3];         /* block extents, first ndim used; each divides grid exactly       */
+                            /* (unless MHLA_FLAG_RAGGED_BLOCKS)                                */
   int64_t batch;            /* B >= 1                                                          */
   int64_t heads;            /* H >= 1                                                          */
   int64_t head_dim;         /* d in {16, 32, 64, 128}                                          */
+  int32_t flags;            /* MHLA_FLAG_* bits (0: every block whole, no CLS token)           */
+  int32_t reserved;         /* must be 0                                                       */
 } mhla_desc;
+
+/* Geometry flags ("MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head":
+ * the rank bound of Key design 1 is stated for general block sizes n_b; DeiT carries a CLS token
+ * beside its patch grid).  Readings:
+ *   MHLA_FLAG_RAGGED_BLOCKS  the block extents need not divide the grid: blocks tile the grid from
+ *                            its origin and the last block along an axis keeps what is left
+ *                            (fewer tokens); blocks are numbered in raster order over the
+ *                            rounded-up block grid.  A block extent above the grid's is clipped.
+ *   MHLA_FLAG_CLS_TOKEN      one extra token precedes the grid (token 0 of every head, N = 1 +
+ *                            product of the grid) and forms block 0 on its own; the grid's blocks
+ *                            are 1 .. M-1, and M_c is M x M with M counting the CLS block.
+ * A descriptor whose struct_size is that of the earlier layout (without flags and reserved) is
+ * accepted with flags = 0. */
+enum { MHLA_FLAG_RAGGED_BLOCKS = 1, MHLA_FLAG_CLS_TOKEN = 2 };
 
 typedef struct mhla_plan* mhla_handle;
 
@@ -111,7 +128,8 @@ typedef struct {
   uint32_t struct_size;     /* caller sets = sizeof(mhla_plan_info)                            */
   int64_t n_tokens;         /* N                                                               */
   int64_t n_blocks;         /* M                                                               */
-  int64_t block_tokens;     /* n_b = N / M                                                     */
+  int64_t block_tokens;     /* n_b = N / M; with ragged blocks or a CLS token, the tokens of a  */
+                            /* whole block (the most any block holds)                          */
   int64_t workspace_bytes;  /* same as mhla_workspace_size                                     */
   int32_t summary_splits;   /* token slices per block in the summary kernel                    */
   int32_t readout_splits;   /* token slices per block in the readout kernel                    */

@@ -52,6 +52,8 @@ class Workload:
     mc_kind: str                     # "softmax_l1" | "softmax_l1_noise" | "softmax_gauss" | "none"
     readout: str = "normalized"      # "normalized" | "unnormalized" | "mala"
     phi: str = "elu1"                # feature map: "elu1" | "relu" | "exp"
+    ragged: bool = False             # blocks need not divide the grid (the last one is cut short)
+    cls: bool = False                # one CLS token before the grid, a block of its own
 
     @property
     def ndim(self) -> int:
@@ -59,15 +61,15 @@ class Workload:
 
     @property
     def n_tokens(self) -> int:
-        return int(np.prod(self.grid))
+        return int(self.cls) + int(np.prod(self.grid))
 
     @property
     def block_tokens(self) -> int:
-        return int(np.prod(self.block))
+        return int(np.prod([min(b, g) for g, b in zip(self.grid, self.block)]))
 
     @property
     def n_blocks(self) -> int:
-        return num_blocks(self.grid, self.block)
+        return int(self.cls) + num_blocks(self.grid, self.block, self.ragged)
 
     @property
     def qkv_shape(self) -> Tuple[int, int, int, int]:
@@ -91,19 +93,20 @@ def get_workload(name: str) -> Workload:
     return WORKLOADS[name]
 
 
-def block_grid_shape(grid, block) -> Tuple[int, ...]:
+def block_grid_shape(grid, block, ragged=False) -> Tuple[int, ...]:
+    """Blocks along each axis; with ``ragged`` a block that does not fit is cut short (rounded up)."""
     grid = tuple(int(g) for g in grid)
     block = tuple(int(b) for b in block)
     if len(grid) != len(block):
         raise ValueError("grid and block must have the same rank")
     for g, b in zip(grid, block):
-        if b <= 0 or g % b != 0:
+        if b <= 0 or (g % b != 0 and not ragged):
             raise ValueError(f"block extent {b} does not divide grid extent {g}")
-    return tuple(g // b for g, b in zip(grid, block))
+    return tuple(-(-g // b) for g, b in zip(grid, block))
 
 
-def num_blocks(grid, block) -> int:
-    return int(np.prod(block_grid_shape(grid, block)))
+def num_blocks(grid, block, ragged=False) -> int:
+    return int(np.prod(block_grid_shape(grid, block, ragged)))
 
 
 # --------------------------------------------------------------------------------------
@@ -217,10 +220,14 @@ def make_grad_output(w: Workload, rng: np.random.Generator, dtype: str = "fp32")
 
 
 def make_mc(w: Workload, rng: np.random.Generator):
-    bg = block_grid_shape(w.grid, w.block)
-    m = int(np.prod(bg))
+    """M_c for ``w`` ([M, M], M counting a CLS block).  With a CLS token only the kinds that
+    need no block-grid geometry apply."""
+    bg = block_grid_shape(w.grid, w.block, w.ragged)
+    m = w.n_blocks
     if w.mc_kind == "none":
         return None
+    if w.cls and w.mc_kind in ("softmax_l1", "softmax_l1_noise", "locality"):
+        raise ValueError(f"M_c kind {w.mc_kind} is laid out on the block grid; a CLS block has no place there")
     if w.mc_kind == "softmax_l1":
         mc = mc_softmax_l1(bg)
     elif w.mc_kind == "softmax_l1_noise":

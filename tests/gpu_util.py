@@ -25,7 +25,7 @@ def run_hip(w: synth.Workload, q, k, v, mc, *, out_dtype="fp32", accuracy="auto"
     mc_per_head = mc is not None and np.ndim(mc) == 3
     plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
                   in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, accuracy=accuracy, phi=w.phi,
-                  mc_per_head=mc_per_head)
+                  mc_per_head=mc_per_head, ragged=w.ragged, cls_token=w.cls)
     tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
     tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
     odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
@@ -52,11 +52,19 @@ def announce(msg: str) -> None:
     sys.stdout.flush()
 
 
+def oracle_geometry(w):
+    """(grid, block) as the oracle takes them: a RaggedGrid for ragged blocks or a CLS token."""
+    if w.ragged or w.cls:
+        return oracle.RaggedGrid(w.grid, w.block, cls=w.cls), None
+    return w.grid, w.block
+
+
 def oracle_full(w, q, k, v, mc, heads=None):
+    grid, block = oracle_geometry(w)
     if w.readout.startswith("causal"):
         mode = "unnormalized" if w.readout == "causal_unnormalized" else "normalized"
-        return oracle.forward_causal(q, k, v, mc, w.grid, w.block, mode=mode, heads=heads, phi=w.phi)
-    return oracle.forward(q, k, v, mc, w.grid, w.block, mode=w.readout, heads=heads, phi=w.phi)
+        return oracle.forward_causal(q, k, v, mc, grid, block, mode=mode, heads=heads, phi=w.phi)
+    return oracle.forward(q, k, v, mc, grid, block, mode=w.readout, heads=heads, phi=w.phi)
 
 
 def run_hip_backward(w: synth.Workload, q, k, v, mc, do, *, out_dtype="fp32", want_dmc=True, repeat=1):
@@ -66,7 +74,7 @@ def run_hip_backward(w: synth.Workload, q, k, v, mc, do, *, out_dtype="fp32", wa
     mc_per_head = mc is not None and np.ndim(mc) == 3
     plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
                   in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, phi=w.phi,
-                  mc_per_head=mc_per_head)
+                  mc_per_head=mc_per_head, ragged=w.ragged, cls_token=w.cls)
     tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
     tdo = to_device(do, out_dtype)
     tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
@@ -84,4 +92,5 @@ def run_hip_backward(w: synth.Workload, q, k, v, mc, do, *, out_dtype="fp32", wa
 
 
 def oracle_backward(w, q, k, v, mc, do, heads=None):
-    return oracle.backward(q, k, v, mc, w.grid, w.block, do, mode=w.readout, heads=heads, phi=w.phi)
+    grid, block = oracle_geometry(w)
+    return oracle.backward(q, k, v, mc, grid, block, do, mode=w.readout, heads=heads, phi=w.phi)

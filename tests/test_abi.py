@@ -39,8 +39,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # mhla_desc: 8 x int32 (incl. struct_size) + 2 x int64[3] + 3 x int64 = 32 + 48 + 24
-    assert ctypes.sizeof(T.MhlaDesc) == 104
+    # mhla_desc: 8 x int32 (incl. struct_size) + 2 x int64[3] + 3 x int64 + 2 x int32
+    #   = 32 + 48 + 24 + 8
+    assert ctypes.sizeof(T.MhlaDesc) == 112
+    assert T.MhlaDesc.flags.offset == 104
     assert ctypes.sizeof(T.MhlaPlanInfo) == 56
 
 
@@ -84,11 +86,49 @@ def test_create_accepts_workload_shapes():
     (lambda d: d.grid.__setitem__(0, 0), 3),
     (lambda d: setattr(d, "readout", T.MHLA_READOUT_MALA), 2),   # MALA needs M == 1
     (lambda d: setattr(d, "mc_per_head", 2), 1),
+    (lambda d: setattr(d, "flags", 4), 1),                # unknown flag bit
+    (lambda d: setattr(d, "reserved", 1), 1),
 ])
 def test_create_rejections(mutate, want):
     d = _desc()
     mutate(d)
     assert _status(d) == want
+
+
+def test_earlier_descriptor_layout_is_accepted_without_flags():
+    d = _desc()
+    d.struct_size = T.MhlaDesc.flags.offset
+    d.flags = T.MHLA_FLAG_CLS_TOKEN          # past the earlier layout's end: not read
+    assert _status(d) == 0
+    d.block[1] = 15                          # and blocks must divide the grid
+    assert _status(d) == 3
+
+
+def _info(**kw):
+    p = T.Plan(**dict(dict(batch=1, heads=1, head_dim=64), **kw))
+    try:
+        return p.info
+    finally:
+        p.close()
+
+
+def test_ragged_blocks_and_cls_token_geometry():
+    _lib_or_skip()
+    # DeiT at 224 px: a 14 x 14 patch grid and a CLS token; 7 x 7 blocks -> 4 + 1 blocks
+    i = _info(grid=(14, 14), block=(7, 7), cls_token=True)
+    assert (i.n_tokens, i.n_blocks, i.block_tokens) == (197, 5, 49)
+    # ragged: 10 x 10 in 4 x 4 blocks -> 3 x 3 blocks of 16, 8, 8, 4 tokens ...
+    i = _info(grid=(10, 10), block=(4, 4), ragged=True)
+    assert (i.n_tokens, i.n_blocks, i.block_tokens) == (100, 9, 16)
+    i = _info(grid=(1000,), block=(300,), ragged=True, cls_token=True)
+    assert (i.n_tokens, i.n_blocks, i.block_tokens) == (1001, 5, 300)
+    # a block extent beyond the grid's is clipped to it
+    i = _info(grid=(5, 40), block=(8, 16), ragged=True)
+    assert (i.n_tokens, i.n_blocks, i.block_tokens) == (200, 3, 80)
+    # without the flag a non-dividing block is still an error
+    assert _status(_desc(grid=(10, 10), block=(4, 4))) == 3
+    # MALA with a CLS token has two blocks: not supported
+    assert _status(_desc(block=(64, 64), readout="mala", cls_token=True)) == 2
 
 
 def test_create_null_arguments():

@@ -15,6 +15,7 @@ __all__ = [
     "MHLA_OK", "MHLA_DTYPE_BF16", "MHLA_DTYPE_FP32", "MHLA_PHI_ELU1", "MHLA_PHI_RELU", "MHLA_PHI_EXP",
     "MHLA_READOUT_NORMALIZED", "MHLA_READOUT_UNNORMALIZED", "MHLA_READOUT_MALA",
     "MHLA_READOUT_CAUSAL_NORMALIZED", "MHLA_READOUT_CAUSAL_UNNORMALIZED",
+    "MHLA_FLAG_RAGGED_BLOCKS", "MHLA_FLAG_CLS_TOKEN",
     "MHLA_ACCURACY_AUTO", "MHLA_ACCURACY_BF16", "MHLA_ACCURACY_SPLIT",
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
@@ -27,6 +28,7 @@ MHLA_DTYPE_BF16, MHLA_DTYPE_FP32 = 0, 1
 MHLA_PHI_ELU1, MHLA_PHI_RELU, MHLA_PHI_EXP = 0, 1, 2
 MHLA_READOUT_NORMALIZED, MHLA_READOUT_UNNORMALIZED, MHLA_READOUT_MALA = 0, 1, 2
 MHLA_READOUT_CAUSAL_NORMALIZED, MHLA_READOUT_CAUSAL_UNNORMALIZED = 3, 4
+MHLA_FLAG_RAGGED_BLOCKS, MHLA_FLAG_CLS_TOKEN = 1, 2
 MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT = 0, 1, 2
 
 _READOUTS = {"normalized": MHLA_READOUT_NORMALIZED, "unnormalized": MHLA_READOUT_UNNORMALIZED,
@@ -58,6 +60,8 @@ class MhlaDesc(ctypes.Structure):
         ("batch", ctypes.c_int64),
         ("heads", ctypes.c_int64),
         ("head_dim", ctypes.c_int64),
+        ("flags", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -212,7 +216,8 @@ def mhla_timing_reset(h) -> None:
 
 def make_desc(*, grid: Sequence[int], block: Sequence[int], batch: int, heads: int, head_dim: int,
               in_dtype: str = "bf16", out_dtype: str = "fp32", readout: str = "normalized",
-              accuracy: str = "auto", mc_per_head: bool = False, phi: str = "elu1") -> MhlaDesc:
+              accuracy: str = "auto", mc_per_head: bool = False, phi: str = "elu1",
+              ragged: bool = False, cls_token: bool = False) -> MhlaDesc:
     if len(grid) != len(block) or not 1 <= len(grid) <= 3:
         raise ValueError("grid and block must have the same rank, 1 to 3")
     d = MhlaDesc()
@@ -228,6 +233,7 @@ def make_desc(*, grid: Sequence[int], block: Sequence[int], batch: int, heads: i
         d.grid[i] = int(g)
         d.block[i] = int(b)
     d.batch, d.heads, d.head_dim = int(batch), int(heads), int(head_dim)
+    d.flags = (MHLA_FLAG_RAGGED_BLOCKS if ragged else 0) | (MHLA_FLAG_CLS_TOKEN if cls_token else 0)
     return d
 
 
@@ -261,6 +267,7 @@ class Plan:
         n = 1
         for g in kw["grid"]:
             n *= int(g)
+        n += 1 if kw.get("cls_token") else 0
         qkv = (int(kw["batch"]), int(kw["heads"]), n, int(kw["head_dim"]))
         m = int(self.info.n_blocks)
         mc = (int(kw["heads"]), m, m) if kw.get("mc_per_head") else (m, m)

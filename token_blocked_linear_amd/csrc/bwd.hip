@@ -42,6 +42,7 @@ struct BwdUnit {
   int32_t j_begin, j_end, base_tok;
   int n_tiles;
   int64_t head_off, row;
+  BlockGeo bg;
 };
 template <int D>
 __device__ inline BwdUnit bwd_unit(const BwdParams& p, int L) {
@@ -60,8 +61,9 @@ __device__ inline BwdUnit bwd_unit(const BwdParams& p, int L) {
   u.blk = r / p.splits;
   u.split = r % p.splits;
   u.j_begin = u.split * p.tok_per_split;
-  u.j_end = min(u.j_begin + p.tok_per_split, g.n_b);
-  u.base_tok = block_base_token(g, u.blk);
+  u.bg = block_geo(g, u.blk);
+  u.j_end = min(u.j_begin + p.tok_per_split, u.bg.n);
+  u.base_tok = u.bg.base;
   u.n_tiles = (u.j_end - u.j_begin + 15) >> 4;
   u.head_off = (int64_t)u.bh * g.N * D;
   u.row = (int64_t)u.bh * g.M + u.blk;
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
   auto token_of = [&](int tile, bool& valid, uint32_t& rel) {
     const int32_t j = U.j_begin + tile * 16 + pr;
     valid = tile < U.n_tiles && j < U.j_end;
-    rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
+    rel = valid ? (uint32_t)(U.base_tok + block_offset(geo, U.bg, (uint32_t)j)) * D : 0u;
   };
   auto issue = [&](In8<TIn> (&cq)[NKC], In8<TOut> (&cdo)[NG], bool valid, uint32_t rel) {
 #pragma unroll
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
   auto token_of = [&](int tile, bool& valid, uint32_t& rel) {
     const int32_t j = U.j_begin + tile * 16 + pr;
     valid = tile < U.n_tiles && j < U.j_end;
-    rel = valid ? (uint32_t)(U.base_tok + block_token_offset(geo, (uint32_t)j)) * D : 0u;
+    rel = valid ? (uint32_t)(U.base_tok + block_offset(geo, U.bg, (uint32_t)j)) * D : 0u;
   };
   auto issue = [&](In8<TIn> (&ck)[NKC], In8<TIn> (&cv)[NKC], bool valid, uint32_t rel) {
 #pragma unroll

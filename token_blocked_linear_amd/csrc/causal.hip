@@ -112,8 +112,9 @@ __global__ __launch_bounds__(CausalShape<D>::NT) void causal_kernel(CausalParams
   }
   const int blk = r / p.splits, split = r % p.splits;
   const int32_t j_begin = split * p.tok_per_split;
-  const int32_t j_end = min(j_begin + p.tok_per_split, geo.n_b);
-  const int32_t base_tok = block_base_token(geo, blk);
+  const BlockGeo bgeo = block_geo(geo, blk);
+  const int32_t j_end = min(j_begin + p.tok_per_split, bgeo.n);
+  const int32_t base_tok = bgeo.base;
   const int64_t head_off = (int64_t)bh * geo.N * D;
   const int64_t row = (int64_t)bh * geo.M + blk;
   const float mii = p.mc ? p.mc[(int64_t)(bh % p.H) * p.mc_head_stride + (int64_t)blk * geo.M + blk] : 1.0f;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(CausalShape<D>::NT) void causal_kernel(CausalParams
     for (int i = 0; i < 2; ++i) {
       const int32_t j = j0 + 2 * tp + i;
       const bool ok = stager && j < j_end;
-      const uint32_t t = ok ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)j)) : 0u;
+      const uint32_t t = ok ? (uint32_t)(base_tok + block_offset(geo, bgeo, (uint32_t)j)) : 0u;
       const uint32_t off = ok ? (t * D + 8 * fg) * ES : kOutOfRange;
       ck[i].template load_buf<0>(rk, off);
       cv[i].template load_buf<0>(rv, off);
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(CausalShape<D>::NT) void causal_kernel(CausalParams
   auto issue_q = [&](In8<TIn> (&dst)[NKC], int32_t j0) {
     const int32_t jq = j0 + 16 * qt + pr;
     const bool ok = jq < j_end;
-    const uint32_t rel = ok ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)jq)) * D : 0u;
+    const uint32_t rel = ok ? (uint32_t)(base_tok + block_offset(geo, bgeo, (uint32_t)jq)) * D : 0u;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) dst[kc].template load_buf<0>(rq, ok ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange);
   };
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(CausalShape<D>::NT) void causal_kernel(CausalParams
     // ---- readout of query tile qt, channel pairs [cp * PPW, (cp + 1) * PPW) ----
     const int32_t jq = j0 + 16 * qt + pr;
     const bool qvalid = jq < j_end;
-    const uint32_t qrel = qvalid ? (uint32_t)(base_tok + block_token_offset(geo, (uint32_t)jq)) * D : 0u;
+    const uint32_t qrel = qvalid ? (uint32_t)(base_tok + block_offset(geo, bgeo, (uint32_t)jq)) * D : 0u;
     u32x4_t bq_hi[NKC], bq_lo[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)

@@ -19,7 +19,7 @@ struct FastDiv {
   uint32_t d, m, s;
 };
 
-inline FastDiv make_fastdiv(uint32_t d) {
+MHLA_HD inline FastDiv make_fastdiv(uint32_t d) {
   FastDiv f;
   f.d = d;
   uint32_t s = 0;

@@ -49,30 +49,55 @@ template <int D> struct Dims {
 
 // Token-grid geometry, padded to 3 axes with leading extents of 1.
 struct Geom {
-  int32_t G1, G2;          // grid extents of axes 1 and 2 (axis 0 is implied)
-  int32_t B0, B1, B2;      // block extents
-  int32_t NB1, NB2;        // block-grid extents of axes 1 and 2
-  FastDiv fB2, fB1;        // divide block-local token indices
-  int32_t n_b;             // tokens per block
-  int32_t N;               // tokens per head
-  int32_t M;               // blocks per head
+  int32_t G1, G2;          // grid extents of axes 1 and 2
+  int32_t B0, B1, B2;      // block extents (of a whole block)
+  int32_t NB1, NB2;        // block-grid extents of axes 1 and 2 (rounded up)
+  FastDiv fB2, fB1;        // divide block-local token indices of a whole block
+  int32_t n_b;             // tokens of a whole block (the most a block holds)
+  int32_t N;               // tokens per head (the CLS token included)
+  int32_t M;               // blocks per head (the CLS block included)
+  int32_t G0;              // grid extent of axis 0
+  int32_t cls;             // 1: token 0 is a CLS token forming block 0; grid tokens follow
 };
 
-// First token (raster index) of block b.
-__device__ inline int32_t block_base_token(const Geom& g, int32_t b) {
-  int32_t b2 = b % g.NB2;
-  int32_t t = b / g.NB2;
-  int32_t b1 = t % g.NB1;
-  int32_t b0 = t / g.NB1;
-  return ((b0 * g.B0) * g.G1 + b1 * g.B1) * g.G2 + b2 * g.B2;
+// One block's place in the sequence: first token, token count, extents along axes 1 and 2 and
+// their divisors.  With ragged blocks the last block along an axis keeps what is left of the
+// grid; the CLS block is its one token.
+struct BlockGeo {
+  int32_t base, n, e1, e2;
+  FastDiv f2, f1;
+};
+__device__ inline BlockGeo block_geo(const Geom& g, int32_t b) {
+  BlockGeo r;
+  if (g.cls) {
+    if (b == 0) {
+      r.base = 0;
+      r.n = 1;
+      r.e1 = r.e2 = 1;
+      r.f2 = r.f1 = FastDiv{1u, 1u, 0u};
+      return r;
+    }
+    --b;
+  }
+  const int32_t b2 = b % g.NB2, t = b / g.NB2;
+  const int32_t b1 = t % g.NB1, b0 = t / g.NB1;
+  const int32_t c0 = b0 * g.B0, c1 = b1 * g.B1, c2 = b2 * g.B2;
+  const int32_t e0 = min(g.B0, g.G0 - c0);
+  r.e1 = min(g.B1, g.G1 - c1);
+  r.e2 = min(g.B2, g.G2 - c2);
+  r.base = g.cls + (c0 * g.G1 + c1) * g.G2 + c2;
+  r.n = e0 * r.e1 * r.e2;
+  r.f2 = r.e2 == g.B2 ? g.fB2 : make_fastdiv((uint32_t)r.e2);
+  r.f1 = r.e1 == g.B1 ? g.fB1 : make_fastdiv((uint32_t)r.e1);
+  return r;
 }
 
-// Raster token index of block-local token j (0 <= j < n_b) relative to the block's base.
-__device__ inline int32_t block_token_offset(const Geom& g, uint32_t j) {
-  uint32_t q2 = fdiv(j, g.fB2);
-  uint32_t j2 = j - q2 * (uint32_t)g.B2;
-  uint32_t j0 = fdiv(q2, g.fB1);
-  uint32_t j1 = q2 - j0 * (uint32_t)g.B1;
+// Raster token index of block-local token j (0 <= j < n) relative to the block's first token.
+__device__ inline int32_t block_offset(const Geom& g, const BlockGeo& bg, uint32_t j) {
+  const uint32_t q2 = fdiv(j, bg.f2);
+  const uint32_t j2 = j - q2 * (uint32_t)bg.e2;
+  const uint32_t j0 = fdiv(q2, bg.f1);
+  const uint32_t j1 = q2 - j0 * (uint32_t)bg.e1;
   return (int32_t)((j0 * (uint32_t)g.G1 + j1) * (uint32_t)g.G2 + j2);
 }
 

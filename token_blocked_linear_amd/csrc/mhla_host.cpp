@@ -121,8 +121,22 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
-  if (d->struct_size != sizeof(mhla_desc)) return MHLA_ERR_INVALID_ARG;
+mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
+  // the earlier layout ended before `flags`: accepted with flags = 0
+  mhla_desc dcopy = {};
+  if (din->struct_size == sizeof(mhla_desc)) {
+    dcopy = *din;
+  } else if (din->struct_size == offsetof(mhla_desc, flags)) {
+    std::memcpy(&dcopy, din, offsetof(mhla_desc, flags));
+    dcopy.struct_size = sizeof(mhla_desc);
+  } else {
+    return MHLA_ERR_INVALID_ARG;
+  }
+  const mhla_desc* d = &dcopy;
+  if ((d->flags & ~(MHLA_FLAG_RAGGED_BLOCKS | MHLA_FLAG_CLS_TOKEN)) != 0 || d->reserved != 0)
+    return MHLA_ERR_INVALID_ARG;
+  const bool ragged = (d->flags & MHLA_FLAG_RAGGED_BLOCKS) != 0;
+  const int64_t cls = (d->flags & MHLA_FLAG_CLS_TOKEN) ? 1 : 0;
   if (d->in_dtype != MHLA_DTYPE_BF16 && d->in_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
   if (d->out_dtype != MHLA_DTYPE_BF16 && d->out_dtype != MHLA_DTYPE_FP32) return MHLA_ERR_UNSUPPORTED;
   if (d->phi != MHLA_PHI_ELU1 && d->phi != MHLA_PHI_RELU && d->phi != MHLA_PHI_EXP)
@@ -138,17 +152,20 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
 
   int64_t grid[3] = {1, 1, 1}, block[3] = {1, 1, 1};
   const int pad = 3 - d->ndim;
+  int64_t nblk[3] = {1, 1, 1};
   for (int a = 0; a < d->ndim; ++a) {
     if (d->grid[a] < 1 || d->block[a] < 1) return MHLA_ERR_SHAPE;
-    if (d->grid[a] % d->block[a] != 0) return MHLA_ERR_SHAPE;
+    if (d->grid[a] % d->block[a] != 0 && !ragged) return MHLA_ERR_SHAPE;
     if (d->grid[a] > (int64_t)1 << 31) return MHLA_ERR_SHAPE;
     grid[pad + a] = d->grid[a];
-    block[pad + a] = d->block[a];
+    block[pad + a] = std::min(d->block[a], d->grid[a]);   // a block never exceeds the grid
+    nblk[pad + a] = (grid[pad + a] + block[pad + a] - 1) / block[pad + a];
   }
-  const int64_t N = grid[0] * grid[1] * grid[2];
-  const int64_t nb = block[0] * block[1] * block[2];
+  const int64_t N = cls + grid[0] * grid[1] * grid[2];
+  const int64_t nb = block[0] * block[1] * block[2];      // tokens of a whole block
   if (N >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
-  const int64_t M = N / nb;
+  if (nblk[0] * nblk[1] * nblk[2] > 65535) return MHLA_ERR_SHAPE;
+  const int64_t M = cls + nblk[0] * nblk[1] * nblk[2];
   const int64_t BH = d->batch * d->heads;
   if (BH > 65535 || M > 65535) return MHLA_ERR_SHAPE;
   if (d->readout == MHLA_READOUT_MALA && M != 1) return MHLA_ERR_UNSUPPORTED;
@@ -174,8 +191,10 @@ mhla_status build_plan(const mhla_desc* d, mhla_plan* P) {
   g.B0 = (int32_t)block[0];
   g.B1 = (int32_t)block[1];
   g.B2 = (int32_t)block[2];
-  g.NB1 = (int32_t)(grid[1] / block[1]);
-  g.NB2 = (int32_t)(grid[2] / block[2]);
+  g.NB1 = (int32_t)nblk[1];
+  g.NB2 = (int32_t)nblk[2];
+  g.G0 = (int32_t)grid[0];
+  g.cls = (int32_t)cls;
   g.fB2 = mhla::make_fastdiv((uint32_t)block[2]);
   g.fB1 = mhla::make_fastdiv((uint32_t)block[1]);
   g.n_b = (int32_t)nb;

@@ -159,6 +159,7 @@ struct RdUnit {
   int32_t j_begin, j_end, base_tok;
   int n_tiles;
   int64_t head_off, row;
+  BlockGeo bg;
 };
 template <int D>
 __device__ inline RdUnit rd_unit(const ReadoutParams& p, int L) {
@@ -177,8 +178,9 @@ __device__ inline RdUnit rd_unit(const ReadoutParams& p, int L) {
   u.blk = r / p.splits;
   const int split = r % p.splits;
   u.j_begin = split * p.tok_per_split;
-  u.j_end = min(u.j_begin + p.tok_per_split, g.n_b);
-  u.base_tok = block_base_token(g, u.blk);
+  u.bg = block_geo(g, u.blk);
+  u.j_end = min(u.j_begin + p.tok_per_split, u.bg.n);
+  u.base_tok = u.bg.base;
   u.n_tiles = (u.j_end - u.j_begin + 15) >> 4;
   u.head_off = (int64_t)u.bh * g.N * D;
   u.row = (int64_t)u.bh * g.M + u.blk;
@@ -194,7 +196,7 @@ __device__ inline void rd_issue(const ReadoutParams& p, const RdUnit& u, int t, 
   const int pr = lane & 15, lg = lane >> 4;
   const int32_t j = u.j_begin + t * 16 + pr;
   v = j < u.j_end;
-  off = v ? u.head_off + (int64_t)(u.base_tok + block_token_offset(p.g, (uint32_t)j)) * D : 0;
+  off = v ? u.head_off + (int64_t)(u.base_tok + block_offset(p.g, u.bg, (uint32_t)j)) * D : 0;
   const Rsrc rsq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + u.head_off, (uint32_t)p.g.N * D * ES);
   const uint32_t rel = (uint32_t)(off - u.head_off);
 #pragma unroll

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
     int split, blk, bh;
     int32_t j_begin, j_end, base_tok;
     int64_t head_off;
+    BlockGeo bg;
   };
   auto make_unit = [&](int u) {
     Unit U;
@@ -121,16 +122,21 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
     U.blk = t % g.M;
     U.bh = t / g.M;
     U.j_begin = U.split * p.tok_per_split;
-    U.j_end = min(U.j_begin + p.tok_per_split, g.n_b);
-    U.base_tok = block_base_token(g, U.blk);
+    U.bg = block_geo(g, U.blk);
+    U.j_end = min(U.j_begin + p.tok_per_split, U.bg.n);
+    U.base_tok = U.bg.base;
     U.head_off = (int64_t)U.bh * g.N * D;
     return U;
   };
 
   // When the block's last extent is a multiple of 8, a thread's 8 block-local tokens
   // j0..j0+7 (j0 a multiple of 8) lie in one grid row: their rows are consecutive in memory
-  // and one index computation serves all 8 loads.
-  const bool contig8 = (g.B2 & 7) == 0;
+  // and one index computation serves all 8 loads.  (Per unit: a ragged edge block may not.)
+  // The token-weight loads there read 16 bytes at token t0 and need t0 a multiple of 4:
+  // t0 = base + row * G2 + (multiple of 8), so base and G2 must be.
+  auto contig8_of = [&](const Unit& U) {
+    return (U.bg.e2 & 7) == 0 && (!TOKW || ((U.bg.base & 3) == 0 && (g.G2 & 3) == 0));
+  };
 
   // Loads of one round into a register buffer.  Rows of tokens past the unit's end are zero:
   // they add nothing to S (their V is zero) and z masks them explicitly.
@@ -144,9 +150,9 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
     const Rsrc rsk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, head_bytes);
     const Rsrc rsv = make_rsrc(reinterpret_cast<const TV*>(p.v) + U.head_off, head_bytes_v);
     const int32_t j0 = round_base + 8 * tgrp;
-    if (contig8) {
+    if (contig8_of(U)) {
       const bool ok = loader && j0 < U.j_end;
-      const uint32_t t0 = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j0)) : 0u;
+      const uint32_t t0 = ok ? (uint32_t)(U.base_tok + block_offset(g, U.bg, (uint32_t)j0)) : 0u;
       const uint32_t e0 = t0 * D + 8 * fgrp;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -154,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
         rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, ok ? (e0 + (uint32_t)(i * D)) * ESV : kOutOfRange);
       }
       if constexpr (TOKW) {
-        // t0 is a multiple of 8 here (block and grid extents along the last axis are), and so
-        // is j_end: the 8 tokens are all in the unit or all past its end
+        // t0 is a multiple of 4 here, and j_end a multiple of 8 (the block's last extent and the
+        // slice length are): the 8 tokens are all in the unit or all past its end
         const Rsrc rs = make_rsrc(p.kscale + (int64_t)U.bh * g.N, (uint32_t)g.N * 4u);
         const Rsrc rz = make_rsrc(p.zw + (int64_t)U.bh * g.N, (uint32_t)g.N * 4u);
         const u32x4_t s0 = buf_ld16(rs, ok ? t0 * 4u : kOutOfRange), s1 = buf_ld16(rs, ok ? t0 * 4u + 16u : kOutOfRange);
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
       for (int i = 0; i < 8; ++i) {
         const int32_t j = j0 + i;
         const bool ok = loader && j < U.j_end;
-        const uint32_t t = ok ? (uint32_t)(U.base_tok + block_token_offset(g, (uint32_t)j)) : 0u;
+        const uint32_t t = ok ? (uint32_t)(U.base_tok + block_offset(g, U.bg, (uint32_t)j)) : 0u;
         const uint32_t e = t * D + 8 * fgrp;
         rk[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsk, ok ? e * ES : kOutOfRange);
         rv[i].template load_buf<MHLA_SUMMARY_LOAD_CPOL>(rsv, ok ? e * ESV : kOutOfRange);
