@@ -457,6 +457,11 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
 // MFMAs.  Positions past FRAG + D (the last step of a (batch, head)) read as zero.
 constexpr int kDmcTile = 64, kDmcK = 64, kDmcPitch = kDmcK + 8;   // pitch in bf16 elements
 
+// SINGLE: every summary has one token slice (ssplits = zsplits_d = 1).  The step's loads then
+// go straight into registers through buffer resources (rows past M and positions past FRAG + D
+// read as zero) and are converted at the LDS store, so they stay in flight during the MFMAs;
+// with several slices they are summed as they arrive.
+template <bool SINGLE>
 __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
   __shared__ __align__(16) uint16_t a_hi[kDmcTile * kDmcPitch], a_lo[kDmcTile * kDmcPitch];
   __shared__ __align__(16) uint16_t b_hi[kDmcTile * kDmcPitch], b_lo[kDmcTile * kDmcPitch];
@@ -506,6 +511,39 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
     }
   };
 
+  // SINGLE: raw words of the step, [h][0..1] = positions pos + 8h + 0..3 and + 4..7
+  u32x4_t ra[2][2], rb[2][2];
+  auto issue_step = [&](int64_t step) {
+    const int j = (int)(step / p.steps_per_bh);
+    const int pos0 = (int)(step % p.steps_per_bh) * kDmcK;   // the step is all S or all z
+    const int bh = p.per_head ? j * p.H + grp : j;
+    const bool in_s = pos0 < FRAG;
+    const Rsrc rsa = in_s ? make_rsrc(p.dps + (int64_t)bh * M * FRAG, (uint32_t)M * FRAG * 4u)
+                          : make_rsrc(p.dpz + (int64_t)bh * M * D, (uint32_t)M * D * 4u);
+    const Rsrc rsb = in_s ? make_rsrc(p.ps + (int64_t)bh * M * FRAG, (uint32_t)M * FRAG * 4u)
+                          : make_rsrc(p.pz + (int64_t)bh * M * D, (uint32_t)M * D * 4u);
+    const int stride = in_s ? FRAG : D, base = in_s ? 0 : FRAG;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pos = pos0 + lcol + 8 * h;
+      const bool okp = pos < FRAG + D;
+      const int ma = i0 + lrow, mb = b0 + lrow;
+      const uint32_t oa = (okp && ma < M) ? (uint32_t)(ma * stride + pos - base) * 4u : kOutOfRange;
+      const uint32_t ob = (okp && mb < M) ? (uint32_t)(mb * stride + pos - base) * 4u : kOutOfRange;
+      ra[h][0] = buf_ld16(rsa, oa);
+      ra[h][1] = buf_ld16(rsa, oa == kOutOfRange ? kOutOfRange : oa + 16u);
+      rb[h][0] = buf_ld16(rsb, ob);
+      rb[h][1] = buf_ld16(rsb, ob == kOutOfRange ? kOutOfRange : ob + 16u);
+    }
+  };
+  auto words = [](const u32x4_t (&w)[2], float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = __uint_as_float(w[0][e]);
+      x[4 + e] = __uint_as_float(w[1][e]);
+    }
+  };
+
   f32x4_t acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -513,10 +551,17 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
     for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   float xa[2][8], xb[2][8];
-  if (s_begin < s_end) load_step(s_begin, xa, xb);
+  if (s_begin < s_end) {
+    if constexpr (SINGLE) issue_step(s_begin);
+    else load_step(s_begin, xa, xb);
+  }
   for (int64_t step = s_begin; step < s_end; ++step) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      if constexpr (SINGLE) {
+        words(ra[h], xa[h]);
+        words(rb[h], xb[h]);
+      }
       u32x4_t ah, al, bhh, bll;
       split8(xa[h], ah, al);
       split8(xb[h], bhh, bll);
@@ -527,7 +572,10 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
       st16(b_lo + o, bll);
     }
     __syncthreads();
-    if (step + 1 < s_end) load_step(step + 1, xa, xb);
+    if (step + 1 < s_end) {
+      if constexpr (SINGLE) issue_step(step + 1);
+      else load_step(step + 1, xa, xb);
+    }
 #pragma unroll
     for (int k2 = 0; k2 < kDmcK; k2 += 32) {
       const int kk = k2 + 8 * (lane >> 4);
@@ -661,7 +709,10 @@ hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream) {
   const int t = (p.M + kDmcTile - 1) / kDmcTile;
   const int groups = p.per_head ? p.H : 1;
   const int c8 = (p.nchunks + 7) / 8;
-  hipLaunchKernelGGL(dmc_kernel, dim3(8 * c8 * t * t, groups), dim3(kThreads), 0, stream, p);
+  if (p.ssplits == 1 && p.zsplits_d == 1)
+    hipLaunchKernelGGL(dmc_kernel<true>, dim3(8 * c8 * t * t, groups), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(dmc_kernel<false>, dim3(8 * c8 * t * t, groups), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t mm = (int64_t)p.M * p.M, n_out = (int64_t)groups * mm;

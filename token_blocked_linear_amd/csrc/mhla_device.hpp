@@ -359,6 +359,14 @@ template <int CPOL = 0>
 __device__ inline u32x4_t buf_ld16(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL));
 }
+// Buffer store: a store whose offset lies outside the range is dropped, so a lane with nothing
+// to write needs no branch.  (The vector-memory counter counts stores as well as loads and
+// drains in issue order; with a branch around stores the count differs between paths and the
+// compiler waits on the smallest count, i.e. for those stores too.)
+template <int CPOL = 0>
+__device__ inline void buf_st16(Rsrc r, uint32_t byte_off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL);
+}
 
 // Input element loaders: 8 consecutive elements starting at element index `idx` as fp32.
 template <typename T> struct In8;

@@ -130,26 +130,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // z partials of this head through a buffer resource (rows b >= M read as zero)
   const int zsp = SPLIT ? p.zsplits : 1;
   const Rsrc rsz = make_rsrc(p.z + (int64_t)bh * M * zsp * D, (uint32_t)M * zsp * D * 4u);
-  auto issue_z = [&](int zj) {
+  auto z_off = [&](int zj, int b, int s) -> uint32_t {
     const int c0 = zj * (PB / 2) + 4 * cg;
+    return (b < M && c0 < D) ? (uint32_t)((b * zsp + s) * D + c0) * 4u : kOutOfRange;
+  };
+  // A z tile is formed at once (z tiles are few): z_b[c0 .. c0 + 3] of each of the thread's rows,
+  // summed over the token slices, as (hi, lo) bf16 pairs.  Its loads are waited for here, so it
+  // leaves nothing in flight.
+  auto issue_z = [&](int zj) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int b = 8 * rg + r;
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (c0 < D) {
-        float zs[4] = {0.f, 0.f, 0.f, 0.f};
-        const int nzs = SPLIT ? p.zsplits : 1;   // the bf16 kernel's z has one token slice
-        for (int s = 0; s < nzs; ++s) {
-          const u32x4_t zz = buf_ld16(rsz, b < M ? (uint32_t)((b * nzs + s) * D + c0) * 4u : kOutOfRange);
+      float zs[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < zsp; ++s) {
+        const u32x4_t zz = buf_ld16(rsz, z_off(zj, b, s));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) zs[j] += __uint_as_float(zz[j]);
-        }
+        for (int j = 0; j < 4; ++j) zs[j] += __uint_as_float(zz[j]);
+      }
+      u32x4_t w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t h, l;
-          split_bf16(zs[j], h, l);
-          w[j] = h | (l << 16);
-        }
+      for (int j = 0; j < 4; ++j) {
+        uint32_t h, l;
+        split_bf16(zs[j], h, l);
+        w[j] = h | (l << 16);
       }
       if constexpr (SPLIT) {
         raw[2 * r] = w;                        // bf16 (hi, lo) pairs: no further split
@@ -163,11 +166,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else issue_z(t - n_tiles);
   };
 
-  int tile = blockIdx.x;
-  if (tile < last) issue_any(tile);
-  for (; tile < last; tile += p.n_wg_x) {
+  // transpose 8 rows x 8 columns into LDS: column-major with blocks contiguous
+  auto transpose = [&](int tile) {
     const bool ztile = tile >= n_tiles;
-    // transpose 8 rows x 8 columns into LDS: column-major with blocks contiguous
     if (SPLIT && !ztile) {
       // fp32 rows: row rr holds columns 0..3 in raw[2rr] and 4..7 in raw[2rr + 1]
 #pragma unroll
@@ -201,12 +202,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if constexpr (SPLIT) *reinterpret_cast<u32x4_t*>(xt_lo + rr * XP + 8 * swz(rr, rg)) = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
-    __syncthreads();
-    if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);   // in flight during the MFMAs
-    const int zbase = (tile - n_tiles) * (PB / 2);
+  };
 
-#pragma unroll 1
-    for (int cgp = wp; cgp < NCG; cgp += WPW) {
+  // Outputs through buffer resources: every lane issues the same stores on every path (rows
+  // past M and z columns past D get an out-of-range offset and are dropped; a z tile of the
+  // split kernel adds an empty store), so that the wait for the next tile's loads, which were
+  // issued before these stores, never has to include them.
+  const Rsrc ry = make_rsrc(y, (uint32_t)M * P * 2u);
+  const Rsrc ryl = make_rsrc(SPLIT ? y_lo : y, (uint32_t)M * P * 2u);
+  const Rsrc rzt = make_rsrc(p.zt + (int64_t)bh * M * D, (uint32_t)M * D * 4u);
+  auto compute_store = [&](int tile) {
+    const bool ztile = tile >= n_tiles;
+    const int zbase = (tile - n_tiles) * (PB / 2);
+    auto column_group = [&](int cgp) {
+      // the lane's row and chunk indices through an empty asm: the operand offsets below are
+      // the same for every tile, and hoisted out of the tile loop they would hold ~30 registers
+      int prv = pr, lgv = lg;
+      asm volatile("" : "+v"(prv), "+v"(lgv));
       f32x4_t accs[2][ITW];
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt)
@@ -220,8 +232,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           u32x4_t ah[2], al[2];
 #pragma unroll
           for (int pt = 0; pt < 2; ++pt) {
-            const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
-            const int ofs = r * XP + 8 * swz(r, 4 * bc + lg);
+            const int r = 32 * cgp + 8 * (prv >> 2) + 4 * pt + (prv & 3);
+            const int ofs = r * XP + 8 * swz(r, 4 * bc + lgv);
             ah[pt] = *reinterpret_cast<const u32x4_t*>(xt + ofs);
             al[pt] = *reinterpret_cast<const u32x4_t*>(xt_lo + ofs);
           }
@@ -237,8 +249,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int bc = 0; bc < NBC; ++bc)
 #pragma unroll
           for (int pt = 0; pt < 2; ++pt) {
-            const int r = 32 * cgp + 8 * (pr >> 2) + 4 * pt + (pr & 3);
-            const int ofs = r * XP + 8 * swz(r, 4 * bc + lg);
+            const int r = 32 * cgp + 8 * (prv >> 2) + 4 * pt + (prv & 3);
+            const int ofs = r * XP + 8 * swz(r, 4 * bc + lgv);
             const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + ofs);
 #pragma unroll
             for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag[a][bc], accs[pt][a]);
@@ -249,32 +261,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int q = 32 * cgp + 8 * lg;         // first of this lane's 8 tile columns
 #pragma unroll
       for (int a = 0; a < ITW; ++a) {
-        if (it0 + a >= nit) break;
-        const int i = 16 * (it0 + a) + pr;
-        if (i >= M) continue;
+        const int i = 16 * (it0 + a) + pr;     // i >= M: nothing to store
         const f32x4_t c0 = accs[0][a], c1 = accs[1][a];
         if (!ztile) {
-          const int64_t o = (int64_t)i * P + (int64_t)tile * PB + q;
+          const uint32_t o = i < M ? (uint32_t)(i * P + tile * PB + q) * 2u : kOutOfRange;
           if constexpr (SPLIT) {
             const float v[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
             uint32_t h[4], l[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) split_bf16x2(v[2 * j], v[2 * j + 1], h[j], l[j]);
-            st16(y + o, u32x4_t{h[0], h[1], h[2], h[3]});
-            st16(y_lo + o, u32x4_t{l[0], l[1], l[2], l[3]});
+            buf_st16(ry, o, u32x4_t{h[0], h[1], h[2], h[3]});
+            buf_st16(ryl, o, u32x4_t{l[0], l[1], l[2], l[3]});
           } else {
-            st16(y + o, u32x4_t{pack_bf16x2(c0[0], c0[1]), pack_bf16x2(c0[2], c0[3]),
-                                pack_bf16x2(c1[0], c1[1]), pack_bf16x2(c1[2], c1[3])});
+            buf_st16(ry, o, u32x4_t{pack_bf16x2(c0[0], c0[1]), pack_bf16x2(c0[2], c0[3]),
+                                    pack_bf16x2(c1[0], c1[1]), pack_bf16x2(c1[2], c1[3])});
           }
-        } else if (zbase + q / 2 < D) {
+        } else {
           // columns 2c, 2c+1 are hi, lo of z index zbase + c: four consecutive z~ values
-          st16(p.zt + ((int64_t)bh * M + i) * D + zbase + q / 2,
-               u32x4_t{__float_as_uint(c0[0] + c0[1]), __float_as_uint(c0[2] + c0[3]),
-                       __float_as_uint(c1[0] + c1[1]), __float_as_uint(c1[2] + c1[3])});
+          const int zi = zbase + q / 2;
+          const uint32_t o = (i < M && zi < D) ? (uint32_t)(i * D + zi) * 4u : kOutOfRange;
+          buf_st16(rzt, o,
+                   u32x4_t{__float_as_uint(c0[0] + c0[1]), __float_as_uint(c0[2] + c0[3]),
+                           __float_as_uint(c1[0] + c1[1]), __float_as_uint(c1[2] + c1[3])});
+          if constexpr (SPLIT) buf_st16(ryl, kOutOfRange, u32x4_t{0u, 0u, 0u, 0u});
         }
       }
+    };
+    if constexpr (NBC >= 2) {
+      // every wave takes all column groups (the host launches 4 waves of rows, WPW = 1): a
+      // fixed number of stores, so the wait for the next tile's loads can count them
+#pragma unroll
+      for (int cgp = 0; cgp < NCG; ++cgp) {
+        column_group(cgp);
+        __builtin_amdgcn_sched_barrier(0);     // no overlap of groups: their registers add up
+      }
+    } else {
+#pragma unroll 1
+      for (int cgp = wp; cgp < NCG; cgp += WPW) column_group(cgp);
     }
+  };
+
+  // Per tile: transpose (waits for its loads), barrier, loads of the next tile, MFMAs and
+  // stores, barrier.  The next tile's loads are in flight during the MFMAs and stores.  After
+  // the first tile's loads the same number of stores as a tile's (all dropped: out of range)
+  // is issued, so that on both paths into the loop the stores issued after the loads are
+  // counted and the transpose waits for its loads alone.
+  int tile = blockIdx.x;
+  if (tile >= last) return;
+  issue_any(tile);
+  if constexpr (NBC >= 2) {
+#pragma unroll
+    for (int j = 0; j < NCG * ITW; ++j) {
+      buf_st16(ry, kOutOfRange, u32x4_t{0u, 0u, 0u, 0u});
+      if constexpr (SPLIT) buf_st16(ryl, kOutOfRange, u32x4_t{0u, 0u, 0u, 0u});
+    }
+  }
+  while (true) {
+    transpose(tile);
     __syncthreads();
+    if (tile + p.n_wg_x < last) issue_any(tile + p.n_wg_x);
+    compute_store(tile);
+    __syncthreads();
+    tile += p.n_wg_x;
+    if (tile >= last) break;
   }
 }
 
@@ -298,6 +347,7 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stre
   const MixShape sh = mix_shape(M, split);
   const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups;
   p.wave_rows = sh.wave_rows;
+  if (NBC >= 2 && sh.wave_rows != 4) return hipErrorInvalidValue;   // the kernel assumes WPW = 1
   const int pb = 16384 / (32 * NBC);
   const int n_tiles = p.frag / pb;
   if (p.frag % pb != 0) return hipErrorInvalidValue;
