@@ -86,7 +86,8 @@ typedef enum {
                             /* near the 2e-2 bar with single bf16 operands)                      */
   MHLA_ACCURACY_BF16 = 1,   /* single bf16 MFMA operands, fp32 accumulation                     */
   MHLA_ACCURACY_SPLIT = 2   /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
-} mhla_accuracy;
+} mhla_accuracy;              /* The causal readouts always take split operands (single bf16    */
+                              /* operands leave them above the 2e-2 bar); the field is ignored.  */
 
 typedef struct {
   uint32_t struct_size;     /* = sizeof(mhla_desc)                                             */
