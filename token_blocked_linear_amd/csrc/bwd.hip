@@ -71,15 +71,15 @@ __device__ inline BwdUnit bwd_unit(const BwdParams& p, int L) {
 }
 
 // A fragment-layout summary (hi and lo) from global memory into LDS.
-template <int D>
+template <int D, int NT>
 __device__ inline void stage_frag(const uint16_t* ghi, const uint16_t* glo, uint16_t* s_hi,
                                   uint16_t* s_lo, int tid) {
   constexpr int FRAG = Dims<D>::FRAG, NCT = Dims<D>::NCT;
-  constexpr int PER = (FRAG + kThreads * 8 - 1) / (kThreads * 8);
+  constexpr int PER = (FRAG + NT * 8 - 1) / (NT * 8);
   u32x4_t th[PER], tl[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = (tid + j * kThreads) * 8;
+    const int i = (tid + j * NT) * 8;
     if (i < FRAG) {
       th[j] = ld16(ghi + i);
       tl[j] = ld16(glo + i);
@@ -87,7 +87,7 @@ __device__ inline void stage_frag(const uint16_t* ghi, const uint16_t* glo, uint
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = (tid + j * kThreads) * 8;
+    const int i = (tid + j * NT) * 8;
     if (i < FRAG) {
       st16(s_hi + lds_pos<NCT>(i), th[j]);
       st16(s_lo + lds_pos<NCT>(i), tl[j]);
@@ -101,11 +101,11 @@ __device__ inline void stage_frag(const uint16_t* ghi, const uint16_t* glo, uint
 // (kc, ct) hold T[r0 + e][c0 + j] (r0 = 32kc + 8g, c0 = 16ct + 8h); row r0 + e of the block is
 // one destination chunk, so a thread does 8 16-byte reads, an 8 x 8 transpose of 16-bit
 // elements in registers and 8 16-byte writes.
-template <int D>
+template <int D, int NT>
 __device__ inline void transpose_frag(const uint16_t* src_hi, const uint16_t* src_lo,
                                       uint16_t* dst_hi, uint16_t* dst_lo, int tid) {
   constexpr int NCT = Dims<D>::NCT, NBLK = Dims<D>::FRAG / 64;
-  for (int blk = tid; blk < 2 * NBLK; blk += kThreads) {   // the hi blocks, then the lo blocks
+  for (int blk = tid; blk < 2 * NBLK; blk += NT) {   // the hi blocks, then the lo blocks
     const bool lo = blk >= NBLK;
     const int bb = lo ? blk - NBLK : blk;
     const uint16_t* src = lo ? src_lo : src_hi;
@@ -189,8 +189,14 @@ __device__ inline void store8(T* dst, const float (&x)[8]) {
 }
 
 // ---- query side: dq, g, dz~ ----------------------------------------------------------------
+// Threads per workgroup of the tile kernels: at d = 128 the two staged summaries take 128 KB
+// of LDS, one workgroup per CU, so it runs 8 waves instead of 4.
+template <int D>
+constexpr int bwd_threads() { return D >= 128 ? 512 : kThreads; }
+
 template <typename TIn, typename TOut, int D, int PHI>
-__global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
+__global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int mode) {
+  constexpr int NT = bwd_threads<D>();
   static_assert(D >= 32, "the backward serves head sizes 32, 64 and 128");
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG, ZF = NKC * 512, NG = NCT / 2;
@@ -206,10 +212,10 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
   const Geom& geo = p.g;
   const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
 
-  stage_frag<D>(p.st_hi + U.row * FRAG, p.st_lo + U.row * FRAG, sa_hi, sa_lo, tid);
+  stage_frag<D, NT>(p.st_hi + U.row * FRAG, p.st_lo + U.row * FRAG, sa_hi, sa_lo, tid);
   if (tid < D) s_zt[tid] = p.zt[U.row * D + tid];
   __syncthreads();
-  transpose_frag<D>(sa_hi, sa_lo, sb_hi, sb_lo, tid);
+  transpose_frag<D, NT>(sa_hi, sa_lo, sb_hi, sb_lo, tid);
   build_zfrag<D>(s_zt, s_z, tid);
   __syncthreads();
 
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
   uint32_t rel;
   token_of(wave, valid, rel);
   issue(cq, cdo, valid, rel);
-  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
+  for (int tile = wave; tile < U.n_tiles; tile += NT / 64) {
 
     // phi(q): fp32 values and hi / lo operands
     float ph[NKC][8];
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
 
     bool nvalid;
     uint32_t nrel;
-    token_of(tile + kThreads / 64, nvalid, nrel);
+    token_of(tile + NT / 64, nvalid, nrel);
     In8<TIn> nq[NKC];
     In8<TOut> ndo[NG];
     issue(nq, ndo, nvalid, nrel);
@@ -343,7 +349,8 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p, int mode) {
 
 // ---- key side: dk, dv --------------------------------------------------------------------
 template <typename TIn, typename TOut, int D, int PHI>
-__global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
+__global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) {
+  constexpr int NT = bwd_threads<D>();
   static_assert(D >= 32, "the backward serves head sizes 32, 64 and 128");
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG, NG = NCT / 2;
@@ -358,10 +365,10 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
   const Geom& geo = p.g;
   const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
 
-  stage_frag<D>(p.ds_hi + U.row * FRAG, p.ds_lo + U.row * FRAG, s1_hi, s1_lo, tid);
+  stage_frag<D, NT>(p.ds_hi + U.row * FRAG, p.ds_lo + U.row * FRAG, s1_hi, s1_lo, tid);
   if (tid < D) s_dz[tid] = p.dz[U.row * D + tid];
   __syncthreads();
-  transpose_frag<D>(s1_hi, s1_lo, s2_hi, s2_lo, tid);
+  transpose_frag<D, NT>(s1_hi, s1_lo, s2_hi, s2_lo, tid);
   __syncthreads();
 
   const AOffsets ao = a_offsets(lane);
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
   uint32_t rel;
   token_of(wave, valid, rel);
   issue(ck, cv, valid, rel);
-  for (int tile = wave; tile < U.n_tiles; tile += kThreads / 64) {
+  for (int tile = wave; tile < U.n_tiles; tile += NT / 64) {
     f32x4_t acc1[NCT], acc2[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void keyside_kernel(BwdParams p) {
     }
     bool nvalid;
     uint32_t nrel;
-    token_of(tile + kThreads / 64, nvalid, nrel);
+    token_of(tile + NT / 64, nvalid, nrel);
     In8<TIn> nk[NKC], nv[NKC];
     issue(nk, nv, nvalid, nrel);
 
@@ -665,13 +672,13 @@ static hipError_t launch_bwd_t(const BwdParams& p, int mode, int n_units, bool k
     const size_t lds = keyside_lds<D>();
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(n_units), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL(kern, dim3(n_units), dim3(bwd_threads<D>()), lds, s, p);
   } else {
     auto kern = dq_kernel<TIn, TOut, D, PHI>;
     const size_t lds = dq_lds<D>();
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(n_units), dim3(kThreads), lds, s, p, mode);
+    hipLaunchKernelGGL(kern, dim3(n_units), dim3(bwd_threads<D>()), lds, s, p, mode);
   }
   return hipGetLastError();
 }
