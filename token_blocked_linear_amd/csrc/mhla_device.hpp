@@ -134,13 +134,24 @@ struct SummaryParams {
 // itw 16-row i-tiles per wave, wave_rows waves sharing a row group's i-tiles, row_groups
 // workgroups per column tile.  Shared by the host plan and the kernel launcher.
 struct MixShape {
-  int nbc, itw, wave_rows, row_groups, nitp;
+  int nbc, itw, wave_rows, row_groups, nitp, nw;
 };
 inline MixShape mix_shape(int M, bool split) {
   MixShape s;
   const int nbc = (M + 31) / 32;
   s.nbc = nbc <= 1 ? 1 : nbc <= 2 ? 2 : nbc <= 4 ? 4 : 8;
   const int nit = (M + 15) / 16;
+  s.nw = 4;
+  if (split && s.nbc == 8) {
+    // split, M > 128: one workgroup of 8 waves x 2 i-tiles covers all 256 rows, so the tile is
+    // loaded, split and transposed once (four 4-wave row groups would each do it)
+    s.nw = 8;
+    s.itw = 2;
+    s.wave_rows = 8;
+    s.row_groups = 1;
+    s.nitp = 16;
+    return s;
+  }
   const int itw = nit <= 4 || split ? 1 : (nit + 3) / 4;   // split: one i-tile per wave
   s.itw = itw <= 1 ? 1 : itw <= 2 ? 2 : 4;
   s.wave_rows = 4;
@@ -358,6 +369,9 @@ __device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
 template <int CPOL = 0>
 __device__ inline u32x4_t buf_ld16(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL));
+}
+__device__ inline u32x2_t buf_ld8(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 // Buffer store: a store whose offset lies outside the range is dropped, so a lane with nothing
 // to write needs no branch.  (The vector-memory counter counts stores as well as loads and

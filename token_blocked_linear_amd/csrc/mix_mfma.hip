@@ -30,16 +30,20 @@
 
 namespace mhla {
 
-// NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave.
-template <int NBC, int ITW, bool SPLIT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void mix_mfma_kernel(
+// NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave; NW:
+// waves per workgroup.  With NW = 8 (the split kernel at M > 128) a loader thread takes 8 rows
+// x 4 columns of the tile instead of 8 x 8, so that the tile's registers halve.
+template <int NBC, int ITW, bool SPLIT, int NW = 4>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void mix_mfma_kernel(
     MixMfmaParams p) {
-  static_assert(!SPLIT || ITW == 1, "the split kernel holds one i-tile of W per wave");
   constexpr int MPAD = 32 * NBC;
   constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
   constexpr int NCG = PB / 32;            // 32-column groups per staged tile
   constexpr int XP = MPAD;                // LDS pitch (elements) of one transposed column
-  constexpr int CG = PB / 8;              // 8-column groups per tile
+  constexpr int LC = NW == 8 ? 4 : 8;     // tile columns per loader thread
+  constexpr int CG = PB / LC;             // column groups per tile
+  static_assert(NW * 64 / CG * 8 == MPAD, "the loader threads cover the padded blocks once");
+  static_assert(NW == 4 || SPLIT, "8 waves: the split kernel only");
   // LDS bank swizzle on the 16-byte chunks (8 blocks) of a transposed column r: columns are
   // written 8 apart (r = 8*cg + e) and read 8 consecutive (r = 16*pt + pr).  With >= 8 chunks
   // per column, chunk c lives at c ^ ((r & 7) ^ ((r >> 3) & 7)); a 64-byte column (MPAD = 32)
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---------------- wave roles -------------------------------------------------------------
   // `wave_rows` waves split the workgroup's i-tiles; the remaining factor splits columns.
   const int WI = p.wave_rows;
-  const int WPW = 4 / WI;
+  const int WPW = NW / WI;
   const int wi = wave % WI, wp = wave / WI;
   const int it0 = (blockIdx.y * WI + wi) * ITW;     // first i-tile of this wave
   const int nit = (M + 15) >> 4;
@@ -68,14 +72,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // W^T operand fragments: lane holds W[16*it + pr][32*bc + 8*lg + e], e = 0..7, one 16-byte
   // load each.
   const int64_t fofs = (int64_t)(p.mcf_per_head ? bh % p.H : 0) * nitp * NBC * 512;
-  u32x4_t bfrag[ITW][NBC], bfrag_lo[SPLIT ? NBC : 1];
+  u32x4_t bfrag[ITW][NBC], bfrag_lo[SPLIT ? ITW : 1][SPLIT ? NBC : 1];
 #pragma unroll
   for (int a = 0; a < ITW; ++a)
 #pragma unroll
     for (int bc = 0; bc < NBC; ++bc) {
       const int64_t o = fofs + (((int64_t)(it0 + a) * NBC + bc) * 64 + lane) * 8;
       bfrag[a][bc] = ld16(p.mcf + o);
-      if constexpr (SPLIT) bfrag_lo[bc] = ld16(p.mcf_lo + o);
+      if constexpr (SPLIT) bfrag_lo[a][bc] = ld16(p.mcf_lo + o);
     }
 
   const int P = p.frag;
@@ -83,9 +87,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   uint16_t* y = p.y + (int64_t)bh * M * P;
   uint16_t* y_lo = SPLIT ? p.y_lo + (int64_t)bh * M * P : nullptr;
 
-  const int cg = tid % CG, rg = tid / CG;           // loader role: rows 8*rg.., columns 8*cg..
-  // raw: bf16 [row][8 columns], or for SPLIT fp32 [row][2][4 columns] summed over token slices
-  u32x4_t raw[SPLIT ? 16 : 8];
+  const int cg = tid % CG, rg = tid / CG;           // loader role: rows 8*rg.., columns LC*cg..
+  // raw: bf16 [row][8 columns], or for SPLIT fp32 [row][LC/4][4 columns] summed over token
+  // slices
+  constexpr int RW = SPLIT ? LC / 4 : 1;            // words of a row
+  u32x4_t raw[8 * RW];
   // the stack of this head through a buffer resource: rows b >= M read as zero, no branch
   const Rsrc rsx = SPLIT ? make_rsrc(p.xf + (int64_t)bh * M * p.xsplits * P, (uint32_t)M * p.xsplits * P * 4u)
                          : make_rsrc(p.x + (int64_t)bh * M * P, (uint32_t)M * P * 2u);
@@ -94,22 +100,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int b = 8 * rg + r;
-        const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits) * P + tile * PB + 8 * cg) * 4u : kOutOfRange;
+        const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits) * P + tile * PB + LC * cg) * 4u : kOutOfRange;
         // default cache policy: the row groups of a column tile run on one XCD and share it
-        raw[2 * r] = buf_ld16(rsx, o0);
-        raw[2 * r + 1] = buf_ld16(rsx, b < M ? o0 + 16u : kOutOfRange);
+#pragma unroll
+        for (int w = 0; w < RW; ++w) raw[RW * r + w] = buf_ld16(rsx, b < M ? o0 + 16u * w : kOutOfRange);
       }
       for (int s = 1; s < p.xsplits; ++s) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int b = 8 * rg + r;
-          const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits + s) * P + tile * PB + 8 * cg) * 4u : kOutOfRange;
-          const u32x4_t w0 = buf_ld16(rsx, o0);
-          const u32x4_t w1 = buf_ld16(rsx, b < M ? o0 + 16u : kOutOfRange);
+          const uint32_t o0 = b < M ? (uint32_t)((b * p.xsplits + s) * P + tile * PB + LC * cg) * 4u : kOutOfRange;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            raw[2 * r][j] = __float_as_uint(__uint_as_float(raw[2 * r][j]) + __uint_as_float(w0[j]));
-            raw[2 * r + 1][j] = __float_as_uint(__uint_as_float(raw[2 * r + 1][j]) + __uint_as_float(w1[j]));
+          for (int w = 0; w < RW; ++w) {
+            const u32x4_t x = buf_ld16(rsx, b < M ? o0 + 16u * w : kOutOfRange);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              raw[RW * r + w][j] = __float_as_uint(__uint_as_float(raw[RW * r + w][j]) + __uint_as_float(x[j]));
           }
         }
       }
@@ -130,35 +136,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // z partials of this head through a buffer resource (rows b >= M read as zero)
   const int zsp = SPLIT ? p.zsplits : 1;
   const Rsrc rsz = make_rsrc(p.z + (int64_t)bh * M * zsp * D, (uint32_t)M * zsp * D * 4u);
+  constexpr int ZW = LC / 2;                        // z values per thread and row
   auto z_off = [&](int zj, int b, int s) -> uint32_t {
-    const int c0 = zj * (PB / 2) + 4 * cg;
+    const int c0 = zj * (PB / 2) + ZW * cg;
     return (b < M && c0 < D) ? (uint32_t)((b * zsp + s) * D + c0) * 4u : kOutOfRange;
   };
-  // A z tile is formed at once (z tiles are few): z_b[c0 .. c0 + 3] of each of the thread's rows,
-  // summed over the token slices, as (hi, lo) bf16 pairs.  Its loads are waited for here, so it
-  // leaves nothing in flight.
+  auto z_load = [&](uint32_t off, float (&x)[ZW]) {
+    if constexpr (ZW == 4) {
+      const u32x4_t w = buf_ld16(rsz, off);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = __uint_as_float(w[j]);
+    } else {
+      const u32x2_t w = buf_ld8(rsz, off);
+      x[0] = __uint_as_float(w[0]);
+      x[1] = __uint_as_float(w[1]);
+    }
+  };
+  // A z tile is formed at once (z tiles are few): z_b[c0 .. c0 + ZW - 1] of each of the thread's
+  // rows, summed over the token slices, as (hi, lo) bf16 pairs.  Its loads are waited for here,
+  // so it leaves nothing in flight.
   auto issue_z = [&](int zj) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int b = 8 * rg + r;
-      float zs[4] = {0.f, 0.f, 0.f, 0.f};
+      float zs[ZW];
+#pragma unroll
+      for (int j = 0; j < ZW; ++j) zs[j] = 0.f;
       for (int s = 0; s < zsp; ++s) {
-        const u32x4_t zz = buf_ld16(rsz, z_off(zj, b, s));
+        float x[ZW];
+        z_load(z_off(zj, b, s), x);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) zs[j] += __uint_as_float(zz[j]);
+        for (int j = 0; j < ZW; ++j) zs[j] += x[j];
       }
-      u32x4_t w;
+      u32x4_t w = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < ZW; ++j) {
         uint32_t h, l;
         split_bf16(zs[j], h, l);
         w[j] = h | (l << 16);
       }
-      if constexpr (SPLIT) {
-        raw[2 * r] = w;                        // bf16 (hi, lo) pairs: no further split
-      } else {
-        raw[r] = w;
-      }
+      raw[RW * r] = w;                         // bf16 (hi, lo) pairs: no further split
     }
   };
   auto issue_any = [&](int t) {
@@ -166,38 +183,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else issue_z(t - n_tiles);
   };
 
-  // transpose 8 rows x 8 columns into LDS: column-major with blocks contiguous
+  // transpose 8 rows x LC columns into LDS: column-major with blocks contiguous
   auto transpose = [&](int tile) {
     const bool ztile = tile >= n_tiles;
     if (SPLIT && !ztile) {
-      // fp32 rows: row rr holds columns 0..3 in raw[2rr] and 4..7 in raw[2rr + 1]
+      // fp32 rows: row rr holds columns 4w .. 4w + 3 in raw[RW * rr + w]
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < LC; ++e) {
         u32x4_t col, col_lo;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           uint32_t h, l;
-          split_bf16x2(__uint_as_float(raw[4 * r + (e >> 2)][e & 3]),
-                       __uint_as_float(raw[4 * r + 2 + (e >> 2)][e & 3]), h, l);
+          split_bf16x2(__uint_as_float(raw[RW * (2 * r) + (e >> 2)][e & 3]),
+                       __uint_as_float(raw[RW * (2 * r + 1) + (e >> 2)][e & 3]), h, l);
           col[r] = h;
           col_lo[r] = l;
         }
-        const int rr = 8 * cg + e;
+        const int rr = LC * cg + e;
         *reinterpret_cast<u32x4_t*>(xt + rr * XP + 8 * swz(rr, rg)) = col;
         *reinterpret_cast<u32x4_t*>(xt_lo + rr * XP + 8 * swz(rr, rg)) = col_lo;
       }
     } else {
       // bf16 rows: word e/2 of a row holds columns e & ~1 (low half) and e | 1.  The split
-      // kernel keeps its bf16 (normaliser) rows in raw[2rr] and an all-zero low part.
+      // kernel keeps its bf16 (normaliser) rows in raw[RW * rr] and an all-zero low part.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < LC; ++e) {
         u32x4_t col;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t w0 = raw[SPLIT ? 4 * r : 2 * r][e >> 1], w1 = raw[SPLIT ? 4 * r + 2 : 2 * r + 1][e >> 1];
+          const uint32_t w0 = raw[RW * (2 * r)][e >> 1], w1 = raw[RW * (2 * r + 1)][e >> 1];
           col[r] = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
         }
-        const int rr = 8 * cg + e;
+        const int rr = LC * cg + e;
         *reinterpret_cast<u32x4_t*>(xt + rr * XP + 8 * swz(rr, rg)) = col;
         if constexpr (SPLIT) *reinterpret_cast<u32x4_t*>(xt_lo + rr * XP + 8 * swz(rr, rg)) = u32x4_t{0u, 0u, 0u, 0u};
       }
@@ -238,11 +255,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             al[pt] = *reinterpret_cast<const u32x4_t*>(xt_lo + ofs);
           }
 #pragma unroll
-          for (int pt = 0; pt < 2; ++pt) accs[pt][0] = mfma_bf16(ah[pt], bfrag[0][bc], accs[pt][0]);
+          for (int a = 0; a < ITW; ++a)
 #pragma unroll
-          for (int pt = 0; pt < 2; ++pt) accs[pt][0] = mfma_bf16(al[pt], bfrag[0][bc], accs[pt][0]);
+            for (int pt = 0; pt < 2; ++pt) accs[pt][a] = mfma_bf16(ah[pt], bfrag[a][bc], accs[pt][a]);
 #pragma unroll
-          for (int pt = 0; pt < 2; ++pt) accs[pt][0] = mfma_bf16(ah[pt], bfrag_lo[bc], accs[pt][0]);
+          for (int a = 0; a < ITW; ++a)
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) accs[pt][a] = mfma_bf16(al[pt], bfrag[a][bc], accs[pt][a]);
+#pragma unroll
+          for (int a = 0; a < ITW; ++a)
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) accs[pt][a] = mfma_bf16(ah[pt], bfrag_lo[a][bc], accs[pt][a]);
         }
       } else {
 #pragma unroll
@@ -288,8 +311,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     };
     if constexpr (NBC >= 2) {
-      // every wave takes all column groups (the host launches 4 waves of rows, WPW = 1): a
-      // fixed number of stores, so the wait for the next tile's loads can count them
+      // every wave takes all column groups (for NBC >= 2 every wave has rows of its own,
+      // WPW = 1): a fixed number of stores, so the wait for the next tile's loads can count them
 #pragma unroll
       for (int cgp = 0; cgp < NCG; ++cgp) {
         column_group(cgp);
@@ -327,14 +350,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-template <int NBC, int ITW, bool SPLIT>
+template <int NBC, int ITW, bool SPLIT, int NW>
 static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipStream_t s) {
   constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD;
   const size_t lds = (size_t)PB * XP * 2 * (SPLIT ? 2 : 1);
-  auto kern = mix_mfma_kernel<NBC, ITW, SPLIT>;
+  auto kern = mix_mfma_kernel<NBC, ITW, SPLIT, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(p.n_wg_x, row_groups, bh), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(p.n_wg_x, row_groups, bh), dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
 
@@ -345,15 +368,17 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stre
   if (split ? (!p.xf || !p.mcf_lo || !p.y_lo || p.xsplits < 1) : (!p.x || p.zsplits != 1))
     return hipErrorInvalidValue;
   const MixShape sh = mix_shape(M, split);
-  const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups;
+  const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups, NW = sh.nw;
   p.wave_rows = sh.wave_rows;
-  if (NBC >= 2 && sh.wave_rows != 4) return hipErrorInvalidValue;   // the kernel assumes WPW = 1
+  if (NBC >= 2 && sh.wave_rows != NW) return hipErrorInvalidValue;   // the kernel assumes WPW = 1
   const int pb = 16384 / (32 * NBC);
   const int n_tiles = p.frag / pb;
   if (p.frag % pb != 0) return hipErrorInvalidValue;
   const int n_all = n_tiles + (2 * p.D + pb - 1) / pb;     // summary tiles + normaliser tiles
-  // about two workgroups per CU across all heads, each striding over many column tiles
-  int want = (512 + bh * row_groups - 1) / (bh * row_groups);
+  // about two 4-wave (or one 8-wave) workgroups per CU across all heads, each striding over
+  // many column tiles
+  const int target = NW == 8 ? 256 : 512;
+  int want = (target + bh * row_groups - 1) / (bh * row_groups);
   if (want > n_all) want = n_all;
   if (want < 1) want = 1;
   // several row groups: a multiple of 8 workgroups per row group puts the row groups of one
@@ -361,10 +386,11 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stre
   // tile they all load is fetched from HBM once into that XCD's L2
   if (row_groups > 1 && want > 8) want &= ~7;
   p.n_wg_x = want;
-#define MHLA_MIX_CASE(N, I, S) \
-  if (NBC == N && ITW == I && split == S) return launch_t<N, I, S>(p, row_groups, bh, stream);
-  MHLA_MIX_CASE(1, 1, false) MHLA_MIX_CASE(2, 1, false) MHLA_MIX_CASE(4, 2, false) MHLA_MIX_CASE(8, 4, false)
-  MHLA_MIX_CASE(1, 1, true) MHLA_MIX_CASE(2, 1, true) MHLA_MIX_CASE(4, 1, true) MHLA_MIX_CASE(8, 1, true)
+#define MHLA_MIX_CASE(N, I, S, W) \
+  if (NBC == N && ITW == I && split == S && NW == W) return launch_t<N, I, S, W>(p, row_groups, bh, stream);
+  MHLA_MIX_CASE(1, 1, false, 4) MHLA_MIX_CASE(2, 1, false, 4) MHLA_MIX_CASE(4, 2, false, 4)
+  MHLA_MIX_CASE(8, 4, false, 4) MHLA_MIX_CASE(1, 1, true, 4) MHLA_MIX_CASE(2, 1, true, 4)
+  MHLA_MIX_CASE(4, 1, true, 4) MHLA_MIX_CASE(8, 2, true, 8)
 #undef MHLA_MIX_CASE
   return hipErrorInvalidValue;
 }
