@@ -177,14 +177,16 @@ __device__ inline float acc_out(const f32x4_t (&acc)[NCT], int cgp, int r) {
   return r < 4 ? acc[2 * cgp][r] : acc[2 * cgp + 1][r - 4];
 }
 
+// 8 outputs at byte offset `off` of a buffer resource (out of range: dropped)
 template <typename T>
-__device__ inline void store8(T* dst, const float (&x)[8]) {
+__device__ inline void buf_store8(Rsrc r, uint32_t off, const float (&x)[8]) {
   if constexpr (sizeof(T) == 4) {
-    st16(dst, u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
-    st16(dst + 4, u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
+    buf_st16(r, off, u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])});
+    buf_st16(r, off == kOutOfRange ? kOutOfRange : off + 16u,
+             u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])});
   } else {
-    st16(dst, u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                      pack_bf16x2(x[6], x[7])});
+    buf_st16(r, off, u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                             pack_bf16x2(x[6], x[7])});
   }
 }
 
@@ -224,35 +226,41 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
   const Rsrc rq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + U.head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rdo = make_rsrc(reinterpret_cast<const TOut*>(p.dout) + U.head_off, (uint32_t)geo.N * D * EO);
 
-  // Per tile: this lane's token (validity, element offset) and its Q, dO loads.  The next tile's
-  // loads are issued before the current tile's stores: the memory counter is in order and
-  // counts stores too, so loads issued after the stores would wait for them.
-  auto token_of = [&](int tile, bool& valid, uint32_t& rel) {
+  // Per tile: this lane's token (validity, element offset) and its Q, dO loads.  Two named
+  // buffers take turns: the next tile's loads go out after the current tile's MFMAs and before
+  // its stores, and a register copy of loaded values (which would wait for them) is never made.
+  // The stores go through buffer resources (invalid tokens: out of range, dropped) so that their
+  // number is the same on every path and the next wait counts them exactly.
+  struct TileBuf {
+    In8<TIn> q[NKC];
+    In8<TOut> d[NG];
+    bool valid;
+    uint32_t rel;
+  };
+  auto load_tile = [&](TileBuf& b, int tile) {
     const int32_t j = U.j_begin + tile * 16 + pr;
-    valid = tile < U.n_tiles && j < U.j_end;
-    rel = valid ? (uint32_t)(U.base_tok + block_offset(geo, U.bg, (uint32_t)j)) * D : 0u;
-  };
-  auto issue = [&](In8<TIn> (&cq)[NKC], In8<TOut> (&cdo)[NG], bool valid, uint32_t rel) {
+    b.valid = tile < U.n_tiles && j < U.j_end;
+    b.rel = b.valid ? (uint32_t)(U.base_tok + block_offset(geo, U.bg, (uint32_t)j)) * D : 0u;
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) cq[kc].template load_buf<0>(rq, valid ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange);
+    for (int kc = 0; kc < NKC; ++kc)
+      b.q[kc].template load_buf<0>(rq, b.valid ? (b.rel + 32 * kc + 8 * lg) * ES : kOutOfRange);
 #pragma unroll
-    for (int c = 0; c < NG; ++c) cdo[c].template load_buf<0>(rdo, valid ? (rel + 32 * c + 8 * lg) * EO : kOutOfRange);
+    for (int c = 0; c < NG; ++c)
+      b.d[c].template load_buf<0>(rdo, b.valid ? (b.rel + 32 * c + 8 * lg) * EO : kOutOfRange);
   };
-  In8<TIn> cq[NKC];
-  In8<TOut> cdo[NG];
-  bool valid;
-  uint32_t rel;
-  token_of(wave, valid, rel);
-  issue(cq, cdo, valid, rel);
-  for (int tile = wave; tile < U.n_tiles; tile += NT / 64) {
+  const Rsrc rdq = make_rsrc(reinterpret_cast<TOut*>(p.dq) + U.head_off, (uint32_t)geo.N * D * EO);
+  const Rsrc rts = make_rsrc(p.tok_scale + (int64_t)U.bh * geo.N, (uint32_t)geo.N * 4u);
+  const Rsrc rtz = make_rsrc(p.tok_zw + (int64_t)U.bh * geo.N, (uint32_t)geo.N * 4u);
 
+  // one tile: `next` is loaded once this tile's MFMAs are issued
+  auto process = [&](const TileBuf& cur, TileBuf& next, int next_tile) {
     // phi(q): fp32 values and hi / lo operands
     float ph[NKC][8];
     u32x4_t bqh[NKC], bql[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ph[kc][e] = phi_map<PHI>(cq[kc].get(e));
+      for (int e = 0; e < 8; ++e) ph[kc][e] = phi_map<PHI>(cur.q[kc].get(e));
       split8(ph[kc], bqh[kc], bql[kc]);
     }
     // num = S~^T q~, den = q~ . z~
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
       for (int c = 0; c < NG; ++c)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const float d_o = cdo[c].get(r);
+          const float d_o = cur.d[c].get(r);
           part = fmaf(d_o, acc_out<NCT>(acc, c, r) * inv, part);
           g[c][r] = d_o * inv;
         }
@@ -291,9 +299,9 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
 #pragma unroll
       for (int c = 0; c < NG; ++c)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) g[c][r] = cdo[c].get(r);
+        for (int r = 0; r < 8; ++r) g[c][r] = cur.d[c].get(r);
     }
-    if (!valid) {                     // tokens past the slice contribute nothing
+    if (!cur.valid) {                 // tokens past the slice contribute nothing
       gden = 0.f;
 #pragma unroll
       for (int c = 0; c < NG; ++c)
@@ -313,37 +321,31 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    bool nvalid;
-    uint32_t nrel;
-    token_of(tile + NT / 64, nvalid, nrel);
-    In8<TIn> nq[NKC];
-    In8<TOut> ndo[NG];
-    issue(nq, ndo, nvalid, nrel);
+    load_tile(next, next_tile);
 
-    if (valid) {
-      const int64_t row = U.head_off + rel;
 #pragma unroll
-      for (int c = 0; c < NG; ++c) {
-        const int f0 = 32 * c + 8 * lg;
-        float out[8];
+    for (int c = 0; c < NG; ++c) {
+      const int f0 = 32 * c + 8 * lg;
+      float out[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-          out[r] = (acc_out<NCT>(acc2, c, r) + s_zt[f0 + r] * gden) * dphi_map<PHI>(cq[c].get(r));
-        store8(reinterpret_cast<TOut*>(p.dq) + row + f0, out);
-      }
-      // the token's weights for dS~ and dz~ (kscale = 1/den, zw = gden * den = -(dO . o))
-      if (lg == 0) {
-        const int64_t t = (int64_t)U.bh * geo.N + rel / D;
-        p.tok_scale[t] = inv;
-        p.tok_zw[t] = -part;
-      }
+      for (int r = 0; r < 8; ++r)
+        out[r] = (acc_out<NCT>(acc2, c, r) + s_zt[f0 + r] * gden) * dphi_map<PHI>(cur.q[c].get(r));
+      buf_store8<TOut>(rdq, cur.valid ? (cur.rel + f0) * EO : kOutOfRange, out);
     }
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) cq[kc] = nq[kc];
-#pragma unroll
-    for (int c = 0; c < NG; ++c) cdo[c] = ndo[c];
-    valid = nvalid;
-    rel = nrel;
+    // the token's weights for dS~ and dz~ (kscale = 1/den, zw = gden * den = -(dO . o)), one
+    // lane per token
+    const uint32_t toff = (cur.valid && lg == 0) ? (cur.rel / D) * 4u : kOutOfRange;
+    buf_st4(rts, toff, __float_as_uint(inv));
+    buf_st4(rtz, toff, __float_as_uint(-part));
+  };
+
+  constexpr int STEP = NT / 64;
+  TileBuf bufA, bufB;
+  load_tile(bufA, wave);
+  for (int tile = wave; tile < U.n_tiles; tile += 2 * STEP) {
+    process(bufA, bufB, tile + STEP);
+    if (tile + STEP >= U.n_tiles) break;
+    process(bufB, bufA, tile + 2 * STEP);
   }
 }
 
@@ -376,26 +378,28 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
   const Rsrc rk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + U.head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + U.head_off, (uint32_t)geo.N * D * ES);
 
-  // next tile's K, V loads before the current tile's stores (see dq_kernel)
-  auto token_of = [&](int tile, bool& valid, uint32_t& rel) {
-    const int32_t j = U.j_begin + tile * 16 + pr;
-    valid = tile < U.n_tiles && j < U.j_end;
-    rel = valid ? (uint32_t)(U.base_tok + block_offset(geo, U.bg, (uint32_t)j)) * D : 0u;
+  // two named tile buffers and buffer-resource stores, as in dq_kernel
+  struct TileBuf {
+    In8<TIn> k[NKC], v[NKC];
+    bool valid;
+    uint32_t rel;
   };
-  auto issue = [&](In8<TIn> (&ck)[NKC], In8<TIn> (&cv)[NKC], bool valid, uint32_t rel) {
+  auto load_tile = [&](TileBuf& b, int tile) {
+    const int32_t j = U.j_begin + tile * 16 + pr;
+    b.valid = tile < U.n_tiles && j < U.j_end;
+    b.rel = b.valid ? (uint32_t)(U.base_tok + block_offset(geo, U.bg, (uint32_t)j)) * D : 0u;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      const uint32_t off = valid ? (rel + 32 * kc + 8 * lg) * ES : kOutOfRange;
-      ck[kc].template load_buf<0>(rk, off);
-      cv[kc].template load_buf<0>(rv, off);
+      const uint32_t off = b.valid ? (b.rel + 32 * kc + 8 * lg) * ES : kOutOfRange;
+      b.k[kc].template load_buf<0>(rk, off);
+      b.v[kc].template load_buf<0>(rv, off);
     }
   };
-  In8<TIn> ck[NKC], cv[NKC];
-  bool valid;
-  uint32_t rel;
-  token_of(wave, valid, rel);
-  issue(ck, cv, valid, rel);
-  for (int tile = wave; tile < U.n_tiles; tile += NT / 64) {
+  constexpr uint32_t EO = sizeof(TOut);
+  const Rsrc rdk = make_rsrc(reinterpret_cast<TOut*>(p.dk) + U.head_off, (uint32_t)geo.N * D * EO);
+  const Rsrc rdv = make_rsrc(reinterpret_cast<TOut*>(p.dv) + U.head_off, (uint32_t)geo.N * D * EO);
+
+  auto process = [&](const TileBuf& cur, TileBuf& next, int next_tile) {
     f32x4_t acc1[NCT], acc2[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -407,51 +411,48 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
       // dv = dS_b^T phi(k): contraction over key features
       float ph[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ph[e] = phi_map<PHI>(ck[kc].get(e));
+      for (int e = 0; e < 8; ++e) ph[e] = phi_map<PHI>(cur.k[kc].get(e));
       u32x4_t bh, bl;
       split8(ph, bh, bl);
       frag_mfma<D, true>(acc1, s1_hi, s1_lo, ao, kc, bh, bl);
       // dk~ = dS_b v: contraction over value channels (bf16 V is exact in one operand)
       if constexpr (sizeof(TIn) == 2) {
-        frag_mfma<D, false>(acc2, s2_hi, s2_lo, ao, kc, cv[kc].w, cv[kc].w);
+        frag_mfma<D, false>(acc2, s2_hi, s2_lo, ao, kc, cur.v[kc].w, cur.v[kc].w);
       } else {
         float vv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e] = cv[kc].get(e);
+        for (int e = 0; e < 8; ++e) vv[e] = cur.v[kc].get(e);
         u32x4_t vh, vl;
         split8(vv, vh, vl);
         frag_mfma<D, true>(acc2, s2_hi, s2_lo, ao, kc, vh, vl);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    bool nvalid;
-    uint32_t nrel;
-    token_of(tile + NT / 64, nvalid, nrel);
-    In8<TIn> nk[NKC], nv[NKC];
-    issue(nk, nv, nvalid, nrel);
 
-    if (valid) {
-      const int64_t row = U.head_off + rel;
+    load_tile(next, next_tile);
+
 #pragma unroll
-      for (int c = 0; c < NG; ++c) {
-        const int f0 = 32 * c + 8 * lg;
-        float dvo[8], dko[8];
+    for (int c = 0; c < NG; ++c) {
+      const int f0 = 32 * c + 8 * lg;
+      float dvo[8], dko[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          dvo[r] = acc_out<NCT>(acc1, c, r);
-          dko[r] = (acc_out<NCT>(acc2, c, r) + s_dz[f0 + r]) * dphi_map<PHI>(ck[c].get(r));
-        }
-        store8(reinterpret_cast<TOut*>(p.dv) + row + f0, dvo);
-        store8(reinterpret_cast<TOut*>(p.dk) + row + f0, dko);
+      for (int r = 0; r < 8; ++r) {
+        dvo[r] = acc_out<NCT>(acc1, c, r);
+        dko[r] = (acc_out<NCT>(acc2, c, r) + s_dz[f0 + r]) * dphi_map<PHI>(cur.k[c].get(r));
       }
+      const uint32_t off = cur.valid ? (cur.rel + f0) * EO : kOutOfRange;
+      buf_store8<TOut>(rdv, off, dvo);
+      buf_store8<TOut>(rdk, off, dko);
     }
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      ck[kc] = nk[kc];
-      cv[kc] = nv[kc];
-    }
-    valid = nvalid;
-    rel = nrel;
+  };
+
+  constexpr int STEP = NT / 64;
+  TileBuf bufA, bufB;
+  load_tile(bufA, wave);
+  for (int tile = wave; tile < U.n_tiles; tile += 2 * STEP) {
+    process(bufA, bufB, tile + STEP);
+    if (tile + STEP >= U.n_tiles) break;
+    process(bufB, bufA, tile + 2 * STEP);
   }
 }
 

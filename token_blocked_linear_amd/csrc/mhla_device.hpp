@@ -381,6 +381,9 @@ template <int CPOL = 0>
 __device__ inline void buf_st16(Rsrc r, uint32_t byte_off, u32x4_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL);
 }
+__device__ inline void buf_st4(Rsrc r, uint32_t byte_off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_off, 0, 0);
+}
 
 // Input element loaders: 8 consecutive elements starting at element index `idx` as fp32.
 template <typename T> struct In8;
