@@ -39,22 +39,24 @@ __device__ inline f32x4_t mfma16_bf16(const u32x2_t& a, const u32x2_t& b, f32x4_
                                                    c, 0, 0, 0);
 }
 
-template <int D>
+// VSPLIT: fp32 V (hi / lo V^T in LDS).  At d = 128 a 64-token sub-chunk fits the LDS with
+// bf16 V (156 KB) and halves the sub-chunk steps (and their barriers); fp32 V takes 32.
+template <int D, bool VSPLIT>
 struct CausalShape {
   static constexpr int NW = D >= 128 ? 8 : 4;      // waves per workgroup
   static constexpr int NT = 64 * NW;               // threads per workgroup
-  static constexpr int SUB = D >= 128 ? 32 : 64;   // tokens per sub-chunk
+  static constexpr int SUB = D >= 128 && VSPLIT ? 32 : 64;   // tokens per sub-chunk
   static constexpr int QT = SUB / 16;              // query tiles per sub-chunk
   static constexpr int WQ = NW / QT;               // waves per query tile (channel pairs split)
   static constexpr int KP = D + 8;                 // LDS pitch of row-major phi(K) (elements)
   static constexpr int TP = SUB + 8;               // LDS pitch of the transposed tiles
 };
 
-template <int D>
-constexpr size_t causal_lds_bytes(bool v_split) {
-  using CS = CausalShape<D>;
+template <int D, bool VSPLIT>
+constexpr size_t causal_lds_bytes() {
+  using CS = CausalShape<D, VSPLIT>;
   return (size_t)2 * (2 * Dims<D>::FRAG + Dims<D>::NKC * 512 + 2 * CS::SUB * CS::KP + 2 * D * CS::TP +
-                      (v_split ? 2 : 1) * D * CS::TP);
+                      (VSPLIT ? 2 : 1) * D * CS::TP);
 }
 
 template <typename TOut>
@@ -69,10 +71,10 @@ __device__ inline void store8_out(TOut* dst, const float (&x)[8]) {
 }
 
 template <typename TIn, typename TOut, int D, int PHI>
-__global__ __launch_bounds__(CausalShape<D>::NT) void causal_kernel(CausalParams p) {
+__global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal_kernel(CausalParams p) {
   static_assert(D >= 32, "the causal readout serves head sizes 32, 64 and 128");
   using Dm = Dims<D>;
-  using CS = CausalShape<D>;
+  using CS = CausalShape<D, sizeof(TIn) == 4>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
   constexpr int SUB = CS::SUB, QT = CS::QT, WQ = CS::WQ, KP = CS::KP, TP = CS::TP, NW = CS::NW;
   constexpr bool VSPLIT = sizeof(TIn) == 4;     // fp32 V needs hi / lo; bf16 V is exact
@@ -421,10 +423,10 @@ __global__ __launch_bounds__(kThreads) void slice_prefix_kernel(float* ps, float
 template <int PHI, typename TIn, typename TOut, int D>
 static hipError_t launch_causal_t(const CausalParams& p, int n_units, hipStream_t s) {
   auto kern = causal_kernel<TIn, TOut, D, PHI>;
-  const size_t lds = causal_lds_bytes<D>(sizeof(TIn) == 4);
+  const size_t lds = causal_lds_bytes<D, sizeof(TIn) == 4>();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(n_units), dim3(CausalShape<D>::NT), lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(n_units), dim3(CausalShape<D, sizeof(TIn) == 4>::NT), lds, s, p);
   return hipGetLastError();
 }
 
