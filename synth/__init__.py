@@ -35,7 +35,7 @@ __all__ = [
     "Workload", "WORKLOADS", "get_workload", "block_grid_shape", "num_blocks",
     "round_to_bf16", "bf16_bits", "bits_to_f32",
     "mc_softmax_l1", "mc_locality_init", "mc_softmax_l1_noisy_clipped", "mc_softmax_gaussian",
-    "make_inputs", "make_mc", "make_grad_output",
+    "make_inputs", "make_mc", "make_grad_output", "standard_normal_parallel",
 ]
 
 
@@ -127,6 +127,26 @@ def bits_to_f32(bits: np.ndarray) -> np.ndarray:
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """float32 array holding the bf16-rounded values of ``x``."""
     return bits_to_f32(bf16_bits(x))
+
+
+def standard_normal_parallel(shape, seed: int, bf16: bool, threads: int = 16) -> np.ndarray:
+    """Large inputs: float32 N(0, 1) of ``shape`` drawn in chunks of 2^24 values, chunk c from
+    ``default_rng(SeedSequence(seed).spawn(n_chunks)[c])``, filled by ``threads`` threads (the
+    generators release the GIL); rounded to bf16 (RNE) chunk by chunk when ``bf16``."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = int(np.prod(shape))
+    chunk = 1 << 24
+    seqs = np.random.SeedSequence(seed).spawn((n + chunk - 1) // chunk)
+    out = np.empty(n, np.float32)
+
+    def fill(c):
+        lo, hi = c * chunk, min(n, (c + 1) * chunk)
+        x = np.random.default_rng(seqs[c]).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = round_to_bf16(x) if bf16 else x
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill, range(len(seqs))))
+    return out.reshape(shape)
 
 
 # --------------------------------------------------------------------------------------

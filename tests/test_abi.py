@@ -131,6 +131,18 @@ def test_ragged_blocks_and_cls_token_geometry():
     assert _status(_desc(block=(64, 64), readout="mala", cls_token=True)) == 2
 
 
+def test_size_limits():
+    """One head's bytes (N * d * 4 < 2^31), the (batch, head) pairs and the blocks (<= 65535)."""
+    _lib_or_skip()
+    n_max = (1 << 31) // (128 * 4) - 1
+    assert _status(_desc(grid=(n_max,), block=(n_max,), batch=1, heads=1, head_dim=128)) == 0
+    assert _status(_desc(grid=(n_max + 1,), block=(n_max + 1,), batch=1, heads=1, head_dim=128)) == 3
+    assert _status(_desc(grid=(8,), block=(4,), batch=65535, heads=1, head_dim=32)) == 0
+    assert _status(_desc(grid=(8,), block=(4,), batch=65536, heads=1, head_dim=32)) == 3
+    assert _status(_desc(grid=(65535,), block=(1,), batch=1, heads=1, head_dim=32)) == 0
+    assert _status(_desc(grid=(65536,), block=(1,), batch=1, heads=1, head_dim=32)) == 3
+
+
 def test_create_null_arguments():
     lib = _lib_or_skip()
     h = ctypes.c_void_p()
