@@ -17,6 +17,10 @@ WRITE_SIZE hardware counters, each scaled by what the counter reads for a plain 
 size), taken from profiles/traffic.md when that record was made from the current kernel sources
 (same digest of the csrc/ files and the header), else null.
 
+Beside the spec peaks (8 TB/s, 2.5 PFLOP/s bf16) the roofline object carries two rates measured
+in the same run: a 1 GiB device copy (`measured_copy_GBps`, read + write bytes) and a dense
+8192^3 bf16 GEMM through torch (`measured_bf16_gemm_TFLOPs`).
+
 `causal` times the chunkwise-causal forward (1D workloads) on the same inputs.
 `backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the same
 inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
@@ -77,6 +81,27 @@ def measured_traffic(workload: str, kernel: str, out_dtype: str):
             if (r.get("workload"), r.get("kernel"), r.get("out_dtype")) == (workload, kernel, out_dtype):
                 return r["hbm_bytes_per_launch"] if r.get("source_digest") == digest else None
     return None
+
+
+def measured_gemm_TFLOPs(n: int = 8192, reps: int = 10) -> float:
+    """Dense bf16 GEMM rate measured now (torch.matmul of two contiguous n x n bf16 matrices,
+    fp32 accumulation in the library): the practical MFMA ceiling, reported beside the spec peak."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.float32, generator=g).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.float32, generator=g).to(torch.bfloat16).contiguous()
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / t / 1e12
 
 
 def measured_copy_GBps(n_bytes: int = 1 << 30, reps: int = 10) -> float:
@@ -385,9 +410,13 @@ def main():
                 "alg_flops_per_launch": a["flops"], "mean_launch_us": pk["us"]}
 
     copy_bw = measured_copy_GBps()
+    gemm_tf = measured_gemm_TFLOPs()
+    roof["measured_copy_GBps"] = round(copy_bw, 1)
+    roof["measured_bf16_gemm_TFLOPs"] = round(gemm_tf, 1)
     if roof["unit"] == "GB/s":
-        roof["measured_copy_GBps"] = round(copy_bw, 1)
         roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_bw, 4)
+    elif roof["bound"] == "mfma":
+        roof["frac_of_measured_gemm"] = round(roof["achieved"] / gemm_tf, 4)
 
     others = {}
     if args.all:
