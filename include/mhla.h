@@ -86,8 +86,9 @@ typedef enum {
                             /* near the 2e-2 bar with single bf16 operands)                      */
   MHLA_ACCURACY_BF16 = 1,   /* single bf16 MFMA operands, fp32 accumulation                     */
   MHLA_ACCURACY_SPLIT = 2   /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
-} mhla_accuracy;              /* The causal readouts always take split operands (single bf16    */
-                              /* operands leave them above the 2e-2 bar); the field is ignored.  */
+} mhla_accuracy;              /* The causal readouts: the field sets the summaries and the mixing */
+                              /* of the earlier blocks; the running in-block state and scores are */
+                              /* always split (single bf16 there leaves them above the 2e-2 bar). */
 
 typedef struct {
   uint32_t struct_size;     /* = sizeof(mhla_desc)                                             */

@@ -71,6 +71,20 @@ def test_causal_small(w):
     assert err <= _tol(w), (w.name, err)
 
 
+@pytest.mark.parametrize("name", ["c_m4", "c_d128_m16", "c_m300_valu"])
+def test_causal_split_accuracy_option(name):
+    """bf16 inputs with ELU+1: the default takes single bf16 operands for the earlier blocks'
+    summaries and mixing; MHLA_ACCURACY_SPLIT splits them too and must be tighter."""
+    w = next(c for c in CASES if c.name == name)
+    announce(f"causal {w.name} accuracy auto / split")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    want = oracle_full(w, q, k, v, mc)
+    e_auto = causal_err(run_hip(w, q, k, v, mc), want)
+    e_split = causal_err(run_hip(w, q, k, v, mc, accuracy="split"), want)
+    print(f"  auto={e_auto:.3e} split={e_split:.3e}")
+    assert e_auto <= BF16_TOL and e_split <= 1e-3 and e_split < e_auto
+
+
 def test_causal_per_head_mc_and_upper_triangle_unused():
     w = W("c_per_head", "bf16", 2, 3, 64, 768, 128, 221, "none")
     announce(w.name)

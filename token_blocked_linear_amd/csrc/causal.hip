@@ -133,7 +133,8 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
     const int pos = (fr * 64 + lane) * 8;
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (p.st_hi) {
-      const u32x4_t h = ld16(p.st_hi + row * FRAG + pos), l = ld16(p.st_lo + row * FRAG + pos);
+      const u32x4_t h = ld16(p.st_hi + row * FRAG + pos);
+      const u32x4_t l = p.st_lo ? ld16(p.st_lo + row * FRAG + pos) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t hw = h[e >> 1], lw = l[e >> 1];

@@ -230,7 +230,7 @@ struct CausalParams {
   const void* v;
   void* o;                 // [BH][N][D] output type
   const uint16_t* st_hi;   // S~<_i fragments (hi, lo) [BH][M][FRAG]; NULL when M == 1
-  const uint16_t* st_lo;
+  const uint16_t* st_lo;   // NULL also after the bf16 mixing (single bf16 operands)
   const float* zt;         // z~<_i [BH][M][D]; NULL when M == 1
   const float* pre;        // exclusive prefix over token slices of the block's partial summaries
   const float* prez;       //   [BH][M][splits][FRAG] and [..][D]; NULL with one slice per block

@@ -206,9 +206,9 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   P->mala = d->readout == MHLA_READOUT_MALA;
   P->causal = causal;
   P->mode = d->readout;
-  if (causal)
-    P->split = true;   // the causal readout always runs on split operands
-  else if (d->accuracy == MHLA_ACCURACY_SPLIT)
+  // The causal kernel keeps its running state and in-sub-chunk scores split whatever this says;
+  // `split` sets the precision of the summaries and the mixing (of the earlier blocks, there).
+  if (d->accuracy == MHLA_ACCURACY_SPLIT)
     P->split = true;
   else if (d->accuracy == MHLA_ACCURACY_BF16)
     P->split = false;
@@ -453,7 +453,8 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
       cp.v = v;
       cp.o = o;
       cp.st_hi = mix_kernel ? st_hi : nullptr;
-      cp.st_lo = mix_kernel ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo) : nullptr;
+      cp.st_lo = mix_kernel && (h->split || h->mix_split) ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo)
+                                                         : nullptr;   // bf16 mixing: no low parts
       cp.zt = mix_kernel ? zt : nullptr;
       cp.pre = h->sum_splits > 1 ? ps : nullptr;
       cp.prez = h->sum_splits > 1 ? pz : nullptr;
