@@ -355,6 +355,7 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
         store8_out(reinterpret_cast<TOut*>(p.o) + head_off + qrel + c0, o);
       }
     }
+    if (j0 + SUB >= j_end) break;   // the last sub-chunk: no later readout needs the state
     __syncthreads();   // the readout is done with the state fragments and the staged tiles
 
     // ---- the state absorbs the sub-chunk: sacc += (m_ii phi(K))^T V, z += (m_ii phi(K))^T 1 ----
