@@ -54,6 +54,10 @@ CASES = [
     W("c_relu", "bf16", 1, 2, 64, 1024, 256, 216, phi="relu"),
     W("c_exp", "bf16", 1, 2, 64, 1024, 256, 217, phi="exp"),
     W("c_exp_d128", "bf16", 1, 2, 128, 1024, 128, 218, phi="exp"),
+    # many heads with fp32 inputs: the outputs with only a few keys in view (the first tokens)
+    # carry the in-sub-chunk products' rounding without averaging
+    W("c_fp32_heads_d64", "fp32", 8, 16, 64, 512, 128, 219),
+    W("c_fp32_heads_d128", "fp32", 32, 16, 128, 128, 128, 220, "none"),
 ]
 
 

@@ -22,7 +22,10 @@
 //      result = k of the 16x16x16 operand); the score sums give the in-chunk normaliser;
 //   3. the state absorbs the sub-chunk: acc += (m_ii phi(K))^T V on MFMA (permuted A rows so
 //      each lane owns 8 consecutive fragment elements), rewritten as hi / lo fragments.
-// Every product uses hi / lo bf16 operand splits (bf16 V is exact): about fp32 accuracy.
+// The readout and update of the state use hi / lo bf16 operand splits (bf16 V is exact).  With
+// bf16 inputs the in-sub-chunk scores and V^T P do too; with fp32 inputs they run on fp32 MFMAs
+// (16x16x4) over fp32 phi(K) and V tiles, since an output with few keys in view averages no
+// rounding error away.
 #include <type_traits>
 
 #include "frag_lds.hpp"
@@ -39,7 +42,13 @@ __device__ inline f32x4_t mfma16_bf16(const u32x2_t& a, const u32x2_t& b, f32x4_
                                                    c, 0, 0, 0);
 }
 
-// VSPLIT: fp32 V (hi / lo V^T in LDS).  At d = 128 a 64-token sub-chunk fits the LDS with
+// v_mfma_f32_16x16x4_f32: A lane l = row l%16, k = l/16; B lane l = k l/16, column l%16; D as
+// above.
+__device__ inline f32x4_t mfma4_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// VSPLIT: fp32 inputs (fp32 phi(K) and V^T tiles in LDS, in the space of the hi / lo planes).  At d = 128 a 64-token sub-chunk fits the LDS with
 // bf16 V (156 KB) and halves the sub-chunk steps (and their barriers); fp32 V takes 32.
 template <int D, bool VSPLIT>
 struct CausalShape {
@@ -96,6 +105,9 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
   uint16_t* kt_lo = kt_hi + D * TP;
   uint16_t* vt_hi = kt_lo + D * TP;             // V^T [D][TP]
   uint16_t* vt_lo = vt_hi + D * TP;             // (fp32 V only)
+  // fp32 inputs: phi(K) row-major [SUB][KP] and V^T [D][TP] as fp32, over the hi / lo planes
+  float* kr32 = reinterpret_cast<float*>(kr_hi);
+  float* vt32 = reinterpret_cast<float*>(vt_hi);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
   const Geom& geo = p.g;
@@ -232,7 +244,13 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
         const bool ok = j0 + 2 * tp + i < j_end;
 #pragma unroll
         for (int e = 0; e < 8; ++e) kf[i][e] = ok ? phi_map<PHI>(ck[i].get(e)) : 0.f;
-        store_frag8<true>(kr_hi, kr_lo, (2 * tp + i) * KP + 8 * fg, kf[i]);
+        if constexpr (VSPLIT) {
+          float* dst = kr32 + (2 * tp + i) * KP + 8 * fg;
+          *reinterpret_cast<float4*>(dst) = make_float4(kf[i][0], kf[i][1], kf[i][2], kf[i][3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(kf[i][4], kf[i][5], kf[i][6], kf[i][7]);
+        } else {
+          store_frag8<true>(kr_hi, kr_lo, (2 * tp + i) * KP + 8 * fg, kf[i]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -242,9 +260,7 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
         *reinterpret_cast<uint32_t*>(kt_hi + at) = h;
         *reinterpret_cast<uint32_t*>(kt_lo + at) = l;
         if constexpr (VSPLIT) {
-          split_bf16x2(cv[0].get(e), cv[1].get(e), h, l);
-          *reinterpret_cast<uint32_t*>(vt_hi + at) = h;
-          *reinterpret_cast<uint32_t*>(vt_lo + at) = l;
+          *reinterpret_cast<float2*>(vt32 + at) = make_float2(cv[0].get(e), cv[1].get(e));
         } else {
           *reinterpret_cast<uint32_t*>(vt_hi + at) = cv[0].bits(e) | (cv[1].bits(e) << 16);   // exact
         }
@@ -258,18 +274,25 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
     const bool qvalid = jq < j_end;
     const uint32_t qrel = qvalid ? (uint32_t)(base_tok + block_offset(geo, bgeo, (uint32_t)jq)) * D : 0u;
     u32x4_t bq_hi[NKC], bq_lo[NKC];
+    float qf[NKC][8];                          // fp32 inputs: phi(q) for the in-sub-chunk scores
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t h, l;
-        split_bf16x2(phi_map<PHI>(cq[kc].get(2 * i)), phi_map<PHI>(cq[kc].get(2 * i + 1)), h, l);
+        const float q0 = phi_map<PHI>(cq[kc].get(2 * i)), q1 = phi_map<PHI>(cq[kc].get(2 * i + 1));
+        if constexpr (VSPLIT) {
+          qf[kc][2 * i] = q0;
+          qf[kc][2 * i + 1] = q1;
+        }
+        split_bf16x2(q0, q1, h, l);
         bq_hi[kc][i] = h;
         bq_lo[kc][i] = l;
       }
     // cq is free now: the next sub-chunk's queries go straight into it (a register copy of
-    // loaded values would make the loop wait for every outstanding load and store)
-    issue_q(cq, j0 + SUB);
+    // loaded values would make the loop wait for every outstanding load and store); with fp32
+    // inputs once the scores are done, so that phi(q) takes cq's registers meanwhile
+    if constexpr (!VSPLIT) issue_q(cq, j0 + SUB);
     f32x4_t accz = {0.f, 0.f, 0.f, 0.f};
     f32x4_t acc[2 * PPW];
 #pragma unroll
@@ -301,11 +324,25 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const int off = (16 * kt + pr) * KP + 32 * kc + 8 * lg;
-        const u32x4_t kh = *reinterpret_cast<const u32x4_t*>(kr_hi + off);
-        const u32x4_t kl = *reinterpret_cast<const u32x4_t*>(kr_lo + off);
-        sc = mfma_bf16(kh, bq_hi[kc], sc);
-        sc = mfma_bf16(kl, bq_hi[kc], sc);
-        sc = mfma_bf16(kh, bq_lo[kc], sc);
+        if constexpr (VSPLIT) {
+          // k index lg of step e = feature 32 kc + 8 lg + e, on both operands
+          const float4 k0 = *reinterpret_cast<const float4*>(kr32 + off);
+          const float4 k1 = *reinterpret_cast<const float4*>(kr32 + off + 4);
+          sc = mfma4_f32(k0.x, qf[kc][0], sc);
+          sc = mfma4_f32(k0.y, qf[kc][1], sc);
+          sc = mfma4_f32(k0.z, qf[kc][2], sc);
+          sc = mfma4_f32(k0.w, qf[kc][3], sc);
+          sc = mfma4_f32(k1.x, qf[kc][4], sc);
+          sc = mfma4_f32(k1.y, qf[kc][5], sc);
+          sc = mfma4_f32(k1.z, qf[kc][6], sc);
+          sc = mfma4_f32(k1.w, qf[kc][7], sc);
+        } else {
+          const u32x4_t kh = *reinterpret_cast<const u32x4_t*>(kr_hi + off);
+          const u32x4_t kl = *reinterpret_cast<const u32x4_t*>(kr_lo + off);
+          sc = mfma_bf16(kh, bq_hi[kc], sc);
+          sc = mfma_bf16(kl, bq_hi[kc], sc);
+          sc = mfma_bf16(kh, bq_lo[kc], sc);
+        }
       }
       // lane: keys 16kt + 4lg + r, query 16qt + pr (positions within the sub-chunk)
       float pv[4];
@@ -314,30 +351,41 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
         pv[rr] = (16 * kt + 4 * lg + rr <= 16 * qt + pr) ? mii * sc[rr] : 0.f;
         dsum += pv[rr];
       }
-      u32x2_t ph, pl;
-      {
-        uint32_t h0, l0, h1, l1;
-        split_bf16x2(pv[0], pv[1], h0, l0);
-        split_bf16x2(pv[2], pv[3], h1, l1);
-        ph = u32x2_t{h0, h1};
-        pl = u32x2_t{l0, l1};
-      }
+      if constexpr (VSPLIT) {
 #pragma unroll
-      for (int t = 0; t < 2 * PPW; ++t) {
-        const int ct = 2 * cp * PPW + t;
-        // A row pr of tile ct is channel 32 (ct / 2) + 8 (pr / 4) + 4 (ct % 2) + pr % 4, so that
-        // lane (t, g) ends with channels 8g .. 8g+7 of its pair, as in the state product
-        const int c = 32 * (ct >> 1) + 8 * (pr >> 2) + 4 * (ct & 1) + (pr & 3);
-        const int off = c * TP + 16 * kt + 4 * lg;
-        const u32x2_t vh = *reinterpret_cast<const u32x2_t*>(vt_hi + off);
-        acc[t] = mfma16_bf16(vh, ph, acc[t]);
-        acc[t] = mfma16_bf16(vh, pl, acc[t]);
-        if constexpr (VSPLIT) {
-          const u32x2_t vl = *reinterpret_cast<const u32x2_t*>(vt_lo + off);
-          acc[t] = mfma16_bf16(vl, ph, acc[t]);
+        for (int t = 0; t < 2 * PPW; ++t) {
+          const int ct = 2 * cp * PPW + t;
+          const int c = 32 * (ct >> 1) + 8 * (pr >> 2) + 4 * (ct & 1) + (pr & 3);
+          // step rr: k index lg = key 16 kt + 4 lg + rr, the lane's own score pv[rr]
+          const float4 vv = *reinterpret_cast<const float4*>(vt32 + c * TP + 16 * kt + 4 * lg);
+          acc[t] = mfma4_f32(vv.x, pv[0], acc[t]);
+          acc[t] = mfma4_f32(vv.y, pv[1], acc[t]);
+          acc[t] = mfma4_f32(vv.z, pv[2], acc[t]);
+          acc[t] = mfma4_f32(vv.w, pv[3], acc[t]);
+        }
+      } else {
+        u32x2_t ph, pl;
+        {
+          uint32_t h0, l0, h1, l1;
+          split_bf16x2(pv[0], pv[1], h0, l0);
+          split_bf16x2(pv[2], pv[3], h1, l1);
+          ph = u32x2_t{h0, h1};
+          pl = u32x2_t{l0, l1};
+        }
+#pragma unroll
+        for (int t = 0; t < 2 * PPW; ++t) {
+          const int ct = 2 * cp * PPW + t;
+          // A row pr of tile ct is channel 32 (ct / 2) + 8 (pr / 4) + 4 (ct % 2) + pr % 4, so that
+          // lane (t, g) ends with channels 8g .. 8g+7 of its pair, as in the state product
+          const int c = 32 * (ct >> 1) + 8 * (pr >> 2) + 4 * (ct & 1) + (pr & 3);
+          const int off = c * TP + 16 * kt + 4 * lg;
+          const u32x2_t vh = *reinterpret_cast<const u32x2_t*>(vt_hi + off);
+          acc[t] = mfma16_bf16(vh, ph, acc[t]);
+          acc[t] = mfma16_bf16(vh, pl, acc[t]);
         }
       }
     }
+    if constexpr (VSPLIT) issue_q(cq, j0 + SUB);
     dsum += __shfl_xor(dsum, 16);
     dsum += __shfl_xor(dsum, 32);
     if (qvalid) {
@@ -373,13 +421,25 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
 #pragma unroll
         for (int a = 0; a < FPW; ++a) {
           const int cb = (16 * (my_ct0 + a) + pr) * TP + 32 * ks + 8 * lg;
-          const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(vt_hi + cb);
+          u32x4_t bh, bl;
+          if constexpr (VSPLIT) {
+            const float4 v0 = *reinterpret_cast<const float4*>(vt32 + cb);
+            const float4 v1 = *reinterpret_cast<const float4*>(vt32 + cb + 4);
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split_bf16x2(v0.x, v0.y, h0, l0);
+            split_bf16x2(v0.z, v0.w, h1, l1);
+            split_bf16x2(v1.x, v1.y, h2, l2);
+            split_bf16x2(v1.z, v1.w, h3, l3);
+            bh = u32x4_t{h0, h1, h2, h3};
+            bl = u32x4_t{l0, l1, l2, l3};
+          } else {
+            bh = *reinterpret_cast<const u32x4_t*>(vt_hi + cb);
+          }
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) sacc[a][rt] = mfma_bf16(ah[rt], bh, sacc[a][rt]);
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) sacc[a][rt] = mfma_bf16(al[rt], bh, sacc[a][rt]);
           if constexpr (VSPLIT) {
-            const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(vt_lo + cb);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) sacc[a][rt] = mfma_bf16(ah[rt], bl, sacc[a][rt]);
           }
