@@ -22,6 +22,10 @@ in the same run: a 1 GiB device copy (`measured_copy_GBps`, read + write bytes) 
 8192^3 bf16 GEMM through torch (`measured_bf16_gemm_TFLOPs`).
 
 `causal` times the chunkwise-causal forward (1D workloads) on the same inputs.
+`decode` times the streaming decode (mhla_decode_step, one position per call) of the long
+sequence's heads (B = 1, 16 heads, d = 128, blocks of 256) over all 65536 positions, and of a
+batch of 32 such sequences over 4096 positions: tokens/s by the wall clock (host launches
+included) and the mean kernel time from HIP events against the algorithmic bytes.
 `backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the same
 inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
 
@@ -338,6 +342,91 @@ def run_backward(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
             "roofline": roof, "kernels": per_kernel}
 
 
+def decode_accounting(BH: int, d: int, nb: int, t0: int, t1: int, in_b: int, out_b: int) -> int:
+    """Algorithmic bytes of decode calls t0 .. t1-1 over BH (batch, head) pairs.  Every token
+    reads S~< and R and writes R (fp32 d x d each), reads z~< and r and writes r, reads q, k, v
+    and writes o; the first token of block i > 0 also reads the finished R, writes it as S_{i-1},
+    reads S_0 .. S_{i-2}, writes S~<_i and writes the restarted R: 4 d^2 (i + 3) bytes."""
+    per_tok = 12 * d * d + 12 * d + 3 * d * in_b + d * out_b
+    total = (t1 - t0) * per_tok
+    for i in range(max(1, -(-t0 // nb)), (t1 - 1) // nb + 1):
+        total += 4 * d * d * (i + 3) + 12 * d
+    return BH * total
+
+
+def run_decode(batch: int, heads: int, d: int, n: int, nb: int, seed: int, pool: int = 512,
+               in_dtype: str = "bf16", out_dtype: str = "bf16"):
+    """Streaming decode through positions 0 .. n-1 of a causal plan (blocks of nb tokens), one
+    mhla_decode_step per position.  The inputs of position t are pool[t % pool] (seeded N(0, 1);
+    the cost does not depend on the values).  One untimed pass, then a pass timed by the wall
+    clock (host launches included: tokens/s) and a pass with HIP events around every call on the
+    launch stream (mean time per call, event overhead included, against the algorithmic bytes)."""
+    import ctypes
+
+    import torch
+    import token_blocked_linear_amd as T
+
+    w = synth.Workload("decode", in_dtype, batch, heads, d, (n,), (nb,), seed, "softmax_gauss", "causal",
+                       ragged=n % nb != 0)
+    plan = T.Plan(grid=w.grid, block=w.block, batch=batch, heads=heads, head_dim=d, in_dtype=in_dtype,
+                  out_dtype=out_dtype, readout="causal", ragged=w.ragged)
+    mc = synth.make_mc(w, np.random.default_rng(seed))
+    tmc = torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    shape = (pool, batch, heads, d)
+    tq, tk, tv = (to_dev(synth.standard_normal_parallel(shape, seed + 1 + i, bf16=in_dtype == "bf16"), in_dtype)
+                  for i in range(3))
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    o = torch.empty((pool, batch, heads, d), dtype=odt, device="cuda:0")
+    state = plan.alloc_decode_state()
+    nbytes = state.numel()
+    stream = torch.cuda.current_stream()
+    lib = T.load_library()
+    ib, ob = tq.element_size() * batch * heads * d, o.element_size() * batch * heads * d
+    qp, kp, vp, op = tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr()
+    args = (plan.handle, state.data_ptr(), nbytes)
+    mcp, sp = ctypes.c_void_p(tmc.data_ptr()), ctypes.c_void_p(stream.cuda_stream)
+    step = lib.mhla_decode_step
+
+    def one(t):
+        j = t % pool
+        st = step(*args, t, qp + j * ib, kp + j * ib, vp + j * ib, mcp, op + j * ob, sp)
+        if st != 0:
+            raise T.MhlaError(st, "mhla_decode_step")
+
+    for _ in range(2):          # untimed pass, then the wall-clock pass
+        plan.decode_reset(state)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(n):
+            one(t)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    plan.decode_reset(state)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(1024)]
+    kern = 0.0
+    for base in range(0, n, len(ev)):
+        cnt = min(len(ev), n - base)
+        for j in range(cnt):
+            ev[j][0].record(stream)
+            one(base + j)
+            ev[j][1].record(stream)
+        torch.cuda.synchronize()
+        kern += sum(a.elapsed_time(b) for a, b in ev[:cnt]) * 1e-3
+    plan.close()
+    in_b, out_b = (2 if in_dtype == "bf16" else 4), (2 if out_dtype == "bf16" else 4)
+    alg = decode_accounting(batch * heads, d, nb, 0, n, in_b, out_b)
+    gbs = alg / kern / 1e9
+    return {"batch": batch, "heads": heads, "head_dim": d, "positions": n, "block_tokens": nb,
+            "n_blocks": w.n_blocks, "in_dtype": in_dtype, "out_dtype": out_dtype,
+            "state_MiB": round(nbytes / 2 ** 20, 1),
+            "wall_us_per_token": round(wall / n * 1e6, 3),
+            "tokens_per_s": round(batch * n / wall, 1),
+            "event_us_mean": round(kern / n * 1e6, 3),
+            "alg_bytes_per_call_mean": int(alg / n),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(res, budget_s: float = 12.0):
     """The fp64 oracle (as it stands) on a bounded sample: whole (batch, head) pairs, cycled
     until the time budget is used."""
@@ -372,6 +461,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-causal", action="store_true", help="skip the causal-readout measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--digest", action="store_true")
     args = ap.parse_args()
@@ -445,6 +535,12 @@ def main():
                   "tokens_per_s": round(rc["tokens_per_s"], 1), "kernels": rc["per_kernel"]}
         del rc
 
+    decode = None
+    if not args.no_decode:
+        # the long sequence's heads decoded one position at a time (B = 1), and a batch of 32
+        # such sequences over their first 4096 positions
+        decode = [run_decode(1, 16, 128, 65536, 256, 701), run_decode(32, 16, 128, 4096, 256, 702)]
+
     bwd = None
     if not args.no_backward and w.readout != "mala":
         bwd = run_backward(args.workload, args.steps, args.warmup, args.out_dtype, res["inputs"])
@@ -481,6 +577,8 @@ def main():
         line["backward"] = bwd
     if causal is not None:
         line["causal"] = causal
+    if decode is not None:
+        line["decode"] = decode
     if others:
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)

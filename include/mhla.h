@@ -180,6 +180,35 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
                           const void* dout, void* dq, void* dk, void* dv, float* dmc, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Streaming decode: one new token per (batch, head) per call, for a causal plan ("MHLA: Restoring
+ * Expressivity of Linear Attention via Token-Level Multi-Head", Method -> Key design 4: MHLA is
+ * compatible with streaming / stateful inference; the causal reading of the causal readout modes
+ * applies).  The plan (readout MHLA_READOUT_CAUSAL_*, a 1D grid of N tokens, blocks of n_b tokens,
+ * ragged allowed, no CLS token) fixes the capacity: positions 0 .. N-1, M blocks.  Token t lies in
+ * block i = t / n_b and reads
+ *     o_t = q~_t^T (S~<_i + m_ii R_t) / q~_t^T (z~<_i + m_ii r_t)    (no division: unnormalised)
+ * with S~<_i = sum_{b<i} m_ib S_b over the completed blocks and R_t, r_t the sums of k~ v^T and k~
+ * over block i's tokens up to t -- the same values as the causal forward's output t.
+ *   state   device, mhla_decode_state_size bytes, 256-byte aligned, owned by the caller: per
+ *           (batch, head) the completed blocks' S_b and z_b, S~<_i and z~<_i of the current block
+ *           and the running R, r, all fp32, in a layout private to the library (the head's
+ *           channels are cut into slices that each keep a copy of the d-vectors: about
+ *           4 (M + 2)(d^2 + d s) bytes per (batch, head), s <= min(d / 8, d^2 / 1024) slices chosen
+ *           from B * H).
+ *           mhla_decode_reset clears it (position 0).
+ *   t       the position of this call's token; calls on one state must come with t = 0, 1, 2, ...
+ *           in order (t outside [0, N): MHLA_ERR_INVALID_ARG).  At the first token of a block the
+ *           call also stores the finished block's summary and forms S~<_i from row i of M_c.
+ *   q, k, v device [B, H, 1, d] of the plan's in_dtype; o: device [B, H, 1, d] of its out_dtype
+ *   mc      device fp32 M_c as for mhla_forward (NULL iff M == 1)
+ * Arithmetic in fp32 (no MFMA: a d x d matrix-vector product per head).  Asynchronous on
+ * `stream`; calls on one state must not overlap.  Not supported (MHLA_ERR_UNSUPPORTED): other
+ * readouts, a CLS token. */
+mhla_status mhla_decode_state_size(mhla_handle h, size_t* bytes);
+mhla_status mhla_decode_reset(mhla_handle h, void* state, size_t state_bytes, void* stream);
+mhla_status mhla_decode_step(mhla_handle h, void* state, size_t state_bytes, int64_t t, const void* q,
+                             const void* k, const void* v, const float* mc, void* o, void* stream);
+
 /* Release a plan.  NULL is accepted. */
 mhla_status mhla_destroy(mhla_handle h);
 

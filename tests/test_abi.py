@@ -237,6 +237,46 @@ def test_backward_argument_errors_before_launch():
     p.close()
 
 
+def test_decode_support_and_state_size():
+    """The decode state: per (batch, head), d^2 + s d floats for each of the M completed blocks,
+    the mixed earlier blocks and the running block, where s is the number of channel slices (the
+    fewest, of at least max(8, 1024 / d) channels each, that give 512 workgroups); causal plans
+    without a CLS token only."""
+    _lib_or_skip()
+    for (b, h, d, s) in ((2, 3, 64, 4), (1, 16, 128, 16), (64, 8, 64, 1), (16, 8, 32, 1), (32, 8, 128, 2)):
+        p = T.Plan(grid=(1000,), block=(128,), batch=b, heads=h, head_dim=d, readout="causal", ragged=True)
+        assert p.info.n_blocks == 8
+        assert T.mhla_decode_state_size(p.handle) == b * h * (8 + 2) * (d * d + s * d) * 4, (b, h, d)
+        p.close()
+    for kw in (dict(readout="normalized"), dict(readout="causal", cls_token=True)):
+        u = T.Plan(**dict(dict(grid=(1000,), block=(125,), batch=1, heads=1, head_dim=64), **kw))
+        with pytest.raises(T.MhlaError) as e:
+            T.mhla_decode_state_size(u.handle)
+        assert e.value.status == 2                           # MHLA_ERR_UNSUPPORTED
+        u.close()
+
+
+def test_decode_argument_errors_before_launch():
+    """Rejected by validation, before any launch (a launch here would give MHLA_ERR_HIP)."""
+    lib = _lib_or_skip()
+    p = T.Plan(grid=(1000,), block=(125,), batch=2, heads=2, head_dim=64, readout="causal")
+    n = T.mhla_decode_state_size(p.handle)
+    S, Q, K, V, MC, O = 0x1000000, 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    f = lambda *a: lib.mhla_decode_step(p.handle, *a)  # noqa: E731
+    assert f(S, n, -1, Q, K, V, MC, O, None) == 1          # t before the sequence
+    assert f(S, n, 1000, Q, K, V, MC, O, None) == 1        # t past its end
+    assert f(S, n, 0, None, K, V, MC, O, None) == 1        # NULL q
+    assert f(S, n, 0, Q, K, V, None, O, None) == 1         # NULL M_c with M > 1
+    assert f(S, n, 0, Q, K, V, MC, Q, None) == 1           # o aliases q
+    assert f(S, n, 0, Q + 1, K, V, MC, O, None) == 1       # misaligned q
+    assert f(S, n - 1, 0, Q, K, V, MC, O, None) == 4       # state too small
+    assert f(S + 16, n, 0, Q, K, V, MC, O, None) == 4      # state misaligned
+    assert lib.mhla_decode_reset(p.handle, S, n - 1, None) == 4
+    assert lib.mhla_decode_reset(p.handle, None, n, None) == 1
+    assert lib.mhla_decode_step(None, S, n, 0, Q, K, V, MC, O, None) == 1
+    p.close()
+
+
 def test_status_strings():
     _lib_or_skip()
     for s in range(7):

@@ -1,0 +1,134 @@
+"""GPU parity of the streaming decode (mhla_decode_step): feeding a sequence one token per call
+gives the chunkwise-causal readout of the whole sequence.
+
+The reference is the fp64 oracle's causal readout (query t reads every t' <= t with weight
+m_{b(t), b(t')}), run on the same seeded inputs; the bar is the causal readout's elementwise one,
+|o_t - ref_t| <= tol * max(RMS(ref), |ref_t|), with tol 2e-2 for bf16 inputs and 1e-4 for fp32
+inputs.  The decode state is fp32 throughout.  The cases cover every channel-slice width the
+library picks (8 .. d channels per workgroup, from the number of (batch, head) pairs).  Each case also checks the decoded sequence against
+the library's own chunkwise causal forward on the same inputs, to the same bar.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import announce, oracle_full, run_hip, to_device
+import token_blocked_linear_amd as T
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+FP32_TOL = 1e-4
+
+
+def W(name, dtype, b, h, d, n, nb, seed, mc="softmax_gauss", readout="causal", phi="elu1"):
+    return synth.Workload(name, dtype, b, h, d, (n,), (nb,), seed, mc, readout, phi, ragged=n % nb != 0)
+
+
+CASES = [
+    # 5 blocks, the last one 88 tokens
+    W("dec_d64_ragged", "bf16", 2, 2, 64, 600, 128, 601),
+    W("dec_d32_fp32_unnorm_relu", "fp32", 1, 3, 32, 500, 96, 602, "softmax_l1", "causal_unnormalized", "relu"),
+    W("dec_d128_exp", "bf16", 1, 2, 128, 700, 200, 603, "locality", phi="exp"),
+    W("dec_d128_fp32", "fp32", 1, 1, 128, 384, 64, 604),
+    # one block: M = 1 and no M_c
+    W("dec_one_block", "bf16", 2, 2, 64, 300, 300, 605, "none"),
+    # blocks of one token (M = N): every call closes a block
+    W("dec_unit_blocks", "fp32", 1, 2, 32, 96, 1, 606, "softmax_l1"),
+    # 32 blocks of 128
+    W("dec_m32_d128", "bf16", 1, 4, 128, 4096, 128, 607, "softmax_l1"),
+    # more (batch, head) pairs: fewer, wider channel slices per head (64 channels; whole heads)
+    W("dec_batch_d128_c64", "bf16", 16, 16, 128, 300, 64, 608),
+    W("dec_batch_d64_c64", "bf16", 64, 8, 64, 200, 48, 609, "softmax_l1"),
+    W("dec_batch_d128_c128", "fp32", 32, 16, 128, 130, 32, 610),
+]
+
+
+def _inputs(w):
+    q, k, v, mc, rng = synth.make_inputs(w)
+    if w.phi == "relu":          # keep every query off ReLU's all-zero features
+        q = np.abs(q)
+    return q, k, v, mc, rng
+
+
+def decode_sequence(w, q, k, v, mc, *, out_dtype="fp32", plan=None, state=None, t0=0, t1=None):
+    """Steps tokens t0 .. t1-1 through mhla_decode_step; returns float64 [B, H, t1-t0, d]."""
+    import torch
+    mc_per_head = mc is not None and np.ndim(mc) == 3
+    own = plan is None
+    if own:
+        plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                      in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, phi=w.phi,
+                      mc_per_head=mc_per_head, ragged=w.ragged)
+        state = plan.alloc_decode_state()
+    t1 = w.grid[0] if t1 is None else t1
+    # token-major copies, so that one token of every (batch, head) is one contiguous [B, H, 1, d]
+    seq = [to_device(np.ascontiguousarray(np.moveaxis(x[:, :, t0:t1], 2, 0)), w.dtype) for x in (q, k, v)]
+    tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.empty((t1 - t0, w.batch, w.heads, 1, w.head_dim), dtype=odt, device="cuda:0")
+    for t in range(t0, t1):
+        i = t - t0
+        plan.decode_step(state, t, *(x[i].unsqueeze(2) for x in seq), tmc, out[i])
+    torch.cuda.synchronize()
+    res = np.moveaxis(out[:, :, :, 0].float().cpu().numpy().astype(np.float64), 0, 2)
+    if own:
+        plan.close()
+    return res
+
+
+def causal_err(got, want):
+    rms = float(np.sqrt(np.mean(want * want)))
+    return float(np.max(np.abs(got - want) / np.maximum(rms, np.abs(want))))
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_decode_matches_causal_readout(w):
+    announce(f"decode {w.name} shape={w.qkv_shape} block={w.block} blocks={w.n_blocks} {w.readout} "
+             f"{w.phi} {w.dtype}")
+    q, k, v, mc, _ = _inputs(w)
+    got = decode_sequence(w, q, k, v, mc)
+    want = oracle_full(w, q, k, v, mc)
+    tol = FP32_TOL if w.dtype == "fp32" else BF16_TOL
+    err = causal_err(got, want)
+    chunk = run_hip(w, q, k, v, mc)
+    err_chunk = causal_err(got, chunk)
+    print(f"  err={err:.3e} vs chunkwise forward {err_chunk:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= tol, (w.name, err)
+    assert err_chunk <= tol, (w.name, err_chunk)
+
+
+def test_decode_bf16_output_and_per_head_mc():
+    w = W("dec_per_head_bf16_out", "bf16", 2, 3, 64, 520, 100, 611, "none")
+    announce(w.name)
+    q, k, v, _, rng = _inputs(w)
+    mc = rng.uniform(0.0, 1.0, (w.heads, w.n_blocks, w.n_blocks))
+    got = decode_sequence(w, q, k, v, mc, out_dtype="bf16")
+    err = causal_err(got, oracle_full(w, q, k, v, mc))
+    print(f"  err={err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_decode_reset_and_resume():
+    """A reset state starts a new sequence; a state carries over between runs of calls, so that
+    a sequence decoded in two parts equals the sequence decoded at once."""
+    import torch
+    w = W("dec_reset", "fp32", 1, 2, 64, 400, 96, 612)
+    announce(w.name)
+    q, k, v, mc, rng = _inputs(w)
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, readout=w.readout, phi=w.phi, ragged=w.ragged)
+    state = plan.alloc_decode_state()
+    # a first, unrelated sequence leaves the state dirty (parts of every block in it)
+    junk = [rng.standard_normal(x.shape) for x in (q, k, v)]
+    decode_sequence(w, *junk, mc, plan=plan, state=state, t1=250)
+    plan.decode_reset(state)
+    a = decode_sequence(w, q, k, v, mc, plan=plan, state=state, t1=150)
+    b = decode_sequence(w, q, k, v, mc, plan=plan, state=state, t0=150)
+    torch.cuda.synchronize()
+    got = np.concatenate([a, b], axis=2)
+    whole = decode_sequence(w, q, k, v, mc)
+    plan.close()
+    assert np.array_equal(got, whole)
+    assert causal_err(got, oracle_full(w, q, k, v, mc)) <= FP32_TOL

@@ -20,7 +20,8 @@ __all__ = [
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
-    "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read", "make_desc", "Plan", "EXPORTED_SYMBOLS",
+    "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
+    "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "make_desc", "Plan", "EXPORTED_SYMBOLS",
 ]
 
 MHLA_OK = 0
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
+    "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step",
 )
 
 
@@ -125,6 +127,9 @@ def load_library() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_char_p)]
     lib.mhla_timing_reset.argtypes = [P]
     lib.mhla_backward_timing_read.argtypes = lib.mhla_timing_read.argtypes
+    lib.mhla_decode_state_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.mhla_decode_reset.argtypes = [P, P, SZ, P]
+    lib.mhla_decode_step.argtypes = [P, P, SZ, I64, P, P, P, P, P, P]
     for name in EXPORTED_SYMBOLS:
         if name != "mhla_status_string":
             getattr(lib, name).restype = I32
@@ -175,6 +180,23 @@ def mhla_backward(h, q: int, k: int, v: int, mc: int, dout: int, dq: int, dk: in
     """Pointers are integer device addresses (0 for NULL); ``stream`` a raw hipStream_t."""
     _check(load_library().mhla_backward(h, q, k, v, mc or None, dout, dq, dk, dv, dmc or None,
                                         workspace or None, workspace_bytes, stream or None), "mhla_backward")
+
+
+def mhla_decode_state_size(h) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mhla_decode_state_size(h, ctypes.byref(n)), "mhla_decode_state_size")
+    return n.value
+
+
+def mhla_decode_reset(h, state: int, state_bytes: int, stream: int) -> None:
+    _check(load_library().mhla_decode_reset(h, state, state_bytes, stream or None), "mhla_decode_reset")
+
+
+def mhla_decode_step(h, state: int, state_bytes: int, t: int, q: int, k: int, v: int, mc: int, o: int,
+                     stream: int) -> None:
+    """One token per (batch, head) at position ``t``; pointers are integer device addresses."""
+    _check(load_library().mhla_decode_step(h, state, state_bytes, t, q, k, v, mc or None, o, stream or None),
+           "mhla_decode_step")
 
 
 def mhla_destroy(h) -> None:
@@ -319,6 +341,41 @@ class Plan:
                       dk.data_ptr(), dv.data_ptr(), dmc.data_ptr() if dmc is not None else 0,
                       workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
         return dq, dk, dv, dmc
+
+    def alloc_decode_state(self, device="cuda"):
+        """A decode state for this (causal) plan, cleared on the current stream."""
+        import torch
+        n = mhla_decode_state_size(self.handle)
+        state = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+        self.decode_reset(state)
+        return state
+
+    def decode_reset(self, state, stream=None):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream(state.device)
+        mhla_decode_reset(self.handle, state.data_ptr(), state.numel(), stream.cuda_stream)
+
+    def decode_step(self, state, t, q, k, v, mc, o, stream=None):
+        """Token ``t`` of every (batch, head): q, k, v [B, H, 1, d] of the plan's in_dtype, o the
+        same shape in its out_dtype (written)."""
+        import torch
+        kw = self.desc_kwargs
+        shape = (int(kw["batch"]), int(kw["heads"]), 1, int(kw["head_dim"]))
+        tin = torch.bfloat16 if kw.get("in_dtype", "bf16") == "bf16" else torch.float32
+        tout = torch.bfloat16 if kw.get("out_dtype", "fp32") == "bf16" else torch.float32
+        for name, x, dt in (("q", q, tin), ("k", k, tin), ("v", v, tin), ("o", o, tout)):
+            if tuple(x.shape) != shape or x.dtype != dt or not x.is_contiguous() or not x.is_cuda:
+                raise ValueError(f"{name}: expected a contiguous {dt} cuda tensor of shape {shape}")
+        _, mc_shape = self.expected_shapes()
+        if mc is not None and (tuple(mc.shape) != mc_shape or mc.dtype != torch.float32
+                               or not mc.is_contiguous() or not mc.is_cuda):
+            raise ValueError(f"mc: expected contiguous float32 cuda tensor {mc_shape}")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        mhla_decode_step(self.handle, state.data_ptr(), state.numel(), int(t), q.data_ptr(), k.data_ptr(),
+                         v.data_ptr(), mc.data_ptr() if mc is not None else 0, o.data_ptr(), stream.cuda_stream)
+        return o
 
     def forward(self, q, k, v, mc, o, workspace, stream=None):
         import torch

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmhla.so")
 
-SOURCES = ["summary.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "mhla_host.cpp"]
+SOURCES = ["summary.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "decode.hip",
+           "mhla_host.cpp"]
 
 
 def hipcc() -> str:

@@ -245,6 +245,21 @@ struct CausalParams {
   int32_t normalized;
 };
 
+// Streaming decode step (one token per (batch, head)); the state layout is in decode.hip.
+struct DecodeParams {
+  float* state;            // per (batch, head): (M + 2) * (D*D + slices*D) floats
+  const void* q;           // [BH][D] of the input dtype (the new token)
+  const void* k;
+  const void* v;
+  void* o;                 // [BH][D] of the output dtype
+  const float* mc;         // M_c; NULL when M == 1
+  int64_t mc_head_stride;
+  int64_t t;               // the token's position
+  int32_t H, M, nb, BH;    // nb: tokens per block
+  int32_t normalized;
+  int32_t log2_c;          // channels per workgroup = 2^log2_c (8 .. D); D >> log2_c workgroups per head
+};
+
 // MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,
 // plus the fp32 normaliser mixing z~[i] = sum_b M_c[i][b] z[b].
 struct MixMfmaParams {

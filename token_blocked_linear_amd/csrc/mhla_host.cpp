@@ -25,6 +25,8 @@ hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_
 hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
                             bool key_side, int n_units, hipStream_t stream);
 hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream);
+hipError_t launch_decode_step(const DecodeParams& p, int d, bool in_fp32, bool out_fp32, int phi, hipStream_t s);
+hipError_t launch_decode_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_causal(const CausalParams& p, int d, bool in_fp32, bool out_fp32, int phi, int n_units,
                          hipStream_t stream);
 hipError_t launch_slice_prefix(float* ps, float* pz, int64_t rows, int splits, int frag, int d, hipStream_t stream);
@@ -753,6 +755,81 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     }
     if (!mark()) return MHLA_ERR_HIP;
     return MHLA_OK;
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
+
+// ---- streaming decode --------------------------------------------------------------------
+static mhla_status decode_supported(const mhla_plan* h) {
+  if (!h->causal || h->geom.cls) return MHLA_ERR_UNSUPPORTED;
+  return MHLA_OK;
+}
+// channels per decode workgroup, as log2: the head's d channels are cut into the fewest slices
+// (powers of two, each of at least max(8, 1024 / d) channels) that give 512 workgroups over all
+// (batch, head) pairs
+static int decode_log2_c(const mhla_plan* h) {
+  const int min_c = h->d >= 128 ? 8 : 1024 / h->d;
+  int slices = 1;
+  while (h->BH * slices < 512 && h->d / (slices * 2) >= min_c) slices *= 2;
+  int lc = 0;
+  while ((slices << lc) < h->d) ++lc;
+  return lc;
+}
+static size_t decode_state_bytes(const mhla_plan* h) {
+  const size_t slices = (size_t)h->d >> decode_log2_c(h);
+  return (size_t)h->BH * (size_t)(h->M + 2) * ((size_t)h->d * h->d + slices * h->d) * 4;
+}
+
+mhla_status mhla_decode_state_size(mhla_handle h, size_t* bytes) {
+  if (!h || !bytes) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = decode_supported(h);
+  if (st != MHLA_OK) return st;
+  *bytes = decode_state_bytes(h);
+  return MHLA_OK;
+}
+
+mhla_status mhla_decode_reset(mhla_handle h, void* state, size_t state_bytes, void* stream) {
+  if (!h || !state) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = decode_supported(h);
+  if (st != MHLA_OK) return st;
+  if (state_bytes < decode_state_bytes(h) || !aligned(state, 256)) return MHLA_ERR_WORKSPACE;
+  const hipError_t e = mhla::launch_decode_zero(static_cast<float*>(state), (int64_t)(decode_state_bytes(h) / 4),
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+}
+
+mhla_status mhla_decode_step(mhla_handle h, void* state, size_t state_bytes, int64_t t, const void* q,
+                             const void* k, const void* v, const float* mc, void* o, void* stream) {
+  if (!h || !state || !q || !k || !v || !o) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = decode_supported(h);
+  if (st != MHLA_OK) return st;
+  if (t < 0 || t >= h->N) return MHLA_ERR_INVALID_ARG;
+  if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
+  const size_t ein = h->in_fp32 ? 4 : 2, eout = h->out_fp32 ? 4 : 2;
+  if (!aligned(q, ein) || !aligned(k, ein) || !aligned(v, ein) || !aligned(o, eout)) return MHLA_ERR_INVALID_ARG;
+  if (mc && !aligned(mc, 4)) return MHLA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v || o == state) return MHLA_ERR_INVALID_ARG;
+  if (state_bytes < decode_state_bytes(h) || !aligned(state, 256)) return MHLA_ERR_WORKSPACE;
+  try {
+    mhla::DecodeParams p = {};
+    p.state = static_cast<float*>(state);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.mc = mc;
+    p.mc_head_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+    p.t = t;
+    p.H = (int32_t)h->H;
+    p.M = (int32_t)h->M;
+    p.nb = (int32_t)h->n_b;
+    p.BH = (int32_t)h->BH;
+    p.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
+    p.log2_c = decode_log2_c(h);
+    const hipError_t e = mhla::launch_decode_step(p, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
   } catch (...) {
     return MHLA_ERR_INTERNAL;
   }
