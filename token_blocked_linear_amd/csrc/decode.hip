@@ -89,17 +89,33 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
         const int e = tid + kThreads * j;
         const float4 done = rr[j];
         hS4[(int64_t)(i - 1) * DC4 + e] = done;
-        float4 a = make_float4(m * done.x, m * done.y, m * done.z, m * done.w);
-        for (int b = 0; b < i - 1; ++b) {
+        // four interleaved partial sums (b mod 4), so that four loads are in flight
+        float4 a[4] = {make_float4(m * done.x, m * done.y, m * done.z, m * done.w), make_float4(0.f, 0.f, 0.f, 0.f),
+                       make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+        int b = 0;
+        for (; b + 4 <= i - 1; b += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float mb = mrow[b + u];
+            const float4 x = hS4[(int64_t)(b + u) * DC4 + e];
+            a[u].x = fmaf(mb, x.x, a[u].x);
+            a[u].y = fmaf(mb, x.y, a[u].y);
+            a[u].z = fmaf(mb, x.z, a[u].z);
+            a[u].w = fmaf(mb, x.w, a[u].w);
+          }
+        }
+        for (; b < i - 1; ++b) {
           const float mb = mrow[b];
           const float4 x = hS4[(int64_t)b * DC4 + e];
-          a.x = fmaf(mb, x.x, a.x);
-          a.y = fmaf(mb, x.y, a.y);
-          a.z = fmaf(mb, x.z, a.z);
-          a.w = fmaf(mb, x.w, a.w);
+          a[0].x = fmaf(mb, x.x, a[0].x);
+          a[0].y = fmaf(mb, x.y, a[0].y);
+          a[0].z = fmaf(mb, x.z, a[0].z);
+          a[0].w = fmaf(mb, x.w, a[0].w);
         }
-        St4[e] = a;
-        ss[j] = a;
+        const float4 sum = make_float4((a[0].x + a[1].x) + (a[2].x + a[3].x), (a[0].y + a[1].y) + (a[2].y + a[3].y),
+                                       (a[0].z + a[1].z) + (a[2].z + a[3].z), (a[0].w + a[1].w) + (a[2].w + a[3].w));
+        St4[e] = sum;
+        ss[j] = sum;
         rr[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     if (tid < D) {
