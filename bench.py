@@ -17,9 +17,10 @@ WRITE_SIZE hardware counters, each scaled by what the counter reads for a plain 
 size), taken from profiles/traffic.md when that record was made from the current kernel sources
 (same digest of the csrc/ files and the header), else null.
 
-Beside the spec peaks (8 TB/s, 2.5 PFLOP/s bf16) the roofline object carries two rates measured
-in the same run: a 1 GiB device copy (`measured_copy_GBps`, read + write bytes) and a dense
-8192^3 bf16 GEMM through torch (`measured_bf16_gemm_TFLOPs`).
+Beside the spec peaks (8 TB/s, 2.5 PFLOP/s bf16) the roofline object carries three rates measured
+in the same run: a 1 GiB device copy (`measured_copy_GBps`, read + write bytes), a dense
+8192^3 bf16 GEMM through torch (`measured_bf16_gemm_TFLOPs`) and a register-only loop of bf16
+MFMAs (`measured_bf16_mfma_loop_TFLOPs`, libmhla_peak.so).
 
 `causal` times the chunkwise-causal forward (1D workloads) on the same inputs.
 `decode` times the streaming decode (mhla_decode_step, one position per call) of the long
@@ -58,6 +59,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.md")
 TRAFFIC_TAG = "traffic-json: "
 
 
+DIGEST_EXCLUDE = {"peak_probe.hip"}   # the measured-peak probe: not part of the MHLA path
+
+
 def source_digest() -> str:
     """sha256 over the kernel and boundary sources (file names and contents, sorted)."""
     import hashlib
@@ -65,7 +69,7 @@ def source_digest() -> str:
     for d in SOURCE_DIRS:
         full = os.path.join(ROOT, d)
         for name in sorted(os.listdir(full)):
-            if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            if name.endswith((".hip", ".hpp", ".cpp", ".h")) and name not in DIGEST_EXCLUDE:
                 h.update(name.encode())
                 with open(os.path.join(full, name), "rb") as f:
                     h.update(f.read())
@@ -106,6 +110,36 @@ def measured_gemm_TFLOPs(n: int = 8192, reps: int = 10) -> float:
     del a, b, c
     torch.cuda.empty_cache()
     return 2.0 * n ** 3 / t / 1e12
+
+
+def measured_mfma_TFLOPs(blocks: int = 1024, iters: int = 1024, reps: int = 3):
+    """Dense bf16 MFMA rate of a register-only loop (libmhla_peak.so): 1024 workgroups of 4 waves,
+    each wave 8 * iters v_mfma_f32_16x16x32_bf16 (16384 flops each); best of `reps` timed launches
+    after one warm-up.  None when the probe library is not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "token_blocked_linear_amd", "libmhla_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mhla_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    flops = blocks * 4 * 8 * iters * 16384
+    best = None
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.mhla_peak_mfma_bf16(blocks, iters, out.data_ptr(), stream.cuda_stream)
+        e1.record(stream)
+        e1.synchronize()
+        if st != 0:
+            raise RuntimeError(f"mhla_peak_mfma_bf16: hip error {st}")
+        if r > 0:
+            t = e0.elapsed_time(e1) * 1e-3
+            best = t if best is None else min(best, t)
+    return flops / best / 1e12
 
 
 def measured_copy_GBps(n_bytes: int = 1 << 30, reps: int = 10) -> float:
@@ -503,6 +537,8 @@ def main():
     gemm_tf = measured_gemm_TFLOPs()
     roof["measured_copy_GBps"] = round(copy_bw, 1)
     roof["measured_bf16_gemm_TFLOPs"] = round(gemm_tf, 1)
+    mfma_tf = measured_mfma_TFLOPs()
+    roof["measured_bf16_mfma_loop_TFLOPs"] = None if mfma_tf is None else round(mfma_tf, 1)
     if roof["unit"] == "GB/s":
         roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_bw, 4)
     elif roof["bound"] == "mfma":

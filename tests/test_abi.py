@@ -38,6 +38,15 @@ def test_library_exports_every_declared_symbol():
         assert name in exported, name
 
 
+def test_peak_probe_library_exports_its_entry():
+    """The benchmark's MFMA-loop probe is a library of its own, built beside libmhla.so."""
+    path = os.path.join(os.path.dirname(T.library_path()), "libmhla_peak.so")
+    if not os.path.exists(path):
+        pytest.skip("libmhla_peak.so is not built (run __graft_entry__.build())")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    assert re.search(r"\sT\smhla_peak_mfma_bf16$", out, re.M)
+
+
 def test_struct_layouts_match_header():
     # mhla_desc: 8 x int32 (incl. struct_size) + 2 x int64[3] + 3 x int64 + 2 x int32
     #   = 32 + 48 + 24 + 8

@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmhla.so")
+# the benchmark's measured-peak probe, a library of its own outside the MHLA path
+PEAK_SOURCE = "peak_probe.hip"
+PEAK_LIB = os.path.join(PKG, "libmhla_peak.so")
 
 SOURCES = ["summary.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "decode.hip",
            "mhla_host.cpp"]
@@ -60,7 +63,22 @@ def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD, defines
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}", file=sys.stderr)
+    if out == LIB:
+        build_peak_probe(build_dir)
     return out
+
+
+def build_peak_probe(build_dir: str = BUILD) -> str:
+    """The benchmark's MFMA-loop probe as its own shared library (``libmhla_peak.so``)."""
+    os.makedirs(build_dir, exist_ok=True)
+    obj = _compile(PEAK_SOURCE, build_dir)
+    tmp = PEAK_LIB + ".tmp"
+    res = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, obj],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, PEAK_LIB)
+    return PEAK_LIB
 
 
 if __name__ == "__main__":
