@@ -201,7 +201,10 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
   }
 
   const AOffsets ao = a_offsets(lane);
-  const int qt = wave % QT, cp = wave / QT;
+  // query tile and channel pairs of this wave.  Waves w and w + 4 share a SIMD, so waves 4 .. 7
+  // take the query tiles in reverse order: every SIMD then walks the same number of in-sub-chunk
+  // key tiles (query tile qt reads qt + 1 of them).
+  const int qt = ((wave >> 2) & 1) ? QT - 1 - wave % QT : wave % QT, cp = wave / QT;
   const Rsrc rq = make_rsrc(reinterpret_cast<const TIn*>(p.q) + head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rk = make_rsrc(reinterpret_cast<const TIn*>(p.k) + head_off, (uint32_t)geo.N * D * ES);
   const Rsrc rv = make_rsrc(reinterpret_cast<const TIn*>(p.v) + head_off, (uint32_t)geo.N * D * ES);
