@@ -11,7 +11,8 @@ resources with 31-bit byte ranges), the number of (batch, head) pairs and the nu
     tokens instead of 4 million).  The mixing kernel still runs (with the identity).  Inputs:
     synth.standard_normal_parallel (seeded child streams, 16 threads), Q then K then V;
   * the most (batch, head) pairs, 65535, with a few tokens each, checked on sampled heads;
-  * 2048 blocks (the VALU mixing kernel), checked in full.
+  * 2048 blocks (the VALU mixing kernel), checked in full;
+  * streaming decode over 65535 (batch, head) pairs, checked on sampled heads.
 Bars as everywhere: max|d| / RMS(o) <= 2e-2 for bf16 inputs, <= 1e-4 for fp32 inputs (RMS over
 the sampled outputs for the longest head); the causal readout relative to max(RMS(o), |o_t|).
 """
@@ -104,6 +105,39 @@ def test_most_heads():
     heads = [(0, 0), (65534, 0)] + [(int(b), 0) for b in rng.choice(65535, 62, replace=False)]
     want = oracle.forward(q, k, v, mc, w.grid, w.block, heads=heads)
     err = rel_err(np.stack([got[b, h] for b, h in heads]), want)
+    print(f"  err={err:.3e} ({len(heads)} heads)")
+    assert np.all(np.isfinite(got))
+    assert err <= BF16_TOL
+
+
+def test_decode_most_heads():
+    """Streaming decode over the most (batch, head) pairs, 65535 (one workgroup per pair at
+    d = 32), position by position through 3 blocks; sampled heads against the oracle's causal
+    readout (elementwise bar relative to max(RMS(o), |o_t|))."""
+    import torch
+    import token_blocked_linear_amd as T
+    from gpu_util import oracle_full, to_device
+    w = synth.Workload("max_heads_decode", "bf16", 65535, 1, 32, (10,), (4,), 506, "softmax_gauss", "causal",
+                       ragged=True)
+    announce(f"{w.name} shape={w.qkv_shape} blocks={w.n_blocks}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype="fp32", readout=w.readout, ragged=True)
+    state = plan.alloc_decode_state()
+    seq = [to_device(np.ascontiguousarray(np.moveaxis(x, 2, 0)), w.dtype) for x in (q, k, v)]
+    tmc = torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    out = torch.empty((w.grid[0], w.batch, w.heads, 1, w.head_dim), dtype=torch.float32, device="cuda:0")
+    for t in range(w.grid[0]):
+        plan.decode_step(state, t, *(x[t].unsqueeze(2) for x in seq), tmc, out[t])
+    torch.cuda.synchronize()
+    got = np.moveaxis(out[:, :, :, 0].cpu().numpy().astype(np.float64), 0, 2)
+    plan.close()
+    rng = np.random.default_rng(507)
+    heads = [(0, 0), (65534, 0)] + [(int(b), 0) for b in rng.choice(65535, 62, replace=False)]
+    want = oracle_full(w, q, k, v, mc, heads=heads)
+    g = np.stack([got[b, h] for b, h in heads])
+    rms = float(np.sqrt(np.mean(want * want)))
+    err = float(np.max(np.abs(g - want) / np.maximum(rms, np.abs(want))))
     print(f"  err={err:.3e} ({len(heads)} heads)")
     assert np.all(np.isfinite(got))
     assert err <= BF16_TOL
