@@ -31,6 +31,10 @@
  *     rejected; partial overlap is undefined).
  *   - mhla_forward is asynchronous on the given HIP stream (NULL = default stream).  One
  *     (plan, workspace) pair may be in flight on one stream at a time.
+ *   - mhla_forward, mhla_backward and the decode calls only launch kernels on `stream`: no
+ *     allocation, memset or host synchronisation.  So they may be captured into a HIP graph,
+ *     and each replay computes what the call would compute on the buffers' contents at replay
+ *     time.  Per-kernel timing (mhla_timing_enable) adds event records to the captured work.
  *
  * Errors
  *   - Every call returns mhla_status; MHLA_OK is 0.  Arguments are validated before any
