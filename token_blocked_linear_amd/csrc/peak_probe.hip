@@ -30,6 +30,9 @@ __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float* out, int ite
     MHLA_PEAK_MFMA(c7, b7);
   }
 #undef MHLA_PEAK_MFMA
+  // the compiler sees no MFMA in the asm, so it inserts no wait states before the VALU reads of
+  // the accumulators below: give them explicitly (more than any MFMA-to-VALU hazard needs)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   const f32x4_t c[8] = {c0, c1, c2, c3, c4, c5, c6, c7};
   float s = 0.f;
 #pragma unroll
