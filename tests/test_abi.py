@@ -286,6 +286,17 @@ def test_decode_argument_errors_before_launch():
     p.close()
 
 
+def test_decode_binding_rejects_a_host_state():
+    """The binding checks the state tensor before handing its pointer to the library."""
+    import torch
+    _lib_or_skip()
+    p = T.Plan(grid=(1000,), block=(125,), batch=1, heads=2, head_dim=64, readout="causal")
+    n = T.mhla_decode_state_size(p.handle)
+    with pytest.raises(ValueError):
+        p.decode_reset(torch.empty(n, dtype=torch.uint8))          # host memory
+    p.close()
+
+
 def test_status_strings():
     _lib_or_skip()
     for s in range(7):

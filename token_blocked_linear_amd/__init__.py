@@ -350,11 +350,19 @@ class Plan:
         self.decode_reset(state)
         return state
 
+    def _check_decode_state(self, state):
+        import torch
+        need = mhla_decode_state_size(self.handle)
+        if (not isinstance(state, torch.Tensor) or not state.is_cuda or not state.is_contiguous()
+                or state.numel() * state.element_size() < need):
+            raise ValueError(f"state: expected a contiguous cuda tensor of at least {need} bytes")
+
     def decode_reset(self, state, stream=None):
         import torch
+        self._check_decode_state(state)
         if stream is None:
             stream = torch.cuda.current_stream(state.device)
-        mhla_decode_reset(self.handle, state.data_ptr(), state.numel(), stream.cuda_stream)
+        mhla_decode_reset(self.handle, state.data_ptr(), state.numel() * state.element_size(), stream.cuda_stream)
 
     def decode_step(self, state, t, q, k, v, mc, o, stream=None):
         """Token ``t`` of every (batch, head): q, k, v [B, H, 1, d] of the plan's in_dtype, o the
@@ -371,9 +379,10 @@ class Plan:
         if mc is not None and (tuple(mc.shape) != mc_shape or mc.dtype != torch.float32
                                or not mc.is_contiguous() or not mc.is_cuda):
             raise ValueError(f"mc: expected contiguous float32 cuda tensor {mc_shape}")
+        self._check_decode_state(state)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
-        mhla_decode_step(self.handle, state.data_ptr(), state.numel(), int(t), q.data_ptr(), k.data_ptr(),
+        mhla_decode_step(self.handle, state.data_ptr(), state.numel() * state.element_size(), int(t), q.data_ptr(), k.data_ptr(),
                          v.data_ptr(), mc.data_ptr() if mc is not None else 0, o.data_ptr(), stream.cuda_stream)
         return o
 
