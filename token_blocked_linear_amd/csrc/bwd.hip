@@ -4,10 +4,10 @@
 // take the chain rule of the forward steps (Overall framework, Key design 2) in reverse:
 //   g_t = dO_t / den_t, gden_t = -(dO_t . o_t) / den_t   (normalised; else dO_t, 0)
 //   dq~_t = S~_i g_t + z~_i gden_t                         dq_kernel (also 1/den_t, -(dO_t . o_t))
-//   dz~_i = sum_{t in i} q~_t gden_t                       the summary kernel (below)
-//   dS~_i = sum_{t in i} q~_t g_t^T                        the summary kernel with K := Q, V := g
-//                                                          (g kept in fp32 and split: a bf16 g
-//                                                          costs percents where phi is exp)
+//   dS~_i = sum_{t in i} (q~_t / den_t) dO_t^T              the summary kernel with K := Q scaled
+//   dz~_i = sum_{t in i} q~_t gden_t                        per token by 1/den (fp32, then split
+//                                                          hi / lo), V := dO, normaliser weights
+//                                                          -(dO_t . o_t): no g tensor
 //   dS_b = sum_i m_ib dS~_i, dz_b likewise                 the mixing kernel with M_c^T
 //   dM_c[i, b] = <dS~_i, S_b> + <dz~_i, z_b>                dmc_kernel, dmc_reduce_kernel
 //   dk~_j = dS_b v_j + dz_b, dv_j = dS_b^T k~_j            keyside_kernel
