@@ -187,9 +187,10 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
 /* Streaming decode: one new token per (batch, head) per call, for a causal plan ("MHLA: Restoring
  * Expressivity of Linear Attention via Token-Level Multi-Head", Method -> Key design 4: MHLA is
  * compatible with streaming / stateful inference; the causal reading of the causal readout modes
- * applies).  The plan (readout MHLA_READOUT_CAUSAL_*, a 1D grid of N tokens, blocks of n_b tokens,
- * ragged allowed, no CLS token) fixes the capacity: positions 0 .. N-1, M blocks.  Token t lies in
- * block i = t / n_b and reads
+ * applies).  The plan (readout MHLA_READOUT_CAUSAL_*, a 1D grid, blocks of n_b tokens, ragged
+ * blocks and a CLS token allowed) fixes the capacity: positions 0 .. N-1 (N counting a CLS token),
+ * M blocks.  Token t lies in block i = t / n_b (with a CLS token: block 0 for t = 0, else
+ * 1 + (t - 1) / n_b) and reads
  *     o_t = q~_t^T (S~<_i + m_ii R_t) / q~_t^T (z~<_i + m_ii r_t)    (no division: unnormalised)
  * with S~<_i = sum_{b<i} m_ib S_b over the completed blocks and R_t, r_t the sums of k~ v^T and k~
  * over block i's tokens up to t -- the same values as the causal forward's output t.
@@ -206,8 +207,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
  *   q, k, v device [B, H, 1, d] of the plan's in_dtype; o: device [B, H, 1, d] of its out_dtype
  *   mc      device fp32 M_c as for mhla_forward (NULL iff M == 1)
  * Arithmetic in fp32 (no MFMA: a d x d matrix-vector product per head).  Asynchronous on
- * `stream`; calls on one state must not overlap.  Not supported (MHLA_ERR_UNSUPPORTED): other
- * readouts, a CLS token. */
+ * `stream`; calls on one state must not overlap.  Not supported (MHLA_ERR_UNSUPPORTED): readouts
+ * other than the causal ones. */
 mhla_status mhla_decode_state_size(mhla_handle h, size_t* bytes);
 mhla_status mhla_decode_reset(mhla_handle h, void* state, size_t state_bytes, void* stream);
 mhla_status mhla_decode_step(mhla_handle h, void* state, size_t state_bytes, int64_t t, const void* q,

@@ -250,14 +250,19 @@ def test_decode_support_and_state_size():
     """The decode state: per (batch, head), d^2 + s d floats for each of the M completed blocks,
     the mixed earlier blocks and the running block, where s is the number of channel slices (the
     fewest, of at least max(8, 1024 / d) channels each, that give 512 workgroups); causal plans
-    without a CLS token only."""
+    only."""
     _lib_or_skip()
     for (b, h, d, s) in ((2, 3, 64, 4), (1, 16, 128, 16), (64, 8, 64, 1), (16, 8, 32, 1), (32, 8, 128, 2)):
         p = T.Plan(grid=(1000,), block=(128,), batch=b, heads=h, head_dim=d, readout="causal", ragged=True)
         assert p.info.n_blocks == 8
         assert T.mhla_decode_state_size(p.handle) == b * h * (8 + 2) * (d * d + s * d) * 4, (b, h, d)
         p.close()
-    for kw in (dict(readout="normalized"), dict(readout="causal", cls_token=True)):
+    # a CLS token is one more block (position 0)
+    p = T.Plan(grid=(1000,), block=(125,), batch=1, heads=2, head_dim=64, readout="causal", cls_token=True)
+    assert p.info.n_blocks == 9
+    assert T.mhla_decode_state_size(p.handle) == 2 * (9 + 2) * (64 * 64 + 4 * 64) * 4
+    p.close()
+    for kw in (dict(readout="normalized"), dict(readout="unnormalized", cls_token=True)):
         u = T.Plan(**dict(dict(grid=(1000,), block=(125,), batch=1, heads=1, head_dim=64), **kw))
         with pytest.raises(T.MhlaError) as e:
             T.mhla_decode_state_size(u.handle)

@@ -5,7 +5,8 @@ The reference is the fp64 oracle's causal readout (query t reads every t' <= t w
 m_{b(t), b(t')}), run on the same seeded inputs; the bar is the causal readout's elementwise one,
 |o_t - ref_t| <= tol * max(RMS(ref), |ref_t|), with tol 2e-2 for bf16 inputs and 1e-4 for fp32
 inputs.  The decode state is fp32 throughout.  The cases cover every channel-slice width the
-library picks (8 .. d channels per workgroup, from the number of (batch, head) pairs).  Each case also checks the decoded sequence against
+library picks (8 .. d channels per workgroup, from the number of (batch, head) pairs), and plans
+with a CLS token (position 0, a block of its own).  Each case also checks the decoded sequence against
 the library's own chunkwise causal forward on the same inputs, to the same bar.
 """
 import numpy as np
@@ -21,8 +22,8 @@ BF16_TOL = 2e-2
 FP32_TOL = 1e-4
 
 
-def W(name, dtype, b, h, d, n, nb, seed, mc="softmax_gauss", readout="causal", phi="elu1"):
-    return synth.Workload(name, dtype, b, h, d, (n,), (nb,), seed, mc, readout, phi, ragged=n % nb != 0)
+def W(name, dtype, b, h, d, n, nb, seed, mc="softmax_gauss", readout="causal", phi="elu1", cls=False):
+    return synth.Workload(name, dtype, b, h, d, (n,), (nb,), seed, mc, readout, phi, ragged=n % nb != 0, cls=cls)
 
 
 CASES = [
@@ -41,6 +42,9 @@ CASES = [
     W("dec_batch_d128_c64", "bf16", 16, 16, 128, 300, 64, 608),
     W("dec_batch_d64_c64", "bf16", 64, 8, 64, 200, 48, 609, "softmax_l1"),
     W("dec_batch_d128_c128", "fp32", 32, 16, 128, 130, 32, 610),
+    # a CLS token: position 0 is block 0 on its own, then blocks of n_b (the last one short)
+    W("dec_cls", "bf16", 2, 2, 64, 500, 128, 613, cls=True),
+    W("dec_cls_fp32_unnorm", "fp32", 1, 3, 128, 300, 64, 614, readout="causal_unnormalized", cls=True),
 ]
 
 
@@ -59,9 +63,9 @@ def decode_sequence(w, q, k, v, mc, *, out_dtype="fp32", plan=None, state=None, 
     if own:
         plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
                       in_dtype=w.dtype, out_dtype=out_dtype, readout=w.readout, phi=w.phi,
-                      mc_per_head=mc_per_head, ragged=w.ragged)
+                      mc_per_head=mc_per_head, ragged=w.ragged, cls_token=w.cls)
         state = plan.alloc_decode_state()
-    t1 = w.grid[0] if t1 is None else t1
+    t1 = w.n_tokens if t1 is None else t1
     # token-major copies, so that one token of every (batch, head) is one contiguous [B, H, 1, d]
     seq = [to_device(np.ascontiguousarray(np.moveaxis(x[:, :, t0:t1], 2, 0)), w.dtype) for x in (q, k, v)]
     tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")

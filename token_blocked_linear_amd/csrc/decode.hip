@@ -3,7 +3,7 @@
 // "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head", Method -> Key
 // design 2 (the token-expanded identity q~^T S~_i = sum_t m_{i,b(t)} (q~^T K~_t) V_t^T) and Key
 // design 4 (compatible with streaming / stateful inference).  With the causal reading of the
-// causal readouts, token t of block i = t / n_b reads
+// causal readouts, token t of block i (t / n_b; with a CLS token 0 for t = 0, else 1 + (t - 1) / n_b) reads
 //   o_t = q~_t^T (S~<_i + m_ii R_t) / q~_t^T (z~<_i + m_ii r_t),   S~<_i = sum_{b<i} m_ib S_b,
 // R_t = sum of k~ v^T over block i's tokens up to t (r_t: of k~).  The state is fp32.
 //
@@ -56,7 +56,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
   float4* R4 = reinterpret_cast<float4*>(R);
   const int DC4 = DC / 4;
 
-  const int i = (int)(p.t / p.nb), pos = (int)(p.t % p.nb);
+  // block i of position t and t's place in it (with a CLS token: block 0 is position 0 alone)
+  const int64_t tg = p.t - p.cls;
+  const int i = tg < 0 ? 0 : (int)(tg / p.nb) + p.cls, pos = tg < 0 ? 0 : (int)(tg % p.nb);
   const float* mrow = p.mc ? p.mc + (int64_t)h * p.mc_head_stride + (int64_t)i * M : nullptr;
   const float mii = mrow ? mrow[i] : 1.0f;
 

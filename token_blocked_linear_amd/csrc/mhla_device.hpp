@@ -258,6 +258,7 @@ struct DecodeParams {
   int32_t H, M, nb, BH;    // nb: tokens per block
   int32_t normalized;
   int32_t log2_c;          // channels per workgroup = 2^log2_c (8 .. D); D >> log2_c workgroups per head
+  int32_t cls;             // 1: position 0 is a CLS token, a block of its own; blocks of nb follow
 };
 
 // MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,

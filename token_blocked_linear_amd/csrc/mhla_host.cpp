@@ -762,7 +762,7 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
 
 // ---- streaming decode --------------------------------------------------------------------
 static mhla_status decode_supported(const mhla_plan* h) {
-  if (!h->causal || h->geom.cls) return MHLA_ERR_UNSUPPORTED;
+  if (!h->causal) return MHLA_ERR_UNSUPPORTED;
   return MHLA_OK;
 }
 // channels per decode workgroup, as log2: the head's d channels are cut into the fewest slices
@@ -827,6 +827,7 @@ mhla_status mhla_decode_step(mhla_handle h, void* state, size_t state_bytes, int
     p.BH = (int32_t)h->BH;
     p.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
     p.log2_c = decode_log2_c(h);
+    p.cls = h->geom.cls;
     const hipError_t e = mhla::launch_decode_step(p, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
                                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
