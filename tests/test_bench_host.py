@@ -52,3 +52,33 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_decode_accounting_by_hand():
+    """Decode bytes: 12 d^2 + 12 d + 3 d s_in + d s_out per call and (batch, head), plus
+    4 d^2 (i + 3) + 12 d at the first position of block i > 0."""
+    d, nb = 128, 256
+    per = 12 * d * d + 12 * d + 3 * d * 2 + d * 2
+    # positions 0 .. 255: block 0 only, no block start after the first
+    assert bench.decode_accounting(1, d, nb, 0, 256, 2, 2) == 256 * per
+    # positions 0 .. 767: blocks 1 and 2 start inside
+    extra = (4 * d * d * 4 + 12 * d) + (4 * d * d * 5 + 12 * d)
+    assert bench.decode_accounting(1, d, nb, 0, 768, 2, 2) == 768 * per + extra
+    # a window that starts at a block start counts it; (batch, head) pairs scale linearly
+    assert bench.decode_accounting(3, d, nb, 256, 512, 2, 2) == 3 * (256 * per + 4 * d * d * 4 + 12 * d)
+
+
+def test_digest_ignores_the_peak_probe(tmp_path, monkeypatch):
+    """The measured-peak probe is outside the MHLA path: editing it leaves the digest alone, while
+    any kernel source changes it."""
+    import shutil
+    root = tmp_path / "r"
+    for d in bench.SOURCE_DIRS:
+        shutil.copytree(os.path.join(ROOT, d), root / d)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    d0 = bench.source_digest()
+    (root / "token_blocked_linear_amd/csrc/peak_probe.hip").write_text("// changed\n")
+    assert bench.source_digest() == d0
+    with open(root / "token_blocked_linear_amd/csrc/decode.hip", "a") as f:
+        f.write("\n// changed\n")
+    assert bench.source_digest() != d0
