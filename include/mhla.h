@@ -205,7 +205,10 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
  *           in order (t outside [0, N): MHLA_ERR_INVALID_ARG).  At the first token of a block the
  *           call also stores the finished block's summary and forms S~<_i from row i of M_c.
  *   q, k, v device [B, H, 1, d] of the plan's in_dtype; o: device [B, H, 1, d] of its out_dtype
- *   mc      device fp32 M_c as for mhla_forward (NULL iff M == 1)
+ *   mc      device fp32 M_c as for mhla_forward (NULL iff M == 1).  Every call reads m_ii of its
+ *           block; the first call of block i also reads row i below the diagonal.  So a caller
+ *           that changes M_c between calls gets the causal readout of the M_c current at each
+ *           block's start only if it changes M_c at block starts.
  * Arithmetic in fp32 (no MFMA: a d x d matrix-vector product per head).  Asynchronous on
  * `stream`; calls on one state must not overlap.  Not supported (MHLA_ERR_UNSUPPORTED): readouts
  * other than the causal ones. */
