@@ -152,6 +152,45 @@ def test_size_limits():
     assert _status(_desc(grid=(65536,), block=(1,), batch=1, heads=1, head_dim=32)) == 3
 
 
+# Descriptors whose extents are each representable but whose products are not: build_plan must
+# bound every factor before it multiplies (an unchecked product once wrapped to N = 0 and the
+# plan then divided by it).  Run in a child process so that a crash fails the test instead of
+# ending the test session.
+OVERFLOW_DESCS = [
+    dict(grid=(1 << 31, 1 << 31, 1 << 31), block=(1 << 31, 1 << 31, 1 << 31), ndim3=True),
+    dict(grid=((1 << 31) - 1, (1 << 31) - 1, (1 << 31) - 1), block=(1, 1, 1), ndim3=True),
+    dict(grid=(1 << 16, 1 << 16), block=(1, 1)),
+    dict(grid=(1 << 20, 1 << 20), block=(1 << 20, 1 << 20)),
+    dict(grid=(1 << 62,), block=(1 << 62,)),
+    dict(grid=(64,), block=(64,), batch=1 << 40, heads=1 << 40),
+    dict(grid=(64,), block=(64,), batch=(1 << 31) + 1, heads=2),
+]
+
+
+def test_products_of_large_extents_are_rejected_not_computed():
+    _lib_or_skip()
+    code = f"""
+import sys
+sys.path.insert(0, {ROOT!r})
+import ctypes
+import token_blocked_linear_amd as T
+cases = {OVERFLOW_DESCS!r}
+lib = T.load_library()
+for c in cases:
+    c = dict(c)
+    c.pop("ndim3", None)
+    d = T.make_desc(grid=c["grid"], block=c["block"], batch=c.get("batch", 1), heads=c.get("heads", 1),
+                    head_dim=64)
+    h = ctypes.c_void_p()
+    st = lib.mhla_create(ctypes.byref(d), ctypes.byref(h))
+    print(st, flush=True)
+"""
+    r = subprocess.run([__import__("sys").executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stderr[-2000:])
+    statuses = [int(x) for x in r.stdout.split()]
+    assert statuses == [3] * len(OVERFLOW_DESCS), statuses
+
+
 def test_create_null_arguments():
     lib = _lib_or_skip()
     h = ctypes.c_void_p()

@@ -24,7 +24,7 @@
 #define MHLA_SUMMARY_LOAD_CPOL 2      // K, V
 #endif
 #ifndef MHLA_MIX_LOAD_CPOL
-#define MHLA_MIX_LOAD_CPOL 2          // the summary stack
+#define MHLA_MIX_LOAD_CPOL 0          // the summary stack (default: it is read from the infinity cache)
 #endif
 #ifndef MHLA_READOUT_LOAD_CPOL
 #define MHLA_READOUT_LOAD_CPOL 0      // Q
@@ -132,17 +132,19 @@ struct SummaryParams {
 
 // Launch shape of the MFMA mixing kernel for M blocks: nbc 32-block chunks of the contraction,
 // itw 16-row i-tiles per wave, wave_rows waves sharing a row group's i-tiles, row_groups
-// workgroups per column tile.  Shared by the host plan and the kernel launcher.
+// workgroups per column tile.  Shared by the host plan and the kernel launcher.  `split`: fp32
+// partials and M_c as hi + lo; `wlo`: the bf16 stack against M_c as hi + lo (both hold twice the
+// W fragments, so beyond 128 blocks they take the 8-wave shape).
 struct MixShape {
   int nbc, itw, wave_rows, row_groups, nitp, nw;
 };
-inline MixShape mix_shape(int M, bool split) {
+inline MixShape mix_shape(int M, bool split, bool wlo = false) {
   MixShape s;
   const int nbc = (M + 31) / 32;
   s.nbc = nbc <= 1 ? 1 : nbc <= 2 ? 2 : nbc <= 4 ? 4 : 8;
   const int nit = (M + 15) / 16;
   s.nw = 4;
-  if (split && s.nbc == 8) {
+  if ((split || wlo) && s.nbc == 8) {
     // split, M > 128: one workgroup of 8 waves x 2 i-tiles covers all 256 rows, so the tile is
     // loaded, split and transposed once (four 4-wave row groups would each do it)
     s.nw = 8;
@@ -268,7 +270,7 @@ struct MixMfmaParams {
   const float* xf;         // fp32 partials [BH][M][xsplits][FRAG] (split kernel)
   const float* z;          // fp32 partials [BH][M][zsplits][D]
   const uint16_t* mcf;     // bf16 W operand fragments (see SummaryParams); hi part if split
-  const uint16_t* mcf_lo;  // low part (split kernel)
+  const uint16_t* mcf_lo;  // low part (split kernel, and the bf16 kernel with W as hi + lo)
   int32_t mcf_per_head;    // 1: fragments per head, 0: shared
   uint16_t* y;             // bf16 [BH][M][FRAG]; hi part if split
   uint16_t* y_lo;          // low part (split kernel)

@@ -19,9 +19,9 @@ hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool spli
 hipError_t launch_summary_tokw(const SummaryParams& p, int d, bool in_fp32, bool v_fp32, int phi, int n_units,
                                hipStream_t stream);
 hipError_t launch_mix(const MixParams& p, int d, int frag, int bh, bool split, hipStream_t stream);
-hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stream);
+hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, bool wlo, hipStream_t stream);
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
-                          bool split, int fuse, int phi, int n_wg, hipStream_t stream);
+                          bool split, int fuse, bool q_stream, int phi, int n_wg, hipStream_t stream);
 hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
                             bool key_side, int n_units, hipStream_t stream);
 hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream);
@@ -42,6 +42,14 @@ enum { kFuseNone = 0, kFuseBf16 = 1, kFusePartials = 2 };
 #define MHLA_FUSE_MAX_BLOCKS 16
 #endif
 constexpr int kFuseMaxBlocks = MHLA_FUSE_MAX_BLOCKS;
+#ifndef MHLA_MIX_IN_PLACE
+#define MHLA_MIX_IN_PLACE 1
+#endif
+constexpr bool kMixInPlace = MHLA_MIX_IN_PLACE != 0;
+#ifndef MHLA_MIX_MC_SPLIT
+#define MHLA_MIX_MC_SPLIT 1
+#endif
+constexpr bool kMixMcSplit = MHLA_MIX_MC_SPLIT != 0;
 
 // Timing: one event before a call's first kernel and one after each of its kernels.
 constexpr int kMaxTimedKernels = 7;
@@ -69,8 +77,11 @@ struct mhla_plan {
   bool in_fp32, out_fp32, mala, split, split_v;
   bool mix_mfma;   // bf16 summary stack (mixed on MFMA or in the readout prologue)
   bool mix_split;  // mixing kernel on MFMA with split operands over fp32 partials
+  bool mix_wlo;    // the bf16 mixing kernel takes M_c as bf16 hi + lo
   bool causal;     // chunkwise-causal readout (1D)
   bool mix_kernel; // a mixing kernel of its own is launched
+  bool mix_in_place; // the mixing kernel overwrites the bf16 summary stack with the mixed one
+  bool q_stream;     // the readout loads the queries with the non-temporal policy
   int fuse;        // kFuse*: where the mixing step runs
   int n_kernels;
   const char* kernel_names[kMaxKernels];
@@ -151,24 +162,33 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
     return MHLA_ERR_UNSUPPORTED;
   if (d->ndim < 1 || d->ndim > 3) return MHLA_ERR_SHAPE;
   if (d->batch < 1 || d->heads < 1) return MHLA_ERR_SHAPE;
+  if (d->batch > 65535 || d->heads > 65535) return MHLA_ERR_SHAPE;   // before their product
 
+  // Extents below 2^31 each; the token and block counts are built one axis at a time and
+  // bounded after every factor, so no product can overflow (each factor and each partial
+  // product stays below 2^31).
+  constexpr int64_t kLim = (int64_t)1 << 31;
   int64_t grid[3] = {1, 1, 1}, block[3] = {1, 1, 1};
   const int pad = 3 - d->ndim;
   int64_t nblk[3] = {1, 1, 1};
+  int64_t n_grid = 1, n_blk = 1, nb = 1;
   for (int a = 0; a < d->ndim; ++a) {
     if (d->grid[a] < 1 || d->block[a] < 1) return MHLA_ERR_SHAPE;
+    if (d->grid[a] >= kLim) return MHLA_ERR_SHAPE;
     if (d->grid[a] % d->block[a] != 0 && !ragged) return MHLA_ERR_SHAPE;
-    if (d->grid[a] > (int64_t)1 << 31) return MHLA_ERR_SHAPE;
     grid[pad + a] = d->grid[a];
     block[pad + a] = std::min(d->block[a], d->grid[a]);   // a block never exceeds the grid
     nblk[pad + a] = (grid[pad + a] + block[pad + a] - 1) / block[pad + a];
+    n_grid *= grid[pad + a];
+    if (n_grid >= kLim) return MHLA_ERR_SHAPE;
+    n_blk *= nblk[pad + a];
+    if (n_blk > 65535) return MHLA_ERR_SHAPE;
+    nb *= block[pad + a];                                 // <= n_grid: bounded with it
   }
-  const int64_t N = cls + grid[0] * grid[1] * grid[2];
-  const int64_t nb = block[0] * block[1] * block[2];      // tokens of a whole block
-  if (N >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
-  if (nblk[0] * nblk[1] * nblk[2] > 65535) return MHLA_ERR_SHAPE;
-  const int64_t M = cls + nblk[0] * nblk[1] * nblk[2];
-  const int64_t BH = d->batch * d->heads;
+  const int64_t N = cls + n_grid;                          // tokens per head
+  if (N >= kLim) return MHLA_ERR_SHAPE;
+  const int64_t M = cls + n_blk;
+  const int64_t BH = d->batch * d->heads;                  // < 2^32: no overflow
   if (BH > 65535 || M > 65535) return MHLA_ERR_SHAPE;
   if (d->readout == MHLA_READOUT_MALA && M != 1) return MHLA_ERR_UNSUPPORTED;
   const bool causal = d->readout == MHLA_READOUT_CAUSAL_NORMALIZED || d->readout == MHLA_READOUT_CAUSAL_UNNORMALIZED;
@@ -285,18 +305,35 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   P->off_ps = off;   off = align256(off + (P->mix_mfma ? 0 : slots * f * 4));
   P->off_pz = off;   off = align256(off + slots * dd * 4);
   P->off_pu = off;   off = align256(off + (P->mala ? slots * dd * 4 : 0));
-  P->off_st_hi = off; off = align256(off + (mix_kernel ? (size_t)BH * M * f * 2 : 0));
+  // The MFMA mixing of the bf16 stack overwrites the stack in place: for M <= 256 one workgroup
+  // covers every row of a column tile and has the whole tile in LDS before its first store, so
+  // the mixed stack needs no space of its own (and the stack traffic of a step touches half as
+  // many bytes, which then stay in the infinity cache between the three kernels).
+  // The bf16 stack's mixing takes M_c as hi + lo: one bf16 M_c perturbs each weight by up to 2^-9
+  // relative, the largest rounding of the bf16 path (M_c enters the fused prologue in fp32).
+  P->mix_wlo = kMixMcSplit && mix_kernel && P->mix_mfma;
+  P->mix_in_place =
+      kMixInPlace && mix_kernel && P->mix_mfma && mhla::mix_shape((int)M, false, P->mix_wlo).row_groups == 1;
+  if (P->mix_in_place) {
+    P->off_st_hi = P->off_sb;
+  } else {
+    P->off_st_hi = off;
+    off = align256(off + (mix_kernel ? (size_t)BH * M * f * 2 : 0));
+  }
+  // Queries larger than half the 256 MiB infinity cache are streamed past it (nt), so that they
+  // do not evict the mixed stack the readout is reading; smaller ones keep the default policy.
+  P->q_stream = mix_kernel && P->mix_mfma && !causal && BH * N * d->head_dim * 2 > ((int64_t)128 << 20);
   P->off_st_lo = off;
   off = align256(off + (mix_kernel && (P->split || P->mix_split) ? (size_t)BH * M * f * 2 : 0));
   P->off_zt = off;   off = align256(off + (mix_kernel ? (size_t)BH * M * dd * 4 : 0));
   // bf16 M_c operand fragments (and their low parts) for the MFMA mixing kernel
   P->mcf_heads = d->mc_per_head ? (int)d->heads : 1;
-  P->mix = mhla::mix_shape((int)M, P->mix_split);
+  P->mix = mhla::mix_shape((int)M, P->mix_split, P->mix_wlo);
   const size_t mcf_bytes = (size_t)P->mcf_heads * P->mix.nitp * P->mix.nbc * 512 * 2;
   P->off_mcf = off;
   off = align256(off + (mix_kernel && (P->mix_mfma || P->mix_split) ? mcf_bytes : 0));
   P->off_mcf_lo = off;
-  off = align256(off + (P->mix_split ? mcf_bytes : 0));
+  off = align256(off + (P->mix_split || P->mix_wlo ? mcf_bytes : 0));
   P->ws_bytes = off;
   if (BH * M * P->rd_splits >= ((int64_t)1 << 31)) return MHLA_ERR_SHAPE;
 
@@ -392,7 +429,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     sp.mc = mc;
     sp.mc_head_stride = mc_stride;
     sp.mcf = (mix_kernel && (h->mix_mfma || h->mix_split)) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
-    sp.mcf_lo = h->mix_split ? reinterpret_cast<uint16_t*>(ws + h->off_mcf_lo) : nullptr;
+    sp.mcf_lo = (h->mix_split || h->mix_wlo) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf_lo) : nullptr;
     sp.mcf_transposed = 0;
     sp.mcf_causal = h->causal ? 1 : 0;
     sp.mcf_heads = h->mcf_heads;
@@ -420,7 +457,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
         mm.H = (int32_t)h->H;
         mm.D = h->d;
         mm.frag = h->frag;
-        e = mhla::launch_mix_mfma(mm, (int)h->BH, h->mix_split, s);
+        e = mhla::launch_mix_mfma(mm, (int)h->BH, h->mix_split, h->mix_wlo, s);
       } else {
         mhla::MixParams mp;
         mp.ps = ps;
@@ -494,7 +531,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
     rp.mc_head_stride = mc_stride;
     rp.H = (int32_t)h->H;
     rp.ssplits = h->sum_splits;
-    e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse,
+    e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse, h->q_stream,
                              (int)h->desc.phi, (int)(h->rd_splits * h->M * h->BH), s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
     return MHLA_OK;
@@ -655,7 +692,7 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
         mm.H = (int32_t)h->H;
         mm.D = h->d;
         mm.frag = h->frag;
-        return mhla::launch_mix_mfma(mm, (int)h->BH, true, s);
+        return mhla::launch_mix_mfma(mm, (int)h->BH, true, false, s);
       }
       mhla::MixParams mp = {};
       mp.ps = xs;

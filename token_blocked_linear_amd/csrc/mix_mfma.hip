@@ -21,7 +21,11 @@
 // (z = hi + lo to about 2^-17) and leaves as fp32 z~ = Y[hi col] + Y[lo col].
 //
 // Two precisions:
-//   SPLIT = false  bf16 stack (one token slice per block) and bf16 W: the bf16 forward;
+//   SPLIT = false  bf16 stack (one token slice per block): the bf16 forward.  With WLO, W enters
+//                  as bf16 hi + lo (two MFMAs per product, W to about 2^-17): rounding M_c to one
+//                  bf16 would perturb every mixing weight by up to 2^-9 relative, and since S~_i
+//                  averages many summaries of both signs, that error does not average away
+//                  (it is the largest rounding of the bf16 path);
 //   SPLIT = true   fp32 partial summaries, summed over their token slices as they are loaded,
 //                  and W, both as bf16 hi + lo; three MFMAs per product (hi*hi + lo*hi + hi*lo,
 //                  about 2^-16 relative) and Y leaves as bf16 hi and lo.  One i-tile per wave
@@ -31,9 +35,10 @@
 namespace mhla {
 
 // NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave; NW:
-// waves per workgroup.  With NW = 8 (the split kernel at M > 128) a loader thread takes 8 rows
-// x 4 columns of the tile instead of 8 x 8, so that the tile's registers halve.
-template <int NBC, int ITW, bool SPLIT, int NW = 4>
+// waves per workgroup.  With NW = 8 (the split kernel and the bf16 kernel with WLO at M > 128) a
+// loader thread takes 8 rows x 4 columns of the tile instead of 8 x 8, so that the tile's
+// registers halve.
+template <int NBC, int ITW, bool SPLIT, int NW = 4, bool WLO = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void mix_mfma_kernel(
     MixMfmaParams p) {
   constexpr int MPAD = 32 * NBC;
@@ -43,7 +48,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int LC = NW == 8 ? 4 : 8;     // tile columns per loader thread
   constexpr int CG = PB / LC;             // column groups per tile
   static_assert(NW * 64 / CG * 8 == MPAD, "the loader threads cover the padded blocks once");
-  static_assert(NW == 4 || SPLIT, "8 waves: the split kernel only");
+  static_assert(NW == 4 || SPLIT || WLO, "8 waves: W as hi + lo only");
+  constexpr bool HAS_LO = SPLIT || WLO;   // W fragments as hi + lo
   // LDS bank swizzle on the 16-byte chunks (8 blocks) of a transposed column r: columns are
   // written 8 apart (r = 8*cg + e) and read 8 consecutive (r = 16*pt + pr).  With >= 8 chunks
   // per column, chunk c lives at c ^ ((r & 7) ^ ((r >> 3) & 7)); a 64-byte column (MPAD = 32)
@@ -72,14 +78,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // W^T operand fragments: lane holds W[16*it + pr][32*bc + 8*lg + e], e = 0..7, one 16-byte
   // load each.
   const int64_t fofs = (int64_t)(p.mcf_per_head ? bh % p.H : 0) * nitp * NBC * 512;
-  u32x4_t bfrag[ITW][NBC], bfrag_lo[SPLIT ? ITW : 1][SPLIT ? NBC : 1];
+  u32x4_t bfrag[ITW][NBC], bfrag_lo[HAS_LO ? ITW : 1][HAS_LO ? NBC : 1];
 #pragma unroll
   for (int a = 0; a < ITW; ++a)
 #pragma unroll
     for (int bc = 0; bc < NBC; ++bc) {
       const int64_t o = fofs + (((int64_t)(it0 + a) * NBC + bc) * 64 + lane) * 8;
       bfrag[a][bc] = ld16(p.mcf + o);
-      if constexpr (SPLIT) bfrag_lo[a][bc] = ld16(p.mcf_lo + o);
+      if constexpr (HAS_LO) bfrag_lo[a][bc] = ld16(p.mcf_lo + o);
     }
 
   const int P = p.frag;
@@ -119,11 +125,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           }
         }
       }
-    } else {
+    } else if constexpr (LC == 8) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int b = 8 * rg + r;
         raw[r] = buf_ld16<MHLA_MIX_LOAD_CPOL>(rsx, b < M ? (uint32_t)(b * P + tile * PB + 8 * cg) * 2u : kOutOfRange);
+      }
+    } else {   // 4 bf16 columns per row: words 0 and 1 (the transpose reads no others)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int b = 8 * rg + r;
+        const u32x2_t w = buf_ld8(rsx, b < M ? (uint32_t)(b * P + tile * PB + 4 * cg) * 2u : kOutOfRange);
+        raw[r] = u32x4_t{w[0], w[1], 0u, 0u};
       }
     }
   };
@@ -277,6 +290,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             const u32x4_t afrag = *reinterpret_cast<const u32x4_t*>(xt + ofs);
 #pragma unroll
             for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag[a][bc], accs[pt][a]);
+            if constexpr (WLO) {
+#pragma unroll
+              for (int a = 0; a < ITW; ++a) accs[pt][a] = mfma_bf16(afrag, bfrag_lo[a][bc], accs[pt][a]);
+            }
             // with 128 registers of M_c fragments, keep each operand read next to its MFMAs
             if constexpr (NBC * ITW >= 32) __builtin_amdgcn_sched_barrier(0);
           }
@@ -350,24 +367,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-template <int NBC, int ITW, bool SPLIT, int NW>
+template <int NBC, int ITW, bool SPLIT, int NW, bool WLO = false>
 static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipStream_t s) {
   constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD;
   const size_t lds = (size_t)PB * XP * 2 * (SPLIT ? 2 : 1);
-  auto kern = mix_mfma_kernel<NBC, ITW, SPLIT, NW>;
+  auto kern = mix_mfma_kernel<NBC, ITW, SPLIT, NW, WLO>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.n_wg_x, row_groups, bh), dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
 
-// Launch with the shape mix_shape(M, split) (the host sized the W fragments with the same shape).
-hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stream) {
+// Launch with the shape mix_shape(M, split, wlo) (the host sized the W fragments with the same
+// shape).  wlo: the bf16 kernel with W as hi + lo (mcf_lo required).
+hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, bool wlo, hipStream_t stream) {
   const int M = p.M;
   if (M < 1 || M > 256) return hipErrorInvalidValue;
   if (split ? (!p.xf || !p.mcf_lo || !p.y_lo || p.xsplits < 1) : (!p.x || p.zsplits != 1))
     return hipErrorInvalidValue;
-  const MixShape sh = mix_shape(M, split);
+  if (split && wlo) return hipErrorInvalidValue;
+  if (wlo && !p.mcf_lo) return hipErrorInvalidValue;
+  const MixShape sh = mix_shape(M, split, wlo);
   const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups, NW = sh.nw;
   p.wave_rows = sh.wave_rows;
   if (NBC >= 2 && sh.wave_rows != NW) return hipErrorInvalidValue;   // the kernel assumes WPW = 1
@@ -386,11 +406,14 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, hipStream_t stre
   // tile they all load is fetched from HBM once into that XCD's L2
   if (row_groups > 1 && want > 8) want &= ~7;
   p.n_wg_x = want;
-#define MHLA_MIX_CASE(N, I, S, W) \
-  if (NBC == N && ITW == I && split == S && NW == W) return launch_t<N, I, S, W>(p, row_groups, bh, stream);
-  MHLA_MIX_CASE(1, 1, false, 4) MHLA_MIX_CASE(2, 1, false, 4) MHLA_MIX_CASE(4, 2, false, 4)
-  MHLA_MIX_CASE(8, 4, false, 4) MHLA_MIX_CASE(1, 1, true, 4) MHLA_MIX_CASE(2, 1, true, 4)
-  MHLA_MIX_CASE(4, 1, true, 4) MHLA_MIX_CASE(8, 2, true, 8)
+#define MHLA_MIX_CASE(N, I, S, W, L) \
+  if (NBC == N && ITW == I && split == S && NW == W && wlo == L) \
+    return launch_t<N, I, S, W, L>(p, row_groups, bh, stream);
+  MHLA_MIX_CASE(1, 1, false, 4, false) MHLA_MIX_CASE(2, 1, false, 4, false) MHLA_MIX_CASE(4, 2, false, 4, false)
+  MHLA_MIX_CASE(8, 4, false, 4, false) MHLA_MIX_CASE(1, 1, true, 4, false) MHLA_MIX_CASE(2, 1, true, 4, false)
+  MHLA_MIX_CASE(4, 1, true, 4, false) MHLA_MIX_CASE(8, 2, true, 8, false)
+  MHLA_MIX_CASE(1, 1, false, 4, true) MHLA_MIX_CASE(2, 1, false, 4, true) MHLA_MIX_CASE(4, 2, false, 4, true)
+  MHLA_MIX_CASE(8, 2, false, 8, true)
 #undef MHLA_MIX_CASE
   return hipErrorInvalidValue;
 }

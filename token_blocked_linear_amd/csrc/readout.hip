@@ -189,7 +189,7 @@ __device__ inline RdUnit rd_unit(const ReadoutParams& p, int L) {
 
 // Issue the query loads of tile t of unit u into `dst` through a buffer resource over the
 // unit's head: tokens past the slice and key features beyond D (d = 16) read as zero.
-template <typename TIn, int D>
+template <typename TIn, int D, int QPOL>
 __device__ inline void rd_issue(const ReadoutParams& p, const RdUnit& u, int t, int lane,
                                 In8<TIn> (&dst)[Dims<D>::NKC], bool& v, int64_t& off) {
   constexpr uint32_t ES = sizeof(TIn);
@@ -202,7 +202,7 @@ __device__ inline void rd_issue(const ReadoutParams& p, const RdUnit& u, int t, 
 #pragma unroll
   for (int kc = 0; kc < Dims<D>::NKC; ++kc) {
     const int k0 = 32 * kc + 8 * lg;
-    dst[kc].template load_buf<MHLA_READOUT_LOAD_CPOL>(rsq, (v && k0 < D) ? (rel + k0) * ES : kOutOfRange);
+    dst[kc].template load_buf<QPOL>(rsq, (v && k0 < D) ? (rel + k0) * ES : kOutOfRange);
   }
 }
 
@@ -214,7 +214,10 @@ constexpr int readout_tiles_per_step() { return sizeof(TIn) == 2 && D <= 64 ? MH
 template <typename TIn, int D>
 constexpr int readout_waves() { return sizeof(TIn) == 4 && D == 128 ? 3 : 4; }
 
-template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE, int PHI>
+// QPOL: cache policy of the query loads (MHLA_READOUT_LOAD_CPOL, or 2 = nt when the queries
+// of one launch are larger than about half the infinity cache and would only evict the
+// summaries from it).
+template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE, int PHI, int QPOL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     readout_waves<TIn, D>()))) void readout_kernel(
     ReadoutParams p, int mode) {
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
       valid[j] = false;
       toff[j] = 0;
       if (t0 + j * WSTEP < U.n_tiles) {
-        rd_issue<TIn, D>(p, U, t0 + j * WSTEP, lane, raw[j], valid[j], toff[j]);
+        rd_issue<TIn, D, QPOL>(p, U, t0 + j * WSTEP, lane, raw[j], valid[j], toff[j]);
       } else {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) raw[j][kc].zero();
@@ -459,11 +462,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <int PHI, typename TIn, typename TOut, int D, bool SPLIT, int FUSE>
+template <int PHI, typename TIn, typename TOut, int D, bool SPLIT, int FUSE, int QPOL = MHLA_READOUT_LOAD_CPOL>
 static hipError_t launch_t(const ReadoutParams& p, int mode, int n_wg, hipStream_t s) {
   using Dm = Dims<D>;
   const size_t lds = (size_t)Dm::FRAG * 2 * (SPLIT ? 2 : 1) + (size_t)Dm::NKC * 512 * 2 + 2 * D * 4;
-  hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, SPLIT, FUSE, PHI>), dim3(n_wg), dim3(kThreads), lds,
+  hipLaunchKernelGGL((readout_kernel<TIn, TOut, D, SPLIT, FUSE, PHI, QPOL>), dim3(n_wg), dim3(kThreads), lds,
                      s, p, mode);
   return hipGetLastError();
 }
@@ -471,12 +474,15 @@ static hipError_t launch_t(const ReadoutParams& p, int mode, int n_wg, hipStream
 // Valid (split, fuse) pairs: the bf16-stack fusion exists for bf16 operands only; the others
 // for both operand precisions.
 template <int PHI, typename TIn, typename TOut, int D>
-static hipError_t dispatch_fuse(const ReadoutParams& p, int mode, bool split, int fuse, int n_wg,
-                                hipStream_t s) {
+static hipError_t dispatch_fuse(const ReadoutParams& p, int mode, bool split, int fuse, bool q_stream,
+                                int n_wg, hipStream_t s) {
   if (split) {
     if (fuse == kFuseNone) return launch_t<PHI, TIn, TOut, D, true, kFuseNone>(p, mode, n_wg, s);
     if (fuse == kFusePartials) return launch_t<PHI, TIn, TOut, D, true, kFusePartials>(p, mode, n_wg, s);
     return hipErrorInvalidValue;
+  }
+  if constexpr (sizeof(TIn) == 2) {   // the streamed-query variant: bf16 stacks of many blocks
+    if (fuse == kFuseNone && q_stream) return launch_t<PHI, TIn, TOut, D, false, kFuseNone, 2>(p, mode, n_wg, s);
   }
   if (fuse == kFuseNone) return launch_t<PHI, TIn, TOut, D, false, kFuseNone>(p, mode, n_wg, s);
   if (fuse == kFusePartials) return launch_t<PHI, TIn, TOut, D, false, kFusePartials>(p, mode, n_wg, s);
@@ -487,27 +493,28 @@ static hipError_t dispatch_fuse(const ReadoutParams& p, int mode, bool split, in
 }
 
 template <int PHI, typename TIn, typename TOut>
-static hipError_t dispatch_d(const ReadoutParams& p, int d, int mode, bool split, int fuse,
+static hipError_t dispatch_d(const ReadoutParams& p, int d, int mode, bool split, int fuse, bool qs,
                              int n_wg, hipStream_t s) {
   switch (d) {
-    case 16: return dispatch_fuse<PHI, TIn, TOut, 16>(p, mode, split, fuse, n_wg, s);
-    case 32: return dispatch_fuse<PHI, TIn, TOut, 32>(p, mode, split, fuse, n_wg, s);
-    case 64: return dispatch_fuse<PHI, TIn, TOut, 64>(p, mode, split, fuse, n_wg, s);
-    case 128: return dispatch_fuse<PHI, TIn, TOut, 128>(p, mode, split, fuse, n_wg, s);
+    case 16: return dispatch_fuse<PHI, TIn, TOut, 16>(p, mode, split, fuse, qs, n_wg, s);
+    case 32: return dispatch_fuse<PHI, TIn, TOut, 32>(p, mode, split, fuse, qs, n_wg, s);
+    case 64: return dispatch_fuse<PHI, TIn, TOut, 64>(p, mode, split, fuse, qs, n_wg, s);
+    case 128: return dispatch_fuse<PHI, TIn, TOut, 128>(p, mode, split, fuse, qs, n_wg, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-// n_wg = splits * M * BH workgroups (one-dimensional grid).
+// n_wg = splits * M * BH workgroups (one-dimensional grid).  q_stream: load the queries with the
+// non-temporal policy (bf16 inputs, single bf16 operands, a mixing kernel of its own).
 hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_fp32, int mode,
-                          bool split, int fuse, int phi, int n_wg, hipStream_t stream) {
+                          bool split, int fuse, bool q_stream, int phi, int n_wg, hipStream_t stream) {
   auto go = [&](auto phi_c) {
     constexpr int PHI = decltype(phi_c)::value;
     if (in_fp32)
-      return out_fp32 ? dispatch_d<PHI, float, float>(p, d, mode, split, fuse, n_wg, stream)
-                      : dispatch_d<PHI, float, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
-    return out_fp32 ? dispatch_d<PHI, uint16_t, float>(p, d, mode, split, fuse, n_wg, stream)
-                    : dispatch_d<PHI, uint16_t, uint16_t>(p, d, mode, split, fuse, n_wg, stream);
+      return out_fp32 ? dispatch_d<PHI, float, float>(p, d, mode, split, fuse, q_stream, n_wg, stream)
+                      : dispatch_d<PHI, float, uint16_t>(p, d, mode, split, fuse, q_stream, n_wg, stream);
+    return out_fp32 ? dispatch_d<PHI, uint16_t, float>(p, d, mode, split, fuse, q_stream, n_wg, stream)
+                    : dispatch_d<PHI, uint16_t, uint16_t>(p, d, mode, split, fuse, q_stream, n_wg, stream);
   };
   switch (phi) {
     case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
