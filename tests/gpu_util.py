@@ -2,6 +2,8 @@
 compare with the fp64 oracle."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -45,6 +47,18 @@ def rel_err(got, want):
     want = np.asarray(want, np.float64)
     rms = float(np.sqrt(np.mean(want * want)))
     return float(np.max(np.abs(np.asarray(got, np.float64) - want))) / rms
+
+
+def record(kind: str, case: str, **values) -> None:
+    """Append one JSON line {kind, case, values...} to the file named by PARITY_METRICS_OUT (when
+    set), so that a run's measured parity figures can be tabulated; numbers are rounded to 4
+    significant digits."""
+    path = os.environ.get("PARITY_METRICS_OUT")
+    if not path:
+        return
+    vals = {k: (float(f"{v:.4g}") if isinstance(v, float) else v) for k, v in values.items()}
+    with open(path, "a") as f:
+        f.write(json.dumps({"kind": kind, "case": case, **vals}) + "\n")
 
 
 def announce(msg: str) -> None:

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import announce, oracle_full, run_hip, to_device
+from gpu_util import announce, oracle_full, record, rel_err, run_hip, to_device
 import token_blocked_linear_amd as T
 
 pytestmark = pytest.mark.gpu
@@ -97,9 +97,13 @@ def test_decode_matches_causal_readout(w):
     err = causal_err(got, want)
     chunk = run_hip(w, q, k, v, mc)
     err_chunk = causal_err(got, chunk)
-    print(f"  err={err:.3e} vs chunkwise forward {err_chunk:.3e}")
+    plain = rel_err(got, want)
+    print(f"  err={err:.3e} (max|d|/RMS {plain:.3e}) vs chunkwise forward {err_chunk:.3e}")
+    record("decode", w.name, r31=err, plain=plain, vs_chunkwise_r31=err_chunk, dtype=w.dtype, phi=w.phi,
+           readout=w.readout)
     assert np.all(np.isfinite(got))
     assert err <= tol, (w.name, err)
+    assert plain <= tol, (w.name, plain)         # the forward's own metric holds as well
     assert err_chunk <= tol, (w.name, err_chunk)
 
 

@@ -10,13 +10,12 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import announce, oracle_full, rel_err, run_hip
+from gpu_util import announce, oracle_full, record, rel_err, run_hip
 
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 FP32_TOL = 1e-4
-FULL_NAMES_BF16_OUT = ["image", "image_mala", "video3d"]
 
 
 def _tol(w):
@@ -207,7 +206,7 @@ def test_relu_zero_denominator_gives_nan_where_the_oracle_does():
     assert np.all(gu[0, 0, [3, 100, 255]] == 0.0) and np.all(gu[0, 1, 17] == 0.0)
 
 
-BF16_OUT = [w for w in SMALL if w.dtype == "bf16"] + [synth.WORKLOADS[n] for n in FULL_NAMES_BF16_OUT]
+BF16_OUT = [w for w in SMALL if w.dtype == "bf16"]   # the full workloads: test_parity_full_size
 
 
 @pytest.mark.parametrize("w", BF16_OUT, ids=lambda w: w.name)
@@ -240,17 +239,40 @@ def test_deterministic():
 # ------------------------------------------------------------------------------------------
 
 FULL = ["deit_t", "image", "image_mala", "video3d"]
+# bf16 outputs that meet the plain bar by themselves (their own rounding floor included: 0.011 to
+# 0.015 of RMS).  image's floor alone is 0.0193: its bf16 output is held to the bar plus the
+# output's half-ulp, and its fp32 output to the plain bar.
+BF16_OUT_PLAIN = {"long1d", "video3d", "image_mala", "deit_t"}
 
 
+def _check_bf16_output(name, got, want):
+    rms = np.sqrt(np.mean(want ** 2))
+    plain = rel_err(got, want)
+    floor = rel_err(synth.round_to_bf16(want.astype(np.float32)), want)
+    excess = np.abs(got - want) - (BF16_TOL * rms + 2.0 ** -8 * np.abs(want))
+    print(f"  bf16 output: max|d|/RMS {plain:.3e} (rounding floor {floor:.3e}), excess over bar+half-ulp "
+          f"{excess.max():.3e}")
+    record("forward_bf16_out", name, plain=plain, rounding_floor=floor)
+    if name in BF16_OUT_PLAIN:
+        assert plain <= BF16_TOL, (name, plain)
+    else:
+        assert excess.max() <= 0, excess.max()
+
+
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("name", FULL)
-def test_parity_full_size(name):
+def test_parity_full_size(name, out_dtype):
     w = synth.WORKLOADS[name]
-    announce(f"full {name} shape={w.qkv_shape}")
+    announce(f"full {name} shape={w.qkv_shape} out={out_dtype}")
     q, k, v, mc, _ = synth.make_inputs(w)
-    got = run_hip(w, q, k, v, mc)
+    got = run_hip(w, q, k, v, mc, out_dtype=out_dtype)
     want = oracle_full(w, q, k, v, mc)
+    if out_dtype == "bf16":
+        _check_bf16_output(name, got, want)
+        return
     err = rel_err(got, want)
     print(f"  err={err:.3e}")
+    record("forward", name, plain=err)
     assert err <= BF16_TOL, (name, err)
     # the plain token-level definition at sampled queries of a few heads
     rng = np.random.default_rng(99)
@@ -264,21 +286,24 @@ def test_parity_full_size(name):
 
 @pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
 def test_parity_long1d_full_size(out_dtype):
-    """The benchmark's headline configuration; with bf16 output the plain bar still holds (the
-    output's own rounding floor on this workload is 0.0083)."""
+    """The benchmark's headline configuration, every head in full; with bf16 output the plain bar
+    still holds (the output's own rounding floor on this workload is 0.0152)."""
     w = synth.WORKLOADS["long1d"]
     announce(f"full long1d shape={w.qkv_shape} out={out_dtype}")
     q, k, v, mc, _ = synth.make_inputs(w)
     got = run_hip(w, q, k, v, mc, out_dtype=out_dtype)
-    heads = [(0, 0), (0, 7), (0, 15)]
-    want = oracle.forward(q, k, v, mc, w.grid, w.block, heads=heads)
-    err = rel_err(np.stack([got[b, h] for b, h in heads]), want)
-    print(f"  err(3 heads)={err:.3e}")
-    assert err <= BF16_TOL
+    want = oracle.forward(q, k, v, mc, w.grid, w.block)
+    assert np.all(np.isfinite(got))
+    if out_dtype == "bf16":
+        _check_bf16_output("long1d", got, want)
+    else:
+        err = rel_err(got, want)
+        print(f"  err(all 16 heads)={err:.3e}")
+        record("forward", "long1d", plain=err)
+        assert err <= BF16_TOL
     rms = np.sqrt(np.mean(want ** 2))
     rng = np.random.default_rng(5)
     samples = [(0, h, sorted(rng.choice(w.n_tokens, 16, replace=False).tolist())) for h in range(w.heads)]
     plain = oracle.forward_sampled(q, k, v, mc, w.grid, w.block, samples)
     for (b, h, toks), ref in zip(samples, plain):
         assert np.max(np.abs(got[b, h, toks] - ref)) / rms <= BF16_TOL, h
-    assert np.all(np.isfinite(got))

@@ -1,0 +1,91 @@
+"""Operand precisions of the forward kernels, decided by emulating their bf16 roundings on the CPU
+(tests/precision_emulation.py) against fp64.  Inputs are seeded N(0, 1) rounded to bf16, as the
+workloads draw them."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from precision_emulation import bf, mala, mhla_1d, rel, split
+
+BAR = 2e-2
+
+
+@pytest.fixture(scope="module")
+def mhla_case():
+    # a long-sequence head: 16384 tokens, 256 blocks of 64, d = 64, a dense row-softmax M_c
+    rng = np.random.default_rng(1234)
+    n, d, n_b = 16384, 64, 64
+    q, k, v = (synth.round_to_bf16(rng.standard_normal((n, d), dtype=np.float32)).astype(np.float64)
+               for _ in range(3))
+    mc = synth.mc_softmax_gaussian(n // n_b, rng).astype(np.float32).astype(np.float64)
+    ref = mhla_1d(q, k, v, mc, n_b)
+    return q, k, v, mc, n_b, ref
+
+
+def test_mc_rounding_dominates_the_bf16_path(mhla_case):
+    """Rounding M_c to one bf16 costs more than any other single rounding of the bf16 path (the
+    mixing averages summaries of both signs, so a 2^-9 relative error of every weight does not
+    average away): the mixing kernel takes M_c as bf16 hi + lo."""
+    q, k, v, mc, n_b, ref = mhla_case
+    single = {name: rel(mhla_1d(q, k, v, mc, n_b, **{name: True}), ref)
+              for name in ("phi_k", "stack", "mc_r", "mixed", "phi_q")}
+    print(single)
+    others = max(e for name, e in single.items() if name != "mc_r")
+    assert single["mc_r"] > 2.0 * others, single
+    every = rel(mhla_1d(q, k, v, mc, n_b, phi_k=True, stack=True, mc_r=True, mixed=True, phi_q=True), ref)
+    split_mc = rel(mhla_1d(q, k, v, mc, n_b, phi_k=True, stack=True, mixed=True, phi_q=True), ref)
+    print(f"all roundings {every:.3e}, with M_c split {split_mc:.3e}")
+    assert split_mc < 0.6 * every
+    assert every < BAR and split_mc < BAR
+
+
+def test_bf16_output_rounding_floor(mhla_case):
+    """The bf16 output's own rounding, relative to RMS(o), on this head: what is left of the
+    2e-2 bar for the kernel is 2e-2 minus this floor (about 2^-9 * max|o| / RMS(o))."""
+    q, k, v, mc, n_b, ref = mhla_case
+    floor = rel(synth.round_to_bf16(ref.astype(np.float32)).astype(np.float64), ref)
+    peak = float(np.max(np.abs(ref)) / np.sqrt(np.mean(ref ** 2)))
+    assert floor <= 2.0 ** -8 * peak
+    assert floor >= 2.0 ** -10 * peak
+    split_mc = mhla_1d(q, k, v, mc, n_b, phi_k=True, stack=True, mixed=True, phi_q=True)
+    both = rel(synth.round_to_bf16(split_mc.astype(np.float32)).astype(np.float64), ref)
+    print(f"floor {floor:.3e}, kernel roundings + bf16 output {both:.3e}")
+    assert both < BAR
+
+
+@pytest.fixture(scope="module")
+def mala_case():
+    rng = np.random.default_rng(4321)
+    n, d = 4096, 64
+    q, k, v = (synth.round_to_bf16(rng.standard_normal((n, d), dtype=np.float32)).astype(np.float64)
+               for _ in range(3))
+    return q, k, v, mala(q, k, v)
+
+
+def test_mala_needs_the_centred_form_and_split_operands(mala_case):
+    """The MALA readout: evaluated as the page's linear form with a bf16 S, the subtraction of
+    gamma u cancels about ten-fold and the error fails the bar; the centred form C = S - z u^T/N
+    with single bf16 operands still sits near the bar; split phi(K), phi(Q) and C (the kernels'
+    MALA path) bring it far below."""
+    q, k, v, ref = mala_case
+    naive = rel(mala(q, k, v, naive=True, rounding=bf), ref)
+    centred = rel(mala(q, k, v, rounding=bf), ref)
+    both = rel(mala(q, k, v, rounding=split), ref)
+    print(f"naive {naive:.3e}, centred single bf16 {centred:.3e}, centred split {both:.3e}")
+    assert naive > BAR
+    assert centred > 0.5 * BAR
+    assert both < BAR / 50
+
+
+def test_mala_centred_identity_is_exact(mala_case):
+    """Y = u/N + beta q~^T C equals beta q~^T S - gamma u without rounding (the identity the
+    kernels rely on)."""
+    q, k, v, ref = mala_case
+    pk = np.where(k > 0, k + 1.0, np.exp(np.minimum(k, 0.0)))
+    pq = np.where(q > 0, q + 1.0, np.exp(np.minimum(q, 0.0)))
+    s, z, u = pk.T @ v, pk.sum(0), v.sum(0)
+    sq = pq @ z
+    direct = (1.0 + 1.0 / sq)[:, None] * (pq @ s) - (sq / len(q))[:, None] * u[None, :]
+    assert math.isclose(rel(direct, ref), 0.0, abs_tol=1e-12)
