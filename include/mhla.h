@@ -59,7 +59,9 @@ typedef enum {
   MHLA_ERR_SHAPE = 3,         /* grid/block extents inconsistent or not divisible              */
   MHLA_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than mhla_workspace_size            */
   MHLA_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed                    */
-  MHLA_ERR_INTERNAL = 6
+  MHLA_ERR_INTERNAL = 6,
+  MHLA_ERR_SCRATCH_LIMIT = 7  /* mhla_forward_noalloc: the plan's workspace exceeds             */
+                              /* MHLA_NOALLOC_SCRATCH_BYTES                                      */
 } mhla_status;
 
 typedef enum { MHLA_DTYPE_BF16 = 0, MHLA_DTYPE_FP32 = 1 } mhla_dtype;
@@ -162,6 +164,21 @@ mhla_status mhla_workspace_size(mhla_handle h, size_t* bytes);
 mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void* v,
                          const float* mc, void* o, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid it): mhla_forward with its workspace in a
+ * fixed device array of MHLA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on (from the first call on that device until the process ends) instead of a caller buffer.
+ * The array holds the workspace of every plan whose mhla_workspace_size is at most that size --
+ * the 65536-token, 16-head, d = 128 sequence in 256 blocks needs 132 MiB; larger plans get
+ * MHLA_ERR_SCRATCH_LIMIT and nothing is launched.  Arguments, validation and results are those
+ * of mhla_forward.  The call allocates nothing; its first call on a device (the current device)
+ * looks up that device's copy of the array.  Every call on a device shares that device's array:
+ * calls that overlap on one device (on different streams, or from several threads) race and
+ * give undefined results; calls in one stream's order are safe. */
+#define MHLA_NOALLOC_SCRATCH_BYTES (160u << 20)
+mhla_status mhla_forward_noalloc(mhla_handle h, const void* q, const void* k, const void* v,
+                                 const float* mc, void* o, void* stream);
 
 /* Backward pass: gradients of L = sum(dout * O) with respect to Q, K, V and M_c, for the
  * normalised and unnormalised readouts (chain rule of the forward steps; M_c is trained end to

@@ -21,7 +21,8 @@ __all__ = [
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
-    "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "make_desc", "Plan", "EXPORTED_SYMBOLS",
+    "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
+    "MHLA_NOALLOC_SCRATCH_BYTES", "MHLA_ERR_SCRATCH_LIMIT", "make_desc", "Plan", "EXPORTED_SYMBOLS",
 ]
 
 MHLA_OK = 0
@@ -31,6 +32,8 @@ MHLA_READOUT_NORMALIZED, MHLA_READOUT_UNNORMALIZED, MHLA_READOUT_MALA = 0, 1, 2
 MHLA_READOUT_CAUSAL_NORMALIZED, MHLA_READOUT_CAUSAL_UNNORMALIZED = 3, 4
 MHLA_FLAG_RAGGED_BLOCKS, MHLA_FLAG_CLS_TOKEN = 1, 2
 MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT = 0, 1, 2
+MHLA_ERR_SCRATCH_LIMIT = 7
+MHLA_NOALLOC_SCRATCH_BYTES = 160 << 20     # the no-alloc forward's scratch array (include/mhla.h)
 
 _READOUTS = {"normalized": MHLA_READOUT_NORMALIZED, "unnormalized": MHLA_READOUT_UNNORMALIZED,
              "mala": MHLA_READOUT_MALA, "causal": MHLA_READOUT_CAUSAL_NORMALIZED,
@@ -43,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
-    "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step",
+    "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
 )
 
 
@@ -116,6 +119,7 @@ def load_library() -> ctypes.CDLL:
     lib.mhla_create.argtypes = [ctypes.POINTER(MhlaDesc), ctypes.POINTER(P)]
     lib.mhla_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
+    lib.mhla_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
     lib.mhla_backward_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.mhla_destroy.argtypes = [P]
@@ -167,6 +171,12 @@ def mhla_forward(h, q: int, k: int, v: int, mc: int, o: int, workspace: int, wor
     """Pointers are integer device addresses (0 for NULL); ``stream`` a raw hipStream_t."""
     _check(load_library().mhla_forward(h, q, k, v, mc or None, o, workspace or None,
                                        workspace_bytes, stream or None), "mhla_forward")
+
+
+def mhla_forward_noalloc(h, q: int, k: int, v: int, mc: int, o: int, stream: int) -> None:
+    """mhla_forward with the library's own scratch array as workspace (no allocation); pointers are
+    integer device addresses (0 for NULL), ``stream`` a raw hipStream_t."""
+    _check(load_library().mhla_forward_noalloc(h, q, k, v, mc or None, o, stream or None), "mhla_forward_noalloc")
 
 
 def mhla_backward_workspace_size(h) -> int:

@@ -22,7 +22,7 @@ PEAK_SOURCE = "peak_probe.hip"
 PEAK_LIB = os.path.join(PKG, "libmhla_peak.so")
 
 SOURCES = ["summary.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "decode.hip",
-           "mhla_host.cpp"]
+           "mhla_host.cpp", "noalloc.hip"]
 
 
 def hipcc() -> str:

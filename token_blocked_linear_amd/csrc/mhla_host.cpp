@@ -891,6 +891,7 @@ const char* mhla_status_string(mhla_status s) {
     case MHLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MHLA_ERR_HIP: return "HIP runtime or launch failure";
     case MHLA_ERR_INTERNAL: return "internal error";
+    case MHLA_ERR_SCRATCH_LIMIT: return "workspace larger than the no-alloc entry point's scratch array";
     default: return "unknown status";
   }
 }
