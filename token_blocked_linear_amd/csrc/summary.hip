@@ -25,14 +25,27 @@ namespace mhla {
 // output's type) as V.  TOKW (backward): phi(K_j) is scaled by kscale[j] and the normaliser
 // product weights token j by zw[j] instead of 1, so that S = sum_j kscale_j phi(K_j) V_j^T and
 // z = sum_j kscale_j zw_j phi(K_j).
+// Token groups of 8 per round: as many as the workgroup's threads cover, at most 32 (256 tokens).
+// With phi(K) split (hi and lo planes of phi(K)^T in LDS) and bf16 inputs at d <= 64 the rounds
+// are shorter (192 tokens: 72 KB of LDS at d = 64, two workgroups per CU instead of one with
+// 256-token rounds; MALA image summary 56.6 -> 44.5 us).
+#ifndef MHLA_SUMMARY_SPLIT_TG
+#define MHLA_SUMMARY_SPLIT_TG 24
+#endif
+template <typename TIn, int D, bool SPLIT_K>
+constexpr int summary_tg() {
+  constexpr int all = kThreads / (D / 8);
+  constexpr int cap = (SPLIT_K && sizeof(TIn) == 2 && D <= 64) ? MHLA_SUMMARY_SPLIT_TG : 32;
+  return all < cap ? all : cap;
+}
+
 template <typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U, bool OUT_BF16, int PHI, typename TV,
           bool TOKW>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int n_units) {
   using Dm = Dims<D>;
   constexpr int DK = Dm::DK, NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
   constexpr int LPR = D / 8;               // threads per token row
-  constexpr int TG_ALL = kThreads / LPR;   // token groups the workgroup could cover
-  constexpr int TG = TG_ALL < 32 ? TG_ALL : 32;   // token groups of 8 per round (<= 256 tokens)
+  constexpr int TG = summary_tg<TIn, D, SPLIT_K>();   // token groups of 8 per round (<= 256 tokens)
   constexpr int ROUND = TG * 8;            // tokens per round
   constexpr int PITCH = ROUND;             // LDS row pitch (bf16 elements): rows start on 128 B
   static_assert(ROUND >= 64, "the chunk swizzle needs at least 8 chunks per row");
@@ -455,7 +468,7 @@ template <int PHI, typename TIn, int D, bool SPLIT_K, bool SPLIT_V, bool WANT_U,
           typename TV = TIn, bool TOKW = false>
 static hipError_t launch_summary_t(const SummaryParams& p, int n_units, hipStream_t stream) {
   using Dm = Dims<D>;
-  constexpr int LPR = D / 8, TG_ALL = kThreads / LPR, TG = TG_ALL < 32 ? TG_ALL : 32;
+  constexpr int TG = summary_tg<TIn, D, SPLIT_K>();
   constexpr int ROUND = TG * 8, PITCH = ROUND;
   const size_t lds = (size_t)(Dm::DK * (SPLIT_K ? 2 : 1) + D * (SPLIT_V ? 2 : 1)) * PITCH * 2 +
                     (TOKW ? (size_t)ROUND * 4 : 0);
@@ -508,9 +521,22 @@ static hipError_t dispatch_d(const SummaryParams& p, int d, bool sk, bool sv, bo
   }
 }
 
+hipError_t launch_summary_dma(const SummaryParams& p, int d, bool split_k, bool want_u, bool out_bf16, int phi,
+                              int n_units, hipStream_t stream);
+
+// bf16 inputs stream through LDS (summary_dma.hip) at d = 32 and 64, and at d = 128 when phi(K) is
+// split (here its hi and lo planes would leave one workgroup per CU); fp32 inputs, d = 16 and the
+// single-operand d = 128 summary run here (on the long-sequence workload this kernel's register
+// buffer sustains 123 us against 132 us for the LDS ring, whose load stream alone takes 114 us).
+#ifndef MHLA_SUMMARY_DMA
+#define MHLA_SUMMARY_DMA 1
+#endif
+
 // n_units = splits * M * BH work units; the kernel picks its own persistent grid.
 hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool split_k, bool split_v,
                           bool want_u, bool out_bf16, int phi, int n_units, hipStream_t stream) {
+  if (MHLA_SUMMARY_DMA && !in_fp32 && d >= 32 && !split_v && (d <= 64 || split_k))
+    return launch_summary_dma(p, d, split_k, want_u, out_bf16, phi, n_units, stream);
   auto go = [&](auto phi_c) {
     constexpr int PHI = decltype(phi_c)::value;
     return in_fp32 ? dispatch_d<PHI, float>(p, d, split_k, split_v, want_u, out_bf16, n_units, stream)
