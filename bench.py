@@ -634,6 +634,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-causal", action="store_true", help="skip the causal-readout measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming-decode measurement")
+    ap.add_argument("--no-measured-rates", action="store_true",
+                    help="skip the copy / GEMM / MFMA-loop rate probes (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--digest", action="store_true")
     args = ap.parse_args()
@@ -666,10 +668,13 @@ def main():
     head_rec = workload_record(res, args.out_dtype)
 
     progress("measured rates")
-    stream_rates = measured_stream_GBps()
-    copy_bw = measured_copy_GBps()
-    gemm_tf = measured_gemm_TFLOPs()
-    mfma_tf = measured_mfma_TFLOPs()
+    if args.no_measured_rates:
+        stream_rates, copy_bw, gemm_tf, mfma_tf = None, float("nan"), float("nan"), None
+    else:
+        stream_rates = measured_stream_GBps()
+        copy_bw = measured_copy_GBps()
+        gemm_tf = measured_gemm_TFLOPs()
+        mfma_tf = measured_mfma_TFLOPs()
     measured = {"read_GBps": None if stream_rates is None else stream_rates["read"],
                 "write_GBps": None if stream_rates is None else stream_rates["write"],
                 "copy_kernel_GBps": None if stream_rates is None else stream_rates["copy"],
