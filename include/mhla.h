@@ -181,18 +181,21 @@ mhla_status mhla_forward_noalloc(mhla_handle h, const void* q, const void* k, co
                                  const float* mc, void* o, void* stream);
 
 /* Backward pass: gradients of L = sum(dout * O) with respect to Q, K, V and M_c, for the
- * normalised and unnormalised readouts (chain rule of the forward steps; M_c is trained end to
- * end per "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head", Method ->
- * Key design 3).
+ * normalised, unnormalised and MALA readouts (chain rule of the forward steps; M_c is trained end
+ * to end per "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head",
+ * Method -> Key design 3; MALA's beta and gamma per "Rectifying Magnitude Neglect in Linear
+ * Attention", Method -> Key design, differentiated through the centred form
+ * Y = u/N + beta q~^T (S - z u^T / N)).
  *   q, k, v      device, as for mhla_forward (plan's in_dtype)
  *   mc           device fp32 M_c as for mhla_forward (NULL iff M == 1)
  *   dout         device [B, H, N, d], the plan's out_dtype: dL/dO
  *   dq, dk, dv   device [B, H, N, d], the plan's out_dtype: written (not accumulated)
  *   dmc          device fp32 with M_c's shape, written; for a shared [M, M] M_c the sum over
- *                batch and heads, for a per-head [H, M, M] one the sum over batch; NULL skips it
+ *                batch and heads, for a per-head [H, M, M] one the sum over batch; NULL skips it.
+ *                MALA has no M_c: dmc must be NULL (else MHLA_ERR_INVALID_ARG)
  * The forward's summaries are recomputed (nothing from mhla_forward is reused); every product
- * uses hi/lo bf16 operand splits.  Not supported (MHLA_ERR_UNSUPPORTED): the MALA readout, head
- * size 16.  Outputs must not alias the inputs, each other or the workspace.  The workspace
+ * uses hi/lo bf16 operand splits.  Not supported (MHLA_ERR_UNSUPPORTED): the causal readouts,
+ * head size 16.  Outputs must not alias the inputs, each other or the workspace.  The workspace
  * (256-byte aligned) size comes from mhla_backward_workspace_size and differs from the
  * forward's.  Every sum runs in a fixed order: repeated calls give identical bits.
  * Asynchronous on `stream`, like mhla_forward. */

@@ -254,12 +254,26 @@ def test_backward_support_and_workspace():
     p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)
     assert T.mhla_backward_workspace_size(p.handle) > 0
     p.close()
-    for kw in (dict(block=(64, 64), readout="mala"), dict(head_dim=16)):
+    m = T.Plan(grid=(64, 64), block=(64, 64), batch=2, heads=2, head_dim=64, readout="mala")
+    assert T.mhla_backward_workspace_size(m.handle) > 0      # MALA: supported
+    m.close()
+    for kw in (dict(grid=(1000,), block=(100,), readout="causal"), dict(head_dim=16)):
         u = T.Plan(**dict(dict(grid=(64, 64), block=(16, 16), batch=2, heads=2, head_dim=64), **kw))
         with pytest.raises(T.MhlaError) as e:
             T.mhla_backward_workspace_size(u.handle)
         assert e.value.status == 2                           # MHLA_ERR_UNSUPPORTED
         u.close()
+
+
+def test_mala_backward_rejects_dmc():
+    """MALA has no M_c: a dM_c pointer is an argument error, found before any launch."""
+    lib = _lib_or_skip()
+    p = T.Plan(grid=(64, 64), block=(64, 64), batch=2, heads=2, head_dim=64, readout="mala")
+    ws = T.mhla_backward_workspace_size(p.handle)
+    Q, K, V, DO, DQ, DK, DV, DMC = (0x10000 * i for i in range(1, 9))
+    W = 0x1000000
+    assert lib.mhla_backward(p.handle, Q, K, V, None, DO, DQ, DK, DV, DMC, W, ws, None) == 1
+    p.close()
 
 
 def test_backward_argument_errors_before_launch():

@@ -1,4 +1,4 @@
-"""GPU parity of the backward pass (dQ, dK, dV, dM_c) against the fp64 oracle.
+"""GPU parity of the backward pass (dQ, dK, dV, dM_c; MALA: dQ, dK, dV) against the fp64 oracle.
 
 The gradients are of L = sum(dO * O) for a seeded standard-normal dO.  Bar, for every gradient
 tensor separately, as max|g_gpu - g_oracle| / RMS(g_oracle):
@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import announce, oracle_backward, rel_err, run_hip_backward
+from gpu_util import announce, oracle_backward, record, rel_err, run_hip_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,7 @@ def _check(w, got, want, tol, heads=None):
         assert np.all(np.isfinite(g)), name
         errs[name] = rel_err(g, r)
     print("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    record("backward", w.name, dtype=w.dtype, readout=w.readout, phi=w.phi, tol=tol, **errs)
     for n, e in errs.items():
         assert e <= tol, (w.name, n, e)
 
@@ -156,6 +157,59 @@ def test_backward_two_plans_in_a_row_smaller_second():
 # full sizes of the image and video workloads (every head), and the long sequence (sampled
 # heads for dQ, dK, dV; dM_c through a property that holds at any size)
 # ------------------------------------------------------------------------------------------
+
+# ------------------------------------------------------------------------------------------
+# MALA (one block): the centred chain rule against the oracle's linear-form chain rule
+# (oracle.mala_backward); no M_c, so no dM_c
+# ------------------------------------------------------------------------------------------
+
+MALA_CASES = [
+    synth.Workload("bw_mala_2d", "bf16", 2, 2, 64, (32, 32), (32, 32), 171, "none", "mala"),
+    synth.Workload("bw_mala_ragged1d", "bf16", 2, 3, 64, (1000,), (1000,), 172, "none", "mala"),
+    synth.Workload("bw_mala_d32", "bf16", 1, 2, 32, (30, 42), (30, 42), 173, "none", "mala"),
+    synth.Workload("bw_mala_d128", "bf16", 1, 2, 128, (6, 10, 12), (6, 10, 12), 174, "none", "mala"),
+    synth.Workload("bw_mala_long", "bf16", 1, 2, 64, (20000,), (20000,), 175, "none", "mala"),
+    synth.Workload("bw_mala_tiny", "bf16", 1, 1, 64, (5,), (5,), 176, "none", "mala"),
+    synth.Workload("bw_mala_fp32", "fp32", 2, 2, 64, (24, 24), (24, 24), 177, "none", "mala"),
+    synth.Workload("bw_mala_fp32_d128", "fp32", 1, 2, 128, (900,), (900,), 178, "none", "mala"),
+    synth.Workload("bw_mala_relu", "bf16", 1, 2, 64, (32, 32), (32, 32), 179, "none", "mala", phi="relu"),
+    synth.Workload("bw_mala_exp", "bf16", 1, 2, 64, (32, 32), (32, 32), 180, "none", "mala", phi="exp"),
+    synth.Workload("bw_mala_exp_fp32_d32", "fp32", 1, 2, 32, (20, 20), (20, 20), 181, "none", "mala",
+                   phi="exp"),
+]
+
+
+@pytest.mark.parametrize("w", MALA_CASES, ids=lambda w: w.name)
+def test_backward_mala(w):
+    announce(f"backward {w.name} phi={w.phi} shape={w.qkv_shape} mala")
+    q, k, v, mc, do = _inputs(w, positive_q=w.phi == "relu")
+    assert mc is None
+    got = run_hip_backward(w, q, k, v, mc, do)
+    assert got[3] is None
+    _check(w, got, oracle_backward(w, q, k, v, mc, do), _tol(w))
+
+
+def test_backward_mala_full_image_and_bf16_gradients():
+    """The full MALA image workload (every head), with fp32 and with bf16 gradients (the plain
+    bar plus each bf16 output's own rounding, as for the MHLA case); repeated calls are
+    bit-identical."""
+    w = synth.WORKLOADS["image_mala"]
+    announce(f"backward full image_mala shape={w.qkv_shape}")
+    q, k, v, mc, do = _inputs(w)
+    runs = run_hip_backward(w, q, k, v, mc, do, repeat=2)
+    for x, y in zip(runs[0][:3], runs[1][:3]):
+        assert np.array_equal(x, y)
+    want = oracle_backward(w, q, k, v, mc, do)
+    _check(w, runs[0], want, BF16_TOL)
+    do16 = synth.round_to_bf16(do)
+    got = run_hip_backward(w, q, k, v, mc, do16, out_dtype="bf16")
+    want = oracle_backward(w, q, k, v, mc, do16)
+    for name, g, r in zip(NAMES[:3], got[:3], want[:3]):
+        rms = np.sqrt(np.mean(r ** 2))
+        excess = np.abs(g - r) - (BF16_TOL * rms + 2.0 ** -8 * np.abs(r))
+        print(f"  bf16 {name} max|d|/rms={rel_err(g, r):.2e}")
+        assert excess.max() <= 0, (name, excess.max())
+
 
 @pytest.mark.parametrize("name", ["image", "video3d"])
 def test_backward_full(name):

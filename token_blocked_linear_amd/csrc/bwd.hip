@@ -12,6 +12,16 @@
 //   dM_c[i, b] = <dS~_i, S_b> + <dz~_i, z_b>                dmc_kernel, dmc_reduce_kernel
 //   dk~_j = dS_b v_j + dz_b, dv_j = dS_b^T k~_j            keyside_kernel
 //   dq = dq~ * phi'(q), dk = dk~ * phi'(k).
+// MALA ("Rectifying Magnitude Neglect in Linear Attention", Method -> Key design: one block,
+// Y_t = u/N + beta_t q~_t^T C with C = S - z u^T / N, s_t = q~_t . z, beta_t = 1 + 1/s_t) takes
+// the same kernels with the centred summary in place of S~:
+//   p_t = (C^T q~_t) . dO_t, g_t = beta_t dO_t, gden_t = -p_t / s_t^2
+//   dq~_t = C g_t + z gden_t                                dq_kernel<MALA>
+//   dS = sum_t q~_t g_t^T, dz' = sum_t q~_t gden_t          the summary kernel (kscale = beta_t)
+//   dz = dz' - dS u / N, du = -(1/N) sum_t s_t dO_t          mala_stage_kernel (stage 1)
+//   dk~_j = dS v_j + dz, dv_j = dS^T k~_j + du              keyside_kernel
+// (the centred forms: C g and dz' - dS u / N are the differences that an uncentred S would leave
+// to cancel in fp32).
 // Every product runs on bf16 MFMA with hi/lo operand splits (about fp32 accuracy).  Head sizes
 // 32, 64 and 128.
 //
@@ -27,7 +37,7 @@
 
 namespace mhla {
 
-enum { kBwdNormalized = 0, kBwdUnnormalized = 1 };
+enum { kBwdNormalized = 0, kBwdUnnormalized = 1, kBwdMala = 2 };
 
 template <int PHI>
 __device__ inline float dphi_map(float x) {
@@ -196,7 +206,9 @@ __device__ inline void buf_store8(Rsrc r, uint32_t off, const float (&x)[8]) {
 template <int D>
 constexpr int bwd_threads() { return D >= 128 ? 512 : kThreads; }
 
-template <typename TIn, typename TOut, int D, int PHI>
+// MALA: the staged summary is C and the normaliser z (see the top of the file); the kernel also
+// leaves the unit's sum_t s_t dO_t in du_part.
+template <typename TIn, typename TOut, int D, int PHI, bool MALA>
 __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int mode) {
   constexpr int NT = bwd_threads<D>();
   static_assert(D >= 32, "the backward serves head sizes 32, 64 and 128");
@@ -252,6 +264,13 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
   const Rsrc rts = make_rsrc(p.tok_scale + (int64_t)U.bh * geo.N, (uint32_t)geo.N * 4u);
   const Rsrc rtz = make_rsrc(p.tok_zw + (int64_t)U.bh * geo.N, (uint32_t)geo.N * 4u);
 
+  // MALA: this lane's share of sum_t s_t dO_t (its channels 32c + 8lg + r)
+  float du_acc[MALA ? NG : 1][8];
+#pragma unroll
+  for (int c = 0; c < (MALA ? NG : 1); ++c)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) du_acc[c][r] = 0.f;
+
   // one tile: `next` is loaded once this tile's MFMAs are issued
   auto process = [&](const TileBuf& cur, TileBuf& next, int next_tile) {
     // phi(q): fp32 values and hi / lo operands
@@ -281,8 +300,25 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
     // g and gden over the lane's channels 32c + 8lg + r; the dot dO . o is completed across the
     // four lanes of the token
     float g[NG][8];
-    float gden = 0.f, inv = 1.0f, part = 0.f;
-    if (mode == kBwdNormalized) {
+    float gden = 0.f, inv = 1.0f, part = 0.f, zw = 0.f;
+    if constexpr (MALA) {
+      // den = s_t, acc = C^T q~_t; part = p_t; kscale = beta_t, zw = gden_t / beta_t
+      const float is = 1.0f / den;
+      inv = 1.0f + is;
+#pragma unroll
+      for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float d_o = cur.d[c].get(r);
+          part = fmaf(d_o, acc_out<NCT>(acc, c, r), part);
+          g[c][r] = d_o * inv;
+          if (cur.valid) du_acc[c][r] = fmaf(den, d_o, du_acc[c][r]);
+        }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      gden = -part * is * is;
+      zw = gden / inv;
+    } else if (mode == kBwdNormalized) {
       inv = 1.0f / den;
 #pragma unroll
       for (int c = 0; c < NG; ++c)
@@ -295,6 +331,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
       part += __shfl_xor(part, 16);
       part += __shfl_xor(part, 32);
       gden = -part * inv;
+      zw = -part;
     } else {
 #pragma unroll
       for (int c = 0; c < NG; ++c)
@@ -332,11 +369,11 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
         out[r] = (acc_out<NCT>(acc2, c, r) + s_zt[f0 + r] * gden) * dphi_map<PHI>(cur.q[c].get(r));
       buf_store8<TOut>(rdq, cur.valid ? (cur.rel + f0) * EO : kOutOfRange, out);
     }
-    // the token's weights for dS~ and dz~ (kscale = 1/den, zw = gden * den = -(dO . o)), one
-    // lane per token
+    // the token's weights for dS~ and dz~ (kscale = 1/den, zw = gden * den = -(dO . o); MALA:
+    // beta and gden / beta), one lane per token
     const uint32_t toff = (cur.valid && lg == 0) ? (cur.rel / D) * 4u : kOutOfRange;
     buf_st4(rts, toff, __float_as_uint(inv));
-    buf_st4(rtz, toff, __float_as_uint(-part));
+    buf_st4(rtz, toff, __float_as_uint(zw));
   };
 
   constexpr int STEP = NT / 64;
@@ -346,6 +383,31 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
     process(bufA, bufB, tile + STEP);
     if (tile + STEP >= U.n_tiles) break;
     process(bufB, bufA, tile + 2 * STEP);
+  }
+
+  if constexpr (MALA) {
+    // the unit's sum_t s_t dO_t: over the 16 token lanes of each lane group, then over the waves
+    // (through LDS, once every wave is done with the staged summaries)
+    __syncthreads();
+    float* s_red = reinterpret_cast<float*>(smem);   // [NT / 64][D]
+#pragma unroll
+    for (int c = 0; c < NG; ++c)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float x = du_acc[c][r];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        if (pr == 0) s_red[wave * D + 32 * c + 8 * lg + r] = x;
+      }
+    __syncthreads();
+    if (tid < D) {
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < STEP; ++w) a += s_red[w * D + tid];
+      p.du_part[(U.row * p.splits + U.split) * D + tid] = a;
+    }
   }
 }
 
@@ -362,13 +424,17 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
   uint16_t* s2_hi = s1_lo + FRAG;         // F(dS_b^T)
   uint16_t* s2_lo = s2_hi + FRAG;
   float* s_dz = reinterpret_cast<float*>(s2_lo + FRAG);   // dz_b [D]
+  float* s_du = s_dz + D;                                  // du (MALA) or zeros [D]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
   const Geom& geo = p.g;
   const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
 
   stage_frag<D, NT>(p.ds_hi + U.row * FRAG, p.ds_lo + U.row * FRAG, s1_hi, s1_lo, tid);
-  if (tid < D) s_dz[tid] = p.dz[U.row * D + tid];
+  if (tid < D) {
+    s_dz[tid] = p.dz[U.row * D + tid];
+    s_du[tid] = p.du ? p.du[(int64_t)U.bh * D + tid] : 0.f;
+  }
   __syncthreads();
   transpose_frag<D, NT>(s1_hi, s1_lo, s2_hi, s2_lo, tid);
   __syncthreads();
@@ -437,7 +503,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
       float dvo[8], dko[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        dvo[r] = acc_out<NCT>(acc1, c, r);
+        dvo[r] = acc_out<NCT>(acc1, c, r) + s_du[f0 + r];
         dko[r] = (acc_out<NCT>(acc2, c, r) + s_dz[f0 + r]) * dphi_map<PHI>(cur.k[c].get(r));
       }
       const uint32_t off = cur.valid ? (cur.rel + f0) * EO : kOutOfRange;
@@ -655,6 +721,85 @@ __global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part,
   }
 }
 
+// ---- MALA: sums of the token-slice partials ------------------------------------------------
+// One workgroup per (batch, head).  Fragment position pos holds T[k][c] for key feature
+// k = 32 kc + 8 (l / 16) + pos % 8 and channel c = 16 ct + l % 16, where l = (pos / 8) % 64 and
+// (kc, ct) = (pos / 512) / NCT, (pos / 512) % NCT: 8 consecutive positions are 8 features of
+// one channel.  Stage 1 keeps dS in LDS (fp32, fragment order) for dz -= dS u / N.
+template <int D>
+__global__ __launch_bounds__(kThreads) void mala_stage_kernel(MalaStageParams p) {
+  using Dm = Dims<D>;
+  constexpr int FRAG = Dm::FRAG, NCT = Dm::NCT;
+  extern __shared__ __align__(16) float fsm[];
+  float* s_x = fsm;             // dS [FRAG] (stage 1)
+  float* s_z = s_x + FRAG;      // [D]
+  float* s_u = s_z + D;         // u / N [D]
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int ss = p.ss;
+  const float inv_n = 1.0f / (float)p.N;
+  if (tid < D) {
+    float z = 0.f, u = 0.f;
+    for (int s = 0; s < ss; ++s) z += p.pz[(bh * ss + s) * D + tid];
+    if (p.stage == 0) {
+      for (int s = 0; s < ss; ++s) u += p.pu[(bh * ss + s) * D + tid];
+      u *= inv_n;
+    } else {
+      u = p.ub[bh * D + tid];
+      float du = 0.f;
+      for (int r = 0; r < p.rs; ++r) du += p.du_part[(bh * p.rs + r) * D + tid];
+      p.du[bh * D + tid] = -du * inv_n;
+    }
+    s_z[tid] = z;
+    s_u[tid] = u;
+  }
+  __syncthreads();
+  for (int pos = tid * 8; pos < FRAG; pos += kThreads * 8) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float* src = p.ps + bh * ss * FRAG + pos;
+    for (int s = 0; s < ss; ++s) {
+      const u32x4_t w0 = ld16(src + (int64_t)s * FRAG), w1 = ld16(src + (int64_t)s * FRAG + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] += __uint_as_float(w0[e]);
+        a[4 + e] += __uint_as_float(w1[e]);
+      }
+    }
+    if (p.stage == 0) {   // centring: C[k][c] = S[k][c] - z[k] u[c] / N
+      const int l = (pos >> 3) & 63, fr = pos >> 9;
+      const int k0 = 32 * (fr / NCT) + 8 * (l >> 4), c = 16 * (fr % NCT) + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = fmaf(-s_z[k0 + e], s_u[c], a[e]);
+    } else {
+      st16(s_x + pos, u32x4_t{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                              __float_as_uint(a[3])});
+      st16(s_x + pos + 4, u32x4_t{__float_as_uint(a[4]), __float_as_uint(a[5]), __float_as_uint(a[6]),
+                                  __float_as_uint(a[7])});
+    }
+    u32x4_t hi, lo;
+    split8(a, hi, lo);
+    st16(p.y_hi + bh * FRAG + pos, hi);
+    st16(p.y_lo + bh * FRAG + pos, lo);
+  }
+  if (p.stage == 0) {
+    if (tid < D) {
+      p.zo[bh * D + tid] = s_z[tid];
+      p.ub_out[bh * D + tid] = s_u[tid];
+    }
+    return;
+  }
+  __syncthreads();
+  if (tid < D) {   // (dS u / N)[k] over the channels c, in channel order
+    const int k = tid, kc = k >> 5, e = k & 7, lgk = (k & 31) >> 3;
+    float a = 0.f;
+    for (int c = 0; c < D; ++c) {
+      const int pos = ((kc * NCT + (c >> 4)) * 64 + 16 * lgk + (c & 15)) * 8 + e;
+      a = fmaf(s_x[pos], s_u[c], a);
+    }
+    p.zo[bh * D + k] = s_z[k] - a;
+  }
+}
+
 // ---- launches -----------------------------------------------------------------------------
 template <int D>
 static size_t dq_lds() {
@@ -663,7 +808,7 @@ static size_t dq_lds() {
 }
 template <int D>
 static size_t keyside_lds() {
-  return (size_t)4 * Dims<D>::FRAG * 2 + (size_t)D * 4;
+  return (size_t)4 * Dims<D>::FRAG * 2 + (size_t)2 * D * 4;
 }
 
 template <int PHI, typename TIn, typename TOut, int D>
@@ -675,7 +820,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, int mode, int n_units, bool k
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(n_units), dim3(bwd_threads<D>()), lds, s, p);
   } else {
-    auto kern = dq_kernel<TIn, TOut, D, PHI>;
+    auto kern = mode == kBwdMala ? dq_kernel<TIn, TOut, D, PHI, true> : dq_kernel<TIn, TOut, D, PHI, false>;
     const size_t lds = dq_lds<D>();
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -709,6 +854,25 @@ hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp
     case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
     case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
     case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// One workgroup per (batch, head); head sizes 32, 64, 128.
+hipError_t launch_mala_stage(const MalaStageParams& p, int d, int bh, hipStream_t stream) {
+  auto go = [&](auto dc) -> hipError_t {
+    constexpr int D = decltype(dc)::value;
+    const size_t lds = ((size_t)Dims<D>::FRAG + 2 * D) * 4;
+    hipError_t e = hipFuncSetAttribute((const void*)mala_stage_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mala_stage_kernel<D>, dim3(bh), dim3(kThreads), lds, stream, p);
+    return hipGetLastError();
+  };
+  switch (d) {
+    case 32: return go(std::integral_constant<int, 32>{});
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 128: return go(std::integral_constant<int, 128>{});
     default: return hipErrorInvalidValue;
   }
 }

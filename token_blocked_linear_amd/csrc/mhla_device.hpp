@@ -199,11 +199,33 @@ struct BwdParams {
   const float* dz;         // dz [BH][M][D]
   float* tok_scale;        // per token 1/den (1 unnormalised) [BH][N]
   float* tok_zw;           // per token -(dO . o) (0 unnormalised) [BH][N]
+  float* du_part;          // MALA: per unit sum_t s_t dO_t over its tokens [BH][splits][D]
+  const float* du;         // MALA: dL/du added to every dv [BH][D]; NULL otherwise
   Geom g;
   int32_t splits;          // token slices per block (readout slicing)
   int32_t tok_per_split;
   int32_t BH;
   int32_t xcd_map;
+};
+
+// MALA backward, one block per (batch, head): sums of the token-slice partials into fragments.
+//   stage 0 (forward):  C = S - z u^T / N (hi / lo), z, u / N
+//   stage 1 (backward): dS (hi / lo), dz = dz' - dS (u / N), du = -(1/N) sum over units of du_part
+struct MalaStageParams {
+  const float* ps;         // fp32 fragment partials [BH][ss][FRAG]: S (stage 0) or dS (stage 1)
+  const float* pz;         // [BH][ss][D]: z or dz'
+  const float* pu;         // stage 0: [BH][ss][D] partials of u
+  const float* ub;         // stage 1: u / N [BH][D]
+  const float* du_part;    // stage 1: [BH][rs][D]
+  uint16_t* y_hi;          // [BH][FRAG]
+  uint16_t* y_lo;
+  float* zo;               // [BH][D]
+  float* ub_out;           // stage 0: u / N [BH][D]
+  float* du;               // stage 1: [BH][D]
+  int32_t ss;              // token slices of the partials
+  int32_t rs;              // units per head of du_part
+  int32_t N;
+  int32_t stage;
 };
 
 // dM_c partials per (batch, head): dmc[bh][i][b] = <dS~_i, S_b> + <dz~_i, z_b>, summaries summed

@@ -25,6 +25,7 @@ hipError_t launch_readout(const ReadoutParams& p, int d, bool in_fp32, bool out_
 hipError_t launch_bwd_tiles(const BwdParams& p, int d, bool in_fp32, bool out_fp32, int mode, int phi,
                             bool key_side, int n_units, hipStream_t stream);
 hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream);
+hipError_t launch_mala_stage(const MalaStageParams& p, int d, int bh, hipStream_t stream);
 hipError_t launch_decode_step(const DecodeParams& p, int d, bool in_fp32, bool out_fp32, int phi, hipStream_t s);
 hipError_t launch_decode_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_causal(const CausalParams& p, int d, bool in_fp32, bool out_fp32, int phi, int n_units,
@@ -546,6 +547,7 @@ namespace {
 // summaries, g, and the per-(batch, head) dM_c partials.
 struct BwdLayout {
   size_t ps, pz, st_hi, st_lo, zt, dps, dpzs, ds_hi, ds_lo, dz, tok_scale, tok_zw, dmcp;
+  size_t pu, ub, du_part, du;                        // MALA: u partials, u / N, du partials, du
   size_t mcf_hi, mcf_lo, mcft_hi, mcft_lo, total;   // M_c and M_c^T operand fragments
   bool mfma_mix;                                     // M <= 256: mixing on MFMA
   mhla::MixShape mix;
@@ -572,6 +574,11 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   take(L.dz, rows * dd * 4);
   take(L.tok_scale, (size_t)h->BH * h->N * 4);
   take(L.tok_zw, (size_t)h->BH * h->N * 4);
+  const size_t mala_rows = h->mala ? rows : 0;
+  take(L.pu, mala_rows * h->sum_splits * dd * 4);
+  take(L.ub, mala_rows * dd * 4);
+  take(L.du_part, mala_rows * h->rd_splits * dd * 4);
+  take(L.du, mala_rows * dd * 4);
   {
     L.dmc_groups = h->desc.mc_per_head ? (int)h->H : 1;
     L.dmc_group_bh = h->desc.mc_per_head ? (int)h->B : (int)h->BH;
@@ -586,8 +593,8 @@ BwdLayout bwd_layout(const mhla_plan* h) {
     L.dmc_steps_per_chunk = (int)spc;
     L.dmc_nchunks = (int)((total + spc - 1) / spc);
   }
-  take(L.dmcp, (size_t)L.dmc_groups * L.dmc_nchunks * h->M * h->M * 4);
-  L.mfma_mix = h->M <= 256;
+  take(L.dmcp, h->mala ? 0 : (size_t)L.dmc_groups * L.dmc_nchunks * h->M * h->M * 4);
+  L.mfma_mix = !h->mala && h->M <= 256;   // MALA (one block) has no mixing
   L.mix = mhla::mix_shape((int)h->M, true);
   const size_t fb = L.mfma_mix ? (size_t)h->mcf_heads * L.mix.nitp * L.mix.nbc * 512 * 2 : 0;
   take(L.mcf_hi, fb);
@@ -599,7 +606,7 @@ BwdLayout bwd_layout(const mhla_plan* h) {
 }
 
 mhla_status bwd_supported(const mhla_plan* h) {
-  if (h->mala || h->causal) return MHLA_ERR_UNSUPPORTED;   // no MALA or causal backward here
+  if (h->causal) return MHLA_ERR_UNSUPPORTED;   // no causal backward here
   if (h->d < 32) return MHLA_ERR_UNSUPPORTED;   // head sizes 32, 64, 128
   return MHLA_OK;
 }
@@ -621,6 +628,7 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
   const mhla_status st = bwd_supported(h);
   if (st != MHLA_OK) return st;
   if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
+  if (h->mala && dmc) return MHLA_ERR_INVALID_ARG;   // MALA has no M_c
   const void* ins[] = {q, k, v, dout};
   void* outs[] = {dq, dk, dv};
   for (const void* a : ins)
@@ -670,9 +678,29 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
       sp.mcf_nitp = L.mix.nitp;
       sp.mcf_nbc = L.mix.nbc;
     }
-    hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, true, h->in_fp32, false, false, phi,
+    if (h->mala) sp.pu = F(L.pu);
+    hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, true, h->in_fp32, h->mala, false, phi,
                                         units_sum, s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+    // MALA: C = S - z u^T / N, z, u / N (stage 0); dS, dz = dz' - dS u / N, du (stage 1)
+    auto mala_stage = [&](int stage) -> hipError_t {
+      mhla::MalaStageParams mp = {};
+      mp.ps = F(stage == 0 ? L.ps : L.dps);
+      mp.pz = F(stage == 0 ? L.pz : L.dpzs);
+      mp.pu = F(L.pu);
+      mp.ub = F(L.ub);
+      mp.du_part = F(L.du_part);
+      mp.y_hi = U16(stage == 0 ? L.st_hi : L.ds_hi);
+      mp.y_lo = U16(stage == 0 ? L.st_lo : L.ds_lo);
+      mp.zo = F(stage == 0 ? L.zt : L.dz);
+      mp.ub_out = F(L.ub);
+      mp.du = F(L.du);
+      mp.ss = h->sum_splits;
+      mp.rs = h->rd_splits;
+      mp.N = (int32_t)h->N;
+      mp.stage = stage;
+      return mhla::launch_mala_stage(mp, h->d, (int)h->BH, s);
+    };
     // mixing with W = M_c (mc_transposed = 0) or M_c^T (1): S~ = M_c S, then dS = M_c^T dS~
     auto mix = [&](const float* xs, const float* zs, int zsplits, int transposed, uint16_t* y_hi,
                    uint16_t* y_lo, float* zo) -> hipError_t {
@@ -710,9 +738,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
       mp.mc_transposed = transposed;
       return mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, true, s);
     };
-    if ((e = mix(F(L.ps), F(L.pz), h->sum_splits, 0, U16(L.st_hi), U16(L.st_lo), F(L.zt))) != hipSuccess ||
-        !mark())
-      return MHLA_ERR_HIP;
+    e = h->mala ? mala_stage(0) : mix(F(L.ps), F(L.pz), h->sum_splits, 0, U16(L.st_hi), U16(L.st_lo), F(L.zt));
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
     // 3. query side: dq, g, dz~ partials
     mhla::BwdParams bp = {};
@@ -731,6 +758,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     bp.dz = F(L.dz);
     bp.tok_scale = F(L.tok_scale);
     bp.tok_zw = F(L.tok_zw);
+    bp.du_part = h->mala ? F(L.du_part) : nullptr;
+    bp.du = nullptr;                                    // set for the key side below
     bp.g = h->geom;
     bp.splits = h->rd_splits;
     bp.tok_per_split = h->rd_tok;
@@ -746,6 +775,7 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     mhla::SummaryParams sq = sp;
     sq.k = q;
     sq.v = dout;
+    sq.pu = nullptr;
     sq.ps = F(L.dps);
     sq.pz = F(L.dpzs);
     sq.kscale = F(L.tok_scale);
@@ -759,11 +789,11 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
     // 5. dS = M_c^T dS~, dz = M_c^T dz~
-    if ((e = mix(F(L.dps), F(L.dpzs), h->sum_splits, 1, U16(L.ds_hi), U16(L.ds_lo), F(L.dz))) != hipSuccess ||
-        !mark())
-      return MHLA_ERR_HIP;
+    e = h->mala ? mala_stage(1) : mix(F(L.dps), F(L.dpzs), h->sum_splits, 1, U16(L.ds_hi), U16(L.ds_lo), F(L.dz));
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
     // 6. key side: dk, dv
+    bp.du = h->mala ? F(L.du) : nullptr;
     if ((e = mhla::launch_bwd_tiles(bp, h->d, h->in_fp32, h->out_fp32, h->mode, phi, true, units_rd, s)) !=
             hipSuccess ||
         !mark())
