@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmhla.so")
 PEAK_SOURCE = "peak_probe.hip"
 PEAK_LIB = os.path.join(PKG, "libmhla_peak.so")
 
-SOURCES = ["summary.hip", "summary_dma.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "decode.hip",
+SOURCES = ["summary.hip", "summary_dma.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "causal_slice.hip", "decode.hip",
            "mhla_host.cpp", "noalloc.hip"]
 
 

@@ -109,7 +109,9 @@ __global__ __launch_bounds__((CausalShape<D, sizeof(TIn) == 4>::NT)) void causal
   float* kr32 = reinterpret_cast<float*>(kr_hi);
   float* vt32 = reinterpret_cast<float*>(vt_hi);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
+  // the wave index in a scalar register: the per-wave roles below are uniform branches
+  const int tid = threadIdx.x, lane = tid & 63, pr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Geom& geo = p.g;
 
   // unit L -> (head, block, token slice); all units of a head on one XCD when BH % 8 == 0
@@ -505,9 +507,18 @@ static hipError_t causal_dispatch_d(const CausalParams& p, int d, int n, hipStre
   }
 }
 
+hipError_t launch_causal_slice(const CausalParams& p, int d, bool out_fp32, int phi, int n_units, hipStream_t stream);
+
+// bf16 inputs: the slice kernel (causal_slice.hip); fp32 inputs: the kernel above.
+#ifndef MHLA_CAUSAL_SLICE
+#define MHLA_CAUSAL_SLICE 1
+#endif
+
 // n_units = splits * M * BH.
 hipError_t launch_causal(const CausalParams& p, int d, bool in_fp32, bool out_fp32, int phi, int n_units,
                          hipStream_t stream) {
+  if (MHLA_CAUSAL_SLICE && !in_fp32 && p.tok_per_split <= 256)
+    return launch_causal_slice(p, d, out_fp32, phi, n_units, stream);
   auto go = [&](auto phi_c) {
     constexpr int PHI = decltype(phi_c)::value;
     if (in_fp32)

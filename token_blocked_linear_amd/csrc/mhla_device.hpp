@@ -267,6 +267,7 @@ struct CausalParams {
   int32_t BH;
   int32_t xcd_map;
   int32_t normalized;
+  int32_t split;           // 1: split (hi / lo) operands throughout (the slice kernel's precision)
 };
 
 // Streaming decode step (one token per (batch, head)); the state layout is in decode.hip.

@@ -229,8 +229,9 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   P->mala = d->readout == MHLA_READOUT_MALA;
   P->causal = causal;
   P->mode = d->readout;
-  // The causal kernel keeps its running state and in-sub-chunk scores split whatever this says;
-  // `split` sets the precision of the summaries and the mixing (of the earlier blocks, there).
+  // `split` sets the precision of the summaries and the mixing (of the earlier blocks, for the
+  // causal readout), and of the bf16-input causal kernel's own products; the fp32-input causal
+  // kernel keeps its running state and in-sub-chunk scores split whatever this says.
   if (d->accuracy == MHLA_ACCURACY_SPLIT)
     P->split = true;
   else if (d->accuracy == MHLA_ACCURACY_BF16)
@@ -507,6 +508,7 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
       cp.BH = (int32_t)h->BH;
       cp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
       cp.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
+      cp.split = h->split ? 1 : 0;
       e = mhla::launch_causal(cp, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
                               (int)(h->rd_splits * h->M * h->BH), s);
       if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
