@@ -222,7 +222,8 @@ __global__ __launch_bounds__(bwd_threads<D>()) void dq_kernel(BwdParams p, int m
   uint16_t* s_z = sb_lo + FRAG;           // normaliser fragments
   float* s_zt = reinterpret_cast<float*>(s_z + ZF);   // z~ [D]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, pr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const Geom& geo = p.g;
   const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
 
@@ -426,7 +427,8 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
   float* s_dz = reinterpret_cast<float*>(s2_lo + FRAG);   // dz_b [D]
   float* s_du = s_dz + D;                                  // du (MALA) or zeros [D]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, pr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, pr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const Geom& geo = p.g;
   const BwdUnit U = bwd_unit<D>(p, blockIdx.x);
 
@@ -524,22 +526,27 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
 
 // ---- dM_c ---------------------------------------------------------------------------------
 // dmc[i][b] = sum over (batch-head, position) of dS~_i and S_b (fragment positions, then the D
-// normaliser entries), both summed over their token slices while loaded.  A 64 x 64 output tile
-// and one chunk of 64-position steps per workgroup; each step is staged through LDS as bf16
-// hi / lo, and each wave owns a 32 x 32 quarter (2 x 2 MFMA tiles): A = dS~ rows, B = S rows,
-// both with 8 consecutive positions per lane.  The next step's loads are in flight during the
-// MFMAs.  Positions past FRAG + D (the last step of a (batch, head)) read as zero.
-constexpr int kDmcTile = 64, kDmcK = 64, kDmcPitch = kDmcK + 8;   // pitch in bf16 elements
+// normaliser entries), both summed over their token slices while loaded.  A TILE x TILE output
+// tile and one chunk of 64-position steps per workgroup; each step is staged through LDS as bf16
+// hi / lo, and each wave owns 32 rows x (TILE / 2) columns (2 x TILE / 32 MFMA tiles): A = dS~
+// rows, B = S rows, both with 8 consecutive positions per lane.  The next step's loads are in
+// flight during the MFMAs.  Positions past FRAG + D (the last step of a (batch, head)) read as
+// zero.  The fp32 -> hi / lo conversion of the staged rows is the kernel's main work, and every
+// row is staged once per output tile of its chunk: 128 x 128 tiles (8 waves) once M > 64 convert
+// half as often as 64 x 64 tiles (4 waves).
+constexpr int kDmcK = 64, kDmcPitch = kDmcK + 8;   // positions per step; LDS pitch in bf16 elements
 
 // SINGLE: every summary has one token slice (ssplits = zsplits_d = 1).  The step's loads then
 // go straight into registers through buffer resources (rows past M and positions past FRAG + D
 // read as zero) and are converted at the LDS store, so they stay in flight during the MFMAs;
 // with several slices they are summed as they arrive.
-template <bool SINGLE>
-__global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
+template <bool SINGLE, int TILE>
+__global__ __launch_bounds__(TILE * 4) void dmc_kernel(DmcParams p) {
+  constexpr int kDmcTile = TILE, WB = TILE / 32;   // WB: MFMA column tiles per wave
   __shared__ __align__(16) uint16_t a_hi[kDmcTile * kDmcPitch], a_lo[kDmcTile * kDmcPitch];
   __shared__ __align__(16) uint16_t b_hi[kDmcTile * kDmcPitch], b_lo[kDmcTile * kDmcPitch];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int M = p.M, FRAG = p.frag, D = p.D;
   const int nt = (M + kDmcTile - 1) / kDmcTile;
   // Workgroup L -> (chunk, output tile): the nt^2 tiles of one chunk read the same rows, so
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
   const int i0 = (tile / nt) * kDmcTile, b0 = (tile % nt) * kDmcTile;
   const int grp = blockIdx.y;
   const int lrow = tid >> 2, lcol = (tid & 3) * 16;   // loader: one row, 16 positions
-  const int wi = (wave >> 1) * 32, wb = (wave & 1) * 32;
+  const int wi = (wave >> 1) * 32, wb = (wave & 1) * (TILE / 2);
   const int64_t total_steps = (int64_t)p.group_bh * p.steps_per_bh;
   const int64_t s_begin = (int64_t)chunk * p.steps_per_chunk;
   const int64_t s_end = min(s_begin + p.steps_per_chunk, total_steps);
@@ -618,11 +625,11 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
     }
   };
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[2][WB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < WB; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   float xa[2][8], xb[2][8];
   if (s_begin < s_end) {
@@ -653,29 +660,32 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
 #pragma unroll
     for (int k2 = 0; k2 < kDmcK; k2 += 32) {
       const int kk = k2 + 8 * (lane >> 4);
-      u32x4_t fah[2], fal[2], fbh[2], fbl[2];
+      u32x4_t fah[2], fal[2], fbh[WB], fbl[WB];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int ra = (wi + 16 * a + (lane & 15)) * kDmcPitch + kk;
-        const int rb = (wb + 16 * a + (lane & 15)) * kDmcPitch + kk;
         fah[a] = *reinterpret_cast<const u32x4_t*>(a_hi + ra);
         fal[a] = *reinterpret_cast<const u32x4_t*>(a_lo + ra);
-        fbh[a] = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
-        fbl[a] = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
       }
-      // three rounds over the four independent accumulators
+#pragma unroll
+      for (int c = 0; c < WB; ++c) {
+        const int rb = (wb + 16 * c + (lane & 15)) * kDmcPitch + kk;
+        fbh[c] = *reinterpret_cast<const u32x4_t*>(b_hi + rb);
+        fbl[c] = *reinterpret_cast<const u32x4_t*>(b_lo + rb);
+      }
+      // three rounds over the independent accumulators
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbh[c], acc[a][c]);
+        for (int c = 0; c < WB; ++c) acc[a][c] = mfma_bf16(fah[a], fbh[c], acc[a][c]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fal[a], fbh[c], acc[a][c]);
+        for (int c = 0; c < WB; ++c) acc[a][c] = mfma_bf16(fal[a], fbh[c], acc[a][c]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = mfma_bf16(fah[a], fbl[c], acc[a][c]);
+        for (int c = 0; c < WB; ++c) acc[a][c] = mfma_bf16(fah[a], fbl[c], acc[a][c]);
     }
     __syncthreads();
   }
@@ -683,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void dmc_kernel(DmcParams p) {
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < WB; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + wi + 16 * a + 4 * (lane >> 4) + r;
@@ -878,13 +888,19 @@ hipError_t launch_mala_stage(const MalaStageParams& p, int d, int bh, hipStream_
 }
 
 hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream) {
-  const int t = (p.M + kDmcTile - 1) / kDmcTile;
+  const int tile = dmc_tile(p.M);
+  const int t = (p.M + tile - 1) / tile;
   const int groups = p.per_head ? p.H : 1;
   const int c8 = (p.nchunks + 7) / 8;
-  if (p.ssplits == 1 && p.zsplits_d == 1)
-    hipLaunchKernelGGL(dmc_kernel<true>, dim3(8 * c8 * t * t, groups), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(dmc_kernel<false>, dim3(8 * c8 * t * t, groups), dim3(kThreads), 0, stream, p);
+  const bool single = p.ssplits == 1 && p.zsplits_d == 1;
+  const dim3 grid(8 * c8 * t * t, groups);
+  if (tile == 128) {
+    if (single) hipLaunchKernelGGL((dmc_kernel<true, 128>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((dmc_kernel<false, 128>), grid, dim3(512), 0, stream, p);
+  } else {
+    if (single) hipLaunchKernelGGL((dmc_kernel<true, 64>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((dmc_kernel<false, 64>), grid, dim3(256), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t mm = (int64_t)p.M * p.M, n_out = (int64_t)groups * mm;

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
   __shared__ float s_q[D], s_k[D], s_v[D], s_den[4];
   __shared__ float4 s_part[kThreads];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int lc = p.log2_c, C = 1 << lc, S = D >> lc;         // C * D >= 1024
   const int DC = D * C, per = DC / (4 * kThreads);            // float4s of a matrix per thread
   const int bh = (int)(blockIdx.x / S), sl = (int)(blockIdx.x % S), h = bh % p.H;

@@ -233,6 +233,9 @@ struct MalaStageParams {
 // The contraction runs over (batch-head, position) pairs of a group: every (batch, head) for a
 // shared M_c, every batch item of head g for a per-head one (bh = j*H + g).  It is cut into
 // `nchunks` chunks of `steps_per_chunk` 64-position steps, each chunk giving one partial.
+// dM_c output tile (rows and columns) of one workgroup: 128 once M > 64, else 64.
+__host__ __device__ constexpr int dmc_tile(int M) { return M > 64 ? 128 : 64; }
+
 struct DmcParams {
   const float* dps;        // dS~ partials [BH][M][ssplits][FRAG]
   const float* ps;         // S partials   [BH][M][ssplits][FRAG]

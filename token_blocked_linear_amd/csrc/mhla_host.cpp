@@ -586,9 +586,10 @@ BwdLayout bwd_layout(const mhla_plan* h) {
     L.dmc_group_bh = h->desc.mc_per_head ? (int)h->B : (int)h->BH;
     L.dmc_steps_per_bh = (h->frag + h->d + 63) / 64;   // 64-position steps (the last one padded)
     const int64_t total = (int64_t)L.dmc_group_bh * L.dmc_steps_per_bh;
-    const int64_t t = (h->M + 63) / 64;
-    // about 2048 workgroups (8 per CU)
-    int64_t n = (2048 + t * t * L.dmc_groups - 1) / (t * t * L.dmc_groups);
+    const int64_t tile = mhla::dmc_tile((int)h->M), t = (h->M + tile - 1) / tile;
+    // about 8 waves' worth of workgroups per SIMD: 2048 of 4 waves, 1024 of 8
+    const int64_t want = tile == 128 ? 1024 : 2048;
+    int64_t n = (want + t * t * L.dmc_groups - 1) / (t * t * L.dmc_groups);
     if (n > total) n = total;
     if (n < 1) n = 1;
     const int64_t spc = (total + n - 1) / n;

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   extern __shared__ __align__(16) uint16_t xt[];   // [PB][XP] (hi), then [PB][XP] (lo) if SPLIT
   uint16_t* xt_lo = xt + PB * XP;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int pr = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.z;
   const int M = p.M;

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const Geom& g = p.g;
   const RdUnit U = rd_unit<D>(p, blockIdx.x);
   const int bh = U.bh, blk = U.blk;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SummaryParams p, int 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const Geom& g = p.g;
   const int fgrp = tid % LPR;              // features [8*fgrp, 8*fgrp+8)
   const int tgrp = tid / LPR;              // tokens [8*tgrp, 8*tgrp+8) of each round

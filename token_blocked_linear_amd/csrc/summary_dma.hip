@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
   float* red = reinterpret_cast<float*>(smem + kStages * kStageBytes);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(MHLA_LDS char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
   const int kc = wave % NKC, kh = wave / NKC;
   const int g = lane >> 4, lam = lane & 15;
   const Geom& geo = p.g;
