@@ -79,3 +79,75 @@ def mala(q, k, v, *, naive=False, rounding=None):
 
 def rel(got, want):
     return float(np.max(np.abs(got - want)) / np.sqrt(np.mean(want ** 2)))
+
+
+def phi_exp(x):
+    return np.exp(x)
+
+
+def causal_1d(q, k, v, mc, n_b, *, q_single=False, k_single=False, p_mode="exact", stack=False):
+    """Chunkwise-causal MHLA readout of one head (1D, blocks of n_b tokens, one token slice per
+    block) as the bf16-input slice kernel computes it: o_t = (q~_t S0_i + sum_{j<=t in i} P_tj v_j)
+    / (q~_t z0_i + sum_{j<=t in i} P_tj) with S0_i = sum_{b<i} m_ib S_b, z0_i likewise and
+    P_tj = q~_t . m_ii k~_j.  Rounds: phi(q) and m_ii phi(K) to single bf16 (the scores' and the
+    S0 readout's MFMA operands), P to single bf16 ("bf") or hi + lo ("split") as the B operand of
+    V^T P, and (stack) the bf16 summary and mixed stacks.  The normaliser sums P unrounded."""
+    n, d = q.shape
+    m = n // n_b
+    pk = phi_elu1(k)
+    s = np.einsum("bjk,bjc->bkc", pk.reshape(m, n_b, d), v.reshape(m, n_b, d))
+    z = pk.reshape(m, n_b, d).sum(1)
+    if stack:
+        s = bf(s)
+    out = np.empty_like(q)
+    rp = {"exact": lambda x: x, "bf": bf, "split": split}[p_mode]
+    for i in range(m):
+        sl = slice(i * n_b, (i + 1) * n_b)
+        s0 = np.einsum("b,bkc->kc", mc[i, :i], s[:i]) if i else np.zeros((d, d))
+        if stack:
+            s0 = bf(s0)
+        z0 = mc[i, :i] @ z[:i] if i else np.zeros(d)
+        qt = phi_elu1(q[sl])
+        qt = bf(qt) if q_single else qt
+        kt = mc[i, i] * pk[sl]
+        kt = bf(kt) if k_single else kt
+        p = np.tril(qt @ kt.T)
+        out[sl] = (qt @ s0 + rp(p) @ v[sl]) / (qt @ z0 + p.sum(1))[:, None]
+    return out
+
+
+def causal_rel(got, want):
+    """max |got - want| / max(RMS(want), |want|) elementwise (the causal readout's metric)."""
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    return float(np.max(np.abs(got - want) / np.maximum(rms, np.abs(want))))
+
+
+def backward_key_side(q, k, v, mc, do, n_b, phi="elu1", *, ds_single=False, phik_single=False):
+    """dK and dV of L = sum(dO * O) for one head of the normalised MHLA readout (1D, blocks of
+    n_b), by the chain rule of the forward steps, with the key-side products' operands optionally
+    single bf16: dS (in dk~ = dS v + dz and dv = dS^T phi(k)) and phi(K) (in dv).  Everything
+    before (S~, g, dS~, dS = M_c^T dS~, dz) is exact."""
+    f, df = (phi_elu1, lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))) if phi == "elu1" \
+        else (phi_exp, phi_exp)
+    n, d = q.shape
+    m = n // n_b
+    pq, pk = f(q), f(k)
+    kb, vb, qb, dob = (x.reshape(m, n_b, d) for x in (pk, v, pq, do))
+    s = np.einsum("bjk,bjc->bkc", kb, vb)
+    z = kb.sum(1)
+    st = np.einsum("ib,bkc->ikc", mc, s)
+    zt = mc @ z
+    num = np.einsum("itk,ikc->itc", qb, st)
+    den = np.einsum("itk,ik->it", qb, zt)
+    o = num / den[..., None]
+    g = dob / den[..., None]
+    gden = -np.einsum("itc,itc->it", dob, o) / den
+    dst = np.einsum("itk,itc->ikc", qb, g)
+    dzt = np.einsum("itk,it->ik", qb, gden)
+    ds = np.einsum("ib,ikc->bkc", mc, dst)
+    dz = mc.T @ dzt
+    ds_r = bf(ds) if ds_single else ds
+    kb_r = bf(kb) if phik_single else kb
+    dkt = np.einsum("bkc,bjc->bjk", ds_r, vb) + dz[:, None, :]
+    dv = np.einsum("bkc,bjk->bjc", ds_r, kb_r)
+    return (dkt.reshape(n, d) * df(k)), dv.reshape(n, d)

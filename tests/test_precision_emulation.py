@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from precision_emulation import bf, mala, mhla_1d, rel, split
+from precision_emulation import backward_key_side, bf, causal_1d, causal_rel, mala, mhla_1d, rel, split
 
 BAR = 2e-2
 
@@ -89,3 +89,52 @@ def test_mala_centred_identity_is_exact(mala_case):
     sq = pq @ z
     direct = (1.0 + 1.0 / sq)[:, None] * (pq @ s) - (sq / len(q))[:, None] * u[None, :]
     assert math.isclose(rel(direct, ref), 0.0, abs_tol=1e-12)
+
+
+@pytest.fixture(scope="module")
+def causal_case():
+    # one head of 1024 tokens in 4 blocks of 256, d = 64, a row-softmax M_c (the c_m4 GPU case's shape)
+    rng = np.random.default_rng(201)
+    n, d, n_b = 1024, 64, 256
+    q, k, v = (synth.round_to_bf16(rng.standard_normal((n, d), dtype=np.float32)).astype(np.float64)
+               for _ in range(3))
+    mc = synth.mc_softmax_gaussian(n // n_b, rng).astype(np.float32).astype(np.float64)
+    return q, k, v, mc, n_b, causal_1d(q, k, v, mc, n_b)
+
+
+def test_causal_scores_stay_split(causal_case):
+    """The bf16-input causal slice kernel: single bf16 phi(q) and m_ii phi(K) keep the causal
+    readout well inside its 2e-2 bar; rounding P (the weights of V) to one bf16 does not -- the
+    weighted sums of V cancel, so the weights' 2^-9 error grows with the keys in view -- and P
+    therefore stays split (hi + lo)."""
+    q, k, v, mc, n_b, ref = causal_case
+    kernel = causal_rel(causal_1d(q, k, v, mc, n_b, q_single=True, k_single=True, p_mode="split", stack=True), ref)
+    p_single = causal_rel(causal_1d(q, k, v, mc, n_b, p_mode="bf"), ref)
+    all_single = causal_rel(causal_1d(q, k, v, mc, n_b, q_single=True, k_single=True, p_mode="bf", stack=True), ref)
+    print(f"kernel roundings {kernel:.3e}, P single alone {p_single:.3e}, all single {all_single:.3e}")
+    assert kernel < BAR / 2
+    assert p_single > BAR and all_single > BAR
+
+
+@pytest.mark.parametrize("phi", ["elu1", "exp"])
+def test_backward_key_side_needs_split_operands(phi):
+    """dK = (dS v + dz) phi'(k): the two terms nearly cancel (the gradient of a normalised average
+    sums to about zero over the keys), so a single bf16 dS fails the backward's bar under the exp
+    map and takes most of it under ELU+1; split operands (the kernels' choice for every backward
+    product) leave it far below."""
+    rng = np.random.default_rng(77)
+    n, d, n_b = 4096, 128, 256
+    q, k, v, do = (synth.round_to_bf16(rng.standard_normal((n, d), dtype=np.float32)).astype(np.float64)
+                   for _ in range(4))
+    mc = synth.mc_softmax_gaussian(n // n_b, rng).astype(np.float32).astype(np.float64)
+    dk, dv = backward_key_side(q, k, v, mc, do, n_b, phi)
+    dk1, dv1 = backward_key_side(q, k, v, mc, do, n_b, phi, ds_single=True, phik_single=True)
+    e_dk, e_dv = rel(dk1, dk), rel(dv1, dv)
+    dk2, dv2 = backward_key_side(q, k, v, mc, do, n_b, phi, ds_single=False)
+    print(f"{phi}: single dS -> dK {e_dk:.3e}, single dS and phi(K) -> dV {e_dv:.3e}")
+    assert rel(dk2, dk) == 0.0
+    if phi == "exp":
+        assert e_dk > BAR
+    else:
+        assert e_dk > BAR / 4
+    assert e_dv < e_dk
