@@ -25,10 +25,12 @@
 //      operand of V^T P as it stands.  Two key tiles form one 16x16x32 step of V^T P whose A
 //      operand (channel rows, keys 4g .. 4g+3 of each tile) is two ds_read_b64_tr_b16 of V.
 //   3. The readout against S0: O^T += S0^T q~ with permuted A rows (lane (t, g) ends with
-//      channels 8g .. 8g+7 of each 32-channel pair), den0 from a normaliser operand built in
-//      registers (rows 4g: hi(z0), 4g + 1: lo(z0)).  An S0 that is a bf16 fragment stack read
-//      with single operands is DMA'd into the LDS space that the keys' low parts would take
-//      (unused then), in the readout kernel's bank-spreading order, at the unit's first phase;
+//      channels 8g .. 8g+7 of each 32-channel pair).  (den0 = q~ . z0 is taken at the unit's
+//      start, from a normaliser operand built in registers, rows 4g: hi(z0), 4g + 1: lo(z0), out
+//      of a z0 row that the previous unit DMA'd into a per-wave slot of the V space.)  An S0 that
+//      is a bf16 fragment stack read with single operands is DMA'd into the LDS space that the
+//      keys' low parts would take (unused then), in the readout kernel's bank-spreading order, at
+//      the unit's first phase;
 //      otherwise the A operands come straight from global memory (the unit's waves share them in
 //      L2) and are combined and split in registers.
 //   4. o_t = num_t / den_t (normalised) or num_t, 16-byte stores.
@@ -88,6 +90,7 @@ struct SliceShape {
   static constexpr int NW = 8, NT = 64 * NW;         // waves, threads per workgroup
   static constexpr int KH = D >= 128 ? 128 : 256;    // keys per phase
   static constexpr int KT = KH / 16;                 // key tiles per phase
+  static constexpr int NPH = 256 / KH;               // phases of a full (256-token) slice
   static constexpr int NCH = D / 8;                  // 16-byte chunks per token row
   static constexpr int RPT = KH * NCH / NT;          // K (and V) chunks staged per thread per phase
   static constexpr int QDMA = 16 * NCH / 64;         // DMA instructions per query tile
@@ -123,6 +126,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
   using SS = SliceShape<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG, NG = NCT / 2;
   constexpr int NT = SS::NT, KH = SS::KH, KT = SS::KT, NCH = SS::NCH, RPT = SS::RPT, QDMA = SS::QDMA;
+  constexpr int NPH = SS::NPH;
   static_assert(RPT >= 1 && KH * NCH % NT == 0 && QDMA >= 1, "staging shape");
   constexpr int NST = 2 * NG * (sizeof(TOut) == 4 ? 2 : 1);   // output stores per wave and unit
 
@@ -175,7 +179,10 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
     U.n_tiles = (U.j_end - U.j_begin + 15) >> 4;
     U.head_off = (int64_t)U.bh * geo.N * D;
     U.row = (int64_t)U.bh * geo.M + blk;
-    U.mii = p.mc ? p.mc[(int64_t)(U.bh % p.H) * p.mc_head_stride + (int64_t)blk * geo.M + blk] : 1.0f;
+    // m_ii through the scalar cache (an input the kernel never writes, at a uniform address), so
+    // that the next unit's value waits in a scalar register rather than a vector one
+    typedef const __attribute__((address_space(4))) float ConstF;
+    U.mii = p.mc ? *(ConstF*)(p.mc + (int64_t)(U.bh % p.H) * p.mc_head_stride + (int64_t)blk * geo.M + blk) : 1.0f;
     return U;
   };
   constexpr uint32_t ES = 2;
@@ -199,6 +206,12 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
       }
     }
   };
+  // Phases take the slice's key pairs (32 keys, two tiles) round robin: local pair kp of phase ph
+  // is pair kp * NPH + ph.  Every wave then meets about the same number of active pairs in each
+  // phase (its two query tiles w and 15 - w see the causal triangle's short and long rows), where
+  // consecutive key ranges would load the waves' barriers unevenly.  Slice-relative key of local
+  // key row rr of phase ph:
+  auto key_of = [](int ph, int rr) -> int32_t { return 32 * ((rr >> 5) * NPH + ph) + (rr & 31); };
   // K and V of phase ph of unit U into registers (rows past the slice read as zero)
   In8<uint16_t> ck[RPT], cv[RPT];
   auto issue_kv = [&](const Unit& U, int ph) {
@@ -208,17 +221,33 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int idx = tid + i * NT, rr = idx / NCH, c = idx % NCH;
-      const int32_t j = ph * KH + rr;
+      const int32_t j = key_of(ph, rr);
       const uint32_t off = U.j_begin + j < U.j_end ? (tok(U, j) + 8 * c) * ES : kOutOfRange;
       ck[i].template load_buf<0>(rk, off);
       cv[i].template load_buf<0>(rv, off);
     }
   };
 
+  // z0 of unit X (the slice's start normaliser: the mixed z~ row plus m_ii times the in-block
+  // prefix of earlier slices) into the wave's own 2 KB slot of the V space: the z~ row at +0, the
+  // prefix row at +1 KB (one 16-byte DMA per lane each; lanes past the row write zeros).  Issued
+  // where no wave reads the V space until the next unit's first staging, older than the wave's
+  // output stores, so that the wait at the top of the next unit covers it.
+  float* const z_slot = reinterpret_cast<float*>(v_s) + wave * 512;
+  const uint32_t z_lds = (uint32_t)(uintptr_t)(MHLA_CS_LDS char*)smem + (uint32_t)(2 * SS::K_BYTES) + (uint32_t)wave * 2048u;
+  static_assert(8 * 2048 <= SS::K_BYTES, "z0 slots");
+  auto dma_z = [&](const Unit& X) {
+    const int lane = tid_v & 63;
+    const uint32_t voff = lane < D / 4 ? (uint32_t)lane * 16u : kOutOfRange;
+    if (p.zt) cs_dma16(z_lds, voff, cs_rsrc_words(p.zt + X.row * D, D * 4u));
+    if (p.prez) cs_dma16(z_lds + 1024u, voff, cs_rsrc_words(p.prez + (X.row * p.splits + X.split) * D, D * 4u));
+  };
+
   int L = blockIdx.x;
   Unit U = decode(L);
   dma_q(U);
   issue_kv(U, 0);
+  dma_z(U);
 
   for (;;) {
     asm volatile("" : "+v"(tid_v));
@@ -254,6 +283,54 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
         }
       }
     }
+    // den0 = phi(q) . z0 on the matrix cores, from the wave's z0 slot (landed: the wait above).
+    // Normaliser operand: rows 4g = hi(z0), 4g + 1 = lo(z0); every lane gets its token's den0,
+    // which seeds the in-slice sum on the lg = 0 lanes only (that sum is reduced over lg).
+    float dsum[2] = {0.f, 0.f};
+    if (p.zt || p.prez) {   // either may be absent (no mixing; one slice per block)
+      f32x4_t accz[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        float z8[8];
+        {
+          f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = a;
+          if (p.zt) {
+            a = *reinterpret_cast<const f32x4_t*>(z_slot + 32 * kc + 8 * lg);
+            b = *reinterpret_cast<const f32x4_t*>(z_slot + 32 * kc + 8 * lg + 4);
+          }
+          if (p.prez) {
+            const f32x4_t c = *reinterpret_cast<const f32x4_t*>(z_slot + 256 + 32 * kc + 8 * lg);
+            const f32x4_t d = *reinterpret_cast<const f32x4_t*>(z_slot + 256 + 32 * kc + 8 * lg + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] = fmaf(U.mii, c[e], a[e]);
+              b[e] = fmaf(U.mii, d[e], b[e]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            z8[e] = a[e];
+            z8[4 + e] = b[e];
+          }
+        }
+        u32x4_t az = {0u, 0u, 0u, 0u};
+        if ((pr & 3) < 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t h, l;
+            split_bf16x2(z8[2 * i], z8[2 * i + 1], h, l);
+            az[i] = (pr & 3) == 0 ? h : l;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          accz[t] = mfma_bf16(az, bqh[t][kc], accz[t]);
+          if constexpr (SPLIT) accz[t] = mfma_bf16(az, bql[t][kc], accz[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) dsum[t] = lg == 0 ? accz[t][0] + accz[t][1] : 0.f;
+    }
     Unit Un = U;
     if (has_next) {
       Un = decode(Ln);
@@ -262,7 +339,6 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
     }
 
     f32x4_t acc[2][NCT];
-    float dsum[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -271,7 +347,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
     const float mii = U.mii;
 
     // ---- 2. the slice's keys, a phase at a time ----
-    const int n_ph = (U.n_tiles + KT - 1) / KT;
+    const int n_ph = min(NPH, (U.n_tiles + 1) >> 1);   // phases that hold a key pair
     for (int ph = 0; ph < n_ph; ++ph) {
       __syncthreads();   // the previous phase (or unit) is done with the key space (and S0)
       if (S0_LDS && ph == 0 && p.st_hi) {
@@ -287,7 +363,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int idx = tid + i * NT, rr = idx / NCH, c = idx % NCH;
-        const bool ok = U.j_begin + ph * KH + rr < U.j_end;
+        const bool ok = U.j_begin + key_of(ph, rr) < U.j_end;
         float kf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) kf[e] = ok ? mii * phi_map<PHI>(ck[i].get(e)) : 0.f;
@@ -299,7 +375,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
       __syncthreads();
 
       for (int kp = 0; kp < KT / 2; ++kp) {
-        const int kt0 = ph * KT + 2 * kp;         // key tiles kt0, kt0 + 1 (slice-relative)
+        const int kt0 = 2 * (kp * NPH + ph);      // key tiles kt0, kt0 + 1 (slice-relative)
         if (kt0 > max_qt || kt0 >= U.n_tiles) break;
         // Query tile t takes part when kt0 <= its index; tile 1 (15 - w) ranks above tile 0, so
         // the cases are: both, tile 1 alone, or (a short slice without tile 1) tile 0 alone.
@@ -317,7 +393,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
             u32x4_t kh[2], kl[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const int krow = (kt0 + h - ph * KT) * 16 + pr;
+              const int krow = (2 * kp + h) * 16 + pr;
               const int off = krow * D + 8 * ((4 * kc + lg) ^ row_swz<D>(krow));
               kh[h] = *reinterpret_cast<const u32x4_t*>(k_hi + off);
               if constexpr (SPLIT) kl[h] = *reinterpret_cast<const u32x4_t*>(k_lo + off);
@@ -360,7 +436,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
           }
           // V^T P over the 32 keys: A = V^T rows (permuted channels), two transposed reads
           const MHLA_CS_LDS char* vbase = (const MHLA_CS_LDS char*)(v_s);
-          const int r0 = (kt0 - ph * KT) * 16 + 4 * lg + (pr >> 2);   // the row this lane supplies
+          const int r0 = 2 * kp * 16 + 4 * lg + (pr >> 2);   // the row this lane supplies
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
             const int ch = 4 * (ct >> 1) + (pr & 3);                   // chunk of the 4 channels
@@ -384,47 +460,21 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
     }
 
     // ---- 3. readout against S0, A operands from the fragment-layout summaries in global memory ----
-    float den0[2] = {0.f, 0.f};
     if constexpr (S0_LDS) {
       // the S0 DMA was issued before the last issue_kv (2 RPT loads), which alone may be newer
       if (has_next) cs_wait_vm<2 * RPT>();
       else cs_wait_vm0();
-      __syncthreads();   // every wave's part of S0
     }
+    __syncthreads();   // every wave's part of S0; no wave reads K or V of this unit any more
+    dma_z(Un);         // (with no next unit Un is U: a harmless reload)
     if (max_qt >= 0) {
       const uint16_t* sh = p.st_hi ? p.st_hi + U.row * FRAG : nullptr;
       const uint16_t* sl = p.st_lo ? p.st_lo + U.row * FRAG : nullptr;
       const float* sp = p.pre ? p.pre + (U.row * p.splits + U.split) * FRAG : nullptr;
       const int b3 = (pr >> 2) & 1;
       const AOffsets ao = a_offsets(lane);
-      f32x4_t accz[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        // normaliser operand: rows 4g = hi(z0), 4g + 1 = lo(z0) over features 32kc + 8lg + e
-        {
-          const int f0 = 32 * kc + 8 * lg;
-          float z8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float zz = p.zt ? p.zt[U.row * D + f0 + e] : 0.f;
-            if (p.prez) zz = fmaf(mii, p.prez[(U.row * p.splits + U.split) * D + f0 + e], zz);
-            z8[e] = zz;
-          }
-          u32x4_t az = {0u, 0u, 0u, 0u};
-          if ((pr & 3) < 2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              uint32_t h, l;
-              split_bf16x2(z8[2 * i], z8[2 * i + 1], h, l);
-              az[i] = (pr & 3) == 0 ? h : l;
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            accz[t] = mfma_bf16(az, bqh[t][kc], accz[t]);
-            if constexpr (SPLIT) accz[t] = mfma_bf16(az, bql[t][kc], accz[t]);
-          }
-        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           // A row pr of tile ct: channel 32(ct/2) + 8(pr/4) + 4(ct%2) + pr%4, i.e. fragment
@@ -479,9 +529,8 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
           if (ct & 1) __builtin_amdgcn_sched_barrier(0);   // two tiles' loads in flight at a time
         }
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) den0[t] = accz[t][0] + accz[t][1];
     }
+
 
     // ---- 4. o = num / den: a fixed number of buffer stores per wave (idle lanes and tiles out of
     //      range, dropped), so that the next unit's wait can leave them outstanding ----
@@ -493,7 +542,7 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
       ds += __shfl_xor(ds, 32);
       const int32_t j = 16 * qtile[t] + pr;
       const bool ok = qv[t] && U.j_begin + j < U.j_end;
-      const float scale = p.normalized ? 1.0f / (den0[t] + ds) : 1.0f;
+      const float scale = p.normalized ? 1.0f / ds : 1.0f;   // ds includes den0
       const uint32_t rel = ok ? tok(U, j) : 0u;
 #pragma unroll
       for (int c = 0; c < NG; ++c) {
