@@ -30,7 +30,7 @@
 //      of a z0 row that the previous unit DMA'd into a per-wave slot of the V space.)  An S0 that
 //      is a bf16 fragment stack read with single operands is DMA'd into the LDS space that the
 //      keys' low parts would take (unused then), in the readout kernel's bank-spreading order, at
-//      the unit's first phase;
+//      the unit's last phase;
 //      otherwise the A operands come straight from global memory (the unit's waves share them in
 //      L2) and are combined and split in registers.
 //   4. o_t = num_t / den_t (normalised) or num_t, 16-byte stores.
@@ -350,9 +350,10 @@ __global__ __launch_bounds__(SliceShape<D>::NT) void causal_slice_kernel(CausalP
     const int n_ph = min(NPH, (U.n_tiles + 1) >> 1);   // phases that hold a key pair
     for (int ph = 0; ph < n_ph; ++ph) {
       __syncthreads();   // the previous phase (or unit) is done with the key space (and S0)
-      if (S0_LDS && ph == 0 && p.st_hi) {
+      if (S0_LDS && ph == n_ph - 1 && p.st_hi) {
         // S0 = this unit's bf16 stack fragments: LDS chunk u holds stack chunk u ^ (bit 3 of u
-        // moved to bit 2), the order of lds_pos (an involution)
+        // moved to bit 2), the order of lds_pos (an involution).  Issued at the last phase, so
+        // that the loads the phases before it wait for do not queue behind it
         constexpr int NDMA = FRAG / 512;        // 1 KB instructions
         const cs_i32x4_t rs = cs_rsrc_words(p.st_hi + U.row * FRAG, FRAG * 2u);
         for (int i = wave; i < NDMA; i += SS::NW) {
