@@ -180,6 +180,28 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
 mhla_status mhla_forward_noalloc(mhla_handle h, const void* q, const void* k, const void* v,
                                  const float* mc, void* o, void* stream);
 
+/* The forward's first two steps on their own, for inspecting them: the block summaries
+ * S_b = sum_{j in b} phi(k_j) v_j^T, z_b = sum_{j in b} phi(k_j) ("MHLA: Restoring Expressivity of
+ * Linear Attention via Token-Level Multi-Head", Overall framework) and the mixed summaries
+ * S~_i = sum_b m_ib S_b, z~_i = sum_b m_ib z_b (Key design 2; for the causal readouts b < i, the
+ * strictly lower part of M_c).  The plan's own summary and mixing kernels run at the plan's
+ * precision on `workspace` (as for mhla_forward); their results are then written out in fp32.
+ *   k, v, mc   as for mhla_forward (q is not read; nothing is written to an output tensor)
+ *   S          device fp32 [B*H][M][d][d], S[bh][b][f][c] = feature f of phi(k), channel c of v
+ *   z          device fp32 [B*H][M][d]
+ *   St, zt     device fp32, the same shapes, for the mixed summaries; both NULL to stop after the
+ *              summaries.  Non-NULL with a plan whose mixing runs inside its readout (at most 16
+ *              blocks, MALA; mhla_plan_info.n_kernels == 2) or with one block in a causal plan,
+ *              which keep no mixed stack: MHLA_ERR_UNSUPPORTED.
+ * Values are those the forward computes and then reads: bf16 where the plan's stacks are bf16
+ * (the summary of a one-slice block under bf16 operands, the mixed stack's high part), else the
+ * sum of fp32 slice partials or of the hi and lo parts.  The buffers belong to the caller and must
+ * not overlap the workspace.  Errors: INVALID_ARG (NULL k, v, S or z; only one of St, zt; mc NULL
+ * with M > 1; misaligned pointers), WORKSPACE, UNSUPPORTED, HIP.  Asynchronous on `stream`. */
+mhla_status mhla_forward_intermediates(mhla_handle h, const void* k, const void* v, const float* mc, float* S,
+                                       float* z, float* St, float* zt, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Backward pass: gradients of L = sum(dout * O) with respect to Q, K, V and M_c, for the
  * normalised, unnormalised and MALA readouts (chain rule of the forward steps; M_c is trained end
  * to end per "MHLA: Restoring Expressivity of Linear Attention via Token-Level Multi-Head",

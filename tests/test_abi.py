@@ -249,6 +249,33 @@ def test_forward_argument_errors_before_launch():
     p.close()
 
 
+def test_intermediates_argument_errors_before_launch():
+    """mhla_forward_intermediates validates before any launch: NULL or unpaired outputs,
+    misalignment, a mixed stack that the plan does not keep (its mixing runs in the readout), the
+    workspace."""
+    lib = _lib_or_skip()
+    p = T.Plan(grid=(4096,), block=(64,), batch=1, heads=2, head_dim=64)    # M = 64: a mixing kernel
+    pf = T.Plan(grid=(32, 32), block=(8, 8), batch=1, heads=2, head_dim=64)  # M = 16: mixed in the readout
+    assert p.info.n_kernels == 3 and pf.info.n_kernels == 2
+    K, V, MC, S, Z, ST, ZT, W = (0x10000 * i for i in range(1, 9))
+    W = 0x1000000
+    f = lambda h, *a: lib.mhla_forward_intermediates(h.handle, *a)  # noqa: E731
+    ws = p.workspace_bytes
+    assert f(p, None, V, MC, S, Z, ST, ZT, W, ws, None) == 1          # NULL k
+    assert f(p, K, V, MC, None, Z, ST, ZT, W, ws, None) == 1          # NULL S
+    assert f(p, K, V, MC, S, Z, ST, None, W, ws, None) == 1           # St without zt
+    assert f(p, K, V, None, S, Z, ST, ZT, W, ws, None) == 1           # NULL M_c with M > 1
+    assert f(p, K + 2, V, MC, S, Z, ST, ZT, W, ws, None) == 1         # misaligned k
+    assert f(p, K, V, MC, S + 2, Z, ST, ZT, W, ws, None) == 1         # misaligned S
+    assert f(p, K, V, MC, S, Z, ST, ZT, None, ws, None) == 4          # no workspace
+    assert f(p, K, V, MC, S, Z, ST, ZT, W, ws - 1, None) == 4         # workspace too small
+    assert f(p, K, V, MC, S, Z, ST, ZT, W + 16, ws, None) == 4        # workspace misaligned
+    assert f(pf, K, V, MC, S, Z, ST, ZT, W, pf.workspace_bytes, None) == 2   # no mixed stack kept
+    assert lib.mhla_forward_intermediates(None, K, V, MC, S, Z, ST, ZT, W, ws, None) == 1
+    p.close()
+    pf.close()
+
+
 def test_backward_support_and_workspace():
     _lib_or_skip()
     p = T.Plan(grid=(64, 64), block=(16, 16), batch=16, heads=8, head_dim=64)

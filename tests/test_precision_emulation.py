@@ -26,7 +26,7 @@ def mhla_case():
 
 def test_mc_rounding_dominates_the_bf16_path(mhla_case):
     """Rounding M_c to one bf16 costs more than any other single rounding of the bf16 path (the
-    mixing averages summaries of both signs, so a 2^-9 relative error of every weight does not
+    mixing averages summaries of both signs, so a relative error of up to 2^-8 in every weight does not
     average away): the mixing kernel takes M_c as bf16 hi + lo."""
     q, k, v, mc, n_b, ref = mhla_case
     single = {name: rel(mhla_1d(q, k, v, mc, n_b, **{name: True}), ref)
@@ -43,7 +43,7 @@ def test_mc_rounding_dominates_the_bf16_path(mhla_case):
 
 def test_bf16_output_rounding_floor(mhla_case):
     """The bf16 output's own rounding, relative to RMS(o), on this head: what is left of the
-    2e-2 bar for the kernel is 2e-2 minus this floor (about 2^-9 * max|o| / RMS(o))."""
+    2e-2 bar for the kernel is 2e-2 minus this floor (up to 2^-8 * max|o| / RMS(o))."""
     q, k, v, mc, n_b, ref = mhla_case
     floor = rel(synth.round_to_bf16(ref.astype(np.float32)).astype(np.float64), ref)
     peak = float(np.max(np.abs(ref)) / np.sqrt(np.mean(ref ** 2)))
@@ -105,7 +105,7 @@ def causal_case():
 def test_causal_scores_stay_split(causal_case):
     """The bf16-input causal slice kernel: single bf16 phi(q) and m_ii phi(K) keep the causal
     readout well inside its 2e-2 bar; rounding P (the weights of V) to one bf16 does not -- the
-    weighted sums of V cancel, so the weights' 2^-9 error grows with the keys in view -- and P
+    weighted sums of V cancel, so the weights' error of up to 2^-8 grows with the keys in view -- and P
     therefore stays split (hi + lo)."""
     q, k, v, mc, n_b, ref = causal_case
     kernel = causal_rel(causal_1d(q, k, v, mc, n_b, q_single=True, k_single=True, p_mode="split", stack=True), ref)

@@ -22,7 +22,7 @@ __all__ = [
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
     "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
-    "MHLA_NOALLOC_SCRATCH_BYTES", "MHLA_ERR_SCRATCH_LIMIT", "make_desc", "Plan", "EXPORTED_SYMBOLS",
+    "mhla_forward_intermediates", "MHLA_NOALLOC_SCRATCH_BYTES", "MHLA_ERR_SCRATCH_LIMIT", "make_desc", "Plan", "EXPORTED_SYMBOLS",
 ]
 
 MHLA_OK = 0
@@ -47,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
     "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
+    "mhla_forward_intermediates",
 )
 
 
@@ -120,6 +121,7 @@ def load_library() -> ctypes.CDLL:
     lib.mhla_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_forward.argtypes = [P, P, P, P, P, P, P, SZ, P]
     lib.mhla_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
+    lib.mhla_forward_intermediates.argtypes = [P, P, P, P, P, P, P, P, P, SZ, P]
     lib.mhla_backward_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.mhla_destroy.argtypes = [P]
@@ -177,6 +179,15 @@ def mhla_forward_noalloc(h, q: int, k: int, v: int, mc: int, o: int, stream: int
     """mhla_forward with the library's own scratch array as workspace (no allocation); pointers are
     integer device addresses (0 for NULL), ``stream`` a raw hipStream_t."""
     _check(load_library().mhla_forward_noalloc(h, q, k, v, mc or None, o, stream or None), "mhla_forward_noalloc")
+
+
+def mhla_forward_intermediates(h, k: int, v: int, mc: int, S: int, z: int, St: int, zt: int, workspace: int,
+                               workspace_bytes: int, stream: int) -> None:
+    """The summaries and mixed summaries in fp32 (St = zt = 0 to stop after the summaries);
+    pointers are integer device addresses (0 for NULL), ``stream`` a raw hipStream_t."""
+    _check(load_library().mhla_forward_intermediates(h, k, v, mc or None, S, z, St or None, zt or None,
+                                                     workspace or None, workspace_bytes, stream or None),
+           "mhla_forward_intermediates")
 
 
 def mhla_backward_workspace_size(h) -> int:
@@ -305,7 +316,7 @@ class Plan:
         mc = (int(kw["heads"]), m, m) if kw.get("mc_per_head") else (m, m)
         return qkv, mc
 
-    def check_args(self, q, k, v, mc, o, workspace, ws_bytes=None):
+    def check_args(self, q, k, v, mc, o, workspace, ws_bytes=None, check_o=True):
         """Host-side checks that every buffer has the shape, dtype and layout the kernels
         index; the C ABI receives bare pointers and cannot see them."""
         import torch
@@ -313,7 +324,8 @@ class Plan:
         qkv, mc_shape = self.expected_shapes()
         tin = torch.bfloat16 if self.desc_kwargs.get("in_dtype", "bf16") == "bf16" else torch.float32
         tout = torch.bfloat16 if self.desc_kwargs.get("out_dtype", "fp32") == "bf16" else torch.float32
-        for name, t, dt in (("q", q, tin), ("k", k, tin), ("v", v, tin), ("o", o, tout)):
+        checks = (("q", q, tin), ("k", k, tin), ("v", v, tin)) + ((("o", o, tout),) if check_o else ())
+        for name, t, dt in checks:
             if tuple(t.shape) != qkv or t.dtype != dt or not t.is_contiguous() or not t.is_cuda:
                 raise ValueError(f"{name}: expected contiguous {dt} cuda tensor of shape {qkv}, "
                                  f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
@@ -395,6 +407,25 @@ class Plan:
         mhla_decode_step(self.handle, state.data_ptr(), state.numel() * state.element_size(), int(t), q.data_ptr(), k.data_ptr(),
                          v.data_ptr(), mc.data_ptr() if mc is not None else 0, o.data_ptr(), stream.cuda_stream)
         return o
+
+    def intermediates(self, k, v, mc, workspace, mixed=True, stream=None):
+        """The forward's summaries (S [B*H, M, d, d], z [B*H, M, d]) and, with ``mixed``, its mixed
+        summaries (St, zt), as fp32 tensors; ``mixed`` needs a plan with a mixing kernel."""
+        import torch
+        self.check_args(k, k, v, mc, torch.empty(0), workspace, check_o=False)
+        if stream is None:
+            stream = torch.cuda.current_stream(k.device)
+        kw = self.desc_kwargs
+        rows, m, d = int(kw["batch"]) * int(kw["heads"]), int(self.info.n_blocks), int(kw["head_dim"])
+        S = torch.empty((rows, m, d, d), dtype=torch.float32, device=k.device)
+        z = torch.empty((rows, m, d), dtype=torch.float32, device=k.device)
+        St = torch.empty_like(S) if mixed else None
+        zt = torch.empty_like(z) if mixed else None
+        mhla_forward_intermediates(self.handle, k.data_ptr(), v.data_ptr(), mc.data_ptr() if mc is not None else 0,
+                                   S.data_ptr(), z.data_ptr(), St.data_ptr() if mixed else 0,
+                                   zt.data_ptr() if mixed else 0, workspace.data_ptr(), workspace.numel(),
+                                   stream.cuda_stream)
+        return (S, z, St, zt) if mixed else (S, z)
 
     def forward(self, q, k, v, mc, o, workspace, stream=None):
         import torch

@@ -22,7 +22,7 @@ PEAK_SOURCE = "peak_probe.hip"
 PEAK_LIB = os.path.join(PKG, "libmhla_peak.so")
 
 SOURCES = ["summary.hip", "summary_dma.hip", "mix.hip", "mix_mfma.hip", "readout.hip", "bwd.hip", "causal.hip", "causal_slice.hip", "decode.hip",
-           "mhla_host.cpp", "noalloc.hip"]
+           "mhla_host.cpp", "noalloc.hip", "stacks.hip"]
 
 
 def hipcc() -> str:

@@ -37,8 +37,8 @@
 // SPLIT (the plan's split accuracy) takes every product on hi / lo operand pairs.  Otherwise
 // phi(q) and m_ii phi(K) are single bf16 operands, the precision at which the non-causal forward
 // reads out bf16 ELU+1 inputs (scores and the readout of S0 on one MFMA each); P stays split in
-// both: the weighted sums of V cancel (V has both signs), so a 2^-9 rounding of the weights
-// grows with the number of keys and alone would exceed the causal readout's bar.
+// both: the weighted sums of V cancel (V has both signs), so a rounding of the weights by up to
+// 2^-8 relative grows with the number of keys and alone would exceed the causal readout's bar.
 #include <type_traits>
 
 #include "frag_lds.hpp"

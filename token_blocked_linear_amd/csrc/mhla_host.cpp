@@ -31,6 +31,9 @@ hipError_t launch_decode_zero(float* x, int64_t n, hipStream_t s);
 hipError_t launch_causal(const CausalParams& p, int d, bool in_fp32, bool out_fp32, int phi, int n_units,
                          hipStream_t stream);
 hipError_t launch_slice_prefix(float* ps, float* pz, int64_t rows, int splits, int frag, int d, hipStream_t stream);
+hipError_t launch_frag_to_rowmajor(const uint16_t* hi, const uint16_t* lo, const float* part, int splits,
+                                   int64_t rows, int d, int frag, float* out, hipStream_t stream);
+hipError_t launch_sum_splits(const float* part, int splits, int64_t rows, int d, float* out, hipStream_t stream);
 }  // namespace mhla
 
 namespace {
@@ -311,7 +314,7 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   // covers every row of a column tile and has the whole tile in LDS before its first store, so
   // the mixed stack needs no space of its own (and the stack traffic of a step touches half as
   // many bytes, which then stay in the infinity cache between the three kernels).
-  // The bf16 stack's mixing takes M_c as hi + lo: one bf16 M_c perturbs each weight by up to 2^-9
+  // The bf16 stack's mixing takes M_c as hi + lo: one bf16 M_c perturbs each weight by up to 2^-8
   // relative, the largest rounding of the bf16 path (M_c enters the fused prologue in fp32).
   P->mix_wlo = kMixMcSplit && mix_kernel && P->mix_mfma;
   P->mix_in_place =
@@ -390,6 +393,177 @@ mhla_status mhla_plan_get_info(mhla_handle h, mhla_plan_info* info) {
   return MHLA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The forward's launches on stream s.  With `im`, the run stops after the mixing step (or after
+// the summaries when im->St is NULL) and leaves those steps' results in im's fp32 layouts.
+struct Intermediates {
+  float* S;
+  float* z;
+  float* St;
+  float* zt;
+};
+mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void* v, const float* mc, void* o,
+                        void* workspace, hipStream_t s, const Intermediates* im) {
+  char* ws = static_cast<char*>(workspace);
+  float* ps = reinterpret_cast<float*>(ws + h->off_ps);
+  float* pz = reinterpret_cast<float*>(ws + h->off_pz);
+  float* pu = h->mala ? reinterpret_cast<float*>(ws + h->off_pu) : nullptr;
+  uint16_t* st_hi = reinterpret_cast<uint16_t*>(ws + h->off_st_hi);
+  uint16_t* st_lo = h->split ? reinterpret_cast<uint16_t*>(ws + h->off_st_lo) : nullptr;
+  float* zt = reinterpret_cast<float*>(ws + h->off_zt);
+  TimedLaunch* tl = nullptr;
+  int ev_i = 0;
+  if (h->timing && !timer_begin(h->fwd_timer, s, tl)) return MHLA_ERR_HIP;
+  auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[++ev_i], s) == hipSuccess; };
+
+  const bool mix_kernel = h->mix_kernel;
+  const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
+
+  mhla::SummaryParams sp = {};
+  sp.k = k;
+  sp.v = v;
+  sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
+  sp.ps = ps;
+  sp.pz = pz;
+  sp.pu = pu;
+  sp.g = h->geom;
+  sp.splits = h->sum_splits;
+  sp.tok_per_split = h->sum_tok;
+  sp.mc = mc;
+  sp.mc_head_stride = mc_stride;
+  sp.mcf = (mix_kernel && (h->mix_mfma || h->mix_split)) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
+  sp.mcf_lo = (h->mix_split || h->mix_wlo) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf_lo) : nullptr;
+  sp.mcf_transposed = 0;
+  sp.mcf_causal = h->causal ? 1 : 0;
+  sp.mcf_heads = h->mcf_heads;
+  sp.mcf_nitp = h->mix.nitp;
+  sp.mcf_nbc = h->mix.nbc;
+  hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
+                                      h->mix_mfma, (int)h->desc.phi, (int)(h->sum_splits * h->M * h->BH), s);
+  if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+  if (im) {   // the block summaries, before a mixing in place overwrites them
+    const int64_t rows = h->BH * h->M;
+    e = h->mix_mfma ? mhla::launch_frag_to_rowmajor(sp.sb, nullptr, nullptr, 1, rows, h->d, h->frag, im->S, s)
+                    : mhla::launch_frag_to_rowmajor(nullptr, nullptr, ps, h->sum_splits, rows, h->d, h->frag, im->S, s);
+    if (e == hipSuccess) e = mhla::launch_sum_splits(pz, h->sum_splits, rows, h->d, im->z, s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+    if (!im->St) return MHLA_OK;
+  }
+
+  if (mix_kernel) {
+    if (h->mix_mfma || h->mix_split) {
+      mhla::MixMfmaParams mm = {};
+      mm.x = sp.sb;
+      mm.xf = ps;
+      mm.xsplits = h->sum_splits;
+      mm.z = pz;
+      mm.zsplits = h->mix_split ? h->sum_splits : 1;
+      mm.mcf = reinterpret_cast<const uint16_t*>(ws + h->off_mcf);
+      mm.mcf_lo = reinterpret_cast<const uint16_t*>(ws + h->off_mcf_lo);
+      mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
+      mm.y = st_hi;
+      mm.y_lo = reinterpret_cast<uint16_t*>(ws + h->off_st_lo);
+      mm.zt = zt;
+      mm.M = (int32_t)h->M;
+      mm.H = (int32_t)h->H;
+      mm.D = h->d;
+      mm.frag = h->frag;
+      e = mhla::launch_mix_mfma(mm, (int)h->BH, h->mix_split, h->mix_wlo, s);
+    } else {
+      mhla::MixParams mp;
+      mp.ps = ps;
+      mp.pz = pz;
+      mp.pu = pu;
+      mp.mc = mc;          // NULL only when M == 1: the kernel then uses the weight 1
+      mp.mc_head_stride = mc_stride;
+      mp.st_hi = st_hi;
+      mp.st_lo = st_lo;
+      mp.zt = zt;
+      mp.M = (int32_t)h->M;
+      mp.splits = h->sum_splits;
+      mp.H = (int32_t)h->H;
+      mp.N = (int32_t)h->N;
+      mp.zsplits = h->sum_splits;
+      mp.mc_transposed = 0;
+      mp.causal = h->causal ? 1 : 0;
+      e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->split, s);
+    }
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+  }
+  if (im) {   // the mixed summaries (hi + lo when the mixing leaves low parts)
+    const int64_t rows = h->BH * h->M;
+    const bool lo = h->split || h->mix_split;
+    e = mhla::launch_frag_to_rowmajor(st_hi, lo ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo) : nullptr,
+                                      nullptr, 1, rows, h->d, h->frag, im->St, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(im->zt, zt, (size_t)rows * h->d * 4, hipMemcpyDeviceToDevice, s);
+    return e == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+  }
+
+  if (h->causal) {
+    const int64_t rows = h->BH * h->M;
+    if (h->sum_splits > 1) {   // partials -> exclusive prefix over the block's token slices
+      e = mhla::launch_slice_prefix(ps, pz, rows, h->sum_splits, h->frag, h->d, s);
+      if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+    }
+    mhla::CausalParams cp = {};
+    cp.q = q;
+    cp.k = k;
+    cp.v = v;
+    cp.o = o;
+    cp.st_hi = mix_kernel ? st_hi : nullptr;
+    cp.st_lo = mix_kernel && (h->split || h->mix_split) ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo)
+                                                       : nullptr;   // bf16 mixing: no low parts
+    cp.zt = mix_kernel ? zt : nullptr;
+    cp.pre = h->sum_splits > 1 ? ps : nullptr;
+    cp.prez = h->sum_splits > 1 ? pz : nullptr;
+    cp.mc = mc;
+    cp.mc_head_stride = mc_stride;
+    cp.H = (int32_t)h->H;
+    cp.g = h->geom;
+    cp.splits = h->rd_splits;
+    cp.tok_per_split = h->rd_tok;
+    cp.BH = (int32_t)h->BH;
+    cp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
+    cp.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
+    cp.split = h->split ? 1 : 0;
+    e = mhla::launch_causal(cp, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
+                            (int)(h->rd_splits * h->M * h->BH), s);
+    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+    return MHLA_OK;
+  }
+
+  mhla::ReadoutParams rp;
+  rp.q = q;
+  rp.o = o;
+  rp.st_hi = st_hi;
+  rp.st_lo = st_lo;
+  rp.zt = zt;
+  rp.g = h->geom;
+  rp.splits = h->rd_splits;
+  rp.tok_per_split = h->rd_tok;
+  rp.BH = (int32_t)h->BH;
+  rp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
+  rp.sb = sp.sb;
+  rp.ps = ps;
+  rp.pz = pz;
+  rp.pu = pu;
+  rp.mc = mc;
+  rp.mc_head_stride = mc_stride;
+  rp.H = (int32_t)h->H;
+  rp.ssplits = h->sum_splits;
+  e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse, h->q_stream,
+                           (int)h->desc.phi, (int)(h->rd_splits * h->M * h->BH), s);
+  if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
+  return MHLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void* v,
                          const float* mc, void* o, void* workspace, size_t workspace_bytes,
                          void* stream) {
@@ -402,142 +576,29 @@ mhla_status mhla_forward(mhla_handle h, const void* q, const void* k, const void
   if (!workspace || workspace_bytes < h->ws_bytes) return MHLA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
   try {
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
-    float* ps = reinterpret_cast<float*>(ws + h->off_ps);
-    float* pz = reinterpret_cast<float*>(ws + h->off_pz);
-    float* pu = h->mala ? reinterpret_cast<float*>(ws + h->off_pu) : nullptr;
-    uint16_t* st_hi = reinterpret_cast<uint16_t*>(ws + h->off_st_hi);
-    uint16_t* st_lo = h->split ? reinterpret_cast<uint16_t*>(ws + h->off_st_lo) : nullptr;
-    float* zt = reinterpret_cast<float*>(ws + h->off_zt);
-    TimedLaunch* tl = nullptr;
-    int ev_i = 0;
-    if (h->timing && !timer_begin(h->fwd_timer, s, tl)) return MHLA_ERR_HIP;
-    auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[++ev_i], s) == hipSuccess; };
+    return forward_run(h, q, k, v, mc, o, workspace, reinterpret_cast<hipStream_t>(stream), nullptr);
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
 
-    const bool mix_kernel = h->mix_kernel;
-    const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
-
-    mhla::SummaryParams sp = {};
-    sp.k = k;
-    sp.v = v;
-    sp.sb = reinterpret_cast<uint16_t*>(ws + h->off_sb);
-    sp.ps = ps;
-    sp.pz = pz;
-    sp.pu = pu;
-    sp.g = h->geom;
-    sp.splits = h->sum_splits;
-    sp.tok_per_split = h->sum_tok;
-    sp.mc = mc;
-    sp.mc_head_stride = mc_stride;
-    sp.mcf = (mix_kernel && (h->mix_mfma || h->mix_split)) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf) : nullptr;
-    sp.mcf_lo = (h->mix_split || h->mix_wlo) ? reinterpret_cast<uint16_t*>(ws + h->off_mcf_lo) : nullptr;
-    sp.mcf_transposed = 0;
-    sp.mcf_causal = h->causal ? 1 : 0;
-    sp.mcf_heads = h->mcf_heads;
-    sp.mcf_nitp = h->mix.nitp;
-    sp.mcf_nbc = h->mix.nbc;
-    hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, h->split, h->split_v, h->mala,
-                                        h->mix_mfma, (int)h->desc.phi, (int)(h->sum_splits * h->M * h->BH), s);
-    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
-
-    if (mix_kernel) {
-      if (h->mix_mfma || h->mix_split) {
-        mhla::MixMfmaParams mm = {};
-        mm.x = sp.sb;
-        mm.xf = ps;
-        mm.xsplits = h->sum_splits;
-        mm.z = pz;
-        mm.zsplits = h->mix_split ? h->sum_splits : 1;
-        mm.mcf = reinterpret_cast<const uint16_t*>(ws + h->off_mcf);
-        mm.mcf_lo = reinterpret_cast<const uint16_t*>(ws + h->off_mcf_lo);
-        mm.mcf_per_head = h->desc.mc_per_head ? 1 : 0;
-        mm.y = st_hi;
-        mm.y_lo = reinterpret_cast<uint16_t*>(ws + h->off_st_lo);
-        mm.zt = zt;
-        mm.M = (int32_t)h->M;
-        mm.H = (int32_t)h->H;
-        mm.D = h->d;
-        mm.frag = h->frag;
-        e = mhla::launch_mix_mfma(mm, (int)h->BH, h->mix_split, h->mix_wlo, s);
-      } else {
-        mhla::MixParams mp;
-        mp.ps = ps;
-        mp.pz = pz;
-        mp.pu = pu;
-        mp.mc = mc;          // NULL only when M == 1: the kernel then uses the weight 1
-        mp.mc_head_stride = mc_stride;
-        mp.st_hi = st_hi;
-        mp.st_lo = st_lo;
-        mp.zt = zt;
-        mp.M = (int32_t)h->M;
-        mp.splits = h->sum_splits;
-        mp.H = (int32_t)h->H;
-        mp.N = (int32_t)h->N;
-        mp.zsplits = h->sum_splits;
-        mp.mc_transposed = 0;
-        mp.causal = h->causal ? 1 : 0;
-        e = mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, h->split, s);
-      }
-      if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
-    }
-
-    if (h->causal) {
-      const int64_t rows = h->BH * h->M;
-      if (h->sum_splits > 1) {   // partials -> exclusive prefix over the block's token slices
-        e = mhla::launch_slice_prefix(ps, pz, rows, h->sum_splits, h->frag, h->d, s);
-        if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
-      }
-      mhla::CausalParams cp = {};
-      cp.q = q;
-      cp.k = k;
-      cp.v = v;
-      cp.o = o;
-      cp.st_hi = mix_kernel ? st_hi : nullptr;
-      cp.st_lo = mix_kernel && (h->split || h->mix_split) ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo)
-                                                         : nullptr;   // bf16 mixing: no low parts
-      cp.zt = mix_kernel ? zt : nullptr;
-      cp.pre = h->sum_splits > 1 ? ps : nullptr;
-      cp.prez = h->sum_splits > 1 ? pz : nullptr;
-      cp.mc = mc;
-      cp.mc_head_stride = mc_stride;
-      cp.H = (int32_t)h->H;
-      cp.g = h->geom;
-      cp.splits = h->rd_splits;
-      cp.tok_per_split = h->rd_tok;
-      cp.BH = (int32_t)h->BH;
-      cp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
-      cp.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
-      cp.split = h->split ? 1 : 0;
-      e = mhla::launch_causal(cp, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
-                              (int)(h->rd_splits * h->M * h->BH), s);
-      if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
-      return MHLA_OK;
-    }
-
-    mhla::ReadoutParams rp;
-    rp.q = q;
-    rp.o = o;
-    rp.st_hi = st_hi;
-    rp.st_lo = st_lo;
-    rp.zt = zt;
-    rp.g = h->geom;
-    rp.splits = h->rd_splits;
-    rp.tok_per_split = h->rd_tok;
-    rp.BH = (int32_t)h->BH;
-    rp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
-    rp.sb = sp.sb;
-    rp.ps = ps;
-    rp.pz = pz;
-    rp.pu = pu;
-    rp.mc = mc;
-    rp.mc_head_stride = mc_stride;
-    rp.H = (int32_t)h->H;
-    rp.ssplits = h->sum_splits;
-    e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse, h->q_stream,
-                             (int)h->desc.phi, (int)(h->rd_splits * h->M * h->BH), s);
-    if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
-    return MHLA_OK;
+mhla_status mhla_forward_intermediates(mhla_handle h, const void* k, const void* v, const float* mc, float* S,
+                                       float* z, float* St, float* zt, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!h || !k || !v || !S || !z || (!St) != (!zt)) return MHLA_ERR_INVALID_ARG;
+  if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || (mc && !aligned(mc, 4))) return MHLA_ERR_INVALID_ARG;
+  if (!aligned(S, 4) || !aligned(z, 4) || (St && (!aligned(St, 4) || !aligned(zt, 4)))) return MHLA_ERR_INVALID_ARG;
+  if (St && !h->mix_kernel) return MHLA_ERR_UNSUPPORTED;   // mixed inside the readout: no mixed stack
+  if (!workspace || workspace_bytes < h->ws_bytes) return MHLA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
+  try {
+    const Intermediates im = {S, z, St, zt};
+    const bool timing = h->timing;
+    h->timing = false;   // these launches are not a forward: the per-kernel timers skip them
+    const mhla_status st = forward_run(h, nullptr, k, v, mc, nullptr, workspace, reinterpret_cast<hipStream_t>(stream), &im);
+    h->timing = timing;
+    return st;
   } catch (...) {
     return MHLA_ERR_INTERNAL;
   }

@@ -23,7 +23,7 @@
 // Two precisions:
 //   SPLIT = false  bf16 stack (one token slice per block): the bf16 forward.  With WLO, W enters
 //                  as bf16 hi + lo (two MFMAs per product, W to about 2^-17): rounding M_c to one
-//                  bf16 would perturb every mixing weight by up to 2^-9 relative, and since S~_i
+//                  bf16 would perturb every mixing weight by up to 2^-8 relative, and since S~_i
 //                  averages many summaries of both signs, that error does not average away
 //                  (it is the largest rounding of the bf16 path);
 //   SPLIT = true   fp32 partial summaries, summed over their token slices as they are loaded,
