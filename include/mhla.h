@@ -77,7 +77,7 @@ typedef enum { MHLA_PHI_ELU1 = 0, MHLA_PHI_RELU = 1, MHLA_PHI_EXP = 2 } mhla_phi
  * form is a reading): the token-expanded sum of Key design 2 masked to keys t' <= t, i.e. query t
  * of block i reads sum_{b<i} m_ib S_b plus m_ii times its own block's prefix up to t; entries of
  * M_c above the diagonal are not read.  1D grids and d >= 32 only (else MHLA_ERR_UNSUPPORTED);
- * always on split operands (the accuracy field is not consulted). */
+ * operand precision as the accuracy field says (see mhla_accuracy). */
 typedef enum {
   MHLA_READOUT_NORMALIZED = 0,    /* o = phi(q)^T S~_i / phi(q)^T z~_i                         */
   MHLA_READOUT_UNNORMALIZED = 1,  /* o = phi(q)^T S~_i                                        */
@@ -92,9 +92,11 @@ typedef enum {
                             /* near the 2e-2 bar with single bf16 operands)                      */
   MHLA_ACCURACY_BF16 = 1,   /* single bf16 MFMA operands, fp32 accumulation                     */
   MHLA_ACCURACY_SPLIT = 2   /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
-} mhla_accuracy;              /* The causal readouts: the field sets the summaries and the mixing */
-                              /* of the earlier blocks; the running in-block state and scores are */
-                              /* always split (single bf16 there leaves them above the 2e-2 bar). */
+} mhla_accuracy;              /* The causal readouts: the field sets the summaries, the mixing of */
+                              /* the earlier blocks and, for bf16 inputs, the in-slice scores and  */
+                              /* the start-state readout; the weights of V (P) are always split    */
+                              /* (one bf16 rounding there grows with the keys in view past the     */
+                              /* 2e-2 bar).  fp32 inputs keep the running state and scores split.  */
 
 typedef struct {
   uint32_t struct_size;     /* = sizeof(mhla_desc)                                             */
