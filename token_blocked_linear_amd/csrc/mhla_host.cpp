@@ -416,7 +416,8 @@ mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void*
   float* zt = reinterpret_cast<float*>(ws + h->off_zt);
   TimedLaunch* tl = nullptr;
   int ev_i = 0;
-  if (h->timing && !timer_begin(h->fwd_timer, s, tl)) return MHLA_ERR_HIP;
+  // (the intermediates' launches are not a forward: the per-kernel timers skip them)
+  if (!im && h->timing && !timer_begin(h->fwd_timer, s, tl)) return MHLA_ERR_HIP;
   auto mark = [&]() -> bool { return !tl || hipEventRecord(tl->ev[++ev_i], s) == hipSuccess; };
 
   const bool mix_kernel = h->mix_kernel;
@@ -594,11 +595,7 @@ mhla_status mhla_forward_intermediates(mhla_handle h, const void* k, const void*
   if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
   try {
     const Intermediates im = {S, z, St, zt};
-    const bool timing = h->timing;
-    h->timing = false;   // these launches are not a forward: the per-kernel timers skip them
-    const mhla_status st = forward_run(h, nullptr, k, v, mc, nullptr, workspace, reinterpret_cast<hipStream_t>(stream), &im);
-    h->timing = timing;
-    return st;
+    return forward_run(h, nullptr, k, v, mc, nullptr, workspace, reinterpret_cast<hipStream_t>(stream), &im);
   } catch (...) {
     return MHLA_ERR_INTERNAL;
   }
