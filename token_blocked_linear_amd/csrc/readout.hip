@@ -210,16 +210,19 @@ __device__ inline void rd_issue(const ReadoutParams& p, const RdUnit& u, int t, 
 // allow it at 4 waves per SIMD; one at d = 128 and for fp32 inputs.
 template <typename TIn, int D>
 constexpr int readout_tiles_per_step() { return sizeof(TIn) == 2 && D <= 64 ? MHLA_READOUT_TILES : 1; }
-// waves per SIMD the register allocation must allow (fp32 inputs at d = 128 need more registers)
-template <typename TIn, int D>
-constexpr int readout_waves() { return sizeof(TIn) == 4 && D == 128 ? 3 : 4; }
+// waves per SIMD the register allocation must allow (fp32 inputs at d = 128 need more registers;
+// the bf16 mixing prologue at d <= 64 is held to 8)
+template <typename TIn, int D, int FUSE = 0>
+constexpr int readout_waves() {
+  return FUSE == kFuseBf16 && sizeof(TIn) == 2 && D <= 64 ? 8 : (sizeof(TIn) == 4 && D == 128 ? 3 : 4);
+}
 
 // QPOL: cache policy of the query loads (MHLA_READOUT_LOAD_CPOL, or 2 = nt when the queries
 // of one launch are larger than about half the infinity cache and would only evict the
 // summaries from it).
 template <typename TIn, typename TOut, int D, bool SPLIT, int FUSE, int PHI, int QPOL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    readout_waves<TIn, D>()))) void readout_kernel(
+    readout_waves<TIn, D, FUSE>()))) void readout_kernel(
     ReadoutParams p, int mode) {
   using Dm = Dims<D>;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
@@ -266,7 +269,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
   const int M = g.M;
   // fragment chunks of 8 elements per thread; the prologues take PC of them per pass
   constexpr int PER = (FRAG + kThreads * 8 - 1) / (kThreads * 8);
-  constexpr int PC = PER < 2 ? PER : 2;
+  // (the mixing prologues take one: fewer loads in flight per thread leave registers for more
+  // waves, 8 per SIMD for the bf16 one at d <= 64, and more waves hide a unit's prologue behind
+  // the other units' query streams)
+  constexpr int PC = FUSE != kFuseNone ? 1 : (PER < 2 ? PER : 2);
   if constexpr (FUSE == kFuseNone) {
     // the mixing kernel's output: every chunk of this thread in flight at once
     const Rsrc rhi = make_rsrc(p.st_hi + U.row * FRAG, FRAG * 2u);
