@@ -14,25 +14,27 @@
 // block, slice of at most 256 tokens = 16 query tiles); wave w owns query tiles w and 15 - w, so
 // every wave meets 17 (query, key) tile pairs of a full slice.  Per unit:
 //   1. phi(q) of the wave's tiles, from LDS (loaded there for this unit by direct-to-LDS DMA while
-//      the previous unit was computed), becomes bf16 hi / lo MFMA B operands in registers; the
-//      wave then starts the DMA of its tiles of the next unit.
-//   2. The slice's keys go to LDS in phases of 128 (d = 128) or 256 keys: m_ii phi(K) as hi / lo
-//      rows and V (bf16, exact), both with 16-byte chunks XOR-swizzled by row so that the operand
-//      reads and the transposing reads are conflict-free.  The registers that fed a phase load
-//      the next one (or the next unit's first) meanwhile.  Per key tile kt <= t: scores
-//      D[j][t] = m_ii phi(k_j) . q~_t on 16x16x32 MFMAs (keys as A rows, split operands), masked
-//      to j <= t on the diagonal tile; a lane then holds keys 4g .. 4g+3 of query t, the B
-//      operand of V^T P as it stands.  Two key tiles form one 16x16x32 step of V^T P whose A
-//      operand (channel rows, keys 4g .. 4g+3 of each tile) is two ds_read_b64_tr_b16 of V.
+//      the previous unit was computed), becomes MFMA B operands in registers.  den0 = q~ . z0
+//      follows on a few MFMAs whose A operand (rows 4g: hi(z0), 4g + 1: lo(z0)) is built from a
+//      z0 row that the previous unit DMA'd into a per-wave slot of the V space; it seeds the
+//      normaliser sum.  The wave then starts the DMA of its tiles of the next unit.
+//   2. The slice's keys go to LDS in phases of 128 (d = 128) or 256 keys: m_ii phi(K) rows (hi /
+//      lo with split operands) and V (bf16, exact), both with 16-byte chunks XOR-swizzled by row
+//      so that the operand reads and the transposing reads are conflict-free.  The registers
+//      that fed a phase load the next one (or the next unit's first) meanwhile.  With two
+//      phases, phase ph takes the slice's 32-key pairs 2p + ph: every wave then has about the
+//      same number of active pairs in each phase, which the barrier between phases needs.  Per
+//      key tile kt <= t: scores D[j][t] = m_ii phi(k_j) . q~_t on 16x16x32 MFMAs (keys as A
+//      rows), masked to j <= t on the diagonal tile; a lane then holds keys 4g .. 4g+3 of query
+//      t, the B operand of V^T P as it stands.  Two key tiles form one 16x16x32 step of V^T P
+//      whose A operand (channel rows, keys 4g .. 4g+3 of each tile) is two ds_read_b64_tr_b16 of
+//      V.
 //   3. The readout against S0: O^T += S0^T q~ with permuted A rows (lane (t, g) ends with
-//      channels 8g .. 8g+7 of each 32-channel pair).  (den0 = q~ . z0 is taken at the unit's
-//      start, from a normaliser operand built in registers, rows 4g: hi(z0), 4g + 1: lo(z0), out
-//      of a z0 row that the previous unit DMA'd into a per-wave slot of the V space.)  An S0 that
-//      is a bf16 fragment stack read with single operands is DMA'd into the LDS space that the
-//      keys' low parts would take (unused then), in the readout kernel's bank-spreading order, at
-//      the unit's last phase;
-//      otherwise the A operands come straight from global memory (the unit's waves share them in
-//      L2) and are combined and split in registers.
+//      channels 8g .. 8g+7 of each 32-channel pair).  An S0 that is a bf16 fragment stack read
+//      with single operands is DMA'd into the LDS space that the keys' low parts would take
+//      (unused then), in the readout kernel's bank-spreading order, at the unit's last phase;
+//      otherwise the A operands come straight from global memory (the unit's waves share them
+//      in L2) and are combined and split in registers.
 //   4. o_t = num_t / den_t (normalised) or num_t, 16-byte stores.
 // SPLIT (the plan's split accuracy) takes every product on hi / lo operand pairs.  Otherwise
 // phi(q) and m_ii phi(K) are single bf16 operands, the precision at which the non-causal forward
