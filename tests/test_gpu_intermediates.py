@@ -157,6 +157,22 @@ def test_intermediates_per_head_mc():
     check(w.name, got, want, bound)
 
 
+def test_intermediates_long_sequence_full_size():
+    """The long-sequence workload at its full size and in the plan the benchmark times (B = 1,
+    16 heads, d = 128, 65536 tokens in 256 blocks): the stacks of heads 0, 7 and 15 against the
+    oracle, every element."""
+    w = synth.WORKLOADS["long1d"]
+    announce(f"intermediates long1d shape={w.qkv_shape}")
+    q, k, v, mc, _ = synth.make_inputs(w)
+    got, info = run_intermediates(w, k, v, mc)
+    assert info.n_kernels == 3 and info.n_blocks == 256
+    heads = (0, 7, 15)
+    sub = w.with_(name="long1d_heads", heads=len(heads))
+    kk, vv = k[:, list(heads)], v[:, list(heads)]
+    want, bound = oracle_stacks(sub, kk, vv, mc, _eps(info))
+    check("long1d", [g[list(heads)] for g in got], want, bound)
+
+
 @pytest.mark.parametrize("w", [
     synth.Workload("i_fused_m16", "bf16", 2, 2, 64, (32, 32), (8, 8), 120, "softmax_l1"),
     synth.Workload("i_mala", "bf16", 1, 2, 64, (700,), (700,), 121, "none", "mala"),
