@@ -32,6 +32,8 @@ through torch and a register-only loop of bf16 MFMAs.
 sequence's heads (B = 1, 16 heads, d = 128, blocks of 256) over all 65536 positions, and of a
 batch of 32 such sequences over 4096 positions: tokens/s by the wall clock (host launches
 included) and the mean kernel time from HIP events against the algorithmic bytes.
+`decode_prefill` times mhla_decode_prefill of the long sequence's 65536 positions in one call (the
+prompt a decode would start from), by HIP events.
 `backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the long1d
 inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
 
@@ -582,6 +584,43 @@ def run_decode(batch: int, heads: int, d: int, n: int, nb: int, seed: int, pool:
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def run_prefill(batch: int, heads: int, d: int, n: int, nb: int, seed: int, reps: int = 5):
+    """mhla_decode_prefill over positions 0 .. n-1 (one call: the chunkwise causal forward at split
+    accuracy plus the state's assembly), the median of `reps` calls timed by HIP events on the
+    launch stream after one untimed call; against n single decode steps this is what a prompt of n
+    positions costs before decoding continues."""
+    import torch
+    import token_blocked_linear_amd as T
+
+    w = synth.Workload("prefill", "bf16", batch, heads, d, (n,), (nb,), seed, "softmax_gauss", "causal",
+                       ragged=n % nb != 0)
+    plan = T.Plan(grid=w.grid, block=w.block, batch=batch, heads=heads, head_dim=d, in_dtype="bf16",
+                  out_dtype="bf16", readout="causal", ragged=w.ragged)
+    mc = synth.make_mc(w, np.random.default_rng(seed))
+    tmc = torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    shape = (batch, heads, n, d)
+    tq, tk, tv = (to_dev(synth.standard_normal_parallel(shape, seed + 1 + i, bf16=True), "bf16") for i in range(3))
+    o = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+    state = plan.alloc_decode_state()
+    ws = plan.alloc_prefill_workspace(n)
+    stream = torch.cuda.current_stream()
+    plan.decode_prefill(state, tq, tk, tv, tmc, o, ws, stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        plan.decode_prefill(state, tq, tk, tv, tmc, o, ws, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    plan.close()
+    ms = float(np.median(times))
+    return {"batch": batch, "heads": heads, "head_dim": d, "positions": n, "block_tokens": nb,
+            "ms": round(ms, 4), "tokens_per_s": round(batch * n / (ms * 1e-3), 1),
+            "protocol": f"median of {reps} calls by HIP events after one untimed call; bf16 inputs and outputs"}
+
+
 def blas_build() -> str:
     """The BLAS numpy is linked against, as threadpoolctl reports it."""
     try:
@@ -726,6 +765,8 @@ def main():
         # the long sequence's heads decoded one position at a time (B = 1), and a batch of 32
         # such sequences over their first 4096 positions
         decode = [run_decode(1, 16, 128, 65536, 256, 701), run_decode(32, 16, 128, 4096, 256, 702)]
+        progress("decode prefill")
+        prefill = run_prefill(1, 16, 128, 65536, 256, 703)
 
     bwd = None
     if not args.no_backward and w.readout != "mala":
@@ -775,6 +816,7 @@ def main():
         line["causal"] = causal
     if decode is not None:
         line["decode"] = decode
+        line["decode_prefill"] = prefill
     print(json.dumps(line), flush=True)
 
 

@@ -261,6 +261,28 @@ mhla_status mhla_decode_reset(mhla_handle h, void* state, size_t state_bytes, vo
 mhla_status mhla_decode_step(mhla_handle h, void* state, size_t state_bytes, int64_t t, const void* q,
                              const void* k, const void* v, const float* mc, void* o, void* stream);
 
+/* Prefill of the streaming decode: positions 0 .. n-1 (a prompt) of every (batch, head) in one call,
+ * through the chunkwise causal forward, leaving in `state` what n calls of mhla_decode_step at
+ * t = 0 .. n-1 would leave (the fp32 block summaries, the mixing of the completed blocks and the
+ * last block's running sums), so that decoding continues at t = n.  The state's earlier contents
+ * do not matter (no mhla_decode_reset is needed).
+ *   n           1 <= n <= N (N counting a CLS token)
+ *   q, k, v     device [B, H, n, d] of the plan's in_dtype (the prompt's positions)
+ *   mc          as for mhla_decode_step (the plan's M x M, or H x M x M)
+ *   o           device [B, H, n, d] of the plan's out_dtype: the outputs at positions 0 .. n-1
+ *   workspace   device, mhla_decode_prefill_workspace_size(h, n) bytes, 256-byte aligned, its
+ *               contents on entry irrelevant (0 bytes when n is a CLS token alone: one decode step)
+ * The prefix's summaries and mixing run at split accuracy whatever the plan's accuracy field
+ * (fp32-exact, as the decode state keeps them); its in-slice products follow the field, as in the
+ * causal forward.  Outputs must not alias the inputs, the state or the workspace.
+ * Errors: INVALID_ARG (NULL pointers, n out of range, mc NULL with M > 1, misalignment, aliasing),
+ * UNSUPPORTED (not a causal plan), WORKSPACE (state or workspace too small or misaligned), HIP.
+ * Asynchronous on `stream`. */
+mhla_status mhla_decode_prefill_workspace_size(mhla_handle h, int64_t n, size_t* bytes);
+mhla_status mhla_decode_prefill(mhla_handle h, void* state, size_t state_bytes, int64_t n, const void* q,
+                                const void* k, const void* v, const float* mc, void* o, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Release a plan.  NULL is accepted. */
 mhla_status mhla_destroy(mhla_handle h);
 

@@ -371,6 +371,44 @@ def test_decode_argument_errors_before_launch():
     p.close()
 
 
+def test_decode_prefill_sizes_and_argument_errors_before_launch():
+    """mhla_decode_prefill: its workspace grows with the prefix; validation rejects bad calls
+    before any launch (a launch here would give MHLA_ERR_HIP)."""
+    lib = _lib_or_skip()
+    p = T.Plan(grid=(1000,), block=(125,), batch=2, heads=2, head_dim=64, readout="causal")
+    pc = T.Plan(grid=(999,), block=(125,), batch=1, heads=1, head_dim=64, readout="causal", ragged=True,
+                cls_token=True)
+    sizes = [T.mhla_decode_prefill_workspace_size(p.handle, n) for n in (1, 125, 126, 1000)]
+    assert sizes[0] > 0 and sizes[0] == sizes[1] < sizes[2] < sizes[3]
+    assert T.mhla_decode_prefill_workspace_size(pc.handle, 1) == 0     # the CLS token alone: a decode step
+    assert T.mhla_decode_prefill_workspace_size(pc.handle, 2) > 0
+    for bad in (0, 1001):
+        with pytest.raises(T.MhlaError):
+            T.mhla_decode_prefill_workspace_size(p.handle, bad)
+    fwd = T.Plan(grid=(64, 64), block=(16, 16), batch=1, heads=1, head_dim=64)
+    with pytest.raises(T.MhlaError):                                     # not a causal plan
+        T.mhla_decode_prefill_workspace_size(fwd.handle, 10)
+    n_state = T.mhla_decode_state_size(p.handle)
+    S, Q, K, V, MC, O, W = 0x1000000, 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x2000000
+    ws = sizes[3]
+    f = lambda *a: lib.mhla_decode_prefill(p.handle, *a)  # noqa: E731
+    assert f(S, n_state, 0, Q, K, V, MC, O, W, ws, None) == 1          # n = 0
+    assert f(S, n_state, 1001, Q, K, V, MC, O, W, ws, None) == 1       # n past the capacity
+    assert f(S, n_state, 500, None, K, V, MC, O, W, ws, None) == 1     # NULL q
+    assert f(S, n_state, 500, Q, K, V, None, O, W, ws, None) == 1      # NULL M_c with M > 1
+    assert f(S, n_state, 500, Q, K, V, MC, K, W, ws, None) == 1        # o aliases k
+    assert f(S, n_state, 500, Q, K, V, MC, O, S, ws, None) == 1        # workspace is the state
+    assert f(S, n_state, 500, Q + 2, K, V, MC, O, W, ws, None) == 1    # misaligned q
+    assert f(S, n_state - 1, 500, Q, K, V, MC, O, W, ws, None) == 4    # state too small
+    assert f(S, n_state, 1000, Q, K, V, MC, O, W, sizes[2], None) == 4   # workspace too small
+    assert f(S, n_state, 500, Q, K, V, MC, O, None, ws, None) == 4     # no workspace
+    assert f(S, n_state, 500, Q, K, V, MC, O, W + 16, ws, None) == 4   # workspace misaligned
+    assert lib.mhla_decode_prefill(fwd.handle, S, n_state, 10, Q, K, V, MC, O, W, ws, None) == 2
+    assert lib.mhla_decode_prefill(None, S, n_state, 10, Q, K, V, MC, O, W, ws, None) == 1
+    for x in (p, pc, fwd):
+        x.close()
+
+
 def test_decode_binding_rejects_a_host_state():
     """The binding checks the state tensor before handing its pointer to the library."""
     import torch

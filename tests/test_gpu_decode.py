@@ -140,3 +140,55 @@ def test_decode_reset_and_resume():
     plan.close()
     assert np.array_equal(got, whole)
     assert causal_err(got, oracle_full(w, q, k, v, mc)) <= FP32_TOL
+
+
+PREFILL_CASES = [
+    # (workload, prefix lengths): a position inside the first block, a block's end, the next
+    # block's first position, mid-sequence, the whole sequence
+    (W("pf_d64_ragged", "bf16", 2, 2, 64, 600, 128, 621), (1, 100, 128, 129, 300, 600)),
+    # a CLS token: the CLS token alone (one decode step), then prefixes into the grid blocks
+    (W("pf_cls", "bf16", 2, 2, 64, 500, 128, 622, cls=True), (1, 2, 129, 300)),
+    (W("pf_d128_fp32", "fp32", 1, 1, 128, 384, 64, 623), (200,)),
+    (W("pf_unit_blocks", "fp32", 1, 2, 32, 96, 1, 624, "softmax_l1"), (50,)),
+    (W("pf_one_block", "bf16", 2, 2, 64, 300, 300, 625, "none"), (150,)),
+    # blocks over 256 tokens: the prefix's summaries come in several token slices
+    (W("pf_big_blocks", "bf16", 1, 2, 64, 1500, 600, 626), (1000,)),
+    (W("pf_unnorm_relu", "fp32", 1, 3, 32, 500, 96, 627, "softmax_l1", "causal_unnormalized", "relu"), (250,)),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: c[0].name)
+def test_decode_prefill_then_steps(case):
+    """mhla_decode_prefill over positions 0 .. n-1, then mhla_decode_step from t = n: the whole
+    sequence matches the causal oracle (both metrics) and the step-by-step decode, for a state
+    left dirty by an unrelated sequence before the prefill."""
+    import torch
+    w, prefixes = case
+    q, k, v, mc, rng = _inputs(w)
+    want = oracle_full(w, q, k, v, mc)
+    whole = decode_sequence(w, q, k, v, mc)
+    tol = FP32_TOL if w.dtype == "fp32" else BF16_TOL
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype="fp32", readout=w.readout, phi=w.phi, ragged=w.ragged,
+                  cls_token=w.cls)
+    state = plan.alloc_decode_state()
+    tmc = None if mc is None else torch.from_numpy(np.ascontiguousarray(mc, np.float32)).to("cuda:0")
+    for n in prefixes:
+        announce(f"prefill {w.name} n={n} of {w.n_tokens} shape={w.qkv_shape} block={w.block} {w.readout}")
+        junk = [rng.standard_normal(x.shape) for x in (q, k, v)]
+        decode_sequence(w, *junk, mc, plan=plan, state=state, t1=min(w.n_tokens, 70))
+        tq, tk, tv = (to_device(np.ascontiguousarray(x[:, :, :n]), w.dtype) for x in (q, k, v))
+        o_pre = torch.empty((w.batch, w.heads, n, w.head_dim), dtype=torch.float32, device="cuda:0")
+        ws = plan.alloc_prefill_workspace(n)
+        plan.decode_prefill(state, tq, tk, tv, tmc, o_pre, ws)
+        torch.cuda.synchronize()
+        parts = [o_pre.cpu().numpy().astype(np.float64)]
+        if n < w.n_tokens:
+            parts.append(decode_sequence(w, q, k, v, mc, plan=plan, state=state, t0=n))
+        got = np.concatenate(parts, axis=2)
+        err, plain, err_steps = causal_err(got, want), rel_err(got, want), causal_err(got, whole)
+        print(f"  n={n}: err={err:.3e} (max|d|/RMS {plain:.3e}) vs step-by-step decode {err_steps:.3e}")
+        record("decode_prefill", f"{w.name}_n{n}", r31=err, plain=plain, vs_steps_r31=err_steps, dtype=w.dtype)
+        assert np.all(np.isfinite(got))
+        assert err <= tol and plain <= tol and err_steps <= tol, (w.name, n, err, plain, err_steps)
+    plan.close()

@@ -22,7 +22,8 @@ __all__ = [
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
     "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
-    "mhla_forward_intermediates", "MHLA_NOALLOC_SCRATCH_BYTES", "MHLA_ERR_SCRATCH_LIMIT", "make_desc", "Plan", "EXPORTED_SYMBOLS",
+    "mhla_forward_intermediates", "mhla_decode_prefill_workspace_size", "mhla_decode_prefill",
+    "MHLA_NOALLOC_SCRATCH_BYTES", "MHLA_ERR_SCRATCH_LIMIT", "make_desc", "Plan", "EXPORTED_SYMBOLS",
 ]
 
 MHLA_OK = 0
@@ -47,7 +48,7 @@ EXPORTED_SYMBOLS = (
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
     "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
-    "mhla_forward_intermediates",
+    "mhla_forward_intermediates", "mhla_decode_prefill_workspace_size", "mhla_decode_prefill",
 )
 
 
@@ -136,6 +137,8 @@ def load_library() -> ctypes.CDLL:
     lib.mhla_decode_state_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_decode_reset.argtypes = [P, P, SZ, P]
     lib.mhla_decode_step.argtypes = [P, P, SZ, I64, P, P, P, P, P, P]
+    lib.mhla_decode_prefill_workspace_size.argtypes = [P, I64, ctypes.POINTER(SZ)]
+    lib.mhla_decode_prefill.argtypes = [P, P, SZ, I64, P, P, P, P, P, P, SZ, P]
     for name in EXPORTED_SYMBOLS:
         if name != "mhla_status_string":
             getattr(lib, name).restype = I32
@@ -218,6 +221,22 @@ def mhla_decode_step(h, state: int, state_bytes: int, t: int, q: int, k: int, v:
     """One token per (batch, head) at position ``t``; pointers are integer device addresses."""
     _check(load_library().mhla_decode_step(h, state, state_bytes, t, q, k, v, mc or None, o, stream or None),
            "mhla_decode_step")
+
+
+def mhla_decode_prefill_workspace_size(h, n: int) -> int:
+    b = ctypes.c_size_t()
+    _check(load_library().mhla_decode_prefill_workspace_size(h, int(n), ctypes.byref(b)),
+           "mhla_decode_prefill_workspace_size")
+    return b.value
+
+
+def mhla_decode_prefill(h, state: int, state_bytes: int, n: int, q: int, k: int, v: int, mc: int, o: int,
+                        workspace: int, workspace_bytes: int, stream: int) -> None:
+    """Positions 0 .. n-1 of every (batch, head) into the decode state; pointers are integer device
+    addresses (0 for NULL), ``stream`` a raw hipStream_t."""
+    _check(load_library().mhla_decode_prefill(h, state, state_bytes, int(n), q, k, v, mc or None, o,
+                                              workspace or None, workspace_bytes, stream or None),
+           "mhla_decode_prefill")
 
 
 def mhla_destroy(h) -> None:
@@ -406,6 +425,40 @@ class Plan:
             stream = torch.cuda.current_stream(q.device)
         mhla_decode_step(self.handle, state.data_ptr(), state.numel() * state.element_size(), int(t), q.data_ptr(), k.data_ptr(),
                          v.data_ptr(), mc.data_ptr() if mc is not None else 0, o.data_ptr(), stream.cuda_stream)
+        return o
+
+    def alloc_prefill_workspace(self, n, device="cuda"):
+        import torch
+        return torch.empty(max(mhla_decode_prefill_workspace_size(self.handle, int(n)), 256), dtype=torch.uint8,
+                           device=device)
+
+    def decode_prefill(self, state, q, k, v, mc, o, workspace, stream=None):
+        """Positions 0 .. n-1 of every (batch, head) in one call: q, k, v [B, H, n, d] of the plan's
+        in_dtype, o the same shape in its out_dtype (written); the state continues at t = n."""
+        import torch
+        kw = self.desc_kwargs
+        n = int(q.shape[2]) if q.dim() == 4 else -1
+        shape = (int(kw["batch"]), int(kw["heads"]), n, int(kw["head_dim"]))
+        tin = torch.bfloat16 if kw.get("in_dtype", "bf16") == "bf16" else torch.float32
+        tout = torch.bfloat16 if kw.get("out_dtype", "fp32") == "bf16" else torch.float32
+        for name, x, dt in (("q", q, tin), ("k", k, tin), ("v", v, tin), ("o", o, tout)):
+            if tuple(x.shape) != shape or x.dtype != dt or not x.is_contiguous() or not x.is_cuda:
+                raise ValueError(f"{name}: expected a contiguous {dt} cuda tensor of shape {shape}")
+        _, mc_shape = self.expected_shapes()
+        if mc is not None and (tuple(mc.shape) != mc_shape or mc.dtype != torch.float32
+                               or not mc.is_contiguous() or not mc.is_cuda):
+            raise ValueError(f"mc: expected contiguous float32 cuda tensor {mc_shape}")
+        self._check_decode_state(state)
+        need = mhla_decode_prefill_workspace_size(self.handle, n)
+        if need and (workspace is None or workspace.dtype != torch.uint8 or workspace.numel() < need
+                     or not workspace.is_cuda):
+            raise ValueError(f"workspace: expected >= {need} bytes of uint8 on the GPU")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        mhla_decode_prefill(self.handle, state.data_ptr(), state.numel() * state.element_size(), n, q.data_ptr(),
+                            k.data_ptr(), v.data_ptr(), mc.data_ptr() if mc is not None else 0, o.data_ptr(),
+                            workspace.data_ptr() if workspace is not None else 0,
+                            workspace.numel() if workspace is not None else 0, stream.cuda_stream)
         return o
 
     def intermediates(self, k, v, mc, workspace, mixed=True, stream=None):

@@ -185,6 +185,65 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(DecodeParams p) {
   }
 }
 
+// The state that decode_step_kernel leaves after positions 0 .. n-1, written at once from a
+// chunkwise causal forward over them.  With i = Mp - 1 the block of position n - 1: the completed
+// blocks b < i are kept (hS[b], hz[b]), S~<_i and z~<_i are row i of the strictly lower mixing,
+// and R, r are block i's sums over its positions up to n - 1 (its whole summary in the prefix:
+// the prefix's last block ends at n - 1).  Element (f, c) of a slice's matrix is feature f,
+// channel sl C + c, at f C + c; the summaries are read from their fragment layout (feature f:
+// chunk f / 32, lane group (f % 32) / 8, element f % 8; channel ch: tile ch / 16, lane ch % 16).
+__global__ __launch_bounds__(kThreads) void prefill_state_kernel(PrefillStateParams p, int D) {
+  const int C = 1 << p.log2_c, S = D >> p.log2_c, DC = D * C, NCT = D / 16, Mp = p.Mp;
+  const int64_t per_slice = (int64_t)(Mp + 1) * (DC + D);   // hS[0 .. Mp-2], St, R; hz[..], zt, r
+  const int64_t total = (int64_t)p.BH * S * per_slice;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t bs = idx / per_slice;
+    int64_t w = idx - bs * per_slice;
+    const int bh = (int)(bs / S), sl = (int)(bs % S);
+    float* slot = p.state + bs * ((int64_t)(p.M + 2) * (DC + D));
+    float* hS = slot;
+    float* hz = hS + (int64_t)p.M * DC;
+    float* St = hz + (int64_t)p.M * D;
+    float* zt = St + DC;
+    float* R = zt + D;
+    float* r = R + DC;
+    const int64_t last = (int64_t)bh * Mp + (Mp - 1);   // the prefix's row of block Mp - 1
+    if (w < (int64_t)(Mp + 1) * DC) {
+      const int m = (int)(w / DC), e = (int)(w % DC);     // m < Mp - 1: hS[m]; Mp - 1: St; Mp: R
+      const int f = e / C, ch = sl * C + e % C;
+      const int pos = (((f >> 5) * NCT + (ch >> 4)) * 64 + 16 * ((f & 31) >> 3) + (ch & 15)) * 8 + (f & 7);
+      float x = 0.f;
+      if (m == Mp - 1) {                                  // S~<_i: hi + lo of the mixing
+        if (p.st_hi) {
+          x = __uint_as_float((uint32_t)p.st_hi[last * p.frag + pos] << 16);
+          if (p.st_lo) x += __uint_as_float((uint32_t)p.st_lo[last * p.frag + pos] << 16);
+        }
+        St[e] = x;
+      } else {                                            // S_b: the sum of its slice partials
+        const int b = m < Mp - 1 ? m : Mp - 1;
+        const int64_t row = (int64_t)bh * Mp + b;
+        for (int s = 0; s < p.splits; ++s) x += p.part[(row * p.splits + s) * p.frag + pos];
+        if (m < Mp - 1) hS[(int64_t)m * DC + e] = x;
+        else R[e] = x;
+      }
+    } else {
+      w -= (int64_t)(Mp + 1) * DC;
+      const int m = (int)(w / D), f = (int)(w % D);
+      float x = 0.f;
+      if (m == Mp - 1) {
+        if (p.zt) x = p.zt[last * D + f];
+        zt[f] = x;
+      } else {
+        const int b = m < Mp - 1 ? m : Mp - 1;
+        const int64_t row = (int64_t)bh * Mp + b;
+        for (int s = 0; s < p.splits; ++s) x += p.pz[(row * p.splits + s) * D + f];
+        if (m < Mp - 1) hz[(int64_t)m * D + f] = x;
+        else r[f] = x;
+      }
+    }
+  }
+}
+
 // zeroes `n` floats (a plain fill: no memset node, so a captured graph replays it correctly)
 __global__ __launch_bounds__(kThreads) void decode_zero_kernel(float* x, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) x[i] = 0.f;
@@ -216,6 +275,15 @@ hipError_t launch_decode_step(const DecodeParams& p, int d, bool in_fp32, bool o
     case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill_state(const PrefillStateParams& p, int d, hipStream_t s) {
+  if (p.log2_c < 3 || (1 << p.log2_c) > d || p.Mp < 1 || p.Mp > p.M) return hipErrorInvalidValue;
+  const int64_t total = (int64_t)p.BH * (d >> p.log2_c) * (int64_t)(p.Mp + 1) * ((int64_t)d * (1 << p.log2_c) + d);
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(prefill_state_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_zero(float* x, int64_t n, hipStream_t s) {

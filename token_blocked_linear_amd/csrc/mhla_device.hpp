@@ -289,6 +289,19 @@ struct DecodeParams {
   int32_t cls;             // 1: position 0 is a CLS token, a block of its own; blocks of nb follow
 };
 
+// The decode state after positions 0 .. n-1, from a chunkwise causal forward over them: its
+// summaries (fp32 slice partials) and its mixing with the strictly lower M_c (hi + lo).
+struct PrefillStateParams {
+  float* state;            // the decode state (layout of decode_step_kernel)
+  const float* part;       // fp32 partials [BH][Mp][splits][FRAG] (fragment layout)
+  const float* pz;         // fp32 partials [BH][Mp][splits][D]
+  const uint16_t* st_hi;   // mixed summaries [BH][Mp][FRAG] (hi, lo); NULL when Mp == 1
+  const uint16_t* st_lo;
+  const float* zt;         // mixed normalisers [BH][Mp][D]; NULL when Mp == 1
+  int32_t splits, BH, Mp, M;   // Mp: blocks of the prefix (the last one holds position n - 1); M: the plan's
+  int32_t frag, log2_c;
+};
+
 // MFMA mixing of a bf16 summary stack: Y[i] = sum_b M_c[i][b] X[b] over fragment positions,
 // plus the fp32 normaliser mixing z~[i] = sum_b M_c[i][b] z[b].
 struct MixMfmaParams {

@@ -34,6 +34,7 @@ hipError_t launch_slice_prefix(float* ps, float* pz, int64_t rows, int splits, i
 hipError_t launch_frag_to_rowmajor(const uint16_t* hi, const uint16_t* lo, const float* part, int splits,
                                    int64_t rows, int d, int frag, float* out, hipStream_t stream);
 hipError_t launch_sum_splits(const float* part, int splits, int64_t rows, int d, float* out, hipStream_t stream);
+hipError_t launch_prefill_state(const PrefillStateParams& p, int d, hipStream_t s);
 }  // namespace mhla
 
 namespace {
@@ -83,6 +84,8 @@ struct mhla_plan {
   bool mix_split;  // mixing kernel on MFMA with split operands over fp32 partials
   bool mix_wlo;    // the bf16 mixing kernel takes M_c as bf16 hi + lo
   bool causal;     // chunkwise-causal readout (1D)
+  bool causal_split;  // the bf16-input causal kernel's own products on split operands (= split,
+                      // except in a decode prefill's plan, which keeps the decode plan's)
   bool mix_kernel; // a mixing kernel of its own is launched
   bool mix_in_place; // the mixing kernel overwrites the bf16 summary stack with the mixed one
   bool q_stream;     // the readout loads the queries with the non-temporal policy
@@ -242,6 +245,7 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   else
     P->split = P->mala || P->in_fp32 || d->phi != MHLA_PHI_ELU1;
   P->split_v = P->split && P->in_fp32;
+  P->causal_split = P->split;
 
   const int dk = P->d < 32 ? 32 : P->d;
   P->frag = (dk / 32) * (P->d / 16) * 512;
@@ -405,8 +409,15 @@ struct Intermediates {
   float* St;
   float* zt;
 };
+// With `pf` (a causal plan over a decode prefix), the decode state is written from the summaries
+// and the mixing before the slice scan reuses the partials, and the run goes on to the readout.
+struct PrefillHook {
+  float* state;
+  int64_t M;      // blocks of the decode plan
+  int log2_c;     // its channel-slice width
+};
 mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void* v, const float* mc, void* o,
-                        void* workspace, hipStream_t s, const Intermediates* im) {
+                        void* workspace, hipStream_t s, const Intermediates* im, const PrefillHook* pf = nullptr) {
   char* ws = static_cast<char*>(workspace);
   float* ps = reinterpret_cast<float*>(ws + h->off_ps);
   float* pz = reinterpret_cast<float*>(ws + h->off_pz);
@@ -503,6 +514,24 @@ mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void*
     return e == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
   }
 
+  if (pf) {   // (split accuracy: fp32 partials, and a mixing with low parts when there is one)
+    mhla::PrefillStateParams pp = {};
+    pp.state = pf->state;
+    pp.part = ps;
+    pp.pz = pz;
+    pp.st_hi = mix_kernel ? st_hi : nullptr;
+    pp.st_lo = mix_kernel ? reinterpret_cast<const uint16_t*>(ws + h->off_st_lo) : nullptr;
+    pp.zt = mix_kernel ? zt : nullptr;
+    pp.splits = h->sum_splits;
+    pp.BH = (int32_t)h->BH;
+    pp.Mp = (int32_t)h->M;
+    pp.M = (int32_t)pf->M;
+    pp.frag = h->frag;
+    pp.log2_c = pf->log2_c;
+    e = mhla::launch_prefill_state(pp, h->d, s);
+    if (e != hipSuccess) return MHLA_ERR_HIP;
+  }
+
   if (h->causal) {
     const int64_t rows = h->BH * h->M;
     if (h->sum_splits > 1) {   // partials -> exclusive prefix over the block's token slices
@@ -529,7 +558,7 @@ mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void*
     cp.BH = (int32_t)h->BH;
     cp.xcd_map = (h->BH % 8 == 0) ? 1 : 0;
     cp.normalized = h->mode == MHLA_READOUT_CAUSAL_NORMALIZED ? 1 : 0;
-    cp.split = h->split ? 1 : 0;
+    cp.split = h->causal_split ? 1 : 0;
     e = mhla::launch_causal(cp, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
                             (int)(h->rd_splits * h->M * h->BH), s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
@@ -959,6 +988,100 @@ mhla_status mhla_decode_step(mhla_handle h, void* state, size_t state_bytes, int
     const hipError_t e = mhla::launch_decode_step(p, h->d, h->in_fp32, h->out_fp32, (int)h->desc.phi,
                                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
+
+namespace {
+
+// A prefill's own plan: positions 0 .. n-1 of h's sequence as a causal plan (the last block cut
+// short where n ends inside it) whose summaries and mixing are at split accuracy, so that the
+// state it leaves is fp32-exact as a decode step's, and whose in-slice products are at the decode
+// plan's accuracy; its workspace, then a copy of the leading Mp x Mp part of M_c (per head if M_c
+// is).
+mhla_status prefill_plan(const mhla_plan* h, int64_t n, mhla_plan* sub, size_t* mc_off, size_t* total) {
+  mhla_desc d = h->desc;
+  d.grid[0] = n - h->geom.cls;
+  d.flags |= MHLA_FLAG_RAGGED_BLOCKS;
+  d.accuracy = MHLA_ACCURACY_SPLIT;
+  const mhla_status st = build_plan(&d, sub);
+  if (st != MHLA_OK) return st;
+  sub->causal_split = h->split;   // the outputs at the decode plan's own accuracy
+  const size_t heads = h->desc.mc_per_head ? (size_t)h->H : 1;
+  *mc_off = sub->ws_bytes;
+  *total = align256(sub->ws_bytes + heads * (size_t)sub->M * (size_t)sub->M * 4);
+  return MHLA_OK;
+}
+
+bool prefill_supported(const mhla_plan* h, int64_t n) {
+  // a prefix of at least one grid token (a prefix of the CLS token alone is one decode step)
+  return h->causal && n - h->geom.cls >= 1 && n <= h->N;
+}
+
+}  // namespace
+
+mhla_status mhla_decode_prefill_workspace_size(mhla_handle h, int64_t n, size_t* bytes) {
+  if (!h || !bytes) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = decode_supported(h);
+  if (st != MHLA_OK) return st;
+  if (n < 1 || n > h->N) return MHLA_ERR_INVALID_ARG;
+  if (!prefill_supported(h, n)) {
+    *bytes = 0;
+    return MHLA_OK;
+  }
+  try {
+    mhla_plan sub;
+    size_t mc_off = 0, total = 0;
+    const mhla_status s2 = prefill_plan(h, n, &sub, &mc_off, &total);
+    if (s2 != MHLA_OK) return s2;
+    *bytes = total;
+    return MHLA_OK;
+  } catch (...) {
+    return MHLA_ERR_INTERNAL;
+  }
+}
+
+mhla_status mhla_decode_prefill(mhla_handle h, void* state, size_t state_bytes, int64_t n, const void* q,
+                                const void* k, const void* v, const float* mc, void* o, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!h || !state || !q || !k || !v || !o) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = decode_supported(h);
+  if (st != MHLA_OK) return st;
+  if (n < 1 || n > h->N) return MHLA_ERR_INVALID_ARG;
+  if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return MHLA_ERR_INVALID_ARG;
+  if (mc && !aligned(mc, 4)) return MHLA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v || o == state || (workspace && (o == workspace || state == workspace)))
+    return MHLA_ERR_INVALID_ARG;
+  if (state_bytes < decode_state_bytes(h) || !aligned(state, 256)) return MHLA_ERR_WORKSPACE;
+  try {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!prefill_supported(h, n)) {
+      // the CLS token alone: one decode step on a cleared state
+      const hipError_t e = mhla::launch_decode_zero(static_cast<float*>(state), (int64_t)(decode_state_bytes(h) / 4), s);
+      if (e != hipSuccess) return MHLA_ERR_HIP;
+      return mhla_decode_step(h, state, state_bytes, 0, q, k, v, mc, o, stream);
+    }
+    mhla_plan sub;
+    size_t mc_off = 0, total = 0;
+    const mhla_status s2 = prefill_plan(h, n, &sub, &mc_off, &total);
+    if (s2 != MHLA_OK) return s2;
+    if (!workspace || workspace_bytes < total) return MHLA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    // the prefix's M_c: the leading Mp x Mp block of every head's M x M
+    float* mc_sub = nullptr;
+    if (mc) {
+      mc_sub = reinterpret_cast<float*>(ws + mc_off);
+      const int64_t heads = h->desc.mc_per_head ? h->H : 1, Mp = sub.M, M = h->M;
+      for (int64_t hh = 0; hh < heads; ++hh)
+        if (hipMemcpy2DAsync(mc_sub + hh * Mp * Mp, (size_t)Mp * 4, mc + hh * M * M, (size_t)M * 4, (size_t)Mp * 4,
+                             (size_t)Mp, hipMemcpyDeviceToDevice, s) != hipSuccess)
+          return MHLA_ERR_HIP;
+    }
+    const PrefillHook hook = {static_cast<float*>(state), h->M, decode_log2_c(h)};
+    return forward_run(&sub, q, k, v, mc_sub, o, workspace, s, nullptr, &hook);
   } catch (...) {
     return MHLA_ERR_INTERNAL;
   }
