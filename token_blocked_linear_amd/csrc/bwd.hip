@@ -531,9 +531,11 @@ __global__ __launch_bounds__(bwd_threads<D>()) void keyside_kernel(BwdParams p) 
 // hi / lo, and each wave owns 32 rows x (TILE / 2) columns (2 x TILE / 32 MFMA tiles): A = dS~
 // rows, B = S rows, both with 8 consecutive positions per lane.  The next step's loads are in
 // flight during the MFMAs.  Positions past FRAG + D (the last step of a (batch, head)) read as
-// zero.  The fp32 -> hi / lo conversion of the staged rows is the kernel's main work, and every
-// row is staged once per output tile of its chunk: 128 x 128 tiles (8 waves) once M > 64 convert
-// half as often as 64 x 64 tiles (4 waves).
+// zero.  Every row is staged once per output tile of its chunk: 128 x 128 tiles (8 waves) once
+// M > 64 load and convert each row half as often as 64 x 64 tiles (4 waves).  The kernel is
+// bound by its loads (a step's 256-byte row pieces, 64 KB apart in the stack): each load
+// instruction covers whole 128-byte lines, and one round of workgroups (one chunk each) keeps
+// two steps per CU in flight without a second round's ramp.
 constexpr int kDmcK = 64, kDmcPitch = kDmcK + 8;   // positions per step; LDS pitch in bf16 elements
 
 // SINGLE: every summary has one token slice (ssplits = zsplits_d = 1).  The step's loads then
@@ -557,42 +559,46 @@ __global__ __launch_bounds__(TILE * 4) void dmc_kernel(DmcParams p) {
   if (chunk >= p.nchunks) return;
   const int i0 = (tile / nt) * kDmcTile, b0 = (tile % nt) * kDmcTile;
   const int grp = blockIdx.y;
-  const int lrow = tid >> 2, lcol = (tid & 3) * 16;   // loader: one row, 16 positions
+  // loader: eight threads per row, 16 bytes each, so that each load instruction of a wave covers
+  // eight whole 128-byte lines; thread t holds positions 4 (t % 8) + 32 hf + 0..3 (hf = 0, 1) of
+  // the tile's rows t / 8 and t / 8 + TILE / 2
+  constexpr int kRowsPass = TILE / 2;
+  const int lrow = tid >> 3, lq = (tid & 7) * 4;
   const int wi = (wave >> 1) * 32, wb = (wave & 1) * (TILE / 2);
   const int64_t total_steps = (int64_t)p.group_bh * p.steps_per_bh;
   const int64_t s_begin = (int64_t)chunk * p.steps_per_chunk;
   const int64_t s_end = min(s_begin + p.steps_per_chunk, total_steps);
 
-  // sum over token slices of 8 consecutive values at position pos of summary row (bh, m)
-  auto load8 = [&](const float* part, const float* zpart, int zsplits, int bh, int m, int pos, float (&x)[8]) {
+  // sum over token slices of 4 consecutive values at position pos of summary row (bh, m)
+  auto load4 = [&](const float* part, const float* zpart, int zsplits, int bh, int m, int pos, float (&x)[4]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int e = 0; e < 4; ++e) x[e] = 0.f;
     if (m >= M || pos >= FRAG + D) return;
     const int64_t r = (int64_t)bh * M + m;
     const bool in_s = pos < FRAG;
     const int ns = in_s ? p.ssplits : zsplits;
     for (int s = 0; s < ns; ++s) {
       const float* src = in_s ? part + (r * p.ssplits + s) * FRAG + pos : zpart + (r * zsplits + s) * D + (pos - FRAG);
-      const u32x4_t w0 = ld16(src), w1 = ld16(src + 4);
+      const u32x4_t w = ld16(src);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] += __uint_as_float(w0[e]);
-        x[4 + e] += __uint_as_float(w1[e]);
-      }
+      for (int e = 0; e < 4; ++e) x[e] += __uint_as_float(w[e]);
     }
   };
-  auto load_step = [&](int64_t step, float (&xa)[2][8], float (&xb)[2][8]) {
+  auto load_step = [&](int64_t step, float (&xa)[2][2][4], float (&xb)[2][2][4]) {
     const int j = (int)(step / p.steps_per_bh);
-    const int pos = (int)(step % p.steps_per_bh) * kDmcK + lcol;
+    const int pos0 = (int)(step % p.steps_per_bh) * kDmcK;
     const int bh = p.per_head ? j * p.H + grp : j;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      load8(p.dps, p.dpz, p.zsplits_d, bh, i0 + lrow, pos + 8 * h, xa[h]);
-      load8(p.ps, p.pz, p.ssplits, bh, b0 + lrow, pos + 8 * h, xb[h]);
-    }
+    for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int pos = pos0 + 32 * hf + lq, r = lrow + kRowsPass * hr;
+        load4(p.dps, p.dpz, p.zsplits_d, bh, i0 + r, pos, xa[hr][hf]);
+        load4(p.ps, p.pz, p.ssplits, bh, b0 + r, pos, xb[hr][hf]);
+      }
   };
 
-  // SINGLE: raw words of the step, [h][0..1] = positions pos + 8h + 0..3 and + 4..7
+  // SINGLE: raw words of the step, [hr][hf] as held by the loader
   u32x4_t ra[2][2], rb[2][2];
   auto issue_step = [&](int64_t step) {
     const int j = (int)(step / p.steps_per_bh);
@@ -605,23 +611,29 @@ __global__ __launch_bounds__(TILE * 4) void dmc_kernel(DmcParams p) {
                           : make_rsrc(p.pz + (int64_t)bh * M * D, (uint32_t)M * D * 4u);
     const int stride = in_s ? FRAG : D, base = in_s ? 0 : FRAG;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int pos = pos0 + lcol + 8 * h;
-      const bool okp = pos < FRAG + D;
-      const int ma = i0 + lrow, mb = b0 + lrow;
-      const uint32_t oa = (okp && ma < M) ? (uint32_t)(ma * stride + pos - base) * 4u : kOutOfRange;
-      const uint32_t ob = (okp && mb < M) ? (uint32_t)(mb * stride + pos - base) * 4u : kOutOfRange;
-      ra[h][0] = buf_ld16(rsa, oa);
-      ra[h][1] = buf_ld16(rsa, oa == kOutOfRange ? kOutOfRange : oa + 16u);
-      rb[h][0] = buf_ld16(rsb, ob);
-      rb[h][1] = buf_ld16(rsb, ob == kOutOfRange ? kOutOfRange : ob + 16u);
-    }
-  };
-  auto words = [](const u32x4_t (&w)[2], float (&x)[8]) {
+    for (int hr = 0; hr < 2; ++hr)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = __uint_as_float(w[0][e]);
-      x[4 + e] = __uint_as_float(w[1][e]);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int pos = pos0 + 32 * hf + lq;
+        const bool okp = pos < FRAG + D;
+        const int ma = i0 + lrow + kRowsPass * hr, mb = b0 + lrow + kRowsPass * hr;
+        const uint32_t oa = (okp && ma < M) ? (uint32_t)(ma * stride + pos - base) * 4u : kOutOfRange;
+        const uint32_t ob = (okp && mb < M) ? (uint32_t)(mb * stride + pos - base) * 4u : kOutOfRange;
+        ra[hr][hf] = buf_ld16(rsa, oa);
+        rb[hr][hf] = buf_ld16(rsb, ob);
+      }
+  };
+  auto words = [](const u32x4_t& w, float (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+  };
+  auto split4 = [](const float (&x)[4], u32x2_t& hi, u32x2_t& lo) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t h, l;
+      split_bf16x2(x[2 * i], x[2 * i + 1], h, l);
+      hi[i] = h;
+      lo[i] = l;
     }
   };
 
@@ -631,31 +643,37 @@ __global__ __launch_bounds__(TILE * 4) void dmc_kernel(DmcParams p) {
 #pragma unroll
     for (int c = 0; c < WB; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  float xa[2][8], xb[2][8];
+  float xa[2][2][4], xb[2][2][4];
   if (s_begin < s_end) {
     if constexpr (SINGLE) issue_step(s_begin);
     else load_step(s_begin, xa, xb);
   }
   for (int64_t step = s_begin; step < s_end; ++step) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (SINGLE) {
-        words(ra[h], xa[h]);
-        words(rb[h], xb[h]);
+    for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if constexpr (SINGLE) {
+          words(ra[hr][hf], xa[hr][hf]);
+          words(rb[hr][hf], xb[hr][hf]);
+        }
+        u32x2_t ah, al, bhh, bll;
+        split4(xa[hr][hf], ah, al);
+        split4(xb[hr][hf], bhh, bll);
+        const int o = (lrow + kRowsPass * hr) * kDmcPitch + 32 * hf + lq;
+        *reinterpret_cast<u32x2_t*>(a_hi + o) = ah;
+        *reinterpret_cast<u32x2_t*>(a_lo + o) = al;
+        *reinterpret_cast<u32x2_t*>(b_hi + o) = bhh;
+        *reinterpret_cast<u32x2_t*>(b_lo + o) = bll;
       }
-      u32x4_t ah, al, bhh, bll;
-      split8(xa[h], ah, al);
-      split8(xb[h], bhh, bll);
-      const int o = lrow * kDmcPitch + lcol + 8 * h;
-      st16(a_hi + o, ah);
-      st16(a_lo + o, al);
-      st16(b_hi + o, bhh);
-      st16(b_lo + o, bll);
+    // the step's words are in LDS: the next step's loads go out before the barrier (SINGLE),
+    // so that they are in flight while the slower waves finish converting
+    if constexpr (SINGLE) {
+      if (step + 1 < s_end) issue_step(step + 1);
     }
     __syncthreads();
-    if (step + 1 < s_end) {
-      if constexpr (SINGLE) issue_step(step + 1);
-      else load_step(step + 1, xa, xb);
+    if constexpr (!SINGLE) {
+      if (step + 1 < s_end) load_step(step + 1, xa, xb);
     }
 #pragma unroll
     for (int k2 = 0; k2 < kDmcK; k2 += 32) {
@@ -702,24 +720,36 @@ __global__ __launch_bounds__(TILE * 4) void dmc_kernel(DmcParams p) {
       }
 }
 
-// dM_c from the chunk partials: out[g][e] = sum over chunks c in order of part[g][c][e].  Many
-// outputs: one thread each (coalesced over e); few: one wave each, lanes striding over the
-// chunks and a fixed shuffle tree.  Both orders are fixed for a given shape.
-__global__ __launch_bounds__(kThreads) void dmc_reduce_kernel(const float* part, float* dmc, int64_t mm,
-                                                              int groups, int nchunks, int wave_per_output) {
+// dM_c from the chunk partials part[g][c][e].  Many outputs: a workgroup of 8 waves takes 64
+// consecutive outputs, wave j sums the chunks c = j, j + 8, ... in order (its lanes over the
+// outputs, so each load is coalesced) and the eight sums are added in the order j = 0 .. 7.
+// Few outputs: one wave each, lanes striding over the chunks and a fixed shuffle tree.  Both
+// orders are fixed for a given shape.
+constexpr int kDmcRedWaves = 8;
+__global__ __launch_bounds__(64 * kDmcRedWaves) void dmc_reduce_kernel(const float* part, float* dmc, int64_t mm,
+                                                                       int groups, int nchunks, int wave_per_output) {
   const int64_t n_out = (int64_t)groups * mm;
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   if (!wave_per_output) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= n_out) return;
-    const int64_t g = idx / mm, e = idx % mm;
-    const float* src = part + g * nchunks * mm + e;
-    float s = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < nchunks; ++c) s += src[(int64_t)c * mm];   // loads issued ahead, adds in order
-    dmc[idx] = s;
+    __shared__ float sums[kDmcRedWaves][64];
+    const int64_t idx = (int64_t)blockIdx.x * 64 + lane;
+    float a = 0.f;
+    if (idx < n_out) {
+      const int64_t g = idx / mm, e = idx % mm;
+      const float* src = part + g * nchunks * mm + e;
+#pragma unroll 4
+      for (int c = j; c < nchunks; c += kDmcRedWaves) a += src[(int64_t)c * mm];   // loads ahead, adds in order
+    }
+    sums[j][lane] = a;
+    __syncthreads();
+    if (j == 0 && idx < n_out) {
+      float t = sums[0][lane];
+#pragma unroll
+      for (int k = 1; k < kDmcRedWaves; ++k) t += sums[k][lane];
+      dmc[idx] = t;
+    }
   } else {
-    const int lane = threadIdx.x & 63;
-    const int64_t idx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t idx = (int64_t)blockIdx.x * kDmcRedWaves + j;
     if (idx >= n_out) return;                      // whole waves leave together
     const int64_t g = idx / mm, e = idx % mm;
     const float* src = part + g * nchunks * mm + e;
@@ -905,8 +935,8 @@ hipError_t launch_dmc(const DmcParams& p, float* dmc, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t mm = (int64_t)p.M * p.M, n_out = (int64_t)groups * mm;
   const int wave_per_output = n_out < 16384 ? 1 : 0;
-  const int64_t per_wg = wave_per_output ? kThreads / 64 : kThreads;
-  hipLaunchKernelGGL(dmc_reduce_kernel, dim3((unsigned)((n_out + per_wg - 1) / per_wg)), dim3(kThreads), 0,
+  const int64_t per_wg = wave_per_output ? kDmcRedWaves : 64;   // outputs per workgroup
+  hipLaunchKernelGGL(dmc_reduce_kernel, dim3((unsigned)((n_out + per_wg - 1) / per_wg)), dim3(64 * kDmcRedWaves), 0,
                      stream, p.out, dmc, mm, groups, p.nchunks, wave_per_output);
   return hipGetLastError();
 }

@@ -674,8 +674,10 @@ BwdLayout bwd_layout(const mhla_plan* h) {
     L.dmc_steps_per_bh = (h->frag + h->d + 63) / 64;   // 64-position steps (the last one padded)
     const int64_t total = (int64_t)L.dmc_group_bh * L.dmc_steps_per_bh;
     const int64_t tile = mhla::dmc_tile((int)h->M), t = (h->M + tile - 1) / tile;
-    // about 8 waves' worth of workgroups per SIMD: 2048 of 4 waves, 1024 of 8
-    const int64_t want = tile == 128 ? 1024 : 2048;
+    // one round of workgroups: two 8-wave workgroups per CU (128 x 128 tiles), four 4-wave ones
+    // (64 x 64); each chunk then has as many steps as the work allows and the partials to
+    // reduce are fewest
+    const int64_t want = tile == 128 ? 512 : 1024;
     int64_t n = (want + t * t * L.dmc_groups - 1) / (t * t * L.dmc_groups);
     if (n > total) n = total;
     if (n < 1) n = 1;
