@@ -113,20 +113,54 @@ def test_backward_per_head_mc():
     _check(w, got, oracle_backward(w, q, k, v, mc, do), BF16_TOL)
 
 
+def _check_bf16_gradients(w, got, want, heads=None):
+    """dQ, dK, dV in bf16: within the bar plus each output's own rounding (2^-8 relative at
+    most); dM_c stays fp32 and takes the plain bar."""
+    errs = {}
+    for name, g, r in zip(NAMES[:3], got[:3], want[:3]):
+        if heads is not None:
+            g = np.stack([g[b, h] for b, h in heads])
+        assert np.all(np.isfinite(g)), name
+        rms = np.sqrt(np.mean(r ** 2))
+        excess = np.abs(g - r) - (BF16_TOL * rms + 2.0 ** -8 * np.abs(r))
+        errs[name] = rel_err(g, r)
+        assert excess.max() <= 0, (w.name, name, excess.max())
+    if got[3] is not None and want[3] is not None:
+        errs["dmc"] = rel_err(got[3], want[3])
+        assert errs["dmc"] <= BF16_TOL, (w.name, errs["dmc"])
+    print("  bf16 gradients " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    record("backward_bf16_gradients", w.name, phi=w.phi, readout=w.readout, **errs)
+
+
 @pytest.mark.parametrize("phi", ["elu1", "exp"])
 def test_backward_bf16_gradients(phi):
-    """dO, dQ, dK, dV in bf16: within the bar plus each output's own rounding (2^-8 relative at
-    most); dM_c stays fp32 and takes the plain bar."""
     w = synth.Workload("bw_bf16_out", "bf16", 2, 2, 64, (1000,), (200,), 141, "softmax_l1", phi=phi)
     announce(f"{w.name} {phi}")
     q, k, v, mc, do = _inputs(w, out_dtype="bf16")
     got = run_hip_backward(w, q, k, v, mc, do, out_dtype="bf16")
-    want = oracle_backward(w, q, k, v, mc, do)
-    for name, g, r in zip(NAMES[:3], got[:3], want[:3]):
-        rms = np.sqrt(np.mean(r ** 2))
-        excess = np.abs(g - r) - (BF16_TOL * rms + 2.0 ** -8 * np.abs(r))
-        assert excess.max() <= 0, (name, excess.max())
-    assert rel_err(got[3], want[3]) <= BF16_TOL
+    _check_bf16_gradients(w, got, oracle_backward(w, q, k, v, mc, do))
+
+
+# bf16 dO takes the LDS-streamed token-weighted summary for dS~: head sizes 32 and 128, odd 2D
+# and 3D blocks (partial stages, gathered token weights), the unnormalised readout, ReLU, and
+# many small blocks
+BF16_GRAD_CASES = [
+    synth.Workload("bwg_odd2d_d32", "bf16", 2, 2, 32, (30, 42), (5, 7), 181, "softmax_l1"),
+    synth.Workload("bwg_odd3d_d128", "bf16", 1, 2, 128, (6, 10, 12), (3, 5, 4), 182, "softmax_l1"),
+    synth.Workload("bwg_unnorm_2d", "bf16", 2, 2, 64, (32, 32), (8, 8), 183, "softmax_l1", "unnormalized"),
+    synth.Workload("bwg_relu_d128", "bf16", 1, 2, 128, (6, 10, 12), (3, 5, 4), 184, "softmax_l1", phi="relu"),
+    synth.Workload("bwg_m200_d128", "bf16", 1, 2, 128, (3200,), (16,), 185, "softmax_gauss"),
+    synth.Workload("bwg_ragged_cls", "bf16", 1, 2, 64, (30, 34), (4, 4), 186, "softmax_gauss", ragged=True,
+                   cls=True),
+]
+
+
+@pytest.mark.parametrize("w", BF16_GRAD_CASES, ids=lambda w: w.name)
+def test_backward_bf16_gradients_shapes(w):
+    announce(f"backward bf16 gradients {w.name} shape={w.qkv_shape} grid={w.grid} block={w.block} {w.readout}")
+    q, k, v, mc, do = _inputs(w, out_dtype="bf16", positive_q=w.phi == "relu")
+    got = run_hip_backward(w, q, k, v, mc, do, out_dtype="bf16")
+    _check_bf16_gradients(w, got, oracle_backward(w, q, k, v, mc, do))
 
 
 def test_backward_without_dmc_and_deterministic():
@@ -220,14 +254,20 @@ def test_backward_full(name):
     _check(w, got, oracle_backward(w, q, k, v, mc, do), BF16_TOL)
 
 
-def test_backward_long1d_sampled():
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_backward_long1d_sampled(out_dtype):
+    """The long-sequence workload at full size, with fp32 gradients and with bf16 gradients (as
+    the benchmark runs it): heads 0 and 15 against the oracle, dM_c through its invariance."""
     w = synth.WORKLOADS["long1d"]
-    announce(f"backward full long1d shape={w.qkv_shape} blocks={w.n_blocks}")
-    q, k, v, mc, do = _inputs(w)
-    got = run_hip_backward(w, q, k, v, mc, do)
+    announce(f"backward full long1d shape={w.qkv_shape} blocks={w.n_blocks} gradients {out_dtype}")
+    q, k, v, mc, do = _inputs(w, out_dtype=out_dtype)
+    got = run_hip_backward(w, q, k, v, mc, do, out_dtype=out_dtype)
     heads = [(0, 0), (0, w.heads - 1)]
     want = oracle_backward(w, q, k, v, mc, do, heads=heads)
-    _check(w, got[:3] + (None,), want[:3] + (None,), BF16_TOL, heads=heads)
+    if out_dtype == "bf16":
+        _check_bf16_gradients(w, got[:3] + (None,), want[:3] + (None,), heads=heads)
+    else:
+        _check(w, got[:3] + (None,), want[:3] + (None,), BF16_TOL, heads=heads)
     # O is invariant under scaling row i of M_c (S~_i and z~_i scale together), so
     # sum_b M_c[i, b] dM_c[i, b] = 0 for every row i.
     dmc = got[3]

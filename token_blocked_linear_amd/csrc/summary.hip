@@ -550,12 +550,16 @@ hipError_t launch_summary(const SummaryParams& p, int d, bool in_fp32, bool spli
   }
 }
 
+hipError_t launch_summary_dma_tokw(const SummaryParams& p, int d, int phi, int n_units, hipStream_t stream);
+
 // The backward's dS~ = sum_t (phi(q_t) / den_t) dO_t^T and dz~ = sum_t phi(q_t) gden_t, as a
 // summary with K := Q scaled per token by kscale = 1/den and V := dO, whose normaliser product
 // weights token t by zw = gden_t * den_t = -(dO_t . o_t).  K split; V split when fp32 (bf16 dO
 // is exact); fp32 partials; head sizes 32, 64, 128.
 hipError_t launch_summary_tokw(const SummaryParams& p, int d, bool in_fp32, bool v_fp32, int phi, int n_units,
                                hipStream_t stream) {
+  // bf16 Q and dO stream through the LDS ring (summary_dma.hip), the weights loaded with each stage
+  if (MHLA_SUMMARY_DMA && !in_fp32 && !v_fp32 && d >= 32) return launch_summary_dma_tokw(p, d, phi, n_units, stream);
   auto go = [&](auto phi_c) -> hipError_t {
     constexpr int PHI = decltype(phi_c)::value;
     auto by_d = [&](auto tin, auto tv) -> hipError_t {

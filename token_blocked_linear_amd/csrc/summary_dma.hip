@@ -19,6 +19,12 @@
 // stored with their 16-byte chunks XOR-swizzled by the token (sigma below), so that the 16 lanes of
 // a transposing read touch 16 different bank pairs.
 //
+// The backward's token-weighted summary (TOKW: K := Q scaled per token by kscale, normaliser product
+// weighted by zw, V := dO) takes the same ring: each slot also receives the stage's kscale and zw
+// through 4-byte direct-to-LDS loads (lane L of wave w: stage token 64 (w % NTW) + L, gathered by
+// its token index, so any block geometry works); the lanes scale phi(Q) before the hi / lo split
+// and feed zw (hi + lo) as the normaliser's B operand.
+//
 // Work split: wave w takes the 32-feature chunk kc = w % NKC and, when NKC < 4, every WK-th 32-token
 // step of a stage (WK = 4 / NKC waves share a chunk); their partial sums are added through LDS at
 // the end of a unit.  The loads are written in inline assembly (the compiler cannot tell which LDS
@@ -37,9 +43,16 @@ namespace {
 #ifndef MHLA_DMA_STAGE_BYTES
 #define MHLA_DMA_STAGE_BYTES 16384
 #endif
-template <int D> struct DmaRing {
+// TOKW (the backward's token-weighted summary): each slot also holds the stage's per-token weights,
+// kscale and zw as fp32 (one 4-byte load per lane, NTW loads of 64 tokens per array); at d = 128 a
+// ring of 4 such slots keeps two workgroups per CU.
+template <int D, bool TOKW = false> struct DmaRing {
   static constexpr int SB = MHLA_DMA_STAGE_BYTES;
-  static constexpr int NS = D == 128 ? 5 : 3;   // 80 KB at d = 128; d < 128 also holds a reduction area
+  static constexpr int NS = D == 128 ? (TOKW ? 4 : 5) : 3;   // 80 KB at d = 128; d < 128 also holds a reduction area
+  static constexpr int T = SB / (4 * D);                     // tokens per stage
+  static constexpr int NTW = TOKW ? (T + 63) / 64 : 0;
+  static constexpr int WB = NTW * 256;                       // bytes of one weight array per slot
+  static constexpr int SLOT = SB + 2 * WB;
 };
 
 // vmcnt(n) alone (expcnt and lgkmcnt at their maxima): the gfx9 s_waitcnt encoding.
@@ -59,6 +72,13 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 __device__ inline i32x4_t rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return i32x4_t{(int32_t)(uint32_t)a, (int32_t)(uint32_t)((a >> 32) & 0xffffu), (int32_t)bytes, 0x00020000};
+}
+
+// One 4-byte load per lane into LDS at lds_byte + 4 * lane (lds_byte wave-uniform; out of range:
+// the lane writes zero), default cache policy.
+__device__ inline void dma4(uint32_t lds_byte, uint32_t voff, i32x4_t rs) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rs) : "memory");
 }
 
 // One 16-byte load per lane into LDS at lds_byte + 16 * lane (lds_byte is wave-uniform); voff is the
@@ -92,11 +112,13 @@ __device__ inline int sigma(int t) {
 
 }  // namespace
 
-template <int D, bool SPLIT_K, bool WANT_U, bool OUT_BF16, int PHI>
+template <int D, bool SPLIT_K, bool WANT_U, bool OUT_BF16, int PHI, bool TOKW = false>
 __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, int n_units) {
   using Dm = Dims<D>;
+  using Ring = DmaRing<D, TOKW>;
   static_assert(D >= 32, "d = 16 runs on summary_kernel");
-  constexpr int kStages = DmaRing<D>::NS, kStageBytes = DmaRing<D>::SB;
+  static_assert(!TOKW || (SPLIT_K && !WANT_U && !OUT_BF16), "token weights: split phi(K), fp32 partials");
+  constexpr int kStages = Ring::NS, kStageBytes = Ring::SB, kSlotBytes = Ring::SLOT;
   constexpr int NKC = Dm::NKC, NCT = Dm::NCT, FRAG = Dm::FRAG;
   constexpr int T = kStageBytes / (4 * D);          // tokens per stage
   constexpr int KS = T / 32;                        // 32-token MFMA steps per stage
@@ -105,14 +127,16 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
   constexpr int ROWB = 2 * D;                       // bytes of one token row
   constexpr int LPR = D / 8;                        // 16-byte chunks (lanes) per row
   constexpr int DMA_PER = (kStageBytes / 2) / (kThreads * 16);   // loads per thread and tensor
-  constexpr int VM_AHEAD = 2 * DMA_PER * (kStages - 2);          // loads issued after a stage's
+  constexpr int LPS = 2 * DMA_PER + (TOKW ? 2 : 0);              // loads per thread and stage
+  constexpr int VM_AHEAD = LPS * (kStages - 2);                  // loads issued after a stage's
   constexpr int NST = NCT * (OUT_BF16 ? 1 : 2) + 2 + (WANT_U ? NCT : 0);   // stores per epilogue
   constexpr uint32_t kOnes = 0x3f803f80u;
   static_assert(KSW >= 1 && KSW * WK == KS, "steps split evenly over the waves of a chunk");
 
   extern __shared__ __align__(16) char smem[];
-  // ring: kStages x [K (SB / 2) | V (SB / 2)]; then the reduction area for WK > 1
-  float* red = reinterpret_cast<float*>(smem + kStages * kStageBytes);
+  // ring: kStages x [K (SB / 2) | V (SB / 2) | TOKW: kscale (WB) | zw (WB)]; then the reduction
+  // area for WK > 1
+  float* red = reinterpret_cast<float*>(smem + kStages * kSlotBytes);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(MHLA_LDS char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -208,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
     const uint32_t hb = (uint32_t)geo.N * D * kES;
     const i32x4_t rk = rsrc_words(live ? reinterpret_cast<const uint16_t*>(p.k) + c.U.head_off : p.k, live ? hb : 0u);
     const i32x4_t rv = rsrc_words(live ? reinterpret_cast<const uint16_t*>(p.v) + c.U.head_off : p.v, live ? hb : 0u);
-    const uint32_t slot_lds = ring_lds + (uint32_t)(slot * kStageBytes);
+    const uint32_t slot_lds = ring_lds + (uint32_t)(slot * kSlotBytes);
 #pragma unroll
     for (int i = 0; i < DMA_PER; ++i) {
       const int blk = i * 4 + wave;
@@ -223,6 +247,20 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
       }
       dma16(slot_lds + (uint32_t)(blk * 1024), off, rk);
       dma16(slot_lds + (uint32_t)(kStageBytes / 2 + blk * 1024), off, rv);
+    }
+    if constexpr (TOKW) {
+      // stage token tau = 64 (wave % NTW) + lane: waves w and w + NTW load the same tokens into the
+      // same bytes (same values), so that every wave issues the same number of loads
+      const int part = wave % Ring::NTW, tau = 64 * part + lane;
+      uint32_t woff = kOutOfRange;
+      if (live && tau < T) {
+        const int32_t j = c.sb + tau;
+        if (j < c.U.j_end) woff = (uint32_t)(c.U.base_tok + block_offset(geo, c.U.bg, (uint32_t)j)) * 4u;
+      }
+      const int64_t tb = live ? (int64_t)c.U.bh * geo.N : 0;
+      const uint32_t wbytes = live ? (uint32_t)geo.N * 4u : 0u;
+      dma4(slot_lds + (uint32_t)(kStageBytes + 256 * part), woff, rsrc_words(p.kscale + tb, wbytes));
+      dma4(slot_lds + (uint32_t)(kStageBytes + Ring::WB + 256 * part), woff, rsrc_words(p.zw + tb, wbytes));
     }
   };
 
@@ -241,13 +279,29 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
 
   // MFMAs of one stage (slot), `valid` tokens of which belong to the unit.
   auto compute = [&](int slot, int32_t valid) {
-    const MHLA_LDS char* ks_base = (const MHLA_LDS char*)smem + slot * kStageBytes;
+    const MHLA_LDS char* ks_base = (const MHLA_LDS char*)smem + slot * kSlotBytes;
     const MHLA_LDS char* vs_base = ks_base + kStageBytes / 2;
+    const MHLA_LDS float* ws_base = (const MHLA_LDS float*)(ks_base + kStageBytes);   // TOKW: kscale
+    const MHLA_LDS float* wz_base = ws_base + Ring::WB / 4;                            // TOKW: zw
 #pragma unroll
     for (int s = 0; s < KSW; ++s) {
       const int step = s * WK + kh;                   // this wave's 32-token step
       const int t0 = 32 * step + 8 * g + (lam >> 2);  // the lane's row in the first read
       const int t1 = t0 + 4;
+      // TOKW: kscale and zw of the lane's 8 tokens 32 step + 8 g + 0..7 (broadcast reads)
+      float sc[8], zwv[8];
+      if constexpr (TOKW) {
+        const int tb = 32 * step + 8 * g;
+        const f32x4_t s0 = *(const MHLA_LDS f32x4_t*)(ws_base + tb), s1 = *(const MHLA_LDS f32x4_t*)(ws_base + tb + 4);
+        const f32x4_t z0 = *(const MHLA_LDS f32x4_t*)(wz_base + tb), z1 = *(const MHLA_LDS f32x4_t*)(wz_base + tb + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[i] = s0[i];
+          sc[4 + i] = s1[i];
+          zwv[i] = z0[i];
+          zwv[4 + i] = z1[i];
+        }
+      }
       // A: phi(K)^T rows of tile r = features 32 kc + 8 q + 4 r + 0..3 of lane group quarter q
       u32x4_t a_hi[2], a_lo[2];
 #pragma unroll
@@ -257,7 +311,11 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
                                     ks_base + t1 * ROWB + 16 * (c ^ sigma<D>(t1)) + 8 * r);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x0 = phi_map<PHI>(bf16lo_to_f32(raw[i])), x1 = phi_map<PHI>(bf16hi_to_f32(raw[i]));
+          float x0 = phi_map<PHI>(bf16lo_to_f32(raw[i])), x1 = phi_map<PHI>(bf16hi_to_f32(raw[i]));
+          if constexpr (TOKW) {
+            x0 *= sc[2 * i];
+            x1 *= sc[2 * i + 1];
+          }
           if constexpr (SPLIT_K) {
             uint32_t h, l;
             split_bf16x2(x0, x1, h, l);
@@ -287,10 +345,24 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
           if constexpr (SPLIT_K) a_lo[r] &= tmask;
         }
       }
+      // TOKW: the normaliser product weights token t by zw_t, split hi (vmask) + lo (wlo)
+      u32x4_t wlo = {0u, 0u, 0u, 0u};
+      if constexpr (TOKW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h, l;
+          split_bf16x2(zwv[2 * i], zwv[2 * i + 1], h, l);
+          vmask[i] = h;
+          wlo[i] = l;
+        }
+        vmask &= tmask;
+        wlo &= tmask;
+      }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         accz[r] = mfma_bf16(a_hi[r], vmask, accz[r]);
         if constexpr (SPLIT_K) accz[r] = mfma_bf16(a_lo[r], vmask, accz[r]);
+        if constexpr (TOKW) accz[r] = mfma_bf16(a_hi[r], wlo, accz[r]);
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -428,12 +500,12 @@ __global__ __launch_bounds__(kThreads) void summary_dma_kernel(SummaryParams p, 
   wait_vm<0>();           // no load of an empty stage may still be writing LDS at the exit
 }
 
-template <int PHI, int D, bool SPLIT_K, bool WANT_U, bool OUT_BF16>
+template <int PHI, int D, bool SPLIT_K, bool WANT_U, bool OUT_BF16, bool TOKW = false>
 static hipError_t launch_dma_t(const SummaryParams& p, int n_units, hipStream_t stream) {
   constexpr int NKC = D / 32, NCT = D / 16, WK = 4 / NKC;
   constexpr size_t red_floats = WK > 1 ? (size_t)(WK - 1) * NKC * (2 * NCT * 64 * 4 + 2 * 64 * 4 + NCT * 64 * 4) : 0;
-  const size_t lds = (size_t)DmaRing<D>::NS * DmaRing<D>::SB + red_floats * 4;
-  auto kern = summary_dma_kernel<D, SPLIT_K, WANT_U, OUT_BF16, PHI>;
+  const size_t lds = (size_t)DmaRing<D, TOKW>::NS * DmaRing<D, TOKW>::SLOT + red_floats * 4;
+  auto kern = summary_dma_kernel<D, SPLIT_K, WANT_U, OUT_BF16, PHI, TOKW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int per_cu = (int)(160 * 1024 / lds) < 1 ? 1 : ((int)(160 * 1024 / lds) > 2 ? 2 : (int)(160 * 1024 / lds));
@@ -464,6 +536,27 @@ hipError_t launch_summary_dma(const SummaryParams& p, int d, bool split_k, bool 
       case 32: return dma_flags<PHI, 32>(p, split_k, want_u, out_bf16, n_units, stream);
       case 64: return dma_flags<PHI, 64>(p, split_k, want_u, out_bf16, n_units, stream);
       case 128: return dma_flags<PHI, 128>(p, split_k, want_u, out_bf16, n_units, stream);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  switch (phi) {
+    case kPhiElu1: return go(std::integral_constant<int, kPhiElu1>{});
+    case kPhiRelu: return go(std::integral_constant<int, kPhiRelu>{});
+    case kPhiExp: return go(std::integral_constant<int, kPhiExp>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The backward's token-weighted summary (K := Q scaled by kscale, normaliser weights zw, V := dO)
+// for bf16 Q and dO, d in {32, 64, 128}: split phi(K), fp32 partials.
+hipError_t launch_summary_dma_tokw(const SummaryParams& p, int d, int phi, int n_units, hipStream_t stream) {
+  if (!p.kscale || !p.zw) return hipErrorInvalidValue;
+  auto go = [&](auto phi_c) -> hipError_t {
+    constexpr int PHI = decltype(phi_c)::value;
+    switch (d) {
+      case 32: return launch_dma_t<PHI, 32, true, false, false, true>(p, n_units, stream);
+      case 64: return launch_dma_t<PHI, 64, true, false, false, true>(p, n_units, stream);
+      case 128: return launch_dma_t<PHI, 128, true, false, false, true>(p, n_units, stream);
       default: return hipErrorInvalidValue;
     }
   };
