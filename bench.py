@@ -36,6 +36,9 @@ included) and the mean kernel time from HIP events against the algorithmic bytes
 prompt a decode would start from), by HIP events.
 `backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the long1d
 inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
+`training` times a training step that keeps the forward's state: the forward with split operands
+(whose summaries and mixed summaries are what the backward recomputes), then mhla_backward_saved
+from its workspace; `recompute_step_ms` beside it is the default forward plus mhla_backward.
 
     python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter calibration
     python bench.py --digest             # digest of the kernel sources
@@ -499,6 +502,70 @@ def run_backward(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
             "roofline": roof, "kernels": per_kernel}
 
 
+def run_training(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
+    """A training step from the forward's saved state: the forward with split operands (its block
+    summaries and mixed summaries are what the backward would recompute), then mhla_backward_saved
+    from its workspace.  Timed three ways with no events (forward alone, saved backward alone,
+    the pair back to back), then the saved backward's kernels with the library's events."""
+    import torch
+    import token_blocked_linear_amd as T
+
+    w = synth.WORKLOADS[name]
+    q, k, v, mc = inputs
+    plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
+                  in_dtype=w.dtype, out_dtype=grad_dtype, readout=w.readout, accuracy="split")
+    do = synth.make_grad_output(w, np.random.default_rng(w.seed + 1000), grad_dtype)
+    tq, tk, tv, tdo = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), to_dev(do, grad_dtype)
+    tmc = None if mc is None else torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    o = torch.empty_like(tdo)
+    dq, dk, dv = (torch.empty_like(tdo) for _ in range(3))
+    dmc = None if tmc is None else torch.empty_like(tmc)
+    fws = plan.alloc_workspace()
+    bws = plan.alloc_backward_saved_workspace()
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        plan.forward(tq, tk, tv, tmc, o, fws, stream)
+
+    def bwd():
+        plan.backward(tq, tk, tv, tmc, tdo, dq, dk, dv, dmc, bws, stream, fwd_workspace=fws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    t_fwd = timed(fwd)
+    t_bwd = timed(bwd)                 # the workspace holds the last forward's state
+    t_step = timed(lambda: (fwd(), bwd()))
+    T.mhla_timing_reset(plan.handle)
+    T.mhla_timing_enable(plan.handle, True)
+    for _ in range(steps):
+        bwd()
+    torch.cuda.synchronize()
+    T.mhla_timing_enable(plan.handle, False)
+    ob = 2 if grad_dtype == "bf16" else 4
+    acc, _, _ = backward_accounting(w, ob)
+    per_kernel = {}
+    for i in range(7):
+        kname, ms, n = T.mhla_backward_timing_read(plan.handle, i)
+        if kname in ("bwd_summary", "bwd_mix"):
+            continue                   # read from the forward's workspace: not launched
+        per_kernel[kname] = price(acc[kname], ms / max(n, 1) * 1e-3)
+    plan.close()
+    return {"grad_dtype": grad_dtype, "forward_split_ms": round(t_fwd * 1e3, 4),
+            "backward_saved_ms": round(t_bwd * 1e3, 4), "step_ms": round(t_step * 1e3, 4),
+            "tokens_per_s": round(w.batch * w.n_tokens / t_step, 1), "kernels": per_kernel,
+            "protocol": "forward with split operands (accuracy split) keeping its summaries, then "
+                        "mhla_backward_saved from its workspace; each of the three times is K calls with "
+                        "no events after W warm-up calls; kernels from a fourth pass with the library's events"}
+
+
 def decode_accounting(BH: int, d: int, nb: int, t0: int, t1: int, in_b: int, out_b: int) -> int:
     """Algorithmic bytes of decode calls t0 .. t1-1 over BH (batch, head) pairs.  Every token
     reads S~< and R and writes R (fp32 d x d each), reads z~< and r and writes r, reads q, k, v
@@ -768,10 +835,13 @@ def main():
         progress("decode prefill")
         prefill = run_prefill(1, 16, 128, 65536, 256, 703)
 
-    bwd = None
+    bwd = train = None
     if not args.no_backward and w.readout != "mala":
         progress("backward")
         bwd = run_backward(args.workload, args.steps, args.warmup, args.out_dtype, res["inputs"])
+        progress("training step from the forward's saved state")
+        train = run_training(args.workload, args.steps, args.warmup, args.out_dtype, res["inputs"])
+        train["recompute_step_ms"] = round(res["step_s"] * 1e3 + bwd["ms_per_step"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -812,6 +882,7 @@ def main():
     line[f"{other_out}_output"] = alt
     if bwd is not None:
         line["backward"] = bwd
+        line["training"] = train
     if causal is not None:
         line["causal"] = causal
     if decode is not None:

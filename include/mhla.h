@@ -228,6 +228,32 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
                           const void* dout, void* dq, void* dk, void* dv, float* dmc, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Backward pass from the forward's saved state, for training: the same gradients as mhla_backward
+ * (the same kernels on the same values: identical bits), without recomputing the forward's block
+ * summaries S_b, z_b (and, except for MALA, its mixed summaries S~_i, z~_i), which are read from
+ * the workspace of the plan's last mhla_forward call instead ("MHLA: Restoring Expressivity of
+ * Linear Attention via Token-Level Multi-Head", Overall framework and Key design 2 give the
+ * steps; Key design 3 trains M_c end to end).
+ *   q, k, v, mc, dout, dq, dk, dv, dmc   as for mhla_backward; q, k, v and mc must be those of
+ *                 that forward call, whose results are only as valid as this requirement
+ *   fwd_workspace the workspace of that mhla_forward call on this plan, unchanged since (device,
+ *                 256-byte aligned, at least mhla_workspace_size bytes, given as fwd_workspace_bytes);
+ *                 only read
+ *   workspace     device, mhla_backward_saved_workspace_size bytes (smaller than the recomputing
+ *                 backward's), 256-byte aligned, not overlapping fwd_workspace
+ * Supported where the forward keeps these summaries at the backward's precision: plans whose
+ * operands are split (MHLA_ACCURACY_SPLIT, or the automatic choice for MALA, fp32 inputs and the
+ * ReLU and exp maps; mhla_plan_info.split_operands == 1) and which either mix in a kernel of their
+ * own (more than 16 blocks: mhla_plan_info.n_kernels == 3) or read out MALA.  Else, and for
+ * everything mhla_backward rejects, MHLA_ERR_UNSUPPORTED.  Errors as mhla_backward, plus
+ * INVALID_ARG (fwd_workspace NULL, or overlapping an output or the workspace) and WORKSPACE
+ * (fwd_workspace too small or misaligned).  Asynchronous on `stream`. */
+mhla_status mhla_backward_saved_workspace_size(mhla_handle h, size_t* bytes);
+mhla_status mhla_backward_saved(mhla_handle h, const void* q, const void* k, const void* v, const float* mc,
+                                const void* dout, void* dq, void* dk, void* dv, float* dmc,
+                                const void* fwd_workspace, size_t fwd_workspace_bytes, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Streaming decode: one new token per (batch, head) per call, for a causal plan ("MHLA: Restoring
  * Expressivity of Linear Attention via Token-Level Multi-Head", Method -> Key design 4: MHLA is
  * compatible with streaming / stateful inference; the causal reading of the causal readout modes

@@ -409,6 +409,43 @@ def test_decode_prefill_sizes_and_argument_errors_before_launch():
         x.close()
 
 
+def test_backward_saved_support_sizes_and_argument_errors_before_launch():
+    """mhla_backward_saved: supported where the forward keeps split summaries and a mixed stack
+    (or reads out MALA); its workspace is smaller than the recomputing backward's; validation
+    rejects bad calls before any launch (a launch here would give MHLA_ERR_HIP)."""
+    lib = _lib_or_skip()
+    split = T.Plan(grid=(4096,), block=(64,), batch=1, heads=2, head_dim=64, accuracy="split")
+    mala = T.Plan(grid=(32, 32), block=(32, 32), batch=1, heads=2, head_dim=64, readout="mala")
+    bf16 = T.Plan(grid=(4096,), block=(64,), batch=1, heads=2, head_dim=64)            # bf16 stack
+    fused = T.Plan(grid=(64, 64), block=(16, 16), batch=1, heads=2, head_dim=64, accuracy="split")  # M = 16
+    causal = T.Plan(grid=(4096,), block=(64,), batch=1, heads=2, head_dim=64, readout="causal",
+                    accuracy="split")
+    for p in (split, mala):
+        assert T.mhla_backward_saved_workspace_size(p.handle) < T.mhla_backward_workspace_size(p.handle)
+    n = ctypes.c_size_t()
+    for p in (bf16, fused, causal):
+        assert lib.mhla_backward_saved_workspace_size(p.handle, ctypes.byref(n)) == 2
+    Q, K, V, MC, DO, DQ, DK, DV, DMC = (0x10000 * i for i in range(1, 10))
+    FW, W = 0x10000000, 0x40000000
+    fb = T.mhla_workspace_size(split.handle)
+    wb = T.mhla_backward_saved_workspace_size(split.handle)
+    f = lambda h, *a: lib.mhla_backward_saved(h, *a)  # noqa: E731
+    args = (Q, K, V, MC, DO, DQ, DK, DV, DMC)
+    assert f(split.handle, *args, None, fb, W, wb, None) == 1            # no forward workspace
+    assert f(split.handle, *args, FW, fb - 1, W, wb, None) == 4          # forward workspace too small
+    assert f(split.handle, *args, FW + 16, fb, W, wb, None) == 4         # forward workspace misaligned
+    assert f(split.handle, *args, FW, fb, W, wb - 1, None) == 4          # workspace too small
+    assert f(split.handle, *args, FW, fb, FW + 256, wb, None) == 1       # workspace inside the forward's
+    assert f(split.handle, Q, K, V, MC, DO, FW, DK, DV, DMC, FW, fb, W, wb, None) == 1   # dq in it
+    assert f(split.handle, None, K, V, MC, DO, DQ, DK, DV, DMC, FW, fb, W, wb, None) == 1  # NULL q
+    assert f(split.handle, Q, K, V, None, DO, DQ, DK, DV, DMC, FW, fb, W, wb, None) == 1  # NULL M_c, M > 1
+    for p in (bf16, fused, causal):
+        assert f(p.handle, *args, FW, fb, W, wb, None) == 2
+    assert f(None, *args, FW, fb, W, wb, None) == 1
+    for p in (split, mala, bf16, fused, causal):
+        p.close()
+
+
 def test_decode_binding_rejects_a_host_state():
     """The binding checks the state tensor before handing its pointer to the library."""
     import torch

@@ -21,6 +21,7 @@ __all__ = [
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
+    "mhla_backward_saved_workspace_size", "mhla_backward_saved",
     "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
     "mhla_forward_intermediates", "mhla_decode_prefill_workspace_size", "mhla_decode_prefill",
     "MHLA_NOALLOC_SCRATCH_BYTES", "MHLA_ERR_SCRATCH_LIMIT", "make_desc", "Plan", "EXPORTED_SYMBOLS",
@@ -49,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "mhla_backward_workspace_size", "mhla_backward", "mhla_backward_timing_read",
     "mhla_decode_state_size", "mhla_decode_reset", "mhla_decode_step", "mhla_forward_noalloc",
     "mhla_forward_intermediates", "mhla_decode_prefill_workspace_size", "mhla_decode_prefill",
+    "mhla_backward_saved_workspace_size", "mhla_backward_saved",
 )
 
 
@@ -125,6 +127,8 @@ def load_library() -> ctypes.CDLL:
     lib.mhla_forward_intermediates.argtypes = [P, P, P, P, P, P, P, P, P, SZ, P]
     lib.mhla_backward_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     lib.mhla_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.mhla_backward_saved_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
+    lib.mhla_backward_saved.argtypes = [P, P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P]
     lib.mhla_destroy.argtypes = [P]
     lib.mhla_status_string.argtypes = [I32]
     lib.mhla_status_string.restype = ctypes.c_char_p
@@ -204,6 +208,23 @@ def mhla_backward(h, q: int, k: int, v: int, mc: int, dout: int, dq: int, dk: in
     """Pointers are integer device addresses (0 for NULL); ``stream`` a raw hipStream_t."""
     _check(load_library().mhla_backward(h, q, k, v, mc or None, dout, dq, dk, dv, dmc or None,
                                         workspace or None, workspace_bytes, stream or None), "mhla_backward")
+
+
+def mhla_backward_saved_workspace_size(h) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().mhla_backward_saved_workspace_size(h, ctypes.byref(n)),
+           "mhla_backward_saved_workspace_size")
+    return n.value
+
+
+def mhla_backward_saved(h, q: int, k: int, v: int, mc: int, dout: int, dq: int, dk: int, dv: int, dmc: int,
+                        fwd_workspace: int, fwd_workspace_bytes: int, workspace: int, workspace_bytes: int,
+                        stream: int) -> None:
+    """As mhla_backward, reading the forward's summaries from ``fwd_workspace`` (integer device
+    addresses, 0 for NULL; ``stream`` a raw hipStream_t)."""
+    _check(load_library().mhla_backward_saved(h, q, k, v, mc or None, dout, dq, dk, dv, dmc or None,
+                                              fwd_workspace or None, fwd_workspace_bytes, workspace or None,
+                                              workspace_bytes, stream or None), "mhla_backward_saved")
 
 
 def mhla_decode_state_size(h) -> int:
@@ -362,11 +383,25 @@ class Plan:
         n = mhla_backward_workspace_size(self.handle)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
-    def backward(self, q, k, v, mc, dout, dq, dk, dv, dmc, workspace, stream=None):
-        """Gradients into dq, dk, dv (the plan's out_dtype, like dout) and dmc (fp32, M_c's shape,
-        or None to skip)."""
+    def alloc_backward_saved_workspace(self, device="cuda"):
         import torch
-        self.check_args(q, k, v, mc, dout, workspace, mhla_backward_workspace_size(self.handle))
+        n = mhla_backward_saved_workspace_size(self.handle)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def backward(self, q, k, v, mc, dout, dq, dk, dv, dmc, workspace, stream=None, fwd_workspace=None):
+        """Gradients into dq, dk, dv (the plan's out_dtype, like dout) and dmc (fp32, M_c's shape,
+        or None to skip).  With ``fwd_workspace`` (the workspace of this plan's last forward on the
+        same q, k, v, mc, unchanged since) the forward's summaries are read from it
+        (mhla_backward_saved) and ``workspace`` is the smaller one of
+        alloc_backward_saved_workspace."""
+        import torch
+        ws_need = (mhla_backward_saved_workspace_size(self.handle) if fwd_workspace is not None
+                   else mhla_backward_workspace_size(self.handle))
+        self.check_args(q, k, v, mc, dout, workspace, ws_need)
+        if fwd_workspace is not None:
+            fb = mhla_workspace_size(self.handle)
+            if fwd_workspace.dtype != torch.uint8 or fwd_workspace.numel() < fb or not fwd_workspace.is_cuda:
+                raise ValueError(f"fwd_workspace: expected the forward's workspace (>= {fb} bytes of uint8)")
         for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
             if t.shape != dout.shape or t.dtype != dout.dtype or not t.is_contiguous() or not t.is_cuda:
                 raise ValueError(f"{name}: expected a contiguous cuda tensor like dout")
@@ -377,10 +412,14 @@ class Plan:
                 raise ValueError(f"dmc: expected contiguous float32 cuda tensor of shape {mc_shape}")
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
-        mhla_backward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                      mc.data_ptr() if mc is not None else 0, dout.data_ptr(), dq.data_ptr(),
-                      dk.data_ptr(), dv.data_ptr(), dmc.data_ptr() if dmc is not None else 0,
-                      workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), mc.data_ptr() if mc is not None else 0,
+                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                dmc.data_ptr() if dmc is not None else 0)
+        if fwd_workspace is not None:
+            mhla_backward_saved(self.handle, *ptrs, fwd_workspace.data_ptr(), fwd_workspace.numel(),
+                                workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
+        else:
+            mhla_backward(self.handle, *ptrs, workspace.data_ptr(), workspace.numel(), stream.cuda_stream)
         return dq, dk, dv, dmc
 
     def alloc_decode_state(self, device="cuda"):

@@ -644,18 +644,21 @@ struct BwdLayout {
   int dmc_groups, dmc_group_bh, dmc_steps_per_bh, dmc_nchunks, dmc_steps_per_chunk;
 };
 
-BwdLayout bwd_layout(const mhla_plan* h) {
+// saved: the forward's summaries (and, unless MALA, its mixed summaries) come from the forward's
+// workspace (mhla_backward_saved), so they take no room here.
+BwdLayout bwd_layout(const mhla_plan* h, bool saved = false) {
   BwdLayout L;
   const size_t f = (size_t)h->frag, dd = (size_t)h->d;
   const size_t rows = (size_t)h->BH * h->M;
   const size_t slots = rows * h->sum_splits;
+  const size_t own_sum = saved ? 0 : 1, own_mix = saved && !h->mala ? 0 : 1;
   size_t off = 0;
   auto take = [&](size_t& at, size_t bytes) { at = off; off = align256(off + bytes); };
-  take(L.ps, slots * f * 4);
-  take(L.pz, slots * dd * 4);
-  take(L.st_hi, rows * f * 2);
-  take(L.st_lo, rows * f * 2);
-  take(L.zt, rows * dd * 4);
+  take(L.ps, own_sum * slots * f * 4);
+  take(L.pz, own_sum * slots * dd * 4);
+  take(L.st_hi, own_mix * rows * f * 2);
+  take(L.st_lo, own_mix * rows * f * 2);
+  take(L.zt, own_mix * rows * dd * 4);
   take(L.dps, slots * f * 4);
   take(L.dpzs, slots * dd * 4);
   take(L.ds_hi, rows * f * 2);
@@ -664,7 +667,7 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   take(L.tok_scale, (size_t)h->BH * h->N * 4);
   take(L.tok_zw, (size_t)h->BH * h->N * 4);
   const size_t mala_rows = h->mala ? rows : 0;
-  take(L.pu, mala_rows * h->sum_splits * dd * 4);
+  take(L.pu, own_sum * mala_rows * h->sum_splits * dd * 4);
   take(L.ub, mala_rows * dd * 4);
   take(L.du_part, mala_rows * h->rd_splits * dd * 4);
   take(L.du, mala_rows * dd * 4);
@@ -689,8 +692,8 @@ BwdLayout bwd_layout(const mhla_plan* h) {
   L.mfma_mix = !h->mala && h->M <= 256;   // MALA (one block) has no mixing
   L.mix = mhla::mix_shape((int)h->M, true);
   const size_t fb = L.mfma_mix ? (size_t)h->mcf_heads * L.mix.nitp * L.mix.nbc * 512 * 2 : 0;
-  take(L.mcf_hi, fb);
-  take(L.mcf_lo, fb);
+  take(L.mcf_hi, saved ? 0 : fb);   // the forward mixing's operands: only when it is recomputed
+  take(L.mcf_lo, saved ? 0 : fb);
   take(L.mcft_hi, fb);
   take(L.mcft_lo, fb);
   L.total = off;
@@ -700,6 +703,17 @@ BwdLayout bwd_layout(const mhla_plan* h) {
 mhla_status bwd_supported(const mhla_plan* h) {
   if (h->causal) return MHLA_ERR_UNSUPPORTED;   // no causal backward here
   if (h->d < 32) return MHLA_ERR_UNSUPPORTED;   // head sizes 32, 64, 128
+  return MHLA_OK;
+}
+
+// The backward can take the forward's summaries when they are the fp32 partials it would compute
+// (split operands) and, unless MALA (whose centring runs in the backward), its mixed summaries
+// when the forward keeps a mixed stack (a mixing kernel of its own).
+mhla_status bwd_saved_supported(const mhla_plan* h) {
+  const mhla_status st = bwd_supported(h);
+  if (st != MHLA_OK) return st;
+  if (!h->split) return MHLA_ERR_UNSUPPORTED;
+  if (!h->mala && !h->mix_kernel) return MHLA_ERR_UNSUPPORTED;
   return MHLA_OK;
 }
 
@@ -713,11 +727,13 @@ mhla_status mhla_backward_workspace_size(mhla_handle h, size_t* bytes) {
   return MHLA_OK;
 }
 
-mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const void* v, const float* mc,
-                          const void* dout, void* dq, void* dk, void* dv, float* dmc, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+// fwd: the forward's workspace (mhla_backward_saved) or NULL (recompute the forward's steps)
+static mhla_status backward_impl(mhla_handle h, const void* q, const void* k, const void* v, const float* mc,
+                                 const void* dout, void* dq, void* dk, void* dv, float* dmc, const char* fwd,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (!h || !q || !k || !v || !dout || !dq || !dk || !dv) return MHLA_ERR_INVALID_ARG;
-  const mhla_status st = bwd_supported(h);
+  const bool saved = fwd != nullptr;
+  const mhla_status st = saved ? bwd_saved_supported(h) : bwd_supported(h);
   if (st != MHLA_OK) return st;
   if (!mc && h->M != 1) return MHLA_ERR_INVALID_ARG;
   if (h->mala && dmc) return MHLA_ERR_INVALID_ARG;   // MALA has no M_c
@@ -734,7 +750,7 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
   if (dq == dk || dq == dv || dk == dv) return MHLA_ERR_INVALID_ARG;
   if (mc && !aligned(mc, 4)) return MHLA_ERR_INVALID_ARG;
   if (dmc && !aligned(dmc, 4)) return MHLA_ERR_INVALID_ARG;
-  const BwdLayout L = bwd_layout(h);
+  const BwdLayout L = bwd_layout(h, saved);
   if (!workspace || workspace_bytes < L.total) return MHLA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MHLA_ERR_WORKSPACE;
   try {
@@ -742,6 +758,16 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     char* ws = static_cast<char*>(workspace);
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+    // the forward's summaries (fp32 slice partials) and mixed summaries (hi, lo, fp32 z~): from the
+    // forward's workspace when saved (MALA: its C comes from the staging kernel below), else here
+    char* fw = const_cast<char*>(fwd);
+    float* ps = saved ? reinterpret_cast<float*>(fw + h->off_ps) : F(L.ps);
+    float* pz = saved ? reinterpret_cast<float*>(fw + h->off_pz) : F(L.pz);
+    float* pu = !h->mala ? nullptr : saved ? reinterpret_cast<float*>(fw + h->off_pu) : F(L.pu);
+    const bool fwd_mix = saved && !h->mala;
+    uint16_t* st_hi = fwd_mix ? reinterpret_cast<uint16_t*>(fw + h->off_st_hi) : U16(L.st_hi);
+    uint16_t* st_lo = fwd_mix ? reinterpret_cast<uint16_t*>(fw + h->off_st_lo) : U16(L.st_lo);
+    float* zt = fwd_mix ? reinterpret_cast<float*>(fw + h->off_zt) : F(L.zt);
     const int64_t mc_stride = h->desc.mc_per_head ? h->M * h->M : 0;
     const int phi = (int)h->desc.phi;
     const int units_sum = (int)(h->sum_splits * h->M * h->BH);
@@ -755,8 +781,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     mhla::SummaryParams sp = {};
     sp.k = k;
     sp.v = v;
-    sp.ps = F(L.ps);
-    sp.pz = F(L.pz);
+    sp.ps = ps;
+    sp.pz = pz;
     sp.g = h->geom;
     sp.splits = h->sum_splits;
     sp.tok_per_split = h->sum_tok;
@@ -770,21 +796,22 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
       sp.mcf_nitp = L.mix.nitp;
       sp.mcf_nbc = L.mix.nbc;
     }
-    if (h->mala) sp.pu = F(L.pu);
-    hipError_t e = mhla::launch_summary(sp, h->d, h->in_fp32, true, h->in_fp32, h->mala, false, phi,
-                                        units_sum, s);
+    if (h->mala) sp.pu = pu;
+    hipError_t e = saved ? hipSuccess
+                         : mhla::launch_summary(sp, h->d, h->in_fp32, true, h->in_fp32, h->mala, false, phi,
+                                                units_sum, s);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
     // MALA: C = S - z u^T / N, z, u / N (stage 0); dS, dz = dz' - dS u / N, du (stage 1)
     auto mala_stage = [&](int stage) -> hipError_t {
       mhla::MalaStageParams mp = {};
-      mp.ps = F(stage == 0 ? L.ps : L.dps);
-      mp.pz = F(stage == 0 ? L.pz : L.dpzs);
-      mp.pu = F(L.pu);
+      mp.ps = stage == 0 ? ps : F(L.dps);
+      mp.pz = stage == 0 ? pz : F(L.dpzs);
+      mp.pu = pu;
       mp.ub = F(L.ub);
       mp.du_part = F(L.du_part);
-      mp.y_hi = U16(stage == 0 ? L.st_hi : L.ds_hi);
-      mp.y_lo = U16(stage == 0 ? L.st_lo : L.ds_lo);
-      mp.zo = F(stage == 0 ? L.zt : L.dz);
+      mp.y_hi = stage == 0 ? st_hi : U16(L.ds_hi);
+      mp.y_lo = stage == 0 ? st_lo : U16(L.ds_lo);
+      mp.zo = stage == 0 ? zt : F(L.dz);
       mp.ub_out = F(L.ub);
       mp.du = F(L.du);
       mp.ss = h->sum_splits;
@@ -830,7 +857,7 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
       mp.mc_transposed = transposed;
       return mhla::launch_mix(mp, h->d, h->frag, (int)h->BH, true, s);
     };
-    e = h->mala ? mala_stage(0) : mix(F(L.ps), F(L.pz), h->sum_splits, 0, U16(L.st_hi), U16(L.st_lo), F(L.zt));
+    e = h->mala ? mala_stage(0) : fwd_mix ? hipSuccess : mix(ps, pz, h->sum_splits, 0, st_hi, st_lo, zt);
     if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
 
     // 3. query side: dq, g, dz~ partials
@@ -842,9 +869,9 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     bp.dq = dq;
     bp.dk = dk;
     bp.dv = dv;
-    bp.st_hi = U16(L.st_hi);
-    bp.st_lo = U16(L.st_lo);
-    bp.zt = F(L.zt);
+    bp.st_hi = st_hi;
+    bp.st_lo = st_lo;
+    bp.zt = zt;
     bp.ds_hi = U16(L.ds_hi);
     bp.ds_lo = U16(L.ds_lo);
     bp.dz = F(L.dz);
@@ -895,9 +922,9 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
     if (dmc) {
       mhla::DmcParams dp = {};
       dp.dps = F(L.dps);
-      dp.ps = F(L.ps);
+      dp.ps = ps;
       dp.dpz = F(L.dpzs);
-      dp.pz = F(L.pz);
+      dp.pz = pz;
       dp.out = F(L.dmcp);
       dp.M = (int32_t)h->M;
       dp.frag = h->frag;
@@ -917,6 +944,42 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
   } catch (...) {
     return MHLA_ERR_INTERNAL;
   }
+}
+
+mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const void* v, const float* mc,
+                          const void* dout, void* dq, void* dk, void* dv, float* dmc, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return backward_impl(h, q, k, v, mc, dout, dq, dk, dv, dmc, nullptr, workspace, workspace_bytes, stream);
+}
+
+mhla_status mhla_backward_saved_workspace_size(mhla_handle h, size_t* bytes) {
+  if (!h || !bytes) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = bwd_saved_supported(h);
+  if (st != MHLA_OK) return st;
+  *bytes = bwd_layout(h, true).total;
+  return MHLA_OK;
+}
+
+mhla_status mhla_backward_saved(mhla_handle h, const void* q, const void* k, const void* v, const float* mc,
+                                const void* dout, void* dq, void* dk, void* dv, float* dmc,
+                                const void* fwd_workspace, size_t fwd_workspace_bytes, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!h) return MHLA_ERR_INVALID_ARG;
+  const mhla_status st = bwd_saved_supported(h);
+  if (st != MHLA_OK) return st;
+  if (!fwd_workspace) return MHLA_ERR_INVALID_ARG;
+  if (fwd_workspace_bytes < h->ws_bytes || !aligned(fwd_workspace, 256)) return MHLA_ERR_WORKSPACE;
+  // the forward's workspace is read: no output and no part of this call's workspace may overlap it
+  const char* f0 = static_cast<const char*>(fwd_workspace);
+  const char* f1 = f0 + h->ws_bytes;
+  for (const void* a : {(const void*)dq, (const void*)dk, (const void*)dv, (const void*)dmc})
+    if (a && static_cast<const char*>(a) >= f0 && static_cast<const char*>(a) < f1) return MHLA_ERR_INVALID_ARG;
+  if (workspace) {
+    const char* w0 = static_cast<const char*>(workspace);
+    const char* w1 = w0 + workspace_bytes;
+    if (w0 < f1 && f0 < w1) return MHLA_ERR_INVALID_ARG;
+  }
+  return backward_impl(h, q, k, v, mc, dout, dq, dk, dv, dmc, f0, workspace, workspace_bytes, stream);
 }
 
 // ---- streaming decode --------------------------------------------------------------------
