@@ -36,8 +36,8 @@ included) and the mean kernel time from HIP events against the algorithmic bytes
 prompt a decode would start from), by HIP events.
 `backward` times mhla_backward (dQ, dK, dV, dM_c; gradients in the output dtype) on the long1d
 inputs, K steps after W warm-ups, with per-kernel durations from the library's events.
-`training` times a training step that keeps the forward's state: the forward with split operands
-(whose summaries and mixed summaries are what the backward recomputes), then mhla_backward_saved
+`training` times a training step that keeps the forward's state: the forward at MHLA_ACCURACY_TRAIN
+(split summaries and mixed summaries, what the backward recomputes), then mhla_backward_saved
 from its workspace; `recompute_step_ms` beside it is the default forward plus mhla_backward.
 
     python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter calibration
@@ -503,8 +503,9 @@ def run_backward(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
 
 
 def run_training(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
-    """A training step from the forward's saved state: the forward with split operands (its block
-    summaries and mixed summaries are what the backward would recompute), then mhla_backward_saved
+    """A training step from the forward's saved state: the forward at MHLA_ACCURACY_TRAIN (split
+    summaries and mixing, what the backward would recompute; the readout at the bf16 level from
+    the mixed stack's high part), then mhla_backward_saved
     from its workspace.  Timed three ways with no events (forward alone, saved backward alone,
     the pair back to back), then the saved backward's kernels with the library's events."""
     import torch
@@ -513,7 +514,7 @@ def run_training(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
     w = synth.WORKLOADS[name]
     q, k, v, mc = inputs
     plan = T.Plan(grid=w.grid, block=w.block, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
-                  in_dtype=w.dtype, out_dtype=grad_dtype, readout=w.readout, accuracy="split")
+                  in_dtype=w.dtype, out_dtype=grad_dtype, readout=w.readout, accuracy="train")
     do = synth.make_grad_output(w, np.random.default_rng(w.seed + 1000), grad_dtype)
     tq, tk, tv, tdo = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), to_dev(do, grad_dtype)
     tmc = None if mc is None else torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
@@ -558,10 +559,10 @@ def run_training(name: str, steps: int, warmup: int, grad_dtype: str, inputs):
             continue                   # read from the forward's workspace: not launched
         per_kernel[kname] = price(acc[kname], ms / max(n, 1) * 1e-3)
     plan.close()
-    return {"grad_dtype": grad_dtype, "forward_split_ms": round(t_fwd * 1e3, 4),
+    return {"grad_dtype": grad_dtype, "forward_train_ms": round(t_fwd * 1e3, 4),
             "backward_saved_ms": round(t_bwd * 1e3, 4), "step_ms": round(t_step * 1e3, 4),
             "tokens_per_s": round(w.batch * w.n_tokens / t_step, 1), "kernels": per_kernel,
-            "protocol": "forward with split operands (accuracy split) keeping its summaries, then "
+            "protocol": "forward at accuracy train (split summaries and mixing kept in its workspace), then "
                         "mhla_backward_saved from its workspace; each of the three times is K calls with "
                         "no events after W warm-up calls; kernels from a fourth pass with the library's events"}
 

@@ -91,7 +91,11 @@ typedef enum {
                             /* MALA, fp32 inputs and the ReLU / exp maps (whose outputs sit      */
                             /* near the 2e-2 bar with single bf16 operands)                      */
   MHLA_ACCURACY_BF16 = 1,   /* single bf16 MFMA operands, fp32 accumulation                     */
-  MHLA_ACCURACY_SPLIT = 2   /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
+  MHLA_ACCURACY_SPLIT = 2,  /* operands not exact in bf16 are split hi + lo (about fp32 accuracy)*/
+  MHLA_ACCURACY_TRAIN = 3   /* summaries and mixing as SPLIT (mhla_backward_saved reads them);   */
+                            /* the readout's operands as AUTO chooses them: with a mixing kernel */
+                            /* of its own, bf16 inputs and ELU+1, the mixed stack's high part    */
+                            /* and single bf16 operands; elsewhere as SPLIT                      */
 } mhla_accuracy;              /* The causal readouts: the field sets the summaries, the mixing of */
                               /* the earlier blocks and, for bf16 inputs, the in-slice scores and  */
                               /* the start-state readout; the weights of V (P) are always split    */
@@ -242,8 +246,8 @@ mhla_status mhla_backward(mhla_handle h, const void* q, const void* k, const voi
  *   workspace     device, mhla_backward_saved_workspace_size bytes (smaller than the recomputing
  *                 backward's), 256-byte aligned, not overlapping fwd_workspace
  * Supported where the forward keeps these summaries at the backward's precision: plans whose
- * operands are split (MHLA_ACCURACY_SPLIT, or the automatic choice for MALA, fp32 inputs and the
- * ReLU and exp maps; mhla_plan_info.split_operands == 1) and which either mix in a kernel of their
+ * summaries are split (MHLA_ACCURACY_SPLIT or MHLA_ACCURACY_TRAIN, or the automatic choice for
+ * MALA, fp32 inputs and the ReLU and exp maps; mhla_plan_info.split_operands == 1) and which either mix in a kernel of their
  * own (more than 16 blocks: mhla_plan_info.n_kernels == 3) or read out MALA.  Else, and for
  * everything mhla_backward rejects, MHLA_ERR_UNSUPPORTED.  Errors as mhla_backward, plus
  * INVALID_ARG (fwd_workspace NULL, or overlapping an output or the workspace) and WORKSPACE

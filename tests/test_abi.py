@@ -85,6 +85,7 @@ def test_create_accepts_workload_shapes():
     (lambda d: setattr(d, "phi", 3), 2),
     (lambda d: setattr(d, "readout", 9), 2),
     (lambda d: setattr(d, "accuracy", 5), 2),
+    (lambda d: setattr(d, "accuracy", 4), 2),
     (lambda d: setattr(d, "head_dim", 48), 2),
     (lambda d: setattr(d, "head_dim", 256), 2),
     (lambda d: setattr(d, "ndim", 0), 3),
@@ -420,6 +421,10 @@ def test_backward_saved_support_sizes_and_argument_errors_before_launch():
     fused = T.Plan(grid=(64, 64), block=(16, 16), batch=1, heads=2, head_dim=64, accuracy="split")  # M = 16
     causal = T.Plan(grid=(4096,), block=(64,), batch=1, heads=2, head_dim=64, readout="causal",
                     accuracy="split")
+    train = T.Plan(grid=(4096,), block=(64,), batch=1, heads=2, head_dim=64, accuracy="train")
+    assert train.info.split_operands == 1
+    assert T.mhla_backward_saved_workspace_size(train.handle) == T.mhla_backward_saved_workspace_size(split.handle)
+    train.close()
     for p in (split, mala):
         assert T.mhla_backward_saved_workspace_size(p.handle) < T.mhla_backward_workspace_size(p.handle)
     n = ctypes.c_size_t()

@@ -6,8 +6,9 @@ Multi-Head", Overall framework and Key design 2 for the steps; Key design 3 for 
 Both backwards run the same kernels on the same values, so the saved one must reproduce the
 recomputing one bit for bit; the recomputing one is held to the oracle in test_gpu_backward.py,
 and here the gradients are checked against the oracle as well, with that file's bars.  The
-forward that saves its state runs with split operands; its output is checked against the oracle
-with the forward's bar.
+forward that saves its state runs with split summaries and mixing (MHLA_ACCURACY_SPLIT, or
+MHLA_ACCURACY_TRAIN, whose readout takes the mixed stack's high part with single operands); its
+output is checked against the oracle with the forward's bar.
 """
 import numpy as np
 import pytest
@@ -91,6 +92,11 @@ CASES = [
                    cls=True),
     synth.Workload("bws_mala", "bf16", 2, 2, 64, (32, 32), (32, 32), 210, "none", "mala"),
     synth.Workload("bws_mala_fp32", "fp32", 1, 2, 128, (900,), (900,), 211, "none", "mala"),
+    # MHLA_ACCURACY_TRAIN: the readout at the bf16 level from the split mixed stack's high part
+    synth.Workload("bws_1d_m64_train", "bf16", 2, 2, 64, (4096,), (64,), 213, "softmax_l1"),
+    synth.Workload("bws_2d_d128_train", "bf16", 1, 2, 128, (48, 48), (8, 8), 214, "softmax_gauss"),
+    synth.Workload("bws_m300_valu_train", "bf16", 1, 1, 32, (4800,), (16,), 215, "softmax_gauss"),
+    synth.Workload("bws_relu_train", "bf16", 1, 2, 64, (48, 48), (8, 8), 216, "softmax_l1", phi="relu"),
 ]
 
 
@@ -101,7 +107,8 @@ def test_backward_saved_matches_recompute(w):
     if w.phi == "relu":
         q = np.abs(q)
     do = synth.make_grad_output(w, rng)
-    accuracy = "auto" if w.name.endswith("_auto") or w.readout == "mala" else "split"
+    accuracy = ("auto" if w.name.endswith("_auto") or w.readout == "mala" else
+                "train" if w.name.endswith("_train") else "split")
     o, saved, recomputed = run_saved_and_recompute(w, q, k, v, mc, do, accuracy=accuracy)
     check(w, o, saved, recomputed, q, k, v, mc, do, bwd_tol=FP32_TOL if w.dtype == "fp32" else BF16_TOL)
 
@@ -126,13 +133,14 @@ def test_backward_saved_per_head_mc_and_bf16_gradients():
 
 def test_backward_saved_long1d_full_size():
     """The long-sequence workload at full size with bf16 gradients, as the training leg of the
-    benchmark runs it: the saved backward equals the recomputing one bit for bit over every head,
-    and the split forward's output and the gradients of heads 0 and 15 match the oracle."""
+    benchmark runs it (MHLA_ACCURACY_TRAIN): the saved backward equals the recomputing one bit for
+    bit over every head, and the forward's output and the gradients of heads 0 and 15 match the
+    oracle."""
     w = synth.WORKLOADS["long1d"]
     announce(f"backward saved long1d shape={w.qkv_shape}")
     q, k, v, mc, rng = synth.make_inputs(w)
     do = synth.make_grad_output(w, rng, "bf16")
-    o, saved, recomputed = run_saved_and_recompute(w, q, k, v, mc, do, out_dtype="bf16")
+    o, saved, recomputed = run_saved_and_recompute(w, q, k, v, mc, do, out_dtype="bf16", accuracy="train")
     for name, a, b in zip(NAMES, saved, recomputed):
         assert np.array_equal(a, b), name
     heads = [(0, 0), (0, w.heads - 1)]

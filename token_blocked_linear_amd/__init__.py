@@ -16,7 +16,7 @@ __all__ = [
     "MHLA_READOUT_NORMALIZED", "MHLA_READOUT_UNNORMALIZED", "MHLA_READOUT_MALA",
     "MHLA_READOUT_CAUSAL_NORMALIZED", "MHLA_READOUT_CAUSAL_UNNORMALIZED",
     "MHLA_FLAG_RAGGED_BLOCKS", "MHLA_FLAG_CLS_TOKEN",
-    "MHLA_ACCURACY_AUTO", "MHLA_ACCURACY_BF16", "MHLA_ACCURACY_SPLIT",
+    "MHLA_ACCURACY_AUTO", "MHLA_ACCURACY_BF16", "MHLA_ACCURACY_SPLIT", "MHLA_ACCURACY_TRAIN",
     "MhlaDesc", "MhlaPlanInfo", "MhlaError", "MhlaLibraryMissing", "library_path", "load_library",
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",
     "mhla_plan_get_info", "mhla_timing_enable", "mhla_timing_read", "mhla_timing_reset",
@@ -33,7 +33,7 @@ MHLA_PHI_ELU1, MHLA_PHI_RELU, MHLA_PHI_EXP = 0, 1, 2
 MHLA_READOUT_NORMALIZED, MHLA_READOUT_UNNORMALIZED, MHLA_READOUT_MALA = 0, 1, 2
 MHLA_READOUT_CAUSAL_NORMALIZED, MHLA_READOUT_CAUSAL_UNNORMALIZED = 3, 4
 MHLA_FLAG_RAGGED_BLOCKS, MHLA_FLAG_CLS_TOKEN = 1, 2
-MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT = 0, 1, 2
+MHLA_ACCURACY_AUTO, MHLA_ACCURACY_BF16, MHLA_ACCURACY_SPLIT, MHLA_ACCURACY_TRAIN = 0, 1, 2, 3
 MHLA_ERR_SCRATCH_LIMIT = 7
 MHLA_NOALLOC_SCRATCH_BYTES = 160 << 20     # the no-alloc forward's scratch array (include/mhla.h)
 
@@ -42,7 +42,8 @@ _READOUTS = {"normalized": MHLA_READOUT_NORMALIZED, "unnormalized": MHLA_READOUT
              "causal_unnormalized": MHLA_READOUT_CAUSAL_UNNORMALIZED}
 _DTYPES = {"bf16": MHLA_DTYPE_BF16, "fp32": MHLA_DTYPE_FP32}
 _PHIS = {"elu1": MHLA_PHI_ELU1, "relu": MHLA_PHI_RELU, "exp": MHLA_PHI_EXP}
-_ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MHLA_ACCURACY_SPLIT}
+_ACCURACY = {"auto": MHLA_ACCURACY_AUTO, "bf16": MHLA_ACCURACY_BF16, "split": MHLA_ACCURACY_SPLIT,
+             "train": MHLA_ACCURACY_TRAIN}
 
 EXPORTED_SYMBOLS = (
     "mhla_create", "mhla_workspace_size", "mhla_forward", "mhla_destroy", "mhla_status_string",

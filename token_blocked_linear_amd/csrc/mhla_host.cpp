@@ -80,6 +80,7 @@ struct mhla_plan {
   int64_t B, H, BH, N, M, n_b;
   mhla::Geom geom;
   bool in_fp32, out_fp32, mala, split, split_v;
+  bool rd_split;   // the readout's own operands split (= split, except at MHLA_ACCURACY_TRAIN)
   bool mix_mfma;   // bf16 summary stack (mixed on MFMA or in the readout prologue)
   bool mix_split;  // mixing kernel on MFMA with split operands over fp32 partials
   bool mix_wlo;    // the bf16 mixing kernel takes M_c as bf16 hi + lo
@@ -163,7 +164,7 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
     return MHLA_ERR_UNSUPPORTED;
   if (d->readout < MHLA_READOUT_NORMALIZED || d->readout > MHLA_READOUT_CAUSAL_UNNORMALIZED)
     return MHLA_ERR_UNSUPPORTED;
-  if (d->accuracy < MHLA_ACCURACY_AUTO || d->accuracy > MHLA_ACCURACY_SPLIT) return MHLA_ERR_UNSUPPORTED;
+  if (d->accuracy < MHLA_ACCURACY_AUTO || d->accuracy > MHLA_ACCURACY_TRAIN) return MHLA_ERR_UNSUPPORTED;
   if (d->mc_per_head != 0 && d->mc_per_head != 1) return MHLA_ERR_INVALID_ARG;
   if (!(d->head_dim == 16 || d->head_dim == 32 || d->head_dim == 64 || d->head_dim == 128))
     return MHLA_ERR_UNSUPPORTED;
@@ -238,7 +239,7 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   // `split` sets the precision of the summaries and the mixing (of the earlier blocks, for the
   // causal readout), and of the bf16-input causal kernel's own products; the fp32-input causal
   // kernel keeps its running state and in-sub-chunk scores split whatever this says.
-  if (d->accuracy == MHLA_ACCURACY_SPLIT)
+  if (d->accuracy == MHLA_ACCURACY_SPLIT || d->accuracy == MHLA_ACCURACY_TRAIN)
     P->split = true;
   else if (d->accuracy == MHLA_ACCURACY_BF16)
     P->split = false;
@@ -296,6 +297,12 @@ mhla_status build_plan(const mhla_desc* din, mhla_plan* P) {
   const bool mix_kernel = P->fuse == kFuseNone && !(causal && M == 1);
   P->mix_split = mix_kernel && !P->mix_mfma && M <= 256;
   P->mix_kernel = mix_kernel;
+  // MHLA_ACCURACY_TRAIN: split summaries and mixing (what mhla_backward_saved reads), and a
+  // readout of the mixed stack's high part with the operands MHLA_ACCURACY_AUTO would choose
+  P->rd_split = P->split;
+  if (d->accuracy == MHLA_ACCURACY_TRAIN && mix_kernel && !causal && !P->mala && !P->in_fp32 &&
+      d->phi == MHLA_PHI_ELU1)
+    P->rd_split = false;
   P->n_kernels = 0;
   P->kernel_names[P->n_kernels++] = "summary";
   if (mix_kernel) P->kernel_names[P->n_kernels++] = "mix";
@@ -569,7 +576,7 @@ mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void*
   rp.q = q;
   rp.o = o;
   rp.st_hi = st_hi;
-  rp.st_lo = st_lo;
+  rp.st_lo = h->rd_split ? st_lo : nullptr;
   rp.zt = zt;
   rp.g = h->geom;
   rp.splits = h->rd_splits;
@@ -584,7 +591,7 @@ mhla_status forward_run(mhla_handle h, const void* q, const void* k, const void*
   rp.mc_head_stride = mc_stride;
   rp.H = (int32_t)h->H;
   rp.ssplits = h->sum_splits;
-  e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->split, h->fuse, h->q_stream,
+  e = mhla::launch_readout(rp, h->d, h->in_fp32, h->out_fp32, h->mode, h->rd_split, h->fuse, h->q_stream,
                            (int)h->desc.phi, (int)(h->rd_splits * h->M * h->BH), s);
   if (e != hipSuccess || !mark()) return MHLA_ERR_HIP;
   return MHLA_OK;
