@@ -34,18 +34,26 @@
 
 namespace mhla {
 
+// Columns (fragment positions) of a staged tile: 16384 / MPAD, so a tile holds 16384 bf16 values.
+// The bf16 kernel with 4 waves and at most 64 blocks stages half as many, so that each workgroup
+// walks two tiles or more and the next tile's loads overlap the current one's MFMAs (the
+// mixing of video3d's 64 blocks: 14.2 -> 12.2 us).
+__host__ __device__ constexpr int mix_tile_cols(int nbc, bool split, int nw) {
+  return ((!split && nw == 4 && nbc <= 2) ? 8192 : 16384) / (32 * nbc);
+}
+
 // NBC: 32-block chunks of the contraction (M <= 32*NBC); ITW: 16-row i-tiles per wave; NW:
-// waves per workgroup.  With NW = 8 (the split kernel and the bf16 kernel with WLO at M > 128) a
-// loader thread takes 8 rows x 4 columns of the tile instead of 8 x 8, so that the tile's
-// registers halve.
+// waves per workgroup.  With NW = 8 (the split kernel and the bf16 kernel with WLO at M > 128),
+// and with the half-size tiles, a loader thread takes 8 rows x 4 columns of the tile instead of
+// 8 x 8, so that the tile's registers halve (and the loader threads still cover its rows once).
 template <int NBC, int ITW, bool SPLIT, int NW = 4, bool WLO = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void mix_mfma_kernel(
     MixMfmaParams p) {
   constexpr int MPAD = 32 * NBC;
-  constexpr int PB = 16384 / MPAD;        // columns (fragment positions) per staged tile
+  constexpr int PB = mix_tile_cols(NBC, SPLIT, NW);   // columns (fragment positions) per staged tile
   constexpr int NCG = PB / 32;            // 32-column groups per staged tile
   constexpr int XP = MPAD;                // LDS pitch (elements) of one transposed column
-  constexpr int LC = NW == 8 ? 4 : 8;     // tile columns per loader thread
+  constexpr int LC = (NW == 8 || PB * MPAD < 16384) ? 4 : 8;   // tile columns per loader thread
   constexpr int CG = PB / LC;             // column groups per tile
   static_assert(NW * 64 / CG * 8 == MPAD, "the loader threads cover the padded blocks once");
   static_assert(NW == 4 || SPLIT || WLO, "8 waves: W as hi + lo only");
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 template <int NBC, int ITW, bool SPLIT, int NW, bool WLO = false>
 static hipError_t launch_t(const MixMfmaParams& p, int row_groups, int bh, hipStream_t s) {
-  constexpr int MPAD = 32 * NBC, PB = 16384 / MPAD, XP = MPAD;
+  constexpr int MPAD = 32 * NBC, PB = mix_tile_cols(NBC, SPLIT, NW), XP = MPAD;
   const size_t lds = (size_t)PB * XP * 2 * (SPLIT ? 2 : 1);
   auto kern = mix_mfma_kernel<NBC, ITW, SPLIT, NW, WLO>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -392,7 +400,7 @@ hipError_t launch_mix_mfma(MixMfmaParams p, int bh, bool split, bool wlo, hipStr
   const int NBC = sh.nbc, ITW = sh.itw, row_groups = sh.row_groups, NW = sh.nw;
   p.wave_rows = sh.wave_rows;
   if (NBC >= 2 && sh.wave_rows != NW) return hipErrorInvalidValue;   // the kernel assumes WPW = 1
-  const int pb = 16384 / (32 * NBC);
+  const int pb = mix_tile_cols(NBC, split, NW);
   const int n_tiles = p.frag / pb;
   if (p.frag % pb != 0) return hipErrorInvalidValue;
   const int n_all = n_tiles + (2 * p.D + pb - 1) / pb;     // summary tiles + normaliser tiles
