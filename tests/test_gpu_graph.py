@@ -1,6 +1,6 @@
 """The library's calls under HIP graph capture.
 
-The forward, the causal forward and the backward launch kernels only: no allocation, no
+The forward, the causal forward, the backward and the backward from saved state launch kernels only: no allocation, no
 memset, no host synchronisation. A graph captured once (torch.cuda.graph around the call, on
 torch's capture stream) must therefore reproduce the eager call. Each test replays the graph
 several times. Before each replay it copies fresh inputs into the captured buffers, eagerly and
@@ -86,6 +86,49 @@ def test_backward_graph_replays_equal_eager():
         torch.cuda.synchronize()
         plan.backward(tq, tk, tv, tmc, tdo, *eager, ws)
         torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "dmc"), outs, eager):
+            assert torch.equal(a, b), (name, rep)
+    plan.close()
+
+
+def test_training_step_graph_replays_equal_eager():
+    """The training step, captured as one graph: the forward at MHLA_ACCURACY_TRAIN, then the
+    backward from its saved state.  Every replay equals the eager pair on the same inputs."""
+    import torch
+    w = synth.Workload("g_train", "bf16", 1, 2, 64, (4096,), (64,), 806, "softmax_gauss")
+    announce(f"graph training step {w.name} shape={w.qkv_shape}")
+    plan = _plan(w, accuracy="train")
+    fws, bws = plan.alloc_workspace(), plan.alloc_backward_saved_workspace()
+    rng = np.random.default_rng(w.seed)
+    q, k, v, mc, _ = synth.make_inputs(w)
+    tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
+    tdo = to_device(synth.make_grad_output(w, rng), "fp32")
+    tmc = torch.from_numpy(mc.astype(np.float32)).to("cuda:0")
+    o = torch.empty_like(tdo)
+    outs = [torch.empty_like(tdo) for _ in range(3)] + [torch.empty_like(tmc)]
+
+    def step(o_, grads):
+        plan.forward(tq, tk, tv, tmc, o_, fws)
+        plan.backward(tq, tk, tv, tmc, tdo, *grads, bws, fwd_workspace=fws)
+
+    step(o, outs)                                  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(o, outs)
+    torch.cuda.synchronize()
+    o_eager = torch.empty_like(o)
+    eager = [torch.empty_like(x) for x in outs]
+    for rep in range(3):
+        tdo.copy_(to_device(rng.standard_normal(w.qkv_shape), "fp32"))
+        for dst in (tq, tk, tv):
+            dst.copy_(to_device(rng.standard_normal(w.qkv_shape).astype(np.float32), w.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(o_eager, eager)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager), ("o", rep)
         for name, a, b in zip(("dq", "dk", "dv", "dmc"), outs, eager):
             assert torch.equal(a, b), (name, rep)
     plan.close()
