@@ -221,7 +221,8 @@ mhla_status mhla_forward_intermediates(mhla_handle h, const void* k, const void*
  *   dmc          device fp32 with M_c's shape, written; for a shared [M, M] M_c the sum over
  *                batch and heads, for a per-head [H, M, M] one the sum over batch; NULL skips it.
  *                MALA has no M_c: dmc must be NULL (else MHLA_ERR_INVALID_ARG)
- * The forward's summaries are recomputed (nothing from mhla_forward is reused); every product
+ * The forward's summaries are recomputed (nothing from mhla_forward is reused; mhla_backward_saved
+ * reads them from the forward's workspace instead); every product
  * uses hi/lo bf16 operand splits.  Not supported (MHLA_ERR_UNSUPPORTED): the causal readouts,
  * head size 16.  Outputs must not alias the inputs, each other or the workspace.  The workspace
  * (256-byte aligned) size comes from mhla_backward_workspace_size and differs from the
