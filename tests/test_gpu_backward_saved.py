@@ -157,3 +157,15 @@ def test_backward_saved_long1d_full_size():
         assert excess.max() <= 0, (name, excess.max())
     print(f"  o={fwd_err:.2e} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + " (saved == recomputed)")
     record("backward_saved", "long1d", o=fwd_err, **errs)
+
+
+def test_backward_saved_video3d_full_size():
+    """The video workload at full size (32 heads, 64 blocks of 4 x 8 x 8 tokens) through the
+    training step at MHLA_ACCURACY_TRAIN: bit-identical gradients to the recomputing backward,
+    and the forward's output and every gradient against the oracle."""
+    w = synth.WORKLOADS["video3d"]
+    announce(f"backward saved video3d shape={w.qkv_shape}")
+    q, k, v, mc, rng = synth.make_inputs(w)
+    do = synth.make_grad_output(w, rng)
+    o, saved, recomputed = run_saved_and_recompute(w, q, k, v, mc, do, accuracy="train")
+    check(w, o, saved, recomputed, q, k, v, mc, do, bwd_tol=BF16_TOL)
