@@ -302,6 +302,8 @@ def make_desc(*, grid: Sequence[int], block: Sequence[int], batch: int, heads: i
               in_dtype: str = "bf16", out_dtype: str = "fp32", readout: str = "normalized",
               accuracy: str = "auto", mc_per_head: bool = False, phi: str = "elu1",
               ragged: bool = False, cls_token: bool = False) -> MhlaDesc:
+    """The plan descriptor of include/mhla.h.  accuracy: "auto", "bf16", "split", or "train" (the
+    summaries and mixing split, as mhla_backward_saved needs them; the readout as "auto")."""
     if len(grid) != len(block) or not 1 <= len(grid) <= 3:
         raise ValueError("grid and block must have the same rank, 1 to 3")
     d = MhlaDesc()
